@@ -1,0 +1,30 @@
+"""fp64 CPU oracle of clustered block-sparse attention.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+cpu_baseline leg of bench.py, never by the library.  It shares no code with the
+HIP path.  See oracle/cbsa.py for the functions and the passages they follow.
+"""
+
+from .cbsa import (  # noqa: F401
+    NEAR_TIE_REL,
+    BisectNode,
+    ClusterCfg,
+    HeadResult,
+    SelectCfg,
+    attention,
+    bisect,
+    bisect_split,
+    cluster_head,
+    cluster_logits,
+    cluster_means,
+    dense_attention,
+    forward_head,
+    kmeans,
+    kmeans_assign,
+    kmeans_update,
+    permute,
+    select,
+    sq_dists,
+    subspace_cluster,
+    subspace_logits,
+)

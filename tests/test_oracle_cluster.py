@@ -1,0 +1,164 @@
+"""Pins of the oracle's clustering steps (CPU only).
+
+k-means is pinned to SciPy's Lloyd implementation (an independent library
+routine with the same first-k / keep-empty semantics) and to invariants; the
+balanced bisection to its size law, to separated blobs and to a brute-force
+optimum of the balanced split; the permutation to bijection/stability laws."""
+
+import itertools
+
+import numpy as np
+import pytest
+import scipy.cluster.vq as vq
+
+import oracle
+
+
+def smooth_points(rng, n, d):
+    t = np.linspace(0, 6, n)[:, None]
+    return np.sin(t * rng.uniform(0.5, 2, size=(1, d)) + rng.uniform(0, 6, size=(1, d))) + 0.05 * rng.normal(size=(n, d))
+
+
+def test_kmeans_matches_scipy_lloyd(rng):
+    for trial in range(5):
+        x = smooth_points(rng, 300, 6) if trial % 2 else rng.normal(size=(300, 6))
+        C, T = 9, 5
+        r = oracle.kmeans(x, C, T)
+        code, label = vq.kmeans2(x.copy(), x[:C].copy(), iter=T, minit="matrix", missing="warn")
+        assert np.array_equal(r["labels"], label)
+        np.testing.assert_allclose(r["centroids"], code, rtol=0, atol=1e-12)
+
+
+def test_kmeans_assign_ties_go_to_smallest_index():
+    x = np.array([[0.0, 0.0], [1.0, 0.0]])
+    c = np.array([[1.0, 1.0], [-1.0, 0.0], [1.0, -1.0], [0.5, 0.0]])
+    labels, dmin, gap, near = oracle.kmeans_assign(x, c)
+    # token 0: centroids 0 and 2 are at distance 2, centroid 1 at 1, 3 at 0.25
+    assert labels[0] == 3
+    # token 1: centroids 0, 2 at distance 1, centroid 3 at 0.25 -> 3; drop 3 to force the tie
+    labels2, _, gap2, near2 = oracle.kmeans_assign(x, c[:3])
+    assert labels2[1] == 0 and gap2[1] == 0 and near2[1]
+    assert labels2[0] == 1
+
+
+def test_kmeans_invariants(rng):
+    x = smooth_points(rng, 400, 8)
+    C = 12
+    c = x[:C].copy()
+    prev = np.inf
+    for _ in range(6):
+        labels, dmin, _, _ = oracle.kmeans_assign(x, c)
+        obj = dmin.sum()
+        assert obj <= prev + 1e-9
+        prev = obj
+        c, sizes = oracle.kmeans_update(x, labels, c)
+        assert sizes.sum() == len(x)
+        for j in range(C):
+            if sizes[j]:
+                np.testing.assert_allclose(c[j], x[labels == j].mean(0), atol=1e-12)
+
+
+def test_kmeans_empty_cluster_keeps_centroid():
+    # duplicate first tokens: centroid 1 equals centroid 0 and loses every tie
+    x = np.array([[0.0, 0.0], [0.0, 0.0], [5.0, 5.0], [5.1, 5.0], [0.1, 0.0]])
+    r = oracle.kmeans(x, 3, 1)
+    assert r["sizes"].tolist() == [3, 0, 2]
+    np.testing.assert_array_equal(r["centroids"][1], [0.0, 0.0])
+    # next round: the kept centroid (0,0) is nearer to the two duplicates than
+    # the moved centroid 0 (0.033, 0), so cluster 1 wins them back
+    r2 = oracle.kmeans(x, 3, 2)
+    assert r2["sizes"].tolist() == [1, 2, 2]
+
+
+# --------------------------------------------------------------------------
+# bisection
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("N,L", [(1000, 128), (256, 128), (300, 64), (129, 128), (128, 128), (77, 8)])
+def test_bisect_size_law(rng, N, L):
+    x = rng.normal(size=(N, 5))
+    r = oracle.bisect(x, L, 3)
+    C = -(-N // L)
+    sizes = np.diff(r["offsets"])
+    assert len(sizes) == C
+    assert np.all(sizes[:-1] == L) and sizes[-1] == N - (C - 1) * L
+    assert sorted(r["perm"].tolist()) == list(range(N))
+    for j in range(C):
+        seg = r["perm"][r["offsets"][j]:r["offsets"][j + 1]]
+        assert np.all(np.diff(seg) > 0)  # ascending original index in a leaf
+        assert np.all(r["labels"][seg] == j)
+
+
+def test_bisect_recovers_separated_blobs(rng):
+    L, k = 16, 3
+    centres = rng.normal(size=(2 ** k, 4)) * 50
+    pts = np.concatenate([c + rng.normal(size=(L, 4)) for c in centres])
+    blob = np.repeat(np.arange(2 ** k), L)
+    sh = rng.permutation(len(pts))
+    pts, blob = pts[sh], blob[sh]
+    r = oracle.bisect(pts, L, 5)
+    for j in range(2 ** k):
+        seg = r["perm"][r["offsets"][j]:r["offsets"][j + 1]]
+        assert len(set(blob[seg].tolist())) == 1
+    assert len(set(blob[r["perm"][r["offsets"][j]:r["offsets"][j + 1]]][0] for j in range(2 ** k))) == 2 ** k
+
+
+def test_bisect_split_is_optimal_balanced_assignment(rng):
+    """For fixed (c1, c2), the (delta, index) rule is the balanced assignment
+    minimising sum_left ||x-c1||^2 + sum_right ||x-c2||^2 (brute force)."""
+    for trial in range(20):
+        n = int(rng.integers(4, 13))
+        n_left = int(rng.integers(1, n))
+        x = rng.normal(size=(n, 3))
+        c1, c2 = rng.normal(size=3), rng.normal(size=3)
+        members = np.arange(n)
+        left, _, _, _ = oracle.bisect_split(x, members, n_left, c1.copy(), c2.copy(), 1)
+        d1 = ((x - c1) ** 2).sum(1)
+        d2 = ((x - c2) ** 2).sum(1)
+        best = min(sum(d1[list(S)]) + d2.sum() - sum(d2[list(S)])
+                   for S in itertools.combinations(range(n), n_left))
+        got = d1[left].sum() + d2[~left].sum()
+        assert left.sum() == n_left
+        assert got <= best + 1e-12
+
+
+def test_bisect_sides_follow_nearest_mean():
+    # two groups: the group near x[0] must go left (sign of delta)
+    x = np.array([[0.0], [10.0], [0.2], [10.2], [0.1], [9.9], [0.3], [10.1]])
+    r = oracle.bisect(x, 4, 2)
+    left = r["perm"][:4]
+    assert set(left.tolist()) == {0, 2, 4, 6}
+
+
+# --------------------------------------------------------------------------
+# permutation, subspace combos
+# --------------------------------------------------------------------------
+
+def test_permute_laws(rng):
+    labels = rng.integers(0, 7, size=200)
+    labels[labels == 3] = 2  # cluster 3 empty
+    perm, off = oracle.permute(labels, 7)
+    assert sorted(perm.tolist()) == list(range(200))
+    assert off[0] == 0 and off[-1] == 200 and off[4] - off[3] == 0
+    x = rng.normal(size=(200, 3))
+    xp = x[perm]
+    back = np.empty_like(xp)
+    back[perm] = xp
+    np.testing.assert_array_equal(back, x)
+    for j in range(7):
+        seg = perm[off[j]:off[j + 1]]
+        assert np.all(labels[seg] == j) and np.all(np.diff(seg) > 0)
+
+
+def test_subspace_combo_ids(rng):
+    k = smooth_points(rng, 500, 8)
+    dims = (2, 3, 3)
+    r = oracle.subspace_cluster(k, dims, 4, 3)
+    off = 0
+    for s, ds in enumerate(dims):
+        rs = oracle.kmeans(k[:, off:off + ds], 4, 3)
+        assert np.array_equal(rs["labels"], r["sub_labels"][s])
+        off += ds
+    a_t, a_h, a_w = r["sub_labels"]
+    assert np.array_equal(r["labels"], a_t * 16 + a_h * 4 + a_w)
+    assert r["combo_sizes"].sum() == 500
