@@ -1,0 +1,676 @@
+// Block-sparse attention over the selected key clusters, with optional mean
+// compensation of the excluded ones, writing rows back in original order.
+//
+// SCOPE (English abstract): attention runs over the selected original keys
+// and values.  ClusterAttention (English abstract): clusters are contiguous
+// power-of-two blocks so block-sparse attention keeps dense per-pair
+// throughput, and an excluded cluster is compensated through its mean.  The
+// closed form for a query n of query cluster i (sel = keys of the selected
+// key clusters, excl = the non-empty excluded clusters, c = compensation):
+//   O_n = [sum_sel e^{s_nm} v_m + c sum_excl |K_j| e^{<q_n,kbar_j>s} vbar_j]
+//       / [sum_sel e^{s_nm}     + c sum_excl |K_j| e^{<q_n,kbar_j>s}]
+//
+// Layout.  Keys/values are in key-cluster order, so a query cluster's
+// selection is a short list of contiguous row ranges (adjacent selected
+// clusters merged).  A workgroup owns one tile of up to 128 query rows of one
+// query cluster and streams the concatenated ranges in 64-key tiles; the
+// compensation runs afterwards over "pseudo keys" (one per key cluster) whose
+// logit carries the bias ln|K_j| (-inf where selected or empty).
+//
+// bf16 path: 4 waves x 32 query rows.  S^T = K Q^T on 32x32x16 bf16 MFMA so
+// every lane owns one query column and keeps the online-softmax state in
+// registers; P stays in registers and feeds O^T = V^T P^T directly (V is
+// stored transposed in LDS).  Rescaling is lazy (only when the running max
+// grows by more than 2^8).  kbar enters the compensation logits as a bf16
+// hi + lo pair so those logits are fp32-accurate.
+// fp32 path: one thread per query row, fp32 FMA (parity-grade, small inputs).
+
+#include <math.h>
+
+#include "sa_internal.h"
+
+namespace sa {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int KT = 64;      // keys per tile
+constexpr int TQ = 128;     // query rows per workgroup (upper bound)
+constexpr int RCH = 512;    // ranges staged in LDS at a time
+constexpr float LOG2E = 1.4426950408889634f;
+
+struct Prep {
+  int4* tiles;        // [H][maxT] {cluster, first position, rows, 0}
+  int32_t* ntiles;    // [H]
+  int2* ranges;       // [H][Cq][Rmax] {start, end}
+  int32_t* rcount;    // [H][Cq]
+  bf16_t* kbh;        // [H][Ckp][D]
+  bf16_t* kbl;        // [H][Ckp][D]
+  bf16_t* vb;         // [H][Ckp][D]
+  float* logsz;       // [H][Ckp]  ln|K_j| or -inf for empty
+  float* kbf;         // fp32 path: [H][Ckp][D]
+  float* vbf;         // fp32 path: [H][Ckp][D]
+  int maxT, Rmax, Ckp, W;
+};
+
+// --------------------------------------------------------------------------
+// preparation
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void ranges_kernel(const uint32_t* __restrict__ mask,
+                                                    const int32_t* __restrict__ k_off, int Cq,
+                                                    int Ck, int W, int Rmax,
+                                                    int2* __restrict__ ranges,
+                                                    int32_t* __restrict__ rcount) {
+  const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const uint32_t* mr = mask + (size_t(h) * Cq + i) * W;
+  const int32_t* ko = k_off + size_t(h) * (Ck + 1);
+  int2* out = ranges + (size_t(h) * Cq + i) * Rmax;
+  int ns = 0, ne = 0;
+  const uint64_t lt = (uint64_t(1) << lane) - 1;
+  for (int j0 = 0; j0 < Ck; j0 += 64) {
+    const int j = j0 + lane;
+    const bool in = j < Ck;
+    const bool sel = in && ((mr[j >> 5] >> (j & 31)) & 1u);
+    const bool selp = in && j > 0 && ((mr[(j - 1) >> 5] >> ((j - 1) & 31)) & 1u);
+    const bool seln = in && (j + 1 < Ck) && ((mr[(j + 1) >> 5] >> ((j + 1) & 31)) & 1u);
+    const bool st = sel && !selp;
+    const bool en = sel && !seln;
+    const uint64_t bs = __ballot(st), be = __ballot(en);
+    if (st) out[ns + __popcll(bs & lt)].x = ko[j];
+    if (en) out[ne + __popcll(be & lt)].y = ko[j + 1];
+    ns += __popcll(bs);
+    ne += __popcll(be);
+  }
+  if (lane == 0) rcount[size_t(h) * Cq + i] = ns;
+}
+
+__global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__ q_off, int Cq,
+                                                     int rows, int maxT, int4* __restrict__ tiles,
+                                                     int32_t* __restrict__ ntiles) {
+  __shared__ int wsum[16];
+  __shared__ int carry;
+  const int h = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int32_t* qo = q_off + size_t(h) * (Cq + 1);
+  if (t == 0) carry = 0;
+  __syncthreads();
+  for (int b = 0; b < Cq; b += 1024) {
+    const int i = b + t;
+    const int sz = i < Cq ? qo[i + 1] - qo[i] : 0;
+    const int nt = ceil_div(sz, rows);
+    int x = nt;
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int pre = carry;
+    for (int j = 0; j < w; ++j) pre += wsum[j];
+    pre += x - nt;
+    for (int u = 0; u < nt; ++u)
+      if (pre + u < maxT)
+        tiles[size_t(h) * maxT + pre + u] = make_int4(i, qo[i] + u * rows, min(rows, sz - u * rows), 0);
+    __syncthreads();
+    if (t == 1023) carry = pre + nt;
+    __syncthreads();
+  }
+  if (t == 0) ntiles[h] = carry;
+}
+
+__global__ __launch_bounds__(128) void comp_prep_kernel(const float* __restrict__ kbar,
+                                                        const float* __restrict__ vbar,
+                                                        const int32_t* __restrict__ k_off, int Ck,
+                                                        int Ckp, int D, bf16_t* kbh, bf16_t* kbl,
+                                                        bf16_t* vb, float* kbf, float* vbf,
+                                                        float* logsz) {
+  const int j = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const size_t o = (size_t(h) * Ckp + j) * D;
+  const bool in = j < Ck;
+  int sz = 0;
+  if (in) sz = k_off[size_t(h) * (Ck + 1) + j + 1] - k_off[size_t(h) * (Ck + 1) + j];
+  for (int c = t; c < D; c += 128) {
+    const float kv = (in && sz > 0) ? kbar[(size_t(h) * Ck + j) * D + c] : 0.f;
+    const float vv = (in && sz > 0) ? vbar[(size_t(h) * Ck + j) * D + c] : 0.f;
+    if (kbh) {
+      const bf16_t hi = f2bf(kv);
+      kbh[o + c] = hi;
+      kbl[o + c] = f2bf(kv - bf2f(hi));
+      vb[o + c] = f2bf(vv);
+    }
+    if (kbf) {
+      kbf[o + c] = kv;
+      vbf[o + c] = vv;
+    }
+  }
+  if (t == 0) logsz[size_t(h) * Ckp + j] = sz > 0 ? logf(float(sz)) : -__builtin_huge_valf();
+}
+
+// Workgroup -> (head, tile).  Workgroups are handed to the 8 XCDs round-robin
+// by linear id; the remap gives each XCD one contiguous run of tiles (heads in
+// order), so the key/value rows a head's neighbouring query clusters share are
+// reused from that XCD's L2.  The grid is padded to a multiple of 8.
+__device__ __forceinline__ void map_tile(int maxT, int H, int& h, int& tix) {
+  const int total = maxT * H;
+  const int per = (total + 7) / 8;
+  const int b = blockIdx.x;
+  const int lin = (b & 7) * per + (b >> 3);
+  h = lin / maxT;  // lin >= total -> h >= H: padding workgroup
+  tix = lin % maxT;
+}
+
+// stage one chunk of ranges in LDS: rs[k] = start, rp[k] = prefix length
+__device__ int stage_ranges(const int2* __restrict__ rg, int c0, int nrc, int* rs, int* rp,
+                            int* wsum) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, nw = blockDim.x >> 6;
+  int carry = 0;
+  for (int b = 0; b < nrc; b += blockDim.x) {
+    const int k = b + t;
+    int len = 0;
+    if (k < nrc) {
+      const int2 r = rg[c0 + k];
+      rs[k] = r.x;
+      len = r.y - r.x;
+    }
+    int x = len;
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int pre = carry, tot = 0;
+    for (int j = 0; j < nw; ++j) {
+      if (j < w) pre += wsum[j];
+      tot += wsum[j];
+    }
+    if (k < nrc) rp[k] = pre + x - len;
+    carry += tot;
+    __syncthreads();
+  }
+  if (t == 0) rp[nrc] = carry;
+  __syncthreads();
+  return rp[nrc];
+}
+
+// key row of concatenated position `pos`, advancing a cursor over rp[]
+__device__ __forceinline__ int cursor_row(const int* rs, const int* rp, int nrc, int pos, int& cur) {
+  while (cur + 1 < nrc && rp[cur + 1] <= pos) ++cur;
+  return rs[cur] + (pos - rp[cur]);
+}
+
+// --------------------------------------------------------------------------
+// fp32 (and generic) path: one thread per query row
+// --------------------------------------------------------------------------
+template <typename T, int D>
+__global__ __launch_bounds__(128) void attn_simple(AttnArgs a, Prep p, float scale) {
+  __shared__ float Ks[32][D];
+  __shared__ float Vs[32][D];
+  __shared__ int rs[RCH + 1], rp[RCH + 1];
+  __shared__ int wsum[16];
+  __shared__ float bias[32];
+  int h, tix;
+  map_tile(p.maxT, a.H, h, tix);
+  if (h >= a.H || tix >= p.ntiles[h]) return;
+  const int4 td = p.tiles[size_t(h) * p.maxT + tix];
+  const int i = td.x, p0 = td.y, nr = td.z;
+  const int t = threadIdx.x;
+  const int N = a.N;
+  const bool qv = t < nr;
+  const T* qp = (const T*)a.q_perm + (size_t(h) * N + p0 + (qv ? t : 0)) * D;
+  float q[D], o[D];
+#pragma unroll
+  for (int c = 0; c < D; ++c) {
+    q[c] = to_f(qp[c]) * scale;
+    o[c] = 0.f;
+  }
+  float m = -__builtin_huge_valf(), l = 0.f;
+  const T* kh = (const T*)a.k_perm + size_t(h) * N * D;
+  const T* vh = (const T*)a.v_perm + size_t(h) * N * D;
+  const int R = p.rcount[size_t(h) * a.Cq + i];
+  const int2* rg = p.ranges + (size_t(h) * a.Cq + i) * p.Rmax;
+  auto consume = [&](int nk, const float* bs) {
+    for (int kk = 0; kk < nk; ++kk) {
+      float s = 0.f;
+#pragma unroll
+      for (int c = 0; c < D; ++c) s = fmaf(q[c], Ks[kk][c], s);
+      if (bs) s += bs[kk];
+      if (s == -__builtin_huge_valf()) continue;
+      if (s > m) {
+        const float al = expf(m - s);
+        l *= al;
+#pragma unroll
+        for (int c = 0; c < D; ++c) o[c] *= al;
+        m = s;
+      }
+      const float pr = expf(s - m);
+      l += pr;
+#pragma unroll
+      for (int c = 0; c < D; ++c) o[c] = fmaf(pr, Vs[kk][c], o[c]);
+    }
+  };
+  for (int c0 = 0; c0 < R; c0 += RCH) {
+    const int nrc = min(RCH, R - c0);
+    __syncthreads();
+    const int total = stage_ranges(rg, c0, nrc, rs, rp, wsum);
+    for (int base = 0; base < total; base += 32) {
+      const int nk = min(32, total - base);
+      __syncthreads();
+      for (int v = t; v < 32 * D; v += 128) {
+        const int kk = v / D, c = v % D;
+        float kv = 0.f, vv = 0.f;
+        if (kk < nk) {
+          // binary search the range of position base+kk
+          const int pos = base + kk;
+          int lo = 0, hi = nrc - 1;
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (rp[mid] <= pos) lo = mid; else hi = mid - 1;
+          }
+          const int row = rs[lo] + (pos - rp[lo]);
+          kv = to_f(kh[size_t(row) * D + c]);
+          vv = to_f(vh[size_t(row) * D + c]);
+        }
+        Ks[kk][c] = kv;
+        Vs[kk][c] = vv;
+      }
+      __syncthreads();
+      consume(nk, nullptr);
+    }
+  }
+  if (a.compensate) {
+    const uint32_t* mr = a.mask + (size_t(h) * a.Cq + i) * p.W;
+    for (int j0 = 0; j0 < a.Ck; j0 += 32) {
+      const int nk = min(32, a.Ck - j0);
+      __syncthreads();
+      for (int v = t; v < 32 * D; v += 128) {
+        const int kk = v / D, c = v % D;
+        const size_t src = (size_t(h) * p.Ckp + j0 + kk) * D + c;
+        Ks[kk][c] = kk < nk ? p.kbf[src] : 0.f;
+        Vs[kk][c] = kk < nk ? p.vbf[src] : 0.f;
+      }
+      if (t < 32) {
+        const int j = j0 + t;
+        float b = -__builtin_huge_valf();
+        if (t < nk && !((mr[j >> 5] >> (j & 31)) & 1u)) b = p.logsz[size_t(h) * p.Ckp + j];
+        bias[t] = b;
+      }
+      __syncthreads();
+      consume(nk, bias);
+    }
+  }
+  if (qv) {
+    const float inv = l > 0.f ? 1.f / l : 0.f;
+    T* op = (T*)a.o + (size_t(h) * N + a.q_idx[size_t(h) * N + p0 + t]) * D;
+#pragma unroll
+    for (int c = 0; c < D; ++c) op[c] = from_f<T>(o[c] * inv);
+  }
+}
+
+// --------------------------------------------------------------------------
+// bf16 MFMA path
+// --------------------------------------------------------------------------
+__device__ __forceinline__ floatx16 mfma32(bf16x8_t a, bf16x8_t b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+  return uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16);
+}
+
+template <int D>
+struct MfmaLds {
+  bf16_t K[2][KT][D + 8];      // key rows, padded against bank conflicts
+  bf16_t V[2][D][KT + 4];      // V^T
+  int rs[RCH + 1];
+  int rp[RCH + 1];
+  int wsum[16];
+  float bias[KT];
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float scale_log2) {
+  static_assert(D == 64 || D == 128, "head dim");
+  constexpr int DS = D / 16;         // MFMA k-steps over d
+  constexpr int DT = D / 32;         // 32-row tiles of d in O^T
+  constexpr int KCH = D / 4;         // K elements per thread (one row, quarter)
+  constexpr int KPT = D / 32;        // V keys per thread
+  constexpr int DG = D / 8;          // V 8-column groups
+  __shared__ __attribute__((aligned(16))) MfmaLds<D> S;
+
+  int h, tix;
+  map_tile(p.maxT, a.H, h, tix);
+  if (h >= a.H || tix >= p.ntiles[h]) return;
+  const int4 td = p.tiles[size_t(h) * p.maxT + tix];
+  const int i = td.x, p0 = td.y, nr = td.z;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, hi = lane >> 5;
+  const int N = a.N;
+
+  // Q fragments (B operand of S^T = K Q^T): query 32w+col, d = 16s + 8hi + e
+  const int qr = 32 * w + col;
+  const bool qv = qr < nr;
+  const bf16_t* qrow = (const bf16_t*)a.q_perm + (size_t(h) * N + p0 + (qv ? qr : 0)) * D;
+  bf16x8_t qf[DS];
+#pragma unroll
+  for (int s = 0; s < DS; ++s) {
+    uint4 u = *reinterpret_cast<const uint4*>(qrow + 16 * s + 8 * hi);
+    if (!qv) u = make_uint4(0, 0, 0, 0);
+    qf[s] = as_bf8(u);
+  }
+
+  floatx16 oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) oacc[dt][r] = 0.f;
+  float m = -__builtin_huge_valf();  // running max, log2 domain
+  float lsum = 0.f;                   // this lane's share of the denominator
+
+  const bf16_t* kh = (const bf16_t*)a.k_perm + size_t(h) * N * D;
+  const bf16_t* vh = (const bf16_t*)a.v_perm + size_t(h) * N * D;
+
+  // loader roles
+  const int k_slot = tid >> 2, k_c0 = (tid & 3) * KCH;     // K: one row quarter
+  const int v_dg = tid % DG, v_kg = tid / DG;              // V: KPT keys x 8 columns
+
+  uint4 kreg[KCH / 8];
+  uint4 vreg[KPT];
+
+  // online-softmax update + P V for one tile whose S^T is in s[0..1]
+  auto softmax_pv = [&](floatx16 (&s)[2], int buf, int nvalid, const float* bias_l2) {
+    float mx = -__builtin_huge_valf();
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
+        float x = s[kt][r] * scale_log2;
+        if (bias_l2) x += bias_l2[key];
+        if (key >= nvalid) x = -__builtin_huge_valf();
+        s[kt][r] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float alpha = 1.f;
+    if (mx > m + 8.f) {
+      alpha = exp2f(m - mx);  // m = -inf -> 0
+      m = mx;
+    }
+    if (__ballot(alpha != 1.f)) {
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+    uint32_t pk[2][8];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const float x0 = s[kt][r], x1 = s[kt][r + 1];
+        const float e0 = (x0 == -__builtin_huge_valf()) ? 0.f : exp2f(x0 - m);
+        const float e1 = (x1 == -__builtin_huge_valf()) ? 0.f : exp2f(x1 - m);
+        lsum += e0 + e1;
+        pk[kt][r >> 1] = pack2(e0, e1);
+      }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kt = ks >> 1, half = ks & 1;
+      const uint4 pu = make_uint4(pk[kt][4 * half + 0], pk[kt][4 * half + 1], pk[kt][4 * half + 2],
+                                  pk[kt][4 * half + 3]);
+      const bf16x8_t pf = as_bf8(pu);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const bf16_t* vr = &S.V[buf][32 * dt + col][16 * ks + 4 * hi];
+        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
+        const uint2 up = *reinterpret_cast<const uint2*>(vr + 8);
+        const bf16x8_t vf = as_bf8(make_uint4(lo.x, lo.y, up.x, up.y));
+        oacc[dt] = mfma32(vf, pf, oacc[dt]);
+      }
+    }
+  };
+
+  auto qk = [&](floatx16 (&s)[2], const bf16_t (*Kb)[D + 8]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int st = 0; st < DS; ++st) {
+        const uint4 u = *reinterpret_cast<const uint4*>(&Kb[32 * kt + col][16 * st + 8 * hi]);
+        s[kt] = mfma32(as_bf8(u), qf[st], s[kt]);
+      }
+    }
+  };
+
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < KCH / 8; ++q)
+      *reinterpret_cast<uint4*>(&S.K[buf][k_slot][k_c0 + 8 * q]) = kreg[q];
+    // transpose KPT keys x 8 columns into V^T
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int c = v_dg * 8 + e;
+      bf16_t* dst = &S.V[buf][c][v_kg * KPT];
+      uint32_t wv[KPT];
+#pragma unroll
+      for (int kq = 0; kq < KPT; ++kq) {
+        const uint32_t word = (e < 2) ? vreg[kq].x : (e < 4) ? vreg[kq].y : (e < 6) ? vreg[kq].z : vreg[kq].w;
+        wv[kq] = (e & 1) ? (word >> 16) : (word & 0xFFFFu);
+      }
+      if constexpr (KPT == 4) {
+        *reinterpret_cast<uint2*>(dst) = make_uint2(wv[0] | (wv[1] << 16), wv[2] | (wv[3] << 16));
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = wv[0] | (wv[1] << 16);
+      }
+    }
+  };
+
+  // ---------------- selected keys ----------------
+  const int R = p.rcount[size_t(h) * a.Cq + i];
+  const int2* rg = p.ranges + (size_t(h) * a.Cq + i) * p.Rmax;
+  for (int c0 = 0; c0 < R; c0 += RCH) {
+    const int nrc = min(RCH, R - c0);
+    __syncthreads();
+    const int total = stage_ranges(rg, c0, nrc, S.rs, S.rp, S.wsum);
+    const int ntile = ceil_div(total, KT);
+    int cur_k = 0, cur_v = 0;
+    auto load_tile = [&](int tt) {
+      const int base = tt * KT;
+      {
+        const int pos = base + k_slot;
+        if (pos < total) {
+          const int row = cursor_row(S.rs, S.rp, nrc, pos, cur_k);
+          const uint4* src = reinterpret_cast<const uint4*>(kh + size_t(row) * D + k_c0);
+#pragma unroll
+          for (int q = 0; q < KCH / 8; ++q) kreg[q] = src[q];
+        } else {
+#pragma unroll
+          for (int q = 0; q < KCH / 8; ++q) kreg[q] = make_uint4(0, 0, 0, 0);
+        }
+      }
+      int cv = cur_v;
+#pragma unroll
+      for (int kq = 0; kq < KPT; ++kq) {
+        const int pos = base + v_kg * KPT + kq;
+        if (pos < total) {
+          const int row = cursor_row(S.rs, S.rp, nrc, pos, cv);
+          if (kq == 0) cur_v = cv;
+          vreg[kq] = *reinterpret_cast<const uint4*>(vh + size_t(row) * D + v_dg * 8);
+        } else {
+          vreg[kq] = make_uint4(0, 0, 0, 0);
+        }
+      }
+    };
+    if (ntile > 0) load_tile(0);
+    for (int tt = 0; tt < ntile; ++tt) {
+      const int buf = tt & 1;
+      store_tile(buf);
+      __syncthreads();
+      if (tt + 1 < ntile) load_tile(tt + 1);
+      floatx16 s[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+      qk(s, S.K[buf]);
+      softmax_pv(s, buf, total - tt * KT, nullptr);
+    }
+  }
+
+  // ---------------- compensation pseudo keys ----------------
+  if (a.compensate) {
+    const uint32_t* mr = a.mask + (size_t(h) * a.Cq + i) * p.W;
+    const bf16_t* kbh = p.kbh + size_t(h) * p.Ckp * D;
+    const bf16_t* kbl = p.kbl + size_t(h) * p.Ckp * D;
+    const bf16_t* vb = p.vb + size_t(h) * p.Ckp * D;
+    for (int j0 = 0; j0 < p.Ckp; j0 += KT) {
+      __syncthreads();
+      int fin = 0;
+      if (tid < KT) {
+        const int j = j0 + tid;
+        float b = -__builtin_huge_valf();
+        if (j < a.Ck && !((mr[j >> 5] >> (j & 31)) & 1u)) b = p.logsz[size_t(h) * p.Ckp + j];
+        S.bias[tid] = b * LOG2E;
+        fin = b != -__builtin_huge_valf();
+      }
+      if (!__syncthreads_or(fin)) continue;
+      {
+        const size_t ro = size_t(j0 + k_slot) * D + k_c0;
+#pragma unroll
+        for (int q = 0; q < KCH / 8; ++q) {
+          *reinterpret_cast<uint4*>(&S.K[0][k_slot][k_c0 + 8 * q]) =
+              reinterpret_cast<const uint4*>(kbh + ro)[q];
+          *reinterpret_cast<uint4*>(&S.K[1][k_slot][k_c0 + 8 * q]) =
+              reinterpret_cast<const uint4*>(kbl + ro)[q];
+        }
+#pragma unroll
+        for (int kq = 0; kq < KPT; ++kq)
+          vreg[kq] = *reinterpret_cast<const uint4*>(vb + size_t(j0 + v_kg * KPT + kq) * D + v_dg * 8);
+        // V^T store (reuses the tile transpose with buffer 0)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = v_dg * 8 + e;
+          bf16_t* dst = &S.V[0][c][v_kg * KPT];
+          uint32_t wv[KPT];
+#pragma unroll
+          for (int kq = 0; kq < KPT; ++kq) {
+            const uint32_t word = (e < 2) ? vreg[kq].x : (e < 4) ? vreg[kq].y : (e < 6) ? vreg[kq].z : vreg[kq].w;
+            wv[kq] = (e & 1) ? (word >> 16) : (word & 0xFFFFu);
+          }
+          if constexpr (KPT == 4) {
+            *reinterpret_cast<uint2*>(dst) = make_uint2(wv[0] | (wv[1] << 16), wv[2] | (wv[3] << 16));
+          } else {
+            *reinterpret_cast<uint32_t*>(dst) = wv[0] | (wv[1] << 16);
+          }
+        }
+      }
+      __syncthreads();
+      floatx16 s[2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+      qk(s, S.K[0]);
+      qk(s, S.K[1]);
+      softmax_pv(s, 0, KT, S.bias);
+    }
+  }
+
+  // ---------------- epilogue: normalise, stage, scatter to original rows ----
+  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+  const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  __syncthreads();
+  bf16_t (*Os)[D + 8] = reinterpret_cast<bf16_t (*)[D + 8]>(&S.K[0][0][0]);
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = 32 * dt + 8 * g + 4 * hi;
+      const uint2 v = make_uint2(pack2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv),
+                                 pack2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv));
+      *reinterpret_cast<uint2*>(&Os[qr][c]) = v;
+    }
+  __syncthreads();
+  const int32_t* qi = a.q_idx + size_t(h) * N + p0;
+  bf16_t* oh = (bf16_t*)a.o + size_t(h) * N * D;
+  for (int v = tid; v < TQ * DG; v += 256) {
+    const int r = v / DG, c = (v % DG) * 8;
+    if (r < nr)
+      *reinterpret_cast<uint4*>(oh + size_t(qi[r]) * D + c) = *reinterpret_cast<const uint4*>(&Os[r][c]);
+  }
+}
+
+Prep carve(const AttnArgs& a, Arena& s) {
+  Prep p{};
+  const int rows = a.tile_rows;
+  p.maxT = a.max_tiles > 0 ? a.max_tiles : a.N / rows + a.Cq + 1;
+  p.Rmax = a.Ck / 2 + 1;
+  p.Ckp = ceil_div(a.Ck, KT) * KT;
+  p.W = ceil_div(a.Ck, 32);
+  p.tiles = s.get<int4>(size_t(a.H) * p.maxT);
+  p.ntiles = s.get<int32_t>(size_t(a.H));
+  p.ranges = s.get<int2>(size_t(a.H) * a.Cq * p.Rmax);
+  p.rcount = s.get<int32_t>(size_t(a.H) * a.Cq);
+  if (a.compensate) {
+    p.logsz = s.get<float>(size_t(a.H) * p.Ckp);
+    if (a.dtype == SA_BF16) {
+      p.kbh = s.get<bf16_t>(size_t(a.H) * p.Ckp * a.d);
+      p.kbl = s.get<bf16_t>(size_t(a.H) * p.Ckp * a.d);
+      p.vb = s.get<bf16_t>(size_t(a.H) * p.Ckp * a.d);
+    } else {
+      p.kbf = s.get<float>(size_t(a.H) * p.Ckp * a.d);
+      p.vbf = s.get<float>(size_t(a.H) * p.Ckp * a.d);
+    }
+  }
+  return p;
+}
+
+}  // namespace
+
+size_t attn_scratch(int H, int N, int d, int Cq, int Ck, int tile_rows, int compensate, int dtype,
+                    int max_tiles) {
+  AttnArgs a{};
+  a.max_tiles = max_tiles;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.Cq = Cq;
+  a.Ck = Ck;
+  a.tile_rows = tile_rows;
+  a.compensate = compensate;
+  a.dtype = dtype;
+  Arena s{nullptr, 0, 0};
+  carve(a, s);
+  return s.used;
+}
+
+hipError_t attn_run(const AttnArgs& a, Arena& s, hipStream_t st) {
+  const Prep p = carve(a, s);
+  ranges_kernel<<<dim3(a.Cq, a.H), 64, 0, st>>>(a.mask, a.k_off, a.Cq, a.Ck, p.W, p.Rmax, p.ranges,
+                                                p.rcount);
+  tiles_kernel<<<a.H, 1024, 0, st>>>(a.q_off, a.Cq, a.tile_rows, p.maxT, p.tiles, p.ntiles);
+  if (a.compensate)
+    comp_prep_kernel<<<dim3(p.Ckp, a.H), 128, 0, st>>>(a.kbar, a.vbar, a.k_off, a.Ck, p.Ckp, a.d,
+                                                       p.kbh, p.kbl, p.vb, p.kbf, p.vbf, p.logsz);
+  const int grid = 8 * ceil_div(p.maxT * a.H, 8);
+  if (a.dtype == SA_BF16) {
+    const float sl2 = a.scale * LOG2E;
+    if (a.d == 128)
+      attn_mfma<128><<<grid, 256, 0, st>>>(a, p, sl2);
+    else
+      attn_mfma<64><<<grid, 256, 0, st>>>(a, p, sl2);
+  } else {
+    if (a.d == 128)
+      attn_simple<float, 128><<<grid, 128, 0, st>>>(a, p, a.scale);
+    else
+      attn_simple<float, 64><<<grid, 128, 0, st>>>(a, p, a.scale);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,259 @@
+// Counting-sort permutation into cluster order, row gather and cluster means.
+//
+// The permutation puts every cluster's tokens in one contiguous range
+// (ascending original index inside a cluster), so that a cluster is a dense
+// block of rows for block-sparse attention (ClusterAttention, English
+// abstract: cluster sizes chosen so block-sparse attention runs at dense
+// speed).  The sort is a stable LSD radix sort on 8-bit digits of the label;
+// every count is an integer, so the result is exact and deterministic.
+
+#include "sa_internal.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int SORT_CHUNK = 2048;  // elements per workgroup in the sort passes
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  return (uint64_t(1) << __lane_id()) - 1;
+}
+
+// per-chunk digit histogram -> chist[h][digit][chunk]
+__global__ __launch_bounds__(256) void sort_hist(const int32_t* __restrict__ keys, int N, int shift,
+                                                 int nchunks, int32_t* __restrict__ chist) {
+  __shared__ int hist[256];
+  const int h = blockIdx.y, chunk = blockIdx.x, t = threadIdx.x;
+  hist[t] = 0;
+  __syncthreads();
+  const int32_t* kh = keys + size_t(h) * N;
+  const int base = chunk * SORT_CHUNK;
+  for (int i = t; i < SORT_CHUNK; i += 256) {
+    int n = base + i;
+    if (n < N) atomicAdd(&hist[(kh[n] >> shift) & 255], 1);
+  }
+  __syncthreads();
+  chist[(size_t(h) * 256 + t) * nchunks + chunk] = hist[t];
+}
+
+// exclusive scan of len ints per head (one workgroup of 1024 threads per head)
+__global__ __launch_bounds__(1024) void scan_rows(const int32_t* __restrict__ in, int32_t* __restrict__ out,
+                                                  int len, int out_stride, bool write_total) {
+  __shared__ int wsum[16];
+  __shared__ int carry_s;
+  const int h = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int32_t* ih = in + size_t(h) * len;
+  int32_t* oh = out + size_t(h) * out_stride;
+  if (t == 0) carry_s = 0;
+  __syncthreads();
+  for (int b = 0; b < len; b += 1024) {
+    int i = b + t;
+    int v = i < len ? ih[i] : 0;
+    // inclusive wave scan
+    int x = v;
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(x, o, 64);
+      if (lane >= o) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int pre = carry_s;
+    for (int j = 0; j < w; ++j) pre += wsum[j];
+    if (i < len) oh[i] = pre + x - v;
+    __syncthreads();
+    if (t == 1023) carry_s = pre + x;
+    __syncthreads();
+  }
+  if (write_total && t == 0) oh[len] = carry_s;
+}
+
+// stable scatter of one radix pass
+__global__ __launch_bounds__(256) void sort_scatter(const int32_t* __restrict__ keys_in,
+                                                    const int32_t* __restrict__ vals_in,
+                                                    int32_t* __restrict__ keys_out,
+                                                    int32_t* __restrict__ vals_out, int N, int shift,
+                                                    int nchunks, const int32_t* __restrict__ cbase) {
+  __shared__ int run[256];
+  __shared__ int wc[4][256];
+  const int h = blockIdx.y, chunk = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  run[t] = cbase[(size_t(h) * 256 + t) * nchunks + chunk];
+  for (int j = 0; j < 4; ++j) wc[j][t] = 0;
+  __syncthreads();
+  const size_t hoff = size_t(h) * N;
+  const int base = chunk * SORT_CHUNK;
+  for (int r = 0; r < SORT_CHUNK; r += 256) {
+    const int n = base + r + t;
+    const bool valid = n < N;
+    const int key = valid ? keys_in[hoff + n] : 0;
+    const int val = valid ? (vals_in ? vals_in[hoff + n] : n) : 0;
+    const int dig = (key >> shift) & 255;
+    uint64_t m = __ballot(valid);
+    for (int b = 0; b < 8; ++b) {
+      uint64_t bal = __ballot(valid && ((dig >> b) & 1));
+      m &= ((dig >> b) & 1) ? bal : ~bal;
+    }
+    const int rank = __popcll(m & lanemask_lt());
+    if (valid && rank == 0) wc[w][dig] = __popcll(m);
+    __syncthreads();
+    if (valid) {
+      int pos = run[dig] + rank;
+      for (int j = 0; j < w; ++j) pos += wc[j][dig];
+      if (keys_out) keys_out[hoff + pos] = key;
+      vals_out[hoff + pos] = val;
+    }
+    __syncthreads();
+    run[t] += wc[0][t] + wc[1][t] + wc[2][t] + wc[3][t];
+    wc[0][t] = wc[1][t] = wc[2][t] = wc[3][t] = 0;
+    __syncthreads();
+  }
+}
+
+__global__ void fill_i32(int32_t* p, size_t n, int32_t v) {
+  size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ __launch_bounds__(256) void count_labels(const int32_t* __restrict__ labels, int N, int C,
+                                                    int32_t* __restrict__ cnt) {
+  const int h = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n < N) atomicAdd(&cnt[size_t(h) * C + labels[size_t(h) * N + n]], 1);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x, T* __restrict__ xp,
+                                                     const int32_t* __restrict__ perm, int N,
+                                                     int vec_per_row) {
+  // 16-byte vectors
+  const int h = blockIdx.y;
+  const size_t g = size_t(blockIdx.x) * 256 + threadIdx.x;
+  const size_t total = size_t(N) * vec_per_row;
+  if (g >= total) return;
+  const int p = int(g / vec_per_row), c = int(g % vec_per_row);
+  const int src = perm[size_t(h) * N + p];
+  const uint4* s = reinterpret_cast<const uint4*>(x) + (size_t(h) * N + src) * vec_per_row + c;
+  uint4* dst = reinterpret_cast<uint4*>(xp) + (size_t(h) * N + p) * vec_per_row + c;
+  *dst = *s;
+}
+
+// one workgroup per (cluster, head); 4 row groups x 64 lanes, fixed-order sums
+template <typename T>
+__global__ __launch_bounds__(256) void means_kernel(const T* __restrict__ x, int d, int col0, int dc,
+                                                    const int32_t* __restrict__ perm,
+                                                    const int32_t* __restrict__ off, int N, int C,
+                                                    float* __restrict__ out, int out_stride,
+                                                    bool keep_empty) {
+  __shared__ float part[4][128];
+  const int c = blockIdx.x, h = blockIdx.y, t = threadIdx.x, lane = t & 63, g = t >> 6;
+  const int a = off[size_t(h) * (C + 1) + c], b = off[size_t(h) * (C + 1) + c + 1];
+  float* o = out + (size_t(h) * C + c) * out_stride;
+  if (b == a) {
+    if (!keep_empty && g == 0)
+      for (int j = lane; j < dc; j += 64) o[j] = 0.f;
+    return;
+  }
+  float s0 = 0.f, s1 = 0.f;
+  const int32_t* ph = perm + size_t(h) * N;
+  for (int p = a + g; p < b; p += 4) {
+    const T* row = x + (size_t(h) * N + ph[p]) * d + col0;
+    if (lane < dc) s0 += to_f(row[lane]);
+    if (lane + 64 < dc) s1 += to_f(row[lane + 64]);
+  }
+  if (lane < dc) part[g][lane] = s0;
+  if (lane + 64 < dc) part[g][lane + 64] = s1;
+  __syncthreads();
+  if (t < dc) {
+    float s = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
+    o[t] = s / float(b - a);
+  }
+}
+
+__global__ __launch_bounds__(256) void labels_from_off_kernel(const int32_t* __restrict__ perm,
+                                                              const int32_t* __restrict__ off,
+                                                              int32_t* __restrict__ labels, int N,
+                                                              int C) {
+  const int c = blockIdx.x, h = blockIdx.y;
+  const int a = off[size_t(h) * (C + 1) + c], b = off[size_t(h) * (C + 1) + c + 1];
+  for (int p = a + threadIdx.x; p < b; p += 256)
+    labels[size_t(h) * N + perm[size_t(h) * N + p]] = c;
+}
+
+}  // namespace
+
+size_t label_sort_scratch(int H, int N, int C) {
+  const int nchunks = ceil_div(N, SORT_CHUNK);
+  Arena a{nullptr, 0, 0};
+  a.get<int32_t>(size_t(H) * 256 * nchunks);  // chist
+  a.get<int32_t>(size_t(H) * 256 * nchunks);  // cbase
+  a.get<int32_t>(size_t(H) * N);              // tmp keys
+  a.get<int32_t>(size_t(H) * N);              // tmp vals
+  a.get<int32_t>(size_t(H) * C);              // counts
+  return a.used;
+}
+
+hipError_t label_sort(const int32_t* labels, int32_t* perm, int32_t* offsets, int H, int N, int C,
+                      Arena& s, hipStream_t st) {
+  const int nchunks = ceil_div(N, SORT_CHUNK);
+  int32_t* chist = s.get<int32_t>(size_t(H) * 256 * nchunks);
+  int32_t* cbase = s.get<int32_t>(size_t(H) * 256 * nchunks);
+  int32_t* tk = s.get<int32_t>(size_t(H) * N);
+  int32_t* tv = s.get<int32_t>(size_t(H) * N);
+  int32_t* cnt = s.get<int32_t>(size_t(H) * C);
+  const int passes = C <= 256 ? 1 : (C <= 65536 ? 2 : 0);
+  if (!passes) return hipErrorInvalidValue;
+  dim3 g(nchunks, H);
+  for (int ps = 0; ps < passes; ++ps) {
+    const int shift = 8 * ps;
+    const int32_t* kin = ps == 0 ? labels : tk;
+    const int32_t* vin = ps == 0 ? nullptr : tv;
+    const bool last = ps == passes - 1;
+    sort_hist<<<g, 256, 0, st>>>(kin, N, shift, nchunks, chist);
+    scan_rows<<<H, 1024, 0, st>>>(chist, cbase, 256 * nchunks, 256 * nchunks, false);
+    // pass 0 of 2 writes to tmp, the last pass writes perm (keys not needed)
+    if (passes == 2 && ps == 0) {
+      sort_scatter<<<g, 256, 0, st>>>(kin, vin, tk, tv, N, shift, nchunks, cbase);
+    } else {
+      // in-place hazard: pass 1 reads tk/tv and writes perm only
+      sort_scatter<<<g, 256, 0, st>>>(kin, vin, nullptr, perm, N, shift, nchunks, cbase);
+    }
+    (void)last;
+  }
+  // offsets from label counts
+  size_t nc = size_t(H) * C;
+  fill_i32<<<ceil_div(int(nc), 256), 256, 0, st>>>(cnt, nc, 0);
+  count_labels<<<dim3(ceil_div(N, 256), H), 256, 0, st>>>(labels, N, C, cnt);
+  scan_rows<<<H, 1024, 0, st>>>(cnt, offsets, C, C + 1, true);
+  return hipGetLastError();
+}
+
+hipError_t gather_rows(const void* x, void* x_perm, const int32_t* perm, int H, int N, int d,
+                       int dtype, hipStream_t st) {
+  const int esz = dtype == SA_F32 ? 4 : 2;
+  const int vpr = d * esz / 16;
+  const size_t total = size_t(N) * vpr;
+  dim3 g(unsigned((total + 255) / 256), H);
+  gather_kernel<uint4><<<g, 256, 0, st>>>(reinterpret_cast<const uint4*>(x),
+                                          reinterpret_cast<uint4*>(x_perm), perm, N, vpr);
+  return hipGetLastError();
+}
+
+hipError_t cluster_means(const void* x, int dtype, int d, int col0, int dc, const int32_t* perm,
+                         const int32_t* offsets, int H, int N, int C, float* out, int out_stride,
+                         bool keep_empty, hipStream_t st) {
+  dim3 g(C, H);
+  if (dtype == SA_F32)
+    means_kernel<float><<<g, 256, 0, st>>>((const float*)x, d, col0, dc, perm, offsets, N, C, out,
+                                           out_stride, keep_empty);
+  else
+    means_kernel<bf16_t><<<g, 256, 0, st>>>((const bf16_t*)x, d, col0, dc, perm, offsets, N, C, out,
+                                            out_stride, keep_empty);
+  return hipGetLastError();
+}
+
+hipError_t labels_from_offsets(const int32_t* perm, const int32_t* offsets, int32_t* labels, int H,
+                               int N, int C, hipStream_t st) {
+  labels_from_off_kernel<<<dim3(C, H), 256, 0, st>>>(perm, offsets, labels, N, C);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,435 @@
+// C ABI of libsa: argument validation, workspace planning and the launch
+// sequence of each entry point.  Nothing here computes on the host beyond
+// sizes; every step of the method runs in the kernels of k_*.hip.
+
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "sa_internal.h"
+
+using namespace sa;
+
+namespace {
+
+constexpr int KMEANS_MAX = 1024;
+constexpr int SUB_MAX = 32;
+constexpr int SELECT_MAX = 1024;
+constexpr int TILE_MAX = 128;
+
+int esize(int dtype) { return dtype == SA_F32 ? 4 : 2; }
+
+sa_status check_problem(const sa_problem* p) {
+  if (!p) return SA_ERR_INVALID_ARG;
+  if (p->dtype != SA_F32 && p->dtype != SA_BF16) return SA_ERR_DTYPE;
+  if (p->heads < 1 || p->n < 1 || p->frames < 1 || p->height < 1 || p->width < 1)
+    return SA_ERR_SHAPE;
+  if (int64_t(p->frames) * p->height * p->width != p->n) return SA_ERR_SHAPE;
+  if (p->d != 64 && p->d != 128) return SA_ERR_SHAPE;
+  if (p->n > (1 << 24) || int64_t(p->heads) * p->n > (int64_t(1) << 31)) return SA_ERR_SHAPE;
+  return SA_OK;
+}
+
+int clusters_of(const sa_problem* p, const sa_cluster_cfg* c) {
+  switch (c->method) {
+    case SA_KMEANS: return c->clusters;
+    case SA_BISECT: return c->leaf >= 1 ? ceil_div(p->n, c->leaf) : -1;
+    case SA_SUBSPACE: return c->clusters * c->clusters * c->clusters;
+    default: return -1;
+  }
+}
+
+int centroid_rows(const sa_problem* p, const sa_cluster_cfg* c) {
+  return c->method == SA_SUBSPACE ? 3 * c->clusters : clusters_of(p, c);
+}
+
+sa_status check_cluster_cfg(const sa_problem* p, const sa_cluster_cfg* c) {
+  if (!c) return SA_ERR_INVALID_ARG;
+  if (c->iters < 1 || c->iters > 1000) return SA_ERR_INVALID_ARG;
+  if (c->tile_cap < 0) return SA_ERR_INVALID_ARG;
+  if (c->init != SA_INIT_FIRST && c->init != SA_INIT_GIVEN) return SA_ERR_INVALID_ARG;
+  switch (c->method) {
+    case SA_KMEANS:
+      if (c->clusters < 1 || c->clusters > KMEANS_MAX) return SA_ERR_INVALID_ARG;
+      if (c->clusters > p->n) return SA_ERR_SHAPE;
+      return SA_OK;
+    case SA_BISECT:
+      if (c->leaf < 2) return SA_ERR_INVALID_ARG;
+      if (c->init != SA_INIT_FIRST) return SA_ERR_INVALID_ARG;
+      if (ceil_div(p->n, c->leaf) > 65536) return SA_ERR_SHAPE;
+      return SA_OK;
+    case SA_SUBSPACE: {
+      if (c->clusters < 1 || c->clusters > SUB_MAX) return SA_ERR_INVALID_ARG;
+      if (c->clusters > p->n) return SA_ERR_SHAPE;
+      if (c->init != SA_INIT_FIRST) return SA_ERR_INVALID_ARG;
+      int sum = 0;
+      for (int s = 0; s < 3; ++s) {
+        if (!kmeans_width_supported(c->sub_dims[s])) return SA_ERR_UNSUPPORTED;
+        sum += c->sub_dims[s];
+      }
+      if (sum != p->d) return SA_ERR_SHAPE;
+      return SA_OK;
+    }
+    default: return SA_ERR_INVALID_ARG;
+  }
+}
+
+sa_status check_select_cfg(const sa_select_cfg* c) {
+  if (!c) return SA_ERR_INVALID_ARG;
+  if (!isfinite(c->top_p)) return SA_ERR_INVALID_ARG;
+  if (c->top_p <= 0.f && c->topk_floor <= 0) return SA_ERR_INVALID_ARG;
+  return SA_OK;
+}
+
+int tile_rows(const sa_cluster_cfg* q) {
+  const int cap = q->tile_cap > 0 ? q->tile_cap : TILE_MAX;
+  return std::min(cap, TILE_MAX);
+}
+
+int max_tiles(const sa_problem* p, const sa_cluster_cfg* q) {
+  const int rows = tile_rows(q);
+  const int C = clusters_of(p, q);
+  if (q->method == SA_BISECT) return C * ceil_div(q->leaf, rows);
+  return p->n / rows + C + 1;
+}
+
+// scratch (transient) bytes of each component
+size_t cluster_scratch(const sa_problem* p, const sa_cluster_cfg* c) {
+  const int H = p->heads, N = p->n;
+  switch (c->method) {
+    case SA_KMEANS: return label_sort_scratch(H, N, c->clusters) + 256;
+    case SA_BISECT: return bisect_scratch(H, N, p->d, c->leaf) + 256;
+    case SA_SUBSPACE: {
+      Arena a{nullptr, 0, 0};
+      a.get<int32_t>(size_t(3) * H * N);  // slice labels
+      size_t comp = 0;
+      for (int s = 0; s < 3; ++s) comp += size_t(H) * c->clusters * c->sub_dims[s];
+      a.get<float>(comp);                  // compact slice centroids
+      a.get<int32_t>(size_t(H) * N);       // slice perm
+      a.get<int32_t>(size_t(H) * (c->clusters + 1));
+      return a.used + std::max(label_sort_scratch(H, N, c->clusters),
+                               label_sort_scratch(H, N, clusters_of(p, c))) + 256;
+    }
+  }
+  return 0;
+}
+
+struct Plan {
+  size_t total;
+};
+
+// carve the persistent buffers of sa_forward; null base = size only
+struct FwdBufs {
+  sa_clusters q, k;
+  void* v_perm;
+  float* v_means;
+  int32_t* counts;
+  int32_t* head_topk;
+  char* scratch;
+  size_t scratch_bytes;
+};
+
+FwdBufs carve_forward(const sa_problem* p, const sa_cluster_cfg* qc, const sa_cluster_cfg* kc,
+                      const sa_attn_cfg* ac, char* base, size_t* used) {
+  const int H = p->heads, N = p->n, d = p->d;
+  const int Cq = clusters_of(p, qc), Ck = clusters_of(p, kc);
+  Arena a{base, 0, 0};
+  FwdBufs b{};
+  auto fill = [&](sa_clusters& c, const sa_cluster_cfg* cfg, int C) {
+    c.labels = a.get<int32_t>(size_t(H) * N);
+    c.perm = a.get<int32_t>(size_t(H) * N);
+    c.offsets = a.get<int32_t>(size_t(H) * (C + 1));
+    c.centroids = a.get<float>(size_t(H) * centroid_rows(p, cfg) * d);
+    c.x_perm = a.take(size_t(H) * N * d * esize(p->dtype));
+  };
+  fill(b.q, qc, Cq);
+  fill(b.k, kc, Ck);
+  b.v_perm = a.take(size_t(H) * N * d * esize(p->dtype));
+  b.v_means = (ac && ac->compensate) ? a.get<float>(size_t(H) * Ck * d) : nullptr;
+  b.counts = a.get<int32_t>(size_t(H) * Cq);
+  b.head_topk = a.get<int32_t>(size_t(H));
+  const size_t fixed = a.used;
+  size_t scr = std::max(cluster_scratch(p, qc), cluster_scratch(p, kc));
+  scr = std::max(scr, select_scratch(H, Cq, Ck, kc->method == SA_SUBSPACE) + 256);
+  scr = std::max(scr, attn_scratch(H, N, d, Cq, Ck, tile_rows(qc), ac ? ac->compensate : 0,
+                                   p->dtype, max_tiles(p, qc)) + 256);
+  b.scratch = base ? base + fixed : nullptr;
+  b.scratch_bytes = scr;
+  *used = fixed + scr;
+  return b;
+}
+
+sa_status hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
+
+// ---------------------------------------------------------------------------
+// component implementations (arguments already validated)
+// ---------------------------------------------------------------------------
+sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x, sa_clusters* out,
+                     Arena& s, hipStream_t st) {
+  const int H = p->heads, N = p->n, d = p->d, dt = p->dtype;
+  const int C = clusters_of(p, c);
+  hipError_t e = hipSuccess;
+  out->num_clusters = C;
+  out->method = c->method;
+  out->sub_clusters = c->method == SA_SUBSPACE ? c->clusters : 0;
+  for (int k = 0; k < 3; ++k) out->sub_dims[k] = c->method == SA_SUBSPACE ? c->sub_dims[k] : 0;
+  if (c->method == SA_KMEANS) {
+    if (c->init == SA_INIT_FIRST) e = kmeans_seed(x, dt, d, 0, d, H, N, C, out->centroids, st);
+    for (int it = 0; it < c->iters && e == hipSuccess; ++it) {
+      Arena tmp = s;
+      e = kmeans_assign(x, dt, d, 0, d, H, N, C, out->centroids, out->labels, st);
+      if (e == hipSuccess) e = label_sort(out->labels, out->perm, out->offsets, H, N, C, tmp, st);
+      if (e == hipSuccess)
+        e = cluster_means(x, dt, d, 0, d, out->perm, out->offsets, H, N, C, out->centroids, d, true, st);
+    }
+  } else if (c->method == SA_BISECT) {
+    Arena tmp = s;
+    e = bisect_run(x, dt, H, N, d, c->leaf, c->iters, out->perm, out->offsets, tmp, st);
+    if (e == hipSuccess) e = labels_from_offsets(out->perm, out->offsets, out->labels, H, N, C, st);
+    if (e == hipSuccess)
+      e = cluster_means(x, dt, d, 0, d, out->perm, out->offsets, H, N, C, out->centroids, d, false, st);
+  } else {
+    const int Cs = c->clusters;
+    Arena tmp = s;
+    int32_t* sub_labels = tmp.get<int32_t>(size_t(3) * H * N);
+    size_t comp = 0;
+    for (int k = 0; k < 3; ++k) comp += size_t(H) * Cs * c->sub_dims[k];
+    float* sub_c = tmp.get<float>(comp);
+    int32_t* sperm = tmp.get<int32_t>(size_t(H) * N);
+    int32_t* soff = tmp.get<int32_t>(size_t(H) * (Cs + 1));
+    size_t coff = 0;
+    int col0 = 0;
+    for (int k = 0; k < 3 && e == hipSuccess; ++k) {
+      const int ds = c->sub_dims[k];
+      float* cs = sub_c + coff;
+      int32_t* lab = sub_labels + size_t(k) * H * N;
+      e = kmeans_seed(x, dt, d, col0, ds, H, N, Cs, cs, st);
+      for (int it = 0; it < c->iters && e == hipSuccess; ++it) {
+        Arena t2 = tmp;
+        e = kmeans_assign(x, dt, d, col0, ds, H, N, Cs, cs, lab, st);
+        if (e == hipSuccess) e = label_sort(lab, sperm, soff, H, N, Cs, t2, st);
+        if (e == hipSuccess)
+          e = cluster_means(x, dt, d, col0, ds, sperm, soff, H, N, Cs, cs, ds, true, st);
+      }
+      coff += size_t(H) * Cs * ds;
+      col0 += ds;
+    }
+    if (e == hipSuccess) e = combo_labels(sub_labels, out->labels, H, N, Cs, st);
+    if (e == hipSuccess) {
+      Arena t2 = tmp;
+      e = label_sort(out->labels, out->perm, out->offsets, H, N, C, t2, st);
+    }
+    if (e == hipSuccess) e = expand_sub_centroids(sub_c, H, Cs, d, c->sub_dims, out->centroids, st);
+  }
+  if (e == hipSuccess) e = gather_rows(x, out->x_perm, out->perm, H, N, d, dt, st);
+  return hip_status(e);
+}
+
+sa_status do_select(const sa_problem* p, const sa_select_cfg* c, const sa_clusters* q,
+                    const sa_clusters* k, uint32_t* mask, int32_t* counts, int32_t* init_counts,
+                    int32_t* head_topk, Arena& s, hipStream_t st) {
+  SelectArgs a{};
+  a.H = p->heads;
+  a.N = p->n;
+  a.d = p->d;
+  a.Cq = q->num_clusters;
+  a.Ck = k->num_clusters;
+  a.q_off = q->offsets;
+  a.qbar = q->centroids;
+  a.k_off = k->offsets;
+  a.kbar = k->centroids;
+  a.subspace = k->method == SA_SUBSPACE;
+  a.Cs = k->sub_clusters;
+  for (int i = 0; i < 3; ++i) a.dims[i] = k->sub_dims[i];
+  a.scale = 1.0 / sqrt(double(p->d));
+  a.top_p = c->top_p;
+  a.floor_units = c->topk_floor;
+  a.online = c->online_topk != 0;
+  a.weighted = c->size_weighted != 0;
+  a.mask = mask;
+  a.counts = counts;
+  a.init_counts = init_counts;
+  a.head_topk = head_topk;
+  Arena tmp = s;
+  return hip_status(select_run(a, tmp, st));
+}
+
+sa_status do_attn(const sa_problem* p, const sa_attn_cfg* c, const sa_clusters* q,
+                  const sa_clusters* k, const void* v_perm, const float* v_means,
+                  const uint32_t* mask, void* o, int rows, int maxt, Arena& s, hipStream_t st) {
+  AttnArgs a{};
+  a.H = p->heads;
+  a.N = p->n;
+  a.d = p->d;
+  a.Cq = q->num_clusters;
+  a.Ck = k->num_clusters;
+  a.dtype = p->dtype;
+  a.tile_rows = rows;
+  a.max_tiles = maxt;
+  a.compensate = c->compensate != 0;
+  a.scale = c->scale > 0.f ? c->scale : float(1.0 / sqrt(double(p->d)));
+  a.q_perm = q->x_perm;
+  a.q_idx = q->perm;
+  a.q_off = q->offsets;
+  a.k_perm = k->x_perm;
+  a.k_off = k->offsets;
+  a.kbar = k->centroids;
+  a.v_perm = v_perm;
+  a.vbar = v_means;
+  a.mask = mask;
+  a.o = o;
+  Arena tmp = s;
+  return hip_status(attn_run(a, tmp, st));
+}
+
+bool clusters_ok(const sa_clusters* c, bool need_xperm) {
+  return c && c->perm && c->offsets && c->centroids && (!need_xperm || c->x_perm) &&
+         c->num_clusters >= 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+SA_API int32_t sa_num_clusters(const sa_problem* p, const sa_cluster_cfg* cfg) {
+  if (check_problem(p) != SA_OK || check_cluster_cfg(p, cfg) != SA_OK) return -1;
+  return clusters_of(p, cfg);
+}
+
+SA_API sa_status sa_workspace_size(const sa_problem* p, const sa_cluster_cfg* qcfg,
+                                   const sa_cluster_cfg* kcfg, const sa_select_cfg* scfg,
+                                   const sa_attn_cfg* acfg, size_t* bytes) {
+  (void)scfg;
+  if (!bytes) return SA_ERR_INVALID_ARG;
+  sa_status st = check_problem(p);
+  if (st != SA_OK) return st;
+  if (qcfg && (st = check_cluster_cfg(p, qcfg)) != SA_OK) return st;
+  if (kcfg && (st = check_cluster_cfg(p, kcfg)) != SA_OK) return st;
+  if (qcfg && kcfg) {
+    size_t used = 0;
+    carve_forward(p, qcfg, kcfg, acfg, nullptr, &used);
+    *bytes = used + 256;
+    return SA_OK;
+  }
+  size_t b = 256;
+  if (qcfg) b = std::max(b, cluster_scratch(p, qcfg));
+  if (kcfg) b = std::max(b, cluster_scratch(p, kcfg));
+  *bytes = b + 256;
+  return SA_OK;
+}
+
+SA_API sa_status sa_cluster(const sa_problem* p, const sa_cluster_cfg* cfg, const void* x,
+                            sa_clusters* out, void* ws, size_t ws_bytes, void* stream) {
+  sa_status st = check_problem(p);
+  if (st != SA_OK) return st;
+  if ((st = check_cluster_cfg(p, cfg)) != SA_OK) return st;
+  if (!x || !out || !out->labels || !out->perm || !out->offsets || !out->centroids || !out->x_perm)
+    return SA_ERR_INVALID_ARG;
+  if (!ws) return SA_ERR_INVALID_ARG;
+  if (ws_bytes < cluster_scratch(p, cfg)) return SA_ERR_WORKSPACE;
+  Arena s{(char*)ws, ws_bytes, 0};
+  return do_cluster(p, cfg, x, out, s, (hipStream_t)stream);
+}
+
+SA_API sa_status sa_permute(const sa_problem* p, const sa_clusters* c, const void* x, void* x_perm,
+                            float* means, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  sa_status st = check_problem(p);
+  if (st != SA_OK) return st;
+  if (!clusters_ok(c, false) || !x || !x_perm) return SA_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = gather_rows(x, x_perm, c->perm, p->heads, p->n, p->d, p->dtype, s);
+  if (e == hipSuccess && means)
+    e = cluster_means(x, p->dtype, p->d, 0, p->d, c->perm, c->offsets, p->heads, p->n,
+                      c->num_clusters, means, p->d, false, s);
+  return hip_status(e);
+}
+
+SA_API sa_status sa_select(const sa_problem* p, const sa_select_cfg* cfg, const sa_clusters* q,
+                           const sa_clusters* k, uint32_t* mask, int32_t* counts,
+                           int32_t* init_counts, int32_t* head_topk, void* ws, size_t ws_bytes,
+                           void* stream) {
+  sa_status st = check_problem(p);
+  if (st != SA_OK) return st;
+  if ((st = check_select_cfg(cfg)) != SA_OK) return st;
+  if (!clusters_ok(q, false) || !clusters_ok(k, false) || !mask || !counts || !head_topk || !ws)
+    return SA_ERR_INVALID_ARG;
+  if (k->method == SA_SUBSPACE) return SA_ERR_UNSUPPORTED;
+  if (k->num_clusters > SELECT_MAX) return SA_ERR_UNSUPPORTED;
+  if (ws_bytes < select_scratch(p->heads, q->num_clusters, k->num_clusters, 0) + 256)
+    return SA_ERR_WORKSPACE;
+  Arena s{(char*)ws, ws_bytes, 0};
+  return do_select(p, cfg, q, k, mask, counts, init_counts, head_topk, s, (hipStream_t)stream);
+}
+
+SA_API sa_status sa_block_sparse_attn(const sa_problem* p, const sa_attn_cfg* cfg,
+                                      const sa_clusters* q, const sa_clusters* k,
+                                      const void* v_perm, const float* v_means,
+                                      const uint32_t* mask, void* o, void* ws, size_t ws_bytes,
+                                      void* stream) {
+  sa_status st = check_problem(p);
+  if (st != SA_OK) return st;
+  if (!cfg || !clusters_ok(q, true) || !clusters_ok(k, true) || !v_perm || !mask || !o || !ws)
+    return SA_ERR_INVALID_ARG;
+  if (!(cfg->scale >= 0.f) || !isfinite(cfg->scale)) return SA_ERR_INVALID_ARG;
+  if (cfg->compensate && !v_means) return SA_ERR_INVALID_ARG;
+  if (cfg->compensate && k->method == SA_SUBSPACE) return SA_ERR_UNSUPPORTED;
+  const int rows = TILE_MAX;
+  const int maxt = p->n / rows + q->num_clusters + 1;
+  const size_t need = attn_scratch(p->heads, p->n, p->d, q->num_clusters, k->num_clusters, rows,
+                                   cfg->compensate, p->dtype, maxt) + 256;
+  if (ws_bytes < need) return SA_ERR_WORKSPACE;
+  Arena s{(char*)ws, ws_bytes, 0};
+  return do_attn(p, cfg, q, k, v_perm, v_means, mask, o, rows, maxt, s, (hipStream_t)stream);
+}
+
+SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
+                            const sa_cluster_cfg* kcfg, const sa_select_cfg* scfg,
+                            const sa_attn_cfg* acfg, const void* q, const void* k, const void* v,
+                            void* o, uint32_t* mask, void* ws, size_t ws_bytes, void* stream) {
+  sa_status st = check_problem(p);
+  if (st != SA_OK) return st;
+  if ((st = check_cluster_cfg(p, qcfg)) != SA_OK) return st;
+  if ((st = check_cluster_cfg(p, kcfg)) != SA_OK) return st;
+  if ((st = check_select_cfg(scfg)) != SA_OK) return st;
+  if (!acfg || !q || !k || !v || !o || !mask || !ws) return SA_ERR_INVALID_ARG;
+  if (!(acfg->scale >= 0.f) || !isfinite(acfg->scale)) return SA_ERR_INVALID_ARG;
+  if (qcfg->method == SA_SUBSPACE) return SA_ERR_INVALID_ARG;
+  if (qcfg->init != SA_INIT_FIRST || kcfg->init != SA_INIT_FIRST) return SA_ERR_INVALID_ARG;
+  if (kcfg->method == SA_SUBSPACE) return SA_ERR_UNSUPPORTED;
+  if (clusters_of(p, kcfg) > SELECT_MAX) return SA_ERR_UNSUPPORTED;
+  size_t used = 0;
+  carve_forward(p, qcfg, kcfg, acfg, nullptr, &used);
+  if (ws_bytes < used) return SA_ERR_WORKSPACE;
+  FwdBufs b = carve_forward(p, qcfg, kcfg, acfg, (char*)ws, &used);
+  hipStream_t s = (hipStream_t)stream;
+  Arena scr{b.scratch, b.scratch_bytes, 0};
+  if ((st = do_cluster(p, qcfg, q, &b.q, scr, s)) != SA_OK) return st;
+  if ((st = do_cluster(p, kcfg, k, &b.k, scr, s)) != SA_OK) return st;
+  hipError_t e = gather_rows(v, b.v_perm, b.k.perm, p->heads, p->n, p->d, p->dtype, s);
+  if (e == hipSuccess && b.v_means)
+    e = cluster_means(v, p->dtype, p->d, 0, p->d, b.k.perm, b.k.offsets, p->heads, p->n,
+                      b.k.num_clusters, b.v_means, p->d, false, s);
+  if (e != hipSuccess) return SA_ERR_HIP;
+  if ((st = do_select(p, scfg, &b.q, &b.k, mask, b.counts, nullptr, b.head_topk, scr, s)) != SA_OK)
+    return st;
+  return do_attn(p, acfg, &b.q, &b.k, b.v_perm, b.v_means, mask, o, tile_rows(qcfg),
+                 max_tiles(p, qcfg), scr, s);
+}
+
+SA_API const char* sa_status_string(sa_status s) {
+  switch (s) {
+    case SA_OK: return "ok";
+    case SA_ERR_INVALID_ARG: return "invalid argument";
+    case SA_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case SA_ERR_DTYPE: return "unsupported dtype";
+    case SA_ERR_WORKSPACE: return "workspace too small";
+    case SA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SA_ERR_HIP: return "HIP launch failure";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

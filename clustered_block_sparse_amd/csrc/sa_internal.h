@@ -1,0 +1,152 @@
+// Internal declarations shared by the libsa HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/sa.h"
+
+namespace sa {
+
+typedef uint16_t bf16_t;
+
+// ---------------------------------------------------------------------------
+// scalar helpers
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+__device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// round-to-nearest-even float -> bf16 (finite inputs)
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return bf16_t(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+
+// order-preserving map of a float to uint32 (+0 and -0 map to the same key)
+__device__ __forceinline__ uint32_t sortable(float f) {
+  f = f + 0.0f;  // -0 -> +0
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// wave64 reductions
+__device__ __forceinline__ float wave_sum(float v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// bump allocator over a caller workspace
+struct Arena {
+  char* base;
+  size_t size;
+  size_t used;
+  __host__ void* take(size_t bytes) {
+    size_t off = (used + 255) & ~size_t(255);
+    used = off + ((bytes + 255) & ~size_t(255));
+    return base ? (void*)(base + off) : nullptr;
+  }
+  template <typename T> __host__ T* get(size_t count) { return (T*)take(count * sizeof(T)); }
+};
+
+// ---------------------------------------------------------------------------
+// launchers (host functions, one translation unit each)
+// ---------------------------------------------------------------------------
+
+// k_permute.hip --------------------------------------------------------------
+// Stable counting sort of labels[h][n] in [0, C): perm (original indices in
+// (label, index) order) and offsets [H][C+1].
+size_t label_sort_scratch(int H, int N, int C);
+hipError_t label_sort(const int32_t* labels, int32_t* perm, int32_t* offsets, int H, int N, int C,
+                      Arena& scratch, hipStream_t st);
+
+// x_perm[h][p][:] = x[h][perm[h][p]][:]
+hipError_t gather_rows(const void* x, void* x_perm, const int32_t* perm, int H, int N, int d,
+                       int dtype, hipStream_t st);
+
+// Member means of columns [col0, col0+dc) of x rows per cluster, fp32, written
+// to out[h][c][0..dc) with row stride out_stride.  Empty clusters: keep the
+// existing value if keep_empty, else zeros.
+hipError_t cluster_means(const void* x, int dtype, int d, int col0, int dc, const int32_t* perm,
+                         const int32_t* offsets, int H, int N, int C, float* out, int out_stride,
+                         bool keep_empty, hipStream_t st);
+
+// labels[h][perm[h][p]] = cluster of position p, from offsets
+hipError_t labels_from_offsets(const int32_t* perm, const int32_t* offsets, int32_t* labels, int H,
+                               int N, int C, hipStream_t st);
+
+// k_kmeans.hip ---------------------------------------------------------------
+// c[h][j][0..dc) = x[h][j][col0..col0+dc) for j < C (first-k seeding)
+hipError_t kmeans_seed(const void* x, int dtype, int d, int col0, int dc, int H, int N, int C,
+                       float* c, hipStream_t st);
+// labels[h][n] = argmin_j sum_t (x[h][n][col0+t] - c[h][j][t])^2, ties -> smallest j
+hipError_t kmeans_assign(const void* x, int dtype, int d, int col0, int dc, int H, int N, int C,
+                         const float* c, int32_t* labels, hipStream_t st);
+bool kmeans_width_supported(int dc);
+// labels = (a_t*Cs + a_h)*Cs + a_w
+hipError_t combo_labels(const int32_t* sub_labels, int32_t* labels, int H, int N, int Cs,
+                        hipStream_t st);
+// centroids [H][3*Cs][d]: row s*Cs+c = slice s centroid in its columns, zeros elsewhere
+hipError_t expand_sub_centroids(const float* sub, int H, int Cs, int d, const int* dims,
+                                float* out, hipStream_t st);
+
+// k_bisect.hip ---------------------------------------------------------------
+size_t bisect_scratch(int H, int N, int d, int leaf);
+hipError_t bisect_run(const void* x, int dtype, int H, int N, int d, int leaf, int iters,
+                      int32_t* perm_out, int32_t* offsets_out, Arena& scratch, hipStream_t st);
+
+// k_select.hip ---------------------------------------------------------------
+struct SelectArgs {
+  int H, N, d, Cq, Ck;
+  const int32_t* q_off;   // [H][Cq+1]
+  const float* qbar;      // [H][Cq][d]
+  const int32_t* k_off;   // [H][Ck+1]
+  const float* kbar;      // [H][Ck][d] or [H][3*Cs][d] (subspace)
+  int subspace, Cs;
+  int dims[3];
+  double scale;
+  double top_p;
+  int floor_units, online, weighted;
+  uint32_t* mask;         // [H][Cq][W]
+  int32_t* counts;        // [H][Cq]
+  int32_t* init_counts;   // [H][Cq] or null
+  int32_t* head_topk;     // [H]
+};
+size_t select_scratch(int H, int Cq, int Ck, int subspace);
+hipError_t select_run(const SelectArgs& a, Arena& scratch, hipStream_t st);
+
+// k_attn.hip -----------------------------------------------------------------
+struct AttnArgs {
+  int H, N, d, Cq, Ck, dtype, tile_rows, compensate;
+  int max_tiles;          // upper bound on query tiles per head (0 = derive)
+  float scale;
+  const void* q_perm;     // [H][N][d] queries in query-cluster order
+  const int32_t* q_idx;   // [H][N] original index of query position
+  const int32_t* q_off;   // [H][Cq+1]
+  const void* k_perm;     // [H][N][d]
+  const int32_t* k_off;   // [H][Ck+1]
+  const float* kbar;      // [H][Ck][d] (compensation)
+  const void* v_perm;     // [H][N][d]
+  const float* vbar;      // [H][Ck][d] (compensation)
+  const uint32_t* mask;   // [H][Cq][W]
+  void* o;                // [H][N][d] original order
+};
+size_t attn_scratch(int H, int N, int d, int Cq, int Ck, int tile_rows, int compensate, int dtype,
+                    int max_tiles);
+hipError_t attn_run(const AttnArgs& a, Arena& scratch, hipStream_t st);
+
+}  // namespace sa

@@ -1,0 +1,205 @@
+/*
+ * sa.h - C ABI of libsa, clustered block-sparse attention on MI355X (gfx950).
+ *
+ * The operation (per attention head) is the training-free sparse attention
+ * described by
+ *   [SCOPE]  "SCOPE: Subspace Clustering with Online Per-Head Top-K Estimation
+ *            for Sparse Video Attention" (arXiv 2608.12780): English abstract,
+ *            technical framework and key design sections;
+ *   [CA]     "ClusterAttention: A training-free speedup of bidirectional
+ *            attention" (arXiv 2608.26965): English and Chinese abstracts.
+ * Post-RoPE queries and keys are clustered and permuted into contiguous
+ * cluster order; centroid proxy scores drive a hybrid Top-p / minimum Top-k
+ * choice of key clusters for every query cluster, with SCOPE's online per-head
+ * Top-k; attention then runs over the selected original keys/values only,
+ * optionally compensating each excluded key cluster through its mean [CA].
+ *
+ * Conventions for every entry point:
+ *  - Tensors are row-major [heads, n, d] with token n = (t*height + h)*width + w.
+ *  - All tensor pointers are DEVICE pointers, allocated and owned by the
+ *    caller.  The library never allocates, frees or retains a pointer after a
+ *    call returns.  Inputs are never modified.
+ *  - Scratch memory is one caller-provided device workspace of at least
+ *    sa_workspace_size() bytes (256-byte aligned).
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues kernels on it: no device->host copy, no synchronisation.
+ *    Calls on distinct workspaces are reentrant.
+ *  - Arguments are validated before anything is enqueued: a call that
+ *    returns an error has done no work.  SA_ERR_HIP reports a launch failure
+ *    (hipGetLastError after a launch).  No C++ exception crosses the ABI.
+ *  - Results are deterministic: identical inputs give bit-identical outputs
+ *    (no floating-point atomics anywhere).
+ */
+#ifndef SA_H_
+#define SA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define SA_API __attribute__((visibility("default")))
+#else
+#define SA_API
+#endif
+
+typedef enum sa_status {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARG = 1, /* null pointer, bad config value */
+  SA_ERR_SHAPE = 2,       /* n != frames*height*width, unsupported d, too many clusters */
+  SA_ERR_DTYPE = 3,       /* dtype not SA_F32 / SA_BF16 */
+  SA_ERR_WORKSPACE = 4,   /* workspace smaller than sa_workspace_size() */
+  SA_ERR_UNSUPPORTED = 5, /* valid but not implemented combination */
+  SA_ERR_HIP = 6          /* a kernel launch failed */
+} sa_status;
+
+enum { SA_F32 = 0, SA_BF16 = 1 };
+
+/* Clustering methods.
+ * SA_KMEANS:   Lloyd k-means, `clusters` centroids seeded with the first
+ *              `clusters` tokens (or caller centroids), `iters` rounds of
+ *              assignment + update.
+ * SA_BISECT:   balanced recursive 2-means down to leaves of `leaf` tokens
+ *              (all leaves full except the last) [CA: recursive clustering,
+ *              power-of-two cluster sizes].  C = ceil(n / leaf).
+ * SA_SUBSPACE: keys only [SCOPE]: the t/h/w RoPE column slices (`sub_dims`)
+ *              are k-means clustered independently with `clusters` centroids
+ *              each; a key's cluster is its combo
+ *              g = (a_t*clusters + a_h)*clusters + a_w, C = clusters^3. */
+enum { SA_KMEANS = 0, SA_BISECT = 1, SA_SUBSPACE = 2 };
+enum { SA_INIT_FIRST = 0, SA_INIT_GIVEN = 1 };
+
+typedef struct sa_problem {
+  int32_t heads, n, d;            /* d in {64, 128}                                 */
+  int32_t frames, height, width;  /* n == frames*height*width; (1,1,n) unstructured */
+  int32_t dtype;                  /* SA_F32 or SA_BF16 (Q, K, V and O)              */
+} sa_problem;
+
+typedef struct sa_cluster_cfg {
+  int32_t method;      /* SA_KMEANS | SA_BISECT | SA_SUBSPACE                       */
+  int32_t clusters;    /* KMEANS: C (1..1024, <= n); SUBSPACE: per-slice C (<= 32)  */
+  int32_t leaf;        /* BISECT leaf size (>= 2)                                   */
+  int32_t tile_cap;    /* upper bound on query rows per attention tile (tiling
+                          only, never changes results; 0 = 128)                    */
+  int32_t iters;       /* rounds per k-means run / per bisection node (>= 1)        */
+  int32_t init;        /* KMEANS: SA_INIT_FIRST, or SA_INIT_GIVEN = start from the
+                          centroids already in out->centroids                      */
+  int32_t sub_dims[3]; /* SUBSPACE column widths (t, h, w), summing to d            */
+} sa_cluster_cfg;
+
+typedef struct sa_select_cfg {
+  float top_p;          /* cumulative proxy mass to reach (>= 1: all non-empty) */
+  int32_t topk_floor;   /* fixed Top-k minimum in units (clusters; keys in
+                           SUBSPACE mode); top_p <= 0 with floor <= 0 is invalid */
+  int32_t online_topk;  /* SCOPE online per-head Top-k on/off                    */
+  int32_t size_weighted;/* 1: proxy logits add ln|K_j| (softmax over per-key
+                           scores); 0: plain centroid softmax                    */
+} sa_select_cfg;
+
+typedef struct sa_attn_cfg {
+  int32_t compensate;  /* mean compensation of excluded key clusters [CA] */
+  float scale;         /* score scale; 0 = 1/sqrt(d)                      */
+} sa_attn_cfg;
+
+/* Clustering of one tensor (Q or K).  Every pointer is caller-owned device
+ * memory, written by sa_cluster and read by sa_select/sa_block_sparse_attn.
+ *   labels    int32 [H, n]      cluster of each token (original order)
+ *   perm      int32 [H, n]      perm[h][p] = original token at cluster-order
+ *                               position p (ascending inside a cluster)
+ *   offsets   int32 [H, C+1]    cluster c occupies positions [off[c], off[c+1])
+ *   centroids f32   [H, Cc, d]  KMEANS/BISECT: Cc = C member means (an empty
+ *                               k-means cluster keeps its previous centroid);
+ *                               SUBSPACE: Cc = 3*clusters slice centroids, row
+ *                               s*clusters+c holds slice s in its own columns
+ *                               and zeros elsewhere
+ *   x_perm    dtype [H, n, d]   rows of x in cluster order
+ * num_clusters, method, sub_clusters and sub_dims are filled by sa_cluster. */
+typedef struct sa_clusters {
+  int32_t* labels;
+  int32_t* perm;
+  int32_t* offsets;
+  float* centroids;
+  void* x_perm;
+  int32_t num_clusters;
+  int32_t method;
+  int32_t sub_clusters;
+  int32_t sub_dims[3];
+} sa_clusters;
+
+/* Number of clusters C a configuration produces (BISECT: ceil(n/leaf);
+ * SUBSPACE: clusters^3), or -1 for an invalid configuration. */
+SA_API int32_t sa_num_clusters(const sa_problem* p, const sa_cluster_cfg* cfg);
+
+/* Workspace bytes sufficient for sa_forward with these configurations and
+ * for each component call (sa_cluster with qcfg or kcfg, sa_select,
+ * sa_permute, sa_block_sparse_attn) on the same problem.  Any cfg may be NULL
+ * only if the matching component is never called with that workspace. */
+SA_API sa_status sa_workspace_size(const sa_problem* p, const sa_cluster_cfg* qcfg,
+                                   const sa_cluster_cfg* kcfg, const sa_select_cfg* scfg,
+                                   const sa_attn_cfg* acfg, size_t* bytes);
+
+/* Cluster x [H, n, d] per head with `cfg` and permute it into cluster order
+ * [SCOPE technical framework: clustering of post-RoPE keys; CA: recursive
+ * power-of-two clustering].  Fills every field of *out. */
+SA_API sa_status sa_cluster(const sa_problem* p, const sa_cluster_cfg* cfg, const void* x,
+                            sa_clusters* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Gather rows of x [H, n, d] into the cluster order of `c` (x_perm) and, if
+ * `means` is not NULL, write the member mean of every cluster to means
+ * f32 [H, C, d] (zeros for an empty cluster).  Used for V. */
+SA_API sa_status sa_permute(const sa_problem* p, const sa_clusters* c, const void* x,
+                            void* x_perm, float* means, void* ws, size_t ws_bytes, void* stream);
+
+/* Hybrid Top-p / fixed Top-k selection with SCOPE's online per-head Top-k.
+ * For each query cluster i: logits l_ij = <qbar_i, kbar_j>*scale (+ ln|K_j|),
+ * p_ij = softmax_j over non-empty key units, ranking by (p desc, j asc); the
+ * initial prefix is the shortest reaching mass >= top_p and count >= floor
+ * (n_i units); with online Top-k, k_h = ceil(sum_i |Q_i| n_i / n) and rows
+ * with n_i < k_h extend along the same ranking to k_h units.  SUBSPACE keys
+ * use SCOPE's lookup-table scores over combos (units = keys).
+ *   mask        uint32 [H, Cq, ceil(Ck/32)]  bit j of row (h,i), LSB first
+ *   counts      int32  [H, Cq]  final selected units
+ *   init_counts int32  [H, Cq]  initial units n_i (may be NULL)
+ *   head_topk   int32  [H]      k_h (0 when online Top-k is off)
+ * `scale` of the proxy scores is 1/sqrt(d). */
+SA_API sa_status sa_select(const sa_problem* p, const sa_select_cfg* cfg, const sa_clusters* q,
+                           const sa_clusters* k, uint32_t* mask, int32_t* counts,
+                           int32_t* init_counts, int32_t* head_topk, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Block-sparse attention [SCOPE: attention over the selected original keys
+ * and values; CA: block-sparse attention over power-of-two clusters, mean
+ * compensation].  For a query token n of query cluster i:
+ *   O_n = [sum_{m in sel} e^{s_nm} v_m + c sum_{j excl} |K_j| e^{<q_n,kbar_j>s} vbar_j]
+ *       / [sum_{m in sel} e^{s_nm}     + c sum_{j excl} |K_j| e^{<q_n,kbar_j>s}]
+ * with s_nm = <q_n, k_m>*scale, sel = keys of the key clusters set in mask row
+ * i, excl = non-empty key clusters not set, c = cfg->compensate.
+ *   v_perm  dtype [H, n, d]  V rows in the key cluster order of k
+ *   v_means f32 [H, Ck, d]   member means of V per key cluster (compensation
+ *                            only; NULL otherwise)
+ *   o       dtype [H, n, d]  output in ORIGINAL token order
+ * Compensation is not supported for SUBSPACE keys (SA_ERR_UNSUPPORTED). */
+SA_API sa_status sa_block_sparse_attn(const sa_problem* p, const sa_attn_cfg* cfg,
+                                      const sa_clusters* q, const sa_clusters* k,
+                                      const void* v_perm, const float* v_means,
+                                      const uint32_t* mask, void* o, void* ws, size_t ws_bytes,
+                                      void* stream);
+
+/* The whole path: cluster Q and K, permute V, select, attend.
+ * o dtype [H, n, d] original order; mask as in sa_select. */
+SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
+                            const sa_cluster_cfg* kcfg, const sa_select_cfg* scfg,
+                            const sa_attn_cfg* acfg, const void* q, const void* k,
+                            const void* v, void* o, uint32_t* mask, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* Static description of a status code. */
+SA_API const char* sa_status_string(sa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SA_H_ */

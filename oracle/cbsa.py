@@ -332,6 +332,9 @@ def select(logits, units, qsizes, top_p, floor, online_topk):
          extend their prefix along the same ranking until the count reaches
          k_h (capped at every non-empty unit); other rows are unchanged.
 
+    An empty query cluster (|Q_i| = 0) has no query to serve: it selects
+    nothing and counts 0 (reading; it does not enter k_h either way).
+
     Returns a dict with mask [Cq, Ck] bool, n_init, n_final, k_h, prefix
     lengths, and per-row near-tie flags (boundary mass within 1e-5 of top_p,
     or a relative logit gap <= 1e-5 at a cut)."""
@@ -368,7 +371,7 @@ def select(logits, units, qsizes, top_p, floor, online_topk):
                 if 1 <= t <= len(cm) and abs(cm[t - 1] - top_p) <= NEAR_TIE_REL:
                     near[i] = True
         tf = _first_reaching(cu, floor) if floor > 0 else 0
-        t = max(tp, tf)
+        t = max(tp, tf) if qsizes[i] > 0 else 0
         t_init[i] = t
         n_init[i] = cu[t - 1] if t > 0 else 0
         orders.append(order)
@@ -384,7 +387,7 @@ def select(logits, units, qsizes, top_p, floor, online_topk):
         k_h = 0
     t_final = t_init.copy()
     for i in range(Cq):
-        if online_topk and n_init[i] < k_h:
+        if online_topk and n_init[i] < k_h and qsizes[i] > 0:
             t_final[i] = max(t_init[i], _first_reaching(cum_units[i], k_h))
     mask = np.zeros((Cq, Ck), dtype=bool)
     n_final = np.zeros(Cq, dtype=np.int64)

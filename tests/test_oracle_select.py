@@ -68,6 +68,13 @@ def test_top_p_edges():
     assert m.sum() == 3 and not m[0, 2]
 
 
+def test_empty_query_cluster_selects_nothing():
+    logits = np.log(np.array([[0.5, 0.3, 0.2], [0.2, 0.3, 0.5]]))
+    r = oracle.select(logits, np.ones(3, np.int64), [0, 7], 0.6, 1, True)
+    assert r["mask"][0].sum() == 0 and r["n_final"][0] == 0
+    assert r["mask"][1].tolist() == [False, True, True] and r["k_h"] == 2
+
+
 def test_ties_rank_lower_index_first():
     logits = np.zeros((1, 5))
     r = oracle.select(logits, np.ones(5, np.int64), [1], 0.39, 0, False)
