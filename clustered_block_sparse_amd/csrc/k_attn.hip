@@ -27,6 +27,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -47,13 +49,15 @@ struct Prep {
   int32_t* ntiles;    // [H]
   int2* ranges;       // [H][Cq][Rmax] {start, end}
   int32_t* rcount;    // [H][Cq]
-  bf16_t* kbh;        // [H][Ckp][D]
-  bf16_t* kbl;        // [H][Ckp][D]
-  bf16_t* vb;         // [H][Ckp][D]
+  int32_t* raligned;  // [H][Cq] 1 if every range starts at a multiple of 64 and ends at one or at N
+  bf16_t* vt;         // [H][NB][D][64] V^T per 64-key block (bf16 path)
+  bf16_t* kbh;        // [H][Ckp][D]  kbar, bf16 high part
+  bf16_t* kbl;        // [H][Ckp][D]  kbar - high, bf16
+  bf16_t* vbt;        // [H][Ckp/64][D][64] vbar^T per 64-cluster block
   float* logsz;       // [H][Ckp]  ln|K_j| or -inf for empty
   float* kbf;         // fp32 path: [H][Ckp][D]
   float* vbf;         // fp32 path: [H][Ckp][D]
-  int maxT, Rmax, Ckp, W;
+  int maxT, Rmax, Ckp, W, NB;
 };
 
 // --------------------------------------------------------------------------
@@ -61,14 +65,16 @@ struct Prep {
 // --------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void ranges_kernel(const uint32_t* __restrict__ mask,
                                                     const int32_t* __restrict__ k_off, int Cq,
-                                                    int Ck, int W, int Rmax,
+                                                    int Ck, int W, int Rmax, int N,
                                                     int2* __restrict__ ranges,
-                                                    int32_t* __restrict__ rcount) {
+                                                    int32_t* __restrict__ rcount,
+                                                    int32_t* __restrict__ raligned) {
   const int i = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   const uint32_t* mr = mask + (size_t(h) * Cq + i) * W;
   const int32_t* ko = k_off + size_t(h) * (Ck + 1);
   int2* out = ranges + (size_t(h) * Cq + i) * Rmax;
   int ns = 0, ne = 0;
+  bool misaligned = false;
   const uint64_t lt = (uint64_t(1) << lane) - 1;
   for (int j0 = 0; j0 < Ck; j0 += 64) {
     const int j = j0 + lane;
@@ -79,12 +85,22 @@ __global__ __launch_bounds__(64) void ranges_kernel(const uint32_t* __restrict__
     const bool st = sel && !selp;
     const bool en = sel && !seln;
     const uint64_t bs = __ballot(st), be = __ballot(en);
-    if (st) out[ns + __popcll(bs & lt)].x = ko[j];
-    if (en) out[ne + __popcll(be & lt)].y = ko[j + 1];
+    if (st) {
+      out[ns + __popcll(bs & lt)].x = ko[j];
+      misaligned |= (ko[j] & (KT - 1)) != 0;
+    }
+    if (en) {
+      out[ne + __popcll(be & lt)].y = ko[j + 1];
+      misaligned |= (ko[j + 1] & (KT - 1)) != 0 && ko[j + 1] != N;
+    }
     ns += __popcll(bs);
     ne += __popcll(be);
   }
-  if (lane == 0) rcount[size_t(h) * Cq + i] = ns;
+  const bool any_mis = __ballot(misaligned) != 0;
+  if (lane == 0) {
+    rcount[size_t(h) * Cq + i] = ns;
+    raligned[size_t(h) * Cq + i] = any_mis ? 0 : 1;
+  }
 }
 
 __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__ q_off, int Cq,
@@ -124,7 +140,7 @@ __global__ __launch_bounds__(128) void comp_prep_kernel(const float* __restrict_
                                                         const float* __restrict__ vbar,
                                                         const int32_t* __restrict__ k_off, int Ck,
                                                         int Ckp, int D, bf16_t* kbh, bf16_t* kbl,
-                                                        bf16_t* vb, float* kbf, float* vbf,
+                                                        bf16_t* vbt, float* kbf, float* vbf,
                                                         float* logsz) {
   const int j = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   const size_t o = (size_t(h) * Ckp + j) * D;
@@ -138,7 +154,7 @@ __global__ __launch_bounds__(128) void comp_prep_kernel(const float* __restrict_
       const bf16_t hi = f2bf(kv);
       kbh[o + c] = hi;
       kbl[o + c] = f2bf(kv - bf2f(hi));
-      vb[o + c] = f2bf(vv);
+      vbt[((size_t(h) * (Ckp / KT) + j / KT) * D + c) * KT + (j % KT)] = f2bf(vv);
     }
     if (kbf) {
       kbf[o + c] = kv;
@@ -312,14 +328,20 @@ __global__ __launch_bounds__(128) void attn_simple(AttnArgs a, Prep p, float sca
 // --------------------------------------------------------------------------
 // bf16 MFMA path
 // --------------------------------------------------------------------------
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ floatx16 mfma32(bf16x8_t a, bf16x8_t b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8_t as_bf8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
+// two floats -> packed bf16 pair (hardware round-to-nearest-even)
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
-  return uint32_t(f2bf(a)) | (uint32_t(f2bf(b)) << 16);
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 template <int D>
@@ -332,14 +354,45 @@ struct MfmaLds {
   float bias[KT];
 };
 
+// V^T in 64-key blocks: vt[h][b][c][k] = v_perm[h][64 b + k][c] (zero past N)
 template <int D>
-__global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float scale_log2) {
+__global__ __launch_bounds__(256) void vt_kernel(const bf16_t* __restrict__ v, int N, int NB,
+                                                 bf16_t* __restrict__ vt) {
+  __shared__ bf16_t tile[KT][D + 8];
+  const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  for (int c = t; c < KT * CPR; c += 256) {
+    const int r = c / CPR, cc = c % CPR;
+    const int pos = b * KT + r;
+    uint4 u = make_uint4(0, 0, 0, 0);
+    if (pos < N) u = *reinterpret_cast<const uint4*>(v + (size_t(h) * N + pos) * D + cc * 8);
+    *reinterpret_cast<uint4*>(&tile[r][cc * 8]) = u;
+  }
+  __syncthreads();
+  bf16_t* dst = vt + (size_t(h) * NB + b) * D * KT;
+  for (int c = t; c < D * (KT / 8); c += 256) {
+    const int d = c / (KT / 8), kc = c % (KT / 8);
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = uint32_t(tile[kc * 8 + 2 * e][d]) | (uint32_t(tile[kc * 8 + 2 * e + 1][d]) << 16);
+    *reinterpret_cast<uint4*>(dst + size_t(d) * KT + kc * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// ALIGNED: rows whose ranges are 64-aligned stream whole 64-key blocks (K rows
+// and pre-transposed V^T are plain 16-byte copies); the other instantiation
+// gathers rows of arbitrary ranges and transposes V while staging it.  Each
+// workgroup runs in the instantiation matching its row and exits in the other.
+template <int D, bool ALIGNED>
+__global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sl2) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int DS = D / 16;         // MFMA k-steps over d
   constexpr int DT = D / 32;         // 32-row tiles of d in O^T
-  constexpr int KCH = D / 4;         // K elements per thread (one row, quarter)
-  constexpr int KPT = D / 32;        // V keys per thread
-  constexpr int DG = D / 8;          // V 8-column groups
+  constexpr int KCH = D / 4;         // general path: K elements per thread (one row quarter)
+  constexpr int KPT = D / 32;        // general path: V keys per thread
+  constexpr int DG = D / 8;          // 8-column groups of a row
+  constexpr int CK = KT * D / 8 / 256;  // aligned path: 16-byte chunks per thread (K and V^T each)
   __shared__ __attribute__((aligned(16))) MfmaLds<D> S;
 
   int h, tix;
@@ -347,6 +400,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sc
   if (h >= a.H || tix >= p.ntiles[h]) return;
   const int4 td = p.tiles[size_t(h) * p.maxT + tix];
   const int i = td.x, p0 = td.y, nr = td.z;
+  if ((p.raligned[size_t(h) * a.Cq + i] != 0) != ALIGNED) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int col = lane & 31, hi = lane >> 5;
   const int N = a.N;
@@ -372,33 +426,30 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sc
   float lsum = 0.f;                   // this lane's share of the denominator
 
   const bf16_t* kh = (const bf16_t*)a.k_perm + size_t(h) * N * D;
-  const bf16_t* vh = (const bf16_t*)a.v_perm + size_t(h) * N * D;
 
-  // loader roles
-  const int k_slot = tid >> 2, k_c0 = (tid & 3) * KCH;     // K: one row quarter
-  const int v_dg = tid % DG, v_kg = tid / DG;              // V: KPT keys x 8 columns
+  auto qk = [&](floatx16 (&s)[2], const bf16_t (*Kb)[D + 8]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+      for (int st = 0; st < DS; ++st) {
+        const uint4 u = *reinterpret_cast<const uint4*>(&Kb[32 * kt + col][16 * st + 8 * hi]);
+        s[kt] = mfma32(as_bf8(u), qf[st], s[kt]);
+      }
+    }
+  };
 
-  uint4 kreg[KCH / 8];
-  uint4 vreg[KPT];
-
-  // online-softmax update + P V for one tile whose S^T is in s[0..1]
-  auto softmax_pv = [&](floatx16 (&s)[2], int buf, int nvalid, const float* bias_l2) {
+  // Online-softmax update and P V for one tile whose S^T holds log2-domain
+  // logits (-inf for masked keys).
+  auto softmax_pv = [&](floatx16 (&s)[2], int vbuf) {
     float mx = -__builtin_huge_valf();
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
-        float x = s[kt][r] * scale_log2;
-        if (bias_l2) x += bias_l2[key];
-        if (key >= nvalid) x = -__builtin_huge_valf();
-        s[kt][r] = x;
-        mx = fmaxf(mx, x);
-      }
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     float alpha = 1.f;
     if (mx > m + 8.f) {
-      alpha = exp2f(m - mx);  // m = -inf -> 0
+      alpha = __builtin_amdgcn_exp2f(m - mx);  // m = -inf -> 0
       m = mx;
     }
     if (__ballot(alpha != 1.f)) {
@@ -413,112 +464,185 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sc
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        const float x0 = s[kt][r], x1 = s[kt][r + 1];
-        const float e0 = (x0 == -__builtin_huge_valf()) ? 0.f : exp2f(x0 - m);
-        const float e1 = (x1 == -__builtin_huge_valf()) ? 0.f : exp2f(x1 - m);
+        // every tile holds a valid key, so m is finite here and -inf maps to 0
+        const float e0 = __builtin_amdgcn_exp2f(s[kt][r] - m);
+        const float e1 = __builtin_amdgcn_exp2f(s[kt][r + 1] - m);
         lsum += e0 + e1;
         pk[kt][r >> 1] = pack2(e0, e1);
       }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int kt = ks >> 1, half = ks & 1;
-      const uint4 pu = make_uint4(pk[kt][4 * half + 0], pk[kt][4 * half + 1], pk[kt][4 * half + 2],
-                                  pk[kt][4 * half + 3]);
-      const bf16x8_t pf = as_bf8(pu);
+      const bf16x8_t pf = as_bf8(make_uint4(pk[kt][4 * half + 0], pk[kt][4 * half + 1],
+                                            pk[kt][4 * half + 2], pk[kt][4 * half + 3]));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const bf16_t* vr = &S.V[buf][32 * dt + col][16 * ks + 4 * hi];
+        const bf16_t* vr = &S.V[vbuf][32 * dt + col][16 * ks + 4 * hi];
         const uint2 lo = *reinterpret_cast<const uint2*>(vr);
         const uint2 up = *reinterpret_cast<const uint2*>(vr + 8);
-        const bf16x8_t vf = as_bf8(make_uint4(lo.x, lo.y, up.x, up.y));
-        oacc[dt] = mfma32(vf, pf, oacc[dt]);
+        oacc[dt] = mfma32(as_bf8(make_uint4(lo.x, lo.y, up.x, up.y)), pf, oacc[dt]);
       }
     }
   };
 
-  auto qk = [&](floatx16 (&s)[2], const bf16_t (*Kb)[D + 8]) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int st = 0; st < DS; ++st) {
-        const uint4 u = *reinterpret_cast<const uint4*>(&Kb[32 * kt + col][16 * st + 8 * hi]);
-        s[kt] = mfma32(as_bf8(u), qf[st], s[kt]);
-      }
-    }
-  };
-
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < KCH / 8; ++q)
-      *reinterpret_cast<uint4*>(&S.K[buf][k_slot][k_c0 + 8 * q]) = kreg[q];
-    // transpose KPT keys x 8 columns into V^T
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int c = v_dg * 8 + e;
-      bf16_t* dst = &S.V[buf][c][v_kg * KPT];
-      uint32_t wv[KPT];
-#pragma unroll
-      for (int kq = 0; kq < KPT; ++kq) {
-        const uint32_t word = (e < 2) ? vreg[kq].x : (e < 4) ? vreg[kq].y : (e < 6) ? vreg[kq].z : vreg[kq].w;
-        wv[kq] = (e & 1) ? (word >> 16) : (word & 0xFFFFu);
-      }
-      if constexpr (KPT == 4) {
-        *reinterpret_cast<uint2*>(dst) = make_uint2(wv[0] | (wv[1] << 16), wv[2] | (wv[3] << 16));
-      } else {
-        *reinterpret_cast<uint32_t*>(dst) = wv[0] | (wv[1] << 16);
-      }
-    }
-  };
-
-  // ---------------- selected keys ----------------
-  const int R = p.rcount[size_t(h) * a.Cq + i];
-  const int2* rg = p.ranges + (size_t(h) * a.Cq + i) * p.Rmax;
-  for (int c0 = 0; c0 < R; c0 += RCH) {
-    const int nrc = min(RCH, R - c0);
-    __syncthreads();
-    const int total = stage_ranges(rg, c0, nrc, S.rs, S.rp, S.wsum);
-    const int ntile = ceil_div(total, KT);
-    int cur_k = 0, cur_v = 0;
-    auto load_tile = [&](int tt) {
-      const int base = tt * KT;
-      {
-        const int pos = base + k_slot;
-        if (pos < total) {
-          const int row = cursor_row(S.rs, S.rp, nrc, pos, cur_k);
-          const uint4* src = reinterpret_cast<const uint4*>(kh + size_t(row) * D + k_c0);
-#pragma unroll
-          for (int q = 0; q < KCH / 8; ++q) kreg[q] = src[q];
-        } else {
-#pragma unroll
-          for (int q = 0; q < KCH / 8; ++q) kreg[q] = make_uint4(0, 0, 0, 0);
-        }
-      }
-      int cv = cur_v;
-#pragma unroll
-      for (int kq = 0; kq < KPT; ++kq) {
-        const int pos = base + v_kg * KPT + kq;
-        if (pos < total) {
-          const int row = cursor_row(S.rs, S.rp, nrc, pos, cv);
-          if (kq == 0) cur_v = cv;
-          vreg[kq] = *reinterpret_cast<const uint4*>(vh + size_t(row) * D + v_dg * 8);
-        } else {
-          vreg[kq] = make_uint4(0, 0, 0, 0);
-        }
-      }
-    };
-    if (ntile > 0) load_tile(0);
-    for (int tt = 0; tt < ntile; ++tt) {
-      const int buf = tt & 1;
-      store_tile(buf);
-      __syncthreads();
-      if (tt + 1 < ntile) load_tile(tt + 1);
-      floatx16 s[2];
+  // scores -> log2-domain logits in place (bias per key, keys >= nvalid masked)
+  auto to_logits = [&](floatx16 (&s)[2], int nvalid, const float* bias_l2) {
+    if (nvalid >= KT && !bias_l2) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-      qk(s, S.K[buf]);
-      softmax_pv(s, buf, total - tt * KT, nullptr);
+        for (int r = 0; r < 16; ++r) s[kt][r] *= sl2;
+      return;
+    }
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
+        float x = s[kt][r] * sl2;
+        if (bias_l2) x += bias_l2[key];
+        if (key >= nvalid) x = -__builtin_huge_valf();
+        s[kt][r] = x;
+      }
+  };
+
+  auto compute_tile = [&](int kbuf, int vbuf, int nvalid) {
+    floatx16 s[2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
+    qk(s, S.K[kbuf]);
+    to_logits(s, nvalid, nullptr);
+    softmax_pv(s, vbuf);
+  };
+
+  // V^T chunk -> LDS (row stride KT+4 is 8-byte aligned: two 8-byte stores)
+  auto store_vt_chunk = [&](int buf, int c, uint4 u) {
+    const int d = c >> 3, kc = c & 7;
+    bf16_t* dst = &S.V[buf][d][kc * 8];
+    *reinterpret_cast<uint2*>(dst) = make_uint2(u.x, u.y);
+    *reinterpret_cast<uint2*>(dst + 4) = make_uint2(u.z, u.w);
+  };
+
+  const int R = p.rcount[size_t(h) * a.Cq + i];
+  const int2* rg = p.ranges + (size_t(h) * a.Cq + i) * p.Rmax;
+
+  if constexpr (ALIGNED) {
+    // ---------------- selected keys, 64-aligned ranges: whole-block tiles ----
+    const bf16_t* vth = p.vt + size_t(h) * p.NB * D * KT;
+    uint4 kreg[CK], vreg[CK];
+    int ri = 0, pos = R > 0 ? rg[0].x : 0, rend = R > 0 ? rg[0].y : 0;
+    auto load = [&](int pos0, int nvalid) {
+#pragma unroll
+      for (int q = 0; q < CK; ++q) {
+        const int c = tid + 256 * q;
+        const int row = c / DG, cc = c % DG;
+        kreg[q] = row < nvalid ? *reinterpret_cast<const uint4*>(kh + size_t(pos0 + row) * D + cc * 8)
+                               : make_uint4(0, 0, 0, 0);
+        vreg[q] = *reinterpret_cast<const uint4*>(vth + size_t(pos0 / KT) * D * KT + size_t(c) * 8);
+      }
+    };
+    auto store = [&](int buf) {
+#pragma unroll
+      for (int q = 0; q < CK; ++q) {
+        const int c = tid + 256 * q;
+        *reinterpret_cast<uint4*>(&S.K[buf][c / DG][(c % DG) * 8]) = kreg[q];
+        store_vt_chunk(buf, c, vreg[q]);
+      }
+    };
+    if (ri < R) load(pos, min(KT, rend - pos));
+    int tt = 0;
+    while (ri < R) {
+      const int nvalid = min(KT, rend - pos);
+      const int buf = tt & 1;
+      // buf last held tile tt-2, whose compute every wave finished before the
+      // barrier of iteration tt-1
+      store(buf);
+      __syncthreads();
+      // advance to the next tile and prefetch it
+      pos += KT;
+      if (pos >= rend) {
+        ++ri;
+        if (ri < R) {
+          const int2 r2 = rg[ri];
+          pos = r2.x;
+          rend = r2.y;
+        }
+      }
+      if (ri < R) load(pos, min(KT, rend - pos));
+      compute_tile(buf, buf, nvalid);
+      ++tt;
+    }
+  } else {
+    // ---------------- selected keys, general ranges: row gather --------------
+    const bf16_t* vh = (const bf16_t*)a.v_perm + size_t(h) * N * D;
+    const int k_slot = tid >> 2, k_c0 = (tid & 3) * KCH;  // K: one row quarter
+    const int v_dg = tid % DG, v_kg = tid / DG;           // V: KPT keys x 8 columns
+    uint4 kreg[KCH / 8];
+    uint4 vreg[KPT];
+    auto store_tile = [&](int buf) {
+#pragma unroll
+      for (int q = 0; q < KCH / 8; ++q)
+        *reinterpret_cast<uint4*>(&S.K[buf][k_slot][k_c0 + 8 * q]) = kreg[q];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = v_dg * 8 + e;
+        bf16_t* dst = &S.V[buf][c][v_kg * KPT];
+        uint32_t wv[KPT];
+#pragma unroll
+        for (int kq = 0; kq < KPT; ++kq) {
+          const uint32_t word = (e < 2) ? vreg[kq].x : (e < 4) ? vreg[kq].y : (e < 6) ? vreg[kq].z : vreg[kq].w;
+          wv[kq] = (e & 1) ? (word >> 16) : (word & 0xFFFFu);
+        }
+        if constexpr (KPT == 4) {
+          *reinterpret_cast<uint2*>(dst) = make_uint2(wv[0] | (wv[1] << 16), wv[2] | (wv[3] << 16));
+        } else {
+          *reinterpret_cast<uint32_t*>(dst) = wv[0] | (wv[1] << 16);
+        }
+      }
+    };
+    for (int c0 = 0; c0 < R; c0 += RCH) {
+      const int nrc = min(RCH, R - c0);
+      __syncthreads();
+      const int total = stage_ranges(rg, c0, nrc, S.rs, S.rp, S.wsum);
+      const int ntile = ceil_div(total, KT);
+      int cur_k = 0, cur_v = 0;
+      auto load_tile = [&](int tt) {
+        const int base = tt * KT;
+        {
+          const int pos = base + k_slot;
+          if (pos < total) {
+            const int row = cursor_row(S.rs, S.rp, nrc, pos, cur_k);
+            const uint4* src = reinterpret_cast<const uint4*>(kh + size_t(row) * D + k_c0);
+#pragma unroll
+            for (int q = 0; q < KCH / 8; ++q) kreg[q] = src[q];
+          } else {
+#pragma unroll
+            for (int q = 0; q < KCH / 8; ++q) kreg[q] = make_uint4(0, 0, 0, 0);
+          }
+        }
+        int cv = cur_v;
+#pragma unroll
+        for (int kq = 0; kq < KPT; ++kq) {
+          const int pos = base + v_kg * KPT + kq;
+          if (pos < total) {
+            const int row = cursor_row(S.rs, S.rp, nrc, pos, cv);
+            if (kq == 0) cur_v = cv;
+            vreg[kq] = *reinterpret_cast<const uint4*>(vh + size_t(row) * D + v_dg * 8);
+          } else {
+            vreg[kq] = make_uint4(0, 0, 0, 0);
+          }
+        }
+      };
+      if (ntile > 0) load_tile(0);
+      for (int tt = 0; tt < ntile; ++tt) {
+        const int buf = tt & 1;
+        store_tile(buf);
+        __syncthreads();
+        if (tt + 1 < ntile) load_tile(tt + 1);
+        compute_tile(buf, buf, total - tt * KT);
+      }
     }
   }
 
@@ -527,7 +651,7 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sc
     const uint32_t* mr = a.mask + (size_t(h) * a.Cq + i) * p.W;
     const bf16_t* kbh = p.kbh + size_t(h) * p.Ckp * D;
     const bf16_t* kbl = p.kbl + size_t(h) * p.Ckp * D;
-    const bf16_t* vb = p.vb + size_t(h) * p.Ckp * D;
+    const bf16_t* vbt = p.vbt + size_t(h) * p.Ckp * D;
     for (int j0 = 0; j0 < p.Ckp; j0 += KT) {
       __syncthreads();
       int fin = 0;
@@ -539,35 +663,13 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sc
         fin = b != -__builtin_huge_valf();
       }
       if (!__syncthreads_or(fin)) continue;
-      {
-        const size_t ro = size_t(j0 + k_slot) * D + k_c0;
 #pragma unroll
-        for (int q = 0; q < KCH / 8; ++q) {
-          *reinterpret_cast<uint4*>(&S.K[0][k_slot][k_c0 + 8 * q]) =
-              reinterpret_cast<const uint4*>(kbh + ro)[q];
-          *reinterpret_cast<uint4*>(&S.K[1][k_slot][k_c0 + 8 * q]) =
-              reinterpret_cast<const uint4*>(kbl + ro)[q];
-        }
-#pragma unroll
-        for (int kq = 0; kq < KPT; ++kq)
-          vreg[kq] = *reinterpret_cast<const uint4*>(vb + size_t(j0 + v_kg * KPT + kq) * D + v_dg * 8);
-        // V^T store (reuses the tile transpose with buffer 0)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int c = v_dg * 8 + e;
-          bf16_t* dst = &S.V[0][c][v_kg * KPT];
-          uint32_t wv[KPT];
-#pragma unroll
-          for (int kq = 0; kq < KPT; ++kq) {
-            const uint32_t word = (e < 2) ? vreg[kq].x : (e < 4) ? vreg[kq].y : (e < 6) ? vreg[kq].z : vreg[kq].w;
-            wv[kq] = (e & 1) ? (word >> 16) : (word & 0xFFFFu);
-          }
-          if constexpr (KPT == 4) {
-            *reinterpret_cast<uint2*>(dst) = make_uint2(wv[0] | (wv[1] << 16), wv[2] | (wv[3] << 16));
-          } else {
-            *reinterpret_cast<uint32_t*>(dst) = wv[0] | (wv[1] << 16);
-          }
-        }
+      for (int q = 0; q < CK; ++q) {
+        const int c = tid + 256 * q;
+        const size_t ro = size_t(j0 + c / DG) * D + (c % DG) * 8;
+        *reinterpret_cast<uint4*>(&S.K[0][c / DG][(c % DG) * 8]) = *reinterpret_cast<const uint4*>(kbh + ro);
+        *reinterpret_cast<uint4*>(&S.K[1][c / DG][(c % DG) * 8]) = *reinterpret_cast<const uint4*>(kbl + ro);
+        store_vt_chunk(0, c, *reinterpret_cast<const uint4*>(vbt + size_t(j0) * D + size_t(c) * 8));
       }
       __syncthreads();
       floatx16 s[2];
@@ -577,7 +679,8 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sc
         for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
       qk(s, S.K[0]);
       qk(s, S.K[1]);
-      softmax_pv(s, 0, KT, S.bias);
+      to_logits(s, KT, S.bias);
+      softmax_pv(s, 0);
     }
   }
 
@@ -612,16 +715,19 @@ Prep carve(const AttnArgs& a, Arena& s) {
   p.Rmax = a.Ck / 2 + 1;
   p.Ckp = ceil_div(a.Ck, KT) * KT;
   p.W = ceil_div(a.Ck, 32);
+  p.NB = ceil_div(a.N, KT);
   p.tiles = s.get<int4>(size_t(a.H) * p.maxT);
   p.ntiles = s.get<int32_t>(size_t(a.H));
   p.ranges = s.get<int2>(size_t(a.H) * a.Cq * p.Rmax);
   p.rcount = s.get<int32_t>(size_t(a.H) * a.Cq);
+  p.raligned = s.get<int32_t>(size_t(a.H) * a.Cq);
+  if (a.dtype == SA_BF16) p.vt = s.get<bf16_t>(size_t(a.H) * p.NB * KT * a.d);
   if (a.compensate) {
     p.logsz = s.get<float>(size_t(a.H) * p.Ckp);
     if (a.dtype == SA_BF16) {
       p.kbh = s.get<bf16_t>(size_t(a.H) * p.Ckp * a.d);
       p.kbl = s.get<bf16_t>(size_t(a.H) * p.Ckp * a.d);
-      p.vb = s.get<bf16_t>(size_t(a.H) * p.Ckp * a.d);
+      p.vbt = s.get<bf16_t>(size_t(a.H) * p.Ckp * a.d);
     } else {
       p.kbf = s.get<float>(size_t(a.H) * p.Ckp * a.d);
       p.vbf = s.get<float>(size_t(a.H) * p.Ckp * a.d);
@@ -651,19 +757,25 @@ size_t attn_scratch(int H, int N, int d, int Cq, int Ck, int tile_rows, int comp
 
 hipError_t attn_run(const AttnArgs& a, Arena& s, hipStream_t st) {
   const Prep p = carve(a, s);
-  ranges_kernel<<<dim3(a.Cq, a.H), 64, 0, st>>>(a.mask, a.k_off, a.Cq, a.Ck, p.W, p.Rmax, p.ranges,
-                                                p.rcount);
+  ranges_kernel<<<dim3(a.Cq, a.H), 64, 0, st>>>(a.mask, a.k_off, a.Cq, a.Ck, p.W, p.Rmax, a.N,
+                                                p.ranges, p.rcount, p.raligned);
   tiles_kernel<<<a.H, 1024, 0, st>>>(a.q_off, a.Cq, a.tile_rows, p.maxT, p.tiles, p.ntiles);
   if (a.compensate)
     comp_prep_kernel<<<dim3(p.Ckp, a.H), 128, 0, st>>>(a.kbar, a.vbar, a.k_off, a.Ck, p.Ckp, a.d,
-                                                       p.kbh, p.kbl, p.vb, p.kbf, p.vbf, p.logsz);
+                                                       p.kbh, p.kbl, p.vbt, p.kbf, p.vbf, p.logsz);
   const int grid = 8 * ceil_div(p.maxT * a.H, 8);
   if (a.dtype == SA_BF16) {
     const float sl2 = a.scale * LOG2E;
-    if (a.d == 128)
-      attn_mfma<128><<<grid, 256, 0, st>>>(a, p, sl2);
-    else
-      attn_mfma<64><<<grid, 256, 0, st>>>(a, p, sl2);
+    const dim3 gv(p.NB, a.H);
+    if (a.d == 128) {
+      vt_kernel<128><<<gv, 256, 0, st>>>((const bf16_t*)a.v_perm, a.N, p.NB, p.vt);
+      attn_mfma<128, true><<<grid, 256, 0, st>>>(a, p, sl2);
+      attn_mfma<128, false><<<grid, 256, 0, st>>>(a, p, sl2);
+    } else {
+      vt_kernel<64><<<gv, 256, 0, st>>>((const bf16_t*)a.v_perm, a.N, p.NB, p.vt);
+      attn_mfma<64, true><<<grid, 256, 0, st>>>(a, p, sl2);
+      attn_mfma<64, false><<<grid, 256, 0, st>>>(a, p, sl2);
+    }
   } else {
     if (a.d == 128)
       attn_simple<float, 128><<<grid, 128, 0, st>>>(a, p, a.scale);
