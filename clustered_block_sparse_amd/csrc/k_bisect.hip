@@ -13,15 +13,23 @@
 // position order is the depth-first leaf order).
 //
 // The tree shape depends only on (n, leaf), so every head shares one table of
-// segments per level.  All heads run each level together:
-//   delta  : chunked, one 16-byte slice per lane, sortable fp32 key per token
-//   select : one workgroup per segment, exact k-th smallest (key, position)
-//            by a radix search below the common prefix of min/max, then an
-//            ordered scan over positions for ties
-//   sums   : chunked fixed-order partial sums of both sides (no float atomics)
-//   update : per segment, partials summed in chunk order -> the two means
-//   part.  : per segment ordered scan -> stable partition of the positions
+// segments per level.  Two phases:
+//  * top phase (segments of more than SUB_N tokens), one level at a time for
+//    all heads:
+//      delta  : chunked, 16-byte slice per lane, sortable fp32 key per token;
+//               the segment's key min / max is folded in with integer atomics
+//      select : one workgroup per segment, exact k-th smallest (key, position)
+//               via an interpolated histogram, then an LDS radix search
+//      sums   : round 0 sums both sides; later rounds only re-read the tokens
+//               that switched side (the sums change by exactly those rows);
+//               per-chunk partials, added in chunk order per segment (fixed
+//               order, no float atomics)
+//      part.  : per segment ordered scan -> stable partition of positions
+//  * subtree phase: one workgroup finishes each segment of at most SUB_N
+//    tokens through all remaining levels, with positions, keys and sides in
+//    LDS and rows re-read through the caches (four rows in flight per lane).
 
+#include <algorithm>
 #include <vector>
 
 #include "sa_internal.h"
@@ -30,12 +38,15 @@ namespace sa {
 
 namespace {
 
-constexpr int BCH = 1024;     // positions per chunk
+constexpr int BCH = 1024;    // positions per chunk (top phase)
+constexpr int SUB_N = 2560;  // segments up to this many tokens finish in one workgroup
 constexpr int MAXLEV = 32;
+constexpr int SUB_THREADS = 512;
 
 struct LevelTabs {
-  int nlev;
-  int nseg[MAXLEV], nchunk[MAXLEV], sb[MAXLEV], cb[MAXLEV];
+  int nlev;  // top levels; the final segment list is level nlev
+  int nseg[MAXLEV + 1], nchunk[MAXLEV], sb[MAXLEV + 1], cb[MAXLEV];
+  int L, subn;
 };
 
 struct TreePlan {
@@ -43,14 +54,20 @@ struct TreePlan {
   int total_seg, total_chunk, max_seg, max_chunk;
 };
 
-TreePlan plan_tree(int N, int L) {
+__host__ __device__ inline bool is_active(int n, int L, int subn) {
+  return ceil_div(n, L) >= 2 && n > subn;
+}
+
+TreePlan plan_tree(int N, int L, int subn) {
   TreePlan p{};
+  p.t.L = L;
+  p.t.subn = subn;
   std::vector<int> st{0}, nn{N};
-  while (true) {
+  while (p.t.nlev < MAXLEV) {
     bool any = false;
     for (int n : nn)
-      if (ceil_div(n, L) >= 2) any = true;
-    if (!any || p.t.nlev >= MAXLEV) break;
+      if (is_active(n, L, subn)) any = true;
+    if (!any) break;
     const int lv = p.t.nlev++;
     p.t.nseg[lv] = int(nn.size());
     p.t.sb[lv] = p.total_seg;
@@ -58,9 +75,8 @@ TreePlan plan_tree(int N, int L) {
     int nch = 0;
     std::vector<int> st2, nn2;
     for (size_t k = 0; k < nn.size(); ++k) {
-      const int c = ceil_div(nn[k], L);
-      if (c >= 2) {
-        const int nl = L * ceil_div(c, 2);
+      if (is_active(nn[k], L, subn)) {
+        const int nl = L * ceil_div(ceil_div(nn[k], L), 2);
         nch += ceil_div(nn[k], BCH);
         st2.push_back(st[k]);
         nn2.push_back(nl);
@@ -79,15 +95,21 @@ TreePlan plan_tree(int N, int L) {
     st.swap(st2);
     nn.swap(nn2);
   }
+  p.t.nseg[p.t.nlev] = int(nn.size());
+  p.t.sb[p.t.nlev] = p.total_seg;
+  p.total_seg += int(nn.size());
+  p.max_seg = max(p.max_seg, 1);
+  p.max_chunk = max(p.max_chunk, 1);
   return p;
 }
 
 // ---------------------------------------------------------------------------
-// block helpers (blockDim = 1024)
+// block helpers
 // ---------------------------------------------------------------------------
+// exclusive scan over the block (blockDim a multiple of 64, <= 1024)
 template <typename V>
-__device__ V block_excl_scan_1024(V v, V* wsum /*[16]*/, V& total) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+__device__ V block_excl_scan(V v, V* wsum /*[16]*/, V& total) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, nw = blockDim.x >> 6;
   V x = v;
   for (int o = 1; o < 64; o <<= 1) {
     V y = __shfl_up(x, o, 64);
@@ -96,7 +118,7 @@ __device__ V block_excl_scan_1024(V v, V* wsum /*[16]*/, V& total) {
   if (lane == 63) wsum[w] = x;
   __syncthreads();
   V pre = 0, tot = 0;
-  for (int j = 0; j < 16; ++j) {
+  for (int j = 0; j < nw; ++j) {
     if (j < w) pre += wsum[j];
     tot += wsum[j];
   }
@@ -105,16 +127,190 @@ __device__ V block_excl_scan_1024(V v, V* wsum /*[16]*/, V& total) {
   return pre + x - v;
 }
 
+__device__ __forceinline__ bool is_left(uint32_t key, int pos, uint2 th) {
+  return key < th.x || (key == th.x && pos <= int(th.y));
+}
+
+// Exact k-th smallest (1-based) of (key[i], i) over i < n: keys read through
+// `get`.  A radix search over 11-bit digits below the common prefix of the
+// minimum and maximum key, then an ordered scan over indices for the tie.
+// All threads of the block call it; the result is (key, index).
+struct SelectShared {
+  int hist[2048];
+  int wsum[16];
+  uint32_t red[2][16];
+  int sel_bin, sel_pos;
+};
+
+template <typename Get>
+__device__ uint2 block_select(Get get, int n, int k, SelectShared& sh) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, nt = blockDim.x, nw = nt >> 6;
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int i = t; i < n; i += nt) {
+    const uint32_t v = get(i);
+    mn = min(mn, v);
+    mx = max(mx, v);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+  }
+  if (lane == 0) {
+    sh.red[0][w] = mn;
+    sh.red[1][w] = mx;
+  }
+  __syncthreads();
+  mn = sh.red[0][0];
+  mx = sh.red[1][0];
+  for (int j = 1; j < nw; ++j) {
+    mn = min(mn, sh.red[0][j]);
+    mx = max(mx, sh.red[1][j]);
+  }
+  __syncthreads();
+  uint32_t prefix = mn;
+  if (mn != mx) {
+    int hb = 31 - __clz(mn ^ mx);
+    prefix = hb == 31 ? 0u : (mn & ~((2u << hb) - 1u));
+    while (true) {
+      const int shift = max(hb - 10, 0);
+      const int width = hb - shift + 1;
+      const uint32_t dmask = (1u << width) - 1u;
+      const int above = shift + width;
+      for (int b = t; b < 2048; b += nt) sh.hist[b] = 0;
+      __syncthreads();
+      for (int i = t; i < n; i += nt) {
+        const uint32_t v = get(i);
+        const bool match = above >= 32 ? true : ((v >> above) == (prefix >> above));
+        if (match) atomicAdd(&sh.hist[(v >> shift) & dmask], 1);
+      }
+      __syncthreads();
+      // bins per thread: 2048 / nt
+      const int bpt = 2048 / nt;
+      int loc = 0;
+      for (int b = 0; b < bpt; ++b) loc += sh.hist[t * bpt + b];
+      int tot;
+      int pre = block_excl_scan<int>(loc, sh.wsum, tot);
+      if (pre < k && k <= pre + loc) {
+        for (int b = 0; b < bpt; ++b) {
+          const int c = sh.hist[t * bpt + b];
+          if (pre < k && k <= pre + c) {
+            sh.sel_bin = t * bpt + b;
+            sh.sel_pos = pre;
+          }
+          pre += c;
+        }
+      }
+      __syncthreads();
+      k -= sh.sel_pos;
+      prefix |= uint32_t(sh.sel_bin) << shift;
+      __syncthreads();
+      if (shift == 0) break;
+      hb = shift - 1;
+    }
+  }
+  int running = 0;
+  for (int base = 0; base < n; base += nt) {
+    const int i = base + t;
+    const int f = (i < n && get(i) == prefix) ? 1 : 0;
+    int tot;
+    const int pre = block_excl_scan<int>(f, sh.wsum, tot);
+    if (f && running + pre + 1 == k) sh.sel_pos = i;
+    running += tot;
+    __syncthreads();
+    if (running >= k) break;
+  }
+  __syncthreads();
+  const uint2 r = make_uint2(prefix, uint32_t(sh.sel_pos));
+  __syncthreads();
+  return r;
+}
+
+// k-th smallest (1-based) of m distinct 64-bit keys held in LDS: radix search
+// over 11-bit digits below the common prefix of the minimum and maximum.
+struct Sel64Shared {
+  int hist[2048];
+  int wsum[16];
+  unsigned long long red[2][16];
+  int sel_bin, sel_pos;
+};
+
+__device__ unsigned long long lds_select64(const unsigned long long* key, int m, int k, Sel64Shared& sh) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, nt = blockDim.x, nw = nt >> 6;
+  unsigned long long mn = ~0ull, mx = 0ull;
+  for (int i = t; i < m; i += nt) {
+    const unsigned long long v = key[i];
+    mn = v < mn ? v : mn;
+    mx = v > mx ? v : mx;
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long a = __shfl_xor(mn, o, 64), c = __shfl_xor(mx, o, 64);
+    mn = a < mn ? a : mn;
+    mx = c > mx ? c : mx;
+  }
+  if (lane == 0) {
+    sh.red[0][w] = mn;
+    sh.red[1][w] = mx;
+  }
+  __syncthreads();
+  mn = sh.red[0][0];
+  mx = sh.red[1][0];
+  for (int j = 1; j < nw; ++j) {
+    mn = sh.red[0][j] < mn ? sh.red[0][j] : mn;
+    mx = sh.red[1][j] > mx ? sh.red[1][j] : mx;
+  }
+  __syncthreads();
+  if (mn == mx) return mn;
+  int hb = 63 - __clzll(mn ^ mx);
+  unsigned long long prefix = hb == 63 ? 0ull : (mn & ~((2ull << hb) - 1ull));
+  while (true) {
+    const int shift = max(hb - 10, 0);
+    const int width = hb - shift + 1;
+    const unsigned long long dmask = (1ull << width) - 1ull;
+    const int above = shift + width;
+    for (int b = t; b < 2048; b += nt) sh.hist[b] = 0;
+    __syncthreads();
+    for (int i = t; i < m; i += nt) {
+      const unsigned long long v = key[i];
+      const bool match = above >= 64 ? true : ((v >> above) == (prefix >> above));
+      if (match) atomicAdd(&sh.hist[int((v >> shift) & dmask)], 1);
+    }
+    __syncthreads();
+    const int bpt = 2048 / nt;
+    int loc = 0;
+    for (int b = 0; b < bpt; ++b) loc += sh.hist[t * bpt + b];
+    int tot;
+    int pre = block_excl_scan<int>(loc, sh.wsum, tot);
+    if (pre < k && k <= pre + loc) {
+      for (int b = 0; b < bpt; ++b) {
+        const int c = sh.hist[t * bpt + b];
+        if (pre < k && k <= pre + c) {
+          sh.sel_bin = t * bpt + b;
+          sh.sel_pos = pre;
+        }
+        pre += c;
+      }
+    }
+    __syncthreads();
+    k -= sh.sel_pos;
+    prefix |= (unsigned long long)sh.sel_bin << shift;
+    __syncthreads();
+    if (shift == 0) break;
+    hb = shift - 1;
+  }
+  return prefix;
+}
+
 // ---------------------------------------------------------------------------
 // tree tables on the device (one workgroup of 1024 threads)
-// segs: int4 {start, n, n_left (0 = leaf), first chunk (level-local)}
+// segs: int4 {start, n, n_left (0 = not split at this level), first chunk}
 // chunks: int4 {segment (level-local), position, count, 0}
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void build_tree_kernel(LevelTabs tb, int N, int L, int4* segs,
+__global__ __launch_bounds__(1024) void build_tree_kernel(LevelTabs tb, int N, int4* segs,
                                                           int4* chunks) {
   __shared__ int wsum[16];
   const int t = threadIdx.x;
   if (t == 0) segs[0] = make_int4(0, N, 0, 0);
+  __threadfence_block();
   __syncthreads();
   for (int lv = 0; lv < tb.nlev; ++lv) {
     int chunk_carry = 0, child_carry = 0;
@@ -124,9 +320,8 @@ __global__ __launch_bounds__(1024) void build_tree_kernel(LevelTabs tb, int N, i
       int nchunk = 0, nchild = 0, nl = 0;
       if (k < tb.nseg[lv]) {
         s = segs[tb.sb[lv] + k];
-        const int c = ceil_div(s.y, L);
-        if (c >= 2) {
-          nl = L * ceil_div(c, 2);
+        if (is_active(s.y, tb.L, tb.subn)) {
+          nl = tb.L * ceil_div(ceil_div(s.y, tb.L), 2);
           nchunk = ceil_div(s.y, BCH);
           nchild = 2;
         } else {
@@ -134,22 +329,20 @@ __global__ __launch_bounds__(1024) void build_tree_kernel(LevelTabs tb, int N, i
         }
       }
       int tot1, tot2;
-      const int cpre = block_excl_scan_1024<int>(nchunk, wsum, tot1) + chunk_carry;
-      const int kpre = block_excl_scan_1024<int>(nchild, wsum, tot2) + child_carry;
+      const int cpre = block_excl_scan<int>(nchunk, wsum, tot1) + chunk_carry;
+      const int kpre = block_excl_scan<int>(nchild, wsum, tot2) + child_carry;
       if (k < tb.nseg[lv]) {
         segs[tb.sb[lv] + k] = make_int4(s.x, s.y, nl, cpre);
         for (int c = 0; c < nchunk; ++c) {
           const int pos = s.x + c * BCH;
           chunks[tb.cb[lv] + cpre + c] = make_int4(k, pos, min(BCH, s.x + s.y - pos), 0);
         }
-        if (lv + 1 < tb.nlev) {
-          int4* nxt = segs + tb.sb[lv + 1] + kpre;
-          if (nchild == 2) {
-            nxt[0] = make_int4(s.x, nl, 0, 0);
-            nxt[1] = make_int4(s.x + nl, s.y - nl, 0, 0);
-          } else {
-            nxt[0] = make_int4(s.x, s.y, 0, 0);
-          }
+        int4* nxt = segs + tb.sb[lv + 1] + kpre;
+        if (nchild == 2) {
+          nxt[0] = make_int4(s.x, nl, 0, 0);
+          nxt[1] = make_int4(s.x + nl, s.y - nl, 0, 0);
+        } else {
+          nxt[0] = make_int4(s.x, s.y, 0, 0);
         }
       }
       chunk_carry += tot1;
@@ -167,8 +360,18 @@ __global__ void iota_kernel(int32_t* p, int N) {
   if (n < N) p[size_t(h) * N + n] = n;
 }
 
+__global__ void init_minmax(uint2* p, size_t n) {
+  const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = make_uint2(0xFFFFFFFFu, 0u);
+}
+
+__global__ void zero_i32(int32_t* p, size_t n) {
+  const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
 // ---------------------------------------------------------------------------
-// delta pass
+// row geometry: one 16-byte vector per lane, LPR lanes per row
 // ---------------------------------------------------------------------------
 template <typename T, int D>
 struct RowGeo {
@@ -178,8 +381,7 @@ struct RowGeo {
 };
 
 template <typename T, int EPV>
-__device__ __forceinline__ void load_vec(const T* p, float (&v)[EPV]) {
-  const uint4 u = *reinterpret_cast<const uint4*>(p);
+__device__ __forceinline__ void unpack_vec(uint4 u, float (&v)[EPV]) {
   if constexpr (sizeof(T) == 4) {
     v[0] = __uint_as_float(u.x);
     v[1] = __uint_as_float(u.y);
@@ -195,27 +397,46 @@ __device__ __forceinline__ void load_vec(const T* p, float (&v)[EPV]) {
   }
 }
 
+template <typename T>
+__device__ __forceinline__ uint4 ld16(const T* p) {
+  return *reinterpret_cast<const uint4*>(p);
+}
+
+// ---------------------------------------------------------------------------
+// top phase kernels (grid.y = heads)
+// ---------------------------------------------------------------------------
+struct TopBufs {
+  const int4* segs;    // level table
+  const int4* chunks;  // level chunk table
+  int32_t* perm;       // [H][N] current order
+  uint32_t* keys;      // [H][N]
+  uint8_t* side;       // [H][N] 1 = left in the previous round
+  float* cen;          // [H][max_seg][2][D]  means of the two sides
+  float* ssum;         // [H][max_seg][2][D]  sums of the two sides
+  uint2* thr;          // [H][max_seg]
+  float* part;         // [H][max_chunk][2][D]
+  int32_t* cnt;        // [H][max_seg] chunk arrival counters (zero between uses)
+  uint2* segmm;        // [H][max_seg] min / max key of the round (reset after use)
+  int max_seg, max_chunk, N, round;  // round: 0 = first round of a level
+};
+
 template <typename T, int D>
-__global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ x,
-                                                    const int32_t* __restrict__ perm,
-                                                    const int4* __restrict__ segs,
-                                                    const int4* __restrict__ chunks,
-                                                    const float* __restrict__ cen, int max_seg,
-                                                    int N, int first, uint32_t* __restrict__ keys) {
+__global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ x, TopBufs b, int first) {
   using G = RowGeo<T, D>;
+  constexpr int U = 4;  // wave steps in flight
   __shared__ float wv[D], mv[D];
   const int h = blockIdx.y, t = threadIdx.x;
-  const int4 ch = chunks[blockIdx.x];
-  const int4 sg = segs[ch.x];
-  const int32_t* ph = perm + size_t(h) * N;
-  const T* xh = x + size_t(h) * N * D;
+  const int4 ch = b.chunks[blockIdx.x];
+  const int4 sg = b.segs[ch.x];
+  const int32_t* ph = b.perm + size_t(h) * b.N;
+  const T* xh = x + size_t(h) * b.N * D;
   if (t < D) {
     float c1, c2;
     if (first) {
       c1 = to_f(xh[size_t(ph[sg.x]) * D + t]);
       c2 = to_f(xh[size_t(ph[sg.x + 1]) * D + t]);
     } else {
-      const float* c = cen + (size_t(h) * max_seg + ch.x) * 2 * D;
+      const float* c = b.cen + (size_t(h) * b.max_seg + ch.x) * 2 * D;
       c1 = c[t];
       c2 = c[D + t];
     }
@@ -231,216 +452,311 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ x,
     wr[e] = wv[sub * G::EPV + e];
     mr[e] = mv[sub * G::EPV + e];
   }
-  for (int rb = w * G::RPW; rb < ch.z; rb += 4 * G::RPW) {
-    const int r = rb + rsub;
-    const bool valid = r < ch.z;
-    const int p = ch.y + (valid ? r : 0);
-    float v[G::EPV];
-    load_vec<T, G::EPV>(xh + size_t(ph[p]) * D + sub * G::EPV, v);
-    float acc = 0.f;
+  constexpr int STEP = 4 * G::RPW;  // rows per block step
+  uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+  for (int rb = w * G::RPW; rb < ch.z; rb += U * STEP) {
+    int pos[U];
+    uint4 raw[U];
 #pragma unroll
-    for (int e = 0; e < G::EPV; ++e) acc = fmaf(wr[e], fmaf(2.f, v[e], -mr[e]), acc);
+    for (int u = 0; u < U; ++u) {
+      const int r = rb + u * STEP + rsub;
+      pos[u] = ch.y + (r < ch.z ? r : 0);
+    }
 #pragma unroll
-    for (int o = 1; o < G::LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
-    if (valid && sub == 0) keys[size_t(h) * N + p] = sortable(acc);
-  }
-}
-
-// ---------------------------------------------------------------------------
-// select: exact k-th smallest (key, position) of a segment
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void select_kernel(const uint32_t* __restrict__ keys,
-                                                      const int4* __restrict__ segs, int max_seg,
-                                                      int N, uint2* __restrict__ thr) {
-  __shared__ int hist[2048];
-  __shared__ int wsum[16];
-  __shared__ uint32_t red[2][16];
-  __shared__ int sel_bin, sel_pos;
-  const int h = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int4 sg = segs[blockIdx.x];
-  if (sg.z == 0) return;
-  const uint32_t* u = keys + size_t(h) * N + sg.x;
-  const int n = sg.y;
-  int k = sg.z;  // 1-based rank of the last left element
-  // min / max
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int i = t; i < n; i += 1024) {
-    const uint32_t v = u[i];
-    mn = min(mn, v);
-    mx = max(mx, v);
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
-  }
-  if (lane == 0) {
-    red[0][w] = mn;
-    red[1][w] = mx;
-  }
-  __syncthreads();
-  mn = red[0][0];
-  mx = red[1][0];
-  for (int j = 1; j < 16; ++j) {
-    mn = min(mn, red[0][j]);
-    mx = max(mx, red[1][j]);
-  }
-  uint32_t prefix = mn;
-  if (mn != mx) {
-    int hb = 31 - __clz(mn ^ mx);  // highest differing bit
-    prefix = mn & ~((hb == 31) ? 0xFFFFFFFFu : ((2u << hb) - 1u));
-    while (true) {
-      const int shift = max(hb - 10, 0);
-      const int width = hb - shift + 1;
-      const uint32_t dmask = (1u << width) - 1u;
-      const int above = shift + width;  // bits >= above must equal prefix's
-      hist[t] = 0;
-      hist[t + 1024] = 0;
-      __syncthreads();
-      for (int i = t; i < n; i += 1024) {
-        const uint32_t v = u[i];
-        const bool match = above >= 32 ? true : ((v >> above) == (prefix >> above));
-        if (match) atomicAdd(&hist[(v >> shift) & dmask], 1);
+    for (int u = 0; u < U; ++u) raw[u] = ld16(xh + size_t(ph[pos[u]]) * D + sub * G::EPV);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float v[G::EPV];
+      unpack_vec<T, G::EPV>(raw[u], v);
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < G::EPV; ++e) acc = fmaf(wr[e], fmaf(2.f, v[e], -mr[e]), acc);
+#pragma unroll
+      for (int o = 1; o < G::LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
+      const int r = rb + u * STEP + rsub;
+      const uint32_t key = sortable(acc);
+      if (r < ch.z) {
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
+        if (sub == 0) b.keys[size_t(h) * b.N + pos[u]] = key;
       }
-      __syncthreads();
-      const int c0 = hist[2 * t], c1 = hist[2 * t + 1];
-      int tot;
-      const int pre = block_excl_scan_1024<int>(c0 + c1, wsum, tot);
-      if (pre < k && k <= pre + c0) {
-        sel_bin = 2 * t;
-        sel_pos = pre;
-      } else if (pre + c0 < k && k <= pre + c0 + c1) {
-        sel_bin = 2 * t + 1;
-        sel_pos = pre + c0;
-      }
-      __syncthreads();
-      k -= sel_pos;
-      prefix |= uint32_t(sel_bin) << shift;
-      __syncthreads();
-      if (shift == 0) break;
-      hb = shift - 1;
     }
   }
-  // ties: the k-th position (in order) holding key == prefix
-  int running = 0;
-  for (int base = 0; base < n; base += 1024) {
-    const int i = base + t;
-    const int f = (i < n && u[i] == prefix) ? 1 : 0;
-    int tot;
-    const int pre = block_excl_scan_1024<int>(f, wsum, tot);
-    if (f && running + pre + 1 == k) sel_pos = sg.x + i;
-    running += tot;
-    __syncthreads();
-    if (running >= k) break;
+  // chunk min / max -> segment (integer atomics: order independent)
+  for (int o = 32; o > 0; o >>= 1) {
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, o, 64));
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, o, 64));
+  }
+  __shared__ uint32_t rmm[2][4];
+  if (lane == 0) {
+    rmm[0][w] = kmin;
+    rmm[1][w] = kmax;
   }
   __syncthreads();
-  if (t == 0) thr[size_t(h) * max_seg + blockIdx.x] = make_uint2(prefix, uint32_t(sel_pos));
+  if (t == 0) {
+    const uint32_t a = min(min(rmm[0][0], rmm[0][1]), min(rmm[0][2], rmm[0][3]));
+    const uint32_t c = max(max(rmm[1][0], rmm[1][1]), max(rmm[1][2], rmm[1][3]));
+    uint2* mm = b.segmm + size_t(h) * b.max_seg + ch.x;
+    atomicMin(&mm->x, a);
+    atomicMax(&mm->y, c);
+  }
 }
 
-__device__ __forceinline__ bool is_left(uint32_t key, int pos, uint2 th) {
-  return key < th.x || (key == th.x && pos <= int(th.y));
-}
+// Exact (key, position) of rank n_left in a segment: the keys' min / max
+// (folded in by the delta pass) spread 2048 interpolated bins; one histogram
+// pass finds the bin of rank n_left, a second pass gathers that bin's keys
+// (with positions, as distinct 64-bit keys) into LDS, where a radix search
+// finishes.  Oversized bins fall back to the generic radix search.
+constexpr int SEL_CAP = 8192;
 
-// ---------------------------------------------------------------------------
-// sums of both sides per chunk
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void sums_kernel(const T* __restrict__ x,
-                                                   const int32_t* __restrict__ perm,
-                                                   const uint32_t* __restrict__ keys,
-                                                   const int4* __restrict__ chunks,
-                                                   const uint2* __restrict__ thr, int max_seg,
-                                                   int max_chunk, int N, float* __restrict__ part) {
-  using G = RowGeo<T, D>;
-  __shared__ float ws[4][2][D];
+struct TopSelShared {
+  unsigned long long cand[SEL_CAP];
+  Sel64Shared s64;
+  int cnt, bin, below;
+};
+
+__global__ __launch_bounds__(1024) void select_kernel(TopBufs b) {
+  __shared__ TopSelShared sh;
+  __shared__ SelectShared gsh;
   const int h = blockIdx.y, t = threadIdx.x;
-  const int4 ch = chunks[blockIdx.x];
-  const uint2 th = thr[size_t(h) * max_seg + ch.x];
-  const int32_t* ph = perm + size_t(h) * N;
-  const uint32_t* kh = keys + size_t(h) * N;
-  const T* xh = x + size_t(h) * N * D;
+  const int4 sg = b.segs[blockIdx.x];
+  if (sg.z == 0) return;
+  uint2* mmp = b.segmm + size_t(h) * b.max_seg + blockIdx.x;
+  const uint2 mm = *mmp;
+  __syncthreads();
+  if (t == 0) *mmp = make_uint2(0xFFFFFFFFu, 0u);  // ready for the next round
+  const uint32_t* u = b.keys + size_t(h) * b.N + sg.x;
+  const int n = sg.y, k = sg.z;
+  uint2 res;
+  if (mm.x == mm.y) {
+    res = make_uint2(mm.x, uint32_t(sg.x + k - 1));  // all keys equal: rank k is position k-1
+  } else {
+    const unsigned long long range = (unsigned long long)(mm.y - mm.x) + 1ull;
+    auto bin_of = [&](uint32_t v) { return int(((unsigned long long)(v - mm.x) * 2048ull) / range); };
+    for (int i = t; i < 2048; i += 1024) sh.s64.hist[i] = 0;
+    if (t == 0) sh.cnt = 0;
+    __syncthreads();
+    constexpr int U = 8;
+    for (int i0 = t; i0 < n; i0 += 1024 * U) {
+      uint32_t v[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int i = i0 + q * 1024;
+        v[q] = i < n ? u[i] : 0u;
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q)
+        if (i0 + q * 1024 < n) atomicAdd(&sh.s64.hist[bin_of(v[q])], 1);
+    }
+    __syncthreads();
+    {
+      const int c0 = sh.s64.hist[2 * t], c1 = sh.s64.hist[2 * t + 1];
+      int tot;
+      const int pre = block_excl_scan<int>(c0 + c1, sh.s64.wsum, tot);
+      if (pre < k && k <= pre + c0) {
+        sh.bin = 2 * t;
+        sh.below = pre;
+      } else if (pre + c0 < k && k <= pre + c0 + c1) {
+        sh.bin = 2 * t + 1;
+        sh.below = pre + c0;
+      }
+    }
+    __syncthreads();
+    const int bstar = sh.bin, kk = k - sh.below;
+    for (int i0 = t; i0 < n; i0 += 1024 * U) {
+      uint32_t v[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int i = i0 + q * 1024;
+        v[q] = i < n ? u[i] : 0u;
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int i = i0 + q * 1024;
+        if (i < n && bin_of(v[q]) == bstar) {
+          const int slot = atomicAdd(&sh.cnt, 1);
+          if (slot < SEL_CAP) sh.cand[slot] = ((unsigned long long)v[q] << 32) | uint32_t(sg.x + i);
+        }
+      }
+    }
+    __syncthreads();
+    const int m = sh.cnt;
+    if (m <= SEL_CAP) {
+      const unsigned long long r = lds_select64(sh.cand, m, kk, sh.s64);
+      res = make_uint2(uint32_t(r >> 32), uint32_t(r & 0xFFFFFFFFull));
+    } else {
+      const uint2 r = block_select([&](int i) { return u[i]; }, n, k, gsh);
+      res = make_uint2(r.x, r.y + sg.x);
+    }
+  }
+  if (t == 0) b.thr[size_t(h) * b.max_seg + blockIdx.x] = res;
+}
+
+// Sums of one chunk into its partial slot.  FULL (round 0): both sides from
+// scratch.  Otherwise: the tokens whose side changed since the previous round,
+// found with vectorised key/side reads and compacted in position order, give
+// the change of the left sum; only their rows are read.  Sides are updated.
+template <typename T, int D, bool FULL>
+__global__ __launch_bounds__(256) void sums_kernel(const T* __restrict__ x, TopBufs b) {
+  using G = RowGeo<T, D>;
+  constexpr int U = 4;
+  constexpr int STEP = 4 * G::RPW;
+  __shared__ float ws[4][2][D];
+  __shared__ int list[BCH];
+  __shared__ int wsum[16];
+  const int h = blockIdx.y, t = threadIdx.x;
+  const int4 ch = b.chunks[blockIdx.x];
+  const uint2 th = b.thr[size_t(h) * b.max_seg + ch.x];
+  const int32_t* ph = b.perm + size_t(h) * b.N;
+  const uint32_t* kh = b.keys + size_t(h) * b.N;
+  uint8_t* sd = b.side + size_t(h) * b.N;
+  const T* xh = x + size_t(h) * b.N * D;
   const int lane = t & 63, w = t >> 6;
   const int sub = lane % G::LPR, rsub = lane / G::LPR;
-  float sl[G::EPV], sr[G::EPV];
+  int cnt = ch.z;
+  if constexpr (!FULL) {
+    // four consecutive positions per thread (chunk starts are 4-aligned: leaf
+    // and chunk sizes are multiples of 4)
+    const int i0 = 4 * t;
+    int sgn4[4] = {0, 0, 0, 0};
+    int ns = 0;
+    if (i0 < ch.z) {
+      const int p0 = ch.y + i0;
+      uint32_t kv[4];
+      uint32_t sv = 0;
+      if (i0 + 4 <= ch.z && (p0 & 3) == 0) {
+        const uint4 k4 = *reinterpret_cast<const uint4*>(kh + p0);
+        kv[0] = k4.x; kv[1] = k4.y; kv[2] = k4.z; kv[3] = k4.w;
+        sv = *reinterpret_cast<const uint32_t*>(sd + p0);
+      } else {
+        for (int q = 0; q < 4; ++q) {
+          kv[q] = i0 + q < ch.z ? kh[p0 + q] : 0u;
+          sv |= uint32_t(i0 + q < ch.z ? sd[p0 + q] : 0) << (8 * q);
+        }
+      }
+      uint32_t nsv = sv;
 #pragma unroll
-  for (int e = 0; e < G::EPV; ++e) sl[e] = sr[e] = 0.f;
-  for (int rb = w * G::RPW; rb < ch.z; rb += 4 * G::RPW) {
-    const int r = rb + rsub;
-    if (r < ch.z) {
-      const int p = ch.y + r;
+      for (int q = 0; q < 4; ++q) {
+        if (i0 + q >= ch.z) break;
+        const bool left = is_left(kv[q], p0 + q, th);
+        const bool was = ((sv >> (8 * q)) & 0xFF) != 0;
+        if (left != was) {
+          sgn4[q] = left ? 1 : -1;
+          ++ns;
+          nsv = (nsv & ~(0xFFu << (8 * q))) | (uint32_t(left ? 1 : 0) << (8 * q));
+        }
+      }
+      if (ns) {
+        if (i0 + 4 <= ch.z && (p0 & 3) == 0) {
+          *reinterpret_cast<uint32_t*>(sd + p0) = nsv;
+        } else {
+          for (int q = 0; q < 4 && i0 + q < ch.z; ++q) sd[p0 + q] = uint8_t((nsv >> (8 * q)) & 0xFF);
+        }
+      }
+    }
+    int tot;
+    int pre = block_excl_scan<int>(ns, wsum, tot);
+    for (int q = 0; q < 4; ++q)
+      if (sgn4[q]) list[pre++] = sgn4[q] > 0 ? (ch.y + i0 + q) : ~(ch.y + i0 + q);
+    cnt = tot;
+    __syncthreads();
+  }
+  float s0[G::EPV], s1[G::EPV];  // FULL: left, right.  Otherwise: change of left
+#pragma unroll
+  for (int e = 0; e < G::EPV; ++e) s0[e] = s1[e] = 0.f;
+  for (int rb = w * G::RPW; rb < cnt; rb += U * STEP) {
+    uint4 raw[U];
+    int sgn[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int r = rb + u * STEP + rsub;
+      sgn[u] = 0;
+      int p = 0;
+      if (r < cnt) {
+        if (FULL) {
+          p = ch.y + r;
+          sgn[u] = is_left(kh[p], p, th) ? 1 : 2;
+        } else {
+          const int e = list[r];
+          p = e >= 0 ? e : ~e;
+          sgn[u] = e >= 0 ? 1 : -1;
+        }
+      }
+      raw[u] = sgn[u] != 0 ? ld16(xh + size_t(ph[p]) * D + sub * G::EPV) : make_uint4(0, 0, 0, 0);
+      if (FULL && sgn[u] != 0 && sub == 0) sd[p] = sgn[u] == 1 ? 1 : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (sgn[u] == 0) continue;
       float v[G::EPV];
-      load_vec<T, G::EPV>(xh + size_t(ph[p]) * D + sub * G::EPV, v);
-      if (is_left(kh[p], p, th)) {
+      unpack_vec<T, G::EPV>(raw[u], v);
+      if (sgn[u] == 2) {
 #pragma unroll
-        for (int e = 0; e < G::EPV; ++e) sl[e] += v[e];
+        for (int e = 0; e < G::EPV; ++e) s1[e] += v[e];
+      } else if (sgn[u] == 1) {
+#pragma unroll
+        for (int e = 0; e < G::EPV; ++e) s0[e] += v[e];
       } else {
 #pragma unroll
-        for (int e = 0; e < G::EPV; ++e) sr[e] += v[e];
+        for (int e = 0; e < G::EPV; ++e) s0[e] -= v[e];
       }
     }
   }
-  // combine the row groups of the wave (lanes with the same slice), fixed order
 #pragma unroll
   for (int o = G::LPR; o < 64; o <<= 1) {
 #pragma unroll
     for (int e = 0; e < G::EPV; ++e) {
-      sl[e] += __shfl_xor(sl[e], o, 64);
-      sr[e] += __shfl_xor(sr[e], o, 64);
+      s0[e] += __shfl_xor(s0[e], o, 64);
+      if constexpr (FULL) s1[e] += __shfl_xor(s1[e], o, 64);
     }
   }
   if (rsub == 0) {
 #pragma unroll
     for (int e = 0; e < G::EPV; ++e) {
-      ws[w][0][sub * G::EPV + e] = sl[e];
-      ws[w][1][sub * G::EPV + e] = sr[e];
+      ws[w][0][sub * G::EPV + e] = s0[e];
+      ws[w][1][sub * G::EPV + e] = FULL ? s1[e] : 0.f;
     }
   }
   __syncthreads();
-  float* out = part + (size_t(h) * max_chunk + blockIdx.x) * 2 * D;
+  float* out = b.part + (size_t(h) * b.max_chunk + blockIdx.x) * 2 * D;
   for (int i = t; i < 2 * D; i += 256) {
-    const int s = i / D, c = i % D;
-    out[i] = ((ws[0][s][c] + ws[1][s][c]) + ws[2][s][c]) + ws[3][s][c];
+    const int sdx = i / D, c = i % D;
+    out[i] = ((ws[0][sdx][c] + ws[1][sdx][c]) + ws[2][sdx][c]) + ws[3][sdx][c];
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(D) void update_kernel(const int4* __restrict__ segs,
-                                                   const float* __restrict__ part, int max_seg,
-                                                   int max_chunk, float* __restrict__ cen) {
+// Per segment: partials in chunk order -> sums and means of the two sides.
+template <int D, bool FULL>
+__global__ __launch_bounds__(256) void update_kernel(TopBufs b) {
   const int h = blockIdx.y, t = threadIdx.x;
-  const int4 sg = segs[blockIdx.x];
+  const int4 sg = b.segs[blockIdx.x];
   if (sg.z == 0) return;
   const int nch = ceil_div(sg.y, BCH);
-  float L = 0.f, R = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const float* p = part + (size_t(h) * max_chunk + sg.w + c) * 2 * D;
-    L += p[t];
-    R += p[D + t];
+  const size_t so = (size_t(h) * b.max_seg + blockIdx.x) * 2 * D;
+  for (int i = t; i < 2 * D; i += 256) {
+    const int sdx = i / D, c = i % D;
+    const int src = FULL ? i : c;
+    float acc = 0.f;
+    for (int q = 0; q < nch; ++q) acc += b.part[(size_t(h) * b.max_chunk + sg.w + q) * 2 * D + src];
+    const float tot = FULL ? acc : b.ssum[so + i] + (sdx == 0 ? acc : -acc);
+    b.ssum[so + i] = tot;
+    b.cen[so + i] = tot / float(sdx == 0 ? sg.z : sg.y - sg.z);
   }
-  float* o = cen + (size_t(h) * max_seg + blockIdx.x) * 2 * D;
-  o[t] = L / float(sg.z);
-  o[D + t] = R / float(sg.y - sg.z);
 }
 
-// ---------------------------------------------------------------------------
-// stable partition
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void partition_kernel(const int32_t* __restrict__ perm_in,
-                                                         int32_t* __restrict__ perm_out,
-                                                         const uint32_t* __restrict__ keys,
-                                                         const int4* __restrict__ segs,
-                                                         const uint2* __restrict__ thr, int max_seg,
-                                                         int N) {
+__global__ __launch_bounds__(1024) void partition_kernel(TopBufs b, const int32_t* __restrict__ perm_in,
+                                                         int32_t* __restrict__ perm_out) {
   __shared__ int wsum[16];
   const int h = blockIdx.y, t = threadIdx.x;
-  const int4 sg = segs[blockIdx.x];
-  const int32_t* pi = perm_in + size_t(h) * N;
-  int32_t* po = perm_out + size_t(h) * N;
+  const int4 sg = b.segs[blockIdx.x];
+  const int32_t* pi = perm_in + size_t(h) * b.N;
+  int32_t* po = perm_out + size_t(h) * b.N;
   if (sg.z == 0) {
     for (int i = t; i < sg.y; i += 1024) po[sg.x + i] = pi[sg.x + i];
     return;
   }
-  const uint2 th = thr[size_t(h) * max_seg + blockIdx.x];
-  const uint32_t* kh = keys + size_t(h) * N;
+  const uint2 th = b.thr[size_t(h) * b.max_seg + blockIdx.x];
+  const uint32_t* kh = b.keys + size_t(h) * b.N;
   int run_left = 0;
   for (int base = 0; base < sg.y; base += 1024) {
     const int i = base + t;
@@ -448,13 +764,318 @@ __global__ __launch_bounds__(1024) void partition_kernel(const int32_t* __restri
     const int p = sg.x + i;
     const int left = (valid && is_left(kh[p], p, th)) ? 1 : 0;
     int tot;
-    const int lpre = block_excl_scan_1024<int>(left, wsum, tot) + run_left;
+    const int lpre = block_excl_scan<int>(left, wsum, tot) + run_left;
     if (valid) {
       const int np = left ? sg.x + lpre : sg.x + sg.z + (i - lpre);
       po[np] = pi[p];
     }
     run_left += tot;
   }
+}
+
+// ---------------------------------------------------------------------------
+// subtree phase: one workgroup per segment of at most SUB_N tokens
+// ---------------------------------------------------------------------------
+constexpr int MAXS = 8;        // active segments handled together
+constexpr int SUB_LIST = 512;  // active segments per level (leaf >= 4)
+
+__device__ __forceinline__ uint64_t lane_lt() { return (uint64_t(1) << __lane_id()) - 1; }
+
+// Exact rank-k (1-based) (key, position) among key[0..n) (LDS) by one wave:
+// bitwise radix search on the key below the common prefix of its min / max,
+// then the k'-th position (in order) among the equal keys.
+__device__ uint2 wave_select(const uint32_t* key, int n, int k, int pos0) {
+  const int lane = __lane_id();
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int i = lane; i < n; i += 64) {
+    const uint32_t v = key[i];
+    mn = min(mn, v);
+    mx = max(mx, v);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+  }
+  uint32_t prefix = mn;
+  if (mn != mx) {
+    const int hb = 31 - __clz(mn ^ mx);
+    prefix = hb == 31 ? 0u : (mn & ~((2u << hb) - 1u));
+    for (int bit = hb; bit >= 0; --bit) {
+      const int above = bit + 1;
+      int c = 0;
+      for (int i = lane; i < n; i += 64) {
+        const uint32_t v = key[i];
+        c += ((uint64_t(v) >> above) == (uint64_t(prefix) >> above) && !((v >> bit) & 1u)) ? 1 : 0;
+      }
+      c = wave_sum_i(c);
+      if (k > c) {
+        k -= c;
+        prefix |= 1u << bit;
+      }
+    }
+  }
+  int run = 0, pos = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int i = base + lane;
+    const bool f = i < n && key[i] == prefix;
+    const uint64_t bal = __ballot(f);
+    const int cnt = __popcll(bal);
+    if (run + cnt >= k) {
+      const uint64_t mine = __ballot(f && __popcll(bal & lane_lt()) == k - run - 1);
+      pos = base + __ffsll((unsigned long long)mine) - 1;
+      break;
+    }
+    run += cnt;
+  }
+  return make_uint2(prefix, uint32_t(pos0 + pos));
+}
+
+template <int D>
+struct SubShared {
+  int pt[SUB_N];          // original token at local position
+  int tmp[SUB_N];
+  uint32_t key[SUB_N];
+  uint8_t side[SUB_N];
+  uint8_t sid[SUB_N];     // batch slot of the active segment owning a position (255: none)
+  float cen[MAXS][2][D];
+  float ssum[MAXS][2][D];
+  float wp[SUB_THREADS / 64][2][D];
+  int4 seg[MAXS];         // start, n, n_left
+  uint2 thr[MAXS];
+  int swc[MAXS];          // tokens that switched side this round
+  int done[MAXS];         // split reached a fixed point: later rounds repeat it exactly
+  int ndone;
+  int2 list[2][SUB_LIST];
+  int nlist[2];
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void subtree_kernel(const T* __restrict__ x, int32_t* perm,
+                                                              const int4* __restrict__ roots, int N,
+                                                              int L, int iters) {
+  using G = RowGeo<T, D>;
+  constexpr int NW = SUB_THREADS / 64;
+  constexpr int U = 4;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  SubShared<D>& S = *reinterpret_cast<SubShared<D>*>(smem);
+  const int h = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int4 root = roots[blockIdx.x];
+  if (ceil_div(root.y, L) < 2) return;  // a leaf already
+  const int start = root.x, n0 = root.y;
+  int32_t* ph = perm + size_t(h) * N + start;
+  const T* xh = x + size_t(h) * N * D;
+  for (int i = t; i < n0; i += SUB_THREADS) S.pt[i] = ph[i];
+  if (t == 0) {
+    S.list[0][0] = make_int2(0, n0);
+    S.nlist[0] = 1;
+  }
+  const int sub = lane % G::LPR, rsub = lane / G::LPR;
+  int cur = 0;
+  __syncthreads();
+  while (S.nlist[cur] > 0) {
+    const int nl_cur = S.nlist[cur];
+    if (t == 0) S.nlist[cur ^ 1] = 0;
+    for (int b0 = 0; b0 < nl_cur; b0 += MAXS) {
+      const int A = min(MAXS, nl_cur - b0);
+      __syncthreads();
+      for (int i = t; i < n0; i += SUB_THREADS) S.sid[i] = 255;
+      if (t < A) {
+        const int2 e = S.list[cur][b0 + t];
+        S.seg[t] = make_int4(e.x, e.y, L * ceil_div(ceil_div(e.y, L), 2), 0);
+        S.done[t] = 0;
+      }
+      __syncthreads();
+      for (int a = 0; a < A; ++a)
+        for (int i = t; i < S.seg[a].y; i += SUB_THREADS) S.sid[S.seg[a].x + i] = uint8_t(a);
+      for (int i = t; i < A * 2 * D; i += SUB_THREADS) {
+        const int a = i / (2 * D), sdx = (i / D) % 2, col = i % D;
+        S.cen[a][sdx][col] = to_f(xh[size_t(S.pt[S.seg[a].x + sdx]) * D + col]);
+      }
+      // waves per segment for the sums (A <= NW), else one wave loops over segments
+      const int wps = A <= NW ? NW / A : 1;
+      for (int it = 0; it < iters; ++it) {
+        __syncthreads();
+        if (t < A) S.swc[t] = 0;
+        // delta over every position of a segment still moving
+        {
+          constexpr int STEP = NW * G::RPW;
+          for (int rb = w * G::RPW; rb < n0; rb += U * STEP) {
+            int pp[U], sl[U];
+            uint4 raw[U];
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+              const int r = rb + q * STEP + rsub;
+              pp[q] = r < n0 ? r : 0;
+              sl[q] = r < n0 ? S.sid[pp[q]] : 255;
+              if (sl[q] != 255 && S.done[sl[q]]) sl[q] = 255;
+              raw[q] = sl[q] != 255 ? ld16(xh + size_t(S.pt[pp[q]]) * D + sub * G::EPV) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < U; ++q) {
+              float v[G::EPV];
+              unpack_vec<T, G::EPV>(raw[q], v);
+              const int a = sl[q] != 255 ? sl[q] : 0;
+              float acc = 0.f;
+#pragma unroll
+              for (int e = 0; e < G::EPV; ++e) {
+                const float c1 = S.cen[a][0][sub * G::EPV + e], c2 = S.cen[a][1][sub * G::EPV + e];
+                acc = fmaf(c2 - c1, fmaf(2.f, v[e], -(c1 + c2)), acc);
+              }
+#pragma unroll
+              for (int o = 1; o < G::LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
+              if (sl[q] != 255 && sub == 0) S.key[pp[q]] = sortable(acc);
+            }
+          }
+        }
+        __syncthreads();
+        for (int a = w; a < A; a += NW) {
+          if (S.done[a]) continue;
+          const int4 sg = S.seg[a];
+          const uint2 th = wave_select(S.key + sg.x, sg.y, sg.z, sg.x);
+          if (lane == 0) S.thr[a] = th;
+        }
+        __syncthreads();
+        if (it + 1 == iters) break;
+        // sums: round 0 both sides, later rounds the tokens that switched side
+        for (int a = (A <= NW ? w / wps : w); a < A; a += (A <= NW ? NW : NW)) {
+          const int part = A <= NW ? w % wps : 0;
+          const int nparts = A <= NW ? wps : 1;
+          if (S.done[a]) continue;
+          const int4 sg = S.seg[a];
+          const uint2 th = S.thr[a];
+          int nsw = 0;
+          float a0[G::EPV], a1[G::EPV];
+#pragma unroll
+          for (int e = 0; e < G::EPV; ++e) a0[e] = a1[e] = 0.f;
+          const int step = nparts * G::RPW;
+          constexpr int U2 = 2;
+          for (int rb = part * G::RPW; rb < sg.y; rb += U2 * step) {
+            uint4 raw[U2];
+            int sgn[U2];
+#pragma unroll
+            for (int q = 0; q < U2; ++q) {
+              const int r = rb + q * step + rsub;
+              sgn[q] = 0;
+              if (r < sg.y) {
+                const int p = sg.x + r;
+                const bool left = is_left(S.key[p], p, th);
+                if (it == 0) sgn[q] = left ? 1 : 2;
+                else if (left != (S.side[p] != 0)) sgn[q] = left ? 1 : -1;
+              }
+              nsw += (it > 0 && sgn[q] != 0 && sub == 0) ? 1 : 0;
+              raw[q] = sgn[q] != 0 ? ld16(xh + size_t(S.pt[sg.x + r]) * D + sub * G::EPV) : make_uint4(0, 0, 0, 0);
+            }
+#pragma unroll
+            for (int q = 0; q < U2; ++q) {
+              if (sgn[q] == 0) continue;
+              float v[G::EPV];
+              unpack_vec<T, G::EPV>(raw[q], v);
+              if (sgn[q] == 2) {
+#pragma unroll
+                for (int e = 0; e < G::EPV; ++e) a1[e] += v[e];
+              } else if (sgn[q] == 1) {
+#pragma unroll
+                for (int e = 0; e < G::EPV; ++e) a0[e] += v[e];
+              } else {
+#pragma unroll
+                for (int e = 0; e < G::EPV; ++e) a0[e] -= v[e];
+              }
+            }
+          }
+#pragma unroll
+          for (int o = G::LPR; o < 64; o <<= 1)
+#pragma unroll
+            for (int e = 0; e < G::EPV; ++e) {
+              a0[e] += __shfl_xor(a0[e], o, 64);
+              a1[e] += __shfl_xor(a1[e], o, 64);
+            }
+          nsw = wave_sum_i(nsw);
+          if (lane == 0 && nsw) atomicAdd(&S.swc[a], nsw);
+          if (A <= NW) {
+            if (rsub == 0)
+#pragma unroll
+              for (int e = 0; e < G::EPV; ++e) {
+                S.wp[w][0][sub * G::EPV + e] = a0[e];
+                S.wp[w][1][sub * G::EPV + e] = a1[e];
+              }
+          } else if (rsub == 0) {
+            // this wave alone owns segment a: update its sums and means now
+#pragma unroll
+            for (int e = 0; e < G::EPV; ++e) {
+              const int col = sub * G::EPV + e;
+              const float l = it == 0 ? a0[e] : S.ssum[a][0][col] + a0[e];
+              const float r = it == 0 ? a1[e] : S.ssum[a][1][col] - a0[e];
+              S.ssum[a][0][col] = l;
+              S.ssum[a][1][col] = r;
+              S.cen[a][0][col] = l / float(sg.z);
+              S.cen[a][1][col] = r / float(sg.y - sg.z);
+            }
+          }
+        }
+        __syncthreads();
+        if (A <= NW) {
+          for (int i = t; i < A * 2 * D; i += SUB_THREADS) {
+            const int a = i / (2 * D), sdx = (i / D) % 2, col = i % D;
+            if (S.done[a]) continue;
+            float acc = 0.f;
+            for (int j = 0; j < wps; ++j) acc += S.wp[a * wps + j][it == 0 ? sdx : 0][col];
+            const float tot = it == 0 ? acc : S.ssum[a][sdx][col] + (sdx == 0 ? acc : -acc);
+            S.ssum[a][sdx][col] = tot;
+            S.cen[a][sdx][col] = tot / float(sdx == 0 ? S.seg[a].z : S.seg[a].y - S.seg[a].z);
+          }
+        }
+        // sides of this round
+        for (int i = t; i < n0; i += SUB_THREADS) {
+          const int a = S.sid[i];
+          if (a != 255 && !S.done[a]) S.side[i] = is_left(S.key[i], i, S.thr[a]) ? 1 : 0;
+        }
+        __syncthreads();
+        // a round that moved no token fixes the split (and the means) for good
+        if (t == 0) {
+          int nd = 0;
+          for (int a = 0; a < A; ++a) {
+            if (it > 0 && !S.done[a] && S.swc[a] == 0) S.done[a] = 1;
+            nd += S.done[a];
+          }
+          S.ndone = nd;
+        }
+        __syncthreads();
+        if (S.ndone == A) break;
+      }
+      // stable partition of every active segment (one wave each)
+      for (int a = w; a < A; a += NW) {
+        const int4 sg = S.seg[a];
+        const uint2 th = S.thr[a];
+        int run_left = 0;
+        for (int base = 0; base < sg.y; base += 64) {
+          const int i = base + lane;
+          const bool valid = i < sg.y;
+          const int p = sg.x + i;
+          const bool left = valid && is_left(S.key[p], p, th);
+          const uint64_t bal = __ballot(left);
+          const int pre = __popcll(bal & lane_lt()) + run_left;
+          if (valid) S.tmp[left ? sg.x + pre : sg.x + sg.z + (i - pre)] = S.pt[p];
+          run_left += __popcll(bal);
+        }
+      }
+      __syncthreads();
+      for (int a = 0; a < A; ++a)
+        for (int i = t; i < S.seg[a].y; i += SUB_THREADS) S.pt[S.seg[a].x + i] = S.tmp[S.seg[a].x + i];
+      if (t == 0) {
+        int k = S.nlist[cur ^ 1];
+        for (int a = 0; a < A; ++a) {
+          const int4 sg = S.seg[a];
+          if (ceil_div(sg.z, L) >= 2) S.list[cur ^ 1][k++] = make_int2(sg.x, sg.z);
+          if (ceil_div(sg.y - sg.z, L) >= 2) S.list[cur ^ 1][k++] = make_int2(sg.x + sg.z, sg.y - sg.z);
+        }
+        S.nlist[cur ^ 1] = k;
+      }
+    }
+    cur ^= 1;
+    __syncthreads();
+  }
+  __syncthreads();
+  for (int i = t; i < n0; i += SUB_THREADS) ph[i] = S.pt[i];
 }
 
 __global__ void leaf_offsets_kernel(int32_t* off, int H, int C, int N, int L) {
@@ -464,77 +1085,101 @@ __global__ void leaf_offsets_kernel(int32_t* off, int H, int C, int N, int L) {
 }
 
 template <typename T, int D>
-hipError_t run_levels(const void* xv, int H, int N, int L, int iters, const TreePlan& P, int4* segs,
-                      int4* chunks, int32_t* pa, int32_t* pb, uint32_t* keys, float* cen,
-                      uint2* thr, float* part, int32_t** final_perm, hipStream_t st) {
+hipError_t run_bisect(const void* xv, int H, int N, int L, int iters, const TreePlan& P, int4* segs,
+                      int4* chunks, int32_t* pa, int32_t* pb, TopBufs b, hipStream_t st) {
   const T* x = (const T*)xv;
+  const size_t sub_lds = sizeof(SubShared<D>);
+  if (hipFuncSetAttribute((const void*)subtree_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          int(sub_lds)) != hipSuccess)
+    return hipErrorInvalidValue;
+  int32_t* cur = pa;
+  int32_t* nxt = pb;
   for (int lv = 0; lv < P.t.nlev; ++lv) {
-    const int4* sg = segs + P.t.sb[lv];
-    const int4* ck = chunks + P.t.cb[lv];
+    b.segs = segs + P.t.sb[lv];
+    b.chunks = chunks + P.t.cb[lv];
+    b.perm = cur;
     const dim3 gs(P.t.nseg[lv], H), gc(P.t.nchunk[lv], H);
     for (int it = 0; it < iters; ++it) {
-      delta_kernel<T, D><<<gc, 256, 0, st>>>(x, pa, sg, ck, cen, P.max_seg, N, it == 0, keys);
-      select_kernel<<<gs, 1024, 0, st>>>(keys, sg, P.max_seg, N, thr);
+      delta_kernel<T, D><<<gc, 256, 0, st>>>(x, b, it == 0);
+      b.round = it;
+      select_kernel<<<gs, 1024, 0, st>>>(b);
       if (it + 1 < iters) {
-        sums_kernel<T, D><<<gc, 256, 0, st>>>(x, pa, keys, ck, thr, P.max_seg, P.max_chunk, N, part);
-        update_kernel<D><<<gs, D, 0, st>>>(sg, part, P.max_seg, P.max_chunk, cen);
+        if (it == 0) {
+          sums_kernel<T, D, true><<<gc, 256, 0, st>>>(x, b);
+          update_kernel<D, true><<<gs, 256, 0, st>>>(b);
+        } else {
+          sums_kernel<T, D, false><<<gc, 256, 0, st>>>(x, b);
+          update_kernel<D, false><<<gs, 256, 0, st>>>(b);
+        }
       }
     }
-    partition_kernel<<<gs, 1024, 0, st>>>(pa, pb, keys, sg, thr, P.max_seg, N);
-    int32_t* tmp = pa;
-    pa = pb;
-    pb = tmp;
+    partition_kernel<<<gs, 1024, 0, st>>>(b, cur, nxt);
+    int32_t* tmp = cur;
+    cur = nxt;
+    nxt = tmp;
   }
-  *final_perm = pa;
+  const int nroots = P.t.nseg[P.t.nlev];
+  subtree_kernel<T, D><<<dim3(nroots, H), SUB_THREADS, sub_lds, st>>>(x, cur, segs + P.t.sb[P.t.nlev], N, L,
+                                                                     iters);
   return hipGetLastError();
 }
 
 }  // namespace
 
 size_t bisect_scratch(int H, int N, int d, int leaf) {
-  const TreePlan P = plan_tree(N, leaf);
+  const TreePlan P = plan_tree(N, leaf, SUB_N);
   Arena a{nullptr, 0, 0};
-  a.get<int4>(size_t(max(P.total_seg, 1)));
-  a.get<int4>(size_t(max(P.total_chunk, 1)));
-  a.get<int32_t>(size_t(H) * N);  // ping
-  a.get<int32_t>(size_t(H) * N);  // pong
+  a.get<int4>(size_t(P.total_seg));
+  a.get<int4>(size_t(P.total_chunk + 1));
+  a.get<int32_t>(size_t(H) * N);   // ping-pong partner of perm_out
   a.get<uint32_t>(size_t(H) * N);  // keys
-  a.get<float>(size_t(H) * max(P.max_seg, 1) * 2 * d);
-  a.get<uint2>(size_t(H) * max(P.max_seg, 1));
-  a.get<float>(size_t(H) * max(P.max_chunk, 1) * 2 * d);
+  a.get<uint8_t>(size_t(H) * N);   // side
+  a.get<float>(size_t(H) * P.max_seg * 2 * d);   // cen
+  a.get<float>(size_t(H) * P.max_seg * 2 * d);   // ssum
+  a.get<uint2>(size_t(H) * P.max_seg);
+  a.get<float>(size_t(H) * P.max_chunk * 2 * d);
+  a.get<int32_t>(size_t(H) * P.max_seg);
+  a.get<uint2>(size_t(H) * P.max_seg);
   return a.used;
 }
 
 hipError_t bisect_run(const void* x, int dtype, int H, int N, int d, int leaf, int iters,
                       int32_t* perm_out, int32_t* offsets_out, Arena& s, hipStream_t st) {
-  const TreePlan P = plan_tree(N, leaf);
-  int4* segs = s.get<int4>(size_t(max(P.total_seg, 1)));
-  int4* chunks = s.get<int4>(size_t(max(P.total_chunk, 1)));
+  const TreePlan P = plan_tree(N, leaf, SUB_N);
+  int4* segs = s.get<int4>(size_t(P.total_seg));
+  int4* chunks = s.get<int4>(size_t(P.total_chunk + 1));
   int32_t* other = s.get<int32_t>(size_t(H) * N);
-  (void)s.get<int32_t>(size_t(H) * N);
-  uint32_t* keys = s.get<uint32_t>(size_t(H) * N);
-  float* cen = s.get<float>(size_t(H) * max(P.max_seg, 1) * 2 * d);
-  uint2* thr = s.get<uint2>(size_t(H) * max(P.max_seg, 1));
-  float* part = s.get<float>(size_t(H) * max(P.max_chunk, 1) * 2 * d);
-  // ping-pong so that the last level writes perm_out
+  TopBufs b{};
+  b.keys = s.get<uint32_t>(size_t(H) * N);
+  b.side = s.get<uint8_t>(size_t(H) * N);
+  b.cen = s.get<float>(size_t(H) * P.max_seg * 2 * d);
+  b.ssum = s.get<float>(size_t(H) * P.max_seg * 2 * d);
+  b.thr = s.get<uint2>(size_t(H) * P.max_seg);
+  b.part = s.get<float>(size_t(H) * P.max_chunk * 2 * d);
+  b.cnt = s.get<int32_t>(size_t(H) * P.max_seg);
+  b.segmm = s.get<uint2>(size_t(H) * P.max_seg);
+  b.max_seg = P.max_seg;
+  b.max_chunk = P.max_chunk;
+  b.N = N;
+  // ping-pong so that the last top level writes perm_out (the subtree phase
+  // then works in place)
   int32_t* pa = (P.t.nlev % 2 == 0) ? perm_out : other;
   int32_t* pb = (P.t.nlev % 2 == 0) ? other : perm_out;
   iota_kernel<<<dim3(ceil_div(N, 256), H), 256, 0, st>>>(pa, N);
-  int32_t* fin = pa;
-  hipError_t e = hipSuccess;
-  if (P.t.nlev > 0) {
-    build_tree_kernel<<<1, 1024, 0, st>>>(P.t, N, leaf, segs, chunks);
-    if (dtype == SA_F32 && d == 64)
-      e = run_levels<float, 64>(x, H, N, leaf, iters, P, segs, chunks, pa, pb, keys, cen, thr, part, &fin, st);
-    else if (dtype == SA_F32 && d == 128)
-      e = run_levels<float, 128>(x, H, N, leaf, iters, P, segs, chunks, pa, pb, keys, cen, thr, part, &fin, st);
-    else if (dtype == SA_BF16 && d == 64)
-      e = run_levels<bf16_t, 64>(x, H, N, leaf, iters, P, segs, chunks, pa, pb, keys, cen, thr, part, &fin, st);
-    else
-      e = run_levels<bf16_t, 128>(x, H, N, leaf, iters, P, segs, chunks, pa, pb, keys, cen, thr, part, &fin, st);
-  }
+  const size_t ncnt = size_t(H) * P.max_seg;
+  zero_i32<<<unsigned((ncnt + 255) / 256), 256, 0, st>>>(b.cnt, ncnt);
+  init_minmax<<<unsigned((ncnt + 255) / 256), 256, 0, st>>>(b.segmm, ncnt);
+  build_tree_kernel<<<1, 1024, 0, st>>>(P.t, N, segs, chunks);
+  hipError_t e;
+  if (dtype == SA_F32 && d == 64)
+    e = run_bisect<float, 64>(x, H, N, leaf, iters, P, segs, chunks, pa, pb, b, st);
+  else if (dtype == SA_F32 && d == 128)
+    e = run_bisect<float, 128>(x, H, N, leaf, iters, P, segs, chunks, pa, pb, b, st);
+  else if (dtype == SA_BF16 && d == 64)
+    e = run_bisect<bf16_t, 64>(x, H, N, leaf, iters, P, segs, chunks, pa, pb, b, st);
+  else
+    e = run_bisect<bf16_t, 128>(x, H, N, leaf, iters, P, segs, chunks, pa, pb, b, st);
   if (e != hipSuccess) return e;
-  if (fin != perm_out) return hipErrorUnknown;  // ping-pong parity is fixed above
   const int C = ceil_div(N, leaf);
   leaf_offsets_kernel<<<dim3(ceil_div(C + 1, 256), H), 256, 0, st>>>(offsets_out, H, C, N, leaf);
   return hipGetLastError();

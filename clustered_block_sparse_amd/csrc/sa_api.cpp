@@ -55,7 +55,7 @@ sa_status check_cluster_cfg(const sa_problem* p, const sa_cluster_cfg* c) {
       if (c->clusters > p->n) return SA_ERR_SHAPE;
       return SA_OK;
     case SA_BISECT:
-      if (c->leaf < 2) return SA_ERR_INVALID_ARG;
+      if (c->leaf < 4) return SA_ERR_INVALID_ARG;
       if (c->init != SA_INIT_FIRST) return SA_ERR_INVALID_ARG;
       if (ceil_div(p->n, c->leaf) > 65536) return SA_ERR_SHAPE;
       return SA_OK;

@@ -81,7 +81,7 @@ typedef struct sa_problem {
 typedef struct sa_cluster_cfg {
   int32_t method;      /* SA_KMEANS | SA_BISECT | SA_SUBSPACE                       */
   int32_t clusters;    /* KMEANS: C (1..1024, <= n); SUBSPACE: per-slice C (<= 32)  */
-  int32_t leaf;        /* BISECT leaf size (>= 2)                                   */
+  int32_t leaf;        /* BISECT leaf size (>= 4)                                   */
   int32_t tile_cap;    /* upper bound on query rows per attention tile (tiling
                           only, never changes results; 0 = 128)                    */
   int32_t iters;       /* rounds per k-means run / per bisection node (>= 1)        */
