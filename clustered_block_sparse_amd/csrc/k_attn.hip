@@ -42,6 +42,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int KT = 64;      // keys per tile
 constexpr int TQ = 128;     // query rows per workgroup (upper bound)
 constexpr int RCH = 512;    // ranges staged in LDS at a time
+constexpr int ALIGNED_MAX_CK = 4096;  // key clusters up to which rows get precomputed ranges
 constexpr float LOG2E = 1.4426950408889634f;
 
 struct Prep {
@@ -101,6 +102,11 @@ __global__ __launch_bounds__(64) void ranges_kernel(const uint32_t* __restrict__
     rcount[size_t(h) * Cq + i] = ns;
     raligned[size_t(h) * Cq + i] = any_mis ? 0 : 1;
   }
+}
+
+__global__ void fill_zero_kernel(int32_t* p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
 }
 
 __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__ q_off, int Cq,
@@ -211,6 +217,80 @@ __device__ int stage_ranges(const int2* __restrict__ rg, int c0, int nrc, int* r
   return rp[nrc];
 }
 
+// Stage the next selected key clusters of a row, in cluster order, straight
+// from its mask bits: rs[k] = first key position of the k-th staged cluster,
+// rp[k] = keys staged before it (rp[n] = total).  Wave 0 scans 16 mask words
+// (512 clusters) at a time while they fit in RCH entries; `word` is the scan
+// position, shared through sh[0].  Returns the number of clusters staged (0:
+// the row is exhausted).  Called by the whole block.
+__device__ int fill_chunk(const uint32_t* __restrict__ mr, int W, int Ck, const int32_t* __restrict__ ko,
+                          int* rs, int* rp, int* wsum, int* sh) {
+  const int t = threadIdx.x, lane = t & 63;
+  if (t < 64) {
+    int word = sh[0];
+    int nr = 0;
+    while (word < W) {
+      uint32_t bits = 0;
+      const int wi = word + lane;
+      if (lane < 16 && wi < W) {
+        bits = mr[wi];
+        const int rem = Ck - 32 * wi;
+        if (rem < 32) bits &= (1u << rem) - 1u;
+      }
+      int c = __popc(bits);
+      int x = c;
+      for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o, 64);
+        if (lane >= o) x += y;
+      }
+      const int blk = __shfl(x, 63, 64);
+      if (nr + blk > RCH) break;
+      int slot = nr + x - c;
+      while (bits) {
+        const int b = __ffs(bits) - 1;
+        bits &= bits - 1;
+        const int j = 32 * wi + b;
+        rs[slot] = ko[j];
+        rp[slot] = ko[j + 1] - ko[j];
+        ++slot;
+      }
+      nr += blk;
+      word += 16;
+    }
+    if (lane == 0) {
+      sh[0] = word;
+      sh[1] = nr;
+    }
+  }
+  __syncthreads();
+  const int nrc = sh[1];
+  // lengths -> exclusive prefix (block scan over nrc entries)
+  const int lane2 = t & 63, w = t >> 6, nw = blockDim.x >> 6;
+  int carry = 0;
+  for (int b = 0; b < nrc; b += blockDim.x) {
+    const int k = b + t;
+    const int len = k < nrc ? rp[k] : 0;
+    int x = len;
+    for (int o = 1; o < 64; o <<= 1) {
+      int y = __shfl_up(x, o, 64);
+      if (lane2 >= o) x += y;
+    }
+    if (lane2 == 63) wsum[w] = x;
+    __syncthreads();
+    int pre = carry, tot = 0;
+    for (int j = 0; j < nw; ++j) {
+      if (j < w) pre += wsum[j];
+      tot += wsum[j];
+    }
+    if (k < nrc) rp[k] = pre + x - len;
+    carry += tot;
+    __syncthreads();
+  }
+  if (t == 0) rp[nrc] = carry;
+  __syncthreads();
+  return nrc;
+}
+
 // key row of concatenated position `pos`, advancing a cursor over rp[]
 __device__ __forceinline__ int cursor_row(const int* rs, const int* rp, int nrc, int pos, int& cur) {
   while (cur + 1 < nrc && rp[cur + 1] <= pos) ++cur;
@@ -226,6 +306,7 @@ __global__ __launch_bounds__(128) void attn_simple(AttnArgs a, Prep p, float sca
   __shared__ float Vs[32][D];
   __shared__ int rs[RCH + 1], rp[RCH + 1];
   __shared__ int wsum[16];
+  __shared__ int fsh[2];
   __shared__ float bias[32];
   int h, tix;
   map_tile(p.maxT, a.H, h, tix);
@@ -245,8 +326,8 @@ __global__ __launch_bounds__(128) void attn_simple(AttnArgs a, Prep p, float sca
   float m = -__builtin_huge_valf(), l = 0.f;
   const T* kh = (const T*)a.k_perm + size_t(h) * N * D;
   const T* vh = (const T*)a.v_perm + size_t(h) * N * D;
-  const int R = p.rcount[size_t(h) * a.Cq + i];
-  const int2* rg = p.ranges + (size_t(h) * a.Cq + i) * p.Rmax;
+  const uint32_t* mrow = a.mask + (size_t(h) * a.Cq + i) * p.W;
+  const int32_t* kof = a.k_off + size_t(h) * (a.Ck + 1);
   auto consume = [&](int nk, const float* bs) {
     for (int kk = 0; kk < nk; ++kk) {
       float s = 0.f;
@@ -267,10 +348,15 @@ __global__ __launch_bounds__(128) void attn_simple(AttnArgs a, Prep p, float sca
       for (int c = 0; c < D; ++c) o[c] = fmaf(pr, Vs[kk][c], o[c]);
     }
   };
-  for (int c0 = 0; c0 < R; c0 += RCH) {
-    const int nrc = min(RCH, R - c0);
+  int scan_word = 0;  // mask scan position
+  while (true) {
     __syncthreads();
-    const int total = stage_ranges(rg, c0, nrc, rs, rp, wsum);
+    if (t == 0) fsh[0] = scan_word;
+    __syncthreads();
+    const int nrc = fill_chunk(mrow, p.W, a.Ck, kof, rs, rp, wsum, fsh);
+    scan_word = fsh[0];
+    if (nrc == 0) break;
+    const int total = rp[nrc];
     for (int base = 0; base < total; base += 32) {
       const int nk = min(32, total - base);
       __syncthreads();
@@ -278,7 +364,7 @@ __global__ __launch_bounds__(128) void attn_simple(AttnArgs a, Prep p, float sca
         const int kk = v / D, c = v % D;
         float kv = 0.f, vv = 0.f;
         if (kk < nk) {
-          // binary search the range of position base+kk
+          // binary search the cluster of position base+kk
           const int pos = base + kk;
           int lo = 0, hi = nrc - 1;
           while (lo < hi) {
@@ -351,6 +437,7 @@ struct MfmaLds {
   int rs[RCH + 1];
   int rp[RCH + 1];
   int wsum[16];
+  int fsh[2];
   float bias[KT];
 };
 
@@ -525,10 +612,9 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sl
     *reinterpret_cast<uint2*>(dst + 4) = make_uint2(u.z, u.w);
   };
 
-  const int R = p.rcount[size_t(h) * a.Cq + i];
-  const int2* rg = p.ranges + (size_t(h) * a.Cq + i) * p.Rmax;
-
   if constexpr (ALIGNED) {
+    const int R = p.rcount[size_t(h) * a.Cq + i];
+    const int2* rg = p.ranges + (size_t(h) * a.Cq + i) * p.Rmax;
     // ---------------- selected keys, 64-aligned ranges: whole-block tiles ----
     const bf16_t* vth = p.vt + size_t(h) * p.NB * D * KT;
     uint4 kreg[CK], vreg[CK];
@@ -602,10 +688,17 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sl
         }
       }
     };
-    for (int c0 = 0; c0 < R; c0 += RCH) {
-      const int nrc = min(RCH, R - c0);
+    const uint32_t* mrow = a.mask + (size_t(h) * a.Cq + i) * p.W;
+    const int32_t* kof = a.k_off + size_t(h) * (a.Ck + 1);
+    int scan_word = 0;
+    while (true) {
       __syncthreads();
-      const int total = stage_ranges(rg, c0, nrc, S.rs, S.rp, S.wsum);
+      if (tid == 0) S.fsh[0] = scan_word;
+      __syncthreads();
+      const int nrc = fill_chunk(mrow, p.W, a.Ck, kof, S.rs, S.rp, S.wsum, S.fsh);
+      scan_word = S.fsh[0];
+      if (nrc == 0) break;
+      const int total = S.rp[nrc];
       const int ntile = ceil_div(total, KT);
       int cur_k = 0, cur_v = 0;
       auto load_tile = [&](int tt) {
@@ -712,13 +805,13 @@ Prep carve(const AttnArgs& a, Arena& s) {
   Prep p{};
   const int rows = a.tile_rows;
   p.maxT = a.max_tiles > 0 ? a.max_tiles : a.N / rows + a.Cq + 1;
-  p.Rmax = a.Ck / 2 + 1;
+  p.Rmax = a.Ck <= ALIGNED_MAX_CK ? a.Ck / 2 + 1 : 0;
   p.Ckp = ceil_div(a.Ck, KT) * KT;
   p.W = ceil_div(a.Ck, 32);
   p.NB = ceil_div(a.N, KT);
   p.tiles = s.get<int4>(size_t(a.H) * p.maxT);
   p.ntiles = s.get<int32_t>(size_t(a.H));
-  p.ranges = s.get<int2>(size_t(a.H) * a.Cq * p.Rmax);
+  p.ranges = p.Rmax ? s.get<int2>(size_t(a.H) * a.Cq * p.Rmax) : nullptr;
   p.rcount = s.get<int32_t>(size_t(a.H) * a.Cq);
   p.raligned = s.get<int32_t>(size_t(a.H) * a.Cq);
   if (a.dtype == SA_BF16) p.vt = s.get<bf16_t>(size_t(a.H) * p.NB * KT * a.d);
@@ -757,8 +850,11 @@ size_t attn_scratch(int H, int N, int d, int Cq, int Ck, int tile_rows, int comp
 
 hipError_t attn_run(const AttnArgs& a, Arena& s, hipStream_t st) {
   const Prep p = carve(a, s);
-  ranges_kernel<<<dim3(a.Cq, a.H), 64, 0, st>>>(a.mask, a.k_off, a.Cq, a.Ck, p.W, p.Rmax, a.N,
-                                                p.ranges, p.rcount, p.raligned);
+  if (p.Rmax)
+    ranges_kernel<<<dim3(a.Cq, a.H), 64, 0, st>>>(a.mask, a.k_off, a.Cq, a.Ck, p.W, p.Rmax, a.N,
+                                                  p.ranges, p.rcount, p.raligned);
+  else
+    fill_zero_kernel<<<ceil_div(a.H * a.Cq, 256), 256, 0, st>>>(p.raligned, a.H * a.Cq);
   tiles_kernel<<<a.H, 1024, 0, st>>>(a.q_off, a.Cq, a.tile_rows, p.maxT, p.tiles, p.ntiles);
   if (a.compensate)
     comp_prep_kernel<<<dim3(p.Ckp, a.H), 128, 0, st>>>(a.kbar, a.vbar, a.k_off, a.Ck, p.Ckp, a.d,
@@ -769,11 +865,11 @@ hipError_t attn_run(const AttnArgs& a, Arena& s, hipStream_t st) {
     const dim3 gv(p.NB, a.H);
     if (a.d == 128) {
       vt_kernel<128><<<gv, 256, 0, st>>>((const bf16_t*)a.v_perm, a.N, p.NB, p.vt);
-      attn_mfma<128, true><<<grid, 256, 0, st>>>(a, p, sl2);
+      if (p.Rmax) attn_mfma<128, true><<<grid, 256, 0, st>>>(a, p, sl2);
       attn_mfma<128, false><<<grid, 256, 0, st>>>(a, p, sl2);
     } else {
       vt_kernel<64><<<gv, 256, 0, st>>>((const bf16_t*)a.v_perm, a.N, p.NB, p.vt);
-      attn_mfma<64, true><<<grid, 256, 0, st>>>(a, p, sl2);
+      if (p.Rmax) attn_mfma<64, true><<<grid, 256, 0, st>>>(a, p, sl2);
       attn_mfma<64, false><<<grid, 256, 0, st>>>(a, p, sl2);
     }
   } else {

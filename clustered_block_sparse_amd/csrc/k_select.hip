@@ -226,21 +226,334 @@ __global__ __launch_bounds__(256) void select_rows(SelectArgs a, unsigned long l
   }
 }
 
+// --------------------------------------------------------------------------
+// SCOPE subspace keys: lookup-table scores over combos, selection in keys
+// --------------------------------------------------------------------------
+// SCOPE (technical framework, key design): T_s[i][c] = <qbar_i|_s, kbar^s_c>
+// scale for each of the t/h/w slices; a combo g = (a_t, a_h, a_w) scores
+// T_t[a_t] + T_h[a_h] + T_w[a_w] (+ ln|g|), and the selection counts keys.
+// Rank order is (logit descending, combo ascending); the boundary of every
+// cumulative target (mass, floor keys, online Top-k keys) is found by an exact
+// weighted radix search over 64-bit order keys, masses in 2^-52 fixed point
+// so their sums are exact and order independent.
+constexpr int SUB_T = 1024;
+constexpr double MASS_ONE = 4503599627370496.0;  // 2^52
+
+struct SubRow {
+  double T[3][32];
+  unsigned long long hw[2048];   // radix bin weights (mass or keys)
+  unsigned long long wsum[16];
+  unsigned long long red[2][16];
+  double dred[16];
+  uint32_t words[1024];
+  int sel_bin;
+  unsigned long long sel_w;
+  int tie_g;
+};
+
+__device__ __forceinline__ unsigned long long order_key(double l) {
+  // ascending order of the key = descending logit
+  unsigned long long u = __double_as_longlong(l + 0.0);
+  u = (u & 0x8000000000000000ull) ? ~u : (u | 0x8000000000000000ull);
+  return ~u;
+}
+
+// A position in rank order: every combo with a smaller order key, or the same
+// key and g' <= g, lies at or before it.  g = -1: before every combo; g = C:
+// past every combo.
+struct Boundary {
+  unsigned long long key;
+  int g;
+};
+
+__device__ __forceinline__ bool before_or_at(unsigned long long k, int g, const Boundary& b) {
+  return k < b.key || (k == b.key && g <= b.g);
+}
+
+template <typename V>
+__device__ V bscan(V v, V* wsum, V& total) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, nw = blockDim.x >> 6;
+  V x = v;
+  for (int o = 1; o < 64; o <<= 1) {
+    V y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
+  __syncthreads();
+  V pre = 0, tot = 0;
+  for (int j = 0; j < nw; ++j) {
+    if (j < w) pre += wsum[j];
+    tot += wsum[j];
+  }
+  total = tot;
+  __syncthreads();
+  return pre + x - v;
+}
+
+// First combo (in rank order) at which the cumulative weight reaches `target`
+// (WK = 0: mass, 1: keys); g = C when the total stays below the target.
+// Radix rounds of up to 11 bits narrow the order key from the top; combos
+// sharing the final key are then taken in ascending g.
+template <int WK, typename Eval>
+__device__ Boundary wselect(Eval ev, int C, unsigned long long target, unsigned long long kmin,
+                            unsigned long long kmax, SubRow& R) {
+  const int t = threadIdx.x;
+  unsigned long long prefix = kmin, rem = target;
+  int hb = kmin == kmax ? -1 : 63 - __clzll(kmin ^ kmax);
+  if (hb >= 0) prefix = hb == 63 ? 0ull : (kmin & ~((2ull << hb) - 1ull));
+  while (hb >= 0) {
+    const int shift = max(hb - 10, 0);
+    const int width = hb - shift + 1;
+    const unsigned long long dmask = (1ull << width) - 1ull;
+    const int above = shift + width;
+    for (int b = t; b < 2048; b += SUB_T) R.hw[b] = 0ull;
+    __syncthreads();
+    for (int g = t; g < C; g += SUB_T) {
+      unsigned long long k, mass, keys;
+      if (!ev(g, k, mass, keys)) continue;
+      if (above < 64 && (k >> above) != (prefix >> above)) continue;
+      atomicAdd(&R.hw[int((k >> shift) & dmask)], WK == 0 ? mass : keys);
+    }
+    __syncthreads();
+    const unsigned long long w0 = R.hw[2 * t], w1 = R.hw[2 * t + 1];
+    unsigned long long tw;
+    const unsigned long long pw = bscan<unsigned long long>(w0 + w1, R.wsum, tw);
+    if (t == 0) R.sel_bin = -1;
+    __syncthreads();
+    if (pw < rem && rem <= pw + w0) {
+      R.sel_bin = 2 * t;
+      R.sel_w = pw;
+    } else if (pw + w0 < rem && rem <= pw + w0 + w1) {
+      R.sel_bin = 2 * t + 1;
+      R.sel_w = pw + w0;
+    }
+    __syncthreads();
+    const int sb = R.sel_bin;
+    const unsigned long long sw = R.sel_w;
+    __syncthreads();
+    if (sb < 0) return Boundary{0ull, C};  // target beyond the total: everything
+    rem -= sw;
+    prefix |= (unsigned long long)sb << shift;
+    if (shift == 0) break;
+    hb = shift - 1;
+  }
+  // ties on the order key: combos in ascending order
+  unsigned long long run = 0;
+  if (t == 0) R.tie_g = -1;
+  __syncthreads();
+  int tg = -1;
+  for (int base = 0; base < C; base += SUB_T) {
+    const int g = base + t;
+    unsigned long long k = 0, mass = 0, keys = 0;
+    const bool f = g < C && ev(g, k, mass, keys) && k == prefix;
+    const unsigned long long wv = f ? (WK == 0 ? mass : keys) : 0ull;
+    unsigned long long tot;
+    const unsigned long long pre = bscan<unsigned long long>(wv, R.wsum, tot);
+    if (f && run + pre < rem && rem <= run + pre + wv) R.tie_g = g;
+    __syncthreads();
+    tg = R.tie_g;
+    __syncthreads();
+    if (tg >= 0) break;
+    run += tot;
+  }
+  // the total weight of the key reaches rem, so a combo is always found
+  return Boundary{prefix, tg};
+}
+
+__device__ __forceinline__ bool later(const Boundary& a, const Boundary& b, int C) {
+  // is boundary a later in rank order than b (C = past every combo)?
+  if (a.g == C) return b.g != C;
+  if (b.g == C) return false;
+  return a.key > b.key || (a.key == b.key && a.g > b.g);
+}
+
+__global__ void logsize_kernel(const int32_t* __restrict__ k_off, int C, double* __restrict__ lg) {
+  const int h = blockIdx.y;
+  const int g = blockIdx.x * 256 + threadIdx.x;
+  if (g >= C) return;
+  const int sz = k_off[size_t(h) * (C + 1) + g + 1] - k_off[size_t(h) * (C + 1) + g];
+  lg[size_t(h) * C + g] = sz > 0 ? log(double(sz)) : -__builtin_huge_val();
+}
+
+__global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const double* __restrict__ lgs,
+                                                         unsigned long long* __restrict__ acc,
+                                                         int pass) {
+  __shared__ SubRow R;
+  const int i = blockIdx.x, h = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int Cq = a.Cq, C = a.Ck, Cs = a.Cs, d = a.d;
+  const int W = ceil_div(C, 32);
+  const size_t row = size_t(h) * Cq + i;
+  const int32_t* qo = a.q_off + size_t(h) * (Cq + 1);
+  const int qsize = qo[i + 1] - qo[i];
+  const bool online = a.online != 0;
+  if (qsize == 0) {
+    if (!online || pass == 1) {
+      for (int x = t; x < W; x += SUB_T) a.mask[row * W + x] = 0u;
+      if (t == 0) {
+        a.counts[row] = 0;
+        if (a.init_counts) a.init_counts[row] = 0;
+        if (i == 0) a.head_topk[h] = online ? int(((long long)acc[h] + a.N - 1) / a.N) : 0;
+      }
+    } else if (t == 0 && a.init_counts) {
+      a.init_counts[row] = 0;
+    }
+    return;
+  }
+  // lookup tables
+  if (t < 3 * Cs) {
+    const int sl = t / Cs, c = t % Cs;
+    const int off = sl == 0 ? 0 : (sl == 1 ? a.dims[0] : a.dims[0] + a.dims[1]);
+    const float* qb = a.qbar + row * d;
+    const float* cb = a.kbar + (size_t(h) * 3 * Cs + sl * Cs + c) * d;
+    double sdot = 0.0;
+    for (int col = off; col < off + a.dims[sl]; ++col) sdot = fma(double(qb[col]), double(cb[col]), sdot);
+    R.T[sl][c] = sdot * a.scale;
+  }
+  __syncthreads();
+  const int32_t* ko = a.k_off + size_t(h) * (C + 1);
+  const double* lh = lgs + size_t(h) * C;
+  const int Cs2 = Cs * Cs;
+  auto logit = [&](int g, double& l) -> bool {
+    const double ls = lh[g];
+    if (ls == -__builtin_huge_val()) return false;
+    l = (R.T[0][g / Cs2] + R.T[1][(g / Cs) % Cs]) + R.T[2][g % Cs];
+    if (a.weighted) l += ls;
+    return true;
+  };
+  // max logit, normaliser, order-key range
+  double mx = -__builtin_huge_val(), mn = __builtin_huge_val();
+  for (int g = t; g < C; g += SUB_T) {
+    double l;
+    if (logit(g, l)) {
+      mx = fmax(mx, l);
+      mn = fmin(mn, l);
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    mx = fmax(mx, __shfl_xor(mx, o, 64));
+    mn = fmin(mn, __shfl_xor(mn, o, 64));
+  }
+  if (lane == 0) {
+    R.red[0][w] = __double_as_longlong(mx);
+    R.red[1][w] = __double_as_longlong(mn);
+  }
+  __syncthreads();
+  mx = __longlong_as_double(R.red[0][0]);
+  mn = __longlong_as_double(R.red[1][0]);
+  for (int j = 1; j < SUB_T / 64; ++j) {
+    mx = fmax(mx, __longlong_as_double(R.red[0][j]));
+    mn = fmin(mn, __longlong_as_double(R.red[1][j]));
+  }
+  __syncthreads();
+  double zs = 0.0;
+  for (int g = t; g < C; g += SUB_T) {
+    double l;
+    if (logit(g, l)) zs += exp(l - mx);
+  }
+  for (int o = 32; o > 0; o >>= 1) zs += __shfl_xor(zs, o, 64);
+  if (lane == 0) R.dred[w] = zs;
+  __syncthreads();
+  double Z = 0.0;
+  for (int j = 0; j < SUB_T / 64; ++j) Z += R.dred[j];
+  __syncthreads();
+  const unsigned long long kmin = order_key(mx), kmax = order_key(mn);
+  auto ev = [&](int g, unsigned long long& k, unsigned long long& mass, unsigned long long& keys) -> bool {
+    double l;
+    if (!logit(g, l)) return false;
+    k = order_key(l);
+    mass = (unsigned long long)llrint(exp(l - mx) / Z * MASS_ONE);
+    keys = (unsigned long long)(ko[g + 1] - ko[g]);
+    return true;
+  };
+  const int Cfull = C;
+  const Boundary b0{0ull, -1};  // before every combo
+  Boundary bp = b0, bf = b0;
+  const double P = a.top_p;
+  if (P >= 1.0) {
+    bp = Boundary{0ull, Cfull};
+  } else if (P > 0.0) {
+    bp = wselect<0>(ev, C, (unsigned long long)llrint(P * MASS_ONE), kmin, kmax, R);
+  }
+  if (a.floor_units > 0) bf = wselect<1>(ev, C, (unsigned long long)a.floor_units, kmin, kmax, R);
+  auto keys_through = [&](const Boundary& b) -> long long {
+    // keys of every combo up to and including the boundary: the predicate
+    // the mask is built from, so counts and mask agree by construction
+    if (b.g < 0) return 0;
+    unsigned long long sk = 0;
+    for (int g = t; g < C; g += SUB_T) {
+      double l;
+      if (!logit(g, l)) continue;
+      if (b.g == Cfull || before_or_at(order_key(l), g, b)) sk += (unsigned long long)(ko[g + 1] - ko[g]);
+    }
+    unsigned long long tot;
+    bscan<unsigned long long>(sk, R.wsum, tot);
+    return (long long)tot;
+  };
+  const Boundary binit = (bp.g < 0) ? bf : (bf.g < 0 ? bp : (later(bf, bp, Cfull) ? bf : bp));
+  const long long n_init = keys_through(binit);
+  if (online && pass == 0) {
+    if (t == 0) {
+      atomicAdd(&acc[h], (unsigned long long)((long long)qsize * n_init));
+      if (a.init_counts) a.init_counts[row] = int(n_init);
+    }
+    return;
+  }
+  Boundary bfin = binit;
+  int kh = 0;
+  if (online) {
+    const long long A = (long long)acc[h];
+    kh = int((A + a.N - 1) / a.N);
+    if (n_init < kh) {
+      const Boundary bk = wselect<1>(ev, C, (unsigned long long)kh, kmin, kmax, R);
+      if (binit.g < 0 || later(bk, binit, Cfull)) bfin = bk;
+    }
+  }
+  const long long n_fin = keys_through(bfin);
+  for (int x = t; x < W; x += SUB_T) R.words[x] = 0u;
+  __syncthreads();
+  if (bfin.g >= 0) {
+    for (int g = t; g < C; g += SUB_T) {
+      unsigned long long k, m2, ky;
+      if (!ev(g, k, m2, ky)) continue;
+      if (bfin.g == Cfull || before_or_at(k, g, bfin)) atomicOr(&R.words[g >> 5], 1u << (g & 31));
+    }
+  }
+  __syncthreads();
+  for (int x = t; x < W; x += SUB_T) a.mask[row * W + x] = R.words[x];
+  if (t == 0) {
+    a.counts[row] = int(n_fin);
+    if (a.init_counts) a.init_counts[row] = int(n_init);
+    if (i == 0) a.head_topk[h] = kh;
+  }
+}
+
 }  // namespace
 
 size_t select_scratch(int H, int Cq, int Ck, int subspace) {
   (void)Cq;
-  (void)Ck;
-  (void)subspace;
   Arena a{nullptr, 0, 0};
   a.get<unsigned long long>(size_t(H));
+  if (subspace) a.get<double>(size_t(H) * Ck);
   return a.used;
 }
 
 hipError_t select_run(const SelectArgs& a, Arena& s, hipStream_t st) {
-  if (a.subspace || a.Ck > SEL_MAX || a.d > 128) return hipErrorInvalidValue;
   unsigned long long* acc = s.get<unsigned long long>(size_t(a.H));
   dim3 g(a.Cq, a.H);
+  if (a.subspace) {
+    if (a.Cs > 32) return hipErrorInvalidValue;
+    double* lgs = s.get<double>(size_t(a.H) * a.Ck);
+    logsize_kernel<<<dim3(ceil_div(a.Ck, 256), a.H), 256, 0, st>>>(a.k_off, a.Ck, lgs);
+    if (a.online) {
+      zero_u64<<<ceil_div(a.H, 256), 256, 0, st>>>(acc, a.H);
+      select_subspace<<<g, SUB_T, 0, st>>>(a, lgs, acc, 0);
+      select_subspace<<<g, SUB_T, 0, st>>>(a, lgs, acc, 1);
+    } else {
+      select_subspace<<<g, SUB_T, 0, st>>>(a, lgs, acc, 0);
+    }
+    return hipGetLastError();
+  }
+  if (a.Ck > SEL_MAX || a.d > 128) return hipErrorInvalidValue;
   if (a.online) {
     zero_u64<<<ceil_div(a.H, 256), 256, 0, st>>>(acc, a.H);
     select_rows<<<g, 256, 0, st>>>(a, acc, 0);

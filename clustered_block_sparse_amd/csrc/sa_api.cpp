@@ -356,9 +356,12 @@ SA_API sa_status sa_select(const sa_problem* p, const sa_select_cfg* cfg, const 
   if ((st = check_select_cfg(cfg)) != SA_OK) return st;
   if (!clusters_ok(q, false) || !clusters_ok(k, false) || !mask || !counts || !head_topk || !ws)
     return SA_ERR_INVALID_ARG;
-  if (k->method == SA_SUBSPACE) return SA_ERR_UNSUPPORTED;
-  if (k->num_clusters > SELECT_MAX) return SA_ERR_UNSUPPORTED;
-  if (ws_bytes < select_scratch(p->heads, q->num_clusters, k->num_clusters, 0) + 256)
+  const int sub = k->method == SA_SUBSPACE;
+  if (sub && (k->sub_clusters < 1 || k->sub_clusters > SUB_MAX ||
+              k->sub_dims[0] + k->sub_dims[1] + k->sub_dims[2] != p->d))
+    return SA_ERR_INVALID_ARG;
+  if (!sub && k->num_clusters > SELECT_MAX) return SA_ERR_UNSUPPORTED;
+  if (ws_bytes < select_scratch(p->heads, q->num_clusters, k->num_clusters, sub) + 256)
     return SA_ERR_WORKSPACE;
   Arena s{(char*)ws, ws_bytes, 0};
   return do_select(p, cfg, q, k, mask, counts, init_counts, head_topk, s, (hipStream_t)stream);
@@ -398,8 +401,8 @@ SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
   if (!(acfg->scale >= 0.f) || !isfinite(acfg->scale)) return SA_ERR_INVALID_ARG;
   if (qcfg->method == SA_SUBSPACE) return SA_ERR_INVALID_ARG;
   if (qcfg->init != SA_INIT_FIRST || kcfg->init != SA_INIT_FIRST) return SA_ERR_INVALID_ARG;
-  if (kcfg->method == SA_SUBSPACE) return SA_ERR_UNSUPPORTED;
-  if (clusters_of(p, kcfg) > SELECT_MAX) return SA_ERR_UNSUPPORTED;
+  if (kcfg->method == SA_SUBSPACE && acfg->compensate) return SA_ERR_UNSUPPORTED;
+  if (kcfg->method != SA_SUBSPACE && clusters_of(p, kcfg) > SELECT_MAX) return SA_ERR_UNSUPPORTED;
   size_t used = 0;
   carve_forward(p, qcfg, kcfg, acfg, nullptr, &used);
   if (ws_bytes < used) return SA_ERR_WORKSPACE;
