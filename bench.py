@@ -1,18 +1,28 @@
 """Benchmark: one clustered block-sparse attention layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan|hy|tab|mid]
+                    [--natural] [--no-cpu-baseline] [--no-dense] [--copy-probe]
 
-Workload: a Wan-2.1-14B-720p-shaped attention layer (40 heads, 21x45x80 =
-75600 tokens, d = 128, bf16; smooth-field + 3D-RoPE queries/keys, Gaussian
-values), balanced bisection into 128-token clusters for queries and keys,
-mean compensation on, at fixed 10% density (Top-k of 59 of 591 key clusters
-per query cluster, Top-p off).  A step is one sa_forward call: cluster Q and
-K, permute V, score + select, block-sparse attention (+ compensation,
-+ unpermute).  Inputs are resident in HBM before timing starts.
+Default workload: a Wan-2.1-14B-720p-shaped attention layer (40 heads,
+21x45x80 = 75600 tokens, d = 128, bf16; smooth-field + 3D-RoPE queries/keys,
+Gaussian values), balanced bisection into 128-token clusters for queries and
+keys, mean compensation on, at fixed 10% density (Top-k of 59 of 591 key
+clusters per query cluster, Top-p off).  `--workload hy` runs the
+HunyuanVideo-720p-shaped layer (24 x 118800 x 128, key subspace clustering,
+lookup-table scores, floor of 10% of the keys), `tab` the unstructured
+tabular-shaped tokens (6 x 131072 x 64), `mid` the 8 x 10800 x 128 k-means
+layer; `--natural` uses the workload's own Top-p (and online Top-k) instead of
+the fixed density.
 
-Prints one JSON line with the headline metric (effective sparse-attention
-TFLOP/s over the whole step), ms per layer, the dense comparison, the
-attention kernel's roofline figure and the oracle's CPU timing.
+A step is one sa_forward call: cluster Q and K, permute V, score + select,
+block-sparse attention (+ compensation, + unpermute).  Inputs are resident in
+HBM before timing starts.  Prints one JSON line: the headline metric
+(effective sparse-attention TFLOP/s over the whole step), ms per layer, a
+per-stage breakdown, the dense comparison, the attention kernels' roofline
+figure (their own duration, from HIP events the library records around them
+on the launch stream) and the oracle's CPU timing on a bounded sample.
+`--copy-probe` finishes with three 1 GiB device copies of known size, the
+calibration for hardware byte counters.
 """
 
 from __future__ import annotations
@@ -33,7 +43,14 @@ from clustered_block_sparse_amd import workloads as wl
 
 METRIC = "effective sparse-attn TFLOP/s + ms per layer vs dense at fixed density, 1 MI355X"
 BF16_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 MFMA (256 CU x 4096 flop/clk x 2.4 GHz)
-HBM_PEAK_GBS = 8000.0
+FP32_PEAK_TFLOPS = 157.3
+
+WORKLOADS = {
+    "wan": (wl.WAN, "wan2.1-14b-720p-shaped attention layer"),
+    "hy": (wl.HUNYUAN, "hunyuanvideo-720p-shaped attention layer, key subspace clustering + lookup-table scores"),
+    "tab": (wl.TABULAR, "tabular-transformer-shaped tokens, gaussian mixture, no positional structure"),
+    "mid": (wl.MID, "mid-size video layer 9x30x40, k-means clusters"),
+}
 
 
 def effective_flops(mask_bits: torch.Tensor, q_off: torch.Tensor, k_off: torch.Tensor, d: int) -> float:
@@ -41,8 +58,16 @@ def effective_flops(mask_bits: torch.Tensor, q_off: torch.Tensor, k_off: torch.T
     4 |Q_i| |K_j| d (real tokens only)."""
     qs = (q_off[:, 1:] - q_off[:, :-1]).double()          # [H, Cq]
     ks = (k_off[:, 1:] - k_off[:, :-1]).double()          # [H, Ck]
-    sel_keys = torch.einsum("hij,hj->hi", mask_bits.double(), ks)
+    sel_keys = torch.bmm(mask_bits.double(), ks.unsqueeze(-1)).squeeze(-1)
     return float(4.0 * d * (qs * sel_keys).sum())
+
+
+def compensation_flops(mask_bits: torch.Tensor, q_off: torch.Tensor, k_off: torch.Tensor, d: int) -> float:
+    """4 d per (query token, excluded non-empty key cluster) pair."""
+    qs = (q_off[:, 1:] - q_off[:, :-1]).double()
+    nonempty = ((k_off[:, 1:] - k_off[:, :-1]) > 0).double()
+    excl = nonempty.sum(-1, keepdim=True) - torch.bmm(mask_bits.double(), nonempty.unsqueeze(-1)).squeeze(-1)
+    return float(4.0 * d * (qs * excl).sum())
 
 
 def unpack_bits(words: torch.Tensor, Ck: int) -> torch.Tensor:
@@ -71,32 +96,44 @@ class Timer:
         return [a.elapsed_time(b) for a, b in self.ev]
 
 
-def cpu_baseline(w, q, k, v, heads=1):
-    """The fp64 oracle on `heads` head(s) of the same inputs, scaled to the
-    metric's unit (effective TFLOP/s of those heads)."""
-    import oracle
+def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
-    qc = oracle.ClusterCfg(method=w.q.method, clusters=w.q.clusters, leaf=w.q.leaf, iters=w.q.iters)
-    kc = oracle.ClusterCfg(method=w.k.method, clusters=w.k.clusters, leaf=w.k.leaf, iters=w.k.iters)
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(w, q, k, v, budget_s=10.0):
+    """The fp64 oracle on whole heads of the same inputs, one head after the
+    other until `budget_s` seconds have passed, scaled to the metric's unit
+    (effective TFLOP/s of those heads)."""
+    import oracle
+    qc, kc = (oracle.ClusterCfg(method=c.method, clusters=c.clusters, leaf=c.leaf, iters=c.iters,
+                                sub_dims=tuple(c.sub_dims), sub_clusters=c.clusters) for c in (w.q, w.k))
     sc = oracle.SelectCfg(top_p=w.top_p, floor=w.floor, online_topk=w.online_topk, size_weighted=w.size_weighted)
     flops = 0.0
+    heads = 0
     t0 = time.perf_counter()
-    for h in range(heads):
-        qs = q[h].double().cpu().numpy()
-        ks = k[h].double().cpu().numpy()
-        vs = v[h].double().cpu().numpy()
+    while heads < w.heads and time.perf_counter() - t0 < budget_s:
+        h = heads
+        qs, ks, vs = (t[h].double().cpu().numpy() for t in (q, k, v))
         r = oracle.forward_head(qs, ks, vs, qc, kc, sc, compensate=w.compensate)
         qsz = np.diff(r.q["offsets"]).astype(np.float64)
         ksz = np.diff(r.k["offsets"]).astype(np.float64)
         flops += 4.0 * w.d * float((qsz[:, None] * r.mask * ksz[None, :]).sum())
+        heads += 1
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{heads} of {w.heads} heads of the same layer (fp64 NumPy oracle: bisection, "
-                      f"selection, attention with compensation), {dt:.1f} s"}
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"{heads} of {w.heads} heads of the same layer and inputs (fp64 NumPy oracle: clustering, "
+                      f"selection, attention{' with compensation' if w.compensate else ''}), {dt:.1f} s"}
+
+
+def describe(name, w, natural, density):
+    base = WORKLOADS[name][1]
+    if natural:
+        return f"{base}, top-p {w.top_p}" + (", online per-head top-k" if w.online_topk else "")
+    return f"{base}, fixed {100 * density:g}% density"
 
 
 def main():
@@ -104,26 +141,29 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="wan")
+    ap.add_argument("--natural", action="store_true", help="the workload's own top-p instead of fixed density")
+    ap.add_argument("--density", type=float, default=0.1)
+    ap.add_argument("--heads", type=int, default=0, help="override the head count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
-    ap.add_argument("--density", type=float, default=0.1)
-    ap.add_argument("--heads", type=int, default=0, help="override head count (default: the workload's 40)")
+    ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported (heads shard across GPUs "
-              f"with no exchange; see the design notes)", file=sys.stderr)
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported here (every step is per head, so "
+              f"heads shard across GPUs with no exchange inside the layer)", file=sys.stderr)
         sys.exit(2)
-    torch.manual_seed(0)
     dev = "cuda"
-    w = wl.WAN.forced_density(args.density)
+    base = WORKLOADS[args.workload][0]
+    w = base if args.natural else base.forced_density(args.density)
     if args.heads:
         w = w.with_heads(args.heads)
     L.load()
     t_gen = time.perf_counter()
     q, k, v = wl.make_inputs(w, device=dev)
     torch.cuda.synchronize()
-    print(f"# inputs {tuple(q.shape)} {q.dtype} generated in {time.perf_counter() - t_gen:.1f}s", file=sys.stderr,
-          flush=True)
+    print(f"# {w.name}: inputs {tuple(q.shape)} {q.dtype} generated in {time.perf_counter() - t_gen:.1f}s",
+          file=sys.stderr, flush=True)
 
     p, qc, kc, sc, ac = api.cfgs(w)
     ws = L.workspace(L.sa_workspace_size(p, qc, kc, sc, ac), dev)
@@ -136,19 +176,24 @@ def main():
 
     for _ in range(args.warmup):
         step()
+    probes = [(L.HipEvent(), L.HipEvent()) for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        L.sa_set_attn_events(*probes[i])
         step()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    print(f"# sa_forward {ms_step:.3f} ms/layer", file=sys.stderr, flush=True)
+    L.sa_set_attn_events(None, None)
+    attn_kernel_ms = [a.elapsed_ms(b) for a, b in probes]
+    print(f"# sa_forward {ms_step:.3f} ms/layer, attention kernels {np.mean(attn_kernel_ms):.3f} ms",
+          file=sys.stderr, flush=True)
 
     # --- per-stage breakdown with the component calls (same kernels, same launch configs)
     qt = L.alloc_clusters(p, qc, dev, q.dtype)
     kt = L.alloc_clusters(p, kc, dev, k.dtype)
     v_perm = torch.empty_like(v)
-    vbar = torch.empty(w.heads, Ck, w.d, dtype=torch.float32, device=dev)
+    vbar = torch.empty(w.heads, Ck, w.d, dtype=torch.float32, device=dev) if w.compensate else None
     counts = torch.empty(w.heads, Cq, dtype=torch.int32, device=dev)
     ktop = torch.empty(w.heads, dtype=torch.int32, device=dev)
     mask2 = torch.empty_like(mask)
@@ -161,7 +206,7 @@ def main():
     for fn in stages.values():
         fn()
     timers = {n: Timer() for n in stages}
-    reps = max(3, args.steps)
+    reps = max(3, min(args.steps, 10))
     for _ in range(reps):
         for n, fn in stages.items():
             timers[n].start()
@@ -173,10 +218,13 @@ def main():
 
     bits = unpack_bits(mask2, Ck)
     eff = effective_flops(bits, qt.offsets, kt.offsets, w.d)
-    density = float(bits.double().mean())
+    comp = compensation_flops(bits, qt.offsets, kt.offsets, w.d) if w.compensate else 0.0
     dense_flops = 4.0 * w.d * w.n * w.n * w.heads
-    attn_ms = stage_ms["attention"]
+    density = eff / dense_flops
+    del bits
+    attn_ms = float(np.mean(attn_kernel_ms))
     attn_tf = eff / (attn_ms * 1e-3) / 1e12
+    fp32 = w.dtype == "f32"
 
     # --- dense comparisons
     dense_own = dense_sdpa = None
@@ -192,6 +240,7 @@ def main():
             L.sa_block_sparse_attn(p, ac0, qt, kt, v_perm, None, full, o2, ws)
             t.stop()
         dense_own = float(np.mean(t.ms()))
+        del full
         try:
             sdpa = torch.nn.functional.scaled_dot_product_attention
             qq, kk, vv = q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0)
@@ -204,12 +253,27 @@ def main():
             dense_sdpa = float(np.mean(t.ms()))
         except Exception as e:  # pragma: no cover
             print(f"# sdpa unavailable: {e}", file=sys.stderr)
-    dense_best = min(x for x in (dense_own, dense_sdpa) if x is not None) if (dense_own or dense_sdpa) else None
+    dense_list = [x for x in (dense_own, dense_sdpa) if x is not None]
+    dense_best = min(dense_list) if dense_list else None
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, q, k, v, heads=1)
+        cpu = cpu_baseline(w, q, k, v)
 
+    if args.copy_probe:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"# copy probe: 3 copies of {src.numel() * 2} bytes", file=sys.stderr, flush=True)
+
+    cfg = {"workload": describe(args.workload, w, args.natural, args.density),
+           "heads": w.heads, "n": w.n, "d": w.d, "grid": [w.frames, w.height, w.width],
+           "clustering": f"q {w.q.method} / k {w.k.method}",
+           "query_clusters": Cq, "key_clusters": Ck,
+           "top_p": w.top_p, "topk_floor": w.floor, "online_topk": w.online_topk,
+           "compensation": w.compensate, "density": density}
     line = {
         "metric": METRIC,
         "value": eff / (ms_step * 1e-3) / 1e12,
@@ -221,24 +285,25 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "f32" if fp32 else "bf16",
         "data": "synthetic",
-        "config": {"workload": "wan2.1-14b-720p-shaped attention layer, fixed 10% density",
-                   "heads": w.heads, "n": w.n, "d": w.d, "grid": [w.frames, w.height, w.width],
-                   "clustering": "bisect leaf 128 (q, k)", "key_clusters": Ck, "topk": w.floor,
-                   "compensation": w.compensate, "density": density},
+        "config": cfg,
         "ms_per_layer": ms_step,
         "effective_flops": eff,
+        "compensation_flops": comp,
         "stage_ms": stage_ms,
+        "attention_kernel_ms": attn_ms,
         "attention_tflops": attn_tf,
         "dense_ms_own_kernel": dense_own,
         "dense_ms_torch_sdpa": dense_sdpa,
         "speedup_vs_dense": (dense_best / ms_step) if dense_best else None,
         "dense_equiv_tflops": dense_flops / (ms_step * 1e-3) / 1e12,
         "forward_matches_components": same,
-        "roofline": {"bound": "mfma", "achieved": attn_tf, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": attn_tf / BF16_PEAK_TFLOPS, "traffic": None,
-                     "kernel": "attn_mfma<128> (timed with its prep kernels)"},
+        "roofline": {"bound": "mfma", "achieved": attn_tf,
+                     "peak": FP32_PEAK_TFLOPS if fp32 else BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": attn_tf / (FP32_PEAK_TFLOPS if fp32 else BF16_PEAK_TFLOPS), "traffic": None,
+                     "kernel": "attention kernels (attn_mfma aligned + general instantiations), selected-block "
+                               "flops over their event-timed duration per launch"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

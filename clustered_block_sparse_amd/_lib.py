@@ -85,10 +85,11 @@ def load():
                                          vp, ctypes.c_size_t, vp]
     lib.sa_forward.argtypes = [P(Problem), P(ClusterCfg), P(ClusterCfg), P(SelectCfg), P(AttnCfg), vp, vp,
                                vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.sa_set_attn_events.argtypes = [vp, vp]
     lib.sa_status_string.argtypes = [I32]
     lib.sa_status_string.restype = ctypes.c_char_p
     for fn in ("sa_workspace_size", "sa_cluster", "sa_permute", "sa_select", "sa_block_sparse_attn",
-               "sa_forward"):
+               "sa_forward", "sa_set_attn_events"):
         getattr(lib, fn).restype = I32
     _lib = lib
     return lib
@@ -223,6 +224,47 @@ def sa_forward(p: Problem, qcfg: ClusterCfg, kcfg: ClusterCfg, scfg: SelectCfg, 
     _check("sa_forward", load().sa_forward(ctypes.byref(p), ctypes.byref(qcfg), ctypes.byref(kcfg),
                                            ctypes.byref(scfg), ctypes.byref(acfg), _ptr(q), _ptr(k), _ptr(v),
                                            _ptr(o), _ptr(mask), _ptr(ws), ws.numel(), _stream()))
+
+
+def sa_set_attn_events(start: "HipEvent | None", stop: "HipEvent | None"):
+    _check("sa_set_attn_events", load().sa_set_attn_events(start.handle if start else None,
+                                                           stop.handle if stop else None))
+
+
+class HipEvent:
+    """A raw hipEvent_t of the HIP runtime this process already runs (the one
+    libsa.so and torch share), for sa_set_attn_events."""
+
+    _hip = None
+
+    def __init__(self):
+        if HipEvent._hip is None:
+            load()
+            HipEvent._hip = ctypes.CDLL("libamdhip64.so.7")
+            HipEvent._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                          ctypes.c_void_p]
+            HipEvent._hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            HipEvent._hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        h = ctypes.c_void_p()
+        err = HipEvent._hip.hipEventCreate(ctypes.byref(h))
+        if err != 0:
+            raise RuntimeError(f"hipEventCreate failed ({err})")
+        self.handle = h
+
+    def elapsed_ms(self, stop: "HipEvent") -> float:
+        """Milliseconds from this event to `stop` (waits for `stop`)."""
+        hip = HipEvent._hip
+        if hip.hipEventSynchronize(stop.handle) != 0:
+            raise RuntimeError("hipEventSynchronize failed")
+        ms = ctypes.c_float()
+        err = hip.hipEventElapsedTime(ctypes.byref(ms), self.handle, stop.handle)
+        if err != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({err})")
+        return float(ms.value)
+
+    def __del__(self):
+        if HipEvent._hip is not None and getattr(self, "handle", None):
+            HipEvent._hip.hipEventDestroy(self.handle)
 
 
 def mask_words(num_key_clusters: int) -> int:

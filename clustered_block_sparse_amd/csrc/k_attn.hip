@@ -848,6 +848,15 @@ size_t attn_scratch(int H, int N, int d, int Cq, int Ck, int tile_rows, int comp
   return s.used;
 }
 
+namespace {
+hipEvent_t g_probe_start = nullptr, g_probe_stop = nullptr;
+}
+
+void attn_set_probe(hipEvent_t start, hipEvent_t stop) {
+  g_probe_start = start;
+  g_probe_stop = stop;
+}
+
 hipError_t attn_run(const AttnArgs& a, Arena& s, hipStream_t st) {
   const Prep p = carve(a, s);
   if (p.Rmax)
@@ -860,15 +869,21 @@ hipError_t attn_run(const AttnArgs& a, Arena& s, hipStream_t st) {
     comp_prep_kernel<<<dim3(p.Ckp, a.H), 128, 0, st>>>(a.kbar, a.vbar, a.k_off, a.Ck, p.Ckp, a.d,
                                                        p.kbh, p.kbl, p.vbt, p.kbf, p.vbf, p.logsz);
   const int grid = 8 * ceil_div(p.maxT * a.H, 8);
+  const float sl2 = a.scale * LOG2E;
+  const dim3 gv(p.NB, a.H);
   if (a.dtype == SA_BF16) {
-    const float sl2 = a.scale * LOG2E;
-    const dim3 gv(p.NB, a.H);
-    if (a.d == 128) {
+    if (a.d == 128)
       vt_kernel<128><<<gv, 256, 0, st>>>((const bf16_t*)a.v_perm, a.N, p.NB, p.vt);
+    else
+      vt_kernel<64><<<gv, 256, 0, st>>>((const bf16_t*)a.v_perm, a.N, p.NB, p.vt);
+  }
+  // the probe events bracket the attention kernels only (prep excluded)
+  if (g_probe_start) (void)hipEventRecord(g_probe_start, st);
+  if (a.dtype == SA_BF16) {
+    if (a.d == 128) {
       if (p.Rmax) attn_mfma<128, true><<<grid, 256, 0, st>>>(a, p, sl2);
       attn_mfma<128, false><<<grid, 256, 0, st>>>(a, p, sl2);
     } else {
-      vt_kernel<64><<<gv, 256, 0, st>>>((const bf16_t*)a.v_perm, a.N, p.NB, p.vt);
       if (p.Rmax) attn_mfma<64, true><<<grid, 256, 0, st>>>(a, p, sl2);
       attn_mfma<64, false><<<grid, 256, 0, st>>>(a, p, sl2);
     }
@@ -878,6 +893,7 @@ hipError_t attn_run(const AttnArgs& a, Arena& s, hipStream_t st) {
     else
       attn_simple<float, 64><<<grid, 128, 0, st>>>(a, p, a.scale);
   }
+  if (g_probe_stop) (void)hipEventRecord(g_probe_stop, st);
   return hipGetLastError();
 }
 

@@ -781,59 +781,10 @@ constexpr int SUB_LIST = 512;  // active segments per level (leaf >= 4)
 
 __device__ __forceinline__ uint64_t lane_lt() { return (uint64_t(1) << __lane_id()) - 1; }
 
-// Exact rank-k (1-based) (key, position) among key[0..n) (LDS) by one wave:
-// bitwise radix search on the key below the common prefix of its min / max,
-// then the k'-th position (in order) among the equal keys.
-__device__ uint2 wave_select(const uint32_t* key, int n, int k, int pos0) {
-  const int lane = __lane_id();
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int i = lane; i < n; i += 64) {
-    const uint32_t v = key[i];
-    mn = min(mn, v);
-    mx = max(mx, v);
-  }
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
-    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
-  }
-  uint32_t prefix = mn;
-  if (mn != mx) {
-    const int hb = 31 - __clz(mn ^ mx);
-    prefix = hb == 31 ? 0u : (mn & ~((2u << hb) - 1u));
-    for (int bit = hb; bit >= 0; --bit) {
-      const int above = bit + 1;
-      int c = 0;
-      for (int i = lane; i < n; i += 64) {
-        const uint32_t v = key[i];
-        c += ((uint64_t(v) >> above) == (uint64_t(prefix) >> above) && !((v >> bit) & 1u)) ? 1 : 0;
-      }
-      c = wave_sum_i(c);
-      if (k > c) {
-        k -= c;
-        prefix |= 1u << bit;
-      }
-    }
-  }
-  int run = 0, pos = 0;
-  for (int base = 0; base < n; base += 64) {
-    const int i = base + lane;
-    const bool f = i < n && key[i] == prefix;
-    const uint64_t bal = __ballot(f);
-    const int cnt = __popcll(bal);
-    if (run + cnt >= k) {
-      const uint64_t mine = __ballot(f && __popcll(bal & lane_lt()) == k - run - 1);
-      pos = base + __ffsll((unsigned long long)mine) - 1;
-      break;
-    }
-    run += cnt;
-  }
-  return make_uint2(prefix, uint32_t(pos0 + pos));
-}
-
 template <int D>
 struct SubShared {
   int pt[SUB_N];          // original token at local position
-  int tmp[SUB_N];
+  int tmp[SUB_N];         // partition target; also select histograms and switcher lists
   uint32_t key[SUB_N];
   uint8_t side[SUB_N];
   uint8_t sid[SUB_N];     // batch slot of the active segment owning a position (255: none)
@@ -842,12 +793,96 @@ struct SubShared {
   float wp[SUB_THREADS / 64][2][D];
   int4 seg[MAXS];         // start, n, n_left
   uint2 thr[MAXS];
+  uint32_t spre[MAXS];    // radix select: key digits fixed so far
+  int srank[MAXS];        // rank still sought among keys with that prefix
+  int scnt[MAXS];         // keys equal to the selected key
   int swc[MAXS];          // tokens that switched side this round
   int done[MAXS];         // split reached a fixed point: later rounds repeat it exactly
   int ndone;
   int2 list[2][SUB_LIST];
   int nlist[2];
 };
+
+// For every active segment a of the batch: the rank-n_left (1-based)
+// (key, position) pair, i.e. the split threshold.  All threads: four radix
+// passes of 8-bit digits with per-segment LDS histograms (aliasing tmp), then
+// the position among equal keys (a block sweep when the key is unique, else
+// an ordered scan by one wave).
+template <int D>
+__device__ void subtree_select(SubShared<D>& S, int A, int n0) {
+  constexpr int NW = SUB_THREADS / 64;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int(*hist)[256] = reinterpret_cast<int(*)[256]>(S.tmp);
+  if (t < A) {
+    S.spre[t] = 0u;
+    S.srank[t] = S.seg[t].z;
+  }
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int i = t; i < A * 256; i += SUB_THREADS) hist[i >> 8][i & 255] = 0;
+    __syncthreads();
+    for (int i = t; i < n0; i += SUB_THREADS) {
+      const int a = S.sid[i];
+      if (a == 255 || S.done[a]) continue;
+      const uint32_t k = S.key[i];
+      if (pass > 0 && (k >> (shift + 8)) != (S.spre[a] >> (shift + 8))) continue;
+      atomicAdd(&hist[a][(k >> shift) & 255], 1);
+    }
+    __syncthreads();
+    for (int a = w; a < A; a += NW) {
+      if (S.done[a]) continue;
+      int c[4], cs = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        c[j] = hist[a][lane * 4 + j];
+        cs += c[j];
+      }
+      int incl = cs;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+      }
+      int run = incl - cs;
+      const int k = S.srank[a];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (run < k && k <= run + c[j]) {
+          S.spre[a] |= uint32_t(lane * 4 + j) << shift;
+          S.srank[a] = k - run;
+          if (pass == 3) S.scnt[a] = c[j];
+        }
+        run += c[j];
+      }
+    }
+    __syncthreads();
+  }
+  // position of the srank-th equal key (in position order)
+  for (int i = t; i < n0; i += SUB_THREADS) {
+    const int a = S.sid[i];
+    if (a == 255 || S.done[a] || S.scnt[a] != 1) continue;
+    if (S.key[i] == S.spre[a]) S.thr[a] = make_uint2(S.spre[a], uint32_t(i));
+  }
+  for (int a = w; a < A; a += NW) {
+    if (S.done[a] || S.scnt[a] == 1) continue;
+    const int4 sg = S.seg[a];
+    const uint32_t K = S.spre[a];
+    const int k = S.srank[a];
+    int run = 0;
+    for (int base = 0; base < sg.y; base += 64) {
+      const int i = base + lane;
+      const bool f = i < sg.y && S.key[sg.x + i] == K;
+      const uint64_t bal = __ballot(f);
+      const int cnt = __popcll(bal);
+      if (run + cnt >= k) {
+        const uint64_t mine = __ballot(f && __popcll(bal & lane_lt()) == k - run - 1);
+        if (lane == 0) S.thr[a] = make_uint2(K, uint32_t(sg.x + base + __ffsll((unsigned long long)mine) - 1));
+        break;
+      }
+      run += cnt;
+    }
+  }
+  __syncthreads();
+}
 
 template <typename T, int D>
 __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void subtree_kernel(const T* __restrict__ x, int32_t* perm,
@@ -928,13 +963,7 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
           }
         }
         __syncthreads();
-        for (int a = w; a < A; a += NW) {
-          if (S.done[a]) continue;
-          const int4 sg = S.seg[a];
-          const uint2 th = wave_select(S.key + sg.x, sg.y, sg.z, sg.x);
-          if (lane == 0) S.thr[a] = th;
-        }
-        __syncthreads();
+        subtree_select<D>(S, A, n0);
         if (it + 1 == iters) break;
         // sums: round 0 both sides, later rounds the tokens that switched side
         for (int a = (A <= NW ? w / wps : w); a < A; a += (A <= NW ? NW : NW)) {
@@ -947,39 +976,90 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
           float a0[G::EPV], a1[G::EPV];
 #pragma unroll
           for (int e = 0; e < G::EPV; ++e) a0[e] = a1[e] = 0.f;
-          const int step = nparts * G::RPW;
-          constexpr int U2 = 2;
-          for (int rb = part * G::RPW; rb < sg.y; rb += U2 * step) {
-            uint4 raw[U2];
-            int sgn[U2];
+          if (it == 0) {
+            // both sides in full
+            const int step = nparts * G::RPW;
+            constexpr int U2 = 2;
+            for (int rb = part * G::RPW; rb < sg.y; rb += U2 * step) {
+              uint4 raw[U2];
+              bool lf[U2], ok[U2];
 #pragma unroll
-            for (int q = 0; q < U2; ++q) {
-              const int r = rb + q * step + rsub;
-              sgn[q] = 0;
-              if (r < sg.y) {
-                const int p = sg.x + r;
-                const bool left = is_left(S.key[p], p, th);
-                if (it == 0) sgn[q] = left ? 1 : 2;
-                else if (left != (S.side[p] != 0)) sgn[q] = left ? 1 : -1;
+              for (int q = 0; q < U2; ++q) {
+                const int r = rb + q * step + rsub;
+                ok[q] = r < sg.y;
+                lf[q] = ok[q] && is_left(S.key[sg.x + r], sg.x + r, th);
+                raw[q] = ok[q] ? ld16(xh + size_t(S.pt[sg.x + r]) * D + sub * G::EPV) : make_uint4(0, 0, 0, 0);
               }
-              nsw += (it > 0 && sgn[q] != 0 && sub == 0) ? 1 : 0;
-              raw[q] = sgn[q] != 0 ? ld16(xh + size_t(S.pt[sg.x + r]) * D + sub * G::EPV) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+              for (int q = 0; q < U2; ++q) {
+                if (!ok[q]) continue;
+                float v[G::EPV];
+                unpack_vec<T, G::EPV>(raw[q], v);
+                if (lf[q]) {
+#pragma unroll
+                  for (int e = 0; e < G::EPV; ++e) a0[e] += v[e];
+                } else {
+#pragma unroll
+                  for (int e = 0; e < G::EPV; ++e) a1[e] += v[e];
+                }
+              }
             }
-#pragma unroll
-            for (int q = 0; q < U2; ++q) {
-              if (sgn[q] == 0) continue;
-              float v[G::EPV];
-              unpack_vec<T, G::EPV>(raw[q], v);
-              if (sgn[q] == 2) {
-#pragma unroll
-                for (int e = 0; e < G::EPV; ++e) a1[e] += v[e];
-              } else if (sgn[q] == 1) {
-#pragma unroll
-                for (int e = 0; e < G::EPV; ++e) a0[e] += v[e];
-              } else {
-#pragma unroll
-                for (int e = 0; e < G::EPV; ++e) a0[e] -= v[e];
+          } else {
+            // only the tokens that switched side: compact their positions (in
+            // position order) into this wave's list, then load the rows with
+            // every load of a batch in flight
+            int* wl = S.tmp + w * 128;
+            int nl = 0;
+            for (int base = part * 64;; base += nparts * 64) {
+              const bool more = base < sg.y;
+              if (more) {
+                const int r = base + lane;
+                const int p = sg.x + r;
+                const bool f = r < sg.y && (is_left(S.key[p], p, th) != (S.side[p] != 0));
+                const uint64_t bal = __ballot(f);
+                if (f) wl[nl + __popcll(bal & lane_lt())] = p;
+                nl += __popcll(bal);
               }
+              if (nl >= 64 || (!more && nl > 0)) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                constexpr int U3 = 4;
+                for (int b = 0; b < nl; b += U3 * G::RPW) {
+                  uint4 raw[U3];
+                  float sgn[U3];
+#pragma unroll
+                  for (int q = 0; q < U3; ++q) {
+                    const int e = b + q * G::RPW + rsub;
+                    sgn[q] = 0.f;
+                    raw[q] = make_uint4(0, 0, 0, 0);
+                    if (e < nl) {
+                      const int pp = wl[e];
+                      sgn[q] = is_left(S.key[pp], pp, th) ? 1.f : -1.f;
+                      raw[q] = ld16(xh + size_t(S.pt[pp]) * D + sub * G::EPV);
+                    }
+                  }
+#pragma unroll
+                  for (int q = 0; q < U3; ++q) {
+                    if (sgn[q] == 0.f) continue;
+                    float v[G::EPV];
+                    unpack_vec<T, G::EPV>(raw[q], v);
+                    if (sgn[q] > 0.f) {
+#pragma unroll
+                      for (int e = 0; e < G::EPV; ++e) a0[e] += v[e];
+                    } else {
+#pragma unroll
+                      for (int e = 0; e < G::EPV; ++e) a0[e] -= v[e];
+                    }
+                  }
+                }
+                nsw += nl;
+                nl = 0;
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+              }
+              if (!more) break;
             }
           }
 #pragma unroll
@@ -989,7 +1069,6 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
               a0[e] += __shfl_xor(a0[e], o, 64);
               a1[e] += __shfl_xor(a1[e], o, 64);
             }
-          nsw = wave_sum_i(nsw);
           if (lane == 0 && nsw) atomicAdd(&S.swc[a], nsw);
           if (A <= NW) {
             if (rsub == 0)

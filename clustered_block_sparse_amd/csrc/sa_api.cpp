@@ -422,6 +422,12 @@ SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
                  max_tiles(p, qcfg), scr, s);
 }
 
+SA_API sa_status sa_set_attn_events(void* start, void* stop) {
+  if ((start == nullptr) != (stop == nullptr)) return SA_ERR_INVALID_ARG;
+  attn_set_probe(static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
+  return SA_OK;
+}
+
 SA_API const char* sa_status_string(sa_status s) {
   switch (s) {
     case SA_OK: return "ok";

@@ -148,5 +148,6 @@ struct AttnArgs {
 size_t attn_scratch(int H, int N, int d, int Cq, int Ck, int tile_rows, int compensate, int dtype,
                     int max_tiles);
 hipError_t attn_run(const AttnArgs& a, Arena& scratch, hipStream_t st);
+void attn_set_probe(hipEvent_t start, hipEvent_t stop);
 
 }  // namespace sa

@@ -196,6 +196,17 @@ SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
                             const void* v, void* o, uint32_t* mask, void* ws, size_t ws_bytes,
                             void* stream);
 
+/* Timing probe for benchmarks.  With two hipEvent_t handles (created by the
+ * caller, passed as void*), every later sa_block_sparse_attn / sa_forward
+ * call records `start` on its stream right before the attention kernels and
+ * `stop` right after them (clustering, selection and the attention call's own
+ * preparation kernels fall outside), so hipEventElapsedTime(start, stop) is
+ * the attention kernels' duration.  NULL, NULL switches it off; one NULL is
+ * SA_ERR_INVALID_ARG.  The setting is process-wide and not synchronised:
+ * set it from the thread that issues the calls it should cover.  The
+ * library never creates, records on its own or destroys these events. */
+SA_API sa_status sa_set_attn_events(void* start, void* stop);
+
 /* Static description of a status code. */
 SA_API const char* sa_status_string(sa_status s);
 

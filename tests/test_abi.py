@@ -98,3 +98,9 @@ def test_select_and_forward_validation(lib):
     r = lib.sa_forward(ctypes.byref(p), ctypes.byref(sub), ctypes.byref(km), ctypes.byref(good),
                        ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
     assert r == 1  # subspace is for keys only
+
+
+def test_attn_events_probe_validation(lib):
+    assert lib.sa_set_attn_events(None, FAKE) == 1
+    assert lib.sa_set_attn_events(FAKE, None) == 1
+    assert lib.sa_set_attn_events(None, None) == 0
