@@ -405,6 +405,9 @@ __device__ __forceinline__ uint4 ld16(const T* p) {
 // ---------------------------------------------------------------------------
 // top phase kernels (grid.y = heads)
 // ---------------------------------------------------------------------------
+constexpr int NBIN = 2048;      // interpolated histogram bins of a segment's keys
+constexpr int CAND_CAP = 4096;  // candidates of the selected bin kept per segment
+
 struct TopBufs {
   const int4* segs;    // level table
   const int4* chunks;  // level chunk table
@@ -415,8 +418,11 @@ struct TopBufs {
   float* ssum;         // [H][max_seg][2][D]  sums of the two sides
   uint2* thr;          // [H][max_seg]
   float* part;         // [H][max_chunk][2][D]
-  int32_t* cnt;        // [H][max_seg] chunk arrival counters (zero between uses)
   uint2* segmm;        // [H][max_seg] min / max key of the round (reset after use)
+  int32_t* ghist;      // [H][max_seg][NBIN] key histogram of the round (zero between uses)
+  int2* selbin;        // [H][max_seg] bin holding rank n_left, rank inside it (bin -1: keys all equal)
+  unsigned long long* cand;  // [H][max_seg][CAND_CAP] (key << 32 | position) of that bin
+  int32_t* ccount;     // [H][max_seg] candidates (zero between uses)
   int max_seg, max_chunk, N, round;  // round: 0 = first round of a level
 };
 
@@ -502,94 +508,123 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ x, Top
   }
 }
 
-// Exact (key, position) of rank n_left in a segment: the keys' min / max
-// (folded in by the delta pass) spread 2048 interpolated bins; one histogram
-// pass finds the bin of rank n_left, a second pass gathers that bin's keys
-// (with positions, as distinct 64-bit keys) into LDS, where a radix search
-// finishes.  Oversized bins fall back to the generic radix search.
-constexpr int SEL_CAP = 8192;
+// Exact (key, position) of rank n_left in every segment, in four launches
+// that spread each segment over its chunks:
+//   hist: per-chunk histograms of NBIN bins interpolated between the
+//         segment's min / max key (folded in by the delta pass), added into
+//         the segment's histogram;
+//   find: the bin holding rank n_left and the rank inside it;
+//   cand: that bin's keys with their positions, as distinct 64-bit values;
+//   pick: the exact rank among them (a radix search in LDS), or, when the
+//         bin overflows CAND_CAP, a radix search over all of the segment's keys.
+// Only integer atomics are used; the selected (key, position) is unique, so
+// the result does not depend on their order.
+__device__ __forceinline__ int bin_of(uint32_t v, uint2 mm) {
+  const unsigned long long range = (unsigned long long)(mm.y - mm.x) + 1ull;
+  return int(((unsigned long long)(v - mm.x) * NBIN) / range);
+}
 
-struct TopSelShared {
-  unsigned long long cand[SEL_CAP];
-  Sel64Shared s64;
-  int cnt, bin, below;
-};
+__global__ __launch_bounds__(256) void hist_kernel(TopBufs b) {
+  __shared__ int hist[NBIN];
+  const int h = blockIdx.y, t = threadIdx.x;
+  const int4 ch = b.chunks[blockIdx.x];
+  const size_t si = size_t(h) * b.max_seg + ch.x;
+  const uint2 mm = b.segmm[si];
+  if (mm.x == mm.y) return;
+  for (int i = t; i < NBIN; i += 256) hist[i] = 0;
+  __syncthreads();
+  const uint32_t* u = b.keys + size_t(h) * b.N + ch.y;
+  for (int i = t; i < ch.z; i += 256) atomicAdd(&hist[bin_of(u[i], mm)], 1);
+  __syncthreads();
+  int* g = b.ghist + si * NBIN;
+  for (int i = t; i < NBIN; i += 256)
+    if (hist[i]) atomicAdd(&g[i], hist[i]);
+}
 
-__global__ __launch_bounds__(1024) void select_kernel(TopBufs b) {
-  __shared__ TopSelShared sh;
+__global__ __launch_bounds__(256) void find_kernel(TopBufs b) {
+  __shared__ int wsum[16];
+  const int h = blockIdx.y, t = threadIdx.x;
+  const int4 sg = b.segs[blockIdx.x];
+  if (sg.z == 0) return;
+  const size_t si = size_t(h) * b.max_seg + blockIdx.x;
+  const uint2 mm = b.segmm[si];
+  if (mm.x == mm.y) {
+    if (t == 0) b.selbin[si] = make_int2(-1, 0);
+    return;
+  }
+  constexpr int BPT = NBIN / 256;
+  int* g = b.ghist + si * NBIN;
+  int c[BPT], loc = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    c[j] = g[t * BPT + j];
+    loc += c[j];
+  }
+  int tot;
+  int pre = block_excl_scan<int>(loc, wsum, tot);
+  const int k = sg.z;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    if (pre < k && k <= pre + c[j]) b.selbin[si] = make_int2(t * BPT + j, k - pre);
+    pre += c[j];
+    g[t * BPT + j] = 0;  // ready for the next round
+  }
+}
+
+__global__ __launch_bounds__(256) void cand_kernel(TopBufs b) {
+  const int h = blockIdx.y, t = threadIdx.x, lane = t & 63;
+  const int4 ch = b.chunks[blockIdx.x];
+  const size_t si = size_t(h) * b.max_seg + ch.x;
+  const int2 sb = b.selbin[si];
+  if (sb.x < 0) return;
+  const uint2 mm = b.segmm[si];
+  const uint32_t* u = b.keys + size_t(h) * b.N + ch.y;
+  unsigned long long* cd = b.cand + si * CAND_CAP;
+  for (int i0 = 0; i0 < ch.z; i0 += 256) {
+    const int i = i0 + t;
+    const uint32_t v = i < ch.z ? u[i] : 0u;
+    const bool f = i < ch.z && bin_of(v, mm) == sb.x;
+    const uint64_t bal = __ballot(f);
+    if (!bal) continue;
+    const int lead = __ffsll((unsigned long long)bal) - 1;
+    int base = 0;
+    if (lane == lead) base = atomicAdd(&b.ccount[si], __popcll(bal));
+    base = __shfl(base, lead, 64);
+    const int slot = base + __popcll(bal & ((uint64_t(1) << lane) - 1));
+    if (f && slot < CAND_CAP) cd[slot] = ((unsigned long long)v << 32) | uint32_t(ch.y + i);
+  }
+}
+
+__global__ __launch_bounds__(1024) void pick_kernel(TopBufs b) {
+  __shared__ unsigned long long cand[CAND_CAP];
+  __shared__ Sel64Shared s64;
   __shared__ SelectShared gsh;
   const int h = blockIdx.y, t = threadIdx.x;
   const int4 sg = b.segs[blockIdx.x];
   if (sg.z == 0) return;
-  uint2* mmp = b.segmm + size_t(h) * b.max_seg + blockIdx.x;
-  const uint2 mm = *mmp;
+  const size_t si = size_t(h) * b.max_seg + blockIdx.x;
+  const uint2 mm = b.segmm[si];
+  const int2 sb = b.selbin[si];
+  const int m = sb.x < 0 ? 0 : b.ccount[si];
   __syncthreads();
-  if (t == 0) *mmp = make_uint2(0xFFFFFFFFu, 0u);  // ready for the next round
-  const uint32_t* u = b.keys + size_t(h) * b.N + sg.x;
-  const int n = sg.y, k = sg.z;
-  uint2 res;
-  if (mm.x == mm.y) {
-    res = make_uint2(mm.x, uint32_t(sg.x + k - 1));  // all keys equal: rank k is position k-1
-  } else {
-    const unsigned long long range = (unsigned long long)(mm.y - mm.x) + 1ull;
-    auto bin_of = [&](uint32_t v) { return int(((unsigned long long)(v - mm.x) * 2048ull) / range); };
-    for (int i = t; i < 2048; i += 1024) sh.s64.hist[i] = 0;
-    if (t == 0) sh.cnt = 0;
-    __syncthreads();
-    constexpr int U = 8;
-    for (int i0 = t; i0 < n; i0 += 1024 * U) {
-      uint32_t v[U];
-#pragma unroll
-      for (int q = 0; q < U; ++q) {
-        const int i = i0 + q * 1024;
-        v[q] = i < n ? u[i] : 0u;
-      }
-#pragma unroll
-      for (int q = 0; q < U; ++q)
-        if (i0 + q * 1024 < n) atomicAdd(&sh.s64.hist[bin_of(v[q])], 1);
-    }
-    __syncthreads();
-    {
-      const int c0 = sh.s64.hist[2 * t], c1 = sh.s64.hist[2 * t + 1];
-      int tot;
-      const int pre = block_excl_scan<int>(c0 + c1, sh.s64.wsum, tot);
-      if (pre < k && k <= pre + c0) {
-        sh.bin = 2 * t;
-        sh.below = pre;
-      } else if (pre + c0 < k && k <= pre + c0 + c1) {
-        sh.bin = 2 * t + 1;
-        sh.below = pre + c0;
-      }
-    }
-    __syncthreads();
-    const int bstar = sh.bin, kk = k - sh.below;
-    for (int i0 = t; i0 < n; i0 += 1024 * U) {
-      uint32_t v[U];
-#pragma unroll
-      for (int q = 0; q < U; ++q) {
-        const int i = i0 + q * 1024;
-        v[q] = i < n ? u[i] : 0u;
-      }
-#pragma unroll
-      for (int q = 0; q < U; ++q) {
-        const int i = i0 + q * 1024;
-        if (i < n && bin_of(v[q]) == bstar) {
-          const int slot = atomicAdd(&sh.cnt, 1);
-          if (slot < SEL_CAP) sh.cand[slot] = ((unsigned long long)v[q] << 32) | uint32_t(sg.x + i);
-        }
-      }
-    }
-    __syncthreads();
-    const int m = sh.cnt;
-    if (m <= SEL_CAP) {
-      const unsigned long long r = lds_select64(sh.cand, m, kk, sh.s64);
-      res = make_uint2(uint32_t(r >> 32), uint32_t(r & 0xFFFFFFFFull));
-    } else {
-      const uint2 r = block_select([&](int i) { return u[i]; }, n, k, gsh);
-      res = make_uint2(r.x, r.y + sg.x);
-    }
+  if (t == 0) {  // ready for the next round
+    b.segmm[si] = make_uint2(0xFFFFFFFFu, 0u);
+    b.ccount[si] = 0;
   }
-  if (t == 0) b.thr[size_t(h) * b.max_seg + blockIdx.x] = res;
+  uint2 res;
+  if (sb.x < 0) {
+    res = make_uint2(mm.x, uint32_t(sg.x + sg.z - 1));  // all keys equal: rank k is position k-1
+  } else if (m <= CAND_CAP) {
+    for (int i = t; i < m; i += 1024) cand[i] = b.cand[si * CAND_CAP + i];
+    __syncthreads();
+    const unsigned long long r = lds_select64(cand, m, sb.y, s64);
+    res = make_uint2(uint32_t(r >> 32), uint32_t(r & 0xFFFFFFFFull));
+  } else {
+    const uint32_t* u = b.keys + size_t(h) * b.N + sg.x;
+    const uint2 r = block_select([&](int i) { return u[i]; }, sg.y, sg.z, gsh);
+    res = make_uint2(r.x, r.y + sg.x);
+  }
+  if (t == 0) b.thr[si] = res;
 }
 
 // Sums of one chunk into its partial slot.  FULL (round 0): both sides from
@@ -1181,7 +1216,10 @@ hipError_t run_bisect(const void* xv, int H, int N, int L, int iters, const Tree
     for (int it = 0; it < iters; ++it) {
       delta_kernel<T, D><<<gc, 256, 0, st>>>(x, b, it == 0);
       b.round = it;
-      select_kernel<<<gs, 1024, 0, st>>>(b);
+      hist_kernel<<<gc, 256, 0, st>>>(b);
+      find_kernel<<<gs, 256, 0, st>>>(b);
+      cand_kernel<<<gc, 256, 0, st>>>(b);
+      pick_kernel<<<gs, 1024, 0, st>>>(b);
       if (it + 1 < iters) {
         if (it == 0) {
           sums_kernel<T, D, true><<<gc, 256, 0, st>>>(x, b);
@@ -1217,8 +1255,11 @@ size_t bisect_scratch(int H, int N, int d, int leaf) {
   a.get<float>(size_t(H) * P.max_seg * 2 * d);   // ssum
   a.get<uint2>(size_t(H) * P.max_seg);
   a.get<float>(size_t(H) * P.max_chunk * 2 * d);
-  a.get<int32_t>(size_t(H) * P.max_seg);
   a.get<uint2>(size_t(H) * P.max_seg);
+  a.get<int32_t>(size_t(H) * P.max_seg * NBIN);
+  a.get<int2>(size_t(H) * P.max_seg);
+  a.get<unsigned long long>(size_t(H) * P.max_seg * CAND_CAP);
+  a.get<int32_t>(size_t(H) * P.max_seg);
   return a.used;
 }
 
@@ -1235,8 +1276,11 @@ hipError_t bisect_run(const void* x, int dtype, int H, int N, int d, int leaf, i
   b.ssum = s.get<float>(size_t(H) * P.max_seg * 2 * d);
   b.thr = s.get<uint2>(size_t(H) * P.max_seg);
   b.part = s.get<float>(size_t(H) * P.max_chunk * 2 * d);
-  b.cnt = s.get<int32_t>(size_t(H) * P.max_seg);
   b.segmm = s.get<uint2>(size_t(H) * P.max_seg);
+  b.ghist = s.get<int32_t>(size_t(H) * P.max_seg * NBIN);
+  b.selbin = s.get<int2>(size_t(H) * P.max_seg);
+  b.cand = s.get<unsigned long long>(size_t(H) * P.max_seg * CAND_CAP);
+  b.ccount = s.get<int32_t>(size_t(H) * P.max_seg);
   b.max_seg = P.max_seg;
   b.max_chunk = P.max_chunk;
   b.N = N;
@@ -1246,7 +1290,8 @@ hipError_t bisect_run(const void* x, int dtype, int H, int N, int d, int leaf, i
   int32_t* pb = (P.t.nlev % 2 == 0) ? other : perm_out;
   iota_kernel<<<dim3(ceil_div(N, 256), H), 256, 0, st>>>(pa, N);
   const size_t ncnt = size_t(H) * P.max_seg;
-  zero_i32<<<unsigned((ncnt + 255) / 256), 256, 0, st>>>(b.cnt, ncnt);
+  zero_i32<<<unsigned((ncnt + 255) / 256), 256, 0, st>>>(b.ccount, ncnt);
+  zero_i32<<<unsigned((ncnt * NBIN + 255) / 256), 256, 0, st>>>(b.ghist, ncnt * NBIN);
   init_minmax<<<unsigned((ncnt + 255) / 256), 256, 0, st>>>(b.segmm, ncnt);
   build_tree_kernel<<<1, 1024, 0, st>>>(P.t, N, segs, chunks);
   hipError_t e;

@@ -113,6 +113,27 @@ __global__ void fill_i32(int32_t* p, size_t n, int32_t v) {
   if (i < n) p[i] = v;
 }
 
+// Cluster sizes.  Few clusters: per-block LDS histograms of COUNT_CHUNK labels,
+// then one global add per non-empty bin; many clusters: one global add per
+// token (the adds spread over many addresses).  Integer adds: the result does
+// not depend on their order.
+constexpr int COUNT_CHUNK = 4096;
+constexpr int COUNT_LDS_MAX = 4096;
+
+__global__ __launch_bounds__(256) void count_labels_lds(const int32_t* __restrict__ labels, int N, int C,
+                                                        int32_t* __restrict__ cnt) {
+  __shared__ int hist[COUNT_LDS_MAX];
+  const int h = blockIdx.y, t = threadIdx.x;
+  for (int c = t; c < C; c += 256) hist[c] = 0;
+  __syncthreads();
+  const int a = blockIdx.x * COUNT_CHUNK, b = min(N, a + COUNT_CHUNK);
+  const int32_t* lh = labels + size_t(h) * N;
+  for (int n = a + t; n < b; n += 256) atomicAdd(&hist[lh[n]], 1);
+  __syncthreads();
+  for (int c = t; c < C; c += 256)
+    if (hist[c]) atomicAdd(&cnt[size_t(h) * C + c], hist[c]);
+}
+
 __global__ __launch_bounds__(256) void count_labels(const int32_t* __restrict__ labels, int N, int C,
                                                     int32_t* __restrict__ cnt) {
   const int h = blockIdx.y;
@@ -136,35 +157,72 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x, T*
   *dst = *s;
 }
 
-// one workgroup per (cluster, head); 4 row groups x 64 lanes, fixed-order sums
+// Member means: one workgroup per (cluster, head).  Each thread owns one
+// 16-byte vector (EPV elements) of the row slice [col0, col0 + dc) and sums
+// its rows r, r + RPI, r + 2 RPI, ... in that order (four loads in flight);
+// the RPI partial sums of a column are then added in row-group order.  The
+// result is independent of timing.
 template <typename T>
 __global__ __launch_bounds__(256) void means_kernel(const T* __restrict__ x, int d, int col0, int dc,
                                                     const int32_t* __restrict__ perm,
                                                     const int32_t* __restrict__ off, int N, int C,
                                                     float* __restrict__ out, int out_stride,
                                                     bool keep_empty) {
-  __shared__ float part[4][128];
-  const int c = blockIdx.x, h = blockIdx.y, t = threadIdx.x, lane = t & 63, g = t >> 6;
+  constexpr int EPV = 16 / sizeof(T);
+  __shared__ float part[256 * EPV];
+  const int c = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   const int a = off[size_t(h) * (C + 1) + c], b = off[size_t(h) * (C + 1) + c + 1];
   float* o = out + (size_t(h) * C + c) * out_stride;
   if (b == a) {
-    if (!keep_empty && g == 0)
-      for (int j = lane; j < dc; j += 64) o[j] = 0.f;
+    if (!keep_empty)
+      for (int j = t; j < dc; j += 256) o[j] = 0.f;
     return;
   }
-  float s0 = 0.f, s1 = 0.f;
+  const int V = dc / EPV;          // vectors per row slice
+  const int RPI = 256 / V;         // rows per iteration
+  const int r = t / V, j = t % V;
+  const bool act = r < RPI;
+  float acc[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
   const int32_t* ph = perm + size_t(h) * N;
-  for (int p = a + g; p < b; p += 4) {
-    const T* row = x + (size_t(h) * N + ph[p]) * d + col0;
-    if (lane < dc) s0 += to_f(row[lane]);
-    if (lane + 64 < dc) s1 += to_f(row[lane + 64]);
+  const T* xh = x + size_t(h) * N * d + col0 + j * EPV;
+  if (act) {
+    constexpr int U = 4;
+    for (int p0 = a + r; p0 < b; p0 += U * RPI) {
+      uint4 raw[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int p = p0 + q * RPI;
+        raw[q] = p < b ? *reinterpret_cast<const uint4*>(xh + size_t(ph[p]) * d) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        if (p0 + q * RPI >= b) break;
+        if constexpr (sizeof(T) == 4) {
+          acc[0] += __uint_as_float(raw[q].x);
+          acc[1] += __uint_as_float(raw[q].y);
+          acc[2] += __uint_as_float(raw[q].z);
+          acc[3] += __uint_as_float(raw[q].w);
+        } else {
+          const uint32_t w4[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            acc[2 * k] += __uint_as_float(w4[k] << 16);
+            acc[2 * k + 1] += __uint_as_float(w4[k] & 0xFFFF0000u);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) part[r * dc + j * EPV + e] = acc[e];
   }
-  if (lane < dc) part[g][lane] = s0;
-  if (lane + 64 < dc) part[g][lane + 64] = s1;
   __syncthreads();
   if (t < dc) {
-    float s = ((part[0][t] + part[1][t]) + part[2][t]) + part[3][t];
-    o[t] = s / float(b - a);
+    const int rows = min(RPI, b - a);
+    float sum = 0.f;
+    for (int k = 0; k < rows; ++k) sum += part[k * dc + t];
+    o[t] = sum / float(b - a);
   }
 }
 
@@ -221,7 +279,10 @@ hipError_t label_sort(const int32_t* labels, int32_t* perm, int32_t* offsets, in
   // offsets from label counts
   size_t nc = size_t(H) * C;
   fill_i32<<<ceil_div(int(nc), 256), 256, 0, st>>>(cnt, nc, 0);
-  count_labels<<<dim3(ceil_div(N, 256), H), 256, 0, st>>>(labels, N, C, cnt);
+  if (C <= COUNT_LDS_MAX)
+    count_labels_lds<<<dim3(ceil_div(N, COUNT_CHUNK), H), 256, 0, st>>>(labels, N, C, cnt);
+  else
+    count_labels<<<dim3(ceil_div(N, 256), H), 256, 0, st>>>(labels, N, C, cnt);
   scan_rows<<<H, 1024, 0, st>>>(cnt, offsets, C, C + 1, true);
   return hipGetLastError();
 }
@@ -240,6 +301,9 @@ hipError_t gather_rows(const void* x, void* x_perm, const int32_t* perm, int H, 
 hipError_t cluster_means(const void* x, int dtype, int d, int col0, int dc, const int32_t* perm,
                          const int32_t* offsets, int H, int N, int C, float* out, int out_stride,
                          bool keep_empty, hipStream_t st) {
+  const int esz = dtype == SA_F32 ? 4 : 2;
+  // 16-byte vectors of the slice; at most 256 of them per row
+  if ((col0 * esz) % 16 || (dc * esz) % 16 || (d * esz) % 16 || dc * esz > 256 * 16) return hipErrorInvalidValue;
   dim3 g(C, H);
   if (dtype == SA_F32)
     means_kernel<float><<<g, 256, 0, st>>>((const float*)x, d, col0, dc, perm, offsets, N, C, out,
