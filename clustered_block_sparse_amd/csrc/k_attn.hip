@@ -142,6 +142,32 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__
   if (t == 0) ntiles[h] = carry;
 }
 
+// ---------------------------------------------------------------------------
+// LDS tile layout of the MFMA kernel.  Tiles are unpadded; bank conflicts are
+// avoided by XOR-swizzling the 16-byte chunks of a row, so whole tiles can
+// arrive by direct global->LDS loads (lane l of such a load lands at 16 l).
+//   K tile:   KT rows of D bf16; chunk c of row r at chunk c ^ swz(r).
+//   V^T tile: D rows of KT keys; chunk c of row d at chunk c ^ swz(d); keys in
+//             MFMA order: within every 16-key group keys 4..7 and 8..11 trade
+//             places, so the 8 keys one lane feeds a 32x32x16 product (keys
+//             4hi..4hi+3 and 8+4hi..8+4hi+3) form one chunk.
+// swz puts the chunks any 16 consecutive rows (or any 8) read at one column on
+// distinct banks, for 64 as for 32 LDS banks.
+// ---------------------------------------------------------------------------
+__host__ __device__ __forceinline__ int mfma_key(int k) {  // an involution
+  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+}
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 16) return r & 15;
+  else return (r & 7) ^ ((r >> 3) & 1);
+}
+// element offset of 16-byte chunk c of row r in a tile of CPR chunks per row
+template <int CPR>
+__device__ __forceinline__ int toff(int r, int c) {
+  return r * (CPR * 8) + ((c ^ swz<CPR>(r)) << 3);
+}
+
 __global__ __launch_bounds__(128) void comp_prep_kernel(const float* __restrict__ kbar,
                                                         const float* __restrict__ vbar,
                                                         const int32_t* __restrict__ k_off, int Ck,
@@ -160,7 +186,7 @@ __global__ __launch_bounds__(128) void comp_prep_kernel(const float* __restrict_
       const bf16_t hi = f2bf(kv);
       kbh[o + c] = hi;
       kbl[o + c] = f2bf(kv - bf2f(hi));
-      vbt[((size_t(h) * (Ckp / KT) + j / KT) * D + c) * KT + (j % KT)] = f2bf(vv);
+      vbt[((size_t(h) * (Ckp / KT) + j / KT) * D + c) * KT + mfma_key(j % KT)] = f2bf(vv);
     }
     if (kbf) {
       kbf[o + c] = kv;
@@ -422,6 +448,8 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8_t a, bf16x8_t b, floatx16 c) {
 
 __device__ __forceinline__ bf16x8_t as_bf8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
+#define BF16_ONES (__builtin_bit_cast(bf16x2_t, 0x3F803F80u))  // (1.0, 1.0)
+
 // two floats -> packed bf16 pair (hardware round-to-nearest-even)
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
   bf16x2_t v;
@@ -432,8 +460,6 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) {
 
 template <int D>
 struct MfmaLds {
-  bf16_t K[2][KT][D + 8];      // key rows, padded against bank conflicts
-  bf16_t V[2][D][KT + 4];      // V^T
   int rs[RCH + 1];
   int rp[RCH + 1];
   int wsum[16];
@@ -441,7 +467,8 @@ struct MfmaLds {
   float bias[KT];
 };
 
-// V^T in 64-key blocks: vt[h][b][c][k] = v_perm[h][64 b + k][c] (zero past N)
+// V^T in 64-key blocks, keys in MFMA order:
+// vt[h][b][c][mfma_key(k)] = v_perm[h][64 b + k][c] (zero past N)
 template <int D>
 __global__ __launch_bounds__(256) void vt_kernel(const bf16_t* __restrict__ v, int N, int NB,
                                                  bf16_t* __restrict__ vt) {
@@ -462,7 +489,7 @@ __global__ __launch_bounds__(256) void vt_kernel(const bf16_t* __restrict__ v, i
     uint32_t w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      w[e] = uint32_t(tile[kc * 8 + 2 * e][d]) | (uint32_t(tile[kc * 8 + 2 * e + 1][d]) << 16);
+      w[e] = uint32_t(tile[mfma_key(kc * 8 + 2 * e)][d]) | (uint32_t(tile[mfma_key(kc * 8 + 2 * e + 1)][d]) << 16);
     *reinterpret_cast<uint4*>(dst + size_t(d) * KT + kc * 8) = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
@@ -472,14 +499,18 @@ __global__ __launch_bounds__(256) void vt_kernel(const bf16_t* __restrict__ v, i
 // gathers rows of arbitrary ranges and transposes V while staging it.  Each
 // workgroup runs in the instantiation matching its row and exits in the other.
 template <int D, bool ALIGNED>
-__global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sl2) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && ALIGNED ? 4 : 2, D == 64 && ALIGNED ? 4 : 2))) void attn_mfma(AttnArgs a, Prep p, float sl2) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int DS = D / 16;         // MFMA k-steps over d
   constexpr int DT = D / 32;         // 32-row tiles of d in O^T
   constexpr int KCH = D / 4;         // general path: K elements per thread (one row quarter)
   constexpr int KPT = D / 32;        // general path: V keys per thread
-  constexpr int DG = D / 8;          // 8-column groups of a row
-  constexpr int CK = KT * D / 8 / 256;  // aligned path: 16-byte chunks per thread (K and V^T each)
+  constexpr int DG = D / 8;          // 16-byte chunks of a K / Q / O row
+  constexpr int VG = KT / 8;         // 16-byte chunks of a V^T row
+  constexpr int CK = KT * D / 8 / 256;  // 16-byte chunks per thread of a K (or V^T) tile
+  // four separate tiles: as distinct objects, a direct load into one pair is
+  // visibly independent of reads from the other
+  __shared__ __attribute__((aligned(16))) bf16_t K0[KT * D], K1[KT * D], V0[D * KT], V1[D * KT];
   __shared__ __attribute__((aligned(16))) MfmaLds<D> S;
 
   int h, tix;
@@ -514,26 +545,28 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sl
 
   const bf16_t* kh = (const bf16_t*)a.k_perm + size_t(h) * N * D;
 
-  auto qk = [&](floatx16 (&s)[2], const bf16_t (*Kb)[D + 8]) {
+  auto qk = [&](floatx16 (&s)[2], const bf16_t* Kb) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int st = 0; st < DS; ++st) {
-        const uint4 u = *reinterpret_cast<const uint4*>(&Kb[32 * kt + col][16 * st + 8 * hi]);
+        const uint4 u = *reinterpret_cast<const uint4*>(Kb + toff<DG>(32 * kt + col, 2 * st + hi));
         s[kt] = mfma32(as_bf8(u), qf[st], s[kt]);
       }
     }
   };
 
-  // Online-softmax update and P V for one tile whose S^T holds log2-domain
-  // logits (-inf for masked keys).
-  auto softmax_pv = [&](floatx16 (&s)[2], int vbuf) {
+  // Online-softmax update and P V for one tile.  The log2-domain logit of an
+  // entry is s * lsc: raw scores with lsc = scale * log2(e), or logits already
+  // formed (masked keys -inf) with lsc = 1.  The row sum adds the bf16 P
+  // values the P V product consumes (dot2 against (1, 1)).
+  auto softmax_pv = [&](floatx16 (&s)[2], const bf16_t* Vb, float lsc) {
     float mx = -__builtin_huge_valf();
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * lsc;
     float alpha = 1.f;
     if (mx > m + 8.f) {
       alpha = __builtin_amdgcn_exp2f(m - mx);  // m = -inf -> 0
@@ -546,16 +579,17 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sl
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
     }
+    // every tile holds a valid key, so m is finite here and -inf maps to 0
+    const float nm = -m;
     uint32_t pk[2][8];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
-        // every tile holds a valid key, so m is finite here and -inf maps to 0
-        const float e0 = __builtin_amdgcn_exp2f(s[kt][r] - m);
-        const float e1 = __builtin_amdgcn_exp2f(s[kt][r + 1] - m);
-        lsum += e0 + e1;
+        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kt][r], lsc, nm));
+        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kt][r + 1], lsc, nm));
         pk[kt][r >> 1] = pack2(e0, e1);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[kt][r >> 1]), BF16_ONES, lsum, false);
       }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -564,23 +598,14 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sl
                                             pk[kt][4 * half + 2], pk[kt][4 * half + 3]));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const bf16_t* vr = &S.V[vbuf][32 * dt + col][16 * ks + 4 * hi];
-        const uint2 lo = *reinterpret_cast<const uint2*>(vr);
-        const uint2 up = *reinterpret_cast<const uint2*>(vr + 8);
-        oacc[dt] = mfma32(as_bf8(make_uint4(lo.x, lo.y, up.x, up.y)), pf, oacc[dt]);
+        const uint4 u = *reinterpret_cast<const uint4*>(Vb + toff<VG>(32 * dt + col, 2 * ks + hi));
+        oacc[dt] = mfma32(as_bf8(u), pf, oacc[dt]);
       }
     }
   };
 
   // scores -> log2-domain logits in place (bias per key, keys >= nvalid masked)
   auto to_logits = [&](floatx16 (&s)[2], int nvalid, const float* bias_l2) {
-    if (nvalid >= KT && !bias_l2) {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] *= sl2;
-      return;
-    }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -593,60 +618,50 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sl
       }
   };
 
-  auto compute_tile = [&](int kbuf, int vbuf, int nvalid) {
+  auto compute_tile = [&](const bf16_t* Kb, const bf16_t* Vb, int nvalid) {
     floatx16 s[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-    qk(s, S.K[kbuf]);
-    to_logits(s, nvalid, nullptr);
-    softmax_pv(s, vbuf);
-  };
-
-  // V^T chunk -> LDS (row stride KT+4 is 8-byte aligned: two 8-byte stores)
-  auto store_vt_chunk = [&](int buf, int c, uint4 u) {
-    const int d = c >> 3, kc = c & 7;
-    bf16_t* dst = &S.V[buf][d][kc * 8];
-    *reinterpret_cast<uint2*>(dst) = make_uint2(u.x, u.y);
-    *reinterpret_cast<uint2*>(dst + 4) = make_uint2(u.z, u.w);
+    qk(s, Kb);
+    if (nvalid < KT) {  // keys past the end of the selection: -inf
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3) >= nvalid) s[kt][r] = -__builtin_huge_valf();
+    }
+    softmax_pv(s, Vb, sl2);
   };
 
   if constexpr (ALIGNED) {
     const int R = p.rcount[size_t(h) * a.Cq + i];
     const int2* rg = p.ranges + (size_t(h) * a.Cq + i) * p.Rmax;
     // ---------------- selected keys, 64-aligned ranges: whole-block tiles ----
+    // Both tiles of a block arrive by direct global->LDS loads: the lanes of a
+    // load pick their source chunks so that the lane-linear LDS placement is
+    // the swizzled layout.  Rows past the end of a range repeat its last row
+    // (their scores are masked).
     const bf16_t* vth = p.vt + size_t(h) * p.NB * D * KT;
-    uint4 kreg[CK], vreg[CK];
     int ri = 0, pos = R > 0 ? rg[0].x : 0, rend = R > 0 ? rg[0].y : 0;
-    auto load = [&](int pos0, int nvalid) {
+    auto issue = [&](bf16_t* Kd, bf16_t* Vd, int pos0, int nvalid) {
+      const bf16_t* vb = vth + size_t(pos0 / KT) * D * KT;
 #pragma unroll
       for (int q = 0; q < CK; ++q) {
-        const int c = tid + 256 * q;
-        const int row = c / DG, cc = c % DG;
-        kreg[q] = row < nvalid ? *reinterpret_cast<const uint4*>(kh + size_t(pos0 + row) * D + cc * 8)
-                               : make_uint4(0, 0, 0, 0);
-        vreg[q] = *reinterpret_cast<const uint4*>(vth + size_t(pos0 / KT) * D * KT + size_t(c) * 8);
+        const int s0 = (4 * q + w) * 64;  // first chunk of this wave's load
+        const int sl = s0 + lane;
+        const int r = sl / DG, kc = (sl % DG) ^ swz<DG>(r);
+        __builtin_amdgcn_global_load_lds(kh + size_t(pos0 + min(r, nvalid - 1)) * D + kc * 8, Kd + s0 * 8,
+                                         16, 0, 0);
+        const int d = sl / VG, vc = (sl % VG) ^ swz<VG>(d);
+        __builtin_amdgcn_global_load_lds(vb + d * KT + vc * 8, Vd + s0 * 8, 16, 0, 0);
       }
     };
-    auto store = [&](int buf) {
-#pragma unroll
-      for (int q = 0; q < CK; ++q) {
-        const int c = tid + 256 * q;
-        *reinterpret_cast<uint4*>(&S.K[buf][c / DG][(c % DG) * 8]) = kreg[q];
-        store_vt_chunk(buf, c, vreg[q]);
-      }
-    };
-    if (ri < R) load(pos, min(KT, rend - pos));
-    int tt = 0;
-    while (ri < R) {
+    auto step = [&](const bf16_t* Kc, const bf16_t* Vc, bf16_t* Kn, bf16_t* Vn) {
       const int nvalid = min(KT, rend - pos);
-      const int buf = tt & 1;
-      // buf last held tile tt-2, whose compute every wave finished before the
-      // barrier of iteration tt-1
-      store(buf);
-      __syncthreads();
-      // advance to the next tile and prefetch it
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of the tile landed
+      __syncthreads();                     // every wave's, and the other pair is free
       pos += KT;
       if (pos >= rend) {
         ++ri;
@@ -656,9 +671,14 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sl
           rend = r2.y;
         }
       }
-      if (ri < R) load(pos, min(KT, rend - pos));
-      compute_tile(buf, buf, nvalid);
-      ++tt;
+      if (ri < R) issue(Kn, Vn, pos, min(KT, rend - pos));
+      compute_tile(Kc, Vc, nvalid);
+    };
+    if (R > 0) issue(K0, V0, pos, min(KT, rend - pos));
+    while (ri < R) {
+      step(K0, V0, K1, V1);
+      if (ri >= R) break;
+      step(K1, V1, K0, V0);
     }
   } else {
     // ---------------- selected keys, general ranges: row gather --------------
@@ -667,14 +687,15 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sl
     const int v_dg = tid % DG, v_kg = tid / DG;           // V: KPT keys x 8 columns
     uint4 kreg[KCH / 8];
     uint4 vreg[KPT];
-    auto store_tile = [&](int buf) {
+    auto store_tile = [&](bf16_t* Kd, bf16_t* Vd) {
 #pragma unroll
       for (int q = 0; q < KCH / 8; ++q)
-        *reinterpret_cast<uint4*>(&S.K[buf][k_slot][k_c0 + 8 * q]) = kreg[q];
+        *reinterpret_cast<uint4*>(Kd + toff<DG>(k_slot, k_c0 / 8 + q)) = kreg[q];
+      const int kp = mfma_key(v_kg * KPT);  // the KPT keys stay contiguous in MFMA order
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int c = v_dg * 8 + e;
-        bf16_t* dst = &S.V[buf][c][v_kg * KPT];
+        bf16_t* dst = Vd + toff<VG>(c, kp >> 3) + (kp & 7);
         uint32_t wv[KPT];
 #pragma unroll
         for (int kq = 0; kq < KPT; ++kq) {
@@ -730,11 +751,12 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sl
       };
       if (ntile > 0) load_tile(0);
       for (int tt = 0; tt < ntile; ++tt) {
-        const int buf = tt & 1;
-        store_tile(buf);
+        bf16_t* Kb = (tt & 1) ? K1 : K0;
+        bf16_t* Vb = (tt & 1) ? V1 : V0;
+        store_tile(Kb, Vb);
         __syncthreads();
         if (tt + 1 < ntile) load_tile(tt + 1);
-        compute_tile(buf, buf, total - tt * KT);
+        compute_tile(Kb, Vb, total - tt * KT);
       }
     }
   }
@@ -759,10 +781,12 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sl
 #pragma unroll
       for (int q = 0; q < CK; ++q) {
         const int c = tid + 256 * q;
-        const size_t ro = size_t(j0 + c / DG) * D + (c % DG) * 8;
-        *reinterpret_cast<uint4*>(&S.K[0][c / DG][(c % DG) * 8]) = *reinterpret_cast<const uint4*>(kbh + ro);
-        *reinterpret_cast<uint4*>(&S.K[1][c / DG][(c % DG) * 8]) = *reinterpret_cast<const uint4*>(kbl + ro);
-        store_vt_chunk(0, c, *reinterpret_cast<const uint4*>(vbt + size_t(j0) * D + size_t(c) * 8));
+        const int row = c / DG, kc = c % DG;
+        const size_t ro = size_t(j0 + row) * D + kc * 8;
+        *reinterpret_cast<uint4*>(K0 + toff<DG>(row, kc)) = *reinterpret_cast<const uint4*>(kbh + ro);
+        *reinterpret_cast<uint4*>(K1 + toff<DG>(row, kc)) = *reinterpret_cast<const uint4*>(kbl + ro);
+        *reinterpret_cast<uint4*>(V0 + toff<VG>(c / VG, c % VG)) =
+            *reinterpret_cast<const uint4*>(vbt + size_t(j0) * D + size_t(c) * 8);
       }
       __syncthreads();
       floatx16 s[2];
@@ -770,10 +794,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sl
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-      qk(s, S.K[0]);
-      qk(s, S.K[1]);
+      qk(s, K0);
+      qk(s, K1);
       to_logits(s, KT, S.bias);
-      softmax_pv(s, 0);
+      softmax_pv(s, V0, 1.f);
     }
   }
 
@@ -781,7 +805,10 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sl
   const float ltot = lsum + __shfl_xor(lsum, 32, 64);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   __syncthreads();
-  bf16_t (*Os)[D + 8] = reinterpret_cast<bf16_t (*)[D + 8]>(&S.K[0][0][0]);
+  // stage O in the K tiles (query rows 0..63 in K0, 64..127 in K1), then
+  // scatter whole rows to their original tokens
+  bf16_t* Ob = w < 2 ? K0 : K1;
+  const int orow = qr & 63;
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
@@ -789,15 +816,16 @@ __global__ __launch_bounds__(256, 2) void attn_mfma(AttnArgs a, Prep p, float sl
       const int c = 32 * dt + 8 * g + 4 * hi;
       const uint2 v = make_uint2(pack2(oacc[dt][4 * g] * inv, oacc[dt][4 * g + 1] * inv),
                                  pack2(oacc[dt][4 * g + 2] * inv, oacc[dt][4 * g + 3] * inv));
-      *reinterpret_cast<uint2*>(&Os[qr][c]) = v;
+      *reinterpret_cast<uint2*>(Ob + toff<DG>(orow, c >> 3) + (c & 7)) = v;
     }
   __syncthreads();
   const int32_t* qi = a.q_idx + size_t(h) * N + p0;
   bf16_t* oh = (bf16_t*)a.o + size_t(h) * N * D;
   for (int v = tid; v < TQ * DG; v += 256) {
-    const int r = v / DG, c = (v % DG) * 8;
+    const int r = v / DG, kc = v % DG;
     if (r < nr)
-      *reinterpret_cast<uint4*>(oh + size_t(qi[r]) * D + c) = *reinterpret_cast<const uint4*>(&Os[r][c]);
+      *reinterpret_cast<uint4*>(oh + size_t(qi[r]) * D + kc * 8) =
+          *reinterpret_cast<const uint4*>((r < 64 ? K0 : K1) + toff<DG>(r & 63, kc));
   }
 }
 

@@ -429,13 +429,15 @@ struct TopBufs {
 template <typename T, int D>
 __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ x, TopBufs b, int first) {
   using G = RowGeo<T, D>;
-  constexpr int U = 4;  // wave steps in flight
+  constexpr int U = 8;  // wave steps in flight
   __shared__ float wv[D], mv[D];
+  __shared__ int pidx[BCH];  // the chunk's rows (original tokens)
   const int h = blockIdx.y, t = threadIdx.x;
   const int4 ch = b.chunks[blockIdx.x];
   const int4 sg = b.segs[ch.x];
   const int32_t* ph = b.perm + size_t(h) * b.N;
   const T* xh = x + size_t(h) * b.N * D;
+  for (int i = t; i < ch.z; i += 256) pidx[i] = ph[ch.y + i];
   if (t < D) {
     float c1, c2;
     if (first) {
@@ -466,10 +468,10 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ x, Top
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int r = rb + u * STEP + rsub;
-      pos[u] = ch.y + (r < ch.z ? r : 0);
+      pos[u] = r < ch.z ? r : 0;
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) raw[u] = ld16(xh + size_t(ph[pos[u]]) * D + sub * G::EPV);
+    for (int u = 0; u < U; ++u) raw[u] = ld16(xh + size_t(pidx[pos[u]]) * D + sub * G::EPV);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       float v[G::EPV];
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ x, Top
       if (r < ch.z) {
         kmin = min(kmin, key);
         kmax = max(kmax, key);
-        if (sub == 0) b.keys[size_t(h) * b.N + pos[u]] = key;
+        if (sub == 0) b.keys[size_t(h) * b.N + ch.y + pos[u]] = key;
       }
     }
   }
@@ -634,7 +636,7 @@ __global__ __launch_bounds__(1024) void pick_kernel(TopBufs b) {
 template <typename T, int D, bool FULL>
 __global__ __launch_bounds__(256) void sums_kernel(const T* __restrict__ x, TopBufs b) {
   using G = RowGeo<T, D>;
-  constexpr int U = 4;
+  constexpr int U = FULL ? 8 : 4;
   constexpr int STEP = 4 * G::RPW;
   __shared__ float ws[4][2][D];
   __shared__ int list[BCH];
@@ -696,6 +698,16 @@ __global__ __launch_bounds__(256) void sums_kernel(const T* __restrict__ x, TopB
     cnt = tot;
     __syncthreads();
   }
+  if constexpr (FULL) {
+    // the chunk's rows and sides, staged (sides are written here)
+    for (int i = t; i < ch.z; i += 256) {
+      const int p = ch.y + i;
+      const bool left = is_left(kh[p], p, th);
+      list[i] = left ? ph[p] : ~ph[p];
+      sd[p] = left ? 1 : 0;
+    }
+    __syncthreads();
+  }
   float s0[G::EPV], s1[G::EPV];  // FULL: left, right.  Otherwise: change of left
 #pragma unroll
   for (int e = 0; e < G::EPV; ++e) s0[e] = s1[e] = 0.f;
@@ -708,17 +720,16 @@ __global__ __launch_bounds__(256) void sums_kernel(const T* __restrict__ x, TopB
       sgn[u] = 0;
       int p = 0;
       if (r < cnt) {
+        const int e = list[r];
         if (FULL) {
-          p = ch.y + r;
-          sgn[u] = is_left(kh[p], p, th) ? 1 : 2;
+          p = e >= 0 ? e : ~e;  // original token
+          sgn[u] = e >= 0 ? 1 : 2;
         } else {
-          const int e = list[r];
-          p = e >= 0 ? e : ~e;
+          p = ph[e >= 0 ? e : ~e];
           sgn[u] = e >= 0 ? 1 : -1;
         }
       }
-      raw[u] = sgn[u] != 0 ? ld16(xh + size_t(ph[p]) * D + sub * G::EPV) : make_uint4(0, 0, 0, 0);
-      if (FULL && sgn[u] != 0 && sub == 0) sd[p] = sgn[u] == 1 ? 1 : 0;
+      raw[u] = sgn[u] != 0 ? ld16(xh + size_t(p) * D + sub * G::EPV) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
