@@ -1,17 +1,22 @@
 // Centroid proxy scores and hybrid Top-p / fixed Top-k selection with SCOPE's
 // online per-head Top-k (SCOPE, English abstract and key design section).
 //
-// One workgroup per (query cluster, head).  The row's proxy logits
-//   l_j = <qbar_i, kbar_j> * scale (+ ln|K_j|),   empty key cluster -> excluded
-// and its softmax are evaluated in fp64 (cheap at this size and accurate
-// enough that the ranking and the Top-p crossing agree with an fp64 reference
-// except at genuine ties).  The row is ranked by (p descending, j ascending)
-// with an LDS bitonic sort; a block prefix sum of the masses gives the Top-p
-// crossing.  The initial prefix is the shortest meeting both the mass and the
-// floor.  With online Top-k, a first pass accumulates A_h = sum_i |Q_i| n_i
-// with integer atomics (order independent, exact); the second pass computes
-// k_h = ceil(A_h / n) and extends the rows below it along the same ranking.
-// Every other reduction runs in a fixed order, so results are deterministic.
+// Proxy logits l_ij = <qbar_i, kbar_j> * scale (+ ln|K_j|) are evaluated in
+// fp64 (an empty key cluster is excluded).  A row is ranked by (logit
+// descending, j ascending); the boundary where a cumulative target is reached
+// (softmax mass >= top_p, a count of units) is found by an exact weighted radix
+// search over 64-bit order keys, with masses in 2^-52 fixed point so that
+// their sums are exact and independent of order.  The initial prefix is the
+// shortest meeting both the mass and the floor.  With online Top-k, a first
+// pass accumulates A_h = sum_i |Q_i| n_i with integer atomics; the second
+// computes k_h = ceil(A_h / n) and extends the rows below it along the same
+// ranking.  Every other reduction runs in a fixed order: results are
+// deterministic.
+//
+// Key clusters (KMEANS / BISECT): a tiled fp64 kernel forms every logit of a
+// head, then one wavefront per query cluster selects.  SCOPE key subspaces:
+// one workgroup per query cluster evaluates the 32^3 combo logits from the
+// per-slice lookup tables on the fly; units are keys.
 
 #include "sa_internal.h"
 
@@ -19,42 +24,7 @@ namespace sa {
 
 namespace {
 
-constexpr int SEL_MAX = 1024;  // key clusters handled by the LDS sort
-
-struct RowEntry {
-  double p;
-  int j;
-};
-
-__device__ __forceinline__ bool before(const RowEntry& a, const RowEntry& b) {
-  return a.p > b.p || (a.p == b.p && a.j < b.j);
-}
-
-// block (256 threads) reductions in a fixed order
-__device__ double block_max_d(double v, double* sh) {
-  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o, 64));
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[w] = v;
-  __syncthreads();
-  return fmax(fmax(sh[0], sh[1]), fmax(sh[2], sh[3]));
-}
-__device__ double block_sum_d(double v, double* sh) {
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[w] = v;
-  __syncthreads();
-  return ((sh[0] + sh[1]) + sh[2]) + sh[3];
-}
-__device__ int block_min_i(int v, int* sh) {
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) sh[w] = v;
-  __syncthreads();
-  return min(min(sh[0], sh[1]), min(sh[2], sh[3]));
-}
+constexpr int SEL_MAX = 1024;  // key clusters per row in cluster mode
 
 __global__ void zero_u64(unsigned long long* p, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
@@ -63,169 +33,6 @@ __global__ void zero_u64(unsigned long long* p, int n) {
 
 // pass 0: single pass (online off) or the first pass (online on, accumulate A_h)
 // pass 1: second pass of online Top-k (extend and write)
-__global__ __launch_bounds__(256) void select_rows(SelectArgs a, unsigned long long* __restrict__ acc,
-                                                   int pass) {
-  __shared__ RowEntry e[SEL_MAX];
-  __shared__ double qd[128];
-  __shared__ double red_d[4];
-  __shared__ int red_i[4];
-  __shared__ double tsum[256];
-  __shared__ uint32_t words[SEL_MAX / 32];
-  const int i = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-  const int Cq = a.Cq, Ck = a.Ck, d = a.d;
-  const int W = ceil_div(Ck, 32);
-  const int32_t* qo = a.q_off + size_t(h) * (Cq + 1);
-  const int qsize = qo[i + 1] - qo[i];
-  const bool online = a.online != 0;
-  const size_t row = size_t(h) * Cq + i;
-
-  // empty query cluster: selects nothing (and adds nothing to A_h)
-  if (qsize == 0) {
-    if (!online || pass == 1) {
-      for (int w = t; w < W; w += 256) a.mask[row * W + w] = 0u;
-      if (t == 0) {
-        a.counts[row] = 0;
-        if (a.init_counts) a.init_counts[row] = 0;
-        if (i == 0) a.head_topk[h] = online ? int(((long long)acc[h] + a.N - 1) / a.N) : 0;
-      }
-    } else if (t == 0 && a.init_counts) {
-      a.init_counts[row] = 0;
-    }
-    return;
-  }
-
-  if (t < d) qd[t] = double(a.qbar[row * d + t]);
-  int n2 = 2;
-  while (n2 < Ck) n2 <<= 1;
-  __syncthreads();
-
-  // logits
-  const int32_t* ko = a.k_off + size_t(h) * (Ck + 1);
-  double lmax = -__builtin_huge_val();
-  for (int j = t; j < n2; j += 256) {
-    double l = -__builtin_huge_val();
-    if (j < Ck) {
-      const int sz = ko[j + 1] - ko[j];
-      if (sz > 0) {
-        const float* kb = a.kbar + (size_t(h) * Ck + j) * d;
-        double s = 0.0;
-        for (int c = 0; c < d; ++c) s = fma(qd[c], double(kb[c]), s);
-        l = s * a.scale;
-        if (a.weighted) l += log(double(sz));
-      }
-    }
-    e[j].p = l;
-    e[j].j = j;
-    lmax = fmax(lmax, l);
-  }
-  lmax = block_max_d(lmax, red_d);
-  double zs = 0.0;
-  for (int j = t; j < n2; j += 256) {
-    const double l = e[j].p;
-    zs += (l == -__builtin_huge_val()) ? 0.0 : exp(l - lmax);
-  }
-  const double Z = block_sum_d(zs, red_d);
-  for (int j = t; j < n2; j += 256) {
-    const double l = e[j].p;
-    e[j].p = (l == -__builtin_huge_val()) ? -1.0 : exp(l - lmax) / Z;
-  }
-  __syncthreads();
-
-  // bitonic sort into rank order
-  for (int k = 2; k <= n2; k <<= 1) {
-    for (int jj = k >> 1; jj > 0; jj >>= 1) {
-      for (int x = t; x < n2; x += 256) {
-        const int y = x ^ jj;
-        if (y > x) {
-          RowEntry A = e[x], B = e[y];
-          const bool asc = (x & k) == 0;
-          if (asc ? before(B, A) : before(A, B)) {
-            e[x] = B;
-            e[y] = A;
-          }
-        }
-      }
-      __syncthreads();
-    }
-  }
-
-  // valid count, prefix masses (each thread owns a contiguous run of n2/256)
-  const int per = (n2 + 255) / 256;
-  const int r0 = t * per;
-  double loc = 0.0;
-  int nvalid = 0;
-  for (int r = r0; r < min(r0 + per, n2); ++r) {
-    if (e[r].p >= 0.0) {
-      loc += e[r].p;
-      ++nvalid;
-    }
-  }
-  tsum[t] = loc;
-  // exclusive scan of the per-thread sums in thread order
-  __syncthreads();
-  __shared__ double tpre[256];
-  if (t == 0) {
-    double run = 0.0;
-    for (int u = 0; u < 256; ++u) {
-      tpre[u] = run;
-      run += tsum[u];
-    }
-  }
-  // valid units: block sum of nvalid
-  int nv = nvalid;
-  for (int o = 32; o > 0; o >>= 1) nv += __shfl_xor(nv, o, 64);
-  __syncthreads();
-  if ((t & 63) == 0) red_i[t >> 6] = nv;
-  __syncthreads();
-  const int Vn = red_i[0] + red_i[1] + red_i[2] + red_i[3];
-
-  int tp;
-  const double P = a.top_p;
-  if (P >= 1.0) {
-    tp = Vn;
-  } else if (P <= 0.0) {
-    tp = 0;
-  } else {
-    int first = 0x7fffffff;
-    double run = tpre[t];
-    for (int r = r0; r < min(r0 + per, n2); ++r) {
-      if (e[r].p >= 0.0) {
-        run += e[r].p;
-        if (run >= P && first == 0x7fffffff) first = r + 1;
-      }
-    }
-    first = block_min_i(first, red_i);
-    tp = first == 0x7fffffff ? Vn : first;
-  }
-  const int tf = a.floor_units > 0 ? min(a.floor_units, Vn) : 0;
-  const int t_init = max(tp, tf);
-
-  if (online && pass == 0) {
-    if (t == 0) {
-      atomicAdd(&acc[h], (unsigned long long)((long long)qsize * t_init));
-      if (a.init_counts) a.init_counts[row] = t_init;
-    }
-    return;
-  }
-  int t_fin = t_init;
-  int kh = 0;
-  if (online) {
-    const long long A = (long long)acc[h];
-    kh = int((A + a.N - 1) / a.N);
-    if (t_init < kh) t_fin = max(t_init, min(kh, Vn));
-  }
-  for (int w = t; w < W; w += 256) words[w] = 0u;
-  __syncthreads();
-  for (int r = t; r < t_fin; r += 256) atomicOr(&words[e[r].j >> 5], 1u << (e[r].j & 31));
-  __syncthreads();
-  for (int w = t; w < W; w += 256) a.mask[row * W + w] = words[w];
-  if (t == 0) {
-    a.counts[row] = t_fin;
-    if (a.init_counts) a.init_counts[row] = t_init;
-    if (i == 0) a.head_topk[h] = kh;
-  }
-}
-
 // --------------------------------------------------------------------------
 // SCOPE subspace keys: lookup-table scores over combos, selection in keys
 // --------------------------------------------------------------------------
@@ -527,13 +334,266 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const dou
   }
 }
 
+
+// --------------------------------------------------------------------------
+// key clusters
+// --------------------------------------------------------------------------
+// Logits of a head: 32 x 32 output tiles; each output sums over d in order.
+constexpr int LT = 32;
+__global__ __launch_bounds__(256) void logits_kernel(SelectArgs a, double* __restrict__ L) {
+  __shared__ double qs[LT][LT + 1], ks[LT][LT + 1];
+  const int h = blockIdx.z, i0 = blockIdx.y * LT, j0 = blockIdx.x * LT, t = threadIdx.x;
+  const int ti = t >> 4, tj = t & 15;  // outputs (i0 + ti + 16 r, j0 + tj + 16 c), r, c < 2
+  double acc[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
+  for (int c0 = 0; c0 < a.d; c0 += LT) {
+    for (int e = t; e < LT * LT; e += 256) {
+      const int r = e / LT, c = e % LT;
+      const int qi = i0 + r, kj = j0 + r;
+      qs[r][c] = qi < a.Cq ? double(a.qbar[(size_t(h) * a.Cq + qi) * a.d + c0 + c]) : 0.0;
+      ks[r][c] = kj < a.Ck ? double(a.kbar[(size_t(h) * a.Ck + kj) * a.d + c0 + c]) : 0.0;
+    }
+    __syncthreads();
+    for (int c = 0; c < LT; ++c)
+#pragma unroll
+      for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) acc[r][cc] = fma(qs[ti + 16 * r][c], ks[tj + 16 * cc][c], acc[r][cc]);
+    __syncthreads();
+  }
+  const int32_t* ko = a.k_off + size_t(h) * (a.Ck + 1);
+#pragma unroll
+  for (int r = 0; r < 2; ++r)
+#pragma unroll
+    for (int cc = 0; cc < 2; ++cc) {
+      const int i = i0 + ti + 16 * r, j = j0 + tj + 16 * cc;
+      if (i >= a.Cq || j >= a.Ck) continue;
+      const int sz = ko[j + 1] - ko[j];
+      double l = -__builtin_huge_val();
+      if (sz > 0) {
+        l = acc[r][cc] * a.scale;
+        if (a.weighted) l += log(double(sz));
+      }
+      L[(size_t(h) * a.Cq + i) * a.Ck + j] = l;
+    }
+}
+
+constexpr int SW_M = SEL_MAX / 64;  // entries per lane
+constexpr unsigned long long NO_KEY = ~0ull;
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <typename V>
+__device__ __forceinline__ V wave_incl_scan(V v) {
+  const int lane = __lane_id();
+  for (int o = 1; o < 64; o <<= 1) {
+    const V y = __shfl_up(v, o, 64);
+    if (lane >= o) v += y;
+  }
+  return v;
+}
+
+// (key, j) position in rank order; j = INT_MAX: past every entry
+struct WBound {
+  unsigned long long key;
+  int j;
+};
+
+// One wavefront: entry j = lane + 64 m (m < SW_M) has order key key[m]
+// (NO_KEY: absent) and weight wt[m].  Returns the first entry, in ascending
+// (key, j), at which the cumulative weight reaches target (>= 1), or
+// {NO_KEY, INT_MAX} when the total stays below it.  8-bit radix passes over
+// the bits below the common prefix of the keys, then the equal keys in j order.
+__device__ WBound wave_select(const unsigned long long (&key)[SW_M], const unsigned long long (&wt)[SW_M],
+                              unsigned long long target, unsigned long long* hist) {
+  const int lane = __lane_id();
+  unsigned long long mn = NO_KEY, mx = 0ull;
+#pragma unroll
+  for (int m = 0; m < SW_M; ++m)
+    if (key[m] != NO_KEY) {
+      mn = key[m] < mn ? key[m] : mn;
+      mx = key[m] > mx ? key[m] : mx;
+    }
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long a = __shfl_xor(mn, o, 64), b = __shfl_xor(mx, o, 64);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  const WBound all{NO_KEY, 0x7fffffff};
+  if (mn == NO_KEY) return all;
+  unsigned long long prefix = mn, rem = target;
+  int hb = mn == mx ? -1 : 63 - __clzll(mn ^ mx);
+  if (hb >= 0) prefix = hb == 63 ? 0ull : (mn & ~((2ull << hb) - 1ull));
+  while (hb >= 0) {
+    const int shift = max(hb - 7, 0);
+    const unsigned long long dmask = (1ull << (hb - shift + 1)) - 1ull;
+    const int above = hb + 1;
+    for (int b = lane; b < 256; b += 64) hist[b] = 0ull;
+    wave_sync();
+#pragma unroll
+    for (int m = 0; m < SW_M; ++m)
+      if (key[m] != NO_KEY && (above >= 64 || (key[m] >> above) == (prefix >> above)))
+        atomicAdd(&hist[int((key[m] >> shift) & dmask)], wt[m]);
+    wave_sync();
+    unsigned long long c[4], loc = 0ull;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[q] = hist[4 * lane + q];
+      loc += c[q];
+    }
+    const unsigned long long incl = wave_incl_scan(loc);
+    unsigned long long run = incl - loc;
+    int bin = -1;
+    unsigned long long below = 0ull;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (bin < 0 && run < rem && rem <= run + c[q]) {
+        bin = 4 * lane + q;
+        below = run;
+      }
+      run += c[q];
+    }
+    const uint64_t bal = __ballot(bin >= 0);
+    wave_sync();
+    if (!bal) return all;
+    const int lead = __ffsll((unsigned long long)bal) - 1;
+    bin = __shfl(bin, lead, 64);
+    below = __shfl(below, lead, 64);
+    prefix |= (unsigned long long)bin << shift;
+    rem -= below;
+    if (shift == 0) break;
+    hb = shift - 1;
+  }
+  unsigned long long run = 0ull;
+#pragma unroll
+  for (int m = 0; m < SW_M; ++m) {
+    const bool f = key[m] == prefix;
+    const unsigned long long w = f ? wt[m] : 0ull;
+    const unsigned long long incl = wave_incl_scan(w);
+    const unsigned long long tot = __shfl(incl, 63, 64);
+    const uint64_t bal = __ballot(f && run + incl - w < rem && rem <= run + incl);
+    if (bal) return WBound{prefix, __ffsll((unsigned long long)bal) - 1 + 64 * m};
+    run += tot;
+  }
+  return all;
+}
+
+__device__ __forceinline__ bool through(unsigned long long k, int j, const WBound& b) {
+  return k != NO_KEY && (b.j == 0x7fffffff || k < b.key || (k == b.key && j <= b.j));
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// One wavefront per query cluster (four per workgroup).
+__global__ __launch_bounds__(256) void select_wave(SelectArgs a, const double* __restrict__ L,
+                                                   unsigned long long* __restrict__ acc, int pass) {
+  __shared__ unsigned long long hist[4][256];
+  __shared__ uint32_t words[4][SEL_MAX / 32];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int i = blockIdx.x * 4 + wv, h = blockIdx.y;
+  if (i >= a.Cq) return;
+  const int Ck = a.Ck, W = ceil_div(Ck, 32);
+  const size_t row = size_t(h) * a.Cq + i;
+  const int32_t* qo = a.q_off + size_t(h) * (a.Cq + 1);
+  const int qsize = qo[i + 1] - qo[i];
+  const bool online = a.online != 0;
+  if (qsize == 0) {  // selects nothing and adds nothing to A_h
+    if (!online || pass == 1) {
+      for (int x = lane; x < W; x += 64) a.mask[row * W + x] = 0u;
+      if (lane == 0) {
+        a.counts[row] = 0;
+        if (a.init_counts) a.init_counts[row] = 0;
+        if (i == 0) a.head_topk[h] = online ? int(((long long)acc[h] + a.N - 1) / a.N) : 0;
+      }
+    } else if (lane == 0 && a.init_counts) {
+      a.init_counts[row] = 0;
+    }
+    return;
+  }
+  const double* lr = L + row * Ck;
+  double l[SW_M];
+  double mx = -__builtin_huge_val();
+#pragma unroll
+  for (int m = 0; m < SW_M; ++m) {
+    const int j = lane + 64 * m;
+    l[m] = j < Ck ? lr[j] : -__builtin_huge_val();
+    mx = fmax(mx, l[m]);
+  }
+  for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+  double z = 0.0;
+#pragma unroll
+  for (int m = 0; m < SW_M; ++m)
+    if (l[m] != -__builtin_huge_val()) z += exp(l[m] - mx);
+  for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
+  unsigned long long key[SW_M], ms[SW_M], one[SW_M];
+  int nv = 0;
+#pragma unroll
+  for (int m = 0; m < SW_M; ++m) {
+    const bool v = l[m] != -__builtin_huge_val();
+    key[m] = v ? order_key(l[m]) : NO_KEY;
+    ms[m] = v ? (unsigned long long)llrint(exp(l[m] - mx) / z * MASS_ONE) : 0ull;
+    one[m] = v ? 1ull : 0ull;
+    nv += v ? 1 : 0;
+  }
+  const int Vn = wave_sum_i32(nv);
+  auto count_through = [&](const WBound& b) {
+    int c = 0;
+#pragma unroll
+    for (int m = 0; m < SW_M; ++m) c += through(key[m], lane + 64 * m, b) ? 1 : 0;
+    return wave_sum_i32(c);
+  };
+  const double P = a.top_p;
+  int np;
+  if (P >= 1.0) np = Vn;
+  else if (P <= 0.0) np = 0;
+  else np = count_through(wave_select(key, ms, (unsigned long long)llrint(P * MASS_ONE), hist[wv]));
+  const int nf = a.floor_units > 0 ? min(a.floor_units, Vn) : 0;
+  const int t_init = max(np, nf);
+  if (online && pass == 0) {
+    if (lane == 0) {
+      atomicAdd(&acc[h], (unsigned long long)((long long)qsize * t_init));
+      if (a.init_counts) a.init_counts[row] = t_init;
+    }
+    return;
+  }
+  int t_fin = t_init, kh = 0;
+  if (online) {
+    kh = int(((long long)acc[h] + a.N - 1) / a.N);
+    if (t_init < kh) t_fin = min(kh, Vn);
+  }
+  uint32_t* wd = words[wv];
+  for (int x = lane; x < W; x += 64) wd[x] = 0u;
+  wave_sync();
+  if (t_fin > 0) {
+    const WBound b = wave_select(key, one, (unsigned long long)t_fin, hist[wv]);
+#pragma unroll
+    for (int m = 0; m < SW_M; ++m) {
+      const int j = lane + 64 * m;
+      if (through(key[m], j, b)) atomicOr(&wd[j >> 5], 1u << (j & 31));
+    }
+  }
+  wave_sync();
+  for (int x = lane; x < W; x += 64) a.mask[row * W + x] = wd[x];
+  if (lane == 0) {
+    a.counts[row] = t_fin;
+    if (a.init_counts) a.init_counts[row] = t_init;
+    if (i == 0) a.head_topk[h] = kh;
+  }
+}
+
 }  // namespace
 
 size_t select_scratch(int H, int Cq, int Ck, int subspace) {
-  (void)Cq;
   Arena a{nullptr, 0, 0};
   a.get<unsigned long long>(size_t(H));
   if (subspace) a.get<double>(size_t(H) * Ck);
+  else a.get<double>(size_t(H) * Cq * Ck);
   return a.used;
 }
 
@@ -553,13 +613,16 @@ hipError_t select_run(const SelectArgs& a, Arena& s, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  if (a.Ck > SEL_MAX || a.d > 128) return hipErrorInvalidValue;
+  if (a.Ck > SEL_MAX || a.d % LT) return hipErrorInvalidValue;
+  double* L = s.get<double>(size_t(a.H) * a.Cq * a.Ck);
+  logits_kernel<<<dim3(ceil_div(a.Ck, LT), ceil_div(a.Cq, LT), a.H), 256, 0, st>>>(a, L);
+  const dim3 gw(ceil_div(a.Cq, 4), a.H);
   if (a.online) {
     zero_u64<<<ceil_div(a.H, 256), 256, 0, st>>>(acc, a.H);
-    select_rows<<<g, 256, 0, st>>>(a, acc, 0);
-    select_rows<<<g, 256, 0, st>>>(a, acc, 1);
+    select_wave<<<gw, 256, 0, st>>>(a, L, acc, 0);
+    select_wave<<<gw, 256, 0, st>>>(a, L, acc, 1);
   } else {
-    select_rows<<<g, 256, 0, st>>>(a, acc, 0);
+    select_wave<<<gw, 256, 0, st>>>(a, L, acc, 0);
   }
   return hipGetLastError();
 }
