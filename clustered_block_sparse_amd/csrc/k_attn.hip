@@ -196,17 +196,23 @@ __global__ __launch_bounds__(128) void comp_prep_kernel(const float* __restrict_
   if (t == 0) logsz[size_t(h) * Ckp + j] = sz > 0 ? logf(float(sz)) : -__builtin_huge_valf();
 }
 
-// Workgroup -> (head, tile).  Workgroups are handed to the 8 XCDs round-robin
-// by linear id; the remap gives each XCD one contiguous run of tiles (heads in
-// order), so the key/value rows a head's neighbouring query clusters share are
-// reused from that XCD's L2.  The grid is padded to a multiple of 8.
-__device__ __forceinline__ void map_tile(int maxT, int H, int& h, int& tix) {
-  const int total = maxT * H;
-  const int per = (total + 7) / 8;
-  const int b = blockIdx.x;
-  const int lin = (b & 7) * per + (b >> 3);
-  h = lin / maxT;  // lin >= total -> h >= H: padding workgroup
-  tix = lin % maxT;
+// Workgroup -> (head, tile).  Workgroups go to the 8 XCDs round-robin by
+// linear id, and each XCD starts them in id order.  XCD x takes, head after
+// head, the x-th eighth of that head's tiles: every XCD works on a contiguous
+// run of neighbouring query clusters (whose key blocks its own L2 can share),
+// while all XCDs stay on the same one or two heads at a time, whose K and V
+// fit the memory-side cache together.  Each head owns ceil(maxT / 8) slots
+// per XCD, of which the first ceil(ntiles / 8) carry tiles, so padding (maxT
+// is only an upper bound) is spread evenly over the XCDs.  The grid is
+// 8 * H * ceil(maxT / 8); h = H or tix = -1 marks a padding workgroup.
+__device__ __forceinline__ void map_tile(int maxT, int H, const int32_t* ntiles, int& h, int& tix) {
+  const int t8 = (maxT + 7) / 8;
+  const int b = blockIdx.x, x = b & 7, k = b >> 3;
+  h = k / t8;
+  tix = -1;
+  if (h >= H) return;
+  const int nt = ntiles[h], n8 = (nt + 7) / 8, kk = k % t8;
+  if (kk < n8 && x * n8 + kk < nt) tix = x * n8 + kk;
 }
 
 // stage one chunk of ranges in LDS: rs[k] = start, rp[k] = prefix length
@@ -335,8 +341,8 @@ __global__ __launch_bounds__(128) void attn_simple(AttnArgs a, Prep p, float sca
   __shared__ int fsh[2];
   __shared__ float bias[32];
   int h, tix;
-  map_tile(p.maxT, a.H, h, tix);
-  if (h >= a.H || tix >= p.ntiles[h]) return;
+  map_tile(p.maxT, a.H, p.ntiles, h, tix);
+  if (h >= a.H || tix < 0) return;
   const int4 td = p.tiles[size_t(h) * p.maxT + tix];
   const int i = td.x, p0 = td.y, nr = td.z;
   const int t = threadIdx.x;
@@ -514,8 +520,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
   __shared__ __attribute__((aligned(16))) MfmaLds<D> S;
 
   int h, tix;
-  map_tile(p.maxT, a.H, h, tix);
-  if (h >= a.H || tix >= p.ntiles[h]) return;
+  map_tile(p.maxT, a.H, p.ntiles, h, tix);
+  if (h >= a.H || tix < 0) return;
   const int4 td = p.tiles[size_t(h) * p.maxT + tix];
   const int i = td.x, p0 = td.y, nr = td.z;
   if ((p.raligned[size_t(h) * a.Cq + i] != 0) != ALIGNED) return;
@@ -896,7 +902,7 @@ hipError_t attn_run(const AttnArgs& a, Arena& s, hipStream_t st) {
   if (a.compensate)
     comp_prep_kernel<<<dim3(p.Ckp, a.H), 128, 0, st>>>(a.kbar, a.vbar, a.k_off, a.Ck, p.Ckp, a.d,
                                                        p.kbh, p.kbl, p.vbt, p.kbf, p.vbf, p.logsz);
-  const int grid = 8 * ceil_div(p.maxT * a.H, 8);
+  const int grid = 8 * a.H * ceil_div(p.maxT, 8);
   const float sl2 = a.scale * LOG2E;
   const dim3 gv(p.NB, a.H);
   if (a.dtype == SA_BF16) {
