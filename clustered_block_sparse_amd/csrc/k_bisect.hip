@@ -517,8 +517,10 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ x, Top
 //         the segment's histogram;
 //   find: the bin holding rank n_left and the rank inside it;
 //   cand: that bin's keys with their positions, as distinct 64-bit values;
-//   pick: the exact rank among them (a radix search in LDS), or, when the
-//         bin overflows CAND_CAP, a radix search over all of the segment's keys.
+//   pick: the exact rank among them (up to 1024: each thread counts the
+//         candidates below its own; up to CAND_CAP: a radix search in LDS),
+//         or, when the bin overflows CAND_CAP, a radix search over all of the
+//         segment's keys.
 // Only integer atomics are used; the selected (key, position) is unique, so
 // the result does not depend on their order.
 __device__ __forceinline__ int bin_of(uint32_t v, uint2 mm) {
@@ -616,6 +618,17 @@ __global__ __launch_bounds__(1024) void pick_kernel(TopBufs b) {
   uint2 res;
   if (sb.x < 0) {
     res = make_uint2(mm.x, uint32_t(sg.x + sg.z - 1));  // all keys equal: rank k is position k-1
+  } else if (m <= 1024) {
+    // distinct values: the one with exactly sb.y - 1 smaller candidates
+    const unsigned long long mine = t < m ? b.cand[si * CAND_CAP + t] : 0ull;
+    if (t < m) cand[t] = mine;
+    __syncthreads();
+    int below = 0;
+    for (int u = 0; u < m; ++u) below += cand[u] < mine ? 1 : 0;
+    if (t < m && below == sb.y - 1) cand[CAND_CAP - 1] = mine;
+    __syncthreads();
+    const unsigned long long r = cand[CAND_CAP - 1];
+    res = make_uint2(uint32_t(r >> 32), uint32_t(r & 0xFFFFFFFFull));
   } else if (m <= CAND_CAP) {
     for (int i = t; i < m; i += 1024) cand[i] = b.cand[si * CAND_CAP + i];
     __syncthreads();
