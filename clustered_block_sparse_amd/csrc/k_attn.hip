@@ -44,6 +44,8 @@ constexpr int TQ = 128;     // query rows per workgroup (upper bound)
 constexpr int RCH = 512;    // ranges staged in LDS at a time
 constexpr int ALIGNED_MAX_CK = 4096;  // key clusters up to which rows get precomputed ranges
 constexpr float LOG2E = 1.4426950408889634f;
+// word 3 of a raw buffer resource on gfx9-family parts (32-bit data format)
+constexpr int BUF_DWORD3 = 0x00020000;
 
 struct Prep {
   int4* tiles;        // [H][maxT] {cluster, first position, rows, 0}
@@ -454,6 +456,13 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8_t a, bf16x8_t b, floatx16 c) {
 
 __device__ __forceinline__ bf16x8_t as_bf8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
+// 16 bytes per lane from a raw buffer over [base, base + nbytes) into LDS
+// (lane l of the wave lands at lds + 16 l); `off` is the lane's byte offset
+__device__ __forceinline__ void buf_load_lds16(const void* base, int nbytes, bf16_t* lds, uint32_t off) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, BUF_DWORD3);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, off, 0, 0, 0);
+}
+
 #define BF16_ONES (__builtin_bit_cast(bf16x2_t, 0x3F803F80u))  // (1.0, 1.0)
 
 // two floats -> packed bf16 pair (hardware round-to-nearest-even)
@@ -525,7 +534,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
   const int4 td = p.tiles[size_t(h) * p.maxT + tix];
   const int i = td.x, p0 = td.y, nr = td.z;
   if ((p.raligned[size_t(h) * a.Cq + i] != 0) != ALIGNED) return;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // the wave index is uniform across the wave: keep it (and what derives from it) in SGPRs
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, hi = lane >> 5;
   const int N = a.N;
 
@@ -551,14 +561,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
 
   const bf16_t* kh = (const bf16_t*)a.k_perm + size_t(h) * N * D;
 
+  // S^T = K Q^T for one 64-key tile.  Each 32-key half reads all its K
+  // fragments before its MFMAs, so LDS latency is paid once per half.
   auto qk = [&](floatx16 (&s)[2], const bf16_t* Kb) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
+      uint4 kf[DS];
 #pragma unroll
-      for (int st = 0; st < DS; ++st) {
-        const uint4 u = *reinterpret_cast<const uint4*>(Kb + toff<DG>(32 * kt + col, 2 * st + hi));
-        s[kt] = mfma32(as_bf8(u), qf[st], s[kt]);
-      }
+      for (int st = 0; st < DS; ++st)
+        kf[st] = *reinterpret_cast<const uint4*>(Kb + toff<DG>(32 * kt + col, 2 * st + hi));
+#pragma unroll
+      for (int st = 0; st < DS; ++st) s[kt] = mfma32(as_bf8(kf[st]), qf[st], s[kt]);
     }
   };
 
@@ -632,11 +645,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
       for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
     qk(s, Kb);
     if (nvalid < KT) {  // keys past the end of the selection: -inf
+      // key of entry r of half kt is 32 kt + 8 (r / 4) + 4 hi + r % 4; compare
+      // the constant part against nvalid - 4 hi
+      const int lim = nvalid - 4 * hi;
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3) >= nvalid) s[kt][r] = -__builtin_huge_valf();
+          if (32 * kt + 8 * (r >> 2) + (r & 3) >= lim) s[kt][r] = -__builtin_huge_valf();
     }
     softmax_pv(s, Vb, sl2);
   };
@@ -651,18 +667,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     // (their scores are masked).
     const bf16_t* vth = p.vt + size_t(h) * p.NB * D * KT;
     int ri = 0, pos = R > 0 ? rg[0].x : 0, rend = R > 0 ? rg[0].y : 0;
-    auto issue = [&](bf16_t* Kd, bf16_t* Vd, int pos0, int nvalid) {
-      const bf16_t* vb = vth + size_t(pos0 / KT) * D * KT;
+    // Buffer resources over this head's K rows and V^T blocks: a load is the
+    // resource (SGPRs) plus one byte offset per lane.  Offsets of a lane's
+    // chunks inside a tile are fixed, so only the tile base is added per load.
+    const int kbytes = N * D * 2, vbytes = p.NB * D * KT * 2;
+    uint32_t koff[CK], voff[CK];
 #pragma unroll
-      for (int q = 0; q < CK; ++q) {
-        const int s0 = (4 * q + w) * 64;  // first chunk of this wave's load
-        const int sl = s0 + lane;
-        const int r = sl / DG, kc = (sl % DG) ^ swz<DG>(r);
-        __builtin_amdgcn_global_load_lds(kh + size_t(pos0 + min(r, nvalid - 1)) * D + kc * 8, Kd + s0 * 8,
-                                         16, 0, 0);
-        const int d = sl / VG, vc = (sl % VG) ^ swz<VG>(d);
-        __builtin_amdgcn_global_load_lds(vb + d * KT + vc * 8, Vd + s0 * 8, 16, 0, 0);
+    for (int q = 0; q < CK; ++q) {
+      const int sl = (4 * q + w) * 64 + lane;  // chunk of this lane's q-th load
+      const int r = sl / DG, kc = (sl % DG) ^ swz<DG>(r);
+      koff[q] = uint32_t(r * D + kc * 8) * 2;
+      const int d = sl / VG, vc = (sl % VG) ^ swz<VG>(d);
+      voff[q] = uint32_t(d * KT + vc * 8) * 2;
+    }
+    auto issue = [&](bf16_t* Kd, bf16_t* Vd, int pos0, int nvalid) {
+      const uint32_t kb = uint32_t(pos0) * (D * 2);
+      const uint32_t vb = uint32_t(pos0 / KT) * (D * KT * 2);
+      if (nvalid == KT) {
+#pragma unroll
+        for (int q = 0; q < CK; ++q)
+          buf_load_lds16(kh, kbytes, Kd + (4 * q + w) * 512, kb + koff[q]);
+      } else {
+        // partial tile: rows past the end of the range repeat its last row
+        // (their scores are masked), so no load leaves the head's keys
+#pragma unroll
+        for (int q = 0; q < CK; ++q) {
+          const int r = ((4 * q + w) * 64 + lane) / DG;
+          const int dr = min(r, nvalid - 1) - r;
+          buf_load_lds16(kh, kbytes, Kd + (4 * q + w) * 512,
+                         kb + koff[q] + uint32_t(dr * D * 2));
+        }
       }
+#pragma unroll
+      for (int q = 0; q < CK; ++q)
+        buf_load_lds16(vth, vbytes, Vd + (4 * q + w) * 512, vb + voff[q]);
     };
     auto step = [&](const bf16_t* Kc, const bf16_t* Vc, bf16_t* Kn, bf16_t* Vn) {
       const int nvalid = min(KT, rend - pos);
