@@ -40,6 +40,8 @@ typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int KT = 64;      // keys per tile
+constexpr int HK = 32;      // keys per half tile (one 32x32 MFMA block)
+constexpr int HG = HK / 8;  // 16-byte chunks of a row of a V^T half tile
 constexpr int TQ = 128;     // query rows per workgroup (upper bound)
 constexpr int RCH = 512;    // ranges staged in LDS at a time
 constexpr int ALIGNED_MAX_CK = 4096;  // key clusters up to which rows get precomputed ranges
@@ -149,12 +151,14 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__
 // avoided by XOR-swizzling the 16-byte chunks of a row, so whole tiles can
 // arrive by direct global->LDS loads (lane l of such a load lands at 16 l).
 //   K tile:   KT rows of D bf16; chunk c of row r at chunk c ^ swz(r).
-//   V^T tile: D rows of KT keys; chunk c of row d at chunk c ^ swz(d); keys in
-//             MFMA order: within every 16-key group keys 4..7 and 8..11 trade
-//             places, so the 8 keys one lane feeds a 32x32x16 product (keys
-//             4hi..4hi+3 and 8+4hi..8+4hi+3) form one chunk.
+//   V^T tile: two half tiles (keys 0..31 and 32..63), each D rows of 32 keys;
+//             chunk c of row d at chunk c ^ swz(d); keys in MFMA order: within
+//             every 16-key group keys 4..7 and 8..11 trade places, so the 8
+//             keys one lane feeds a 32x32x16 product (keys 4hi..4hi+3 and
+//             8+4hi..8+4hi+3) form one chunk.
 // swz puts the chunks any 16 consecutive rows (or any 8) read at one column on
-// distinct banks, for 64 as for 32 LDS banks.
+// distinct banks, for 64 as for 32 LDS banks; for the 4-chunk rows of V^T half
+// tiles the choice was checked with the LDS bank-conflict counter.
 // ---------------------------------------------------------------------------
 __host__ __device__ __forceinline__ int mfma_key(int k) {  // an involution
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
@@ -162,7 +166,8 @@ __host__ __device__ __forceinline__ int mfma_key(int k) {  // an involution
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (CPR == 16) return r & 15;
-  else return (r & 7) ^ ((r >> 3) & 1);
+  else if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
+  else return (r >> 2) & 3;  // CPR == 4 (measured conflict-free for the P V reads)
 }
 // element offset of 16-byte chunk c of row r in a tile of CPR chunks per row
 template <int CPR>
@@ -463,6 +468,20 @@ __device__ __forceinline__ void buf_load_lds16(const void* base, int nbytes, bf1
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, off, 0, 0, 0);
 }
 
+// max and sum of a value over lanes l and l ^ 32.  v_permlane32_swap trades
+// the upper half of one copy with the lower half of the other (no LDS round
+// trip), so every lane finds both values among the two results.
+__device__ __forceinline__ float pair_max(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, uint32_t(r[0])), __builtin_bit_cast(float, uint32_t(r[1])));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __builtin_bit_cast(float, uint32_t(r[0])) + __builtin_bit_cast(float, uint32_t(r[1]));
+}
+
 #define BF16_ONES (__builtin_bit_cast(bf16x2_t, 0x3F803F80u))  // (1.0, 1.0)
 
 // two floats -> packed bf16 pair (hardware round-to-nearest-even)
@@ -514,18 +533,20 @@ __global__ __launch_bounds__(256) void vt_kernel(const bf16_t* __restrict__ v, i
 // gathers rows of arbitrary ranges and transposes V while staging it.  Each
 // workgroup runs in the instantiation matching its row and exits in the other.
 template <int D, bool ALIGNED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && ALIGNED ? 4 : 2, D == 64 && ALIGNED ? 4 : 2))) void attn_mfma(AttnArgs a, Prep p, float sl2) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && ALIGNED ? 3 : 2, D == 64 && ALIGNED ? 3 : 2))) void attn_mfma(AttnArgs a, Prep p, float sl2) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int DS = D / 16;         // MFMA k-steps over d
   constexpr int DT = D / 32;         // 32-row tiles of d in O^T
   constexpr int KCH = D / 4;         // general path: K elements per thread (one row quarter)
   constexpr int KPT = D / 32;        // general path: V keys per thread
   constexpr int DG = D / 8;          // 16-byte chunks of a K / Q / O row
-  constexpr int VG = KT / 8;         // 16-byte chunks of a V^T row
-  constexpr int CK = KT * D / 8 / 256;  // 16-byte chunks per thread of a K (or V^T) tile
-  // four separate tiles: as distinct objects, a direct load into one pair is
-  // visibly independent of reads from the other
-  __shared__ __attribute__((aligned(16))) bf16_t K0[KT * D], K1[KT * D], V0[D * KT], V1[D * KT];
+  constexpr int CK = KT * D / 8 / 256;  // 16-byte chunks per thread of a K tile
+  constexpr int CH = CK / 2;            // ... of a V^T half tile
+  // Six separate tiles: K double buffered, and V^T split into its lower and
+  // upper 32 keys (VL, VH), each double buffered.  As distinct objects, a
+  // direct load into one is visibly independent of reads from the others.
+  __shared__ __attribute__((aligned(16))) bf16_t K0[KT * D], K1[KT * D];
+  __shared__ __attribute__((aligned(16))) bf16_t VL0[D * HK], VL1[D * HK], VH0[D * HK], VH1[D * HK];
   __shared__ __attribute__((aligned(16))) MfmaLds<D> S;
 
   int h, tix;
@@ -561,31 +582,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
 
   const bf16_t* kh = (const bf16_t*)a.k_perm + size_t(h) * N * D;
 
-  // S^T = K Q^T for one 64-key tile.  Each 32-key half reads all its K
-  // fragments before its MFMAs, so LDS latency is paid once per half.
-  auto qk = [&](floatx16 (&s)[2], const bf16_t* Kb) {
+  // Score tiles are handled in 32-key halves: half kt of a 64-key tile is one
+  // 32x32 block of S^T, whose lane (col, hi) holds keys
+  // 32 kt + 8 (r / 4) + 4 hi + r % 4 (r = 0..15) of query column col.
+  auto zero16 = [&](floatx16& s) {
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-      uint4 kf[DS];
-#pragma unroll
-      for (int st = 0; st < DS; ++st)
-        kf[st] = *reinterpret_cast<const uint4*>(Kb + toff<DG>(32 * kt + col, 2 * st + hi));
-#pragma unroll
-      for (int st = 0; st < DS; ++st) s[kt] = mfma32(as_bf8(kf[st]), qf[st], s[kt]);
-    }
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
   };
-
-  // Online-softmax update and P V for one tile.  The log2-domain logit of an
-  // entry is s * lsc: raw scores with lsc = scale * log2(e), or logits already
-  // formed (masked keys -inf) with lsc = 1.  The row sum adds the bf16 P
-  // values the P V product consumes (dot2 against (1, 1)).
-  auto softmax_pv = [&](floatx16 (&s)[2], const bf16_t* Vb, float lsc) {
-    float mx = -__builtin_huge_valf();
+  // S^T half kt = K[32 kt .. 32 kt + 31] Q^T; all K fragments are read first,
+  // so LDS latency is paid once per half
+  auto qk_half = [&](floatx16& s, const bf16_t* Kb, int kt) {
+    uint4 kf[DS];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int st = 0; st < DS; ++st)
+      kf[st] = *reinterpret_cast<const uint4*>(Kb + toff<DG>(32 * kt + col, 2 * st + hi));
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kt][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * lsc;
+    for (int st = 0; st < DS; ++st) s = mfma32(as_bf8(kf[st]), qf[st], s);
+  };
+  // keys of half kt at or past nvalid -> -inf (the constant part of the key
+  // index is compared with nvalid - 32 kt - 4 hi)
+  auto mask_half = [&](floatx16& s, int nvalid, int kt) {
+    const int lim = nvalid - 32 * kt - 4 * hi;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r >> 2) + (r & 3) >= lim) s[r] = -__builtin_huge_valf();
+  };
+  // log2-domain maximum of a half's scores over the query column
+  auto max_half = [&](const floatx16& s, float lsc) {
+    float mx = s[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+    return pair_max(mx) * lsc;
+  };
+  // lazy rescale: the running maximum moves only when a block's maximum
+  // exceeds it by more than 2^8, so probabilities stay below 256
+  auto rescale_to = [&](float mx) {
     float alpha = 1.f;
     if (mx > m + 8.f) {
       alpha = __builtin_amdgcn_exp2f(m - mx);  // m = -inf -> 0
@@ -598,91 +629,90 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
     }
-    // every tile holds a valid key, so m is finite here and -inf maps to 0
+  };
+  // P = 2^(s lsc - m) as packed bf16 pairs, the B operand of P V; the row sum
+  // adds the same bf16 values (dot2 against (1, 1))
+  auto exp_half = [&](const floatx16& s, float lsc, uint32_t (&pk)[8]) {
     const float nm = -m;
-    uint32_t pk[2][8];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
+    for (int r = 0; r < 16; r += 2) {
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[r], lsc, nm));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], lsc, nm));
+      pk[r >> 1] = pack2(e0, e1);
+      lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[r >> 1]), BF16_ONES, lsum, false);
+    }
+  };
+  // O^T += V^T P^T over one 32-key half (Vh: that half of the V^T tile)
+  auto pv_half = [&](const uint32_t (&pk)[8], const bf16_t* Vh) {
 #pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[kt][r], lsc, nm));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[kt][r + 1], lsc, nm));
-        pk[kt][r >> 1] = pack2(e0, e1);
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[kt][r >> 1]), BF16_ONES, lsum, false);
-      }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kt = ks >> 1, half = ks & 1;
-      const bf16x8_t pf = as_bf8(make_uint4(pk[kt][4 * half + 0], pk[kt][4 * half + 1],
-                                            pk[kt][4 * half + 2], pk[kt][4 * half + 3]));
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8_t pf = as_bf8(make_uint4(pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint4 u = *reinterpret_cast<const uint4*>(Vb + toff<VG>(32 * dt + col, 2 * ks + hi));
+        const uint4 u = *reinterpret_cast<const uint4*>(Vh + toff<HG>(32 * dt + col, 2 * ks + hi));
         oacc[dt] = mfma32(as_bf8(u), pf, oacc[dt]);
       }
     }
   };
-
-  // scores -> log2-domain logits in place (bias per key, keys >= nvalid masked)
-  auto to_logits = [&](floatx16 (&s)[2], int nvalid, const float* bias_l2) {
+  // One whole 64-key tile, unpipelined (general path and compensation): the
+  // scores (already log2-domain logits when lsc = 1) of both halves, then the
+  // rescale, then P V.
+  auto softmax_pv = [&](floatx16 (&s)[2], const bf16_t* VLb, const bf16_t* VHb, float lsc) {
+    rescale_to(fmaxf(max_half(s[0], lsc), max_half(s[1], lsc)));
+    uint32_t pk[8];
+    exp_half(s[0], lsc, pk);
+    pv_half(pk, VLb);
+    exp_half(s[1], lsc, pk);
+    pv_half(pk, VHb);
+  };
+  // scores -> log2-domain logits in place (bias per key)
+  auto to_logits = [&](floatx16 (&s)[2], const float* bias_l2) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
-        float x = s[kt][r] * sl2;
-        if (bias_l2) x += bias_l2[key];
-        if (key >= nvalid) x = -__builtin_huge_valf();
-        s[kt][r] = x;
+        s[kt][r] = s[kt][r] * sl2 + bias_l2[key];
       }
   };
-
-  auto compute_tile = [&](const bf16_t* Kb, const bf16_t* Vb, int nvalid) {
+  auto compute_tile = [&](const bf16_t* Kb, const bf16_t* VLb, const bf16_t* VHb, int nvalid) {
     floatx16 s[2];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-    qk(s, Kb);
-    if (nvalid < KT) {  // keys past the end of the selection: -inf
-      // key of entry r of half kt is 32 kt + 8 (r / 4) + 4 hi + r % 4; compare
-      // the constant part against nvalid - 4 hi
-      const int lim = nvalid - 4 * hi;
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * kt + 8 * (r >> 2) + (r & 3) >= lim) s[kt][r] = -__builtin_huge_valf();
+    for (int kt = 0; kt < 2; ++kt) {
+      zero16(s[kt]);
+      qk_half(s[kt], Kb, kt);
+      if (nvalid < KT) mask_half(s[kt], nvalid, kt);
     }
-    softmax_pv(s, Vb, sl2);
+    softmax_pv(s, VLb, VHb, sl2);
   };
 
   if constexpr (ALIGNED) {
     const int R = p.rcount[size_t(h) * a.Cq + i];
     const int2* rg = p.ranges + (size_t(h) * a.Cq + i) * p.Rmax;
     // ---------------- selected keys, 64-aligned ranges: whole-block tiles ----
-    // Both tiles of a block arrive by direct global->LDS loads: the lanes of a
-    // load pick their source chunks so that the lane-linear LDS placement is
-    // the swizzled layout.  Rows past the end of a range repeat its last row
-    // (their scores are masked).
+    // Every tile arrives by direct buffer->LDS loads: the lanes of a load pick
+    // their source chunks so that the lane-linear LDS placement is the
+    // swizzled layout.  A load is the buffer resource (SGPRs) plus one byte
+    // offset per lane; a lane's offsets inside a tile are fixed, so only the
+    // tile base is added per load.
     const bf16_t* vth = p.vt + size_t(h) * p.NB * D * KT;
     int ri = 0, pos = R > 0 ? rg[0].x : 0, rend = R > 0 ? rg[0].y : 0;
-    // Buffer resources over this head's K rows and V^T blocks: a load is the
-    // resource (SGPRs) plus one byte offset per lane.  Offsets of a lane's
-    // chunks inside a tile are fixed, so only the tile base is added per load.
     const int kbytes = N * D * 2, vbytes = p.NB * D * KT * 2;
-    uint32_t koff[CK], voff[CK];
+    uint32_t koff[CK], voff[CH];
 #pragma unroll
     for (int q = 0; q < CK; ++q) {
-      const int sl = (4 * q + w) * 64 + lane;  // chunk of this lane's q-th load
+      const int sl = (4 * q + w) * 64 + lane;  // K tile chunk of this lane's q-th load
       const int r = sl / DG, kc = (sl % DG) ^ swz<DG>(r);
       koff[q] = uint32_t(r * D + kc * 8) * 2;
-      const int d = sl / VG, vc = (sl % VG) ^ swz<VG>(d);
-      voff[q] = uint32_t(d * KT + vc * 8) * 2;
     }
-    auto issue = [&](bf16_t* Kd, bf16_t* Vd, int pos0, int nvalid) {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const int sl = (4 * q + w) * 64 + lane;  // V^T half-tile chunk
+      const int d = sl / HG, c = (sl % HG) ^ swz<HG>(d);
+      voff[q] = uint32_t(d * KT + c * 8) * 2;  // lower half; the upper one is 64 bytes on
+    }
+    auto issue_k = [&](bf16_t* Kd, int pos0, int nvalid) {
       const uint32_t kb = uint32_t(pos0) * (D * 2);
-      const uint32_t vb = uint32_t(pos0 / KT) * (D * KT * 2);
       if (nvalid == KT) {
 #pragma unroll
         for (int q = 0; q < CK; ++q)
@@ -698,31 +728,126 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
                          kb + koff[q] + uint32_t(dr * D * 2));
         }
       }
+    };
+    // half kt (0: keys 0..31, 1: keys 32..63) of the V^T block holding pos0
+    auto issue_v = [&](bf16_t* Vd, int pos0, int kt) {
+      const uint32_t vb = uint32_t(pos0 / KT) * (D * KT * 2) + 64 * kt;
 #pragma unroll
-      for (int q = 0; q < CK; ++q)
+      for (int q = 0; q < CH; ++q)
         buf_load_lds16(vth, vbytes, Vd + (4 * q + w) * 512, vb + voff[q]);
     };
-    auto step = [&](const bf16_t* Kc, const bf16_t* Vc, bf16_t* Kn, bf16_t* Vn) {
-      const int nvalid = min(KT, rend - pos);
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of the tile landed
-      __syncthreads();                     // every wave's, and the other pair is free
+    // every wave's loads issued before this point have landed, and every
+    // wave is done reading the buffers the next loads overwrite
+    auto sync_loads = [&]() {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      __syncthreads();
+    };
+    // Move the cursor to the next whole 64-key tile.  False once the ranges
+    // are done, or when the next tile is partial: only the last tile of a
+    // range ending at N can be, and it is kept aside as the tail.
+    bool have_tail = false;
+    int tail_pos = 0, tail_nv = 0;
+    auto next_full = [&]() -> bool {
       pos += KT;
       if (pos >= rend) {
-        ++ri;
-        if (ri < R) {
-          const int2 r2 = rg[ri];
-          pos = r2.x;
-          rend = r2.y;
-        }
+        if (++ri >= R) return false;
+        const int2 r2 = rg[ri];
+        pos = r2.x;
+        rend = r2.y;
       }
-      if (ri < R) issue(Kn, Vn, pos, min(KT, rend - pos));
-      compute_tile(Kc, Vc, nvalid);
+      if (rend - pos < KT) {
+        have_tail = true;
+        tail_pos = pos;
+        tail_nv = rend - pos;
+        return false;
+      }
+      return true;
     };
-    if (R > 0) issue(K0, V0, pos, min(KT, rend - pos));
-    while (ri < R) {
-      step(K0, V0, K1, V1);
-      if (ri >= R) break;
-      step(K1, V1, K0, V0);
+    // Software pipeline over the whole tiles, in 32-key halves.  Each half
+    // step forms the scores of one half while the probabilities of the
+    // previous half are exponentiated, then accumulates P V of the previous
+    // half while the new half's row maximum is taken:
+    //   tile n, half 0:  S(n,0) | P(n-1,1);  P(n-1,1) V(n-1,hi) | max S(n,0)
+    //   tile n, half 1:  S(n,1) | P(n,0);    P(n,0) V(n,lo)     | max S(n,1)
+    // So tile n reads K(n), VH(n-1) and VL(n), and meanwhile K(n+1), VH(n) and
+    // VL(n+1) land in the other halves of the double buffers.
+    floatx16 s0, s1;  // scores of halves 0 and 1 (s1 carries into the next tile)
+    uint32_t pk[8];
+    auto tile = [&](const bf16_t* Kc, const bf16_t* VLc, const bf16_t* VHp) {
+      zero16(s0);
+      qk_half(s0, Kc, 0);
+      exp_half(s1, sl2, pk);
+      pv_half(pk, VHp);
+      rescale_to(max_half(s0, sl2));
+      zero16(s1);
+      qk_half(s1, Kc, 1);
+      exp_half(s0, sl2, pk);
+      pv_half(pk, VLc);
+      rescale_to(max_half(s1, sl2));
+    };
+    if (R > 0 && rend - pos < KT) {
+      have_tail = true;
+      tail_pos = pos;
+      tail_nv = rend - pos;
+    } else if (R > 0) {
+      int pn = pos;
+      issue_k(K0, pn, KT);
+      issue_v(VL0, pn, 0);
+      bool more = next_full();
+      sync_loads();
+      if (more) {
+        issue_k(K1, pos, KT);
+        issue_v(VL1, pos, 0);
+      }
+      issue_v(VH0, pn, 1);
+      // tile 0: its lower half has no predecessor
+      zero16(s0);
+      qk_half(s0, K0, 0);
+      rescale_to(max_half(s0, sl2));
+      zero16(s1);
+      qk_half(s1, K0, 1);
+      exp_half(s0, sl2, pk);
+      pv_half(pk, VL0);
+      rescale_to(max_half(s1, sl2));
+      bool last_odd = false;  // parity of the last tile
+      while (more) {
+        pn = pos;
+        more = next_full();
+        sync_loads();
+        if (more) {
+          issue_k(K0, pos, KT);
+          issue_v(VL0, pos, 0);
+        }
+        issue_v(VH1, pn, 1);
+        tile(K1, VL1, VH0);
+        if (!more) {
+          last_odd = true;
+          break;
+        }
+        pn = pos;
+        more = next_full();
+        sync_loads();
+        if (more) {
+          issue_k(K1, pos, KT);
+          issue_v(VL1, pos, 0);
+        }
+        issue_v(VH0, pn, 1);
+        tile(K0, VL0, VH1);
+      }
+      // drain: P V of the last tile's upper half
+      sync_loads();
+      exp_half(s1, sl2, pk);
+      pv_half(pk, last_odd ? VH1 : VH0);
+    }
+    if (have_tail) {
+      // the partial last tile, unpipelined (every buffer is free after the
+      // barrier)
+      __syncthreads();
+      issue_k(K0, tail_pos, tail_nv);
+      issue_v(VL0, tail_pos, 0);
+      issue_v(VH0, tail_pos, 1);
+      sync_loads();
+      compute_tile(K0, VL0, VH0, tail_nv);
     }
   } else {
     // ---------------- selected keys, general ranges: row gather --------------
@@ -731,15 +856,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     const int v_dg = tid % DG, v_kg = tid / DG;           // V: KPT keys x 8 columns
     uint4 kreg[KCH / 8];
     uint4 vreg[KPT];
-    auto store_tile = [&](bf16_t* Kd, bf16_t* Vd) {
+    auto store_tile = [&](bf16_t* Kd, bf16_t* VLd, bf16_t* VHd) {
 #pragma unroll
       for (int q = 0; q < KCH / 8; ++q)
         *reinterpret_cast<uint4*>(Kd + toff<DG>(k_slot, k_c0 / 8 + q)) = kreg[q];
       const int kp = mfma_key(v_kg * KPT);  // the KPT keys stay contiguous in MFMA order
+      bf16_t* Vd = kp < HK ? VLd : VHd;
+      const int kl = kp & (HK - 1);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int c = v_dg * 8 + e;
-        bf16_t* dst = Vd + toff<VG>(c, kp >> 3) + (kp & 7);
+        bf16_t* dst = Vd + toff<HG>(c, kl >> 3) + (kl & 7);
         uint32_t wv[KPT];
 #pragma unroll
         for (int kq = 0; kq < KPT; ++kq) {
@@ -796,11 +923,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
       if (ntile > 0) load_tile(0);
       for (int tt = 0; tt < ntile; ++tt) {
         bf16_t* Kb = (tt & 1) ? K1 : K0;
-        bf16_t* Vb = (tt & 1) ? V1 : V0;
-        store_tile(Kb, Vb);
+        bf16_t* VLb = (tt & 1) ? VL1 : VL0;
+        bf16_t* VHb = (tt & 1) ? VH1 : VH0;
+        store_tile(Kb, VLb, VHb);
         __syncthreads();
         if (tt + 1 < ntile) load_tile(tt + 1);
-        compute_tile(Kb, Vb, total - tt * KT);
+        compute_tile(Kb, VLb, VHb, total - tt * KT);
       }
     }
   }
@@ -829,24 +957,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
         const size_t ro = size_t(j0 + row) * D + kc * 8;
         *reinterpret_cast<uint4*>(K0 + toff<DG>(row, kc)) = *reinterpret_cast<const uint4*>(kbh + ro);
         *reinterpret_cast<uint4*>(K1 + toff<DG>(row, kc)) = *reinterpret_cast<const uint4*>(kbl + ro);
-        *reinterpret_cast<uint4*>(V0 + toff<VG>(c / VG, c % VG)) =
+        // chunk c of the [D][64] V^T block: row c / 8, chunk c % 8 (halves of 4)
+        const int vr = c >> 3, vc = c & 7;
+        *reinterpret_cast<uint4*>((vc < 4 ? VL0 : VH0) + toff<HG>(vr, vc & 3)) =
             *reinterpret_cast<const uint4*>(vbt + size_t(j0) * D + size_t(c) * 8);
       }
       __syncthreads();
       floatx16 s[2];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[kt][r] = 0.f;
-      qk(s, K0);
-      qk(s, K1);
-      to_logits(s, KT, S.bias);
-      softmax_pv(s, V0, 1.f);
+      for (int kt = 0; kt < 2; ++kt) {
+        zero16(s[kt]);
+        qk_half(s[kt], K0, kt);
+        qk_half(s[kt], K1, kt);
+      }
+      to_logits(s, S.bias);
+      softmax_pv(s, VL0, VH0, 1.f);
     }
   }
 
   // ---------------- epilogue: normalise, stage, scatter to original rows ----
-  const float ltot = lsum + __shfl_xor(lsum, 32, 64);
+  const float ltot = pair_sum(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
   __syncthreads();
   // stage O in the K tiles (query rows 0..63 in K0, 64..127 in K1), then
