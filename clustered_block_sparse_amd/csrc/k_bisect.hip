@@ -402,6 +402,19 @@ __device__ __forceinline__ uint4 ld16(const T* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// Rows of head h.  Two tensors of the same shape can be bisected together as
+// one problem of H0 + H1 heads: heads below h0 are those of x0, the others
+// those of x1, so every launch covers both.
+template <typename T>
+struct Src2 {
+  const T* x0;
+  const T* x1;
+  int h0;
+  __device__ __forceinline__ const T* head(int h, int N, int D) const {
+    return h < h0 ? x0 + size_t(h) * N * D : x1 + size_t(h - h0) * N * D;
+  }
+};
+
 // ---------------------------------------------------------------------------
 // top phase kernels (grid.y = heads)
 // ---------------------------------------------------------------------------
@@ -427,7 +440,7 @@ struct TopBufs {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ x, TopBufs b, int first) {
+__global__ __launch_bounds__(256) void delta_kernel(Src2<T> x, TopBufs b, int first) {
   using G = RowGeo<T, D>;
   constexpr int U = 8;  // wave steps in flight
   __shared__ float wv[D], mv[D];
@@ -436,7 +449,7 @@ __global__ __launch_bounds__(256) void delta_kernel(const T* __restrict__ x, Top
   const int4 ch = b.chunks[blockIdx.x];
   const int4 sg = b.segs[ch.x];
   const int32_t* ph = b.perm + size_t(h) * b.N;
-  const T* xh = x + size_t(h) * b.N * D;
+  const T* __restrict__ xh = x.head(h, b.N, D);
   for (int i = t; i < ch.z; i += 256) pidx[i] = ph[ch.y + i];
   if (t < D) {
     float c1, c2;
@@ -647,7 +660,7 @@ __global__ __launch_bounds__(1024) void pick_kernel(TopBufs b) {
 // found with vectorised key/side reads and compacted in position order, give
 // the change of the left sum; only their rows are read.  Sides are updated.
 template <typename T, int D, bool FULL>
-__global__ __launch_bounds__(256) void sums_kernel(const T* __restrict__ x, TopBufs b) {
+__global__ __launch_bounds__(256) void sums_kernel(Src2<T> x, TopBufs b) {
   using G = RowGeo<T, D>;
   constexpr int U = FULL ? 8 : 4;
   constexpr int STEP = 4 * G::RPW;
@@ -660,7 +673,7 @@ __global__ __launch_bounds__(256) void sums_kernel(const T* __restrict__ x, TopB
   const int32_t* ph = b.perm + size_t(h) * b.N;
   const uint32_t* kh = b.keys + size_t(h) * b.N;
   uint8_t* sd = b.side + size_t(h) * b.N;
-  const T* xh = x + size_t(h) * b.N * D;
+  const T* __restrict__ xh = x.head(h, b.N, D);
   const int lane = t & 63, w = t >> 6;
   const int sub = lane % G::LPR, rsub = lane / G::LPR;
   int cnt = ch.z;
@@ -944,7 +957,8 @@ __device__ void subtree_select(SubShared<D>& S, int A, int n0) {
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void subtree_kernel(const T* __restrict__ x, int32_t* perm,
+__global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void subtree_kernel(Src2<T> x, const int32_t* __restrict__ perm,
+                                                              int32_t* out0, int32_t* out1,
                                                               const int4* __restrict__ roots, int N,
                                                               int L, int iters) {
   using G = RowGeo<T, D>;
@@ -954,10 +968,14 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
   SubShared<D>& S = *reinterpret_cast<SubShared<D>*>(smem);
   const int h = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int4 root = roots[blockIdx.x];
-  if (ceil_div(root.y, L) < 2) return;  // a leaf already
   const int start = root.x, n0 = root.y;
-  int32_t* ph = perm + size_t(h) * N + start;
-  const T* xh = x + size_t(h) * N * D;
+  const int32_t* ph = perm + size_t(h) * N + start;
+  int32_t* po = (h < x.h0 ? out0 + size_t(h) * N : out1 + size_t(h - x.h0) * N) + start;
+  if (ceil_div(n0, L) < 2) {  // a leaf already: its order is final
+    for (int i = t; i < n0; i += SUB_THREADS) po[i] = ph[i];
+    return;
+  }
+  const T* __restrict__ xh = x.head(h, N, D);
   for (int i = t; i < n0; i += SUB_THREADS) S.pt[i] = ph[i];
   if (t == 0) {
     S.list[0][0] = make_int2(0, n0);
@@ -1213,19 +1231,21 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
     __syncthreads();
   }
   __syncthreads();
-  for (int i = t; i < n0; i += SUB_THREADS) ph[i] = S.pt[i];
+  for (int i = t; i < n0; i += SUB_THREADS) po[i] = S.pt[i];
 }
 
-__global__ void leaf_offsets_kernel(int32_t* off, int H, int C, int N, int L) {
+__global__ void leaf_offsets_kernel(int32_t* off0, int32_t* off1, int h0, int C, int N, int L) {
   const int h = blockIdx.y;
   const int c = blockIdx.x * 256 + threadIdx.x;
-  if (c <= C) off[size_t(h) * (C + 1) + c] = min(c * L, N);
+  int32_t* off = h < h0 ? off0 + size_t(h) * (C + 1) : off1 + size_t(h - h0) * (C + 1);
+  if (c <= C) off[c] = min(c * L, N);
 }
 
 template <typename T, int D>
-hipError_t run_bisect(const void* xv, int H, int N, int L, int iters, const TreePlan& P, int4* segs,
-                      int4* chunks, int32_t* pa, int32_t* pb, TopBufs b, hipStream_t st) {
-  const T* x = (const T*)xv;
+hipError_t run_bisect(const void* x0, const void* x1, int h0, int H, int N, int L, int iters,
+                      const TreePlan& P, int4* segs, int4* chunks, int32_t* pa, int32_t* pb,
+                      int32_t* out0, int32_t* out1, TopBufs b, hipStream_t st) {
+  const Src2<T> x{(const T*)x0, (const T*)x1, h0};
   const size_t sub_lds = sizeof(SubShared<D>);
   if (hipFuncSetAttribute((const void*)subtree_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           int(sub_lds)) != hipSuccess)
@@ -1260,8 +1280,8 @@ hipError_t run_bisect(const void* xv, int H, int N, int L, int iters, const Tree
     nxt = tmp;
   }
   const int nroots = P.t.nseg[P.t.nlev];
-  subtree_kernel<T, D><<<dim3(nroots, H), SUB_THREADS, sub_lds, st>>>(x, cur, segs + P.t.sb[P.t.nlev], N, L,
-                                                                     iters);
+  subtree_kernel<T, D><<<dim3(nroots, H), SUB_THREADS, sub_lds, st>>>(x, cur, out0, out1,
+                                                                     segs + P.t.sb[P.t.nlev], N, L, iters);
   return hipGetLastError();
 }
 
@@ -1272,7 +1292,8 @@ size_t bisect_scratch(int H, int N, int d, int leaf) {
   Arena a{nullptr, 0, 0};
   a.get<int4>(size_t(P.total_seg));
   a.get<int4>(size_t(P.total_chunk + 1));
-  a.get<int32_t>(size_t(H) * N);   // ping-pong partner of perm_out
+  a.get<int32_t>(size_t(H) * N);   // perm ping-pong
+  a.get<int32_t>(size_t(H) * N);
   a.get<uint32_t>(size_t(H) * N);  // keys
   a.get<uint8_t>(size_t(H) * N);   // side
   a.get<float>(size_t(H) * P.max_seg * 2 * d);   // cen
@@ -1287,12 +1308,14 @@ size_t bisect_scratch(int H, int N, int d, int leaf) {
   return a.used;
 }
 
-hipError_t bisect_run(const void* x, int dtype, int H, int N, int d, int leaf, int iters,
-                      int32_t* perm_out, int32_t* offsets_out, Arena& s, hipStream_t st) {
+hipError_t bisect_run(const void* x0, const void* x1, int h0, int dtype, int H, int N, int d, int leaf,
+                      int iters, int32_t* perm0, int32_t* perm1, int32_t* off0, int32_t* off1, Arena& s,
+                      hipStream_t st) {
   const TreePlan P = plan_tree(N, leaf, SUB_N);
   int4* segs = s.get<int4>(size_t(P.total_seg));
   int4* chunks = s.get<int4>(size_t(P.total_chunk + 1));
-  int32_t* other = s.get<int32_t>(size_t(H) * N);
+  int32_t* pa = s.get<int32_t>(size_t(H) * N);
+  int32_t* pb = s.get<int32_t>(size_t(H) * N);
   TopBufs b{};
   b.keys = s.get<uint32_t>(size_t(H) * N);
   b.side = s.get<uint8_t>(size_t(H) * N);
@@ -1308,10 +1331,8 @@ hipError_t bisect_run(const void* x, int dtype, int H, int N, int d, int leaf, i
   b.max_seg = P.max_seg;
   b.max_chunk = P.max_chunk;
   b.N = N;
-  // ping-pong so that the last top level writes perm_out (the subtree phase
-  // then works in place)
-  int32_t* pa = (P.t.nlev % 2 == 0) ? perm_out : other;
-  int32_t* pb = (P.t.nlev % 2 == 0) ? other : perm_out;
+  // the top levels ping-pong between two scratch orders; the subtree phase
+  // writes each head's final order to its tensor's output
   iota_kernel<<<dim3(ceil_div(N, 256), H), 256, 0, st>>>(pa, N);
   const size_t ncnt = size_t(H) * P.max_seg;
   zero_i32<<<unsigned((ncnt + 255) / 256), 256, 0, st>>>(b.ccount, ncnt);
@@ -1320,16 +1341,16 @@ hipError_t bisect_run(const void* x, int dtype, int H, int N, int d, int leaf, i
   build_tree_kernel<<<1, 1024, 0, st>>>(P.t, N, segs, chunks);
   hipError_t e;
   if (dtype == SA_F32 && d == 64)
-    e = run_bisect<float, 64>(x, H, N, leaf, iters, P, segs, chunks, pa, pb, b, st);
+    e = run_bisect<float, 64>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, pa, pb, perm0, perm1, b, st);
   else if (dtype == SA_F32 && d == 128)
-    e = run_bisect<float, 128>(x, H, N, leaf, iters, P, segs, chunks, pa, pb, b, st);
+    e = run_bisect<float, 128>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, pa, pb, perm0, perm1, b, st);
   else if (dtype == SA_BF16 && d == 64)
-    e = run_bisect<bf16_t, 64>(x, H, N, leaf, iters, P, segs, chunks, pa, pb, b, st);
+    e = run_bisect<bf16_t, 64>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, pa, pb, perm0, perm1, b, st);
   else
-    e = run_bisect<bf16_t, 128>(x, H, N, leaf, iters, P, segs, chunks, pa, pb, b, st);
+    e = run_bisect<bf16_t, 128>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, pa, pb, perm0, perm1, b, st);
   if (e != hipSuccess) return e;
   const int C = ceil_div(N, leaf);
-  leaf_offsets_kernel<<<dim3(ceil_div(C + 1, 256), H), 256, 0, st>>>(offsets_out, H, C, N, leaf);
+  leaf_offsets_kernel<<<dim3(ceil_div(C + 1, 256), H), 256, 0, st>>>(off0, off1, h0, C, N, leaf);
   return hipGetLastError();
 }
 

@@ -119,6 +119,13 @@ struct Plan {
   size_t total;
 };
 
+// Q and K bisected with the same leaf size and round count form one problem
+// of 2H heads: every launch of the bisection covers both tensors.
+bool paired_bisect(const sa_cluster_cfg* qc, const sa_cluster_cfg* kc) {
+  return qc->method == SA_BISECT && kc->method == SA_BISECT && qc->leaf == kc->leaf &&
+         qc->iters == kc->iters;
+}
+
 // carve the persistent buffers of sa_forward; null base = size only
 struct FwdBufs {
   sa_clusters q, k;
@@ -150,7 +157,8 @@ FwdBufs carve_forward(const sa_problem* p, const sa_cluster_cfg* qc, const sa_cl
   b.counts = a.get<int32_t>(size_t(H) * Cq);
   b.head_topk = a.get<int32_t>(size_t(H));
   const size_t fixed = a.used;
-  size_t scr = std::max(cluster_scratch(p, qc), cluster_scratch(p, kc));
+  size_t scr = paired_bisect(qc, kc) ? bisect_scratch(2 * H, N, d, qc->leaf) + 256
+                                     : std::max(cluster_scratch(p, qc), cluster_scratch(p, kc));
   scr = std::max(scr, select_scratch(H, Cq, Ck, kc->method == SA_SUBSPACE) + 256);
   scr = std::max(scr, attn_scratch(H, N, d, Cq, Ck, tile_rows(qc), ac ? ac->compensate : 0,
                                    p->dtype, max_tiles(p, qc)) + 256);
@@ -165,6 +173,36 @@ sa_status hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP
 // ---------------------------------------------------------------------------
 // component implementations (arguments already validated)
 // ---------------------------------------------------------------------------
+// after the bisection proper: labels, member means and the rows in cluster
+// order (shared by the one- and two-tensor paths)
+sa_status bisect_tail(const sa_problem* p, const sa_cluster_cfg* c, const void* x, sa_clusters* out,
+                      hipStream_t st) {
+  const int H = p->heads, N = p->n, d = p->d, dt = p->dtype;
+  const int C = clusters_of(p, c);
+  out->num_clusters = C;
+  out->method = c->method;
+  out->sub_clusters = 0;
+  for (int k = 0; k < 3; ++k) out->sub_dims[k] = 0;
+  hipError_t e = labels_from_offsets(out->perm, out->offsets, out->labels, H, N, C, st);
+  if (e == hipSuccess)
+    e = cluster_means(x, dt, d, 0, d, out->perm, out->offsets, H, N, C, out->centroids, d, false, st);
+  if (e == hipSuccess) e = gather_rows(x, out->x_perm, out->perm, H, N, d, dt, st);
+  return hip_status(e);
+}
+
+sa_status do_cluster_pair(const sa_problem* p, const sa_cluster_cfg* qc, const sa_cluster_cfg* kc,
+                          const void* q, const void* k, sa_clusters* qo, sa_clusters* ko, Arena& s,
+                          hipStream_t st) {
+  const int H = p->heads;
+  Arena tmp = s;
+  const hipError_t e = bisect_run(q, k, H, p->dtype, 2 * H, p->n, p->d, qc->leaf, qc->iters, qo->perm,
+                                  ko->perm, qo->offsets, ko->offsets, tmp, st);
+  if (e != hipSuccess) return SA_ERR_HIP;
+  sa_status r = bisect_tail(p, qc, q, qo, st);
+  if (r == SA_OK) r = bisect_tail(p, kc, k, ko, st);
+  return r;
+}
+
 sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x, sa_clusters* out,
                      Arena& s, hipStream_t st) {
   const int H = p->heads, N = p->n, d = p->d, dt = p->dtype;
@@ -185,10 +223,9 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
     }
   } else if (c->method == SA_BISECT) {
     Arena tmp = s;
-    e = bisect_run(x, dt, H, N, d, c->leaf, c->iters, out->perm, out->offsets, tmp, st);
-    if (e == hipSuccess) e = labels_from_offsets(out->perm, out->offsets, out->labels, H, N, C, st);
-    if (e == hipSuccess)
-      e = cluster_means(x, dt, d, 0, d, out->perm, out->offsets, H, N, C, out->centroids, d, false, st);
+    e = bisect_run(x, x, H, dt, H, N, d, c->leaf, c->iters, out->perm, out->perm, out->offsets,
+                   out->offsets, tmp, st);
+    if (e == hipSuccess) return bisect_tail(p, c, x, out, st);
   } else {
     const int Cs = c->clusters;
     Arena tmp = s;
@@ -409,8 +446,12 @@ SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
   FwdBufs b = carve_forward(p, qcfg, kcfg, acfg, (char*)ws, &used);
   hipStream_t s = (hipStream_t)stream;
   Arena scr{b.scratch, b.scratch_bytes, 0};
-  if ((st = do_cluster(p, qcfg, q, &b.q, scr, s)) != SA_OK) return st;
-  if ((st = do_cluster(p, kcfg, k, &b.k, scr, s)) != SA_OK) return st;
+  if (paired_bisect(qcfg, kcfg)) {
+    if ((st = do_cluster_pair(p, qcfg, kcfg, q, k, &b.q, &b.k, scr, s)) != SA_OK) return st;
+  } else {
+    if ((st = do_cluster(p, qcfg, q, &b.q, scr, s)) != SA_OK) return st;
+    if ((st = do_cluster(p, kcfg, k, &b.k, scr, s)) != SA_OK) return st;
+  }
   hipError_t e = gather_rows(v, b.v_perm, b.k.perm, p->heads, p->n, p->d, p->dtype, s);
   if (e == hipSuccess && b.v_means)
     e = cluster_means(v, p->dtype, p->d, 0, p->d, b.k.perm, b.k.offsets, p->heads, p->n,

@@ -106,8 +106,11 @@ hipError_t expand_sub_centroids(const float* sub, int H, int Cs, int d, const in
 
 // k_bisect.hip ---------------------------------------------------------------
 size_t bisect_scratch(int H, int N, int d, int leaf);
-hipError_t bisect_run(const void* x, int dtype, int H, int N, int d, int leaf, int iters,
-                      int32_t* perm_out, int32_t* offsets_out, Arena& scratch, hipStream_t st);
+// Heads below h0 are rows of x0 (order and leaf offsets to perm0 / off0), the
+// others of x1 (perm1 / off1); H counts both.  One tensor: x1 = x0, h0 = H.
+hipError_t bisect_run(const void* x0, const void* x1, int h0, int dtype, int H, int N, int d, int leaf,
+                      int iters, int32_t* perm0, int32_t* perm1, int32_t* off0, int32_t* off1, Arena& s,
+                      hipStream_t st);
 
 // k_select.hip ---------------------------------------------------------------
 struct SelectArgs {
