@@ -14,7 +14,8 @@ tabular-shaped tokens (6 x 131072 x 64), `mid` the 8 x 10800 x 128 k-means
 layer; `--natural` uses the workload's own Top-p (and online Top-k) instead of
 the fixed density.
 
-A step is one sa_forward call: cluster Q and K, permute V, score + select,
+A step is one sa_forward call: cluster Q and K (one bisection problem of 2H
+heads when both bisect), permute V, score + select,
 block-sparse attention (+ compensation, + unpermute).  Inputs are resident in
 HBM before timing starts.  Prints one JSON line: the headline metric
 (effective sparse-attention TFLOP/s over the whole step), ms per layer, a
@@ -198,8 +199,7 @@ def main():
     ktop = torch.empty(w.heads, dtype=torch.int32, device=dev)
     mask2 = torch.empty_like(mask)
     o2 = torch.empty_like(o)
-    stages = {"cluster_q": lambda: L.sa_cluster(p, qc, q, qt, ws),
-              "cluster_k": lambda: L.sa_cluster(p, kc, k, kt, ws),
+    stages = {"cluster_qk": lambda: L.sa_cluster_qk(p, qc, kc, q, k, qt, kt, ws),
               "permute_v": lambda: L.sa_permute(p, kt, v, v_perm, vbar),
               "select": lambda: L.sa_select(p, sc, qt, kt, mask2, counts, None, ktop, ws),
               "attention": lambda: L.sa_block_sparse_attn(p, ac, qt, kt, v_perm, vbar, mask2, o2, ws)}

@@ -78,6 +78,8 @@ def load():
     lib.sa_workspace_size.argtypes = [P(Problem), P(ClusterCfg), P(ClusterCfg), P(SelectCfg), P(AttnCfg),
                                       P(ctypes.c_size_t)]
     lib.sa_cluster.argtypes = [P(Problem), P(ClusterCfg), vp, P(Clusters), vp, ctypes.c_size_t, vp]
+    lib.sa_cluster_qk.argtypes = [P(Problem), P(ClusterCfg), P(ClusterCfg), vp, vp, P(Clusters), P(Clusters),
+                                  vp, ctypes.c_size_t, vp]
     lib.sa_permute.argtypes = [P(Problem), P(Clusters), vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sa_select.argtypes = [P(Problem), P(SelectCfg), P(Clusters), P(Clusters), vp, vp, vp, vp, vp,
                               ctypes.c_size_t, vp]
@@ -88,8 +90,8 @@ def load():
     lib.sa_set_attn_events.argtypes = [vp, vp]
     lib.sa_status_string.argtypes = [I32]
     lib.sa_status_string.restype = ctypes.c_char_p
-    for fn in ("sa_workspace_size", "sa_cluster", "sa_permute", "sa_select", "sa_block_sparse_attn",
-               "sa_forward", "sa_set_attn_events"):
+    for fn in ("sa_workspace_size", "sa_cluster", "sa_cluster_qk", "sa_permute", "sa_select",
+               "sa_block_sparse_attn", "sa_forward", "sa_set_attn_events"):
         getattr(lib, fn).restype = I32
     _lib = lib
     return lib
@@ -195,6 +197,18 @@ def sa_cluster(p: Problem, cfg: ClusterCfg, x: torch.Tensor, out: ClusterTensors
     out.num_clusters, out.method, out.sub_clusters = s.num_clusters, s.method, s.sub_clusters
     out.sub_dims = tuple(s.sub_dims)
     return out
+
+
+def sa_cluster_qk(p: Problem, qcfg: ClusterCfg, kcfg: ClusterCfg, q: torch.Tensor, k: torch.Tensor,
+                  qout: ClusterTensors, kout: ClusterTensors, ws: torch.Tensor):
+    sq, sk = qout.struct(), kout.struct()
+    _check("sa_cluster_qk", load().sa_cluster_qk(ctypes.byref(p), ctypes.byref(qcfg), ctypes.byref(kcfg), _ptr(q),
+                                                 _ptr(k), ctypes.byref(sq), ctypes.byref(sk), _ptr(ws), ws.numel(),
+                                                 _stream()))
+    for out, s in ((qout, sq), (kout, sk)):
+        out.num_clusters, out.method, out.sub_clusters = s.num_clusters, s.method, s.sub_clusters
+        out.sub_dims = tuple(s.sub_dims)
+    return qout, kout
 
 
 def sa_permute(p: Problem, c: ClusterTensors, x: torch.Tensor, x_perm: torch.Tensor, means=None,

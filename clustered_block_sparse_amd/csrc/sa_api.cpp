@@ -126,6 +126,13 @@ bool paired_bisect(const sa_cluster_cfg* qc, const sa_cluster_cfg* kc) {
          qc->iters == kc->iters;
 }
 
+// scratch the two-tensor clustering needs (the paired bisection's, or the
+// larger of the two separate ones)
+size_t cluster_qk_scratch(const sa_problem* p, const sa_cluster_cfg* qc, const sa_cluster_cfg* kc) {
+  return paired_bisect(qc, kc) ? bisect_scratch(2 * p->heads, p->n, p->d, qc->leaf) + 256
+                               : std::max(cluster_scratch(p, qc), cluster_scratch(p, kc));
+}
+
 // carve the persistent buffers of sa_forward; null base = size only
 struct FwdBufs {
   sa_clusters q, k;
@@ -157,8 +164,7 @@ FwdBufs carve_forward(const sa_problem* p, const sa_cluster_cfg* qc, const sa_cl
   b.counts = a.get<int32_t>(size_t(H) * Cq);
   b.head_topk = a.get<int32_t>(size_t(H));
   const size_t fixed = a.used;
-  size_t scr = paired_bisect(qc, kc) ? bisect_scratch(2 * H, N, d, qc->leaf) + 256
-                                     : std::max(cluster_scratch(p, qc), cluster_scratch(p, kc));
+  size_t scr = cluster_qk_scratch(p, qc, kc);
   scr = std::max(scr, select_scratch(H, Cq, Ck, kc->method == SA_SUBSPACE) + 256);
   scr = std::max(scr, attn_scratch(H, N, d, Cq, Ck, tile_rows(qc), ac ? ac->compensate : 0,
                                    p->dtype, max_tiles(p, qc)) + 256);
@@ -261,6 +267,15 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
   }
   if (e == hipSuccess) e = gather_rows(x, out->x_perm, out->perm, H, N, d, dt, st);
   return hip_status(e);
+}
+
+sa_status do_cluster_qk(const sa_problem* p, const sa_cluster_cfg* qc, const sa_cluster_cfg* kc,
+                        const void* q, const void* k, sa_clusters* qo, sa_clusters* ko, Arena& s,
+                        hipStream_t st) {
+  if (paired_bisect(qc, kc)) return do_cluster_pair(p, qc, kc, q, k, qo, ko, s, st);
+  sa_status r = do_cluster(p, qc, q, qo, s, st);
+  if (r == SA_OK) r = do_cluster(p, kc, k, ko, s, st);
+  return r;
 }
 
 sa_status do_select(const sa_problem* p, const sa_select_cfg* c, const sa_clusters* q,
@@ -369,6 +384,22 @@ SA_API sa_status sa_cluster(const sa_problem* p, const sa_cluster_cfg* cfg, cons
   return do_cluster(p, cfg, x, out, s, (hipStream_t)stream);
 }
 
+SA_API sa_status sa_cluster_qk(const sa_problem* p, const sa_cluster_cfg* qcfg,
+                               const sa_cluster_cfg* kcfg, const void* q, const void* k,
+                               sa_clusters* qout, sa_clusters* kout, void* ws, size_t ws_bytes,
+                               void* stream) {
+  sa_status st = check_problem(p);
+  if (st != SA_OK) return st;
+  if ((st = check_cluster_cfg(p, qcfg)) != SA_OK) return st;
+  if ((st = check_cluster_cfg(p, kcfg)) != SA_OK) return st;
+  for (const sa_clusters* c : {qout, kout})
+    if (!c || !c->labels || !c->perm || !c->offsets || !c->centroids || !c->x_perm) return SA_ERR_INVALID_ARG;
+  if (!q || !k || !ws) return SA_ERR_INVALID_ARG;
+  if (ws_bytes < cluster_qk_scratch(p, qcfg, kcfg)) return SA_ERR_WORKSPACE;
+  Arena s{(char*)ws, ws_bytes, 0};
+  return do_cluster_qk(p, qcfg, kcfg, q, k, qout, kout, s, (hipStream_t)stream);
+}
+
 SA_API sa_status sa_permute(const sa_problem* p, const sa_clusters* c, const void* x, void* x_perm,
                             float* means, void* ws, size_t ws_bytes, void* stream) {
   (void)ws;
@@ -446,12 +477,7 @@ SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
   FwdBufs b = carve_forward(p, qcfg, kcfg, acfg, (char*)ws, &used);
   hipStream_t s = (hipStream_t)stream;
   Arena scr{b.scratch, b.scratch_bytes, 0};
-  if (paired_bisect(qcfg, kcfg)) {
-    if ((st = do_cluster_pair(p, qcfg, kcfg, q, k, &b.q, &b.k, scr, s)) != SA_OK) return st;
-  } else {
-    if ((st = do_cluster(p, qcfg, q, &b.q, scr, s)) != SA_OK) return st;
-    if ((st = do_cluster(p, kcfg, k, &b.k, scr, s)) != SA_OK) return st;
-  }
+  if ((st = do_cluster_qk(p, qcfg, kcfg, q, k, &b.q, &b.k, scr, s)) != SA_OK) return st;
   hipError_t e = gather_rows(v, b.v_perm, b.k.perm, p->heads, p->n, p->d, p->dtype, s);
   if (e == hipSuccess && b.v_means)
     e = cluster_means(v, p->dtype, p->d, 0, p->d, b.k.perm, b.k.offsets, p->heads, p->n,

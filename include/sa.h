@@ -147,6 +147,16 @@ SA_API sa_status sa_workspace_size(const sa_problem* p, const sa_cluster_cfg* qc
 SA_API sa_status sa_cluster(const sa_problem* p, const sa_cluster_cfg* cfg, const void* x,
                             sa_clusters* out, void* ws, size_t ws_bytes, void* stream);
 
+/* Cluster Q with qcfg and K with kcfg, exactly as two sa_cluster calls would
+ * (bit-identical results), as sa_forward does.  When both use BISECT with
+ * the same leaf and iters, the two tensors are bisected together as one
+ * problem of 2H heads, so every kernel launch covers both.  Workspace: as
+ * returned by sa_workspace_size with both configurations. */
+SA_API sa_status sa_cluster_qk(const sa_problem* p, const sa_cluster_cfg* qcfg,
+                               const sa_cluster_cfg* kcfg, const void* q, const void* k,
+                               sa_clusters* qout, sa_clusters* kout, void* ws, size_t ws_bytes,
+                               void* stream);
+
 /* Gather rows of x [H, n, d] into the cluster order of `c` (x_perm) and, if
  * `means` is not NULL, write the member mean of every cluster to means
  * f32 [H, C, d] (zeros for an empty cluster).  Used for V. */

@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_symbols()
-    assert set(names) >= {"sa_cluster", "sa_select", "sa_block_sparse_attn", "sa_forward",
+    assert set(names) >= {"sa_cluster", "sa_cluster_qk", "sa_select", "sa_block_sparse_attn", "sa_forward",
                           "sa_workspace_size", "sa_status_string", "sa_permute", "sa_num_clusters"}
     for n in names:
         assert hasattr(lib, n), n

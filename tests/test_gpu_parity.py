@@ -263,6 +263,17 @@ def test_stage_G_forward(w):
     kt = L.alloc_clusters(p, kc, DEV, k.dtype)
     L.sa_cluster(p, qc, q, qt, ws)
     L.sa_cluster(p, kc, k, kt, ws)
+    # both tensors in one call (one problem of 2H heads when both bisect):
+    # identical to the two separate calls
+    qt2 = L.alloc_clusters(p, qc, DEV, q.dtype)
+    kt2 = L.alloc_clusters(p, kc, DEV, k.dtype)
+    L.sa_cluster_qk(p, qc, kc, q, k, qt2, kt2, ws)
+    torch.cuda.synchronize()
+    for a, b in ((qt, qt2), (kt, kt2)):
+        assert a.num_clusters == b.num_clusters
+        for f in ("labels", "perm", "offsets", "centroids", "x_perm"):
+            assert torch.equal(getattr(a, f), getattr(b, f)), f
+    del qt2, kt2
     v_perm = torch.empty_like(v)
     vbar = torch.empty(w.heads, kt.num_clusters, w.d, dtype=torch.float32, device=DEV)
     L.sa_permute(p, kt, v, v_perm, vbar)
