@@ -130,6 +130,25 @@ def cpu_baseline(w, q, k, v, budget_s=10.0):
                       f"selection, attention{' with compensation' if w.compensate else ''}), {dt:.1f} s"}
 
 
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", "attention_traffic_wan720p.json")
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per attention launch from the committed counter measurement
+    (FETCH_SIZE + WRITE_SIZE, calibrated on device copies of known size), or
+    None when it was taken on another workload or another version of the
+    attention kernel source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    from clustered_block_sparse_amd.profiling import source_hash
+    if rec.get("source_sha256") != source_hash() or rec.get("workload") != workload:
+        return None
+    return rec.get("bytes_per_launch")
+
+
 def describe(name, w, natural, density):
     base = WORKLOADS[name][1]
     if natural:
@@ -301,9 +320,11 @@ def main():
         "forward_matches_components": same,
         "roofline": {"bound": "mfma", "achieved": attn_tf,
                      "peak": FP32_PEAK_TFLOPS if fp32 else BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": attn_tf / (FP32_PEAK_TFLOPS if fp32 else BF16_PEAK_TFLOPS), "traffic": None,
+                     "frac": attn_tf / (FP32_PEAK_TFLOPS if fp32 else BF16_PEAK_TFLOPS),
+                     "traffic": stored_traffic(cfg["workload"]),
                      "kernel": "attention kernels (attn_mfma aligned + general instantiations), selected-block "
-                               "flops over their event-timed duration per launch"},
+                               "flops over their event-timed duration per launch; traffic: HBM bytes per launch "
+                               "of the aligned instantiation (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -1,0 +1,133 @@
+"""Summaries of rocprofv3 output for the profiles/ folder.
+
+    python -m clustered_block_sparse_amd.profiling trace STATS_CSV --title T --cmd C
+        Markdown table (kernel, calls, total ms, average us, %) from the
+        kernel_stats.csv of `rocprofv3 --kernel-trace --stats --output-format csv`.
+
+    python -m clustered_block_sparse_amd.profiling traffic --fetch CSV --write CSV \
+            --kernel NAME --copy-bytes B --workload W --out JSON [--cmd C]
+        HBM bytes per launch of kernel NAME from two counter passes
+        (`rocprofv3 --pmc FETCH_SIZE`, then `--pmc WRITE_SIZE`, of a bench run
+        with --copy-probe).  Each counter reads in KiB per dispatch; it is
+        scaled by what it reads for the probe's device copies of B bytes each
+        (B read and B written), which calibrates the counter against a transfer
+        of known size.  The JSON keeps the sha256 of the attention kernel
+        source it was measured on; bench.py reports the figure only while the
+        source is unchanged.
+
+Only summarises files; nothing here touches the GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+import sys
+from collections import defaultdict
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ATTN_SOURCE = os.path.join(HERE, "csrc", "k_attn.hip")
+
+
+def source_hash(path: str = ATTN_SOURCE) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def short_name(n: str) -> str:
+    if n.startswith("void at::") or n.startswith("at::") or n.startswith("Cijk_"):
+        return "torch (input generation, bench bookkeeping, dense SDPA)"
+    n = n.replace("(anonymous namespace)::", "").replace("sa::", "").replace("void ", "")
+    n = re.sub(r"\(.*", "", n)
+    n = n.replace("HIP_vector_type<unsigned int, 4u>", "uint4").replace("unsigned short", "bf16")
+    return n.strip() or "(unnamed)"
+
+
+def trace_table(stats_csv: str, title: str, cmd: str) -> str:
+    rows = list(csv.DictReader(open(stats_csv)))
+    agg: dict[str, list[float]] = {}
+    for r in rows:
+        s = short_name(r["Name"])
+        c, t = int(r["Calls"]), float(r["TotalDurationNs"])
+        a = agg.setdefault(s, [0, 0.0])
+        a[0] += c
+        a[1] += t
+    total = sum(t for _, t in agg.values()) or 1.0
+    out = [f"# {title}", "", "Command (from the repo root on the GPU box):", "", "```", cmd, "```", "",
+           "| kernel | calls | total ms | avg us | % |", "|---|---|---|---|---|"]
+    for s, (c, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        out.append(f"| {s} | {c} | {t / 1e6:.2f} | {t / c / 1e3:.1f} | {100 * t / total:.1f} |")
+    return "\n".join(out) + "\n"
+
+
+def per_dispatch(counter_csv: str, counter: str) -> dict[str, list[float]]:
+    """kernel short name -> per-dispatch totals of `counter` (rows of one
+    dispatch, e.g. per hardware block, are summed)."""
+    acc: dict[tuple[str, str], float] = defaultdict(float)
+    for r in csv.DictReader(open(counter_csv)):
+        if r.get("Counter_Name") != counter:
+            continue
+        acc[(short_name(r["Kernel_Name"]), r["Dispatch_Id"])] += float(r["Counter_Value"])
+    out: dict[str, list[float]] = defaultdict(list)
+    for (k, _), v in acc.items():
+        out[k].append(v)
+    return out
+
+
+def copy_reading(d: dict[str, list[float]]) -> float:
+    """Mean counter value of the probe's large copies: the copy-kernel
+    dispatches within 10% of the largest one."""
+    vals = [v for k, vs in d.items() if "copyBuffer" in k or "copy_kernel" in k for v in vs]
+    if not vals:
+        raise SystemExit("no copy kernel dispatches in the counter file (run the bench with --copy-probe)")
+    top = max(vals)
+    big = [v for v in vals if v >= 0.9 * top]
+    return sum(big) / len(big)
+
+
+def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int) -> dict:
+    f, w = per_dispatch(fetch_csv, "FETCH_SIZE"), per_dispatch(write_csv, "WRITE_SIZE")
+    if kernel not in f or kernel not in w:
+        raise SystemExit(f"kernel {kernel!r} not found; kernels: {sorted(f)}")
+    fk, wk = sum(f[kernel]) / len(f[kernel]), sum(w[kernel]) / len(w[kernel])
+    f_scale = copy_bytes / (copy_reading(f) * 1024.0)
+    w_scale = copy_bytes / (copy_reading(w) * 1024.0)
+    return {"kernel": kernel, "dispatches": len(f[kernel]),
+            "fetch_kib": fk, "write_kib": wk, "fetch_scale": f_scale, "write_scale": w_scale,
+            "read_bytes": fk * 1024.0 * f_scale, "write_bytes": wk * 1024.0 * w_scale,
+            "bytes_per_launch": fk * 1024.0 * f_scale + wk * 1024.0 * w_scale}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd_name", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("stats_csv")
+    t.add_argument("--title", required=True)
+    t.add_argument("--cmd", required=True)
+    r = sub.add_parser("traffic")
+    r.add_argument("--fetch", required=True)
+    r.add_argument("--write", required=True)
+    r.add_argument("--kernel", required=True)
+    r.add_argument("--copy-bytes", type=int, required=True)
+    r.add_argument("--workload", required=True)
+    r.add_argument("--out", required=True)
+    r.add_argument("--cmd", default="")
+    a = ap.parse_args(argv)
+    if a.cmd_name == "trace":
+        sys.stdout.write(trace_table(a.stats_csv, a.title, a.cmd))
+    else:
+        res = traffic(a.fetch, a.write, a.kernel, a.copy_bytes)
+        res.update({"workload": a.workload, "source_sha256": source_hash(), "command": a.cmd})
+        with open(a.out, "w") as fh:
+            json.dump(res, fh, indent=1)
+            fh.write("\n")
+        print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()
