@@ -226,6 +226,73 @@ __global__ __launch_bounds__(256) void means_kernel(const T* __restrict__ x, int
   }
 }
 
+// Rows into cluster order and member means in one pass: one workgroup per
+// (cluster, head) copies its rows to their cluster-order positions and sums
+// them in the order of means_kernel (thread (r, j) takes rows r, r + RPI, ...;
+// the RPI partial sums are added in row-group order), so both results equal
+// those of the two separate kernels.  An empty cluster's mean is zero.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_means_kernel(const T* __restrict__ x, T* __restrict__ xp,
+                                                           const int32_t* __restrict__ perm,
+                                                           const int32_t* __restrict__ off, int N, int C,
+                                                           int d, float* __restrict__ out) {
+  constexpr int EPV = 16 / sizeof(T);
+  __shared__ float part[256 * EPV];
+  const int c = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  const int a = off[size_t(h) * (C + 1) + c], b = off[size_t(h) * (C + 1) + c + 1];
+  float* o = out + (size_t(h) * C + c) * d;
+  if (b == a) {
+    for (int j = t; j < d; j += 256) o[j] = 0.f;
+    return;
+  }
+  const int V = d / EPV;   // vectors per row
+  const int RPI = 256 / V; // rows per iteration
+  const int r = t / V, j = t % V;
+  float acc[EPV];
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) acc[e] = 0.f;
+  const int32_t* ph = perm + size_t(h) * N;
+  const uint4* xh = reinterpret_cast<const uint4*>(x + size_t(h) * N * d) + j;
+  uint4* yh = reinterpret_cast<uint4*>(xp + size_t(h) * N * d) + j;
+  constexpr int U = 4;
+  for (int p0 = a + r; p0 < b; p0 += U * RPI) {
+    uint4 raw[U];
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int p = p0 + q * RPI;
+      raw[q] = p < b ? xh[size_t(ph[p]) * V] : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int q = 0; q < U; ++q) {
+      const int p = p0 + q * RPI;
+      if (p >= b) break;
+      yh[size_t(p) * V] = raw[q];
+      if constexpr (sizeof(T) == 4) {
+        acc[0] += __uint_as_float(raw[q].x);
+        acc[1] += __uint_as_float(raw[q].y);
+        acc[2] += __uint_as_float(raw[q].z);
+        acc[3] += __uint_as_float(raw[q].w);
+      } else {
+        const uint32_t w4[4] = {raw[q].x, raw[q].y, raw[q].z, raw[q].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          acc[2 * k] += __uint_as_float(w4[k] << 16);
+          acc[2 * k + 1] += __uint_as_float(w4[k] & 0xFFFF0000u);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPV; ++e) part[r * d + j * EPV + e] = acc[e];
+  __syncthreads();
+  if (t < d) {
+    const int rows = min(RPI, b - a);
+    float sum = 0.f;
+    for (int k = 0; k < rows; ++k) sum += part[k * d + t];
+    o[t] = sum / float(b - a);
+  }
+}
+
 __global__ __launch_bounds__(256) void labels_from_off_kernel(const int32_t* __restrict__ perm,
                                                               const int32_t* __restrict__ off,
                                                               int32_t* __restrict__ labels, int N,
@@ -311,6 +378,20 @@ hipError_t cluster_means(const void* x, int dtype, int d, int col0, int dc, cons
   else
     means_kernel<bf16_t><<<g, 256, 0, st>>>((const bf16_t*)x, d, col0, dc, perm, offsets, N, C, out,
                                             out_stride, keep_empty);
+  return hipGetLastError();
+}
+
+hipError_t gather_means(const void* x, int dtype, int d, const int32_t* perm, const int32_t* offsets,
+                        int H, int N, int C, void* x_perm, float* means, hipStream_t st) {
+  const int esz = dtype == SA_F32 ? 4 : 2;
+  // 16-byte vectors, at most 256 of them per row
+  if ((d * esz) % 16 || d * esz > 256 * 16) return hipErrorInvalidValue;
+  dim3 g(C, H);
+  if (dtype == SA_F32)
+    gather_means_kernel<float><<<g, 256, 0, st>>>((const float*)x, (float*)x_perm, perm, offsets, N, C, d, means);
+  else
+    gather_means_kernel<bf16_t><<<g, 256, 0, st>>>((const bf16_t*)x, (bf16_t*)x_perm, perm, offsets, N, C, d,
+                                                   means);
   return hipGetLastError();
 }
 

@@ -190,9 +190,7 @@ sa_status bisect_tail(const sa_problem* p, const sa_cluster_cfg* c, const void* 
   out->sub_clusters = 0;
   for (int k = 0; k < 3; ++k) out->sub_dims[k] = 0;
   hipError_t e = labels_from_offsets(out->perm, out->offsets, out->labels, H, N, C, st);
-  if (e == hipSuccess)
-    e = cluster_means(x, dt, d, 0, d, out->perm, out->offsets, H, N, C, out->centroids, d, false, st);
-  if (e == hipSuccess) e = gather_rows(x, out->x_perm, out->perm, H, N, d, dt, st);
+  if (e == hipSuccess) e = gather_means(x, dt, d, out->perm, out->offsets, H, N, C, out->x_perm, out->centroids, st);
   return hip_status(e);
 }
 
@@ -408,10 +406,9 @@ SA_API sa_status sa_permute(const sa_problem* p, const sa_clusters* c, const voi
   if (st != SA_OK) return st;
   if (!clusters_ok(c, false) || !x || !x_perm) return SA_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = gather_rows(x, x_perm, c->perm, p->heads, p->n, p->d, p->dtype, s);
-  if (e == hipSuccess && means)
-    e = cluster_means(x, p->dtype, p->d, 0, p->d, c->perm, c->offsets, p->heads, p->n,
-                      c->num_clusters, means, p->d, false, s);
+  const hipError_t e = means ? gather_means(x, p->dtype, p->d, c->perm, c->offsets, p->heads, p->n,
+                                             c->num_clusters, x_perm, means, s)
+                             : gather_rows(x, x_perm, c->perm, p->heads, p->n, p->d, p->dtype, s);
   return hip_status(e);
 }
 
@@ -478,10 +475,9 @@ SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
   hipStream_t s = (hipStream_t)stream;
   Arena scr{b.scratch, b.scratch_bytes, 0};
   if ((st = do_cluster_qk(p, qcfg, kcfg, q, k, &b.q, &b.k, scr, s)) != SA_OK) return st;
-  hipError_t e = gather_rows(v, b.v_perm, b.k.perm, p->heads, p->n, p->d, p->dtype, s);
-  if (e == hipSuccess && b.v_means)
-    e = cluster_means(v, p->dtype, p->d, 0, p->d, b.k.perm, b.k.offsets, p->heads, p->n,
-                      b.k.num_clusters, b.v_means, p->d, false, s);
+  const hipError_t e = b.v_means ? gather_means(v, p->dtype, p->d, b.k.perm, b.k.offsets, p->heads, p->n,
+                                                b.k.num_clusters, b.v_perm, b.v_means, s)
+                                 : gather_rows(v, b.v_perm, b.k.perm, p->heads, p->n, p->d, p->dtype, s);
   if (e != hipSuccess) return SA_ERR_HIP;
   if ((st = do_select(p, scfg, &b.q, &b.k, mask, b.counts, nullptr, b.head_topk, scr, s)) != SA_OK)
     return st;

@@ -81,6 +81,10 @@ hipError_t gather_rows(const void* x, void* x_perm, const int32_t* perm, int H, 
 // Member means of columns [col0, col0+dc) of x rows per cluster, fp32, written
 // to out[h][c][0..dc) with row stride out_stride.  Empty clusters: keep the
 // existing value if keep_empty, else zeros.
+// gather_rows and cluster_means (whole rows, empty clusters -> zero) in one
+// pass over the rows; results identical to the two calls
+hipError_t gather_means(const void* x, int dtype, int d, const int32_t* perm, const int32_t* offsets,
+                        int H, int N, int C, void* x_perm, float* means, hipStream_t st);
 hipError_t cluster_means(const void* x, int dtype, int d, int col0, int dc, const int32_t* perm,
                          const int32_t* offsets, int H, int N, int C, float* out, int out_stride,
                          bool keep_empty, hipStream_t st);
