@@ -482,6 +482,15 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __builtin_bit_cast(float, uint32_t(r[0])) + __builtin_bit_cast(float, uint32_t(r[1]));
 }
 
+// p[i] of memory that no thread writes during the kernel, read through the
+// constant address space (a scalar load when the index is uniform, so the
+// vector-memory counter is left to the tile loads)
+__device__ __forceinline__ int2 const_load_int2(const int2* p, int i) {
+  const __attribute__((address_space(4))) long long* q = (const __attribute__((address_space(4))) long long*)p;
+  const long long v = q[i];
+  return make_int2(int(v), int(v >> 32));
+}
+
 #define BF16_ONES (__builtin_bit_cast(bf16x2_t, 0x3F803F80u))  // (1.0, 1.0)
 
 // two floats -> packed bf16 pair (hardware round-to-nearest-even)
@@ -751,7 +760,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
       pos += KT;
       if (pos >= rend) {
         if (++ri >= R) return false;
-        const int2 r2 = rg[ri];
+        const int2 r2 = const_load_int2(rg, ri);
         pos = r2.x;
         rend = r2.y;
       }
