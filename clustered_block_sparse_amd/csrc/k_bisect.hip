@@ -39,6 +39,7 @@ namespace sa {
 namespace {
 
 constexpr int BCH = 1024;    // positions per chunk (top phase)
+constexpr int DELTA_SPLIT = 4;  // delta pass: workgroups per chunk
 constexpr int SUB_N = 2560;  // segments up to this many tokens finish in one workgroup
 constexpr int MAXLEV = 32;
 constexpr int SUB_THREADS = 512;
@@ -444,9 +445,14 @@ __global__ __launch_bounds__(256) void delta_kernel(Src2<T> x, TopBufs b, int fi
   using G = RowGeo<T, D>;
   constexpr int U = 8;  // wave steps in flight
   __shared__ float wv[D], mv[D];
-  __shared__ int pidx[BCH];  // the chunk's rows (original tokens)
+  __shared__ int pidx[BCH / DELTA_SPLIT];  // the part's rows (original tokens)
   const int h = blockIdx.y, t = threadIdx.x;
-  const int4 ch = b.chunks[blockIdx.x];
+  // a workgroup takes one of the DELTA_SPLIT equal parts of a chunk: more,
+  // shorter workgroups keep the last wave of the launch from idling the chip
+  const int4 chunk = b.chunks[blockIdx.x / DELTA_SPLIT];
+  const int r0 = (blockIdx.x % DELTA_SPLIT) * (BCH / DELTA_SPLIT);
+  if (r0 >= chunk.z) return;
+  const int4 ch = make_int4(chunk.x, chunk.y + r0, min(BCH / DELTA_SPLIT, chunk.z - r0), chunk.w);
   const int4 sg = b.segs[ch.x];
   const int32_t* ph = b.perm + size_t(h) * b.N;
   const T* __restrict__ xh = x.head(h, b.N, D);
@@ -1258,7 +1264,7 @@ hipError_t run_bisect(const void* x0, const void* x1, int h0, int H, int N, int 
     b.perm = cur;
     const dim3 gs(P.t.nseg[lv], H), gc(P.t.nchunk[lv], H);
     for (int it = 0; it < iters; ++it) {
-      delta_kernel<T, D><<<gc, 256, 0, st>>>(x, b, it == 0);
+      delta_kernel<T, D><<<dim3(gc.x * DELTA_SPLIT, gc.y), 256, 0, st>>>(x, b, it == 0);
       b.round = it;
       hist_kernel<<<gc, 256, 0, st>>>(b);
       find_kernel<<<gs, 256, 0, st>>>(b);
