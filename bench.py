@@ -1,7 +1,8 @@
 """Benchmark: one clustered block-sparse attention layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan|hy|tab|mid]
-                    [--natural] [--no-cpu-baseline] [--no-dense] [--copy-probe]
+                    [--natural] [--cold] [--no-cpu-baseline] [--no-dense] [--copy-probe]
+                    [--gemm-probe]
 
 Default workload: a Wan-2.1-14B-720p-shaped attention layer (40 heads,
 21x45x80 = 75600 tokens, d = 128, bf16; smooth-field + 3D-RoPE queries/keys,
@@ -24,6 +25,14 @@ figure (their own duration, from HIP events the library records around them
 on the launch stream) and the oracle's CPU timing on a bounded sample.
 `--copy-probe` finishes with three 1 GiB device copies of known size, the
 calibration for hardware byte counters.
+
+Every timed step is also bracketed by stream events: the line carries their
+median, minimum and mean.  `--cold` writes a 512 MB scratch buffer before every
+step (warm-up and timed), which evicts the 256 MB memory-side cache, so each
+step starts from HBM; the fills sit between the events, and in that mode
+`ms_per_step` and `value` come from the events' mean.  `--gemm-probe` adds the
+rate of torch's bf16 GEMM (hipBLASLt) on 16384^3, a practical ceiling for MFMA
+work on the same box.
 """
 
 from __future__ import annotations
@@ -163,11 +172,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="wan")
     ap.add_argument("--natural", action="store_true", help="the workload's own top-p instead of fixed density")
+    ap.add_argument("--cold", action="store_true", help="evict the memory-side cache before every step")
     ap.add_argument("--density", type=float, default=0.1)
     ap.add_argument("--heads", type=int, default=0, help="override the head count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--gemm-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported here (every step is per head, so "
@@ -194,18 +205,34 @@ def main():
     def step():
         L.sa_forward(p, qc, kc, sc, ac, q, k, v, o, mask, ws)
 
-    for _ in range(args.warmup):
+    # 512 MB written before each step in --cold mode: twice the memory-side cache
+    scratch = torch.empty(256 << 20, dtype=torch.bfloat16, device=dev) if args.cold else None
+
+    def evict(i):
+        if scratch is not None:
+            scratch.fill_(float(i % 7))
+
+    for i in range(args.warmup):
+        evict(i)
         step()
     probes = [(L.HipEvent(), L.HipEvent()) for _ in range(args.steps)]
+    step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
+        evict(i)
         L.sa_set_attn_events(*probes[i])
+        step_ev[i][0].record()
         step()
+        step_ev[i][1].record()
     torch.cuda.synchronize()
-    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_wall = (time.perf_counter() - t0) * 1e3 / args.steps
     L.sa_set_attn_events(None, None)
     attn_kernel_ms = [a.elapsed_ms(b) for a, b in probes]
+    step_ms = [a.elapsed_time(b) for a, b in step_ev]
+    ms_step = float(np.mean(step_ms)) if args.cold else ms_wall
+    del scratch
     print(f"# sa_forward {ms_step:.3f} ms/layer, attention kernels {np.mean(attn_kernel_ms):.3f} ms",
           file=sys.stderr, flush=True)
 
@@ -287,6 +314,22 @@ def main():
         torch.cuda.synchronize()
         print(f"# copy probe: 3 copies of {src.numel() * 2} bytes", file=sys.stderr, flush=True)
 
+    gemm = None
+    if args.gemm_probe:
+        n = 16384
+        a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+        for _ in range(2):
+            c = a @ b
+        t = Timer()
+        for _ in range(5):
+            t.start()
+            c = a @ b
+            t.stop()
+        gms = float(np.median(t.ms()))
+        gemm = {"shape": [n, n, n], "ms": gms, "tflops": 2.0 * n ** 3 / (gms * 1e-3) / 1e12}
+        del a, b, c
+
     cfg = {"workload": describe(args.workload, w, args.natural, args.density),
            "heads": w.heads, "n": w.n, "d": w.d, "grid": [w.frames, w.height, w.width],
            "clustering": f"q {w.q.method} / k {w.k.method}",
@@ -308,10 +351,14 @@ def main():
         "data": "synthetic",
         "config": cfg,
         "ms_per_layer": ms_step,
+        "cache": "cold: 512 MB written before every step" if args.cold else "warm",
+        "step_ms_events": {"median": float(np.median(step_ms)), "min": float(np.min(step_ms)),
+                           "mean": float(np.mean(step_ms))},
         "effective_flops": eff,
         "compensation_flops": comp,
         "stage_ms": stage_ms,
         "attention_kernel_ms": attn_ms,
+        "attention_kernel_ms_median_min": [float(np.median(attn_kernel_ms)), float(np.min(attn_kernel_ms))],
         "attention_tflops": attn_tf,
         "dense_ms_own_kernel": dense_own,
         "dense_ms_torch_sdpa": dense_sdpa,
@@ -327,6 +374,8 @@ def main():
                                "of the aligned instantiation (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)"},
         "cpu_baseline": cpu,
     }
+    if gemm is not None:
+        line["gemm_probe_bf16"] = gemm
     print(json.dumps(line), flush=True)
 
 

@@ -4,6 +4,16 @@
         Markdown table (kernel, calls, total ms, average us, %) from the
         kernel_stats.csv of `rocprofv3 --kernel-trace --stats --output-format csv`.
 
+    python -m clustered_block_sparse_amd.profiling bench JSONL... --title T --cmd C
+        Markdown table of bench.py result lines (one JSON object per line,
+        other lines ignored): per run the workload, density, ms per layer,
+        the stage breakdown, the attention kernels' rate and the dense
+        comparison.
+
+    python -m clustered_block_sparse_amd.profiling counters CSV --title T --cmd C
+        Markdown table of per-dispatch means of every counter in a
+        counter_collection.csv of `rocprofv3 --pmc`, one row per kernel.
+
     python -m clustered_block_sparse_amd.profiling traffic --fetch CSV --write CSV \
             --kernel NAME --copy-bytes B --workload W --out JSON [--cmd C]
         HBM bytes per launch of kernel NAME from two counter passes
@@ -64,6 +74,57 @@ def trace_table(stats_csv: str, title: str, cmd: str) -> str:
     return "\n".join(out) + "\n"
 
 
+def bench_table(paths: list[str], title: str, cmd: str) -> str:
+    rows = []
+    for path in paths:
+        for line in open(path):
+            line = line.strip()
+            if line.startswith("{"):
+                try:
+                    rows.append(json.loads(line))
+                except ValueError:
+                    pass
+    out = [f"# {title}", "", "Commands (from the repo root on the GPU box):", "", "```", cmd, "```", "",
+           "| workload | H x N x d | density | cache | ms/layer | step median / min (ms) | cluster | permute V | "
+           "select | attention call | attention kernels (ms) | TFLOP/s (frac) | dense own / SDPA (ms) | "
+           "speedup | value TFLOP/s |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        c, st, rf = r["config"], r.get("stage_ms", {}), r["roofline"]
+        ev = r.get("step_ms_events", {})
+        cl = st.get("cluster_qk", st.get("cluster_q", 0.0) + st.get("cluster_k", 0.0))
+        dense = "/".join(f"{x:.1f}" if x else "-" for x in (r.get("dense_ms_own_kernel"), r.get("dense_ms_torch_sdpa")))
+        sp = r.get("speedup_vs_dense")
+        out.append(
+            f"| {c['workload']} | {c['heads']} x {c['n']} x {c['d']} | {100 * c['density']:.2f}% | "
+            f"{r.get('cache', 'warm').split(':')[0]} | {r['ms_per_step']:.2f} | "
+            f"{ev.get('median', float('nan')):.2f} / {ev.get('min', float('nan')):.2f} | {cl:.2f} | "
+            f"{st.get('permute_v', 0.0):.2f} | {st.get('select', 0.0):.2f} | {st.get('attention', 0.0):.2f} | "
+            f"{r['attention_kernel_ms']:.2f} | {rf['achieved']:.0f} ({rf['frac']:.3f}) | {dense} | "
+            f"{'%.2fx' % sp if sp else '-'} | {r['value']:.0f} |")
+    return "\n".join(out) + "\n"
+
+
+def counters_table(counter_csv: str, title: str, cmd: str) -> str:
+    acc: dict[tuple[str, str], dict[str, float]] = defaultdict(lambda: defaultdict(float))
+    names: set[str] = set()
+    for r in csv.DictReader(open(counter_csv)):
+        k = (short_name(r["Kernel_Name"]), r["Dispatch_Id"])
+        acc[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        names.add(r["Counter_Name"])
+    per: dict[str, list[dict[str, float]]] = defaultdict(list)
+    for (kn, _), d in acc.items():
+        per[kn].append(d)
+    cols = sorted(names)
+    out = [f"# {title}", "", "Command (from the repo root on the GPU box):", "", "```", cmd, "```", "",
+           "Per-dispatch means.", "", "| kernel | dispatches | " + " | ".join(cols) + " |",
+           "|---|---|" + "---|" * len(cols)]
+    for kn, ds in sorted(per.items()):
+        vals = [sum(d.get(c, 0.0) for d in ds) / len(ds) for c in cols]
+        out.append(f"| {kn} | {len(ds)} | " + " | ".join(f"{v:.4g}" for v in vals) + " |")
+    return "\n".join(out) + "\n"
+
+
 def per_dispatch(counter_csv: str, counter: str) -> dict[str, list[float]]:
     """kernel short name -> per-dispatch totals of `counter` (rows of one
     dispatch, e.g. per hardware block, are summed)."""
@@ -109,6 +170,14 @@ def main(argv=None):
     t.add_argument("stats_csv")
     t.add_argument("--title", required=True)
     t.add_argument("--cmd", required=True)
+    b = sub.add_parser("bench")
+    b.add_argument("jsonl", nargs="+")
+    b.add_argument("--title", required=True)
+    b.add_argument("--cmd", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("--title", required=True)
+    c.add_argument("--cmd", required=True)
     r = sub.add_parser("traffic")
     r.add_argument("--fetch", required=True)
     r.add_argument("--write", required=True)
@@ -120,6 +189,10 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd_name == "trace":
         sys.stdout.write(trace_table(a.stats_csv, a.title, a.cmd))
+    elif a.cmd_name == "bench":
+        sys.stdout.write(bench_table(a.jsonl, a.title, a.cmd))
+    elif a.cmd_name == "counters":
+        sys.stdout.write(counters_table(a.csv, a.title, a.cmd))
     else:
         res = traffic(a.fetch, a.write, a.kernel, a.copy_bytes)
         res.update({"workload": a.workload, "source_sha256": source_hash(), "command": a.cmd})
