@@ -6,7 +6,8 @@
 // ||c||^2 - 2 x.c expansion, so no cancellation); ties go to the smallest
 // centroid index.  The data here is small next to attention (at most a few
 // GFLOP per layer), so the kernel keeps centroid chunks in LDS and token rows
-// in registers rather than using matrix cores.
+// in registers rather than using matrix cores: the work is two vector ALU
+// operations per (token, centroid, dimension).
 
 #include "sa_internal.h"
 
@@ -14,21 +15,49 @@ namespace sa {
 
 namespace {
 
-constexpr int CCH = 128;  // centroids per LDS chunk
+// One token per lane: the token's slice sits in registers, and every lane of
+// the workgroup walks the same centroids in ascending order, so each centroid
+// element is one LDS read that the whole wave shares (a broadcast).  Four
+// centroids are evaluated at once for instruction-level parallelism; each
+// distance is still sum_t (x_t - c_t)^2 accumulated over t in order, and the
+// four are compared in index order, so the smallest index wins ties.
+template <int DC>
+constexpr int cchunk() {
+  return DC >= 128 ? 64 : 128;  // centroids per LDS chunk (at most 32 KB)
+}
 
-template <typename T, int DC>
+template <typename T, int DC, bool VEC>
 __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ x, int d, int col0, int N,
                                                      int C, const float* __restrict__ cent,
                                                      int32_t* __restrict__ labels) {
-  extern __shared__ float cs[];  // [CCH][DC]
+  constexpr int CCH = cchunk<DC>();
+  __shared__ __attribute__((aligned(16))) float cs[CCH * DC];
   const int h = blockIdx.y;
-  const int tok = blockIdx.x * 64 + (threadIdx.x >> 2);
-  const int sub = threadIdx.x & 3;
-  float xr[DC];
+  const int tok = blockIdx.x * 256 + threadIdx.x;
   const bool valid = tok < N;
   const T* row = x + (size_t(h) * N + (valid ? tok : 0)) * d + col0;
+  float xr[DC];
+  if constexpr (VEC) {
+    constexpr int EPV = 16 / int(sizeof(T));  // elements per 16-byte vector
 #pragma unroll
-  for (int t = 0; t < DC; ++t) xr[t] = to_f(row[t]);
+    for (int q = 0; q < DC / EPV; ++q) {
+      const uint4 u = reinterpret_cast<const uint4*>(row)[q];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+      if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xr[4 * q + e] = __uint_as_float(w[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          xr[8 * q + 2 * e] = __uint_as_float(w[e] << 16);
+          xr[8 * q + 2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
+        }
+      }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < DC; ++t) xr[t] = to_f(row[t]);
+  }
   float best = __builtin_huge_valf();
   int bj = 0x7fffffff;
   const float* ch = cent + size_t(h) * C * DC;
@@ -37,12 +66,36 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ x, in
     __syncthreads();
     for (int i = threadIdx.x; i < nj * DC; i += 256) cs[i] = ch[size_t(j0) * DC + i];
     __syncthreads();
-    for (int jj = sub; jj < nj; jj += 4) {
-      const float* c = cs + jj * DC;
+    int jj = 0;
+    for (; jj + 4 <= nj; jj += 4) {
+      float dist[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < DC; t += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float4 c4 = *reinterpret_cast<const float4*>(cs + (jj + u) * DC + t);
+          float df = xr[t] - c4.x;
+          dist[u] = fmaf(df, df, dist[u]);
+          df = xr[t + 1] - c4.y;
+          dist[u] = fmaf(df, df, dist[u]);
+          df = xr[t + 2] - c4.z;
+          dist[u] = fmaf(df, df, dist[u]);
+          df = xr[t + 3] - c4.w;
+          dist[u] = fmaf(df, df, dist[u]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if (dist[u] < best) {
+          best = dist[u];
+          bj = j0 + jj + u;
+        }
+    }
+    for (; jj < nj; ++jj) {
       float dist = 0.f;
 #pragma unroll
       for (int t = 0; t < DC; ++t) {
-        const float df = xr[t] - c[t];
+        const float df = xr[t] - cs[jj * DC + t];
         dist = fmaf(df, df, dist);
       }
       if (dist < best) {
@@ -51,16 +104,7 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ x, in
       }
     }
   }
-#pragma unroll
-  for (int o = 1; o < 4; o <<= 1) {
-    const float ob = __shfl_xor(best, o, 64);
-    const int oj = __shfl_xor(bj, o, 64);
-    if (ob < best || (ob == best && oj < bj)) {
-      best = ob;
-      bj = oj;
-    }
-  }
-  if (valid && sub == 0) labels[size_t(h) * N + tok] = bj;
+  if (valid) labels[size_t(h) * N + tok] = bj;
 }
 
 template <typename T>
@@ -101,9 +145,14 @@ __global__ void expand_kernel(const float* __restrict__ sub, int H, int Cs, int 
 template <typename T, int DC>
 hipError_t assign_launch(const void* x, int d, int col0, int H, int N, int C, const float* c,
                          int32_t* labels, hipStream_t st) {
-  dim3 g(ceil_div(N, 64), H);
-  const size_t lds = size_t(CCH) * DC * sizeof(float);
-  assign_kernel<T, DC><<<g, 256, lds, st>>>((const T*)x, d, col0, N, C, c, labels);
+  dim3 g(ceil_div(N, 256), H);
+  // 16-byte row loads need the base, the row pitch and the slice start aligned
+  const bool vec = (reinterpret_cast<uintptr_t>(x) % 16 == 0) && (size_t(d) * sizeof(T)) % 16 == 0 &&
+                   (size_t(col0) * sizeof(T)) % 16 == 0 && (DC * sizeof(T)) % 16 == 0;
+  if (vec)
+    assign_kernel<T, DC, true><<<g, 256, 0, st>>>((const T*)x, d, col0, N, C, c, labels);
+  else
+    assign_kernel<T, DC, false><<<g, 256, 0, st>>>((const T*)x, d, col0, N, C, c, labels);
   return hipGetLastError();
 }
 
