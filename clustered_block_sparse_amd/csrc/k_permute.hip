@@ -157,27 +157,25 @@ __global__ __launch_bounds__(256) void gather_kernel(const T* __restrict__ x, T*
   *dst = *s;
 }
 
-// Member means: one workgroup per (cluster, head).  Each thread owns one
-// 16-byte vector (EPV elements) of the row slice [col0, col0 + dc) and sums
-// its rows r, r + RPI, r + 2 RPI, ... in that order (four loads in flight);
-// the RPI partial sums of a column are then added in row-group order.  The
-// result is independent of timing.
+// Member means in two launches.  means_part_kernel: workgroup (c S + s, h)
+// sums slice s of cluster c's rows (the cluster's rows cut into S equal
+// runs); each thread owns one 16-byte vector (EPV elements) of the row slice
+// [col0, col0 + dc) and sums its rows r, r + RPI, r + 2 RPI, ... of the run in
+// that order (four loads in flight); the RPI partial sums of a column are then
+// added in row-group order.  means_combine_kernel adds the S run sums in run
+// order and divides by the cluster size.  The result is independent of timing.
 template <typename T>
-__global__ __launch_bounds__(256) void means_kernel(const T* __restrict__ x, int d, int col0, int dc,
-                                                    const int32_t* __restrict__ perm,
-                                                    const int32_t* __restrict__ off, int N, int C,
-                                                    float* __restrict__ out, int out_stride,
-                                                    bool keep_empty) {
+__global__ __launch_bounds__(256) void means_part_kernel(const T* __restrict__ x, int d, int col0, int dc,
+                                                         const int32_t* __restrict__ perm,
+                                                         const int32_t* __restrict__ off, int N, int C, int S,
+                                                         float* __restrict__ part_out) {
   constexpr int EPV = 16 / sizeof(T);
   __shared__ float part[256 * EPV];
-  const int c = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-  const int a = off[size_t(h) * (C + 1) + c], b = off[size_t(h) * (C + 1) + c + 1];
-  float* o = out + (size_t(h) * C + c) * out_stride;
-  if (b == a) {
-    if (!keep_empty)
-      for (int j = t; j < dc; j += 256) o[j] = 0.f;
-    return;
-  }
+  const int c = blockIdx.x / S, sl = blockIdx.x % S, h = blockIdx.y, t = threadIdx.x;
+  const int ca = off[size_t(h) * (C + 1) + c], cb = off[size_t(h) * (C + 1) + c + 1];
+  const int len = ceil_div(cb - ca, S);
+  const int a = min(cb, ca + sl * len), b = min(cb, a + len);
+  float* o = part_out + ((size_t(h) * C + c) * S + sl) * dc;
   const int V = dc / EPV;          // vectors per row slice
   const int RPI = 256 / V;         // rows per iteration
   const int r = t / V, j = t % V;
@@ -222,15 +220,34 @@ __global__ __launch_bounds__(256) void means_kernel(const T* __restrict__ x, int
     const int rows = min(RPI, b - a);
     float sum = 0.f;
     for (int k = 0; k < rows; ++k) sum += part[k * dc + t];
-    o[t] = sum / float(b - a);
+    o[t] = sum;
+  }
+}
+
+__global__ __launch_bounds__(256) void means_combine_kernel(const float* __restrict__ part_in,
+                                                            const int32_t* __restrict__ off, int C, int S,
+                                                            int dc, float* __restrict__ out, int out_stride,
+                                                            bool keep_empty) {
+  const int c = blockIdx.x, h = blockIdx.y;
+  const int n = off[size_t(h) * (C + 1) + c + 1] - off[size_t(h) * (C + 1) + c];
+  float* o = out + (size_t(h) * C + c) * out_stride;
+  const float* pi = part_in + (size_t(h) * C + c) * S * dc;
+  for (int t = threadIdx.x; t < dc; t += blockDim.x) {
+    if (n == 0) {
+      if (!keep_empty) o[t] = 0.f;
+      continue;
+    }
+    float sum = 0.f;
+    for (int sl = 0; sl < S; ++sl) sum += pi[sl * dc + t];
+    o[t] = sum / float(n);
   }
 }
 
 // Rows into cluster order and member means in one pass: one workgroup per
 // (cluster, head) copies its rows to their cluster-order positions and sums
-// them in the order of means_kernel (thread (r, j) takes rows r, r + RPI, ...;
-// the RPI partial sums are added in row-group order), so both results equal
-// those of the two separate kernels.  An empty cluster's mean is zero.
+// them in the order of means_part_kernel with a single run (thread (r, j)
+// takes rows r, r + RPI, ...; the RPI partial sums are added in row-group
+// order).  An empty cluster's mean is zero.
 template <typename T>
 __global__ __launch_bounds__(256) void gather_means_kernel(const T* __restrict__ x, T* __restrict__ xp,
                                                            const int32_t* __restrict__ perm,
@@ -365,19 +382,30 @@ hipError_t gather_rows(const void* x, void* x_perm, const int32_t* perm, int H, 
   return hipGetLastError();
 }
 
+int means_runs(int H, int N, int C) {
+  // enough workgroups to fill the chip (about 4096), runs of at least 32 rows
+  const int want = ceil_div(4096, max(1, C * H));
+  const int cap = max(1, N / max(1, C * 32));
+  return max(1, min(16, min(want, cap)));
+}
+
+size_t means_scratch(int H, int N, int C, int dc) {
+  return size_t(H) * C * means_runs(H, N, C) * dc * sizeof(float);
+}
+
 hipError_t cluster_means(const void* x, int dtype, int d, int col0, int dc, const int32_t* perm,
                          const int32_t* offsets, int H, int N, int C, float* out, int out_stride,
-                         bool keep_empty, hipStream_t st) {
+                         bool keep_empty, float* scratch, hipStream_t st) {
   const int esz = dtype == SA_F32 ? 4 : 2;
   // 16-byte vectors of the slice; at most 256 of them per row
   if ((col0 * esz) % 16 || (dc * esz) % 16 || (d * esz) % 16 || dc * esz > 256 * 16) return hipErrorInvalidValue;
-  dim3 g(C, H);
+  const int S = means_runs(H, N, C);
+  dim3 g(C * S, H);
   if (dtype == SA_F32)
-    means_kernel<float><<<g, 256, 0, st>>>((const float*)x, d, col0, dc, perm, offsets, N, C, out,
-                                           out_stride, keep_empty);
+    means_part_kernel<float><<<g, 256, 0, st>>>((const float*)x, d, col0, dc, perm, offsets, N, C, S, scratch);
   else
-    means_kernel<bf16_t><<<g, 256, 0, st>>>((const bf16_t*)x, d, col0, dc, perm, offsets, N, C, out,
-                                            out_stride, keep_empty);
+    means_part_kernel<bf16_t><<<g, 256, 0, st>>>((const bf16_t*)x, d, col0, dc, perm, offsets, N, C, S, scratch);
+  means_combine_kernel<<<dim3(C, H), 128, 0, st>>>(scratch, offsets, C, S, dc, out, out_stride, keep_empty);
   return hipGetLastError();
 }
 

@@ -98,7 +98,7 @@ int max_tiles(const sa_problem* p, const sa_cluster_cfg* q) {
 size_t cluster_scratch(const sa_problem* p, const sa_cluster_cfg* c) {
   const int H = p->heads, N = p->n;
   switch (c->method) {
-    case SA_KMEANS: return label_sort_scratch(H, N, c->clusters) + 256;
+    case SA_KMEANS: return means_scratch(H, N, c->clusters, p->d) + label_sort_scratch(H, N, c->clusters) + 512;
     case SA_BISECT: return bisect_scratch(H, N, p->d, c->leaf) + 256;
     case SA_SUBSPACE: {
       Arena a{nullptr, 0, 0};
@@ -108,6 +108,9 @@ size_t cluster_scratch(const sa_problem* p, const sa_cluster_cfg* c) {
       a.get<float>(comp);                  // compact slice centroids
       a.get<int32_t>(size_t(H) * N);       // slice perm
       a.get<int32_t>(size_t(H) * (c->clusters + 1));
+      size_t ms = 0;
+      for (int s = 0; s < 3; ++s) ms = std::max(ms, means_scratch(H, N, c->clusters, c->sub_dims[s]));
+      a.take(ms);                          // member-mean run sums
       return a.used + std::max(label_sort_scratch(H, N, c->clusters),
                                label_sort_scratch(H, N, clusters_of(p, c))) + 256;
     }
@@ -220,10 +223,11 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
     if (c->init == SA_INIT_FIRST) e = kmeans_seed(x, dt, d, 0, d, H, N, C, out->centroids, st);
     for (int it = 0; it < c->iters && e == hipSuccess; ++it) {
       Arena tmp = s;
+      float* msc = (float*)tmp.take(means_scratch(H, N, C, d));
       e = kmeans_assign(x, dt, d, 0, d, H, N, C, out->centroids, out->labels, st);
       if (e == hipSuccess) e = label_sort(out->labels, out->perm, out->offsets, H, N, C, tmp, st);
       if (e == hipSuccess)
-        e = cluster_means(x, dt, d, 0, d, out->perm, out->offsets, H, N, C, out->centroids, d, true, st);
+        e = cluster_means(x, dt, d, 0, d, out->perm, out->offsets, H, N, C, out->centroids, d, true, msc, st);
     }
   } else if (c->method == SA_BISECT) {
     Arena tmp = s;
@@ -239,6 +243,9 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
     float* sub_c = tmp.get<float>(comp);
     int32_t* sperm = tmp.get<int32_t>(size_t(H) * N);
     int32_t* soff = tmp.get<int32_t>(size_t(H) * (Cs + 1));
+    size_t ms = 0;
+    for (int k = 0; k < 3; ++k) ms = std::max(ms, means_scratch(H, N, Cs, c->sub_dims[k]));
+    float* msc = (float*)tmp.take(ms);
     size_t coff = 0;
     int col0 = 0;
     for (int k = 0; k < 3 && e == hipSuccess; ++k) {
@@ -251,7 +258,7 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
         e = kmeans_assign(x, dt, d, col0, ds, H, N, Cs, cs, lab, st);
         if (e == hipSuccess) e = label_sort(lab, sperm, soff, H, N, Cs, t2, st);
         if (e == hipSuccess)
-          e = cluster_means(x, dt, d, col0, ds, sperm, soff, H, N, Cs, cs, ds, true, st);
+          e = cluster_means(x, dt, d, col0, ds, sperm, soff, H, N, Cs, cs, ds, true, msc, st);
       }
       coff += size_t(H) * Cs * ds;
       col0 += ds;

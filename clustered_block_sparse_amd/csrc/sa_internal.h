@@ -81,13 +81,16 @@ hipError_t gather_rows(const void* x, void* x_perm, const int32_t* perm, int H, 
 // Member means of columns [col0, col0+dc) of x rows per cluster, fp32, written
 // to out[h][c][0..dc) with row stride out_stride.  Empty clusters: keep the
 // existing value if keep_empty, else zeros.
-// gather_rows and cluster_means (whole rows, empty clusters -> zero) in one
-// pass over the rows; results identical to the two calls
+// gather_rows and the member means (whole rows, empty clusters -> zero) in
+// one pass over the rows, one workgroup per cluster
 hipError_t gather_means(const void* x, int dtype, int d, const int32_t* perm, const int32_t* offsets,
                         int H, int N, int C, void* x_perm, float* means, hipStream_t st);
+// Rows are summed in runs (one workgroup each) whose partial sums go to
+// `scratch` (means_scratch bytes) and are added in run order.
+size_t means_scratch(int H, int N, int C, int dc);
 hipError_t cluster_means(const void* x, int dtype, int d, int col0, int dc, const int32_t* perm,
                          const int32_t* offsets, int H, int N, int C, float* out, int out_stride,
-                         bool keep_empty, hipStream_t st);
+                         bool keep_empty, float* scratch, hipStream_t st);
 
 // labels[h][perm[h][p]] = cluster of position p, from offsets
 hipError_t labels_from_offsets(const int32_t* perm, const int32_t* offsets, int32_t* labels, int H,
