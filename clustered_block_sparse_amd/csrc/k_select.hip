@@ -46,16 +46,27 @@ __global__ void zero_u64(unsigned long long* p, int n) {
 constexpr int SUB_T = 1024;
 constexpr double MASS_ONE = 4503599627370496.0;  // 2^52
 
+constexpr int CAND = 1024;  // combos of the selected interpolated bin kept in LDS
+
 struct SubRow {
   double T[3][32];
   unsigned long long hw[2048];   // radix bin weights (mass or keys)
+  unsigned long long hk[2048];   // keys per interpolated bin (mass selection)
   unsigned long long wsum[16];
   unsigned long long red[2][16];
   double dred[16];
   uint32_t words[1024];
+  unsigned long long ck[CAND];   // candidates: order key, weight, combo, keys
+  unsigned long long cw[CAND];
+  int cg[CAND];
+  uint32_t ckeys[CAND];
+  int ncand;
   int sel_bin;
   unsigned long long sel_w;
+  unsigned long long sel_k;      // keys of the bins before the selected one
   int tie_g;
+  unsigned long long tie_key;
+  long long tie_keys;
 };
 
 __device__ __forceinline__ unsigned long long order_key(double l) {
@@ -167,6 +178,108 @@ __device__ Boundary wselect(Eval ev, int C, unsigned long long target, unsigned 
   return Boundary{prefix, tg};
 }
 
+// The same boundary as wselect, with the keys of every combo at or before it,
+// in two passes over the combos.  Pass 1 bins every combo by its logit,
+// interpolated between the row's largest and smallest (bin = floor((mx - l)
+// 2048 / (mx - mn)) is monotone in the logit, so the bins follow rank order),
+// and finds the bin where the cumulative weight reaches the target.  Pass 2
+// keeps that bin's combos in LDS; each counts the weight ranked before it,
+// which names the boundary exactly.  ok = false when the bin holds more than
+// CAND combos (the caller then runs wselect).
+struct BoundK {
+  Boundary b;
+  long long keys;
+  bool ok;
+};
+
+template <int WK, typename Eval>
+__device__ BoundK wselect_interp(Eval ev2, int C, unsigned long long target, double mx, double mn,
+                                 SubRow& R) {
+  const int t = threadIdx.x;
+  const double span = mx - mn;
+  const double inv = span > 1e-280 ? 2048.0 / span : 0.0;
+  auto bin_of = [&](double l) -> int {
+    const int b = int((mx - l) * inv);
+    return b < 2047 ? b : 2047;
+  };
+  for (int b = t; b < 2048; b += SUB_T) {
+    R.hw[b] = 0ull;
+    R.hk[b] = 0ull;
+  }
+  if (t == 0) R.ncand = 0;
+  __syncthreads();
+  for (int g = t; g < C; g += SUB_T) {
+    double l;
+    unsigned long long k, mass, keys;
+    if (!ev2(g, l, k, mass, keys)) continue;
+    const int b = bin_of(l);
+    atomicAdd(&R.hw[b], WK == 0 ? mass : keys);
+    if (WK == 0) atomicAdd(&R.hk[b], keys);
+  }
+  __syncthreads();
+  const unsigned long long w0 = R.hw[2 * t], w1 = R.hw[2 * t + 1];
+  const unsigned long long k0 = WK == 0 ? R.hk[2 * t] : w0, k1 = WK == 0 ? R.hk[2 * t + 1] : w1;
+  unsigned long long tw, tk;
+  const unsigned long long pw = bscan<unsigned long long>(w0 + w1, R.wsum, tw);
+  const unsigned long long pk = bscan<unsigned long long>(k0 + k1, R.wsum, tk);
+  if (t == 0) R.sel_bin = -1;
+  __syncthreads();
+  const unsigned long long rem0 = target;
+  if (pw < rem0 && rem0 <= pw + w0) {
+    R.sel_bin = 2 * t;
+    R.sel_w = pw;
+    R.sel_k = pk;
+  } else if (pw + w0 < rem0 && rem0 <= pw + w0 + w1) {
+    R.sel_bin = 2 * t + 1;
+    R.sel_w = pw + w0;
+    R.sel_k = pk + k0;
+  }
+  __syncthreads();
+  const int sb = R.sel_bin;
+  if (sb < 0) return BoundK{Boundary{0ull, C}, (long long)tk, true};  // target beyond the total
+  const unsigned long long rem = rem0 - R.sel_w;
+  const unsigned long long kbefore = R.sel_k;
+  for (int g = t; g < C; g += SUB_T) {
+    double l;
+    unsigned long long k, mass, keys;
+    if (!ev2(g, l, k, mass, keys) || bin_of(l) != sb) continue;
+    const int slot = atomicAdd(&R.ncand, 1);
+    if (slot < CAND) {
+      R.ck[slot] = k;
+      R.cg[slot] = g;
+      R.cw[slot] = WK == 0 ? mass : keys;
+      R.ckeys[slot] = uint32_t(keys);
+    }
+  }
+  if (t == 0) R.tie_g = -1;
+  __syncthreads();
+  const int m = R.ncand;
+  if (m > CAND) return BoundK{Boundary{0ull, -1}, 0, false};
+  if (t < m) {
+    const unsigned long long mk = R.ck[t];
+    const int mg = R.cg[t];
+    unsigned long long sw = 0, sk = 0;
+    for (int j = 0; j < m; ++j) {
+      const unsigned long long kj = R.ck[j];
+      if (kj < mk || (kj == mk && R.cg[j] < mg)) {
+        sw += R.cw[j];
+        sk += R.ckeys[j];
+      }
+    }
+    const unsigned long long wt = R.cw[t];
+    if (sw < rem && rem <= sw + wt) {
+      R.tie_g = mg;
+      R.tie_key = mk;
+      R.tie_keys = (long long)(kbefore + sk + R.ckeys[t]);
+    }
+  }
+  __syncthreads();
+  // the bin's weight reaches rem, so exactly one candidate matched
+  const BoundK r{Boundary{R.tie_key, R.tie_g}, R.tie_keys, true};
+  __syncthreads();
+  return r;
+}
+
 __device__ __forceinline__ bool later(const Boundary& a, const Boundary& b, int C) {
   // is boundary a later in rank order than b (C = past every combo)?
   if (a.g == C) return b.g != C;
@@ -252,17 +365,22 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const dou
     mn = fmin(mn, __longlong_as_double(R.red[1][j]));
   }
   __syncthreads();
-  double zs = 0.0;
-  for (int g = t; g < C; g += SUB_T) {
-    double l;
-    if (logit(g, l)) zs += exp(l - mx);
+  const double P = a.top_p;
+  const bool need_mass = P > 0.0 && P < 1.0;  // otherwise no mass target: no normaliser
+  double Z = 1.0;
+  if (need_mass) {
+    double zs = 0.0;
+    for (int g = t; g < C; g += SUB_T) {
+      double l;
+      if (logit(g, l)) zs += exp(l - mx);
+    }
+    for (int o = 32; o > 0; o >>= 1) zs += __shfl_xor(zs, o, 64);
+    if (lane == 0) R.dred[w] = zs;
+    __syncthreads();
+    Z = 0.0;
+    for (int j = 0; j < SUB_T / 64; ++j) Z += R.dred[j];
+    __syncthreads();
   }
-  for (int o = 32; o > 0; o >>= 1) zs += __shfl_xor(zs, o, 64);
-  if (lane == 0) R.dred[w] = zs;
-  __syncthreads();
-  double Z = 0.0;
-  for (int j = 0; j < SUB_T / 64; ++j) Z += R.dred[j];
-  __syncthreads();
   const unsigned long long kmin = order_key(mx), kmax = order_key(mn);
   auto ev = [&](int g, unsigned long long& k, unsigned long long& mass, unsigned long long& keys) -> bool {
     double l;
@@ -272,16 +390,16 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const dou
     keys = (unsigned long long)(ko[g + 1] - ko[g]);
     return true;
   };
+  auto ev2 = [&](int g, double& l, unsigned long long& k, unsigned long long& mass,
+                 unsigned long long& keys) -> bool {
+    if (!logit(g, l)) return false;
+    k = order_key(l);
+    mass = (unsigned long long)llrint(exp(l - mx) / Z * MASS_ONE);
+    keys = (unsigned long long)(ko[g + 1] - ko[g]);
+    return true;
+  };
   const int Cfull = C;
   const Boundary b0{0ull, -1};  // before every combo
-  Boundary bp = b0, bf = b0;
-  const double P = a.top_p;
-  if (P >= 1.0) {
-    bp = Boundary{0ull, Cfull};
-  } else if (P > 0.0) {
-    bp = wselect<0>(ev, C, (unsigned long long)llrint(P * MASS_ONE), kmin, kmax, R);
-  }
-  if (a.floor_units > 0) bf = wselect<1>(ev, C, (unsigned long long)a.floor_units, kmin, kmax, R);
   auto keys_through = [&](const Boundary& b) -> long long {
     // keys of every combo up to and including the boundary: the predicate
     // the mask is built from, so counts and mask agree by construction
@@ -296,8 +414,32 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const dou
     bscan<unsigned long long>(sk, R.wsum, tot);
     return (long long)tot;
   };
-  const Boundary binit = (bp.g < 0) ? bf : (bf.g < 0 ? bp : (later(bf, bp, Cfull) ? bf : bp));
-  const long long n_init = keys_through(binit);
+  // boundary of a cumulative target and the keys through it
+  auto select_mass = [&](unsigned long long target) -> BoundK {
+    BoundK r = wselect_interp<0>(ev2, C, target, mx, mn, R);
+    if (!r.ok) {
+      r.b = wselect<0>(ev, C, target, kmin, kmax, R);
+      r.keys = keys_through(r.b);
+    }
+    return r;
+  };
+  auto select_keys = [&](unsigned long long target) -> BoundK {
+    BoundK r = wselect_interp<1>(ev2, C, target, mx, mn, R);
+    if (!r.ok) {
+      r.b = wselect<1>(ev, C, target, kmin, kmax, R);
+      r.keys = keys_through(r.b);
+    }
+    return r;
+  };
+  BoundK bp{b0, 0, true}, bf{b0, 0, true};
+  if (P >= 1.0) {
+    bp = BoundK{Boundary{0ull, Cfull}, keys_through(Boundary{0ull, Cfull}), true};
+  } else if (P > 0.0) {
+    bp = select_mass((unsigned long long)llrint(P * MASS_ONE));
+  }
+  if (a.floor_units > 0) bf = select_keys((unsigned long long)a.floor_units);
+  const BoundK binit = (bp.b.g < 0) ? bf : (bf.b.g < 0 ? bp : (later(bf.b, bp.b, Cfull) ? bf : bp));
+  const long long n_init = binit.keys;
   if (online && pass == 0) {
     if (t == 0) {
       atomicAdd(&acc[h], (unsigned long long)((long long)qsize * n_init));
@@ -305,17 +447,18 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const dou
     }
     return;
   }
-  Boundary bfin = binit;
+  BoundK bfin_k = binit;
   int kh = 0;
   if (online) {
     const long long A = (long long)acc[h];
     kh = int((A + a.N - 1) / a.N);
     if (n_init < kh) {
-      const Boundary bk = wselect<1>(ev, C, (unsigned long long)kh, kmin, kmax, R);
-      if (binit.g < 0 || later(bk, binit, Cfull)) bfin = bk;
+      const BoundK bk = select_keys((unsigned long long)kh);
+      if (binit.b.g < 0 || later(bk.b, binit.b, Cfull)) bfin_k = bk;
     }
   }
-  const long long n_fin = keys_through(bfin);
+  const Boundary bfin = bfin_k.b;
+  const long long n_fin = bfin_k.keys;
   for (int x = t; x < W; x += SUB_T) R.words[x] = 0u;
   __syncthreads();
   if (bfin.g >= 0) {
