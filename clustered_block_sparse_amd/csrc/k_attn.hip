@@ -330,12 +330,6 @@ __device__ int fill_chunk(const uint32_t* __restrict__ mr, int W, int Ck, const 
   return nrc;
 }
 
-// key row of concatenated position `pos`, advancing a cursor over rp[]
-__device__ __forceinline__ int cursor_row(const int* rs, const int* rp, int nrc, int pos, int& cur) {
-  while (cur + 1 < nrc && rp[cur + 1] <= pos) ++cur;
-  return rs[cur] + (pos - rp[cur]);
-}
-
 // --------------------------------------------------------------------------
 // fp32 (and generic) path: one thread per query row
 // --------------------------------------------------------------------------
@@ -508,6 +502,7 @@ struct MfmaLds {
   int wsum[16];
   int fsh[2];
   float bias[KT];
+  int rowidx[2][KT];  // general path: key row of each position of a tile (by tile parity)
 };
 
 // V^T in 64-key blocks, keys in MFMA order:
@@ -901,13 +896,49 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
       if (nrc == 0) break;
       const int total = S.rp[nrc];
       const int ntile = ceil_div(total, KT);
-      int cur_k = 0, cur_v = 0;
+      // Wave 0 lists the key row of every position of tile t in
+      // S.rowidx[t & 1].  Window: the 64 ranges from r0, the range holding the
+      // tile's first position; ranges are never empty, so they cover the
+      // tile.  Short ranges: lane l writes the positions range r0 + l shares
+      // with the tile.  When some range covers more than 8 of them, lane j
+      // instead finds the range of position j by binary search in the window.
+      // r0 then moves to the range holding the next tile's start.
+      int r0 = 0;
+      auto build_rows = [&](int t) {
+        const int base = t * KT, end = min(base + KT, total);
+        const int r = r0 + lane;
+        int st = 0, en = 0;
+        if (r < nrc) {
+          st = S.rp[r];
+          en = S.rp[r + 1];
+        }
+        const int lo = max(st, base), hi = min(en, end);
+        int* ri = S.rowidx[t & 1];
+        if (__ballot(r < nrc && hi - lo > 8)) {
+          const int pos = base + lane;
+          if (pos < end) {
+            int L = r0, R = min(r0 + 64, nrc);  // S.rp[L] <= pos < S.rp[R]
+            while (R - L > 1) {
+              const int mid = (L + R) >> 1;
+              if (S.rp[mid] <= pos) L = mid;
+              else R = mid;
+            }
+            ri[lane] = S.rs[L] + (pos - S.rp[L]);
+          }
+        } else if (r < nrc) {
+          const int rsr = S.rs[r];
+          for (int pos = lo; pos < hi; ++pos) ri[pos - base] = rsr + (pos - st);
+        }
+        const uint64_t bal = __ballot(r < nrc && st <= base + KT);
+        r0 += 63 - __clzll((unsigned long long)bal);
+      };
       auto load_tile = [&](int tt) {
         const int base = tt * KT;
+        const int* ri = S.rowidx[tt & 1];
         {
           const int pos = base + k_slot;
           if (pos < total) {
-            const int row = cursor_row(S.rs, S.rp, nrc, pos, cur_k);
+            const int row = ri[k_slot];
             const uint4* src = reinterpret_cast<const uint4*>(kh + size_t(row) * D + k_c0);
 #pragma unroll
             for (int q = 0; q < KCH / 8; ++q) kreg[q] = src[q];
@@ -916,25 +947,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
             for (int q = 0; q < KCH / 8; ++q) kreg[q] = make_uint4(0, 0, 0, 0);
           }
         }
-        int cv = cur_v;
 #pragma unroll
         for (int kq = 0; kq < KPT; ++kq) {
           const int pos = base + v_kg * KPT + kq;
           if (pos < total) {
-            const int row = cursor_row(S.rs, S.rp, nrc, pos, cv);
-            if (kq == 0) cur_v = cv;
+            const int row = ri[v_kg * KPT + kq];
             vreg[kq] = *reinterpret_cast<const uint4*>(vh + size_t(row) * D + v_dg * 8);
           } else {
             vreg[kq] = make_uint4(0, 0, 0, 0);
           }
         }
       };
-      if (ntile > 0) load_tile(0);
+      if (ntile > 0) {
+        if (w == 0) build_rows(0);
+        __syncthreads();
+        load_tile(0);
+      }
       for (int tt = 0; tt < ntile; ++tt) {
         bf16_t* Kb = (tt & 1) ? K1 : K0;
         bf16_t* VLb = (tt & 1) ? VL1 : VL0;
         bf16_t* VHb = (tt & 1) ? VH1 : VH0;
         store_tile(Kb, VLb, VHb);
+        if (w == 0 && tt + 1 < ntile) build_rows(tt + 1);
         __syncthreads();
         if (tt + 1 < ntile) load_tile(tt + 1);
         compute_tile(Kb, VLb, VHb, total - tt * KT);
