@@ -307,7 +307,7 @@ __device__ unsigned long long lds_select64(const unsigned long long* key, int m,
 // chunks: int4 {segment (level-local), position, count, 0}
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void build_tree_kernel(LevelTabs tb, int N, int4* segs,
-                                                          int4* chunks) {
+                                                          int4* chunks, int32_t* kids) {
   __shared__ int wsum[16];
   const int t = threadIdx.x;
   if (t == 0) segs[0] = make_int4(0, N, 0, 0);
@@ -334,6 +334,7 @@ __global__ __launch_bounds__(1024) void build_tree_kernel(LevelTabs tb, int N, i
       const int kpre = block_excl_scan<int>(nchild, wsum, tot2) + child_carry;
       if (k < tb.nseg[lv]) {
         segs[tb.sb[lv] + k] = make_int4(s.x, s.y, nl, cpre);
+        kids[tb.sb[lv] + k] = kpre;  // index of its first child one level down
         for (int c = 0; c < nchunk; ++c) {
           const int pos = s.x + c * BCH;
           chunks[tb.cb[lv] + cpre + c] = make_int4(k, pos, min(BCH, s.x + s.y - pos), 0);
@@ -437,14 +438,64 @@ struct TopBufs {
   int2* selbin;        // [H][max_seg] bin holding rank n_left, rank inside it (bin -1: keys all equal)
   unsigned long long* cand;  // [H][max_seg][CAND_CAP] (key << 32 | position) of that bin
   int32_t* ccount;     // [H][max_seg] candidates (zero between uses)
+  // children's first round formed during the parent's last one (see
+  // predict_children below)
+  const int32_t* kids; // level table: index of each segment's first child one level down
+  int4* pred;          // [H][max_seg] predicted first two left / right positions (-1: none)
+  uint32_t* keyL;      // [H][N] round-0 key of each row for the predicted left child
+  uint32_t* keyR;      // [H][N] ... for the predicted right child
+  uint32_t* keys_next; // [H][N] children's round-0 keys, in the children's order
+  int32_t* pred_ok;    // [H][max_seg] (next level) 1: the child's round-0 keys are in place
   int max_seg, max_chunk, N, round;  // round: 0 = first round of a level
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void delta_kernel(Src2<T> x, TopBufs b, int first) {
+// A child segment starts its first round from its first two tokens, which
+// are the first two positions (in the parent's order) of its side of the
+// parent's final split.  Before the parent's last round they are predicted
+// from the sides of the round before; the last round's delta pass then also
+// forms, for every row, the child's first-round key under that prediction
+// (the same arithmetic, in the same order, as the child's own pass), and the
+// partition carries the keys of each row's side into the children's order
+// and checks the prediction against the actual first positions.  A child
+// whose prediction held skips its first delta pass; the others run it.
+__global__ __launch_bounds__(64) void firsts_kernel(TopBufs b) {
+  const int h = blockIdx.y, lane = threadIdx.x;
+  const int4 sg = b.segs[blockIdx.x];
+  if (sg.z == 0) return;
+  const uint8_t* sd = b.side + size_t(h) * b.N + sg.x;
+  int fl0 = -1, fl1 = -1, fr0 = -1, fr1 = -1, nl = 0, nr = 0;
+  for (int base = 0; base < sg.y && (nl < 2 || nr < 2); base += 64) {
+    const int i = base + lane;
+    const bool v = i < sg.y;
+    const bool left = v && sd[i] != 0;
+    uint64_t ml = __ballot(left), mr = __ballot(v && !left);
+    while (nl < 2 && ml) {
+      const int p = sg.x + base + __ffsll((unsigned long long)ml) - 1;
+      if (nl == 0) fl0 = p; else fl1 = p;
+      ++nl;
+      ml &= ml - 1;
+    }
+    while (nr < 2 && mr) {
+      const int p = sg.x + base + __ffsll((unsigned long long)mr) - 1;
+      if (nr == 0) fr0 = p; else fr1 = p;
+      ++nr;
+      mr &= mr - 1;
+    }
+  }
+  if (lane == 0)
+    b.pred[size_t(h) * b.max_seg + blockIdx.x] =
+        make_int4(nl == 2 ? fl0 : -1, nl == 2 ? fl1 : -1, nr == 2 ? fr0 : -1, nr == 2 ? fr1 : -1);
+}
+
+// PRED: also the predicted children's first-round keys of every row.
+// use_ok: a segment whose first-round keys (and their min / max) its parent
+// already formed has nothing to do.
+template <typename T, int D, bool PRED>
+__global__ __launch_bounds__(256) void delta_kernel(Src2<T> x, TopBufs b, int first, int use_ok) {
   using G = RowGeo<T, D>;
-  constexpr int U = 8;  // wave steps in flight
+  constexpr int U = PRED ? 16 : 8;  // wave steps in flight
   __shared__ float wv[D], mv[D];
+  __shared__ float wvc[PRED ? 2 : 1][D], mvc[PRED ? 2 : 1][D];  // children (left, right)
   __shared__ int pidx[BCH / DELTA_SPLIT];  // the part's rows (original tokens)
   const int h = blockIdx.y, t = threadIdx.x;
   // a workgroup takes one of the DELTA_SPLIT equal parts of a chunk: more,
@@ -453,59 +504,103 @@ __global__ __launch_bounds__(256) void delta_kernel(Src2<T> x, TopBufs b, int fi
   const int r0 = (blockIdx.x % DELTA_SPLIT) * (BCH / DELTA_SPLIT);
   if (r0 >= chunk.z) return;
   const int4 ch = make_int4(chunk.x, chunk.y + r0, min(BCH / DELTA_SPLIT, chunk.z - r0), chunk.w);
-  const int4 sg = b.segs[ch.x];
-  const int32_t* ph = b.perm + size_t(h) * b.N;
-  const T* __restrict__ xh = x.head(h, b.N, D);
-  for (int i = t; i < ch.z; i += 256) pidx[i] = ph[ch.y + i];
-  if (t < D) {
-    float c1, c2;
-    if (first) {
-      c1 = to_f(xh[size_t(ph[sg.x]) * D + t]);
-      c2 = to_f(xh[size_t(ph[sg.x + 1]) * D + t]);
-    } else {
-      const float* c = b.cen + (size_t(h) * b.max_seg + ch.x) * 2 * D;
-      c1 = c[t];
-      c2 = c[D + t];
-    }
-    wv[t] = c2 - c1;
-    mv[t] = c1 + c2;
-  }
-  __syncthreads();
   const int lane = t & 63, w = t >> 6;
-  const int sub = lane % G::LPR, rsub = lane / G::LPR;
-  float wr[G::EPV], mr[G::EPV];
-#pragma unroll
-  for (int e = 0; e < G::EPV; ++e) {
-    wr[e] = wv[sub * G::EPV + e];
-    mr[e] = mv[sub * G::EPV + e];
-  }
-  constexpr int STEP = 4 * G::RPW;  // rows per block step
   uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-  for (int rb = w * G::RPW; rb < ch.z; rb += U * STEP) {
-    int pos[U];
-    uint4 raw[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int r = rb + u * STEP + rsub;
-      pos[u] = r < ch.z ? r : 0;
+  if (use_ok && b.pred_ok[size_t(h) * b.max_seg + ch.x]) return;
+  {
+    const int4 sg = b.segs[ch.x];
+    const int32_t* ph = b.perm + size_t(h) * b.N;
+    const T* __restrict__ xh = x.head(h, b.N, D);
+    for (int i = t; i < ch.z; i += 256) pidx[i] = ph[ch.y + i];
+    if (t < D) {
+      float c1, c2;
+      if (first) {
+        c1 = to_f(xh[size_t(ph[sg.x]) * D + t]);
+        c2 = to_f(xh[size_t(ph[sg.x + 1]) * D + t]);
+      } else {
+        const float* c = b.cen + (size_t(h) * b.max_seg + ch.x) * 2 * D;
+        c1 = c[t];
+        c2 = c[D + t];
+      }
+      wv[t] = c2 - c1;
+      mv[t] = c1 + c2;
+      if constexpr (PRED) {
+        // a child without a prediction gets zero centroids (its keys go unused)
+        const int4 pr = b.pred[size_t(h) * b.max_seg + ch.x];
+        float a1 = 0.f, a2 = 0.f, q1 = 0.f, q2 = 0.f;
+        if (pr.x >= 0) {
+          a1 = to_f(xh[size_t(ph[pr.x]) * D + t]);
+          a2 = to_f(xh[size_t(ph[pr.y]) * D + t]);
+        }
+        if (pr.z >= 0) {
+          q1 = to_f(xh[size_t(ph[pr.z]) * D + t]);
+          q2 = to_f(xh[size_t(ph[pr.w]) * D + t]);
+        }
+        wvc[0][t] = a2 - a1;
+        mvc[0][t] = a1 + a2;
+        wvc[PRED ? 1 : 0][t] = q2 - q1;
+        mvc[PRED ? 1 : 0][t] = q1 + q2;
+      }
     }
+    __syncthreads();
+    const int sub = lane % G::LPR, rsub = lane / G::LPR;
+    float wr[G::EPV], mr[G::EPV];
+    float wl[PRED ? G::EPV : 1], ml[PRED ? G::EPV : 1], wq[PRED ? G::EPV : 1], mq[PRED ? G::EPV : 1];
 #pragma unroll
-    for (int u = 0; u < U; ++u) raw[u] = ld16(xh + size_t(pidx[pos[u]]) * D + sub * G::EPV);
+    for (int e = 0; e < G::EPV; ++e) {
+      wr[e] = wv[sub * G::EPV + e];
+      mr[e] = mv[sub * G::EPV + e];
+      if constexpr (PRED) {
+        wl[e] = wvc[0][sub * G::EPV + e];
+        ml[e] = mvc[0][sub * G::EPV + e];
+        wq[e] = wvc[PRED ? 1 : 0][sub * G::EPV + e];
+        mq[e] = mvc[PRED ? 1 : 0][sub * G::EPV + e];
+      }
+    }
+    constexpr int STEP = 4 * G::RPW;  // rows per block step
+    for (int rb = w * G::RPW; rb < ch.z; rb += U * STEP) {
+      int pos[U];
+      uint4 raw[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      float v[G::EPV];
-      unpack_vec<T, G::EPV>(raw[u], v);
-      float acc = 0.f;
+      for (int u = 0; u < U; ++u) {
+        const int r = rb + u * STEP + rsub;
+        pos[u] = r < ch.z ? r : 0;
+      }
 #pragma unroll
-      for (int e = 0; e < G::EPV; ++e) acc = fmaf(wr[e], fmaf(2.f, v[e], -mr[e]), acc);
+      for (int u = 0; u < U; ++u) raw[u] = ld16(xh + size_t(pidx[pos[u]]) * D + sub * G::EPV);
 #pragma unroll
-      for (int o = 1; o < G::LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
-      const int r = rb + u * STEP + rsub;
-      const uint32_t key = sortable(acc);
-      if (r < ch.z) {
-        kmin = min(kmin, key);
-        kmax = max(kmax, key);
-        if (sub == 0) b.keys[size_t(h) * b.N + ch.y + pos[u]] = key;
+      for (int u = 0; u < U; ++u) {
+        float v[G::EPV];
+        unpack_vec<T, G::EPV>(raw[u], v);
+        float acc = 0.f;
+#pragma unroll
+        for (int e = 0; e < G::EPV; ++e) acc = fmaf(wr[e], fmaf(2.f, v[e], -mr[e]), acc);
+#pragma unroll
+        for (int o = 1; o < G::LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
+        const int r = rb + u * STEP + rsub;
+        const uint32_t key = sortable(acc);
+        if (r < ch.z) {
+          kmin = min(kmin, key);
+          kmax = max(kmax, key);
+          if (sub == 0) b.keys[size_t(h) * b.N + ch.y + pos[u]] = key;
+        }
+        if constexpr (PRED) {
+          float al = 0.f, aq = 0.f;
+#pragma unroll
+          for (int e = 0; e < G::EPV; ++e) {
+            al = fmaf(wl[e], fmaf(2.f, v[e], -ml[e]), al);
+            aq = fmaf(wq[e], fmaf(2.f, v[e], -mq[e]), aq);
+          }
+#pragma unroll
+          for (int o = 1; o < G::LPR; o <<= 1) {
+            al += __shfl_xor(al, o, 64);
+            aq += __shfl_xor(aq, o, 64);
+          }
+          if (r < ch.z && sub == 0) {
+            b.keyL[size_t(h) * b.N + ch.y + pos[u]] = sortable(al);
+            b.keyR[size_t(h) * b.N + ch.y + pos[u]] = sortable(aq);
+          }
+        }
       }
     }
   }
@@ -822,9 +917,16 @@ __global__ __launch_bounds__(256) void update_kernel(TopBufs b) {
   }
 }
 
+// Stable partition of every split segment.  PRED: each row also carries its
+// side's predicted first-round key into the children's order, the prediction
+// of each child (its first two positions) is checked, and a child whose
+// prediction held gets the min / max of its keys (for its first selection).
+template <bool PRED>
 __global__ __launch_bounds__(1024) void partition_kernel(TopBufs b, const int32_t* __restrict__ perm_in,
                                                          int32_t* __restrict__ perm_out) {
   __shared__ int wsum[16];
+  __shared__ int firsts[4];  // actual first two left, first two right positions
+  __shared__ uint32_t cmm[2][2];  // children's key min / max (left, right)
   const int h = blockIdx.y, t = threadIdx.x;
   const int4 sg = b.segs[blockIdx.x];
   const int32_t* pi = perm_in + size_t(h) * b.N;
@@ -833,8 +935,14 @@ __global__ __launch_bounds__(1024) void partition_kernel(TopBufs b, const int32_
     for (int i = t; i < sg.y; i += 1024) po[sg.x + i] = pi[sg.x + i];
     return;
   }
-  const uint2 th = b.thr[size_t(h) * b.max_seg + blockIdx.x];
+  const size_t si = size_t(h) * b.max_seg + blockIdx.x;
+  const uint2 th = b.thr[si];
   const uint32_t* kh = b.keys + size_t(h) * b.N;
+  if (PRED && t < 4) {
+    firsts[t] = -1;
+    cmm[t >> 1][t & 1] = (t & 1) ? 0u : 0xFFFFFFFFu;
+  }
+  uint32_t mn[2] = {0xFFFFFFFFu, 0xFFFFFFFFu}, mx[2] = {0u, 0u};
   int run_left = 0;
   for (int base = 0; base < sg.y; base += 1024) {
     const int i = base + t;
@@ -846,8 +954,44 @@ __global__ __launch_bounds__(1024) void partition_kernel(TopBufs b, const int32_
     if (valid) {
       const int np = left ? sg.x + lpre : sg.x + sg.z + (i - lpre);
       po[np] = pi[p];
+      if constexpr (PRED) {
+        const size_t hn = size_t(h) * b.N;
+        const uint32_t ck = left ? b.keyL[hn + p] : b.keyR[hn + p];
+        b.keys_next[hn + np] = ck;
+        mn[left ? 0 : 1] = min(mn[left ? 0 : 1], ck);
+        mx[left ? 0 : 1] = max(mx[left ? 0 : 1], ck);
+        const int rank = left ? lpre : i - lpre;
+        if (rank < 2) firsts[(left ? 0 : 2) + rank] = p;
+      }
     }
     run_left += tot;
+  }
+  if constexpr (PRED) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+      for (int o = 32; o > 0; o >>= 1) {
+        mn[c] = min(mn[c], (uint32_t)__shfl_xor((int)mn[c], o, 64));
+        mx[c] = max(mx[c], (uint32_t)__shfl_xor((int)mx[c], o, 64));
+      }
+    if ((t & 63) == 0) {
+      atomicMin(&cmm[0][0], mn[0]);
+      atomicMax(&cmm[0][1], mx[0]);
+      atomicMin(&cmm[1][0], mn[1]);
+      atomicMax(&cmm[1][1], mx[1]);
+    }
+    __syncthreads();
+    if (t == 0) {
+      const int4 pr = b.pred[si];
+      const int kid = b.kids[blockIdx.x];
+      const size_t ko = size_t(h) * b.max_seg + kid;
+      const bool okl = pr.x >= 0 && pr.x == firsts[0] && pr.y == firsts[1];
+      const bool okr = pr.z >= 0 && pr.z == firsts[2] && pr.w == firsts[3];
+      b.pred_ok[ko] = okl;
+      b.pred_ok[ko + 1] = okr;
+      // (min / max of the segments one level down: reset since their last use)
+      if (okl) b.segmm[ko] = make_uint2(cmm[0][0], cmm[0][1]);
+      if (okr) b.segmm[ko + 1] = make_uint2(cmm[1][0], cmm[1][1]);
+    }
   }
 }
 
@@ -1249,7 +1393,8 @@ __global__ void leaf_offsets_kernel(int32_t* off0, int32_t* off1, int h0, int C,
 
 template <typename T, int D>
 hipError_t run_bisect(const void* x0, const void* x1, int h0, int H, int N, int L, int iters,
-                      const TreePlan& P, int4* segs, int4* chunks, int32_t* pa, int32_t* pb,
+                      const TreePlan& P, int4* segs, int4* chunks, const int32_t* kids, int32_t* pa,
+                      int32_t* pb,
                       int32_t* out0, int32_t* out1, TopBufs b, hipStream_t st) {
   const Src2<T> x{(const T*)x0, (const T*)x1, h0};
   const size_t sub_lds = sizeof(SubShared<D>);
@@ -1258,13 +1403,23 @@ hipError_t run_bisect(const void* x0, const void* x1, int h0, int H, int N, int 
     return hipErrorInvalidValue;
   int32_t* cur = pa;
   int32_t* nxt = pb;
+  bool predicted = false;  // this level's first-round keys were formed by its parent
   for (int lv = 0; lv < P.t.nlev; ++lv) {
     b.segs = segs + P.t.sb[lv];
     b.chunks = chunks + P.t.cb[lv];
+    b.kids = kids + P.t.sb[lv];
     b.perm = cur;
     const dim3 gs(P.t.nseg[lv], H), gc(P.t.nchunk[lv], H);
+    // predict the children's first round when they stay in the top phase
+    const bool predict = iters >= 2 && lv + 1 < P.t.nlev;
     for (int it = 0; it < iters; ++it) {
-      delta_kernel<T, D><<<dim3(gc.x * DELTA_SPLIT, gc.y), 256, 0, st>>>(x, b, it == 0);
+      const dim3 gd(gc.x * DELTA_SPLIT, gc.y);
+      if (predict && it + 1 == iters) {
+        firsts_kernel<<<gs, 64, 0, st>>>(b);
+        delta_kernel<T, D, true><<<gd, 256, 0, st>>>(x, b, 0, 0);
+      } else {
+        delta_kernel<T, D, false><<<gd, 256, 0, st>>>(x, b, it == 0, it == 0 && predicted);
+      }
       b.round = it;
       hist_kernel<<<gc, 256, 0, st>>>(b);
       find_kernel<<<gs, 256, 0, st>>>(b);
@@ -1280,7 +1435,15 @@ hipError_t run_bisect(const void* x0, const void* x1, int h0, int H, int N, int 
         }
       }
     }
-    partition_kernel<<<gs, 1024, 0, st>>>(b, cur, nxt);
+    if (predict) {
+      partition_kernel<true><<<gs, 1024, 0, st>>>(b, cur, nxt);
+      uint32_t* k = b.keys;  // the children's keys become the next level's
+      b.keys = b.keys_next;
+      b.keys_next = k;
+    } else {
+      partition_kernel<false><<<gs, 1024, 0, st>>>(b, cur, nxt);
+    }
+    predicted = predict;
     int32_t* tmp = cur;
     cur = nxt;
     nxt = tmp;
@@ -1311,6 +1474,12 @@ size_t bisect_scratch(int H, int N, int d, int leaf) {
   a.get<int2>(size_t(H) * P.max_seg);
   a.get<unsigned long long>(size_t(H) * P.max_seg * CAND_CAP);
   a.get<int32_t>(size_t(H) * P.max_seg);
+  a.get<int32_t>(size_t(P.total_seg));  // kids
+  a.get<int4>(size_t(H) * P.max_seg);   // pred
+  a.get<uint32_t>(size_t(H) * N);       // keyL
+  a.get<uint32_t>(size_t(H) * N);       // keyR
+  a.get<uint32_t>(size_t(H) * N);       // keys_next
+  a.get<int32_t>(size_t(H) * P.max_seg);  // pred_ok
   return a.used;
 }
 
@@ -1334,6 +1503,12 @@ hipError_t bisect_run(const void* x0, const void* x1, int h0, int dtype, int H, 
   b.selbin = s.get<int2>(size_t(H) * P.max_seg);
   b.cand = s.get<unsigned long long>(size_t(H) * P.max_seg * CAND_CAP);
   b.ccount = s.get<int32_t>(size_t(H) * P.max_seg);
+  int32_t* kids = s.get<int32_t>(size_t(P.total_seg));
+  b.pred = s.get<int4>(size_t(H) * P.max_seg);
+  b.keyL = s.get<uint32_t>(size_t(H) * N);
+  b.keyR = s.get<uint32_t>(size_t(H) * N);
+  b.keys_next = s.get<uint32_t>(size_t(H) * N);
+  b.pred_ok = s.get<int32_t>(size_t(H) * P.max_seg);
   b.max_seg = P.max_seg;
   b.max_chunk = P.max_chunk;
   b.N = N;
@@ -1344,16 +1519,16 @@ hipError_t bisect_run(const void* x0, const void* x1, int h0, int dtype, int H, 
   zero_i32<<<unsigned((ncnt + 255) / 256), 256, 0, st>>>(b.ccount, ncnt);
   zero_i32<<<unsigned((ncnt * NBIN + 255) / 256), 256, 0, st>>>(b.ghist, ncnt * NBIN);
   init_minmax<<<unsigned((ncnt + 255) / 256), 256, 0, st>>>(b.segmm, ncnt);
-  build_tree_kernel<<<1, 1024, 0, st>>>(P.t, N, segs, chunks);
+  build_tree_kernel<<<1, 1024, 0, st>>>(P.t, N, segs, chunks, kids);
   hipError_t e;
   if (dtype == SA_F32 && d == 64)
-    e = run_bisect<float, 64>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, pa, pb, perm0, perm1, b, st);
+    e = run_bisect<float, 64>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, kids, pa, pb, perm0, perm1, b, st);
   else if (dtype == SA_F32 && d == 128)
-    e = run_bisect<float, 128>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, pa, pb, perm0, perm1, b, st);
+    e = run_bisect<float, 128>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, kids, pa, pb, perm0, perm1, b, st);
   else if (dtype == SA_BF16 && d == 64)
-    e = run_bisect<bf16_t, 64>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, pa, pb, perm0, perm1, b, st);
+    e = run_bisect<bf16_t, 64>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, kids, pa, pb, perm0, perm1, b, st);
   else
-    e = run_bisect<bf16_t, 128>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, pa, pb, perm0, perm1, b, st);
+    e = run_bisect<bf16_t, 128>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, kids, pa, pb, perm0, perm1, b, st);
   if (e != hipSuccess) return e;
   const int C = ceil_div(N, leaf);
   leaf_offsets_kernel<<<dim3(ceil_div(C + 1, 256), H), 256, 0, st>>>(off0, off1, h0, C, N, leaf);

@@ -213,7 +213,15 @@ def test_stage_C_bisect_gmm_exact():
         np.testing.assert_allclose(out.centroids[h].cpu().numpy(), means, rtol=1e-5, atol=1e-5)
 
 
-@pytest.mark.parametrize("w", [WAN_S, replace(WAN_S, d=64, name="wan_small_d64")], ids=lambda w: w.name)
+# Three levels of device-wide top-phase splits (segments above 2560 tokens),
+# so the children's first rounds formed during their parents' last rounds are
+# exercised at two levels: a smooth field and a Gaussian mixture.
+WAN_M = replace(wl.WAN, name="wan_mid", heads=2, frames=10, height=30, width=40)  # N = 12000
+TAB_M = replace(wl.TABULAR, name="tab_mid", heads=2, width=20000 + 77)             # N = 20077, d = 64
+
+
+@pytest.mark.parametrize("w", [WAN_S, replace(WAN_S, d=64, name="wan_small_d64"), WAN_M, TAB_M],
+                         ids=lambda w: w.name)
 def test_stage_C_bisect_smooth(w):
     """Smooth fields have near-tie medians; every split the GPU takes on the
     same token set as the oracle must agree unless the oracle flags the node
