@@ -25,6 +25,10 @@
 //               per-chunk partials, added in chunk order per segment (fixed
 //               order, no float atomics)
 //      part.  : per segment ordered scan -> stable partition of positions
+//      next   : a level's last delta pass also forms its children's
+//               first-round keys under a prediction of their first two
+//               tokens; the partition checks it, and a verified child skips
+//               its first delta pass (results identical either way)
 //  * subtree phase: one workgroup finishes each segment of at most SUB_N
 //    tokens through all remaining levels, with positions, keys and sides in
 //    LDS and rows re-read through the caches (four rows in flight per lane).
