@@ -26,7 +26,7 @@ SOURCES = ["sa_api.cpp", "k_permute.hip", "k_kmeans.hip", "k_bisect.hip", "k_sel
 
 CFLAGS = [
     "-x", "hip", "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",
-    "-fvisibility=hidden", "-Wall", "-Wno-unused-function", "-Wno-unused-variable",
+    "-fvisibility=hidden", "-Wall", "-Wextra",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 

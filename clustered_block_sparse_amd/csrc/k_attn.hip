@@ -17,6 +17,12 @@
 // compensation runs afterwards over "pseudo keys" (one per key cluster) whose
 // logit carries the bias ln|K_j| (-inf where selected or empty).
 //
+// Rows whose ranges all start at multiples of 64 (and end at one or at N)
+// stream whole 64-key blocks by direct buffer-to-LDS loads, with V read from a
+// pre-transposed copy.  Other rows (and SCOPE's key combos) gather their key
+// rows one by one: before each tile one wave lists the key row of each
+// position, and V is transposed while it is staged through registers.
+//
 // bf16 path: 4 waves x 32 query rows.  S^T = K Q^T on 32x32x16 bf16 MFMA so
 // every lane owns one query column and keeps the online-softmax state in
 // registers; P stays in registers and feeds O^T = V^T P^T directly (V is
@@ -220,40 +226,6 @@ __device__ __forceinline__ void map_tile(int maxT, int H, const int32_t* ntiles,
   if (h >= H) return;
   const int nt = ntiles[h], n8 = (nt + 7) / 8, kk = k % t8;
   if (kk < n8 && x * n8 + kk < nt) tix = x * n8 + kk;
-}
-
-// stage one chunk of ranges in LDS: rs[k] = start, rp[k] = prefix length
-__device__ int stage_ranges(const int2* __restrict__ rg, int c0, int nrc, int* rs, int* rp,
-                            int* wsum) {
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, nw = blockDim.x >> 6;
-  int carry = 0;
-  for (int b = 0; b < nrc; b += blockDim.x) {
-    const int k = b + t;
-    int len = 0;
-    if (k < nrc) {
-      const int2 r = rg[c0 + k];
-      rs[k] = r.x;
-      len = r.y - r.x;
-    }
-    int x = len;
-    for (int o = 1; o < 64; o <<= 1) {
-      int y = __shfl_up(x, o, 64);
-      if (lane >= o) x += y;
-    }
-    if (lane == 63) wsum[w] = x;
-    __syncthreads();
-    int pre = carry, tot = 0;
-    for (int j = 0; j < nw; ++j) {
-      if (j < w) pre += wsum[j];
-      tot += wsum[j];
-    }
-    if (k < nrc) rp[k] = pre + x - len;
-    carry += tot;
-    __syncthreads();
-  }
-  if (t == 0) rp[nrc] = carry;
-  __syncthreads();
-  return rp[nrc];
 }
 
 // Stage the next selected key clusters of a row, in cluster order, straight

@@ -1100,7 +1100,7 @@ __device__ void subtree_select(SubShared<D>& S, int A, int n0) {
       const uint64_t bal = __ballot(f);
       const int cnt = __popcll(bal);
       if (run + cnt >= k) {
-        const uint64_t mine = __ballot(f && __popcll(bal & lane_lt()) == k - run - 1);
+        const uint64_t mine = __ballot(f && int(__popcll(bal & lane_lt())) == k - run - 1);
         if (lane == 0) S.thr[a] = make_uint2(K, uint32_t(sg.x + base + __ffsll((unsigned long long)mine) - 1));
         break;
       }

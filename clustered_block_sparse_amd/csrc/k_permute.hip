@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void sort_scatter(const int32_t* __restrict__ 
                                                     int nchunks, const int32_t* __restrict__ cbase) {
   __shared__ int run[256];
   __shared__ int wc[4][256];
-  const int h = blockIdx.y, chunk = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int h = blockIdx.y, chunk = blockIdx.x, t = threadIdx.x, w = t >> 6;
   run[t] = cbase[(size_t(h) * 256 + t) * nchunks + chunk];
   for (int j = 0; j < 4; ++j) wc[j][t] = 0;
   __syncthreads();
