@@ -1015,6 +1015,7 @@ struct SubShared {
   uint8_t side[SUB_N];
   uint8_t sid[SUB_N];     // batch slot of the active segment owning a position (255: none)
   float cen[MAXS][2][D];
+  float wm[MAXS][2][D];   // per round: c2 - c1 and c1 + c2 of every active segment
   float ssum[MAXS][2][D];
   float wp[SUB_THREADS / 64][2][D];
   int4 seg[MAXS];         // start, n, n_left
@@ -1162,6 +1163,15 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
       for (int it = 0; it < iters; ++it) {
         __syncthreads();
         if (t < A) S.swc[t] = 0;
+        // the round's per-segment difference and sum of the two means (the
+        // delta of every row reads them instead of recomputing them)
+        for (int i = t; i < A * D; i += SUB_THREADS) {
+          const int a = i / D, col = i % D;
+          const float c1 = S.cen[a][0][col], c2 = S.cen[a][1][col];
+          S.wm[a][0][col] = c2 - c1;
+          S.wm[a][1][col] = c1 + c2;
+        }
+        __syncthreads();
         // delta over every position of a segment still moving
         {
           constexpr int STEP = NW * G::RPW;
@@ -1182,10 +1192,15 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
               unpack_vec<T, G::EPV>(raw[q], v);
               const int a = sl[q] != 255 ? sl[q] : 0;
               float acc = 0.f;
+              const float4* w4 = reinterpret_cast<const float4*>(&S.wm[a][0][sub * G::EPV]);
+              const float4* m4 = reinterpret_cast<const float4*>(&S.wm[a][1][sub * G::EPV]);
 #pragma unroll
-              for (int e = 0; e < G::EPV; ++e) {
-                const float c1 = S.cen[a][0][sub * G::EPV + e], c2 = S.cen[a][1][sub * G::EPV + e];
-                acc = fmaf(c2 - c1, fmaf(2.f, v[e], -(c1 + c2)), acc);
+              for (int e4 = 0; e4 < G::EPV / 4; ++e4) {
+                const float4 wq = w4[e4], mq = m4[e4];
+                acc = fmaf(wq.x, fmaf(2.f, v[4 * e4], -mq.x), acc);
+                acc = fmaf(wq.y, fmaf(2.f, v[4 * e4 + 1], -mq.y), acc);
+                acc = fmaf(wq.z, fmaf(2.f, v[4 * e4 + 2], -mq.z), acc);
+                acc = fmaf(wq.w, fmaf(2.f, v[4 * e4 + 3], -mq.w), acc);
               }
 #pragma unroll
               for (int o = 1; o < G::LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
