@@ -280,6 +280,13 @@ __device__ BoundK wselect_interp(Eval ev2, int C, unsigned long long target, dou
   return r;
 }
 
+// c ? x : y, field by field: a select between two whole structs becomes a
+// select between their addresses, which puts both in private memory.
+__device__ __forceinline__ BoundK pick_bound(bool c, const BoundK& x, const BoundK& y) {
+  return BoundK{Boundary{c ? x.b.key : y.b.key, c ? x.b.g : y.b.g}, c ? x.keys : y.keys,
+                c ? x.ok : y.ok};
+}
+
 __device__ __forceinline__ bool later(const Boundary& a, const Boundary& b, int C) {
   // is boundary a later in rank order than b (C = past every combo)?
   if (a.g == C) return b.g != C;
@@ -326,7 +333,10 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const dou
     const float* qb = a.qbar + row * d;
     const float* cb = a.kbar + (size_t(h) * 3 * Cs + sl * Cs + c) * d;
     double sdot = 0.0;
-    for (int col = off; col < off + a.dims[sl]; ++col) sdot = fma(double(qb[col]), double(cb[col]), sdot);
+    // (constant indices only: a runtime index into the argument struct would
+    // copy it to private memory in every thread)
+    const int dsl = sl == 0 ? a.dims[0] : (sl == 1 ? a.dims[1] : a.dims[2]);
+    for (int col = off; col < off + dsl; ++col) sdot = fma(double(qb[col]), double(cb[col]), sdot);
     R.T[sl][c] = sdot * a.scale;
   }
   __syncthreads();
@@ -438,7 +448,8 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const dou
     bp = select_mass((unsigned long long)llrint(P * MASS_ONE));
   }
   if (a.floor_units > 0) bf = select_keys((unsigned long long)a.floor_units);
-  const BoundK binit = (bp.b.g < 0) ? bf : (bf.b.g < 0 ? bp : (later(bf.b, bp.b, Cfull) ? bf : bp));
+  const BoundK binit =
+      pick_bound(bp.b.g < 0 || (bf.b.g >= 0 && later(bf.b, bp.b, Cfull)), bf, bp);
   const long long n_init = binit.keys;
   if (online && pass == 0) {
     if (t == 0) {
@@ -454,7 +465,7 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const dou
     kh = int((A + a.N - 1) / a.N);
     if (n_init < kh) {
       const BoundK bk = select_keys((unsigned long long)kh);
-      if (binit.b.g < 0 || later(bk.b, binit.b, Cfull)) bfin_k = bk;
+      bfin_k = pick_bound(binit.b.g < 0 || later(bk.b, binit.b, Cfull), bk, binit);
     }
   }
   const Boundary bfin = bfin_k.b;

@@ -14,6 +14,12 @@
         Markdown table of per-dispatch means of every counter in a
         counter_collection.csv of `rocprofv3 --pmc`, one row per kernel.
 
+    python -m clustered_block_sparse_amd.profiling kernel_traffic --fetch CSV --write CSV \
+            --stats KERNEL_STATS_CSV --copy-bytes B --title T --cmd C
+        Markdown table of every kernel's HBM traffic per dispatch (the two
+        counters, copy-calibrated as below), its average duration from a
+        kernel trace of the same command, and the rate they give.
+
     python -m clustered_block_sparse_amd.profiling traffic --fetch CSV --write CSV \
             --kernel NAME --copy-bytes B --workload W --out JSON [--cmd C]
         HBM bytes per launch of kernel NAME from two counter passes
@@ -163,6 +169,35 @@ def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int) -> dic
             "bytes_per_launch": fk * 1024.0 * f_scale + wk * 1024.0 * w_scale}
 
 
+def kernel_traffic_table(fetch_csv: str, write_csv: str, stats_csv: str, copy_bytes: int, title: str,
+                         cmd: str) -> str:
+    f, w = per_dispatch(fetch_csv, "FETCH_SIZE"), per_dispatch(write_csv, "WRITE_SIZE")
+    fs = copy_bytes / (copy_reading(f) * 1024.0)
+    wsc = copy_bytes / (copy_reading(w) * 1024.0)
+    dur: dict[str, list[float]] = {}
+    for r in csv.DictReader(open(stats_csv)):
+        s = short_name(r["Name"])
+        a = dur.setdefault(s, [0, 0.0])
+        a[0] += int(r["Calls"])
+        a[1] += float(r["TotalDurationNs"])
+    rows = []
+    for k in sorted(set(f) & set(w)):
+        if k.startswith("torch") or "copyBuffer" in k or "fillBuffer" in k or k not in dur:
+            continue
+        rd = sum(f[k]) / len(f[k]) * 1024.0 * fs
+        wr = sum(w[k]) / len(w[k]) * 1024.0 * wsc
+        us = dur[k][1] / dur[k][0] / 1e3
+        rows.append((dur[k][1], f"| {k} | {len(f[k])} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {us:.1f} | "
+                                f"{(rd + wr) / (us * 1e-6) / 1e12:.2f} |"))
+    out = [f"# {title}", "", "Commands (from the repo root on the GPU box):", "", "```", cmd, "```", "",
+           f"Counters scaled by the readings of 1 GiB device copies: FETCH_SIZE x {fs:.3f}, WRITE_SIZE x {wsc:.3f}.",
+           "Rows by total time in the trace.", "",
+           "| kernel | dispatches | read MB / dispatch | written MB / dispatch | avg us (trace) | TB/s |",
+           "|---|---|---|---|---|---|"]
+    out += [r for _, r in sorted(rows, key=lambda x: -x[0])]
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd_name", required=True)
@@ -178,6 +213,13 @@ def main(argv=None):
     c.add_argument("csv")
     c.add_argument("--title", required=True)
     c.add_argument("--cmd", required=True)
+    kt = sub.add_parser("kernel_traffic")
+    kt.add_argument("--fetch", required=True)
+    kt.add_argument("--write", required=True)
+    kt.add_argument("--stats", required=True)
+    kt.add_argument("--copy-bytes", type=int, required=True)
+    kt.add_argument("--title", required=True)
+    kt.add_argument("--cmd", required=True)
     r = sub.add_parser("traffic")
     r.add_argument("--fetch", required=True)
     r.add_argument("--write", required=True)
@@ -193,6 +235,8 @@ def main(argv=None):
         sys.stdout.write(bench_table(a.jsonl, a.title, a.cmd))
     elif a.cmd_name == "counters":
         sys.stdout.write(counters_table(a.csv, a.title, a.cmd))
+    elif a.cmd_name == "kernel_traffic":
+        sys.stdout.write(kernel_traffic_table(a.fetch, a.write, a.stats, a.copy_bytes, a.title, a.cmd))
     else:
         res = traffic(a.fetch, a.write, a.kernel, a.copy_bytes)
         res.update({"workload": a.workload, "source_sha256": source_hash(), "command": a.cmd})
