@@ -47,6 +47,7 @@ constexpr int SUB_T = 1024;
 constexpr double MASS_ONE = 4503599627370496.0;  // 2^52
 
 constexpr int CAND = 1024;  // combos of the selected interpolated bin kept in LDS
+constexpr int LOGT = 1024;  // ln(size) of combos smaller than this from an LDS table
 
 struct SubRow {
   double T[3][32];
@@ -55,7 +56,8 @@ struct SubRow {
   unsigned long long wsum[16];
   unsigned long long red[2][16];
   double dred[16];
-  uint32_t words[1024];
+  double lt[LOGT];               // lt[s] = ln(s), lt[0] = -inf
+  uint32_t words[1024];          // the row's mask, built by the selections
   unsigned long long ck[CAND];   // candidates: order key, weight, combo, keys
   unsigned long long cw[CAND];
   int cg[CAND];
@@ -106,6 +108,38 @@ __device__ V bscan(V v, V* wsum, V& total) {
   total = tot;
   __syncthreads();
   return pre + x - v;
+}
+
+// Every combo of the row, this thread's share, with sizes loaded four combos
+// ahead of their use: f(g, size), size 0 for an empty combo.
+constexpr int SUB_U = 4;
+template <typename F>
+__device__ __forceinline__ void for_combos(const int32_t* __restrict__ ksz, int C, F f) {
+  for (int g = threadIdx.x; g < C; g += SUB_U * SUB_T) {
+    int sz[SUB_U];
+#pragma unroll
+    for (int u = 0; u < SUB_U; ++u) sz[u] = g + u * SUB_T < C ? ksz[g + u * SUB_T] : 0;
+#pragma unroll
+    for (int u = 0; u < SUB_U; ++u)
+      if (g + u * SUB_T < C) f(g + u * SUB_T, sz[u]);
+  }
+}
+// The same with the wave kept together (for ballots): f(g0, size) for the
+// lane's combo g0 + lane, size 0 past the end; g0 is the same in every lane.
+template <typename F>
+__device__ __forceinline__ void for_combo_waves(const int32_t* __restrict__ ksz, int C, F f) {
+  const int lane = threadIdx.x & 63;
+  for (int g0 = threadIdx.x - lane; g0 < C; g0 += SUB_U * SUB_T) {
+    int sz[SUB_U];
+#pragma unroll
+    for (int u = 0; u < SUB_U; ++u) {
+      const int g = g0 + u * SUB_T + lane;
+      sz[u] = g < C ? ksz[g] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < SUB_U; ++u)
+      if (g0 + u * SUB_T < C) f(g0 + u * SUB_T, sz[u]);
+  }
 }
 
 // First combo (in rank order) at which the cumulative weight reaches `target`
@@ -192,15 +226,21 @@ struct BoundK {
   bool ok;
 };
 
+// With `mark`, every combo at or before the boundary is also ORed into
+// R.words, and `marked` says so (not when the target exceeds the total or the
+// bin overflows): the bins before the selected one from a ballot in pass 2,
+// the selected bin's combos from the candidates once the boundary is known.
 template <int WK, typename Eval>
-__device__ BoundK wselect_interp(Eval ev2, int C, unsigned long long target, double mx, double mn,
-                                 SubRow& R) {
-  const int t = threadIdx.x;
+__device__ BoundK wselect_interp(Eval evs, const int32_t* __restrict__ ksz, int C,
+                                 unsigned long long target, double mx, double mn, SubRow& R, bool mark,
+                                 bool& marked) {
+  const int t = threadIdx.x, lane = t & 63;
+  marked = false;
   const double span = mx - mn;
   const double inv = span > 1e-280 ? 2048.0 / span : 0.0;
   auto bin_of = [&](double l) -> int {
     const int b = int((mx - l) * inv);
-    return b < 2047 ? b : 2047;
+    return b < 0 ? 0 : (b < 2047 ? b : 2047);
   };
   for (int b = t; b < 2048; b += SUB_T) {
     R.hw[b] = 0ull;
@@ -208,14 +248,14 @@ __device__ BoundK wselect_interp(Eval ev2, int C, unsigned long long target, dou
   }
   if (t == 0) R.ncand = 0;
   __syncthreads();
-  for (int g = t; g < C; g += SUB_T) {
+  for_combos(ksz, C, [&](int g, int sz) {
     double l;
     unsigned long long k, mass, keys;
-    if (!ev2(g, l, k, mass, keys)) continue;
+    if (!evs(g, sz, l, k, mass, keys)) return;
     const int b = bin_of(l);
     atomicAdd(&R.hw[b], WK == 0 ? mass : keys);
     if (WK == 0) atomicAdd(&R.hk[b], keys);
-  }
+  });
   __syncthreads();
   const unsigned long long w0 = R.hw[2 * t], w1 = R.hw[2 * t + 1];
   const unsigned long long k0 = WK == 0 ? R.hk[2 * t] : w0, k1 = WK == 0 ? R.hk[2 * t + 1] : w1;
@@ -239,10 +279,19 @@ __device__ BoundK wselect_interp(Eval ev2, int C, unsigned long long target, dou
   if (sb < 0) return BoundK{Boundary{0ull, C}, (long long)tk, true};  // target beyond the total
   const unsigned long long rem = rem0 - R.sel_w;
   const unsigned long long kbefore = R.sel_k;
-  for (int g = t; g < C; g += SUB_T) {
+  // a wave's lanes take 64 consecutive combos: two whole mask words
+  for_combo_waves(ksz, C, [&](int g0, int sz) {
+    const int g = g0 + lane;
     double l;
-    unsigned long long k, mass, keys;
-    if (!ev2(g, l, k, mass, keys) || bin_of(l) != sb) continue;
+    unsigned long long k = 0, mass = 0, keys = 0;
+    const bool v = sz > 0 && evs(g, sz, l, k, mass, keys);
+    const int b = v ? bin_of(l) : 2048;
+    if (mark) {
+      const unsigned long long bits = __ballot(b < sb);
+      if (lane == 0) R.words[g0 >> 5] |= uint32_t(bits);
+      if (lane == 32 && g < C) R.words[(g0 >> 5) + 1] |= uint32_t(bits >> 32);
+    }
+    if (b != sb) return;
     const int slot = atomicAdd(&R.ncand, 1);
     if (slot < CAND) {
       R.ck[slot] = k;
@@ -250,7 +299,7 @@ __device__ BoundK wselect_interp(Eval ev2, int C, unsigned long long target, dou
       R.cw[slot] = WK == 0 ? mass : keys;
       R.ckeys[slot] = uint32_t(keys);
     }
-  }
+  });
   if (t == 0) R.tie_g = -1;
   __syncthreads();
   const int m = R.ncand;
@@ -276,6 +325,10 @@ __device__ BoundK wselect_interp(Eval ev2, int C, unsigned long long target, dou
   __syncthreads();
   // the bin's weight reaches rem, so exactly one candidate matched
   const BoundK r{Boundary{R.tie_key, R.tie_g}, R.tie_keys, true};
+  if (mark) {
+    if (t < m && before_or_at(R.ck[t], R.cg[t], r.b)) atomicOr(&R.words[R.cg[t] >> 5], 1u << (R.cg[t] & 31));
+    marked = true;
+  }
   __syncthreads();
   return r;
 }
@@ -294,17 +347,23 @@ __device__ __forceinline__ bool later(const Boundary& a, const Boundary& b, int 
   return a.key > b.key || (a.key == b.key && a.g > b.g);
 }
 
-__global__ void logsize_kernel(const int32_t* __restrict__ k_off, int C, double* __restrict__ lg) {
+__global__ void logsize_kernel(const int32_t* __restrict__ k_off, int C, double* __restrict__ lg,
+                               int32_t* __restrict__ ksz) {
   const int h = blockIdx.y;
   const int g = blockIdx.x * 256 + threadIdx.x;
   if (g >= C) return;
   const int sz = k_off[size_t(h) * (C + 1) + g + 1] - k_off[size_t(h) * (C + 1) + g];
   lg[size_t(h) * C + g] = sz > 0 ? log(double(sz)) : -__builtin_huge_val();
+  ksz[size_t(h) * C + g] = sz;
 }
 
+// The online mode runs twice: pass 0 finds every row's initial boundary and
+// adds its keys to the head's total, keeping the row's logit range and
+// boundary in `state` (5 words per row); pass 1 starts from that state.
 __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const double* __restrict__ lgs,
+                                                         const int32_t* __restrict__ kszs,
                                                          unsigned long long* __restrict__ acc,
-                                                         int pass) {
+                                                         long long* __restrict__ state, int pass) {
   __shared__ SubRow R;
   const int i = blockIdx.x, h = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int Cq = a.Cq, C = a.Ck, Cs = a.Cs, d = a.d;
@@ -326,64 +385,110 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const dou
     }
     return;
   }
-  // lookup tables
-  if (t < 3 * Cs) {
-    const int sl = t / Cs, c = t % Cs;
-    const int off = sl == 0 ? 0 : (sl == 1 ? a.dims[0] : a.dims[0] + a.dims[1]);
-    const float* qb = a.qbar + row * d;
-    const float* cb = a.kbar + (size_t(h) * 3 * Cs + sl * Cs + c) * d;
-    double sdot = 0.0;
+  // lookup tables: T[slice][cluster] one wave-wide dot at a time (lanes over
+  // the slice's columns, then a butterfly sum; lane 0's result is kept)
+  for (int pr = w; pr < 3 * Cs; pr += SUB_T / 64) {
+    const int sl = pr / Cs, c = pr - sl * Cs;
     // (constant indices only: a runtime index into the argument struct would
     // copy it to private memory in every thread)
+    const int off = sl == 0 ? 0 : (sl == 1 ? a.dims[0] : a.dims[0] + a.dims[1]);
     const int dsl = sl == 0 ? a.dims[0] : (sl == 1 ? a.dims[1] : a.dims[2]);
-    for (int col = off; col < off + dsl; ++col) sdot = fma(double(qb[col]), double(cb[col]), sdot);
-    R.T[sl][c] = sdot * a.scale;
+    const float* qb = a.qbar + row * d + off;
+    const float* cb = a.kbar + (size_t(h) * 3 * Cs + pr) * d + off;
+    double sdot = 0.0;
+    for (int col = lane; col < dsl; col += 64) sdot = fma(double(qb[col]), double(cb[col]), sdot);
+    for (int o = 32; o > 0; o >>= 1) sdot += __shfl_xor(sdot, o, 64);
+    if (lane == 0) R.T[sl][c] = sdot * a.scale;
   }
+  // the same function of the same size as the per-combo table in global memory
+  for (int z = t; z < LOGT; z += SUB_T) R.lt[z] = z > 0 ? log(double(z)) : -__builtin_huge_val();
+  for (int x = t; x < W; x += SUB_T) R.words[x] = 0u;
   __syncthreads();
-  const int32_t* ko = a.k_off + size_t(h) * (C + 1);
+  const int32_t* ksz = kszs + size_t(h) * C;  // keys per combo
   const double* lh = lgs + size_t(h) * C;
   const int Cs2 = Cs * Cs;
-  auto logit = [&](int g, double& l) -> bool {
-    const double ls = lh[g];
-    if (ls == -__builtin_huge_val()) return false;
-    l = (R.T[0][g / Cs2] + R.T[1][(g / Cs) % Cs]) + R.T[2][g % Cs];
-    if (a.weighted) l += ls;
+  // g / Cs and g / Cs^2 as a multiply by ceil(2^31 / divisor) and a shift:
+  // exact for every g < 2^15 and divisor <= 1024 (combos < 32^3)
+  const uint32_t m1 = uint32_t(((1ull << 31) + Cs - 1) / Cs);
+  const uint32_t m2 = uint32_t(((1ull << 31) + Cs2 - 1) / Cs2);
+  // logit of combo g given its size sz; false for an empty combo
+  auto logit_sz = [&](int g, int sz, double& l) -> bool {
+    if (sz <= 0) return false;
+    const int q1 = int((uint64_t(uint32_t(g)) * m1) >> 31);
+    const int c0 = int((uint64_t(uint32_t(g)) * m2) >> 31);
+    l = (R.T[0][c0] + R.T[1][q1 - c0 * Cs]) + R.T[2][g - q1 * Cs];
+    if (a.weighted) l += sz < LOGT ? R.lt[sz] : lh[g];
     return true;
   };
+  auto logit = [&](int g, double& l, int& sz) -> bool {
+    sz = ksz[g];
+    return logit_sz(g, sz, l);
+  };
+  const bool resume = online && pass == 1;
+  long long* rs = state + row * 5;
+  const double P = a.top_p;
+  // no mass target (or none left to find): no normaliser, and the logit range
+  // only places the interpolation bins, so bounds serve
+  const bool need_mass = P > 0.0 && P < 1.0 && !resume;
   // max logit, normaliser, order-key range
   double mx = -__builtin_huge_val(), mn = __builtin_huge_val();
-  for (int g = t; g < C; g += SUB_T) {
-    double l;
-    if (logit(g, l)) {
-      mx = fmax(mx, l);
-      mn = fmin(mn, l);
+  if (resume) {
+    mx = __longlong_as_double(rs[0]);
+    mn = __longlong_as_double(rs[1]);
+  } else if (need_mass) {
+    for_combos(ksz, C, [&](int g, int sz) {
+      double l;
+      if (logit_sz(g, sz, l)) {
+        mx = fmax(mx, l);
+        mn = fmin(mn, l);
+      }
+    });
+    for (int o = 32; o > 0; o >>= 1) {
+      mx = fmax(mx, __shfl_xor(mx, o, 64));
+      mn = fmin(mn, __shfl_xor(mn, o, 64));
+    }
+    if (lane == 0) {
+      R.red[0][w] = __double_as_longlong(mx);
+      R.red[1][w] = __double_as_longlong(mn);
+    }
+    __syncthreads();
+    mx = __longlong_as_double(R.red[0][0]);
+    mn = __longlong_as_double(R.red[1][0]);
+    for (int j = 1; j < SUB_T / 64; ++j) {
+      mx = fmax(mx, __longlong_as_double(R.red[0][j]));
+      mn = fmin(mn, __longlong_as_double(R.red[1][j]));
+    }
+    __syncthreads();
+  } else {
+    // Bounds on every logit: the sums of the slices' extremes, added in the
+    // logits' own order (rounding is monotone), with ln(size) in [0, ln N]
+    // given a margin far above the error of ln.  Each half-wave reduces
+    // clusters lane & 31 < Cs.
+    const int c = lane & 31;
+    double hi[3], lo[3];
+#pragma unroll
+    for (int sl = 0; sl < 3; ++sl) {
+      hi[sl] = c < Cs ? R.T[sl][c] : -__builtin_huge_val();
+      lo[sl] = c < Cs ? R.T[sl][c] : __builtin_huge_val();
+      for (int o = 16; o > 0; o >>= 1) {
+        hi[sl] = fmax(hi[sl], __shfl_xor(hi[sl], o, 64));
+        lo[sl] = fmin(lo[sl], __shfl_xor(lo[sl], o, 64));
+      }
+    }
+    mx = (hi[0] + hi[1]) + hi[2];
+    mn = (lo[0] + lo[1]) + lo[2];
+    if (a.weighted) {
+      mx += log(double(a.N)) + 1e-9;
+      mn -= 1e-9;
     }
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    mx = fmax(mx, __shfl_xor(mx, o, 64));
-    mn = fmin(mn, __shfl_xor(mn, o, 64));
-  }
-  if (lane == 0) {
-    R.red[0][w] = __double_as_longlong(mx);
-    R.red[1][w] = __double_as_longlong(mn);
-  }
-  __syncthreads();
-  mx = __longlong_as_double(R.red[0][0]);
-  mn = __longlong_as_double(R.red[1][0]);
-  for (int j = 1; j < SUB_T / 64; ++j) {
-    mx = fmax(mx, __longlong_as_double(R.red[0][j]));
-    mn = fmin(mn, __longlong_as_double(R.red[1][j]));
-  }
-  __syncthreads();
-  const double P = a.top_p;
-  const bool need_mass = P > 0.0 && P < 1.0;  // otherwise no mass target: no normaliser
   double Z = 1.0;
   if (need_mass) {
     double zs = 0.0;
-    for (int g = t; g < C; g += SUB_T) {
+    for_combos(ksz, C, [&](int g, int sz) {
       double l;
-      if (logit(g, l)) zs += exp(l - mx);
-    }
+      if (logit_sz(g, sz, l)) zs += exp(l - mx);
+    });
     for (int o = 32; o > 0; o >>= 1) zs += __shfl_xor(zs, o, 64);
     if (lane == 0) R.dred[w] = zs;
     __syncthreads();
@@ -392,21 +497,17 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const dou
     __syncthreads();
   }
   const unsigned long long kmin = order_key(mx), kmax = order_key(mn);
-  auto ev = [&](int g, unsigned long long& k, unsigned long long& mass, unsigned long long& keys) -> bool {
-    double l;
-    if (!logit(g, l)) return false;
+  auto evs = [&](int g, int sz, double& l, unsigned long long& k, unsigned long long& mass,
+                 unsigned long long& keys) -> bool {
+    if (!logit_sz(g, sz, l)) return false;
     k = order_key(l);
     mass = (unsigned long long)llrint(exp(l - mx) / Z * MASS_ONE);
-    keys = (unsigned long long)(ko[g + 1] - ko[g]);
+    keys = (unsigned long long)sz;
     return true;
   };
-  auto ev2 = [&](int g, double& l, unsigned long long& k, unsigned long long& mass,
-                 unsigned long long& keys) -> bool {
-    if (!logit(g, l)) return false;
-    k = order_key(l);
-    mass = (unsigned long long)llrint(exp(l - mx) / Z * MASS_ONE);
-    keys = (unsigned long long)(ko[g + 1] - ko[g]);
-    return true;
+  auto ev = [&](int g, unsigned long long& k, unsigned long long& mass, unsigned long long& keys) -> bool {
+    double l;
+    return evs(g, ksz[g], l, k, mass, keys);
   };
   const int Cfull = C;
   const Boundary b0{0ull, -1};  // before every combo
@@ -417,16 +518,24 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const dou
     unsigned long long sk = 0;
     for (int g = t; g < C; g += SUB_T) {
       double l;
-      if (!logit(g, l)) continue;
-      if (b.g == Cfull || before_or_at(order_key(l), g, b)) sk += (unsigned long long)(ko[g + 1] - ko[g]);
+      int sz;
+      if (!logit(g, l, sz)) continue;
+      if (b.g == Cfull || before_or_at(order_key(l), g, b)) sk += (unsigned long long)sz;
     }
     unsigned long long tot;
     bscan<unsigned long long>(sk, R.wsum, tot);
     return (long long)tot;
   };
   // boundary of a cumulative target and the keys through it
+  // Without the online pass the row's mask is the union of what the
+  // selections mark (each marks a prefix in rank order; the mask is the
+  // longest); when one of them cannot, a last pass builds it instead.
+  const bool mark = !online;
+  bool words_ok = mark;
   auto select_mass = [&](unsigned long long target) -> BoundK {
-    BoundK r = wselect_interp<0>(ev2, C, target, mx, mn, R);
+    bool marked;
+    BoundK r = wselect_interp<0>(evs, ksz, C, target, mx, mn, R, mark, marked);
+    words_ok &= marked;
     if (!r.ok) {
       r.b = wselect<0>(ev, C, target, kmin, kmax, R);
       r.keys = keys_through(r.b);
@@ -434,27 +543,42 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const dou
     return r;
   };
   auto select_keys = [&](unsigned long long target) -> BoundK {
-    BoundK r = wselect_interp<1>(ev2, C, target, mx, mn, R);
+    bool marked;
+    BoundK r = wselect_interp<1>(evs, ksz, C, target, mx, mn, R, mark, marked);
+    words_ok &= marked;
     if (!r.ok) {
       r.b = wselect<1>(ev, C, target, kmin, kmax, R);
       r.keys = keys_through(r.b);
     }
     return r;
   };
-  BoundK bp{b0, 0, true}, bf{b0, 0, true};
-  if (P >= 1.0) {
-    bp = BoundK{Boundary{0ull, Cfull}, keys_through(Boundary{0ull, Cfull}), true};
-  } else if (P > 0.0) {
-    bp = select_mass((unsigned long long)llrint(P * MASS_ONE));
+  BoundK binit{b0, 0, true};
+  if (resume) {
+    binit = BoundK{Boundary{(unsigned long long)rs[2], int(rs[3])}, rs[4], true};
+  } else {
+    BoundK bp{b0, 0, true}, bf{b0, 0, true};
+    if (P >= 1.0) {
+      bp = BoundK{Boundary{0ull, Cfull}, keys_through(Boundary{0ull, Cfull}), true};
+      words_ok = false;
+    } else if (P > 0.0) {
+      bp = select_mass((unsigned long long)llrint(P * MASS_ONE));
+    }
+    // Keys grow along rank order, so when the Top-p boundary already holds
+    // the floor's keys the floor's boundary is at or before it.
+    if (a.floor_units > 0 && (bp.b.g < 0 || bp.keys < a.floor_units))
+      bf = select_keys((unsigned long long)a.floor_units);
+    binit = pick_bound(bp.b.g < 0 || (bf.b.g >= 0 && later(bf.b, bp.b, Cfull)), bf, bp);
   }
-  if (a.floor_units > 0) bf = select_keys((unsigned long long)a.floor_units);
-  const BoundK binit =
-      pick_bound(bp.b.g < 0 || (bf.b.g >= 0 && later(bf.b, bp.b, Cfull)), bf, bp);
   const long long n_init = binit.keys;
   if (online && pass == 0) {
     if (t == 0) {
       atomicAdd(&acc[h], (unsigned long long)((long long)qsize * n_init));
       if (a.init_counts) a.init_counts[row] = int(n_init);
+      rs[0] = __double_as_longlong(mx);
+      rs[1] = __double_as_longlong(mn);
+      rs[2] = (long long)binit.b.key;
+      rs[3] = binit.b.g;
+      rs[4] = n_init;
     }
     return;
   }
@@ -470,17 +594,23 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const dou
   }
   const Boundary bfin = bfin_k.b;
   const long long n_fin = bfin_k.keys;
-  for (int x = t; x < W; x += SUB_T) R.words[x] = 0u;
-  __syncthreads();
-  if (bfin.g >= 0) {
-    for (int g = t; g < C; g += SUB_T) {
-      unsigned long long k, m2, ky;
-      if (!ev(g, k, m2, ky)) continue;
-      if (bfin.g == Cfull || before_or_at(k, g, bfin)) atomicOr(&R.words[g >> 5], 1u << (g & 31));
-    }
+  if (words_ok) {
+    for (int x = t; x < W; x += SUB_T) a.mask[row * W + x] = R.words[x];
   }
-  __syncthreads();
-  for (int x = t; x < W; x += SUB_T) a.mask[row * W + x] = R.words[x];
+  // A wave's 64 lanes hold 64 consecutive combos (two whole mask words) at
+  // every step, so the words are written from a ballot.
+  if (!words_ok) {
+    for_combo_waves(ksz, C, [&](int g0, int sz) {
+      const int g = g0 + lane;
+      double l;
+      unsigned long long k = 0, m2, ky;
+      const bool in = bfin.g >= 0 && sz > 0 && evs(g, sz, l, k, m2, ky) &&
+                      (bfin.g == Cfull || before_or_at(k, g, bfin));
+      const unsigned long long bits = __ballot(in);
+      if (lane == 0) a.mask[row * W + (g0 >> 5)] = uint32_t(bits);
+      if (lane == 32 && g < C) a.mask[row * W + (g0 >> 5) + 1] = uint32_t(bits >> 32);
+    });
+  }
   if (t == 0) {
     a.counts[row] = int(n_fin);
     if (a.init_counts) a.init_counts[row] = int(n_init);
@@ -746,8 +876,13 @@ __global__ __launch_bounds__(256) void select_wave(SelectArgs a, const double* _
 size_t select_scratch(int H, int Cq, int Ck, int subspace) {
   Arena a{nullptr, 0, 0};
   a.get<unsigned long long>(size_t(H));
-  if (subspace) a.get<double>(size_t(H) * Ck);
-  else a.get<double>(size_t(H) * Cq * Ck);
+  if (subspace) {
+    a.get<double>(size_t(H) * Ck);
+    a.get<int32_t>(size_t(H) * Ck);
+    a.get<long long>(size_t(H) * Cq * 5);
+  } else {
+    a.get<double>(size_t(H) * Cq * Ck);
+  }
   return a.used;
 }
 
@@ -755,15 +890,17 @@ hipError_t select_run(const SelectArgs& a, Arena& s, hipStream_t st) {
   unsigned long long* acc = s.get<unsigned long long>(size_t(a.H));
   dim3 g(a.Cq, a.H);
   if (a.subspace) {
-    if (a.Cs > 32) return hipErrorInvalidValue;
+    if (a.Cs > 32 || a.Ck != a.Cs * a.Cs * a.Cs) return hipErrorInvalidValue;
     double* lgs = s.get<double>(size_t(a.H) * a.Ck);
-    logsize_kernel<<<dim3(ceil_div(a.Ck, 256), a.H), 256, 0, st>>>(a.k_off, a.Ck, lgs);
+    int32_t* ksz = s.get<int32_t>(size_t(a.H) * a.Ck);
+    long long* rstate = s.get<long long>(size_t(a.H) * a.Cq * 5);
+    logsize_kernel<<<dim3(ceil_div(a.Ck, 256), a.H), 256, 0, st>>>(a.k_off, a.Ck, lgs, ksz);
     if (a.online) {
       zero_u64<<<ceil_div(a.H, 256), 256, 0, st>>>(acc, a.H);
-      select_subspace<<<g, SUB_T, 0, st>>>(a, lgs, acc, 0);
-      select_subspace<<<g, SUB_T, 0, st>>>(a, lgs, acc, 1);
+      select_subspace<<<g, SUB_T, 0, st>>>(a, lgs, ksz, acc, rstate, 0);
+      select_subspace<<<g, SUB_T, 0, st>>>(a, lgs, ksz, acc, rstate, 1);
     } else {
-      select_subspace<<<g, SUB_T, 0, st>>>(a, lgs, acc, 0);
+      select_subspace<<<g, SUB_T, 0, st>>>(a, lgs, ksz, acc, rstate, 0);
     }
     return hipGetLastError();
   }
