@@ -58,6 +58,7 @@ struct SubRow {
   double dred[16];
   double lt[LOGT];               // lt[s] = ln(s), lt[0] = -inf
   uint32_t words[1024];          // the row's mask, built by the selections
+  uint16_t bin[32768];           // each combo's interpolated bin (0xffff: empty)
   unsigned long long ck[CAND];   // candidates: order key, weight, combo, keys
   unsigned long long cw[CAND];
   int cg[CAND];
@@ -251,8 +252,12 @@ __device__ BoundK wselect_interp(Eval evs, const int32_t* __restrict__ ksz, int 
   for_combos(ksz, C, [&](int g, int sz) {
     double l;
     unsigned long long k, mass, keys;
-    if (!evs(g, sz, l, k, mass, keys)) return;
+    if (!evs(g, sz, l, k, mass, keys)) {
+      R.bin[g] = 0xffff;
+      return;
+    }
     const int b = bin_of(l);
+    R.bin[g] = uint16_t(b);
     atomicAdd(&R.hw[b], WK == 0 ? mass : keys);
     if (WK == 0) atomicAdd(&R.hk[b], keys);
   });
@@ -279,19 +284,20 @@ __device__ BoundK wselect_interp(Eval evs, const int32_t* __restrict__ ksz, int 
   if (sb < 0) return BoundK{Boundary{0ull, C}, (long long)tk, true};  // target beyond the total
   const unsigned long long rem = rem0 - R.sel_w;
   const unsigned long long kbefore = R.sel_k;
-  // a wave's lanes take 64 consecutive combos: two whole mask words
-  for_combo_waves(ksz, C, [&](int g0, int sz) {
+  // Only the selected bin's combos are evaluated again.  A wave's lanes take
+  // 64 consecutive combos: two whole mask words.
+  for (int g0 = t - lane; g0 < C; g0 += SUB_T) {
     const int g = g0 + lane;
-    double l;
-    unsigned long long k = 0, mass = 0, keys = 0;
-    const bool v = sz > 0 && evs(g, sz, l, k, mass, keys);
-    const int b = v ? bin_of(l) : 2048;
+    const int b = g < C ? int(R.bin[g]) : 0xffff;
     if (mark) {
       const unsigned long long bits = __ballot(b < sb);
       if (lane == 0) R.words[g0 >> 5] |= uint32_t(bits);
       if (lane == 32 && g < C) R.words[(g0 >> 5) + 1] |= uint32_t(bits >> 32);
     }
-    if (b != sb) return;
+    if (b != sb) continue;
+    double l;
+    unsigned long long k, mass, keys;
+    evs(g, ksz[g], l, k, mass, keys);
     const int slot = atomicAdd(&R.ncand, 1);
     if (slot < CAND) {
       R.ck[slot] = k;
@@ -299,7 +305,7 @@ __device__ BoundK wselect_interp(Eval evs, const int32_t* __restrict__ ksz, int 
       R.cw[slot] = WK == 0 ? mass : keys;
       R.ckeys[slot] = uint32_t(keys);
     }
-  });
+  }
   if (t == 0) R.tie_g = -1;
   __syncthreads();
   const int m = R.ncand;
