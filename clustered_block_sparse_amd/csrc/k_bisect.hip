@@ -632,7 +632,10 @@ __global__ __launch_bounds__(256) void delta_kernel(Src2<T> x, TopBufs b, int fi
 // that spread each segment over its chunks:
 //   hist: per-chunk histograms of NBIN bins interpolated between the
 //         segment's min / max key (folded in by the delta pass), added into
-//         the segment's histogram;
+//         the segment's histogram (linear in the keys' float values: the
+//         keys' own bits are close to logarithmic in |delta|, and a round
+//         whose deltas take both signs would put a large share of the tokens
+//         into the median's bin);
 //   find: the bin holding rank n_left and the rank inside it;
 //   cand: that bin's keys with their positions, as distinct 64-bit values;
 //   pick: the exact rank among them (up to 1024: each thread counts the
@@ -641,9 +644,21 @@ __global__ __launch_bounds__(256) void delta_kernel(Src2<T> x, TopBufs b, int fi
 //         segment's keys.
 // Only integer atomics are used; the selected (key, position) is unique, so
 // the result does not depend on their order.
-__device__ __forceinline__ int bin_of(uint32_t v, uint2 mm) {
-  const unsigned long long range = (unsigned long long)(mm.y - mm.x) + 1ull;
-  return int(((unsigned long long)(v - mm.x) * NBIN) / range);
+__device__ __forceinline__ float key_value(uint32_t k) {  // inverse of sortable()
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+// Bins of a segment's round, monotone in the key: (value - min) scaled to
+// [0, NBIN) in fp64 (each step rounds monotonically), clamped.
+struct BinMap {
+  double lo, scale;
+};
+__device__ __forceinline__ BinMap bin_map(uint2 mm) {
+  const double lo = key_value(mm.x), hi = key_value(mm.y);
+  return BinMap{lo, hi > lo ? double(NBIN) / (hi - lo) : 0.0};
+}
+__device__ __forceinline__ int bin_of(uint32_t v, const BinMap& bm) {
+  const int b = int((double(key_value(v)) - bm.lo) * bm.scale);
+  return b < 0 ? 0 : (b < NBIN ? b : NBIN - 1);
 }
 
 __global__ __launch_bounds__(256) void hist_kernel(TopBufs b) {
@@ -656,7 +671,8 @@ __global__ __launch_bounds__(256) void hist_kernel(TopBufs b) {
   for (int i = t; i < NBIN; i += 256) hist[i] = 0;
   __syncthreads();
   const uint32_t* u = b.keys + size_t(h) * b.N + ch.y;
-  for (int i = t; i < ch.z; i += 256) atomicAdd(&hist[bin_of(u[i], mm)], 1);
+  const BinMap bm = bin_map(mm);
+  for (int i = t; i < ch.z; i += 256) atomicAdd(&hist[bin_of(u[i], bm)], 1);
   __syncthreads();
   int* g = b.ghist + si * NBIN;
   for (int i = t; i < NBIN; i += 256)
@@ -702,10 +718,11 @@ __global__ __launch_bounds__(256) void cand_kernel(TopBufs b) {
   const uint2 mm = b.segmm[si];
   const uint32_t* u = b.keys + size_t(h) * b.N + ch.y;
   unsigned long long* cd = b.cand + si * CAND_CAP;
+  const BinMap bm = bin_map(mm);
   for (int i0 = 0; i0 < ch.z; i0 += 256) {
     const int i = i0 + t;
     const uint32_t v = i < ch.z ? u[i] : 0u;
-    const bool f = i < ch.z && bin_of(v, mm) == sb.x;
+    const bool f = i < ch.z && bin_of(v, bm) == sb.x;
     const uint64_t bal = __ballot(f);
     if (!bal) continue;
     const int lead = __ffsll((unsigned long long)bal) - 1;
