@@ -18,16 +18,16 @@
 // logit carries the bias ln|K_j| (-inf where selected or empty).
 //
 // Rows whose ranges all start at multiples of 64 (and end at one or at N)
-// stream whole 64-key blocks by direct buffer-to-LDS loads, with V read from a
-// pre-transposed copy.  Other rows (and SCOPE's key combos) gather their key
-// rows one by one: before each tile one wave lists the key row of each
-// position, and V is transposed while it is staged through registers.
+// stream whole 64-key blocks of K and V rows by direct buffer-to-LDS loads.
+// Other rows (and SCOPE's key combos) gather their key rows one by one:
+// before each tile one wave lists the key row of each position, and the K and
+// V rows are staged through registers.
 //
 // bf16 path: 4 waves x 32 query rows.  S^T = K Q^T on 32x32x16 bf16 MFMA so
 // every lane owns one query column and keeps the online-softmax state in
-// registers; P stays in registers and feeds O^T = V^T P^T directly (V is
-// stored transposed in LDS).  Rescaling is lazy (only when the running max
-// grows by more than 2^8).  kbar enters the compensation logits as a bf16
+// registers; P stays in registers and feeds O^T = V^T P^T directly, whose V^T
+// operand comes from row-major V tiles by the LDS transpose read.  Rescaling
+// is lazy (only when the running max grows by more than 2^8).  kbar enters the compensation logits as a bf16
 // hi + lo pair so those logits are fp32-accurate.
 // fp32 path: one thread per query row, fp32 FMA (parity-grade, small inputs).
 
@@ -47,7 +47,6 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int KT = 64;      // keys per tile
 constexpr int HK = 32;      // keys per half tile (one 32x32 MFMA block)
-constexpr int HG = HK / 8;  // 16-byte chunks of a row of a V^T half tile
 constexpr int TQ = 128;     // query rows per workgroup (upper bound)
 constexpr int RCH = 512;    // ranges staged in LDS at a time
 constexpr int ALIGNED_MAX_CK = 4096;  // key clusters up to which rows get precomputed ranges
@@ -61,14 +60,13 @@ struct Prep {
   int2* ranges;       // [H][Cq][Rmax] {start, end}
   int32_t* rcount;    // [H][Cq]
   int32_t* raligned;  // [H][Cq] 1 if every range starts at a multiple of 64 and ends at one or at N
-  bf16_t* vt;         // [H][NB][D][64] V^T per 64-key block (bf16 path)
   bf16_t* kbh;        // [H][Ckp][D]  kbar, bf16 high part
   bf16_t* kbl;        // [H][Ckp][D]  kbar - high, bf16
-  bf16_t* vbt;        // [H][Ckp/64][D][64] vbar^T per 64-cluster block
+  bf16_t* vbr;        // [H][Ckp][D]  vbar, bf16
   float* logsz;       // [H][Ckp]  ln|K_j| or -inf for empty
   float* kbf;         // fp32 path: [H][Ckp][D]
   float* vbf;         // fp32 path: [H][Ckp][D]
-  int maxT, Rmax, Ckp, W, NB;
+  int maxT, Rmax, Ckp, W;
 };
 
 // --------------------------------------------------------------------------
@@ -156,24 +154,16 @@ __global__ __launch_bounds__(1024) void tiles_kernel(const int32_t* __restrict__
 // LDS tile layout of the MFMA kernel.  Tiles are unpadded; bank conflicts are
 // avoided by XOR-swizzling the 16-byte chunks of a row, so whole tiles can
 // arrive by direct global->LDS loads (lane l of such a load lands at 16 l).
-//   K tile:   KT rows of D bf16; chunk c of row r at chunk c ^ swz(r).
-//   V^T tile: two half tiles (keys 0..31 and 32..63), each D rows of 32 keys;
-//             chunk c of row d at chunk c ^ swz(d); keys in MFMA order: within
-//             every 16-key group keys 4..7 and 8..11 trade places, so the 8
-//             keys one lane feeds a 32x32x16 product (keys 4hi..4hi+3 and
-//             8+4hi..8+4hi+3) form one chunk.
+//   K tile: KT rows of D bf16; chunk c of row r at chunk c ^ swz(r).
+//   V tile: two half tiles (keys 0..31 and 32..63) of 32 rows of D bf16;
+//           chunk c of row r at chunk c ^ vswz(r) (below).
 // swz puts the chunks any 16 consecutive rows (or any 8) read at one column on
-// distinct banks, for 64 as for 32 LDS banks; for the 4-chunk rows of V^T half
-// tiles the choice was checked with the LDS bank-conflict counter.
+// distinct banks, for 64 as for 32 LDS banks.
 // ---------------------------------------------------------------------------
-__host__ __device__ __forceinline__ int mfma_key(int k) {  // an involution
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
-}
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
   if constexpr (CPR == 16) return r & 15;
-  else if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
-  else return (r >> 2) & 3;  // CPR == 4 (measured conflict-free for the P V reads)
+  else return (r & 7) ^ ((r >> 3) & 1);  // CPR == 8
 }
 // element offset of 16-byte chunk c of row r in a tile of CPR chunks per row
 template <int CPR>
@@ -181,11 +171,33 @@ __device__ __forceinline__ int toff(int r, int c) {
   return r * (CPR * 8) + ((c ^ swz<CPR>(r)) << 3);
 }
 
+// V half tiles are row-major too (32 keys of D columns) and are read with the
+// LDS transpose read: within each 16-lane group, lane i receives element i % 4
+// of the 8-byte pieces addressed by lanes i / 4 + 4 j (j = 0..3).  Lanes that
+// address 4 keys x 4 column pieces thus receive 4 keys of one column each,
+// which is the A operand of O^T = V^T P^T, so V needs no transposed copy.
+// Their chunks are XOR-swizzled by 2 (r mod CPR/2): every 16-lane group of such
+// a read then meets 32 distinct banks, and a wave each of 64 banks twice (the
+// best XOR swizzle of the row bits, found by exhaustive search).
+template <int CPR>
+__device__ __forceinline__ int vswz(int r) {
+  return (r & (CPR / 2 - 1)) << 1;
+}
+template <int CPR>
+__device__ __forceinline__ int vtoff(int r, int c) {
+  return r * (CPR * 8) + ((c ^ vswz<CPR>(r)) << 3);
+}
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* p) {
+  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4i16_t __attribute__((address_space(3)))*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+
 __global__ __launch_bounds__(128) void comp_prep_kernel(const float* __restrict__ kbar,
                                                         const float* __restrict__ vbar,
                                                         const int32_t* __restrict__ k_off, int Ck,
                                                         int Ckp, int D, bf16_t* kbh, bf16_t* kbl,
-                                                        bf16_t* vbt, float* kbf, float* vbf,
+                                                        bf16_t* vbr, float* kbf, float* vbf,
                                                         float* logsz) {
   const int j = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
   const size_t o = (size_t(h) * Ckp + j) * D;
@@ -199,7 +211,7 @@ __global__ __launch_bounds__(128) void comp_prep_kernel(const float* __restrict_
       const bf16_t hi = f2bf(kv);
       kbh[o + c] = hi;
       kbl[o + c] = f2bf(kv - bf2f(hi));
-      vbt[((size_t(h) * (Ckp / KT) + j / KT) * D + c) * KT + mfma_key(j % KT)] = f2bf(vv);
+      vbr[o + c] = f2bf(vv);
     }
     if (kbf) {
       kbf[o + c] = kv;
@@ -477,48 +489,20 @@ struct MfmaLds {
   int rowidx[2][KT];  // general path: key row of each position of a tile (by tile parity)
 };
 
-// V^T in 64-key blocks, keys in MFMA order:
-// vt[h][b][c][mfma_key(k)] = v_perm[h][64 b + k][c] (zero past N)
-template <int D>
-__global__ __launch_bounds__(256) void vt_kernel(const bf16_t* __restrict__ v, int N, int NB,
-                                                 bf16_t* __restrict__ vt) {
-  __shared__ bf16_t tile[KT][D + 8];
-  const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-  for (int c = t; c < KT * CPR; c += 256) {
-    const int r = c / CPR, cc = c % CPR;
-    const int pos = b * KT + r;
-    uint4 u = make_uint4(0, 0, 0, 0);
-    if (pos < N) u = *reinterpret_cast<const uint4*>(v + (size_t(h) * N + pos) * D + cc * 8);
-    *reinterpret_cast<uint4*>(&tile[r][cc * 8]) = u;
-  }
-  __syncthreads();
-  bf16_t* dst = vt + (size_t(h) * NB + b) * D * KT;
-  for (int c = t; c < D * (KT / 8); c += 256) {
-    const int d = c / (KT / 8), kc = c % (KT / 8);
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = uint32_t(tile[mfma_key(kc * 8 + 2 * e)][d]) | (uint32_t(tile[mfma_key(kc * 8 + 2 * e + 1)][d]) << 16);
-    *reinterpret_cast<uint4*>(dst + size_t(d) * KT + kc * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
-
-// ALIGNED: rows whose ranges are 64-aligned stream whole 64-key blocks (K rows
-// and pre-transposed V^T are plain 16-byte copies); the other instantiation
-// gathers rows of arbitrary ranges and transposes V while staging it.  Each
-// workgroup runs in the instantiation matching its row and exits in the other.
+// ALIGNED: rows whose ranges are 64-aligned stream whole 64-key blocks (K and
+// V rows are plain 16-byte copies); the other instantiation gathers rows of
+// arbitrary ranges through registers.  Each workgroup runs in the
+// instantiation matching its row and exits in the other.
 template <int D, bool ALIGNED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && ALIGNED ? 3 : 2, D == 64 && ALIGNED ? 3 : 2))) void attn_mfma(AttnArgs a, Prep p, float sl2) {
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int DS = D / 16;         // MFMA k-steps over d
   constexpr int DT = D / 32;         // 32-row tiles of d in O^T
-  constexpr int KCH = D / 4;         // general path: K elements per thread (one row quarter)
-  constexpr int KPT = D / 32;        // general path: V keys per thread
+  constexpr int KCH = D / 4;         // general path: K (and V) elements per thread (one row quarter)
   constexpr int DG = D / 8;          // 16-byte chunks of a K / Q / O row
   constexpr int CK = KT * D / 8 / 256;  // 16-byte chunks per thread of a K tile
-  constexpr int CH = CK / 2;            // ... of a V^T half tile
-  // Six separate tiles: K double buffered, and V^T split into its lower and
+  constexpr int CH = CK / 2;            // ... of a V half tile
+  // Six separate tiles: K double buffered, and V split into its lower and
   // upper 32 keys (VL, VH), each double buffered.  As distinct objects, a
   // direct load into one is visibly independent of reads from the others.
   __shared__ __attribute__((aligned(16))) bf16_t K0[KT * D], K1[KT * D];
@@ -618,15 +602,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
       lsum = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, pk[r >> 1]), BF16_ONES, lsum, false);
     }
   };
-  // O^T += V^T P^T over one 32-key half (Vh: that half of the V^T tile)
+  // O^T += V^T P^T over one 32-key half (Vh: that half of the V tile).  The
+  // lane's 8 probabilities of step ks are keys 16 ks + 4 hi + 0..3 and
+  // 16 ks + 8 + 4 hi + 0..3 of the half; two transpose reads give column
+  // 32 dt + col of the same keys: lane a of each 16-lane group addresses key
+  // (a / 4) of the four and columns 4 (a % 4) .. + 3 of the group's sixteen.
+  // Rows 16 ks + 8 j + tr_row share tr_row's swizzle, so one offset per 32
+  // columns serves all four reads of a column block (the rest is immediate).
+  int tr_off[DT];
+  {
+    const int tr_row = 4 * hi + ((lane & 15) >> 2);
+    const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const int cc = 32 * dt + tr_col;
+      tr_off[dt] = vtoff<DG>(tr_row, cc >> 3) + (cc & 7);
+    }
+  }
   auto pv_half = [&](const uint32_t (&pk)[8], const bf16_t* Vh) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8_t pf = as_bf8(make_uint4(pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]));
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint4 u = *reinterpret_cast<const uint4*>(Vh + toff<HG>(32 * dt + col, 2 * ks + hi));
-        oacc[dt] = mfma32(as_bf8(u), pf, oacc[dt]);
+        const uint2 v0 = lds_read_tr16(Vh + tr_off[dt] + (16 * ks) * D);
+        const uint2 v1 = lds_read_tr16(Vh + tr_off[dt] + (16 * ks + 8) * D);
+        oacc[dt] = mfma32(as_bf8(make_uint4(v0.x, v0.y, v1.x, v1.y)), pf, oacc[dt]);
       }
     }
   };
@@ -671,9 +672,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     // swizzled layout.  A load is the buffer resource (SGPRs) plus one byte
     // offset per lane; a lane's offsets inside a tile are fixed, so only the
     // tile base is added per load.
-    const bf16_t* vth = p.vt + size_t(h) * p.NB * D * KT;
+    const bf16_t* vrh = (const bf16_t*)a.v_perm + size_t(h) * N * D;
     int ri = 0, pos = R > 0 ? rg[0].x : 0, rend = R > 0 ? rg[0].y : 0;
-    const int kbytes = N * D * 2, vbytes = p.NB * D * KT * 2;
+    const int kbytes = N * D * 2, vbytes = N * D * 2;
     uint32_t koff[CK], voff[CH];
 #pragma unroll
     for (int q = 0; q < CK; ++q) {
@@ -683,9 +684,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     }
 #pragma unroll
     for (int q = 0; q < CH; ++q) {
-      const int sl = (4 * q + w) * 64 + lane;  // V^T half-tile chunk
-      const int d = sl / HG, c = (sl % HG) ^ swz<HG>(d);
-      voff[q] = uint32_t(d * KT + c * 8) * 2;  // lower half; the upper one is 64 bytes on
+      const int sl = (4 * q + w) * 64 + lane;  // V half-tile chunk
+      const int r = sl / DG, c = (sl % DG) ^ vswz<DG>(r);
+      voff[q] = uint32_t(r * D + c * 8) * 2;
     }
     auto issue_k = [&](bf16_t* Kd, int pos0, int nvalid) {
       const uint32_t kb = uint32_t(pos0) * (D * 2);
@@ -705,12 +706,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
         }
       }
     };
-    // half kt (0: keys 0..31, 1: keys 32..63) of the V^T block holding pos0
+    // half kt (0: keys 0..31, 1: keys 32..63) of the V rows of the tile at
+    // pos0 (rows past N read as zeros: the buffer's bound)
     auto issue_v = [&](bf16_t* Vd, int pos0, int kt) {
-      const uint32_t vb = uint32_t(pos0 / KT) * (D * KT * 2) + 64 * kt;
+      const uint32_t vb = uint32_t(pos0 + HK * kt) * (D * 2);
 #pragma unroll
       for (int q = 0; q < CH; ++q)
-        buf_load_lds16(vth, vbytes, Vd + (4 * q + w) * 512, vb + voff[q]);
+        buf_load_lds16(vrh, vbytes, Vd + (4 * q + w) * 512, vb + voff[q]);
     };
     // every wave's loads issued before this point have landed, and every
     // wave is done reading the buffers the next loads overwrite
@@ -828,32 +830,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
   } else {
     // ---------------- selected keys, general ranges: row gather --------------
     const bf16_t* vh = (const bf16_t*)a.v_perm + size_t(h) * N * D;
-    const int k_slot = tid >> 2, k_c0 = (tid & 3) * KCH;  // K: one row quarter
-    const int v_dg = tid % DG, v_kg = tid / DG;           // V: KPT keys x 8 columns
+    const int k_slot = tid >> 2, k_c0 = (tid & 3) * KCH;  // K and V: one row quarter
     uint4 kreg[KCH / 8];
-    uint4 vreg[KPT];
+    uint4 vreg[KCH / 8];
     auto store_tile = [&](bf16_t* Kd, bf16_t* VLd, bf16_t* VHd) {
+      bf16_t* Vd = k_slot < HK ? VLd : VHd;
 #pragma unroll
-      for (int q = 0; q < KCH / 8; ++q)
+      for (int q = 0; q < KCH / 8; ++q) {
         *reinterpret_cast<uint4*>(Kd + toff<DG>(k_slot, k_c0 / 8 + q)) = kreg[q];
-      const int kp = mfma_key(v_kg * KPT);  // the KPT keys stay contiguous in MFMA order
-      bf16_t* Vd = kp < HK ? VLd : VHd;
-      const int kl = kp & (HK - 1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = v_dg * 8 + e;
-        bf16_t* dst = Vd + toff<HG>(c, kl >> 3) + (kl & 7);
-        uint32_t wv[KPT];
-#pragma unroll
-        for (int kq = 0; kq < KPT; ++kq) {
-          const uint32_t word = (e < 2) ? vreg[kq].x : (e < 4) ? vreg[kq].y : (e < 6) ? vreg[kq].z : vreg[kq].w;
-          wv[kq] = (e & 1) ? (word >> 16) : (word & 0xFFFFu);
-        }
-        if constexpr (KPT == 4) {
-          *reinterpret_cast<uint2*>(dst) = make_uint2(wv[0] | (wv[1] << 16), wv[2] | (wv[3] << 16));
-        } else {
-          *reinterpret_cast<uint32_t*>(dst) = wv[0] | (wv[1] << 16);
-        }
+        *reinterpret_cast<uint4*>(Vd + vtoff<DG>(k_slot & (HK - 1), k_c0 / 8 + q)) = vreg[q];
       }
     };
     const uint32_t* mrow = a.mask + (size_t(h) * a.Cq + i) * p.W;
@@ -907,26 +892,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
       auto load_tile = [&](int tt) {
         const int base = tt * KT;
         const int* ri = S.rowidx[tt & 1];
-        {
-          const int pos = base + k_slot;
-          if (pos < total) {
-            const int row = ri[k_slot];
-            const uint4* src = reinterpret_cast<const uint4*>(kh + size_t(row) * D + k_c0);
+        const int pos = base + k_slot;
+        if (pos < total) {
+          const int row = ri[k_slot];
+          const uint4* src = reinterpret_cast<const uint4*>(kh + size_t(row) * D + k_c0);
+          const uint4* srv = reinterpret_cast<const uint4*>(vh + size_t(row) * D + k_c0);
 #pragma unroll
-            for (int q = 0; q < KCH / 8; ++q) kreg[q] = src[q];
-          } else {
-#pragma unroll
-            for (int q = 0; q < KCH / 8; ++q) kreg[q] = make_uint4(0, 0, 0, 0);
+          for (int q = 0; q < KCH / 8; ++q) {
+            kreg[q] = src[q];
+            vreg[q] = srv[q];
           }
-        }
+        } else {
 #pragma unroll
-        for (int kq = 0; kq < KPT; ++kq) {
-          const int pos = base + v_kg * KPT + kq;
-          if (pos < total) {
-            const int row = ri[v_kg * KPT + kq];
-            vreg[kq] = *reinterpret_cast<const uint4*>(vh + size_t(row) * D + v_dg * 8);
-          } else {
-            vreg[kq] = make_uint4(0, 0, 0, 0);
+          for (int q = 0; q < KCH / 8; ++q) {
+            kreg[q] = make_uint4(0, 0, 0, 0);
+            vreg[q] = make_uint4(0, 0, 0, 0);
           }
         }
       };
@@ -953,7 +933,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     const uint32_t* mr = a.mask + (size_t(h) * a.Cq + i) * p.W;
     const bf16_t* kbh = p.kbh + size_t(h) * p.Ckp * D;
     const bf16_t* kbl = p.kbl + size_t(h) * p.Ckp * D;
-    const bf16_t* vbt = p.vbt + size_t(h) * p.Ckp * D;
+    const bf16_t* vbr = p.vbr + size_t(h) * p.Ckp * D;
     for (int j0 = 0; j0 < p.Ckp; j0 += KT) {
       __syncthreads();
       int fin = 0;
@@ -972,10 +952,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
         const size_t ro = size_t(j0 + row) * D + kc * 8;
         *reinterpret_cast<uint4*>(K0 + toff<DG>(row, kc)) = *reinterpret_cast<const uint4*>(kbh + ro);
         *reinterpret_cast<uint4*>(K1 + toff<DG>(row, kc)) = *reinterpret_cast<const uint4*>(kbl + ro);
-        // chunk c of the [D][64] V^T block: row c / 8, chunk c % 8 (halves of 4)
-        const int vr = c >> 3, vc = c & 7;
-        *reinterpret_cast<uint4*>((vc < 4 ? VL0 : VH0) + toff<HG>(vr, vc & 3)) =
-            *reinterpret_cast<const uint4*>(vbt + size_t(j0) * D + size_t(c) * 8);
+        *reinterpret_cast<uint4*>((row < HK ? VL0 : VH0) + vtoff<DG>(row & (HK - 1), kc)) =
+            *reinterpret_cast<const uint4*>(vbr + ro);
       }
       __syncthreads();
       floatx16 s[2];
@@ -1025,19 +1003,17 @@ Prep carve(const AttnArgs& a, Arena& s) {
   p.Rmax = a.Ck <= ALIGNED_MAX_CK ? a.Ck / 2 + 1 : 0;
   p.Ckp = ceil_div(a.Ck, KT) * KT;
   p.W = ceil_div(a.Ck, 32);
-  p.NB = ceil_div(a.N, KT);
   p.tiles = s.get<int4>(size_t(a.H) * p.maxT);
   p.ntiles = s.get<int32_t>(size_t(a.H));
   p.ranges = p.Rmax ? s.get<int2>(size_t(a.H) * a.Cq * p.Rmax) : nullptr;
   p.rcount = s.get<int32_t>(size_t(a.H) * a.Cq);
   p.raligned = s.get<int32_t>(size_t(a.H) * a.Cq);
-  if (a.dtype == SA_BF16) p.vt = s.get<bf16_t>(size_t(a.H) * p.NB * KT * a.d);
   if (a.compensate) {
     p.logsz = s.get<float>(size_t(a.H) * p.Ckp);
     if (a.dtype == SA_BF16) {
       p.kbh = s.get<bf16_t>(size_t(a.H) * p.Ckp * a.d);
       p.kbl = s.get<bf16_t>(size_t(a.H) * p.Ckp * a.d);
-      p.vbt = s.get<bf16_t>(size_t(a.H) * p.Ckp * a.d);
+      p.vbr = s.get<bf16_t>(size_t(a.H) * p.Ckp * a.d);
     } else {
       p.kbf = s.get<float>(size_t(a.H) * p.Ckp * a.d);
       p.vbf = s.get<float>(size_t(a.H) * p.Ckp * a.d);
@@ -1084,16 +1060,9 @@ hipError_t attn_run(const AttnArgs& a, Arena& s, hipStream_t st) {
   tiles_kernel<<<a.H, 1024, 0, st>>>(a.q_off, a.Cq, a.tile_rows, p.maxT, p.tiles, p.ntiles);
   if (a.compensate)
     comp_prep_kernel<<<dim3(p.Ckp, a.H), 128, 0, st>>>(a.kbar, a.vbar, a.k_off, a.Ck, p.Ckp, a.d,
-                                                       p.kbh, p.kbl, p.vbt, p.kbf, p.vbf, p.logsz);
+                                                       p.kbh, p.kbl, p.vbr, p.kbf, p.vbf, p.logsz);
   const int grid = 8 * a.H * ceil_div(p.maxT, 8);
   const float sl2 = a.scale * LOG2E;
-  const dim3 gv(p.NB, a.H);
-  if (a.dtype == SA_BF16) {
-    if (a.d == 128)
-      vt_kernel<128><<<gv, 256, 0, st>>>((const bf16_t*)a.v_perm, a.N, p.NB, p.vt);
-    else
-      vt_kernel<64><<<gv, 256, 0, st>>>((const bf16_t*)a.v_perm, a.N, p.NB, p.vt);
-  }
   // the probe events bracket the attention kernels only (prep excluded)
   if (g_probe_start) (void)hipEventRecord(g_probe_start, st);
   if (a.dtype == SA_BF16) {
