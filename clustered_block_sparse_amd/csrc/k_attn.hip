@@ -498,7 +498,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
   static_assert(D == 64 || D == 128, "head dim");
   constexpr int DS = D / 16;         // MFMA k-steps over d
   constexpr int DT = D / 32;         // 32-row tiles of d in O^T
-  constexpr int KCH = D / 4;         // general path: K (and V) elements per thread (one row quarter)
   constexpr int DG = D / 8;          // 16-byte chunks of a K / Q / O row
   constexpr int CK = KT * D / 8 / 256;  // 16-byte chunks per thread of a K tile
   constexpr int CH = CK / 2;            // ... of a V half tile
@@ -830,17 +829,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
   } else {
     // ---------------- selected keys, general ranges: row gather --------------
     const bf16_t* vh = (const bf16_t*)a.v_perm + size_t(h) * N * D;
-    const int k_slot = tid >> 2, k_c0 = (tid & 3) * KCH;  // K and V: one row quarter
-    uint4 kreg[KCH / 8];
-    uint4 vreg[KCH / 8];
-    auto store_tile = [&](bf16_t* Kd, bf16_t* VLd, bf16_t* VHd) {
-      bf16_t* Vd = k_slot < HK ? VLd : VHd;
-#pragma unroll
-      for (int q = 0; q < KCH / 8; ++q) {
-        *reinterpret_cast<uint4*>(Kd + toff<DG>(k_slot, k_c0 / 8 + q)) = kreg[q];
-        *reinterpret_cast<uint4*>(Vd + vtoff<DG>(k_slot & (HK - 1), k_c0 / 8 + q)) = vreg[q];
-      }
-    };
+    const int hbytes = N * D * 2;
     const uint32_t* mrow = a.mask + (size_t(h) * a.Cq + i) * p.W;
     const int32_t* kof = a.k_off + size_t(h) * (a.Ck + 1);
     int scan_word = 0;
@@ -889,40 +878,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
         const uint64_t bal = __ballot(r < nrc && st <= base + KT);
         r0 += 63 - __clzll((unsigned long long)bal);
       };
-      auto load_tile = [&](int tt) {
-        const int base = tt * KT;
+      // Tile tt's K and V rows by direct buffer->LDS loads: lane l of a load
+      // lands at slot 64 q' + l of the tile, i.e. at (row, chunk), and
+      // fetches the chunk the swizzled layout keeps there from the listed
+      // key row.  Positions past the end repeat the last listed row (their
+      // scores are masked and their probabilities are zero).
+      auto issue_tile = [&](int tt, bf16_t* Kd, bf16_t* VLd, bf16_t* VHd) {
+        const int nv = min(KT, total - tt * KT);
         const int* ri = S.rowidx[tt & 1];
-        const int pos = base + k_slot;
-        if (pos < total) {
-          const int row = ri[k_slot];
-          const uint4* src = reinterpret_cast<const uint4*>(kh + size_t(row) * D + k_c0);
-          const uint4* srv = reinterpret_cast<const uint4*>(vh + size_t(row) * D + k_c0);
 #pragma unroll
-          for (int q = 0; q < KCH / 8; ++q) {
-            kreg[q] = src[q];
-            vreg[q] = srv[q];
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < KCH / 8; ++q) {
-            kreg[q] = make_uint4(0, 0, 0, 0);
-            vreg[q] = make_uint4(0, 0, 0, 0);
-          }
+        for (int q = 0; q < CK; ++q) {
+          const int sl = (4 * q + w) * 64 + lane;
+          const int r = sl / DG, c = (sl % DG) ^ swz<DG>(r);
+          const uint32_t row = uint32_t(ri[min(r, nv - 1)]);
+          buf_load_lds16(kh, hbytes, Kd + (4 * q + w) * 512, row * (D * 2) + uint32_t(c * 16));
         }
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int q = 0; q < CH; ++q) {
+            const int sl = (4 * q + w) * 64 + lane;  // slot in the half tile
+            const int rh = sl / DG, c = (sl % DG) ^ vswz<DG>(rh);
+            const uint32_t row = uint32_t(ri[min(HK * kt + rh, nv - 1)]);
+            buf_load_lds16(vh, hbytes, (kt ? VHd : VLd) + (4 * q + w) * 512, row * (D * 2) + uint32_t(c * 16));
+          }
       };
       if (ntile > 0) {
         if (w == 0) build_rows(0);
         __syncthreads();
-        load_tile(0);
+        issue_tile(0, K0, VL0, VH0);
       }
       for (int tt = 0; tt < ntile; ++tt) {
         bf16_t* Kb = (tt & 1) ? K1 : K0;
         bf16_t* VLb = (tt & 1) ? VL1 : VL0;
         bf16_t* VHb = (tt & 1) ? VH1 : VH0;
-        store_tile(Kb, VLb, VHb);
         if (w == 0 && tt + 1 < ntile) build_rows(tt + 1);
+        // this wave's loads of tile tt have landed; after the barrier so have
+        // every wave's, the next row list is visible, and the other buffers
+        // (tile tt - 1) are no longer read
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
         __syncthreads();
-        if (tt + 1 < ntile) load_tile(tt + 1);
+        if (tt + 1 < ntile) issue_tile(tt + 1, (tt & 1) ? K0 : K1, (tt & 1) ? VL0 : VL1, (tt & 1) ? VH0 : VH1);
         compute_tile(Kb, VLb, VHb, total - tt * KT);
       }
     }
