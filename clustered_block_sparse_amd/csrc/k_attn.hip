@@ -486,7 +486,7 @@ struct MfmaLds {
   int wsum[16];
   int fsh[2];
   float bias[KT];
-  int rowidx[2][KT];  // general path: key row of each position of a tile (by tile parity)
+  int rowidx[3][KT];  // general path: key row of each position of tile t in [t % 3]
 };
 
 // ALIGNED: rows whose ranges are 64-aligned stream whole 64-key blocks (K and
@@ -662,6 +662,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     softmax_pv(s, VLb, VHb, sl2);
   };
 
+  // every wave's loads issued before this point have landed, and every
+  // wave is done reading the buffers the next loads overwrite
+  auto sync_loads = [&]() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+  };
+  // Software pipeline over the whole tiles, in 32-key halves (both paths).  Each half
+  // step forms the scores of one half while the probabilities of the
+  // previous half are exponentiated, then accumulates P V of the previous
+  // half while the new half's row maximum is taken:
+  //   tile n, half 0:  S(n,0) | P(n-1,1);  P(n-1,1) V(n-1,hi) | max S(n,0)
+  //   tile n, half 1:  S(n,1) | P(n,0);    P(n,0) V(n,lo)     | max S(n,1)
+  // So tile n reads K(n), VH(n-1) and VL(n), and meanwhile K(n+1), VH(n) and
+  // VL(n+1) land in the other halves of the double buffers.
+  floatx16 s0, s1;  // scores of halves 0 and 1 (s1 carries into the next tile)
+  uint32_t pk[8];
+  auto tile = [&](const bf16_t* Kc, const bf16_t* VLc, const bf16_t* VHp) {
+    zero16(s0);
+    qk_half(s0, Kc, 0);
+    exp_half(s1, sl2, pk);
+    pv_half(pk, VHp);
+    rescale_to(max_half(s0, sl2));
+    zero16(s1);
+    qk_half(s1, Kc, 1);
+    exp_half(s0, sl2, pk);
+    pv_half(pk, VLc);
+    rescale_to(max_half(s1, sl2));
+  };
+  // tile 0 of a pipeline: its lower half has no predecessor
+  auto first_tile = [&](const bf16_t* Kc, const bf16_t* VLc) {
+    zero16(s0);
+    qk_half(s0, Kc, 0);
+    rescale_to(max_half(s0, sl2));
+    zero16(s1);
+    qk_half(s1, Kc, 1);
+    exp_half(s0, sl2, pk);
+    pv_half(pk, VLc);
+    rescale_to(max_half(s1, sl2));
+  };
+
   if constexpr (ALIGNED) {
     const int R = p.rcount[size_t(h) * a.Cq + i];
     const int2* rg = p.ranges + (size_t(h) * a.Cq + i) * p.Rmax;
@@ -713,12 +753,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
       for (int q = 0; q < CH; ++q)
         buf_load_lds16(vrh, vbytes, Vd + (4 * q + w) * 512, vb + voff[q]);
     };
-    // every wave's loads issued before this point have landed, and every
-    // wave is done reading the buffers the next loads overwrite
-    auto sync_loads = [&]() {
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-      __syncthreads();
-    };
     // Move the cursor to the next whole 64-key tile.  False once the ranges
     // are done, or when the next tile is partial: only the last tile of a
     // range ending at N can be, and it is kept aside as the tail.
@@ -740,28 +774,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
       }
       return true;
     };
-    // Software pipeline over the whole tiles, in 32-key halves.  Each half
-    // step forms the scores of one half while the probabilities of the
-    // previous half are exponentiated, then accumulates P V of the previous
-    // half while the new half's row maximum is taken:
-    //   tile n, half 0:  S(n,0) | P(n-1,1);  P(n-1,1) V(n-1,hi) | max S(n,0)
-    //   tile n, half 1:  S(n,1) | P(n,0);    P(n,0) V(n,lo)     | max S(n,1)
-    // So tile n reads K(n), VH(n-1) and VL(n), and meanwhile K(n+1), VH(n) and
-    // VL(n+1) land in the other halves of the double buffers.
-    floatx16 s0, s1;  // scores of halves 0 and 1 (s1 carries into the next tile)
-    uint32_t pk[8];
-    auto tile = [&](const bf16_t* Kc, const bf16_t* VLc, const bf16_t* VHp) {
-      zero16(s0);
-      qk_half(s0, Kc, 0);
-      exp_half(s1, sl2, pk);
-      pv_half(pk, VHp);
-      rescale_to(max_half(s0, sl2));
-      zero16(s1);
-      qk_half(s1, Kc, 1);
-      exp_half(s0, sl2, pk);
-      pv_half(pk, VLc);
-      rescale_to(max_half(s1, sl2));
-    };
     if (R > 0 && rend - pos < KT) {
       have_tail = true;
       tail_pos = pos;
@@ -777,15 +789,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
         issue_v(VL1, pos, 0);
       }
       issue_v(VH0, pn, 1);
-      // tile 0: its lower half has no predecessor
-      zero16(s0);
-      qk_half(s0, K0, 0);
-      rescale_to(max_half(s0, sl2));
-      zero16(s1);
-      qk_half(s1, K0, 1);
-      exp_half(s0, sl2, pk);
-      pv_half(pk, VL0);
-      rescale_to(max_half(s1, sl2));
+      first_tile(K0, VL0);
       bool last_odd = false;  // parity of the last tile
       while (more) {
         pn = pos;
@@ -841,9 +845,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
       scan_word = S.fsh[0];
       if (nrc == 0) break;
       const int total = S.rp[nrc];
-      const int ntile = ceil_div(total, KT);
       // Wave 0 lists the key row of every position of tile t in
-      // S.rowidx[t & 1].  Window: the 64 ranges from r0, the range holding the
+      // S.rowidx[t % 3].  Window: the 64 ranges from r0, the range holding the
       // tile's first position; ranges are never empty, so they cover the
       // tile.  Short ranges: lane l writes the positions range r0 + l shares
       // with the tile.  When some range covers more than 8 of them, lane j
@@ -859,7 +862,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
           en = S.rp[r + 1];
         }
         const int lo = max(st, base), hi = min(en, end);
-        int* ri = S.rowidx[t & 1];
+        int* ri = S.rowidx[t % 3];
         if (__ballot(r < nrc && hi - lo > 8)) {
           const int pos = base + lane;
           if (pos < end) {
@@ -878,14 +881,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
         const uint64_t bal = __ballot(r < nrc && st <= base + KT);
         r0 += 63 - __clzll((unsigned long long)bal);
       };
-      // Tile tt's K and V rows by direct buffer->LDS loads: lane l of a load
-      // lands at slot 64 q' + l of the tile, i.e. at (row, chunk), and
-      // fetches the chunk the swizzled layout keeps there from the listed
-      // key row.  Positions past the end repeat the last listed row (their
-      // scores are masked and their probabilities are zero).
-      auto issue_tile = [&](int tt, bf16_t* Kd, bf16_t* VLd, bf16_t* VHd) {
-        const int nv = min(KT, total - tt * KT);
-        const int* ri = S.rowidx[tt & 1];
+      // K rows of tile t, and half kt of its V rows, by direct buffer->LDS
+      // loads: lane l of a load lands at slot 64 q' + l of the tile, i.e. at
+      // (row, chunk), and fetches the chunk the swizzled layout keeps there
+      // from the listed key row.  Positions past nv repeat the last listed
+      // row (their scores are masked and their probabilities are zero).
+      auto issue_k = [&](bf16_t* Kd, int t, int nv) {
+        const int* ri = S.rowidx[t % 3];
 #pragma unroll
         for (int q = 0; q < CK; ++q) {
           const int sl = (4 * q + w) * 64 + lane;
@@ -893,33 +895,80 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
           const uint32_t row = uint32_t(ri[min(r, nv - 1)]);
           buf_load_lds16(kh, hbytes, Kd + (4 * q + w) * 512, row * (D * 2) + uint32_t(c * 16));
         }
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int q = 0; q < CH; ++q) {
-            const int sl = (4 * q + w) * 64 + lane;  // slot in the half tile
-            const int rh = sl / DG, c = (sl % DG) ^ vswz<DG>(rh);
-            const uint32_t row = uint32_t(ri[min(HK * kt + rh, nv - 1)]);
-            buf_load_lds16(vh, hbytes, (kt ? VHd : VLd) + (4 * q + w) * 512, row * (D * 2) + uint32_t(c * 16));
-          }
       };
-      if (ntile > 0) {
+      auto issue_v = [&](bf16_t* Vd, int t, int kt, int nv) {
+        const int* ri = S.rowidx[t % 3];
+#pragma unroll
+        for (int q = 0; q < CH; ++q) {
+          const int sl = (4 * q + w) * 64 + lane;  // slot in the half tile
+          const int rh = sl / DG, c = (sl % DG) ^ vswz<DG>(rh);
+          const uint32_t row = uint32_t(ri[min(HK * kt + rh, nv - 1)]);
+          buf_load_lds16(vh, hbytes, Vd + (4 * q + w) * 512, row * (D * 2) + uint32_t(c * 16));
+        }
+      };
+      // The whole tiles run the aligned path's pipeline.  Wave 0 lists tile
+      // n + 1's rows before the barrier that precedes its loads; tile n's
+      // list is still read after that barrier (its upper V half), and tile
+      // n - 1's slot is free by then, hence three slots.
+      const int nfull = total / KT, tail_nv = total - nfull * KT;
+      if (nfull > 0) {
         if (w == 0) build_rows(0);
         __syncthreads();
-        issue_tile(0, K0, VL0, VH0);
+        issue_k(K0, 0, KT);
+        issue_v(VL0, 0, 0, KT);
+        bool more = nfull > 1;
+        if (w == 0 && more) build_rows(1);
+        sync_loads();
+        if (more) {
+          issue_k(K1, 1, KT);
+          issue_v(VL1, 1, 0, KT);
+        }
+        issue_v(VH0, 0, 1, KT);
+        first_tile(K0, VL0);
+        bool last_odd = false;  // parity of the last tile
+        int n = 1;
+        while (more) {
+          more = n + 1 < nfull;
+          if (w == 0 && more) build_rows(n + 1);
+          sync_loads();
+          if (more) {
+            issue_k(K0, n + 1, KT);
+            issue_v(VL0, n + 1, 0, KT);
+          }
+          issue_v(VH1, n, 1, KT);
+          tile(K1, VL1, VH0);
+          ++n;
+          if (!more) {
+            last_odd = true;
+            break;
+          }
+          more = n + 1 < nfull;
+          if (w == 0 && more) build_rows(n + 1);
+          sync_loads();
+          if (more) {
+            issue_k(K1, n + 1, KT);
+            issue_v(VL1, n + 1, 0, KT);
+          }
+          issue_v(VH0, n, 1, KT);
+          tile(K0, VL0, VH1);
+          ++n;
+        }
+        // drain: P V of the last tile's upper half
+        sync_loads();
+        exp_half(s1, sl2, pk);
+        pv_half(pk, last_odd ? VH1 : VH0);
       }
-      for (int tt = 0; tt < ntile; ++tt) {
-        bf16_t* Kb = (tt & 1) ? K1 : K0;
-        bf16_t* VLb = (tt & 1) ? VL1 : VL0;
-        bf16_t* VHb = (tt & 1) ? VH1 : VH0;
-        if (w == 0 && tt + 1 < ntile) build_rows(tt + 1);
-        // this wave's loads of tile tt have landed; after the barrier so have
-        // every wave's, the next row list is visible, and the other buffers
-        // (tile tt - 1) are no longer read
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      if (tail_nv > 0) {
+        // the partial last tile, unpipelined (every buffer is free after the
+        // barrier)
         __syncthreads();
-        if (tt + 1 < ntile) issue_tile(tt + 1, (tt & 1) ? K0 : K1, (tt & 1) ? VL0 : VL1, (tt & 1) ? VH0 : VH1);
-        compute_tile(Kb, VLb, VHb, total - tt * KT);
+        if (w == 0) build_rows(nfull);
+        __syncthreads();
+        issue_k(K0, nfull, tail_nv);
+        issue_v(VL0, nfull, 0, tail_nv);
+        issue_v(VH0, nfull, 1, tail_nv);
+        sync_loads();
+        compute_tile(K0, VL0, VH0, tail_nv);
       }
     }
   }
