@@ -107,6 +107,100 @@ __global__ __launch_bounds__(256) void assign_kernel(const T* __restrict__ x, in
   if (valid) labels[size_t(h) * N + tok] = bj;
 }
 
+// bf16 rows: the same assignment on the matrix cores.  argmin_j ||x - c_j||^2
+// = argmin_j (||c_j||^2 - 2 x.c_j).  x is exact in bf16; each centroid is split
+// into three bf16 terms (c = hi + mid + lo, the residual below 2^-24 |c|), so
+// the dot products are fp32-accurate, and the expansion's rounding stays far
+// inside the near-tie scale 1e-5 (||x||^2 + ||c||^2).  S^T = C X^T per block of
+// 32 centroids x 32 tokens on 32x32x16 bf16 MFMA: lane (col, hi) owns token col
+// and centroids 8 (r / 4) + 4 hi + r % 4 (r = 0..15) of the block, walked in
+// ascending order with a strict compare, and the two lanes of a token keep
+// the smaller (distance, index).  Centroid rows sit in LDS with a pitch of
+// DC + 8 elements, an odd number of 16-byte chunks, so the 32 rows a fragment
+// read touches fall on distinct banks.
+template <int DC>
+constexpr int mfma_pitch() {
+  return DC + 8;
+}
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+__device__ __forceinline__ floatx16 kmfma(bf16x8_t a, bf16x8_t b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+template <int DC>
+__global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restrict__ x, int d, int col0,
+                                                          int N, int C, const float* __restrict__ cent,
+                                                          int32_t* __restrict__ labels) {
+  constexpr int P = mfma_pitch<DC>();
+  constexpr int KS = DC / 16;  // k-steps of 16 columns
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int CP = (C + 31) & ~31;
+  bf16_t* ct = reinterpret_cast<bf16_t*>(smem);                  // [3][CP][P]
+  float* cn = reinterpret_cast<float*>(smem + size_t(3) * CP * P * 2);  // [CP] ||c||^2
+  const int h = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int col = lane & 31, hi = lane >> 5;
+  const float* ch = cent + size_t(h) * C * DC;
+  for (int e = t; e < CP * DC; e += 256) {
+    const int c = e / DC, k = e % DC;
+    const float v = c < C ? ch[size_t(c) * DC + k] : 0.f;
+    const bf16_t t0 = f2bf(v);
+    const float r1 = v - bf2f(t0);
+    const bf16_t t1 = f2bf(r1);
+    const bf16_t t2 = f2bf(r1 - bf2f(t1));
+    ct[size_t(c) * P + k] = t0;
+    ct[size_t(CP + c) * P + k] = t1;
+    ct[size_t(2 * CP + c) * P + k] = t2;
+  }
+  for (int c = t; c < CP; c += 256) {
+    float sq = 0.f;
+    if (c < C)
+      for (int k = 0; k < DC; ++k) sq = fmaf(ch[size_t(c) * DC + k], ch[size_t(c) * DC + k], sq);
+    cn[c] = sq;
+  }
+  __syncthreads();
+  // each wave: two blocks of 32 tokens
+#pragma unroll 1
+  for (int b = 0; b < 2; ++b) {
+    const int tok = blockIdx.x * 256 + (2 * w + b) * 32 + col;
+    const bool valid = tok < N;
+    const bf16_t* row = x + (size_t(h) * N + (valid ? tok : 0)) * d + col0;
+    bf16x8_t xf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      uint4 u = *reinterpret_cast<const uint4*>(row + 16 * s + 8 * hi);
+      if (!valid) u = make_uint4(0, 0, 0, 0);
+      xf[s] = __builtin_bit_cast(bf16x8_t, u);
+    }
+    float best = __builtin_huge_valf();
+    int bj = 0x7fffffff;
+    for (int cb = 0; cb < CP; cb += 32) {
+      floatx16 acc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+      for (int term = 0; term < 3; ++term)
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+          const uint4 u = *reinterpret_cast<const uint4*>(ct + size_t(term * CP + cb + col) * P + 16 * s + 8 * hi);
+          acc = kmfma(__builtin_bit_cast(bf16x8_t, u), xf[s], acc);
+        }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = cb + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const float dv = cn[c] - 2.f * acc[r];
+        if (c < C && dv < best) {
+          best = dv;
+          bj = c;
+        }
+      }
+    }
+    const float ob = __shfl_xor(best, 32, 64);
+    const int oj = __shfl_xor(bj, 32, 64);
+    if (ob < best || (ob == best && oj < bj)) bj = oj;
+    if (valid && hi == 0) labels[size_t(h) * N + tok] = bj;
+  }
+}
+
 template <typename T>
 __global__ void seed_kernel(const T* __restrict__ x, int d, int col0, int dc, int N, int C,
                             float* __restrict__ c) {
@@ -156,9 +250,43 @@ hipError_t assign_launch(const void* x, int d, int col0, int H, int N, int C, co
   return hipGetLastError();
 }
 
+template <int DC>
+hipError_t assign_mfma_launch(const void* x, int d, int col0, int H, int N, int C, const float* c,
+                              int32_t* labels, hipStream_t st) {
+  const int CP = (C + 31) & ~31;
+  const size_t lds = size_t(3) * CP * mfma_pitch<DC>() * 2 + size_t(CP) * 4;
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute((const void*)assign_mfma_kernel<DC>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          int(lds)) != hipSuccess)
+    return hipErrorInvalidValue;
+  assign_mfma_kernel<DC><<<dim3(ceil_div(N, 256), H), 256, lds, st>>>((const bf16_t*)x, d, col0, N, C, c,
+                                                                      labels);
+  return hipGetLastError();
+}
+
+// The matrix-core path: bf16 rows whose 16-byte slices are aligned, widths
+// that are whole 16-column steps, and up to 128 centroids (centroid terms in
+// at most 105 KB of LDS).
+bool assign_mfma_ok(const void* x, int d, int col0, int dc, int C) {
+  return (reinterpret_cast<uintptr_t>(x) % 16 == 0) && d % 8 == 0 && col0 % 8 == 0 && dc % 16 == 0 &&
+         C >= 1 && C <= 128;
+}
+
 template <typename T>
 hipError_t assign_dispatch(const void* x, int d, int col0, int dc, int H, int N, int C,
                            const float* c, int32_t* labels, hipStream_t st) {
+  if constexpr (sizeof(T) == 2) {
+    if (assign_mfma_ok(x, d, col0, dc, C)) {
+      switch (dc) {
+        case 16: return assign_mfma_launch<16>(x, d, col0, H, N, C, c, labels, st);
+        case 32: return assign_mfma_launch<32>(x, d, col0, H, N, C, c, labels, st);
+        case 48: return assign_mfma_launch<48>(x, d, col0, H, N, C, c, labels, st);
+        case 64: return assign_mfma_launch<64>(x, d, col0, H, N, C, c, labels, st);
+        case 128: return assign_mfma_launch<128>(x, d, col0, H, N, C, c, labels, st);
+        default: break;
+      }
+    }
+  }
   switch (dc) {
     case 16: return assign_launch<T, 16>(x, d, col0, H, N, C, c, labels, st);
     case 24: return assign_launch<T, 24>(x, d, col0, H, N, C, c, labels, st);
