@@ -2,14 +2,16 @@
 // per-subspace key clustering (SCOPE, technical framework: the t/h/w slices
 // of the post-RoPE keys are clustered independently).
 //
-// Distances are evaluated directly as sum_t (x_t - c_t)^2 in fp32 (no
-// ||c||^2 - 2 x.c expansion, so no cancellation); ties go to the smallest
-// centroid index.  The data here is small next to attention (at most a few
-// GFLOP per layer), so the kernel keeps centroid chunks in LDS and token rows
-// in registers rather than using matrix cores: the work is two vector ALU
-// operations per (token, centroid, dimension).
+// bf16 rows (the common case) go to the matrix cores: ||c||^2 - 2 x.c with
+// the centroids split into three bf16 terms, so the dot products are
+// fp32-accurate.  Other rows (fp32, or slices that are not whole 16-column
+// steps) evaluate sum_t (x_t - c_t)^2 directly in fp32 on the vector ALU, two
+// operations per (token, centroid, dimension).  Ties go to the smallest
+// centroid index in both.
 
 #include "sa_internal.h"
+
+#include <algorithm>
 
 namespace sa {
 
@@ -201,6 +203,214 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
   }
 }
 
+// One Lloyd step for bf16 rows in one pass over them: the assignment above,
+// then every workgroup's sums of its tokens' slices per cluster, as
+// onehot(labels)^T X on the same MFMA (bf16 products of x and 1 are exact,
+// sums in fp32 in a fixed order), and its per-cluster counts.  A workgroup
+// takes G groups of 128 tokens (one 32-token block per wave); each group's
+// rows go to LDS, where the X^T operand is read with the LDS transpose read
+// (ds_read_b64_tr_b16: lane i of each 16 receives element i % 4 of the pieces
+// addressed by lanes i / 4 + 4 j, so 4 tokens x 4 column pieces give 4 tokens
+// of one column per lane).  The waves share out the (32 clusters, 32 columns)
+// blocks of the sums.  Workgroup partials are added in workgroup order by
+// kmeans_combine_kernel, which keeps the previous centroid of an empty cluster.
+// Rows are staged with chunk c of row r at c ^ xswz(r), which puts every 16-lane
+// group of a transpose read on distinct banks (exhaustive search over XOR
+// swizzles of the row bits).
+template <int CPR>
+__device__ __forceinline__ int xswz(int r) {
+  if constexpr (CPR == 16) return (r & 7) << 1;
+  else if constexpr (CPR == 8) return (r & 3) << 1;
+  else return ((r >> 1) & 1) << 1;  // CPR == 4
+}
+typedef short v4i16k_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_tr16(const bf16_t* p) {
+  const v4i16k_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4i16k_t __attribute__((address_space(3)))*)p);
+  return __builtin_bit_cast(uint2, r);
+}
+constexpr int KSTEP_TOK = 128;  // tokens per group
+template <int DC>
+constexpr int step_dcp() {
+  return (DC + 31) & ~31;  // columns of the staged rows (zero padded)
+}
+template <int DC>
+__global__ __launch_bounds__(256) void kmeans_step_kernel(const bf16_t* __restrict__ x, int d, int col0, int N,
+                                                          int C, int G, const float* __restrict__ cent,
+                                                          int32_t* __restrict__ labels, float* __restrict__ psum,
+                                                          int32_t* __restrict__ pcnt) {
+  constexpr int P = mfma_pitch<DC>();
+  constexpr int KS = DC / 16;
+  constexpr int DCP = step_dcp<DC>();
+  constexpr int CPR = DCP / 8;      // 16-byte chunks of a staged row
+  constexpr int NDB = DCP / 32;     // 32-column blocks of the sums
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int CP = (C + 31) & ~31;
+  bf16_t* ct = reinterpret_cast<bf16_t*>(smem);                              // [3][CP][P]
+  float* cn = reinterpret_cast<float*>(smem + size_t(3) * CP * P * 2);       // [CP]
+  bf16_t* xs = reinterpret_cast<bf16_t*>(cn + CP);                           // [128][DCP]
+  int* lab = reinterpret_cast<int*>(xs + KSTEP_TOK * DCP);                   // [128]
+  int* cnt = lab + KSTEP_TOK;                                                // [CP]
+  const int h = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int col = lane & 31, hi = lane >> 5;
+  const float* ch = cent + size_t(h) * C * DC;
+  for (int e = t; e < CP * DC; e += 256) {
+    const int c = e / DC, k = e % DC;
+    const float v = c < C ? ch[size_t(c) * DC + k] : 0.f;
+    const bf16_t t0 = f2bf(v);
+    const float r1 = v - bf2f(t0);
+    const bf16_t t1 = f2bf(r1);
+    const bf16_t t2 = f2bf(r1 - bf2f(t1));
+    ct[size_t(c) * P + k] = t0;
+    ct[size_t(CP + c) * P + k] = t1;
+    ct[size_t(2 * CP + c) * P + k] = t2;
+  }
+  for (int c = t; c < CP; c += 256) {
+    float sq = 0.f;
+    if (c < C)
+      for (int k = 0; k < DC; ++k) sq = fmaf(ch[size_t(c) * DC + k], ch[size_t(c) * DC + k], sq);
+    cn[c] = sq;
+    cnt[c] = 0;
+  }
+  // zero padding columns of the staged rows (never written afterwards)
+  if constexpr (CPR > DC / 8) {
+    constexpr int PADC = CPR - DC / 8;
+    for (int e = t; e < KSTEP_TOK * PADC; e += 256) {
+      const int r = e / PADC, c = DC / 8 + e % PADC;
+      *reinterpret_cast<uint4*>(xs + r * DCP + ((c ^ xswz<CPR>(r)) << 3)) = make_uint4(0, 0, 0, 0);
+    }
+  }
+  __syncthreads();
+  // this wave's (cluster block, column block) pairs of the sums
+  const int npairs = (CP / 32) * NDB;
+  floatx16 acc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.f;
+  // transpose-read offsets: rows 16 ks + 8 j + tr_row share tr_row's swizzle
+  const int tr_row = 4 * hi + ((lane & 15) >> 2);
+  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  int tr_off[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    const int cc = 32 * db + tr_col;
+    tr_off[db] = tr_row * DCP + (((cc >> 3) ^ xswz<CPR>(tr_row)) << 3) + (cc & 7);
+  }
+  const int ntile = (N + KSTEP_TOK - 1) / KSTEP_TOK;
+#pragma unroll 1
+  for (int g = 0; g < G; ++g) {
+    const int tile = blockIdx.x * G + g;
+    if (tile >= ntile) break;  // uniform across the workgroup
+    // assignment of the wave's 32 tokens (as assign_mfma_kernel)
+    const int lr = 32 * w + col;  // row in the group
+    const int tok = tile * KSTEP_TOK + lr;
+    const bool valid = tok < N;
+    const bf16_t* row = x + (size_t(h) * N + (valid ? tok : 0)) * d + col0;
+    bf16x8_t xf[KS];
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      uint4 u = *reinterpret_cast<const uint4*>(row + 16 * s2 + 8 * hi);
+      if (!valid) u = make_uint4(0, 0, 0, 0);
+      xf[s2] = __builtin_bit_cast(bf16x8_t, u);
+      *reinterpret_cast<uint4*>(xs + lr * DCP + (((2 * s2 + hi) ^ xswz<CPR>(lr)) << 3)) = u;
+    }
+    float best = __builtin_huge_valf();
+    int bj = 0x7fffffff;
+    for (int cb = 0; cb < CP; cb += 32) {
+      floatx16 a2;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a2[r] = 0.f;
+#pragma unroll
+      for (int term = 0; term < 3; ++term)
+#pragma unroll
+        for (int s2 = 0; s2 < KS; ++s2) {
+          const uint4 u = *reinterpret_cast<const uint4*>(ct + size_t(term * CP + cb + col) * P + 16 * s2 + 8 * hi);
+          a2 = kmfma(__builtin_bit_cast(bf16x8_t, u), xf[s2], a2);
+        }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = cb + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const float dv = cn[c] - 2.f * a2[r];
+        if (c < C && dv < best) {
+          best = dv;
+          bj = c;
+        }
+      }
+    }
+    const float ob = __shfl_xor(best, 32, 64);
+    const int oj = __shfl_xor(bj, 32, 64);
+    if (ob < best || (ob == best && oj < bj)) bj = oj;
+    if (hi == 0) {
+      lab[lr] = valid ? bj : -1;
+      if (valid) {
+        labels[size_t(h) * N + tok] = bj;
+        atomicAdd(&cnt[bj], 1);
+      }
+    }
+    __syncthreads();
+    // sums: for every 16-token step, the one-hot B operand from the labels of
+    // the lane's 8 tokens (in the order the transpose reads give them)
+#pragma unroll 1
+    for (int ks = 0; ks < KSTEP_TOK / 16; ++ks) {
+      int lv[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lv[e] = lab[16 * ks + 4 * hi + e];
+        lv[4 + e] = lab[16 * ks + 8 + 4 * hi + e];
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int pr = w + 4 * j;
+        if (pr >= npairs) break;  // uniform across the wave
+        const int cb = pr / NDB, db = pr % NDB;
+        const int me = 32 * cb + col;
+        uint32_t bw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          bw[e] = (lv[2 * e] == me ? 0x3F80u : 0u) | (lv[2 * e + 1] == me ? 0x3F800000u : 0u);
+        const uint2 v0 = lds_tr16(xs + tr_off[db] + (16 * ks) * DCP);
+        const uint2 v1 = lds_tr16(xs + tr_off[db] + (16 * ks + 8) * DCP);
+        acc[j] = kmfma(__builtin_bit_cast(bf16x8_t, make_uint4(v0.x, v0.y, v1.x, v1.y)),
+                       __builtin_bit_cast(bf16x8_t, make_uint4(bw[0], bw[1], bw[2], bw[3])), acc[j]);
+      }
+    }
+    __syncthreads();  // the next group overwrites the staged rows and labels
+  }
+  // partials: lane (col, hi) of pair (cb, db) holds the sums of cluster
+  // 32 cb + col over columns 32 db + 8 (r / 4) + 4 hi + r % 4
+  const size_t pb = size_t(h) * gridDim.x + blockIdx.x;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int pr = w + 4 * j;
+    if (pr >= npairs) break;
+    const int cb = pr / NDB, db = pr % NDB;
+    float* dst = psum + (pb * CP + 32 * cb + col) * DC;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int dim = 32 * db + 8 * (r >> 2) + 4 * hi + (r & 3);
+      if (dim < DC) dst[dim] = acc[j][r];
+    }
+  }
+  for (int c = t; c < CP; c += 256) pcnt[pb * CP + c] = cnt[c];
+}
+
+// centroid = (sum of the workgroup partials, in workgroup order) / count;
+// an empty cluster keeps its centroid
+__global__ void kmeans_combine_kernel(const float* __restrict__ psum, const int32_t* __restrict__ pcnt,
+                                      int nblk, int C, int CP, int DC, float* __restrict__ cent) {
+  const int c = blockIdx.x, h = blockIdx.y;
+  for (int dim = threadIdx.x; dim < DC; dim += blockDim.x) {
+    float s2 = 0.f;
+    long long n = 0;
+    for (int b = 0; b < nblk; ++b) {
+      const size_t pb = size_t(h) * nblk + b;
+      s2 += psum[(pb * CP + c) * DC + dim];
+      n += pcnt[pb * CP + c];
+    }
+    if (n > 0) cent[(size_t(h) * C + c) * DC + dim] = s2 / float(n);
+  }
+}
+
 template <typename T>
 __global__ void seed_kernel(const T* __restrict__ x, int d, int col0, int dc, int N, int C,
                             float* __restrict__ c) {
@@ -298,7 +508,61 @@ hipError_t assign_dispatch(const void* x, int d, int col0, int dc, int H, int N,
   }
 }
 
+// Workgroups per head of the fused step: about 1024 in all, but at most one
+// per 4 CP tokens (so the partials, written and read once, move no more bytes
+// than the rows), and whole groups of 128 tokens each.
+void step_geometry(int H, int N, int C, int& nblk, int& G) {
+  const int CP = (C + 31) & ~31;
+  const int ntile = (N + KSTEP_TOK - 1) / KSTEP_TOK;
+  int bh = std::max(1, std::min(ntile, (1024 + H - 1) / H));
+  bh = std::max(1, std::min(bh, N / (4 * CP)));
+  G = (ntile + bh - 1) / bh;
+  nblk = (ntile + G - 1) / G;
+}
+
+template <int DC>
+hipError_t kmeans_step_launch(const void* x, int d, int col0, int H, int N, int C, float* c,
+                              int32_t* labels, float* psum, hipStream_t st) {
+  const int CP = (C + 31) & ~31;
+  int nblk, G;
+  step_geometry(H, N, C, nblk, G);
+  int32_t* pcnt = reinterpret_cast<int32_t*>(psum + size_t(H) * nblk * CP * DC);
+  const size_t lds = size_t(3) * CP * mfma_pitch<DC>() * 2 + size_t(CP) * 4 +
+                     size_t(KSTEP_TOK) * step_dcp<DC>() * 2 + size_t(KSTEP_TOK) * 4 + size_t(CP) * 4;
+  if (lds > 64 * 1024 &&
+      hipFuncSetAttribute((const void*)kmeans_step_kernel<DC>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          int(lds)) != hipSuccess)
+    return hipErrorInvalidValue;
+  kmeans_step_kernel<DC><<<dim3(nblk, H), 256, lds, st>>>((const bf16_t*)x, d, col0, N, C, G, c, labels,
+                                                          psum, pcnt);
+  kmeans_combine_kernel<<<dim3(C, H), std::min(DC, 128), 0, st>>>(psum, pcnt, nblk, C, CP, DC, c);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+bool kmeans_step_supported(int dtype, const void* x, int d, int col0, int dc, int C) {
+  return dtype == SA_BF16 && dc % 16 == 0 && dc <= 128 && assign_mfma_ok(x, d, col0, dc, C);
+}
+
+size_t kmeans_step_scratch(int H, int N, int C, int dc) {
+  int nblk, G;
+  step_geometry(H, N, C, nblk, G);
+  const int CP = (C + 31) & ~31;
+  return size_t(H) * nblk * CP * (size_t(dc) * sizeof(float) + sizeof(int32_t)) + 256;
+}
+
+hipError_t kmeans_step(const void* x, int d, int col0, int dc, int H, int N, int C, float* c,
+                       int32_t* labels, float* scratch, hipStream_t st) {
+  switch (dc) {
+    case 16: return kmeans_step_launch<16>(x, d, col0, H, N, C, c, labels, scratch, st);
+    case 32: return kmeans_step_launch<32>(x, d, col0, H, N, C, c, labels, scratch, st);
+    case 48: return kmeans_step_launch<48>(x, d, col0, H, N, C, c, labels, scratch, st);
+    case 64: return kmeans_step_launch<64>(x, d, col0, H, N, C, c, labels, scratch, st);
+    case 128: return kmeans_step_launch<128>(x, d, col0, H, N, C, c, labels, scratch, st);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 bool kmeans_width_supported(int dc) {
   return dc == 16 || dc == 24 || dc == 32 || dc == 48 || dc == 64 || dc == 128;

@@ -98,7 +98,9 @@ int max_tiles(const sa_problem* p, const sa_cluster_cfg* q) {
 size_t cluster_scratch(const sa_problem* p, const sa_cluster_cfg* c) {
   const int H = p->heads, N = p->n;
   switch (c->method) {
-    case SA_KMEANS: return means_scratch(H, N, c->clusters, p->d) + label_sort_scratch(H, N, c->clusters) + 512;
+    case SA_KMEANS:
+      return std::max(means_scratch(H, N, c->clusters, p->d), kmeans_step_scratch(H, N, c->clusters, p->d)) +
+             label_sort_scratch(H, N, c->clusters) + 512;
     case SA_BISECT: return bisect_scratch(H, N, p->d, c->leaf) + 256;
     case SA_SUBSPACE: {
       Arena a{nullptr, 0, 0};
@@ -109,8 +111,10 @@ size_t cluster_scratch(const sa_problem* p, const sa_cluster_cfg* c) {
       a.get<int32_t>(size_t(H) * N);       // slice perm
       a.get<int32_t>(size_t(H) * (c->clusters + 1));
       size_t ms = 0;
-      for (int s = 0; s < 3; ++s) ms = std::max(ms, means_scratch(H, N, c->clusters, c->sub_dims[s]));
-      a.take(ms);                          // member-mean run sums
+      for (int s = 0; s < 3; ++s)
+        ms = std::max(ms, std::max(means_scratch(H, N, c->clusters, c->sub_dims[s]),
+                                   kmeans_step_scratch(H, N, c->clusters, c->sub_dims[s])));
+      a.take(ms);                          // member-mean run sums or step partials
       return a.used + std::max(label_sort_scratch(H, N, c->clusters),
                                label_sort_scratch(H, N, clusters_of(p, c))) + 256;
     }
@@ -221,8 +225,16 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
   for (int k = 0; k < 3; ++k) out->sub_dims[k] = c->method == SA_SUBSPACE ? c->sub_dims[k] : 0;
   if (c->method == SA_KMEANS) {
     if (c->init == SA_INIT_FIRST) e = kmeans_seed(x, dt, d, 0, d, H, N, C, out->centroids, st);
+    const bool fused = kmeans_step_supported(dt, x, d, 0, d, C);
     for (int it = 0; it < c->iters && e == hipSuccess; ++it) {
       Arena tmp = s;
+      if (fused) {
+        float* ksc = (float*)tmp.take(kmeans_step_scratch(H, N, C, d));
+        e = kmeans_step(x, d, 0, d, H, N, C, out->centroids, out->labels, ksc, st);
+        if (e == hipSuccess && it + 1 == c->iters)
+          e = label_sort(out->labels, out->perm, out->offsets, H, N, C, tmp, st);
+        continue;
+      }
       float* msc = (float*)tmp.take(means_scratch(H, N, C, d));
       e = kmeans_assign(x, dt, d, 0, d, H, N, C, out->centroids, out->labels, st);
       if (e == hipSuccess) e = label_sort(out->labels, out->perm, out->offsets, H, N, C, tmp, st);
@@ -244,7 +256,9 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
     int32_t* sperm = tmp.get<int32_t>(size_t(H) * N);
     int32_t* soff = tmp.get<int32_t>(size_t(H) * (Cs + 1));
     size_t ms = 0;
-    for (int k = 0; k < 3; ++k) ms = std::max(ms, means_scratch(H, N, Cs, c->sub_dims[k]));
+    for (int k = 0; k < 3; ++k)
+      ms = std::max(ms, std::max(means_scratch(H, N, Cs, c->sub_dims[k]),
+                                 kmeans_step_scratch(H, N, Cs, c->sub_dims[k])));
     float* msc = (float*)tmp.take(ms);
     size_t coff = 0;
     int col0 = 0;
@@ -253,8 +267,13 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
       float* cs = sub_c + coff;
       int32_t* lab = sub_labels + size_t(k) * H * N;
       e = kmeans_seed(x, dt, d, col0, ds, H, N, Cs, cs, st);
+      const bool fused = kmeans_step_supported(dt, x, d, col0, ds, Cs);
       for (int it = 0; it < c->iters && e == hipSuccess; ++it) {
         Arena t2 = tmp;
+        if (fused) {
+          e = kmeans_step(x, d, col0, ds, H, N, Cs, cs, lab, msc, st);
+          continue;
+        }
         e = kmeans_assign(x, dt, d, col0, ds, H, N, Cs, cs, lab, st);
         if (e == hipSuccess) e = label_sort(lab, sperm, soff, H, N, Cs, t2, st);
         if (e == hipSuccess)
