@@ -353,21 +353,18 @@ __device__ __forceinline__ bool later(const Boundary& a, const Boundary& b, int 
   return a.key > b.key || (a.key == b.key && a.g > b.g);
 }
 
-__global__ void logsize_kernel(const int32_t* __restrict__ k_off, int C, double* __restrict__ lg,
-                               int32_t* __restrict__ ksz) {
+// keys per combo, from the offsets
+__global__ void sizes_kernel(const int32_t* __restrict__ k_off, int C, int32_t* __restrict__ ksz) {
   const int h = blockIdx.y;
   const int g = blockIdx.x * 256 + threadIdx.x;
   if (g >= C) return;
-  const int sz = k_off[size_t(h) * (C + 1) + g + 1] - k_off[size_t(h) * (C + 1) + g];
-  lg[size_t(h) * C + g] = sz > 0 ? log(double(sz)) : -__builtin_huge_val();
-  ksz[size_t(h) * C + g] = sz;
+  ksz[size_t(h) * C + g] = k_off[size_t(h) * (C + 1) + g + 1] - k_off[size_t(h) * (C + 1) + g];
 }
 
 // The online mode runs twice: pass 0 finds every row's initial boundary and
 // adds its keys to the head's total, keeping the row's logit range and
 // boundary in `state` (5 words per row); pass 1 starts from that state.
-__global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const double* __restrict__ lgs,
-                                                         const int32_t* __restrict__ kszs,
+__global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const int32_t* __restrict__ kszs,
                                                          unsigned long long* __restrict__ acc,
                                                          long long* __restrict__ state, int pass) {
   __shared__ SubRow R;
@@ -406,24 +403,35 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const dou
     for (int o = 32; o > 0; o >>= 1) sdot += __shfl_xor(sdot, o, 64);
     if (lane == 0) R.T[sl][c] = sdot * a.scale;
   }
-  // the same function of the same size as the per-combo table in global memory
   for (int z = t; z < LOGT; z += SUB_T) R.lt[z] = z > 0 ? log(double(z)) : -__builtin_huge_val();
   for (int x = t; x < W; x += SUB_T) R.words[x] = 0u;
   __syncthreads();
   const int32_t* ksz = kszs + size_t(h) * C;  // keys per combo
-  const double* lh = lgs + size_t(h) * C;
   const int Cs2 = Cs * Cs;
   // g / Cs and g / Cs^2 as a multiply by ceil(2^31 / divisor) and a shift:
   // exact for every g < 2^15 and divisor <= 1024 (combos < 32^3)
   const uint32_t m1 = uint32_t(((1ull << 31) + Cs - 1) / Cs);
   const uint32_t m2 = uint32_t(((1ull << 31) + Cs2 - 1) / Cs2);
   // logit of combo g given its size sz; false for an empty combo
+  // (a power-of-two Cs, the usual case, takes shifts and masks instead)
+  const int csh = (Cs & (Cs - 1)) == 0 ? __builtin_ctz(Cs) : -1;
   auto logit_sz = [&](int g, int sz, double& l) -> bool {
     if (sz <= 0) return false;
-    const int q1 = int((uint64_t(uint32_t(g)) * m1) >> 31);
-    const int c0 = int((uint64_t(uint32_t(g)) * m2) >> 31);
-    l = (R.T[0][c0] + R.T[1][q1 - c0 * Cs]) + R.T[2][g - q1 * Cs];
-    if (a.weighted) l += sz < LOGT ? R.lt[sz] : lh[g];
+    int c0, c1, c2;
+    if (csh >= 0) {
+      c0 = g >> (2 * csh);
+      c1 = (g >> csh) & (Cs - 1);
+      c2 = g & (Cs - 1);
+    } else {
+      const int q1 = int((uint64_t(uint32_t(g)) * m1) >> 31);
+      c0 = int((uint64_t(uint32_t(g)) * m2) >> 31);
+      c1 = q1 - c0 * Cs;
+      c2 = g - q1 * Cs;
+    }
+    l = (R.T[0][c0] + R.T[1][c1]) + R.T[2][c2];
+    // (the rare large combo takes ln directly: a select between the LDS table
+    // and a global one would become one flat load waiting on every counter)
+    if (a.weighted) l += sz < LOGT ? R.lt[sz] : log(double(sz));
     return true;
   };
   auto logit = [&](int g, double& l, int& sz) -> bool {
@@ -883,7 +891,6 @@ size_t select_scratch(int H, int Cq, int Ck, int subspace) {
   Arena a{nullptr, 0, 0};
   a.get<unsigned long long>(size_t(H));
   if (subspace) {
-    a.get<double>(size_t(H) * Ck);
     a.get<int32_t>(size_t(H) * Ck);
     a.get<long long>(size_t(H) * Cq * 5);
   } else {
@@ -897,16 +904,15 @@ hipError_t select_run(const SelectArgs& a, Arena& s, hipStream_t st) {
   dim3 g(a.Cq, a.H);
   if (a.subspace) {
     if (a.Cs > 32 || a.Ck != a.Cs * a.Cs * a.Cs) return hipErrorInvalidValue;
-    double* lgs = s.get<double>(size_t(a.H) * a.Ck);
     int32_t* ksz = s.get<int32_t>(size_t(a.H) * a.Ck);
     long long* rstate = s.get<long long>(size_t(a.H) * a.Cq * 5);
-    logsize_kernel<<<dim3(ceil_div(a.Ck, 256), a.H), 256, 0, st>>>(a.k_off, a.Ck, lgs, ksz);
+    sizes_kernel<<<dim3(ceil_div(a.Ck, 256), a.H), 256, 0, st>>>(a.k_off, a.Ck, ksz);
     if (a.online) {
       zero_u64<<<ceil_div(a.H, 256), 256, 0, st>>>(acc, a.H);
-      select_subspace<<<g, SUB_T, 0, st>>>(a, lgs, ksz, acc, rstate, 0);
-      select_subspace<<<g, SUB_T, 0, st>>>(a, lgs, ksz, acc, rstate, 1);
+      select_subspace<<<g, SUB_T, 0, st>>>(a, ksz, acc, rstate, 0);
+      select_subspace<<<g, SUB_T, 0, st>>>(a, ksz, acc, rstate, 1);
     } else {
-      select_subspace<<<g, SUB_T, 0, st>>>(a, lgs, ksz, acc, rstate, 0);
+      select_subspace<<<g, SUB_T, 0, st>>>(a, ksz, acc, rstate, 0);
     }
     return hipGetLastError();
   }
