@@ -485,8 +485,8 @@ struct MfmaLds {
   int rp[RCH + 1];
   int wsum[16];
   int fsh[2];
-  float bias[KT];
   int rowidx[3][KT];  // general path: key row of each position of tile t in [t % 3]
+  float cbias[3][HK];  // compensation: log2-domain bias of the pseudo keys of half j in [j % 3]
 };
 
 // ALIGNED: rows whose ranges are 64-aligned stream whole 64-key blocks (K and
@@ -640,16 +640,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     pv_half(pk, VLb);
     exp_half(s[1], lsc, pk);
     pv_half(pk, VHb);
-  };
-  // scores -> log2-domain logits in place (bias per key)
-  auto to_logits = [&](floatx16 (&s)[2], const float* bias_l2) {
-#pragma unroll
-    for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * kt + 8 * (r >> 2) + 4 * hi + (r & 3);
-        s[kt][r] = s[kt][r] * sl2 + bias_l2[key];
-      }
   };
   auto compute_tile = [&](const bf16_t* Kb, const bf16_t* VLb, const bf16_t* VHb, int nvalid) {
     floatx16 s[2];
@@ -979,37 +969,61 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     const bf16_t* kbh = p.kbh + size_t(h) * p.Ckp * D;
     const bf16_t* kbl = p.kbl + size_t(h) * p.Ckp * D;
     const bf16_t* vbr = p.vbr + size_t(h) * p.Ckp * D;
-    for (int j0 = 0; j0 < p.Ckp; j0 += KT) {
-      __syncthreads();
+    // Pseudo keys in 32-key halves, pipelined: half j + 1 arrives by direct
+    // loads while half j is computed.  Stage j & 1 holds K̄ hi in rows 0..31
+    // and K̄ lo in rows 32..63 of its K buffer, and V̄ in its lower V half.
+    // The biases of half j (-inf where selected or empty) sit in slot j % 3:
+    // written before the barrier that precedes the half's loads, read after
+    // the next one.  A half with no live pseudo key is neither loaded nor
+    // computed.
+    const int cbytes = p.Ckp * D * 2;
+    const int nh = p.Ckp / HK;
+    auto comp_bias = [&](int j) -> int {
       int fin = 0;
-      if (tid < KT) {
-        const int j = j0 + tid;
+      if (tid < HK) {
+        const int jj = j * HK + tid;
         float b = -__builtin_huge_valf();
-        if (j < a.Ck && !((mr[j >> 5] >> (j & 31)) & 1u)) b = p.logsz[size_t(h) * p.Ckp + j];
-        S.bias[tid] = b * LOG2E;
+        if (jj < a.Ck && !((mr[jj >> 5] >> (jj & 31)) & 1u)) b = p.logsz[size_t(h) * p.Ckp + jj];
+        S.cbias[j % 3][tid] = b * LOG2E;
         fin = b != -__builtin_huge_valf();
       }
-      if (!__syncthreads_or(fin)) continue;
+      return fin;
+    };
+    auto issue_comp = [&](int j) {
+      bf16_t* Kd = (j & 1) ? K1 : K0;
+      bf16_t* Vd = (j & 1) ? VL1 : VL0;
+      const uint32_t rb = uint32_t(j * HK) * (D * 2);
 #pragma unroll
-      for (int q = 0; q < CK; ++q) {
-        const int c = tid + 256 * q;
-        const int row = c / DG, kc = c % DG;
-        const size_t ro = size_t(j0 + row) * D + kc * 8;
-        *reinterpret_cast<uint4*>(K0 + toff<DG>(row, kc)) = *reinterpret_cast<const uint4*>(kbh + ro);
-        *reinterpret_cast<uint4*>(K1 + toff<DG>(row, kc)) = *reinterpret_cast<const uint4*>(kbl + ro);
-        *reinterpret_cast<uint4*>((row < HK ? VL0 : VH0) + vtoff<DG>(row & (HK - 1), kc)) =
-            *reinterpret_cast<const uint4*>(vbr + ro);
+      for (int q = 0; q < CH; ++q) {
+        const int sl = (4 * q + w) * 64 + lane;
+        const int r = sl / DG, c = sl % DG;
+        buf_load_lds16(kbh, cbytes, Kd + (4 * q + w) * 512, rb + uint32_t(r * D + ((c ^ swz<DG>(r)) << 3)) * 2);
+        buf_load_lds16(kbl, cbytes, Kd + HK * D + (4 * q + w) * 512,
+                       rb + uint32_t(r * D + ((c ^ swz<DG>(HK + r)) << 3)) * 2);
+        buf_load_lds16(vbr, cbytes, Vd + (4 * q + w) * 512, rb + uint32_t(r * D + ((c ^ vswz<DG>(r)) << 3)) * 2);
       }
-      __syncthreads();
-      floatx16 s[2];
+    };
+    int live = __syncthreads_or(comp_bias(0));  // also: every buffer is free
+    if (live) issue_comp(0);
+    for (int j = 0; j < nh; ++j) {
+      const int fin = j + 1 < nh ? comp_bias(j + 1) : 0;
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of half j
+      const int live_next = __syncthreads_or(fin);
+      if (live_next) issue_comp(j + 1);
+      if (live) {
+        const bf16_t* Kc = (j & 1) ? K1 : K0;
+        floatx16 sc;
+        zero16(sc);
+        qk_half(sc, Kc, 0);  // q . kbar hi
+        qk_half(sc, Kc, 1);  // + q . kbar lo
+        const float* cb = S.cbias[j % 3];
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        zero16(s[kt]);
-        qk_half(s[kt], K0, kt);
-        qk_half(s[kt], K1, kt);
+        for (int r = 0; r < 16; ++r) sc[r] = sc[r] * sl2 + cb[8 * (r >> 2) + 4 * hi + (r & 3)];
+        rescale_to(max_half(sc, 1.f));
+        exp_half(sc, 1.f, pk);
+        pv_half(pk, (j & 1) ? VL1 : VL0);
       }
-      to_logits(s, S.bias);
-      softmax_pv(s, VL0, VH0, 1.f);
+      live = live_next;
     }
   }
 
