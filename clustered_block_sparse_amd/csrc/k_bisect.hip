@@ -965,25 +965,38 @@ __global__ __launch_bounds__(1024) void partition_kernel(TopBufs b, const int32_
   }
   uint32_t mn[2] = {0xFFFFFFFFu, 0xFFFFFFFFu}, mx[2] = {0u, 0u};
   int run_left = 0;
-  for (int base = 0; base < sg.y; base += 1024) {
-    const int i = base + t;
-    const bool valid = i < sg.y;
-    const int p = sg.x + i;
-    const int left = (valid && is_left(kh[p], p, th)) ? 1 : 0;
+  // four consecutive positions per thread and step (their loads overlap);
+  // the scan of the per-thread counts keeps the order stable
+  constexpr int PU = 4;
+  for (int base = 0; base < sg.y; base += PU * 1024) {
+    int lf[PU], cl = 0;
+#pragma unroll
+    for (int u = 0; u < PU; ++u) {
+      const int i = base + PU * t + u;
+      lf[u] = (i < sg.y && is_left(kh[sg.x + i], sg.x + i, th)) ? 1 : 0;
+      cl += lf[u];
+    }
     int tot;
-    const int lpre = block_excl_scan<int>(left, wsum, tot) + run_left;
-    if (valid) {
-      const int np = left ? sg.x + lpre : sg.x + sg.z + (i - lpre);
-      po[np] = pi[p];
-      if constexpr (PRED) {
-        const size_t hn = size_t(h) * b.N;
-        const uint32_t ck = left ? b.keyL[hn + p] : b.keyR[hn + p];
-        b.keys_next[hn + np] = ck;
-        mn[left ? 0 : 1] = min(mn[left ? 0 : 1], ck);
-        mx[left ? 0 : 1] = max(mx[left ? 0 : 1], ck);
-        const int rank = left ? lpre : i - lpre;
-        if (rank < 2) firsts[(left ? 0 : 2) + rank] = p;
+    int lpre = block_excl_scan<int>(cl, wsum, tot) + run_left;
+#pragma unroll
+    for (int u = 0; u < PU; ++u) {
+      const int i = base + PU * t + u;
+      if (i < sg.y) {
+        const int p = sg.x + i;
+        const int left = lf[u];
+        const int np = left ? sg.x + lpre : sg.x + sg.z + (i - lpre);
+        po[np] = pi[p];
+        if constexpr (PRED) {
+          const size_t hn = size_t(h) * b.N;
+          const uint32_t ck = left ? b.keyL[hn + p] : b.keyR[hn + p];
+          b.keys_next[hn + np] = ck;
+          mn[left ? 0 : 1] = min(mn[left ? 0 : 1], ck);
+          mx[left ? 0 : 1] = max(mx[left ? 0 : 1], ck);
+          const int rank = left ? lpre : i - lpre;
+          if (rank < 2) firsts[(left ? 0 : 2) + rank] = p;
+        }
       }
+      lpre += lf[u];
     }
     run_left += tot;
   }
