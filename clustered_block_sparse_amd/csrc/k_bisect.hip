@@ -561,6 +561,17 @@ __global__ __launch_bounds__(256) void delta_kernel(Src2<T> x, TopBufs b, int fi
         mq[e] = mvc[PRED ? 1 : 0][sub * G::EPV + e];
       }
     }
+    // delta = sum w (2 x - m) = 2 (w . x) - w . m: the lane's share of w . m
+    // is a constant of the round, so each element costs one FMA per key
+    float cr = 0.f, cl = 0.f, cq = 0.f;
+#pragma unroll
+    for (int e = 0; e < G::EPV; ++e) {
+      cr = fmaf(wr[e], mr[e], cr);
+      if constexpr (PRED) {
+        cl = fmaf(wl[e], ml[e], cl);
+        cq = fmaf(wq[e], mq[e], cq);
+      }
+    }
     constexpr int STEP = 4 * G::RPW;  // rows per block step
     for (int rb = w * G::RPW; rb < ch.z; rb += U * STEP) {
       int pos[U];
@@ -578,7 +589,8 @@ __global__ __launch_bounds__(256) void delta_kernel(Src2<T> x, TopBufs b, int fi
         unpack_vec<T, G::EPV>(raw[u], v);
         float acc = 0.f;
 #pragma unroll
-        for (int e = 0; e < G::EPV; ++e) acc = fmaf(wr[e], fmaf(2.f, v[e], -mr[e]), acc);
+        for (int e = 0; e < G::EPV; ++e) acc = fmaf(wr[e], v[e], acc);
+        acc = fmaf(2.f, acc, -cr);
 #pragma unroll
         for (int o = 1; o < G::LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
         const int r = rb + u * STEP + rsub;
@@ -592,9 +604,11 @@ __global__ __launch_bounds__(256) void delta_kernel(Src2<T> x, TopBufs b, int fi
           float al = 0.f, aq = 0.f;
 #pragma unroll
           for (int e = 0; e < G::EPV; ++e) {
-            al = fmaf(wl[e], fmaf(2.f, v[e], -ml[e]), al);
-            aq = fmaf(wq[e], fmaf(2.f, v[e], -mq[e]), aq);
+            al = fmaf(wl[e], v[e], al);
+            aq = fmaf(wq[e], v[e], aq);
           }
+          al = fmaf(2.f, al, -cl);
+          aq = fmaf(2.f, aq, -cq);
 #pragma unroll
           for (int o = 1; o < G::LPR; o <<= 1) {
             al += __shfl_xor(al, o, 64);
@@ -1045,7 +1059,7 @@ struct SubShared {
   uint8_t side[SUB_N];
   uint8_t sid[SUB_N];     // batch slot of the active segment owning a position (255: none)
   float cen[MAXS][2][D];
-  float wm[MAXS][2][D];   // per round: c2 - c1 and c1 + c2 of every active segment
+  float wm[MAXS][2][D];   // per round: c2 - c1, and in [1][0..LPR) each lane slice's share of (c2 - c1).(c1 + c2)
   float ssum[MAXS][2][D];
   float wp[SUB_THREADS / 64][2][D];
   int4 seg[MAXS];         // start, n, n_left
@@ -1193,13 +1207,21 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
       for (int it = 0; it < iters; ++it) {
         __syncthreads();
         if (t < A) S.swc[t] = 0;
-        // the round's per-segment difference and sum of the two means (the
-        // delta of every row reads them instead of recomputing them)
+        // the round's per-segment difference of the two means, and each lane
+        // slice's share of w . m (m = c1 + c2): delta = 2 (w . x) - w . m
         for (int i = t; i < A * D; i += SUB_THREADS) {
           const int a = i / D, col = i % D;
-          const float c1 = S.cen[a][0][col], c2 = S.cen[a][1][col];
-          S.wm[a][0][col] = c2 - c1;
-          S.wm[a][1][col] = c1 + c2;
+          S.wm[a][0][col] = S.cen[a][1][col] - S.cen[a][0][col];
+        }
+        for (int i = t; i < A * G::LPR; i += SUB_THREADS) {
+          const int a = i / G::LPR, sb = i % G::LPR;
+          float cs = 0.f;
+#pragma unroll
+          for (int e = 0; e < G::EPV; ++e) {
+            const float c1 = S.cen[a][0][sb * G::EPV + e], c2 = S.cen[a][1][sb * G::EPV + e];
+            cs = fmaf(c2 - c1, c1 + c2, cs);
+          }
+          S.wm[a][1][sb] = cs;
         }
         __syncthreads();
         // delta over every position of a segment still moving
@@ -1223,15 +1245,15 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
               const int a = sl[q] != 255 ? sl[q] : 0;
               float acc = 0.f;
               const float4* w4 = reinterpret_cast<const float4*>(&S.wm[a][0][sub * G::EPV]);
-              const float4* m4 = reinterpret_cast<const float4*>(&S.wm[a][1][sub * G::EPV]);
 #pragma unroll
               for (int e4 = 0; e4 < G::EPV / 4; ++e4) {
-                const float4 wq = w4[e4], mq = m4[e4];
-                acc = fmaf(wq.x, fmaf(2.f, v[4 * e4], -mq.x), acc);
-                acc = fmaf(wq.y, fmaf(2.f, v[4 * e4 + 1], -mq.y), acc);
-                acc = fmaf(wq.z, fmaf(2.f, v[4 * e4 + 2], -mq.z), acc);
-                acc = fmaf(wq.w, fmaf(2.f, v[4 * e4 + 3], -mq.w), acc);
+                const float4 wq = w4[e4];
+                acc = fmaf(wq.x, v[4 * e4], acc);
+                acc = fmaf(wq.y, v[4 * e4 + 1], acc);
+                acc = fmaf(wq.z, v[4 * e4 + 2], acc);
+                acc = fmaf(wq.w, v[4 * e4 + 3], acc);
               }
+              acc = fmaf(2.f, acc, -S.wm[a][1][sub]);
 #pragma unroll
               for (int o = 1; o < G::LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
               if (sl[q] != 255 && sub == 0) S.key[pp[q]] = sortable(acc);
