@@ -1227,6 +1227,11 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
         // delta over every position of a segment still moving
         {
           constexpr int STEP = NW * G::RPW;
+          // the lane's slice of w and its constant, kept while consecutive
+          // rows stay in one segment
+          int ca = -1;
+          float4 wc[G::EPV / 4];
+          float cc = 0.f;
           for (int rb = w * G::RPW; rb < n0; rb += U * STEP) {
             int pp[U], sl[U];
             uint4 raw[U];
@@ -1244,16 +1249,21 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
               unpack_vec<T, G::EPV>(raw[q], v);
               const int a = sl[q] != 255 ? sl[q] : 0;
               float acc = 0.f;
-              const float4* w4 = reinterpret_cast<const float4*>(&S.wm[a][0][sub * G::EPV]);
+              if (a != ca) {
+                const float4* w4 = reinterpret_cast<const float4*>(&S.wm[a][0][sub * G::EPV]);
+#pragma unroll
+                for (int e4 = 0; e4 < G::EPV / 4; ++e4) wc[e4] = w4[e4];
+                cc = S.wm[a][1][sub];
+                ca = a;
+              }
 #pragma unroll
               for (int e4 = 0; e4 < G::EPV / 4; ++e4) {
-                const float4 wq = w4[e4];
-                acc = fmaf(wq.x, v[4 * e4], acc);
-                acc = fmaf(wq.y, v[4 * e4 + 1], acc);
-                acc = fmaf(wq.z, v[4 * e4 + 2], acc);
-                acc = fmaf(wq.w, v[4 * e4 + 3], acc);
+                acc = fmaf(wc[e4].x, v[4 * e4], acc);
+                acc = fmaf(wc[e4].y, v[4 * e4 + 1], acc);
+                acc = fmaf(wc[e4].z, v[4 * e4 + 2], acc);
+                acc = fmaf(wc[e4].w, v[4 * e4 + 3], acc);
               }
-              acc = fmaf(2.f, acc, -S.wm[a][1][sub]);
+              acc = fmaf(2.f, acc, -cc);
 #pragma unroll
               for (int o = 1; o < G::LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
               if (sl[q] != 255 && sub == 0) S.key[pp[q]] = sortable(acc);
