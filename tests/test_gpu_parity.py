@@ -124,7 +124,14 @@ def test_stage_E_select(w):
             assert np.array_equal(init[h].cpu().numpy(), s["n_init"])
 
 
-@pytest.mark.parametrize("w", [TINY, MID_S], ids=lambda w: w.name)
+# cluster counts that are not multiples of 32 (padded centroid blocks of the
+# matrix-core step) at d = 128 and d = 64
+MID_ODD = replace(MID_S, name="mid_small_odd_c", q=replace(MID_S.q, clusters=50), k=replace(MID_S.k, clusters=77))
+TAB_KM = replace(TAB_S, name="tab_small_kmeans", q=wl.ClusterSpec("kmeans", 40, iters=5),
+                 k=wl.ClusterSpec("kmeans", 100, iters=5))
+
+
+@pytest.mark.parametrize("w", [TINY, MID_S, MID_ODD, TAB_KM], ids=lambda w: w.name)
 def test_stage_AB_kmeans_step(w):
     """One assignment + update from given centroids."""
     say(f"[stage A/B] {w.name}")
