@@ -386,6 +386,25 @@ struct RowGeo {
   static constexpr int RPW = 64 / LPR;             // rows per wave step
 };
 
+// Sum over each aligned group of LPR lanes (every lane gets it) by DPP moves
+// inside 16-lane rows: quad_perm [1,0,3,2] and [2,3,0,1], then the half-row
+// and row mirrors (a shuffle would go through the LDS crossbar); groups wider
+// than a row add the rows by shuffles.
+template <int DPPC>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), DPPC, 0xF, 0xF, false));
+}
+template <int LPR>
+__device__ __forceinline__ float row_sum(float v) {
+  if constexpr (LPR >= 2) v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  if constexpr (LPR >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  if constexpr (LPR >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+  if constexpr (LPR >= 16) v += dpp_f<0x140>(v); // row_mirror
+  if constexpr (LPR >= 32) v += __shfl_xor(v, 16, 64);
+  if constexpr (LPR >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 template <typename T, int EPV>
 __device__ __forceinline__ void unpack_vec(uint4 u, float (&v)[EPV]) {
   if constexpr (sizeof(T) == 4) {
@@ -591,8 +610,7 @@ __global__ __launch_bounds__(256) void delta_kernel(Src2<T> x, TopBufs b, int fi
 #pragma unroll
         for (int e = 0; e < G::EPV; ++e) acc = fmaf(wr[e], v[e], acc);
         acc = fmaf(2.f, acc, -cr);
-#pragma unroll
-        for (int o = 1; o < G::LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
+        acc = row_sum<G::LPR>(acc);
         const int r = rb + u * STEP + rsub;
         const uint32_t key = sortable(acc);
         if (r < ch.z) {
@@ -609,11 +627,8 @@ __global__ __launch_bounds__(256) void delta_kernel(Src2<T> x, TopBufs b, int fi
           }
           al = fmaf(2.f, al, -cl);
           aq = fmaf(2.f, aq, -cq);
-#pragma unroll
-          for (int o = 1; o < G::LPR; o <<= 1) {
-            al += __shfl_xor(al, o, 64);
-            aq += __shfl_xor(aq, o, 64);
-          }
+          al = row_sum<G::LPR>(al);
+          aq = row_sum<G::LPR>(aq);
           if (r < ch.z && sub == 0) {
             b.keyL[size_t(h) * b.N + ch.y + pos[u]] = sortable(al);
             b.keyR[size_t(h) * b.N + ch.y + pos[u]] = sortable(aq);
@@ -1264,8 +1279,7 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
                 acc = fmaf(wc[e4].w, v[4 * e4 + 3], acc);
               }
               acc = fmaf(2.f, acc, -cc);
-#pragma unroll
-              for (int o = 1; o < G::LPR; o <<= 1) acc += __shfl_xor(acc, o, 64);
+              acc = row_sum<G::LPR>(acc);
               if (sl[q] != 255 && sub == 0) S.key[pp[q]] = sortable(acc);
             }
           }
