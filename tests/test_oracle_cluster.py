@@ -6,12 +6,16 @@ balanced bisection to its size law, to separated blobs and to a brute-force
 optimum of the balanced split; the permutation to bijection/stability laws."""
 
 import itertools
+import json
+import os
 
 import numpy as np
 import pytest
 import scipy.cluster.vq as vq
 
 import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 
 def smooth_points(rng, n, d):
@@ -70,9 +74,94 @@ def test_kmeans_empty_cluster_keeps_centroid():
     assert r2["sizes"].tolist() == [1, 2, 2]
 
 
+def test_kmeans_empty_cluster_keeps_nonzero_centroid():
+    """An empty cluster keeps its previous (non-zero) centroid, so it can win
+    tokens back in the next round.  Hand derivation (first-k seeding):
+    round 1: c = (1,1), (1,1), (5,5); every tie goes to the lower index, so
+    cluster 1 is empty and keeps (1,1); c0 = mean of (1,1),(1,1),(1.5,1) =
+    (7/6, 1), c2 = (5.25, 5).  Round 2: the two (1,1) tokens are at 0 from c1
+    and 1/36 from c0, so they move to cluster 1; (1.5,1) is 1/9 from c0 and
+    1/4 from c1 and stays.  A centroid reset to the origin instead would be 2
+    away from (1,1) and cluster 1 would stay empty."""
+    x = np.array([[1.0, 1.0], [1.0, 1.0], [5.0, 5.0], [5.5, 5.0], [1.5, 1.0]])
+    r = oracle.kmeans(x, 3, 1)
+    assert r["labels"].tolist() == [0, 0, 2, 2, 0] and r["sizes"].tolist() == [3, 0, 2]
+    np.testing.assert_array_equal(r["centroids"][1], [1.0, 1.0])
+    np.testing.assert_allclose(r["centroids"][0], [7.0 / 6.0, 1.0], rtol=0, atol=1e-15)
+    r2 = oracle.kmeans(x, 3, 2)
+    assert r2["labels"].tolist() == [1, 1, 2, 2, 0] and r2["sizes"].tolist() == [1, 2, 2]
+    np.testing.assert_array_equal(r2["centroids"], [[1.5, 1.0], [1.0, 1.0], [5.25, 5.0]])
+
+
 # --------------------------------------------------------------------------
 # bisection
 # --------------------------------------------------------------------------
+
+def test_bisect_worked_example():
+    """Hand-derived two-round bisection on six integer points
+    (tests/golden/bisect_worked_example.json): an odd leaf count at the root,
+    a delta tie across the cut in the last round (a duplicated point) and a
+    second round whose split differs from the first."""
+    with open(os.path.join(GOLDEN, "bisect_worked_example.json")) as f:
+        g = json.load(f)
+    x = np.array(g["points"], dtype=np.float64)
+    r = oracle.bisect(x, g["leaf"], g["iters"])
+    leaves = [r["perm"][r["offsets"][j]:r["offsets"][j + 1]].tolist() for j in range(len(r["offsets"]) - 1)]
+    assert leaves == g["expected_leaves"]
+    assert r["labels"].tolist() == g["expected_labels"]
+    assert r["offsets"].tolist() == g["expected_offsets"]
+    assert len(r["nodes"]) == len(g["expected_nodes"])
+    for node, want in zip(r["nodes"], g["expected_nodes"]):
+        assert node.members.tolist() == want["members"]
+        assert node.n_left == want["n_left"]
+        assert node.left.tolist() == want["left"]
+        np.testing.assert_array_equal(node.c1, want["c1"])
+        np.testing.assert_array_equal(node.c2, want["c2"])
+    # the first round alone, from the seeds x[0], x[1]
+    r1 = g["expected_root_round1"]
+    left, c1, c2, _ = oracle.bisect_split(x, np.arange(len(x)), 4, x[0].copy(), x[1].copy(), 1)
+    assert np.nonzero(left)[0].tolist() == r1["left"]
+    np.testing.assert_array_equal(c1, r1["c1"])
+    np.testing.assert_array_equal(c2, r1["c2"])
+
+
+def test_bisect_split_rounds_compose(rng):
+    """T rounds of the split rule = T-1 rounds followed by one round from the
+    means they return; the returned means are the means of the returned
+    sides; every round's split is a minimum-cost balanced assignment for the
+    means it started from (brute force)."""
+    for trial in range(12):
+        n = int(rng.integers(5, 12))
+        n_left = int(rng.integers(1, n))
+        x = rng.normal(size=(n, 3))
+        x[int(rng.integers(0, n))] = x[0]  # a duplicate: a delta tie every round
+        members = np.arange(n)
+        c1, c2 = x[0].copy(), x[1].copy()
+        for T in range(1, 5):
+            left_T, a_T, b_T, _ = oracle.bisect_split(x, members, n_left, x[0].copy(), x[1].copy(), T)
+            np.testing.assert_allclose(a_T, x[left_T].mean(0), rtol=0, atol=1e-14)
+            np.testing.assert_allclose(b_T, x[~left_T].mean(0), rtol=0, atol=1e-14)
+            one, a1, b1, _ = oracle.bisect_split(x, members, n_left, c1.copy(), c2.copy(), 1)
+            assert np.array_equal(one, left_T)
+            d1 = ((x - c1) ** 2).sum(1)
+            d2 = ((x - c2) ** 2).sum(1)
+            best = min(d1[list(S)].sum() + d2.sum() - d2[list(S)].sum()
+                       for S in itertools.combinations(range(n), n_left))
+            assert d1[one].sum() + d2[~one].sum() <= best + 1e-12
+            c1, c2 = a1, b1
+
+
+def test_bisect_left_child_takes_the_larger_half():
+    """The root's left child takes L*ceil(c/2) tokens, the larger half for an
+    odd leaf count c: N = 5L (c = 5) sends 3L left, N = 5L + 3 (c = 6) 3L,
+    N = 3L + 1 (c = 4) 2L."""
+    rng = np.random.default_rng(7)
+    for N, L in [(5 * 8 + 3, 8), (5 * 8, 8), (3 * 16 + 1, 16)]:
+        x = rng.normal(size=(N, 4))
+        r = oracle.bisect(x, L, 2)
+        c = -(-N // L)
+        assert r["nodes"][0].n_left == L * ((c + 1) // 2)
+        assert r["nodes"][0].start == 0 and r["nodes"][0].n == N
 
 @pytest.mark.parametrize("N,L", [(1000, 128), (256, 128), (300, 64), (129, 128), (128, 128), (77, 8)])
 def test_bisect_size_law(rng, N, L):
