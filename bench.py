@@ -21,8 +21,8 @@ block-sparse attention (+ compensation, + unpermute).  Inputs are resident in
 HBM before timing starts.  Prints one JSON line: the headline metric
 (effective sparse-attention TFLOP/s over the whole step), ms per layer, a
 per-stage breakdown, the dense comparison, the attention kernels' roofline
-figure (their own duration, from HIP events the library records around them
-on the launch stream) and the oracle's CPU timing on a bounded sample.
+figure (their own duration, from HIP events that each timed call's attention
+configuration asks the library to record around them on the launch stream) and the oracle's CPU timing on a bounded sample.
 `--copy-probe` finishes with three 1 GiB device copies of known size, the
 calibration for hardware byte counters.
 
@@ -215,20 +215,21 @@ def main():
     for i in range(args.warmup):
         evict(i)
         step()
+    # each timed step records its own pair of events around the attention
+    # kernels (passed in that step's attention configuration)
     probes = [(L.HipEvent(), L.HipEvent()) for _ in range(args.steps)]
+    timed_ac = [L.attn_cfg(ac.compensate, ac.scale, events=pr) for pr in probes]
     step_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         evict(i)
-        L.sa_set_attn_events(*probes[i])
         step_ev[i][0].record()
-        step()
+        L.sa_forward(p, qc, kc, sc, timed_ac[i], q, k, v, o, mask, ws)
         step_ev[i][1].record()
     torch.cuda.synchronize()
     ms_wall = (time.perf_counter() - t0) * 1e3 / args.steps
-    L.sa_set_attn_events(None, None)
     attn_kernel_ms = [a.elapsed_ms(b) for a, b in probes]
     step_ms = [a.elapsed_time(b) for a, b in step_ev]
     ms_step = float(np.mean(step_ms)) if args.cold else ms_wall

@@ -44,7 +44,8 @@ class SelectCfg(ctypes.Structure):
 
 
 class AttnCfg(ctypes.Structure):
-    _fields_ = [("compensate", I32), ("scale", ctypes.c_float)]
+    _fields_ = [("compensate", I32), ("scale", ctypes.c_float), ("ev_start", ctypes.c_void_p),
+                ("ev_stop", ctypes.c_void_p)]
 
 
 class Clusters(ctypes.Structure):
@@ -80,18 +81,17 @@ def load():
     lib.sa_cluster.argtypes = [P(Problem), P(ClusterCfg), vp, P(Clusters), vp, ctypes.c_size_t, vp]
     lib.sa_cluster_qk.argtypes = [P(Problem), P(ClusterCfg), P(ClusterCfg), vp, vp, P(Clusters), P(Clusters),
                                   vp, ctypes.c_size_t, vp]
-    lib.sa_permute.argtypes = [P(Problem), P(Clusters), vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.sa_permute.argtypes = [P(Problem), P(Clusters), vp, vp, vp, vp]
     lib.sa_select.argtypes = [P(Problem), P(SelectCfg), P(Clusters), P(Clusters), vp, vp, vp, vp, vp,
                               ctypes.c_size_t, vp]
     lib.sa_block_sparse_attn.argtypes = [P(Problem), P(AttnCfg), P(Clusters), P(Clusters), vp, vp, vp, vp,
                                          vp, ctypes.c_size_t, vp]
     lib.sa_forward.argtypes = [P(Problem), P(ClusterCfg), P(ClusterCfg), P(SelectCfg), P(AttnCfg), vp, vp,
                                vp, vp, vp, vp, ctypes.c_size_t, vp]
-    lib.sa_set_attn_events.argtypes = [vp, vp]
     lib.sa_status_string.argtypes = [I32]
     lib.sa_status_string.restype = ctypes.c_char_p
     for fn in ("sa_workspace_size", "sa_cluster", "sa_cluster_qk", "sa_permute", "sa_select",
-               "sa_block_sparse_attn", "sa_forward", "sa_set_attn_events"):
+               "sa_block_sparse_attn", "sa_forward"):
         getattr(lib, fn).restype = I32
     _lib = lib
     return lib
@@ -121,8 +121,12 @@ def select_cfg(top_p=0.9, topk_floor=1, online_topk=False, size_weighted=True) -
     return SelectCfg(float(top_p), int(topk_floor), int(bool(online_topk)), int(bool(size_weighted)))
 
 
-def attn_cfg(compensate=False, scale=0.0) -> AttnCfg:
-    return AttnCfg(int(bool(compensate)), float(scale))
+def attn_cfg(compensate=False, scale=0.0, events=None) -> AttnCfg:
+    """events: optional (start, stop) HipEvent pair recorded around the
+    attention kernels of the calls made with this configuration."""
+    start, stop = events if events is not None else (None, None)
+    return AttnCfg(int(bool(compensate)), float(scale), start.handle if start else None,
+                   stop.handle if stop else None)
 
 
 def _ptr(t):
@@ -211,11 +215,10 @@ def sa_cluster_qk(p: Problem, qcfg: ClusterCfg, kcfg: ClusterCfg, q: torch.Tenso
     return qout, kout
 
 
-def sa_permute(p: Problem, c: ClusterTensors, x: torch.Tensor, x_perm: torch.Tensor, means=None,
-               ws: torch.Tensor | None = None):
+def sa_permute(p: Problem, c: ClusterTensors, x: torch.Tensor, x_perm: torch.Tensor, means=None):
     s = c.struct()
     _check("sa_permute", load().sa_permute(ctypes.byref(p), ctypes.byref(s), _ptr(x), _ptr(x_perm),
-                                           _ptr(means), _ptr(ws), 0 if ws is None else ws.numel(), _stream()))
+                                           _ptr(means), _stream()))
 
 
 def sa_select(p: Problem, cfg: SelectCfg, q: ClusterTensors, k: ClusterTensors, mask, counts, init_counts,
@@ -240,14 +243,9 @@ def sa_forward(p: Problem, qcfg: ClusterCfg, kcfg: ClusterCfg, scfg: SelectCfg, 
                                            _ptr(o), _ptr(mask), _ptr(ws), ws.numel(), _stream()))
 
 
-def sa_set_attn_events(start: "HipEvent | None", stop: "HipEvent | None"):
-    _check("sa_set_attn_events", load().sa_set_attn_events(start.handle if start else None,
-                                                           stop.handle if stop else None))
-
-
 class HipEvent:
     """A raw hipEvent_t of the HIP runtime this process already runs (the one
-    libsa.so and torch share), for sa_set_attn_events."""
+    libsa.so and torch share), for the timing events of attn_cfg."""
 
     _hip = None
 

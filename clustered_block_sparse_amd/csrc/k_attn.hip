@@ -21,7 +21,8 @@
 // stream whole 64-key blocks of K and V rows by direct buffer-to-LDS loads.
 // Other rows (and SCOPE's key combos) gather their key rows one by one:
 // before each tile one wave lists the key row of each position, and the K and
-// V rows are staged through registers.
+// V rows then arrive by direct buffer-to-LDS loads too, each lane's source
+// offset taken from the listed row of the slot it fills.
 //
 // bf16 path: 4 waves x 32 query rows.  S^T = K Q^T on 32x32x16 bf16 MFMA so
 // every lane owns one query column and keeps the online-softmax state in
@@ -1100,15 +1101,6 @@ size_t attn_scratch(int H, int N, int d, int Cq, int Ck, int tile_rows, int comp
   return s.used;
 }
 
-namespace {
-hipEvent_t g_probe_start = nullptr, g_probe_stop = nullptr;
-}
-
-void attn_set_probe(hipEvent_t start, hipEvent_t stop) {
-  g_probe_start = start;
-  g_probe_stop = stop;
-}
-
 hipError_t attn_run(const AttnArgs& a, Arena& s, hipStream_t st) {
   const Prep p = carve(a, s);
   if (p.Rmax)
@@ -1122,8 +1114,8 @@ hipError_t attn_run(const AttnArgs& a, Arena& s, hipStream_t st) {
                                                        p.kbh, p.kbl, p.vbr, p.kbf, p.vbf, p.logsz);
   const int grid = 8 * a.H * ceil_div(p.maxT, 8);
   const float sl2 = a.scale * LOG2E;
-  // the probe events bracket the attention kernels only (prep excluded)
-  if (g_probe_start) (void)hipEventRecord(g_probe_start, st);
+  // the caller's timing events bracket the attention kernels only (prep excluded)
+  if (a.ev_start && hipEventRecord(a.ev_start, st) != hipSuccess) return hipErrorInvalidValue;
   if (a.dtype == SA_BF16) {
     if (a.d == 128) {
       if (p.Rmax) attn_mfma<128, true><<<grid, 256, 0, st>>>(a, p, sl2);
@@ -1138,8 +1130,9 @@ hipError_t attn_run(const AttnArgs& a, Arena& s, hipStream_t st) {
     else
       attn_simple<float, 64><<<grid, 128, 0, st>>>(a, p, a.scale);
   }
-  if (g_probe_stop) (void)hipEventRecord(g_probe_stop, st);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess && a.ev_stop && hipEventRecord(a.ev_stop, st) != hipSuccess) e = hipErrorInvalidValue;
+  return e;
 }
 
 }  // namespace sa

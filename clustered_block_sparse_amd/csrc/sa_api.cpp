@@ -75,6 +75,13 @@ sa_status check_cluster_cfg(const sa_problem* p, const sa_cluster_cfg* c) {
   }
 }
 
+sa_status check_attn_cfg(const sa_attn_cfg* c) {
+  if (!c) return SA_ERR_INVALID_ARG;
+  if (!(c->scale >= 0.f) || !isfinite(c->scale)) return SA_ERR_INVALID_ARG;
+  if ((c->ev_start == nullptr) != (c->ev_stop == nullptr)) return SA_ERR_INVALID_ARG;
+  return SA_OK;
+}
+
 sa_status check_select_cfg(const sa_select_cfg* c) {
   if (!c) return SA_ERR_INVALID_ARG;
   if (!isfinite(c->top_p)) return SA_ERR_INVALID_ARG;
@@ -355,6 +362,8 @@ sa_status do_attn(const sa_problem* p, const sa_attn_cfg* c, const sa_clusters* 
   a.vbar = v_means;
   a.mask = mask;
   a.o = o;
+  a.ev_start = static_cast<hipEvent_t>(c->ev_start);
+  a.ev_stop = static_cast<hipEvent_t>(c->ev_stop);
   Arena tmp = s;
   return hip_status(attn_run(a, tmp, st));
 }
@@ -425,9 +434,7 @@ SA_API sa_status sa_cluster_qk(const sa_problem* p, const sa_cluster_cfg* qcfg,
 }
 
 SA_API sa_status sa_permute(const sa_problem* p, const sa_clusters* c, const void* x, void* x_perm,
-                            float* means, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
+                            float* means, void* stream) {
   sa_status st = check_problem(p);
   if (st != SA_OK) return st;
   if (!clusters_ok(c, false) || !x || !x_perm) return SA_ERR_INVALID_ARG;
@@ -467,7 +474,7 @@ SA_API sa_status sa_block_sparse_attn(const sa_problem* p, const sa_attn_cfg* cf
   if (st != SA_OK) return st;
   if (!cfg || !clusters_ok(q, true) || !clusters_ok(k, true) || !v_perm || !mask || !o || !ws)
     return SA_ERR_INVALID_ARG;
-  if (!(cfg->scale >= 0.f) || !isfinite(cfg->scale)) return SA_ERR_INVALID_ARG;
+  if ((st = check_attn_cfg(cfg)) != SA_OK) return st;
   if (cfg->compensate && !v_means) return SA_ERR_INVALID_ARG;
   if (cfg->compensate && k->method == SA_SUBSPACE) return SA_ERR_UNSUPPORTED;
   const int rows = TILE_MAX;
@@ -488,8 +495,8 @@ SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
   if ((st = check_cluster_cfg(p, qcfg)) != SA_OK) return st;
   if ((st = check_cluster_cfg(p, kcfg)) != SA_OK) return st;
   if ((st = check_select_cfg(scfg)) != SA_OK) return st;
-  if (!acfg || !q || !k || !v || !o || !mask || !ws) return SA_ERR_INVALID_ARG;
-  if (!(acfg->scale >= 0.f) || !isfinite(acfg->scale)) return SA_ERR_INVALID_ARG;
+  if ((st = check_attn_cfg(acfg)) != SA_OK) return st;
+  if (!q || !k || !v || !o || !mask || !ws) return SA_ERR_INVALID_ARG;
   if (qcfg->method == SA_SUBSPACE) return SA_ERR_INVALID_ARG;
   if (qcfg->init != SA_INIT_FIRST || kcfg->init != SA_INIT_FIRST) return SA_ERR_INVALID_ARG;
   if (kcfg->method == SA_SUBSPACE && acfg->compensate) return SA_ERR_UNSUPPORTED;
@@ -509,12 +516,6 @@ SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
     return st;
   return do_attn(p, acfg, &b.q, &b.k, b.v_perm, b.v_means, mask, o, tile_rows(qcfg),
                  max_tiles(p, qcfg), scr, s);
-}
-
-SA_API sa_status sa_set_attn_events(void* start, void* stop) {
-  if ((start == nullptr) != (stop == nullptr)) return SA_ERR_INVALID_ARG;
-  attn_set_probe(static_cast<hipEvent_t>(start), static_cast<hipEvent_t>(stop));
-  return SA_OK;
 }
 
 SA_API const char* sa_status_string(sa_status s) {

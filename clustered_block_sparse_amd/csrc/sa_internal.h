@@ -162,10 +162,11 @@ struct AttnArgs {
   const float* vbar;      // [H][Ck][d] (compensation)
   const uint32_t* mask;   // [H][Cq][W]
   void* o;                // [H][N][d] original order
+  hipEvent_t ev_start;    // recorded right before / after the attention
+  hipEvent_t ev_stop;     // kernels when not null (caller's timing events)
 };
 size_t attn_scratch(int H, int N, int d, int Cq, int Ck, int tile_rows, int compensate, int dtype,
                     int max_tiles);
 hipError_t attn_run(const AttnArgs& a, Arena& scratch, hipStream_t st);
-void attn_set_probe(hipEvent_t start, hipEvent_t stop);
 
 }  // namespace sa

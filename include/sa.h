@@ -102,6 +102,15 @@ typedef struct sa_select_cfg {
 typedef struct sa_attn_cfg {
   int32_t compensate;  /* mean compensation of excluded key clusters [CA] */
   float scale;         /* score scale; 0 = 1/sqrt(d)                      */
+  /* Optional timing events (hipEvent_t passed as void*, created and owned by
+   * the caller), or both NULL.  When set, this call records ev_start on its
+   * stream right before the attention kernels and ev_stop right after them
+   * (the call's preparation kernels and, in sa_forward, clustering and
+   * selection fall outside), so hipEventElapsedTime(ev_start, ev_stop) is
+   * the attention kernels' duration.  Only this call records on them.  One
+   * NULL with one non-NULL is SA_ERR_INVALID_ARG. */
+  void* ev_start;
+  void* ev_stop;
 } sa_attn_cfg;
 
 /* Clustering of one tensor (Q or K).  Every pointer is caller-owned device
@@ -135,7 +144,7 @@ SA_API int32_t sa_num_clusters(const sa_problem* p, const sa_cluster_cfg* cfg);
 
 /* Workspace bytes sufficient for sa_forward with these configurations and
  * for each component call (sa_cluster with qcfg or kcfg, sa_select,
- * sa_permute, sa_block_sparse_attn) on the same problem.  Any cfg may be NULL
+ * sa_block_sparse_attn) on the same problem.  Any cfg may be NULL
  * only if the matching component is never called with that workspace. */
 SA_API sa_status sa_workspace_size(const sa_problem* p, const sa_cluster_cfg* qcfg,
                                    const sa_cluster_cfg* kcfg, const sa_select_cfg* scfg,
@@ -159,9 +168,10 @@ SA_API sa_status sa_cluster_qk(const sa_problem* p, const sa_cluster_cfg* qcfg,
 
 /* Gather rows of x [H, n, d] into the cluster order of `c` (x_perm) and, if
  * `means` is not NULL, write the member mean of every cluster to means
- * f32 [H, C, d] (zeros for an empty cluster).  Used for V. */
+ * f32 [H, C, d] (zeros for an empty cluster).  Used for V (the compensation
+ * of [CA] needs the mean value of every key cluster).  Needs no workspace. */
 SA_API sa_status sa_permute(const sa_problem* p, const sa_clusters* c, const void* x,
-                            void* x_perm, float* means, void* ws, size_t ws_bytes, void* stream);
+                            void* x_perm, float* means, void* stream);
 
 /* Hybrid Top-p / fixed Top-k selection with SCOPE's online per-head Top-k.
  * For each query cluster i: logits l_ij = <qbar_i, kbar_j>*scale (+ ln|K_j|),
@@ -205,17 +215,6 @@ SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
                             const sa_attn_cfg* acfg, const void* q, const void* k,
                             const void* v, void* o, uint32_t* mask, void* ws, size_t ws_bytes,
                             void* stream);
-
-/* Timing probe for benchmarks.  With two hipEvent_t handles (created by the
- * caller, passed as void*), every later sa_block_sparse_attn / sa_forward
- * call records `start` on its stream right before the attention kernels and
- * `stop` right after them (clustering, selection and the attention call's own
- * preparation kernels fall outside), so hipEventElapsedTime(start, stop) is
- * the attention kernels' duration.  NULL, NULL switches it off; one NULL is
- * SA_ERR_INVALID_ARG.  The setting is process-wide and not synchronised:
- * set it from the thread that issues the calls it should cover.  The
- * library never creates, records on its own or destroys these events. */
-SA_API sa_status sa_set_attn_events(void* start, void* stop);
 
 /* Static description of a status code. */
 SA_API const char* sa_status_string(sa_status s);

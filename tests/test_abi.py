@@ -100,7 +100,26 @@ def test_select_and_forward_validation(lib):
     assert r == 1  # subspace is for keys only
 
 
-def test_attn_events_probe_validation(lib):
-    assert lib.sa_set_attn_events(None, FAKE) == 1
-    assert lib.sa_set_attn_events(FAKE, None) == 1
-    assert lib.sa_set_attn_events(None, None) == 0
+def test_attn_timing_events_come_in_pairs(lib):
+    """The optional timing events of the attention configuration are both set
+    or both null; one alone is rejected before any work."""
+    p = L.problem(1, 256, 64, 4, 8, 8, "f32")
+    km = L.cluster_cfg("kmeans", clusters=8)
+    good = L.select_cfg(0.9, 2)
+    for start, stop in ((FAKE, None), (None, FAKE)):
+        a = L.AttnCfg(0, 0.0, start, stop)
+        r = lib.sa_forward(ctypes.byref(p), ctypes.byref(km), ctypes.byref(km), ctypes.byref(good),
+                           ctypes.byref(a), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+        assert r == 1
+        cl = L.Clusters(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0, 0, (L.I32 * 3)(0, 0, 0))
+        r = lib.sa_block_sparse_attn(ctypes.byref(p), ctypes.byref(a), ctypes.byref(cl), ctypes.byref(cl), FAKE,
+                                     None, FAKE, FAKE, FAKE, 1 << 30, None)
+        assert r == 1
+
+
+def test_permute_validation(lib):
+    p = L.problem(1, 256, 64, 4, 8, 8, "f32")
+    cl = L.Clusters(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0, 0, (L.I32 * 3)(0, 0, 0))
+    assert lib.sa_permute(ctypes.byref(p), ctypes.byref(cl), None, FAKE, None, None) == 1
+    assert lib.sa_permute(ctypes.byref(L.problem(1, 256, 96, 4, 8, 8, "f32")), ctypes.byref(cl), FAKE, FAKE,
+                          None, None) == 2
