@@ -86,12 +86,14 @@ def load():
                               ctypes.c_size_t, vp]
     lib.sa_block_sparse_attn.argtypes = [P(Problem), P(AttnCfg), P(Clusters), P(Clusters), vp, vp, vp, vp,
                                          vp, ctypes.c_size_t, vp]
+    lib.sa_block_sparse_attn_noalloc.argtypes = [P(Problem), P(AttnCfg), P(Clusters), P(Clusters), vp, vp, vp,
+                                                 vp, vp]
     lib.sa_forward.argtypes = [P(Problem), P(ClusterCfg), P(ClusterCfg), P(SelectCfg), P(AttnCfg), vp, vp,
                                vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sa_status_string.argtypes = [I32]
     lib.sa_status_string.restype = ctypes.c_char_p
     for fn in ("sa_workspace_size", "sa_cluster", "sa_cluster_qk", "sa_permute", "sa_select",
-               "sa_block_sparse_attn", "sa_forward"):
+               "sa_block_sparse_attn", "sa_block_sparse_attn_noalloc", "sa_forward"):
         getattr(lib, fn).restype = I32
     _lib = lib
     return lib
@@ -234,6 +236,14 @@ def sa_block_sparse_attn(p: Problem, cfg: AttnCfg, q: ClusterTensors, k: Cluster
            load().sa_block_sparse_attn(ctypes.byref(p), ctypes.byref(cfg), ctypes.byref(q.struct()),
                                        ctypes.byref(k.struct()), _ptr(v_perm), _ptr(v_means), _ptr(mask),
                                        _ptr(o), _ptr(ws), ws.numel(), _stream()))
+
+
+def sa_block_sparse_attn_noalloc(p: Problem, cfg: AttnCfg, q: ClusterTensors, k: ClusterTensors, v_perm, v_means,
+                                 mask, o):
+    _check("sa_block_sparse_attn_noalloc",
+           load().sa_block_sparse_attn_noalloc(ctypes.byref(p), ctypes.byref(cfg), ctypes.byref(q.struct()),
+                                               ctypes.byref(k.struct()), _ptr(v_perm), _ptr(v_means), _ptr(mask),
+                                               _ptr(o), _stream()))
 
 
 def sa_forward(p: Problem, qcfg: ClusterCfg, kcfg: ClusterCfg, scfg: SelectCfg, acfg: AttnCfg, q, k, v, o,

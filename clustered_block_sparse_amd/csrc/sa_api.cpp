@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "sa_internal.h"
 
@@ -368,6 +369,34 @@ sa_status do_attn(const sa_problem* p, const sa_attn_cfg* c, const sa_clusters* 
   return hip_status(attn_run(a, tmp, st));
 }
 
+// ---------------------------------------------------------------------------
+// Library-owned attention scratch for sa_block_sparse_attn_noalloc: one array
+// per GPU in the code object, so that entry point allocates nothing.  In host
+// code `scratch` only names the symbol; its device address on the current GPU
+// comes from hipGetSymbolAddress (once per device) and only that address is
+// handed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(SA_NOALLOC_ATTN_SCRATCH_BYTES);
+__device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES];
+
+// device address of the current GPU's scratch array (looked up on first use)
+sa_status device_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return SA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
+
 bool clusters_ok(const sa_clusters* c, bool need_xperm) {
   return c && c->perm && c->offsets && c->centroids && (!need_xperm || c->x_perm) &&
          c->num_clusters >= 1;
@@ -483,6 +512,28 @@ SA_API sa_status sa_block_sparse_attn(const sa_problem* p, const sa_attn_cfg* cf
                                    cfg->compensate, p->dtype, maxt) + 256;
   if (ws_bytes < need) return SA_ERR_WORKSPACE;
   Arena s{(char*)ws, ws_bytes, 0};
+  return do_attn(p, cfg, q, k, v_perm, v_means, mask, o, rows, maxt, s, (hipStream_t)stream);
+}
+
+SA_API sa_status sa_block_sparse_attn_noalloc(const sa_problem* p, const sa_attn_cfg* cfg,
+                                              const sa_clusters* q, const sa_clusters* k,
+                                              const void* v_perm, const float* v_means,
+                                              const uint32_t* mask, void* o, void* stream) {
+  sa_status st = check_problem(p);
+  if (st != SA_OK) return st;
+  if (!cfg || !clusters_ok(q, true) || !clusters_ok(k, true) || !v_perm || !mask || !o)
+    return SA_ERR_INVALID_ARG;
+  if ((st = check_attn_cfg(cfg)) != SA_OK) return st;
+  if (cfg->compensate && !v_means) return SA_ERR_INVALID_ARG;
+  if (cfg->compensate && k->method == SA_SUBSPACE) return SA_ERR_UNSUPPORTED;
+  const int rows = TILE_MAX;
+  const int maxt = p->n / rows + q->num_clusters + 1;
+  const size_t need = attn_scratch(p->heads, p->n, p->d, q->num_clusters, k->num_clusters, rows,
+                                   cfg->compensate, p->dtype, maxt);
+  if (need > NOALLOC_SCRATCH_BYTES) return SA_ERR_WORKSPACE;
+  void* base = nullptr;
+  if ((st = device_scratch(&base)) != SA_OK) return st;
+  Arena s{(char*)base, NOALLOC_SCRATCH_BYTES, 0};
   return do_attn(p, cfg, q, k, v_perm, v_means, mask, o, rows, maxt, s, (hipStream_t)stream);
 }
 

@@ -208,6 +208,27 @@ SA_API sa_status sa_block_sparse_attn(const sa_problem* p, const sa_attn_cfg* cf
                                       const uint32_t* mask, void* o, void* ws, size_t ws_bytes,
                                       void* stream);
 
+/* Bytes of the library-owned scratch of sa_block_sparse_attn_noalloc (one
+ * array per GPU, held from library load until the process ends). */
+#define SA_NOALLOC_ATTN_SCRATCH_BYTES (128u << 20)
+
+/* sa_block_sparse_attn for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): same arguments, same kernels and bit-identical results, but
+ * the scratch comes from a fixed array inside the library (the GPU's own
+ * copy, SA_NOALLOC_ATTN_SCRATCH_BYTES) instead of a caller workspace.  The
+ * caller still passes every input and output.  The call allocates and frees
+ * nothing (no hipMalloc, no library allocation).  A problem whose attention
+ * scratch exceeds the array (roughly H*Cq*(Ck/2+1)*8 bytes of range lists
+ * plus, with compensation, 6*H*Ck*d bytes) returns SA_ERR_WORKSPACE before
+ * any work.  Nothing in the array needs to start at zero: every call writes
+ * what it reads.  All calls on one GPU share its array, so calls that can
+ * overlap on one GPU (two streams, two threads) race: serialise them. */
+SA_API sa_status sa_block_sparse_attn_noalloc(const sa_problem* p, const sa_attn_cfg* cfg,
+                                              const sa_clusters* q, const sa_clusters* k,
+                                              const void* v_perm, const float* v_means,
+                                              const uint32_t* mask, void* o, void* stream);
+
 /* The whole path: cluster Q and K, permute V, select, attend.
  * o dtype [H, n, d] original order; mask as in sa_select. */
 SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
