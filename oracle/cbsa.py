@@ -29,9 +29,17 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-# Near-tie tolerance for decisions taken on floating-point comparisons
-# (relative to the magnitude of the compared quantities).
+# Near-tie tolerance of decisions taken on fp32 evaluations (k-means
+# assignments and bisection splits), relative to the magnitude of the compared
+# quantities: a distance gap below 1e-5 relative may flip under fp32 rounding.
 NEAR_TIE_REL = 1e-5
+# Near-tie tolerances of the selection.  Its logits and masses are evaluated
+# in fp64 on both sides from identical centroids, so only the order of fp64
+# operations separates them: logit gaps below 1e-11 relative (to max(1, |l|))
+# and cumulative masses within 1e-10 of top_p (32768 fp64 or 2^-52
+# fixed-point terms) are the decisions rounding order can change.
+SELECT_TIE_LOGIT_REL = 1e-11
+SELECT_TIE_MASS = 1e-10
 
 
 def _f64(a):
@@ -313,7 +321,25 @@ def _first_reaching(cum, target):
     return int(idx[0]) + 1 if len(idx) else len(cum)
 
 
-def select(logits, units, qsizes, top_p, floor, online_topk):
+def _tie_run(sl, cut):
+    """Ranked positions [a, b) around the boundary before position `cut`
+    whose order is uncertain: the maximal run of consecutive logit gaps within
+    SELECT_TIE_LOGIT_REL that contains the gap at the cut ([cut, cut) if that
+    gap is wide)."""
+    def close(k):  # gap between ranked positions k - 1 and k
+        a, b = sl[k - 1], sl[k]
+        return a - b <= SELECT_TIE_LOGIT_REL * max(1.0, abs(a), abs(b))
+    if not (0 < cut < len(sl)) or not close(cut):
+        return cut, cut
+    a, b = cut - 1, cut + 1
+    while a > 0 and close(a):
+        a -= 1
+    while b < len(sl) and close(b):
+        b += 1
+    return a, b
+
+
+def select(logits, units, qsizes, top_p, floor, online_topk, k_h=None):
     """Per-row selection over one head.
 
     logits [Cq, Ck] (-inf = empty unit), units [Ck] count of each unit
@@ -331,13 +357,19 @@ def select(logits, units, qsizes, top_p, floor, online_topk):
          k_h = ceil(A / sum_i |Q_i|) in exact integers; rows with n_i < k_h
          extend their prefix along the same ranking until the count reaches
          k_h (capped at every non-empty unit); other rows are unchanged.
+         `k_h` given: step 5 runs with that value (a staged comparison, given
+         the other side's k_h).
 
     An empty query cluster (|Q_i| = 0) has no query to serve: it selects
     nothing and counts 0 (reading; it does not enter k_h either way).
 
     Returns a dict with mask [Cq, Ck] bool, n_init, n_final, k_h, prefix
-    lengths, and per-row near-tie flags (boundary mass within 1e-5 of top_p,
-    or a relative logit gap <= 1e-5 at a cut)."""
+    lengths t_init / t_final, the ranking, and per-row near-tie flags with the
+    range of prefix lengths an evaluation in another fp64 operation order may
+    take: [init_lo, init_hi] for the initial prefix, [cut_lo, cut_hi] for the
+    final one (both equal to the prefix length on unflagged rows).  A row is
+    flagged when its Top-p crossing sits within SELECT_TIE_MASS of top_p, or a
+    cut falls inside a run of logits within SELECT_TIE_LOGIT_REL."""
     logits = _f64(logits)
     units = np.asarray(units, dtype=np.int64)
     qsizes = np.asarray(qsizes, dtype=np.int64)
@@ -347,6 +379,8 @@ def select(logits, units, qsizes, top_p, floor, online_topk):
     orders, cum_mass, cum_units, sorted_l = [], [], [], []
     t_init = np.zeros(Cq, dtype=np.int64)
     n_init = np.zeros(Cq, dtype=np.int64)
+    init_lo = np.zeros(Cq, dtype=np.int64)
+    init_hi = np.zeros(Cq, dtype=np.int64)
     near = np.zeros(Cq, dtype=bool)
     for i in range(Cq):
         row = logits[i]
@@ -359,50 +393,73 @@ def select(logits, units, qsizes, top_p, floor, online_topk):
         order = js[o]
         cm = np.cumsum(p[o])
         cu = np.cumsum(units[order])
+        sl = row[order]
+        tp_lo = tp_hi = 0
         if top_p >= 1:
             tp = len(order)
         elif top_p <= 0:
             tp = 0
         else:
             tp = _first_reaching(cm, top_p)
-            # the crossing decision is a near tie when a neighbouring prefix
-            # mass is within tolerance of top_p
-            for t in (tp - 1, tp):
-                if 1 <= t <= len(cm) and abs(cm[t - 1] - top_p) <= NEAR_TIE_REL:
-                    near[i] = True
+            tp_lo = tp_hi = tp
+            # a neighbouring prefix mass within tolerance of top_p: the
+            # crossing may move by one position either way
+            if tp >= 2 and abs(cm[tp - 2] - top_p) <= SELECT_TIE_MASS:
+                tp_lo = tp - 1
+            if abs(cm[tp - 1] - top_p) <= SELECT_TIE_MASS and tp < len(cm):
+                tp_hi = tp + 1
         tf = _first_reaching(cu, floor) if floor > 0 else 0
-        t = max(tp, tf) if qsizes[i] > 0 else 0
-        t_init[i] = t
+        if qsizes[i] > 0:
+            t = max(tp, tf)
+            lo, hi = t, t
+            if 0 < top_p < 1 and tp >= tf:  # the mass decides the cut
+                lo, hi = max(tp_lo, tf), max(tp_hi, tf)
+            # units tied in logit with the ones at a candidate cut
+            a0, _ = _tie_run(sl, lo)
+            _, b1 = _tie_run(sl, hi)
+            lo, hi = min(lo, a0), max(hi, b1)
+        else:
+            t = lo = hi = 0
+        t_init[i], init_lo[i], init_hi[i] = t, lo, hi
         n_init[i] = cu[t - 1] if t > 0 else 0
+        near[i] = (lo, hi) != (t, t)
         orders.append(order)
         cum_mass.append(cm)
         cum_units.append(cu)
-        sorted_l.append(row[order])
+        sorted_l.append(sl)
     # online per-head Top-k
     total = int(qsizes.sum())
     if online_topk:
-        A = int((qsizes * n_init).sum())
-        k_h = -(-A // total) if total > 0 else 0
+        if k_h is None:
+            A = int((qsizes * n_init).sum())
+            k_h = -(-A // total) if total > 0 else 0
+        k_h = int(k_h)
     else:
         k_h = 0
     t_final = t_init.copy()
+    cut_lo = init_lo.copy()
+    cut_hi = init_hi.copy()
     for i in range(Cq):
         if online_topk and n_init[i] < k_h and qsizes[i] > 0:
-            t_final[i] = max(t_init[i], _first_reaching(cum_units[i], k_h))
+            tk = _first_reaching(cum_units[i], k_h)
+            t_final[i] = max(t_init[i], tk)
+            # another evaluation's initial prefix may lie anywhere in
+            # [init_lo, init_hi]; each is extended to tk (whole units) unless
+            # it already reaches k_h
+            a, b = _tie_run(sorted_l[i], tk)
+            lo = max(init_lo[i], min(tk, a))
+            hi = max(init_hi[i], b if b > tk else tk)
+            cut_lo[i], cut_hi[i] = lo, hi
+            near[i] = near[i] or (lo, hi) != (t_final[i], t_final[i])
     mask = np.zeros((Cq, Ck), dtype=bool)
     n_final = np.zeros(Cq, dtype=np.int64)
     for i in range(Cq):
         t = t_final[i]
         mask[i, orders[i][:t]] = True
         n_final[i] = cum_units[i][t - 1] if t > 0 else 0
-        sl = sorted_l[i]
-        for cut in {int(t_init[i]), int(t)}:
-            if 0 < cut < len(sl):
-                a, b = sl[cut - 1], sl[cut]
-                if a - b <= NEAR_TIE_REL * max(1.0, abs(a), abs(b)):
-                    near[i] = True
     return dict(mask=mask, n_init=n_init, n_final=n_final, k_h=k_h, t_init=t_init,
-                t_final=t_final, near_tie=near, orders=orders)
+                t_final=t_final, near_tie=near, orders=orders, init_lo=init_lo, init_hi=init_hi,
+                cut_lo=cut_lo, cut_hi=cut_hi, cum_units=cum_units)
 
 
 # --------------------------------------------------------------------------

@@ -184,3 +184,37 @@ def test_lut_equals_concatenated_representative(rng):
                 assert lut[i, g] == -np.inf
             else:
                 assert abs(lut[i, g] - (0.25 * np.dot(qbar[i], rep) + math.log(sizes[g]))) < 1e-12
+
+
+def test_near_tie_cut_ranges():
+    """A cut inside a run of equal logits is flagged and its range covers
+    every equal unit; a cut with a clear gap is exact (range = the cut)."""
+    one = np.ones(5, np.int64)
+    # units 1 and 3 share a logit across the floor-2 cut: either may be second
+    lg = np.log(np.array([[0.4, 0.2, 0.1, 0.2, 0.1]]))
+    r = oracle.select(lg, one, [3], 0.0, 2, False)
+    assert r["near_tie"][0] and r["t_final"][0] == 2
+    assert r["cut_lo"][0] == 1 and r["cut_hi"][0] == 3
+    assert set(r["orders"][0][:3].tolist()) == {0, 1, 3}
+    # a clear gap at the cut
+    lg2 = np.log(np.array([[0.4, 0.3, 0.1, 0.15, 0.05]]))
+    r2 = oracle.select(lg2, one, [3], 0.0, 2, False)
+    assert not r2["near_tie"][0] and r2["cut_lo"][0] == r2["cut_hi"][0] == 2
+    # Top-p crossing exactly at a prefix mass (0.4 + 0.3 = 0.7 with P = 0.7):
+    # an evaluation in another order may need one unit more
+    r3 = oracle.select(np.log(np.array([[0.4, 0.3, 0.2, 0.1]])), np.ones(4, np.int64), [3], 0.7, 1, False)
+    assert r3["near_tie"][0] and r3["t_final"][0] == 2 and (r3["cut_lo"][0], r3["cut_hi"][0]) == (2, 3)
+
+
+def test_given_head_topk():
+    """select(..., k_h=k) runs the online extension with k instead of its own
+    estimate: rows below k extend to k, the others are unchanged."""
+    rng = np.random.default_rng(5)
+    lg = rng.normal(size=(6, 12))
+    qs = np.array([5, 9, 3, 7, 2, 8])
+    own = oracle.select(lg, np.ones(12, np.int64), qs, 0.5, 1, True)
+    for k in (own["k_h"], own["k_h"] + 2, 1):
+        r = oracle.select(lg, np.ones(12, np.int64), qs, 0.5, 1, True, k_h=k)
+        assert r["k_h"] == k
+        assert np.array_equal(r["n_init"], own["n_init"])
+        assert np.array_equal(r["n_final"], np.maximum(own["n_init"], k))
