@@ -39,7 +39,7 @@ class ClusterCfg(ctypes.Structure):
 
 
 class SelectCfg(ctypes.Structure):
-    _fields_ = [("top_p", ctypes.c_float), ("topk_floor", I32), ("online_topk", I32),
+    _fields_ = [("top_p", ctypes.c_double), ("topk_floor", I32), ("online_topk", I32),
                 ("size_weighted", I32)]
 
 

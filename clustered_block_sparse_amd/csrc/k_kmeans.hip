@@ -446,6 +446,21 @@ __global__ void expand_kernel(const float* __restrict__ sub, int H, int Cs, int 
   }
 }
 
+// inverse of expand_kernel: the slice columns of each expanded row back into
+// the compact blocks [3][H][Cs][d_s]
+__global__ void compact_kernel(const float* __restrict__ in, int H, int Cs, int d, int d0, int d1, int d2,
+                               float* __restrict__ sub) {
+  const int h = blockIdx.y, row = blockIdx.x;  // row in [0, 3*Cs)
+  const int s = row / Cs, c = row % Cs;
+  const int ds[3] = {d0, d1, d2};
+  const int off[3] = {0, d0, d0 + d1};
+  size_t base = 0;
+  for (int q = 0; q < s; ++q) base += size_t(H) * Cs * ds[q];
+  float* dst = sub + base + (size_t(h) * Cs + c) * ds[s];
+  const float* src = in + (size_t(h) * 3 * Cs + row) * d + off[s];
+  for (int t = threadIdx.x; t < ds[s]; t += blockDim.x) dst[t] = src[t];
+}
+
 template <typename T, int DC>
 hipError_t assign_launch(const void* x, int d, int col0, int H, int N, int C, const float* c,
                          int32_t* labels, hipStream_t st) {
@@ -593,6 +608,12 @@ hipError_t combo_labels(const int32_t* sub_labels, int32_t* labels, int H, int N
 hipError_t expand_sub_centroids(const float* sub, int H, int Cs, int d, const int* dims, float* out,
                                 hipStream_t st) {
   expand_kernel<<<dim3(3 * Cs, H), 128, 0, st>>>(sub, H, Cs, d, dims[0], dims[1], dims[2], out);
+  return hipGetLastError();
+}
+
+hipError_t compact_sub_centroids(const float* expanded, int H, int Cs, int d, const int* dims, float* sub,
+                                 hipStream_t st) {
+  compact_kernel<<<dim3(3 * Cs, H), 128, 0, st>>>(expanded, H, Cs, d, dims[0], dims[1], dims[2], sub);
   return hipGetLastError();
 }
 

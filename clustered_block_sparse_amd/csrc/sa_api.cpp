@@ -63,7 +63,6 @@ sa_status check_cluster_cfg(const sa_problem* p, const sa_cluster_cfg* c) {
     case SA_SUBSPACE: {
       if (c->clusters < 1 || c->clusters > SUB_MAX) return SA_ERR_INVALID_ARG;
       if (c->clusters > p->n) return SA_ERR_SHAPE;
-      if (c->init != SA_INIT_FIRST) return SA_ERR_INVALID_ARG;
       int sum = 0;
       for (int s = 0; s < 3; ++s) {
         if (!kmeans_width_supported(c->sub_dims[s])) return SA_ERR_UNSUPPORTED;
@@ -86,7 +85,7 @@ sa_status check_attn_cfg(const sa_attn_cfg* c) {
 sa_status check_select_cfg(const sa_select_cfg* c) {
   if (!c) return SA_ERR_INVALID_ARG;
   if (!isfinite(c->top_p)) return SA_ERR_INVALID_ARG;
-  if (c->top_p <= 0.f && c->topk_floor <= 0) return SA_ERR_INVALID_ARG;
+  if (c->top_p <= 0.0 && c->topk_floor <= 0) return SA_ERR_INVALID_ARG;
   return SA_OK;
 }
 
@@ -268,13 +267,16 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
       ms = std::max(ms, std::max(means_scratch(H, N, Cs, c->sub_dims[k]),
                                  kmeans_step_scratch(H, N, Cs, c->sub_dims[k])));
     float* msc = (float*)tmp.take(ms);
+    // SA_INIT_GIVEN: every slice starts from the centroids already in
+    // out->centroids (expanded layout)
+    if (c->init == SA_INIT_GIVEN) e = compact_sub_centroids(out->centroids, H, Cs, d, c->sub_dims, sub_c, st);
     size_t coff = 0;
     int col0 = 0;
     for (int k = 0; k < 3 && e == hipSuccess; ++k) {
       const int ds = c->sub_dims[k];
       float* cs = sub_c + coff;
       int32_t* lab = sub_labels + size_t(k) * H * N;
-      e = kmeans_seed(x, dt, d, col0, ds, H, N, Cs, cs, st);
+      if (c->init == SA_INIT_FIRST) e = kmeans_seed(x, dt, d, col0, ds, H, N, Cs, cs, st);
       const bool fused = kmeans_step_supported(dt, x, d, col0, ds, Cs);
       for (int it = 0; it < c->iters && e == hipSuccess; ++it) {
         Arena t2 = tmp;

@@ -118,6 +118,9 @@ hipError_t combo_labels(const int32_t* sub_labels, int32_t* labels, int H, int N
 // centroids [H][3*Cs][d]: row s*Cs+c = slice s centroid in its columns, zeros elsewhere
 hipError_t expand_sub_centroids(const float* sub, int H, int Cs, int d, const int* dims,
                                 float* out, hipStream_t st);
+// inverse: compact blocks [3][H][Cs][d_s] from the expanded layout
+hipError_t compact_sub_centroids(const float* expanded, int H, int Cs, int d, const int* dims, float* sub,
+                                 hipStream_t st);
 
 // k_bisect.hip ---------------------------------------------------------------
 size_t bisect_scratch(int H, int N, int d, int leaf);

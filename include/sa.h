@@ -85,13 +85,15 @@ typedef struct sa_cluster_cfg {
   int32_t tile_cap;    /* upper bound on query rows per attention tile (tiling
                           only, never changes results; 0 = 128)                    */
   int32_t iters;       /* rounds per k-means run / per bisection node (>= 1)        */
-  int32_t init;        /* KMEANS: SA_INIT_FIRST, or SA_INIT_GIVEN = start from the
-                          centroids already in out->centroids                      */
+  int32_t init;        /* KMEANS / SUBSPACE: SA_INIT_FIRST, or SA_INIT_GIVEN = start
+                          from the centroids already in out->centroids (SUBSPACE:
+                          the expanded [3*clusters, d] layout below)               */
   int32_t sub_dims[3]; /* SUBSPACE column widths (t, h, w), summing to d            */
 } sa_cluster_cfg;
 
 typedef struct sa_select_cfg {
-  float top_p;          /* cumulative proxy mass to reach (>= 1: all non-empty) */
+  double top_p;         /* cumulative proxy mass to reach (>= 1: all non-empty);
+                           double, so a configured 0.9 is compared as 0.9      */
   int32_t topk_floor;   /* fixed Top-k minimum in units (clusters; keys in
                            SUBSPACE mode); top_p <= 0 with floor <= 0 is invalid */
   int32_t online_topk;  /* SCOPE online per-head Top-k on/off                    */

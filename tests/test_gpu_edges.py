@@ -26,7 +26,8 @@ from clustered_block_sparse_amd import _lib as L
 from clustered_block_sparse_amd import api
 from clustered_block_sparse_amd import workloads as wl
 
-from gpu_helpers import DEV, WAN_S, assert_attn_close, inputs, say, scale_of, to_np, unpack_mask, workspace_for
+from gpu_helpers import (DEV, WAN_S, assert_attn_close, check_selection_head, inputs, say, scale_of, to_np,
+                         unpack_mask, workspace_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,11 +93,15 @@ def test_edge_case(w):
         ksz = np.diff(kt.offsets[h].cpu().numpy())
         qsz = np.diff(qt.offsets[h].cpu().numpy())
         lg = oracle.cluster_logits(qbar, kt.centroids[h].double().cpu().numpy(), ksz, scale_of(w), w.size_weighted)
-        s = oracle.select(lg, np.ones(Ck, np.int64), qsz, w.top_p, w.floor, w.online_topk)
-        bad = np.nonzero((gm[h] != s["mask"]).any(axis=1))[0]
-        say(f"  head {h}: {Cq} x {Ck} clusters, selected {int(gm[h].sum())}, rows differing {len(bad)} "
-            f"(flagged near ties {int(s['near_tie'].sum())})")
-        assert all(s["near_tie"][i] for i in bad)
+        units = np.ones(Ck, np.int64)
+
+        def redo(kh, lg=lg, qsz=qsz):
+            return oracle.select(lg, units, qsz, w.top_p, w.floor, w.online_topk, k_h=kh)
+
+        s = oracle.select(lg, units, qsz, w.top_p, w.floor, w.online_topk)
+        say(f"  head {h}: {Cq} x {Ck} clusters, selected {int(gm[h].sum())}")
+        check_selection_head(gm[h], counts[h].cpu().numpy(), None, ktop[h], s, redo, qsz, w.n, w.online_topk,
+                             f"{w.name} head {h}")
         every &= bool(gm[h].all())
         ref = oracle.attention(qs[h], ks[h], vs[h], qt.perm[h].cpu().numpy(), qt.offsets[h].cpu().numpy(),
                                kt.perm[h].cpu().numpy(), kt.offsets[h].cpu().numpy(), gm[h], scale_of(w),
