@@ -6,7 +6,12 @@ HIP path.  See oracle/cbsa.py for the functions and the passages they follow.
 """
 
 from .cbsa import (  # noqa: F401
+    DOMAIN_GROUP,
+    DOMAIN_HEAD,
+    DOMAIN_ROW,
     NEAR_TIE_REL,
+    SELECT_TIE_LOGIT_REL,
+    SELECT_TIE_MASS,
     BisectNode,
     ClusterCfg,
     HeadResult,
@@ -18,12 +23,17 @@ from .cbsa import (  # noqa: F401
     cluster_logits,
     cluster_means,
     dense_attention,
+    domains,
     forward_head,
+    head_entropy,
     kmeans,
     kmeans_assign,
     kmeans_update,
     permute,
+    pool_counts,
+    proxy_probs,
     select,
+    select_domains,
     sq_dists,
     subspace_cluster,
     subspace_logits,

@@ -339,7 +339,7 @@ def _tie_run(sl, cut):
     return a, b
 
 
-def select(logits, units, qsizes, top_p, floor, online_topk, k_h=None):
+def select(logits, units, qsizes, top_p, floor, online_topk, k_h=None, pool=None):
     """Per-row selection over one head.
 
     logits [Cq, Ck] (-inf = empty unit), units [Ck] count of each unit
@@ -359,6 +359,11 @@ def select(logits, units, qsizes, top_p, floor, online_topk, k_h=None):
          k_h (capped at every non-empty unit); other rows are unchanged.
          `k_h` given: step 5 runs with that value (a staged comparison, given
          the other side's k_h).
+
+    `pool` (from pool_counts): rows of a head that competes in a pooled
+    domain take their Top-p count from the pool instead of step 3, with the
+    pool's range of counts under near ties; the floor and the online Top-k
+    then apply as above.
 
     An empty query cluster (|Q_i| = 0) has no query to serve: it selects
     nothing and counts 0 (reading; it does not enter k_h either way).
@@ -408,11 +413,15 @@ def select(logits, units, qsizes, top_p, floor, online_topk, k_h=None):
                 tp_lo = tp - 1
             if abs(cm[tp - 1] - top_p) <= SELECT_TIE_MASS and tp < len(cm):
                 tp_hi = tp + 1
+        if pool is not None and pool["count"][i] >= 0:
+            tp = int(pool["count"][i])
+            tp_lo, tp_hi = int(pool["lo"][i]), int(pool["hi"][i])
         tf = _first_reaching(cu, floor) if floor > 0 else 0
         if qsizes[i] > 0:
             t = max(tp, tf)
             lo, hi = t, t
-            if 0 < top_p < 1 and tp >= tf:  # the mass decides the cut
+            pooled = pool is not None and pool["count"][i] >= 0
+            if (0 < top_p < 1 or pooled) and tp >= tf:  # the mass decides the cut
                 lo, hi = max(tp_lo, tf), max(tp_hi, tf)
             # units tied in logit with the ones at a candidate cut
             a0, _ = _tie_run(sl, lo)
@@ -460,6 +469,149 @@ def select(logits, units, qsizes, top_p, floor, online_topk, k_h=None):
     return dict(mask=mask, n_init=n_init, n_final=n_final, k_h=k_h, t_init=t_init,
                 t_final=t_final, near_tie=near, orders=orders, init_lo=init_lo, init_hi=init_hi,
                 cut_lo=cut_lo, cut_hi=cut_hi, cum_units=cum_units)
+
+
+# --------------------------------------------------------------------------
+# Competition domains (EG-Sparse: entropy-gated grouped cross-head pools;
+# VMoBA: global block selection over a whole head)
+# --------------------------------------------------------------------------
+
+def proxy_probs(logits):
+    """Row-wise softmax of proxy logits (-inf = empty unit -> 0)."""
+    logits = _f64(logits)
+    out = np.zeros_like(logits)
+    for i in range(logits.shape[0]):
+        v = np.isfinite(logits[i])
+        if v.any():
+            e = np.exp(logits[i][v] - logits[i][v].max())
+            out[i][v] = e / e.sum()
+    return out
+
+
+def head_entropy(logits, qsizes):
+    """Entropy of one head's proxy attention (EG-Sparse, abstract: heads are
+    routed by entropy, from scores the sparse pipeline already has).
+
+    Reading: the Shannon entropy of each row's proxy distribution, divided by
+    the log of its number of non-empty units (1 -> 0), so that it lies in
+    [0, 1]; the head's entropy is their mean weighted by query-cluster size
+    (the expected normalised entropy of a query's proxy attention)."""
+    P = proxy_probs(logits)
+    qsizes = np.asarray(qsizes, dtype=np.float64)
+    ent = np.zeros(len(P))
+    for i in range(len(P)):
+        p = P[i][P[i] > 0]
+        if len(p) > 1:
+            ent[i] = -(p * np.log(p)).sum() / math.log(len(p))
+    total = qsizes.sum()
+    return float((qsizes * ent).sum() / total) if total > 0 else 0.0
+
+
+DOMAIN_ROW, DOMAIN_HEAD, DOMAIN_GROUP = 0, 1, 2
+
+
+def domains(entropies, domain, group, max_entropy):
+    """Pools of heads.  ROW: every head selects per row (no pool).  HEAD
+    (VMoBA global block selection): every head is a pool of its own.  GROUP
+    (EG-Sparse): heads are cut into groups of `group` consecutive heads; the
+    heads of a group whose entropy is below `max_entropy` form one pool, the
+    others select per row.  Returns a list of pools (lists of head indices)."""
+    H = len(entropies)
+    if domain == DOMAIN_ROW:
+        return []
+    if domain == DOMAIN_HEAD:
+        return [[h] for h in range(H)]
+    pools = []
+    for g0 in range(0, H, group):
+        low = [h for h in range(g0, min(g0 + group, H)) if entropies[h] < max_entropy]
+        if low:
+            pools.append(low)
+    return pools
+
+
+def pool_counts(logits, qsizes, heads, top_p):
+    """Pooled Top-p over the (head, row, unit) pairs of the heads in `heads`.
+
+    Reading (VMoBA, abstract (2): the most salient query-key block
+    interactions are chosen across a whole head; EG-Sparse, abstract: a grouped
+    cross-head pool): every pair of a non-empty query cluster and a non-empty
+    unit competes by its proxy probability p_ij (descending; ties by head,
+    row, unit ascending), carrying the mass |Q_i| p_ij / N, so that a head's
+    pairs sum to 1 and a pool of m heads to m; the pool takes the shortest
+    prefix whose mass reaches top_p * m (top_p >= 1: every pair; top_p <= 0:
+    none).  A row's pooled pairs are then the first ones of its own ranking,
+    and their number is the row's Top-p count.
+
+    Returns {h: dict(count, lo, hi)} with per-row counts and their range
+    under near ties (a crossing within SELECT_TIE_MASS of the target, or a cut
+    inside a run of probabilities within SELECT_TIE_LOGIT_REL relative)."""
+    pairs = []   # (p, h, i, j, mass)
+    for h in heads:
+        P = proxy_probs(logits[h])
+        N = float(np.sum(qsizes[h]))
+        for i in range(P.shape[0]):
+            if qsizes[h][i] <= 0:
+                continue
+            for j in np.nonzero(P[i] > 0)[0]:
+                pairs.append((P[i, j], h, i, int(j), qsizes[h][i] * P[i, j] / N))
+    pairs.sort(key=lambda t: (-t[0], t[1], t[2], t[3]))
+    m = len(heads)
+    cm = np.cumsum([t[4] for t in pairs]) if pairs else np.zeros(0)
+    if top_p >= 1:
+        cut = lo = hi = len(pairs)
+    elif top_p <= 0:
+        cut = lo = hi = 0
+    else:
+        target = top_p * m
+        cut = _first_reaching(cm, target)
+        lo = hi = cut
+        if cut >= 2 and abs(cm[cut - 2] - target) <= SELECT_TIE_MASS * m:
+            lo = cut - 1
+        if abs(cm[cut - 1] - target) <= SELECT_TIE_MASS * m and cut < len(pairs):
+            hi = cut + 1
+        pv = np.array([t[0] for t in pairs])
+
+        def close(k):
+            a, b = pv[k - 1], pv[k]
+            return a - b <= SELECT_TIE_LOGIT_REL * max(a, b)
+        while 0 < lo < len(pairs) and close(lo):
+            lo -= 1
+        while 0 < hi < len(pairs) and close(hi):
+            hi += 1
+    out = {}
+    for h in heads:
+        Cq = logits[h].shape[0]
+        out[h] = dict(count=np.zeros(Cq, np.int64), lo=np.zeros(Cq, np.int64), hi=np.zeros(Cq, np.int64))
+    for k, (_, h, i, _, _) in enumerate(pairs):
+        if k < cut:
+            out[h]["count"][i] += 1
+        if k < lo:
+            out[h]["lo"][i] += 1
+        if k < hi:
+            out[h]["hi"][i] += 1
+    return out
+
+
+def select_domains(logits, units, qsizes, top_p, floor, online_topk, domain=DOMAIN_ROW, group=1,
+                   max_entropy=0.0):
+    """Selection of every head under a competition rule (EG-Sparse, VMoBA).
+
+    logits [H, Cq, Ck], qsizes [H, Cq], units [Ck] (clusters: ones).  Steps:
+    head entropies; pools from the rule (`domains`); each pool's Top-p counts
+    (`pool_counts`); then every head's selection as `select`, with its rows'
+    Top-p counts taken from its pool when it has one.  Returns dict(heads =
+    per-head select() results, entropy [H], pools)."""
+    H = len(logits)
+    ent = np.array([head_entropy(logits[h], qsizes[h]) for h in range(H)])
+    pools = domains(ent, domain, group, max_entropy)
+    pooled = {}
+    for pl in pools:
+        pooled.update(pool_counts(logits, qsizes, pl, top_p))
+    res = []
+    for h in range(H):
+        pc = pooled.get(h)
+        res.append(select(logits[h], units, qsizes[h], top_p, floor, online_topk, pool=pc))
+    return dict(heads=res, entropy=ent, pools=pools)
 
 
 # --------------------------------------------------------------------------
