@@ -40,7 +40,7 @@ class ClusterCfg(ctypes.Structure):
 
 class SelectCfg(ctypes.Structure):
     _fields_ = [("top_p", ctypes.c_double), ("topk_floor", I32), ("online_topk", I32),
-                ("size_weighted", I32)]
+                ("size_weighted", I32), ("domain", I32), ("group", I32), ("max_entropy", ctypes.c_double)]
 
 
 class AttnCfg(ctypes.Structure):
@@ -82,7 +82,7 @@ def load():
     lib.sa_cluster_qk.argtypes = [P(Problem), P(ClusterCfg), P(ClusterCfg), vp, vp, P(Clusters), P(Clusters),
                                   vp, ctypes.c_size_t, vp]
     lib.sa_permute.argtypes = [P(Problem), P(Clusters), vp, vp, vp, vp]
-    lib.sa_select.argtypes = [P(Problem), P(SelectCfg), P(Clusters), P(Clusters), vp, vp, vp, vp, vp,
+    lib.sa_select.argtypes = [P(Problem), P(SelectCfg), P(Clusters), P(Clusters), vp, vp, vp, vp, vp, vp,
                               ctypes.c_size_t, vp]
     lib.sa_block_sparse_attn.argtypes = [P(Problem), P(AttnCfg), P(Clusters), P(Clusters), vp, vp, vp, vp,
                                          vp, ctypes.c_size_t, vp]
@@ -119,8 +119,15 @@ def cluster_cfg(method="kmeans", clusters=0, leaf=128, tile_cap=0, iters=5, init
     return ClusterCfg(m, clusters, leaf, tile_cap, iters, init, (I32 * 3)(*sub_dims))
 
 
-def select_cfg(top_p=0.9, topk_floor=1, online_topk=False, size_weighted=True) -> SelectCfg:
-    return SelectCfg(float(top_p), int(topk_floor), int(bool(online_topk)), int(bool(size_weighted)))
+SA_DOMAIN_ROW, SA_DOMAIN_HEAD, SA_DOMAIN_GROUP = 0, 1, 2
+DOMAINS = {"row": SA_DOMAIN_ROW, "head": SA_DOMAIN_HEAD, "group": SA_DOMAIN_GROUP}
+
+
+def select_cfg(top_p=0.9, topk_floor=1, online_topk=False, size_weighted=True, domain="row", group=1,
+               max_entropy=0.0) -> SelectCfg:
+    d = DOMAINS[domain] if isinstance(domain, str) else int(domain)
+    return SelectCfg(float(top_p), int(topk_floor), int(bool(online_topk)), int(bool(size_weighted)), d,
+                     int(group), float(max_entropy))
 
 
 def attn_cfg(compensate=False, scale=0.0, events=None) -> AttnCfg:
@@ -224,10 +231,10 @@ def sa_permute(p: Problem, c: ClusterTensors, x: torch.Tensor, x_perm: torch.Ten
 
 
 def sa_select(p: Problem, cfg: SelectCfg, q: ClusterTensors, k: ClusterTensors, mask, counts, init_counts,
-              head_topk, ws):
+              head_topk, ws, head_entropy=None):
     _check("sa_select", load().sa_select(ctypes.byref(p), ctypes.byref(cfg), ctypes.byref(q.struct()),
                                          ctypes.byref(k.struct()), _ptr(mask), _ptr(counts), _ptr(init_counts),
-                                         _ptr(head_topk), _ptr(ws), ws.numel(), _stream()))
+                                         _ptr(head_topk), _ptr(head_entropy), _ptr(ws), ws.numel(), _stream()))
 
 
 def sa_block_sparse_attn(p: Problem, cfg: AttnCfg, q: ClusterTensors, k: ClusterTensors, v_perm, v_means,

@@ -19,7 +19,8 @@ def cfgs(w: Workload):
         return L.cluster_cfg(spec.method, spec.clusters, spec.leaf, spec.tile_cap, spec.iters,
                              L.SA_INIT_FIRST, spec.sub_dims)
 
-    return (p, cc(w.q), cc(w.k), L.select_cfg(w.top_p, w.floor, w.online_topk, w.size_weighted),
+    return (p, cc(w.q), cc(w.k),
+            L.select_cfg(w.top_p, w.floor, w.online_topk, w.size_weighted, w.domain, w.group, w.max_entropy),
             L.attn_cfg(w.compensate))
 
 

@@ -31,6 +31,11 @@ __global__ void zero_u64(unsigned long long* p, int n) {
   if (i < n) p[i] = 0ull;
 }
 
+__global__ void fill_u64_kernel(unsigned long long* p, size_t n) {
+  const size_t i = size_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = 0ull;
+}
+
 // pass 0: single pass (online off) or the first pass (online on, accumulate A_h)
 // pass 1: second pass of online Top-k (extend and write)
 // --------------------------------------------------------------------------
@@ -790,7 +795,8 @@ __device__ __forceinline__ int wave_sum_i32(int v) {
 
 // One wavefront per query cluster (four per workgroup).
 __global__ __launch_bounds__(256) void select_wave(SelectArgs a, const double* __restrict__ L,
-                                                   unsigned long long* __restrict__ acc, int pass) {
+                                                   unsigned long long* __restrict__ acc,
+                                                   const int32_t* __restrict__ pool_cnt, int pass) {
   __shared__ unsigned long long hist[4][256];
   __shared__ uint32_t words[4][SEL_MAX / 32];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -848,7 +854,8 @@ __global__ __launch_bounds__(256) void select_wave(SelectArgs a, const double* _
   };
   const double P = a.top_p;
   int np;
-  if (P >= 1.0) np = Vn;
+  if (pool_cnt && pool_cnt[row] >= 0) np = pool_cnt[row];  // decided by the row's pool
+  else if (P >= 1.0) np = Vn;
   else if (P <= 0.0) np = 0;
   else np = count_through(wave_select(key, ms, (unsigned long long)llrint(P * MASS_ONE), hist[wv]));
   const int nf = a.floor_units > 0 ? min(a.floor_units, Vn) : 0;
@@ -885,9 +892,306 @@ __global__ __launch_bounds__(256) void select_wave(SelectArgs a, const double* _
   }
 }
 
+// --------------------------------------------------------------------------
+// Competition domains (EG-Sparse: low-entropy heads share a grouped
+// cross-head pool, high-entropy heads keep per-row selection; VMoBA: global
+// block selection over a whole head).  A pool's (head, row, unit) pairs
+// compete by proxy probability p_ij (descending; ties by head, row, unit),
+// each carrying the mass |Q_i| p_ij / N in 2^-52 fixed point; the pool keeps
+// the shortest prefix whose mass reaches top_p times its number of heads.
+// The pooled pairs of a row are the first of its own ranking, so the pool
+// hands each row a Top-p count and the per-row selection does the rest
+// (floor, online Top-k, mask).
+// --------------------------------------------------------------------------
+constexpr int PBIN = 2048;  // radix bins (11-bit digits of the 64-bit keys)
+
+struct PoolState {
+  unsigned long long prefix;  // key digits fixed so far
+  long long rem;              // mass still needed inside the keys of that prefix
+  int all;                    // the pool's whole mass stays below the target: take every pair
+  int heads;                  // heads in the pool
+};
+
+// pool of head h: -1 = per-row selection
+__device__ __forceinline__ int pool_of(const SelectArgs& a, const double* E, int h) {
+  if (a.domain == SA_DOMAIN_HEAD) return h;
+  if (a.domain == SA_DOMAIN_GROUP && E[h] < a.max_entropy) return h / a.group;
+  return -1;
+}
+__host__ __device__ inline int pool_slots(int domain, int group) { return domain == SA_DOMAIN_GROUP ? group : 1; }
+
+// One wavefront per row: max, normaliser and normalised entropy of the row's
+// proxy distribution (sums in a fixed order: lane partials in unit order, then
+// a fixed butterfly).
+__global__ __launch_bounds__(256) void rowstat_kernel(SelectArgs a, const double* __restrict__ L,
+                                                      double* __restrict__ stat) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (long long)a.H * a.Cq) return;
+  const double* lr = L + row * a.Ck;
+  double mx = -__builtin_huge_val();
+  int nv = 0;
+  for (int j = lane; j < a.Ck; j += 64) {
+    const double l = lr[j];
+    if (l != -__builtin_huge_val()) {
+      mx = fmax(mx, l);
+      ++nv;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+  nv = wave_sum_i32(nv);
+  double z = 0.0;
+  for (int j = lane; j < a.Ck; j += 64) {
+    const double l = lr[j];
+    if (l != -__builtin_huge_val()) z += exp(l - mx);
+  }
+  for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
+  double plp = 0.0;
+  for (int j = lane; j < a.Ck; j += 64) {
+    const double l = lr[j];
+    if (l != -__builtin_huge_val()) {
+      const double pr = exp(l - mx) / z;
+      if (pr > 0.0) plp += pr * log(pr);
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) plp += __shfl_xor(plp, o, 64);
+  if (lane == 0) {
+    stat[3 * row] = mx;
+    stat[3 * row + 1] = z;
+    stat[3 * row + 2] = nv > 1 ? -plp / log(double(nv)) : 0.0;
+  }
+}
+
+// One workgroup per head: E_h = sum_i |Q_i| ent_i / N in a fixed order.
+__global__ __launch_bounds__(256) void head_entropy_kernel(SelectArgs a, const double* __restrict__ stat,
+                                                           double* __restrict__ E) {
+  __shared__ double part[256];
+  const int h = blockIdx.x, t = threadIdx.x;
+  const int32_t* qo = a.q_off + size_t(h) * (a.Cq + 1);
+  double acc = 0.0;
+  for (int i = t; i < a.Cq; i += 256)
+    acc += double(qo[i + 1] - qo[i]) * stat[3 * (size_t(h) * a.Cq + i) + 2];
+  part[t] = acc;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (t < o) part[t] += part[t + o];
+    __syncthreads();
+  }
+  if (t == 0) {
+    const double e = part[0] / double(a.N);
+    E[h] = e;
+    if (a.head_entropy) a.head_entropy[h] = e;
+  }
+}
+
+__global__ void fill_i32_kernel(int32_t* p, long long n, int v) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// probability, order key and fixed-point mass of pair (row, j)
+struct PairVal {
+  unsigned long long key, w;
+  bool valid;
+};
+__device__ __forceinline__ PairVal pair_val(const double* lr, const double* st, int j, double qscale) {
+  const double l = lr[j];
+  PairVal v{0ull, 0ull, false};
+  if (l == -__builtin_huge_val()) return v;
+  const double pr = exp(l - st[0]) / st[1];
+  v.key = order_key(pr);
+  v.w = (unsigned long long)llrint(pr * qscale);
+  v.valid = true;
+  return v;
+}
+
+// Radix pass: mass histogram of the digit below the fixed prefix, over the
+// pairs of the pooled rows.  Workgroup: 16 rows (4 per wavefront) of one head
+// slot of one pool.  grid (ceil(Cq/16), slots, pools).
+__global__ __launch_bounds__(256) void pool_hist_kernel(SelectArgs a, const double* __restrict__ L,
+                                                        const double* __restrict__ stat,
+                                                        const double* __restrict__ E,
+                                                        const PoolState* __restrict__ ps,
+                                                        unsigned long long* __restrict__ ghist, int shift,
+                                                        int width) {
+  __shared__ unsigned long long hist[PBIN];
+  const int g = blockIdx.z, slot = blockIdx.y, t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int h = a.domain == SA_DOMAIN_GROUP ? g * a.group + slot : g;
+  if (h >= a.H || pool_of(a, E, h) != g || ps[g].all) return;
+  for (int b = t; b < PBIN; b += 256) hist[b] = 0ull;
+  __syncthreads();
+  const int above = shift + width;
+  const unsigned long long pre = ps[g].prefix;
+  const unsigned long long dmask = (1ull << width) - 1ull;
+  const int32_t* qo = a.q_off + size_t(h) * (a.Cq + 1);
+  for (int r = 0; r < 4; ++r) {
+    const int i = blockIdx.x * 16 + wv * 4 + r;
+    if (i >= a.Cq) break;
+    const int qs = qo[i + 1] - qo[i];
+    if (qs == 0) continue;
+    const size_t row = size_t(h) * a.Cq + i;
+    const double qscale = double(qs) / double(a.N) * MASS_ONE;
+    for (int j = lane; j < a.Ck; j += 64) {
+      const PairVal v = pair_val(L + row * a.Ck, stat + 3 * row, j, qscale);
+      if (!v.valid || v.w == 0ull) continue;
+      if (above < 64 && (v.key >> above) != (pre >> above)) continue;
+      atomicAdd(&hist[(v.key >> shift) & dmask], v.w);
+    }
+  }
+  __syncthreads();
+  unsigned long long* gh = ghist + size_t(g) * PBIN;
+  for (int b = t; b < PBIN; b += 256)
+    if (hist[b]) atomicAdd(&gh[b], hist[b]);
+}
+
+// One thread per pool: its heads and its target, top_p times their number.
+__global__ void pool_init_kernel(SelectArgs a, const double* __restrict__ E, PoolState* __restrict__ ps,
+                                 int pools) {
+  const int g = blockIdx.x * 64 + threadIdx.x;
+  if (g >= pools) return;
+  int m = 0;
+  for (int s = 0; s < pool_slots(a.domain, a.group); ++s) {
+    const int h = a.domain == SA_DOMAIN_GROUP ? g * a.group + s : g;
+    if (h < a.H && pool_of(a, E, h) == g) ++m;
+  }
+  ps[g].heads = m;
+  ps[g].prefix = 0ull;
+  ps[g].rem = llrint(a.top_p * double(m) * MASS_ONE);
+  ps[g].all = 0;
+}
+
+// One workgroup per pool: the bin where the cumulative mass reaches the
+// remaining target; fixes that digit.  Clears the histogram for the next pass.
+__global__ __launch_bounds__(256) void pool_pick_kernel(PoolState* __restrict__ ps,
+                                                        unsigned long long* __restrict__ ghist, int shift) {
+  __shared__ unsigned long long wsum[16];
+  __shared__ int sel_bin;
+  __shared__ unsigned long long sel_pre;
+  const int g = blockIdx.x, t = threadIdx.x;
+  unsigned long long* gh = ghist + size_t(g) * PBIN;
+  if (t == 0) sel_bin = -1;
+  __syncthreads();
+  if (ps[g].heads == 0 || ps[g].all) {
+    for (int b = t; b < PBIN; b += 256) gh[b] = 0ull;
+    return;
+  }
+  constexpr int BPT = PBIN / 256;
+  unsigned long long c[BPT], loc = 0ull;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    c[q] = gh[t * BPT + q];
+    loc += c[q];
+  }
+  unsigned long long tot;
+  unsigned long long pre = bscan<unsigned long long>(loc, wsum, tot);
+  const unsigned long long rem = (unsigned long long)ps[g].rem;
+#pragma unroll
+  for (int q = 0; q < BPT; ++q) {
+    if (pre < rem && rem <= pre + c[q]) {
+      sel_bin = t * BPT + q;
+      sel_pre = pre;
+    }
+    pre += c[q];
+  }
+  __syncthreads();
+  for (int b = t; b < PBIN; b += 256) gh[b] = 0ull;
+  if (t == 0) {
+    if (sel_bin < 0) {
+      ps[g].all = 1;  // the pool's mass never reaches the target: every pair
+    } else {
+      ps[g].prefix |= (unsigned long long)sel_bin << shift;
+      ps[g].rem = (long long)(rem - sel_pre);
+    }
+  }
+}
+
+// Per pooled row: pairs before the boundary key (all pairs if the pool takes
+// everything), plus the count and mass of its pairs on the boundary key.
+__global__ __launch_bounds__(256) void pool_count_kernel(SelectArgs a, const double* __restrict__ L,
+                                                         const double* __restrict__ stat,
+                                                         const double* __restrict__ E,
+                                                         const PoolState* __restrict__ ps,
+                                                         int32_t* __restrict__ pool_cnt,
+                                                         int32_t* __restrict__ tie_n,
+                                                         unsigned long long* __restrict__ tie_w) {
+  const int g = blockIdx.z, slot = blockIdx.y, t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int h = a.domain == SA_DOMAIN_GROUP ? g * a.group + slot : g;
+  if (h >= a.H || pool_of(a, E, h) != g) return;
+  const unsigned long long K = ps[g].prefix;
+  const bool all = ps[g].all != 0;
+  const int32_t* qo = a.q_off + size_t(h) * (a.Cq + 1);
+  for (int r = 0; r < 4; ++r) {
+    const int i = blockIdx.x * 16 + wv * 4 + r;
+    if (i >= a.Cq) break;
+    const int qs = qo[i + 1] - qo[i];
+    const size_t row = size_t(h) * a.Cq + i;
+    const double qscale = double(qs) / double(a.N) * MASS_ONE;
+    int nlt = 0, neq = 0;
+    unsigned long long weq = 0ull;
+    if (qs > 0) {
+      for (int j = lane; j < a.Ck; j += 64) {
+        const PairVal v = pair_val(L + row * a.Ck, stat + 3 * row, j, qscale);
+        if (!v.valid) continue;
+        if (all || v.key < K) ++nlt;
+        else if (v.key == K) {
+          ++neq;
+          weq += v.w;
+        }
+      }
+    }
+    nlt = wave_sum_i32(nlt);
+    neq = wave_sum_i32(neq);
+    for (int o = 32; o > 0; o >>= 1) weq += __shfl_xor(weq, o, 64);
+    if (lane == 0) {
+      pool_cnt[row] = nlt;
+      tie_n[row] = all ? 0 : neq;
+      tie_w[row] = all ? 0ull : weq;
+    }
+  }
+}
+
+// One workgroup per pool: the pairs on the boundary key are taken in (head,
+// row, unit) order until the remaining mass is reached.
+__global__ __launch_bounds__(64) void pool_tie_kernel(SelectArgs a, const double* __restrict__ L,
+                                                      const double* __restrict__ stat,
+                                                      const double* __restrict__ E,
+                                                      const PoolState* __restrict__ ps,
+                                                      int32_t* __restrict__ pool_cnt,
+                                                      const int32_t* __restrict__ tie_n,
+                                                      const unsigned long long* __restrict__ tie_w) {
+  const int g = blockIdx.x;
+  if (threadIdx.x != 0 || ps[g].heads == 0 || ps[g].all) return;
+  const unsigned long long K = ps[g].prefix;
+  unsigned long long need = (unsigned long long)ps[g].rem;  // >= 1
+  for (int s = 0; s < pool_slots(a.domain, a.group) && need > 0ull; ++s) {
+    const int h = a.domain == SA_DOMAIN_GROUP ? g * a.group + s : g;
+    if (h >= a.H || pool_of(a, E, h) != g) continue;
+    const int32_t* qo = a.q_off + size_t(h) * (a.Cq + 1);
+    for (int i = 0; i < a.Cq && need > 0ull; ++i) {
+      const size_t row = size_t(h) * a.Cq + i;
+      if (tie_n[row] == 0) continue;
+      if (tie_w[row] < need) {
+        pool_cnt[row] += tie_n[row];
+        need -= tie_w[row];
+        continue;
+      }
+      // the boundary row: its tied units in unit order
+      const double qscale = double(qo[i + 1] - qo[i]) / double(a.N) * MASS_ONE;
+      int taken = 0;
+      for (int j = 0; j < a.Ck && need > 0ull; ++j) {
+        const PairVal v = pair_val(L + row * a.Ck, stat + 3 * row, j, qscale);
+        if (!v.valid || v.key != K) continue;
+        ++taken;
+        need = v.w >= need ? 0ull : need - v.w;
+      }
+      pool_cnt[row] += taken;
+    }
+  }
+}
+
 }  // namespace
 
-size_t select_scratch(int H, int Cq, int Ck, int subspace) {
+size_t select_scratch(int H, int Cq, int Ck, int subspace, int domain, int group) {
   Arena a{nullptr, 0, 0};
   a.get<unsigned long long>(size_t(H));
   if (subspace) {
@@ -895,6 +1199,16 @@ size_t select_scratch(int H, int Cq, int Ck, int subspace) {
     a.get<long long>(size_t(H) * Cq * 5);
   } else {
     a.get<double>(size_t(H) * Cq * Ck);
+    if (domain != SA_DOMAIN_ROW) {
+      const int pools = domain == SA_DOMAIN_GROUP ? ceil_div(H, group) : H;
+      a.get<double>(size_t(H) * Cq * 3);   // row max, normaliser, entropy
+      a.get<double>(size_t(H));            // head entropies
+      a.get<int32_t>(size_t(H) * Cq);      // pooled Top-p counts
+      a.get<int32_t>(size_t(H) * Cq);      // boundary-key pairs per row
+      a.get<unsigned long long>(size_t(H) * Cq);
+      a.get<PoolState>(size_t(pools));
+      a.get<unsigned long long>(size_t(pools) * PBIN);
+    }
   }
   return a.used;
 }
@@ -919,13 +1233,45 @@ hipError_t select_run(const SelectArgs& a, Arena& s, hipStream_t st) {
   if (a.Ck > SEL_MAX || a.d % LT) return hipErrorInvalidValue;
   double* L = s.get<double>(size_t(a.H) * a.Cq * a.Ck);
   logits_kernel<<<dim3(ceil_div(a.Ck, LT), ceil_div(a.Cq, LT), a.H), 256, 0, st>>>(a, L);
+  int32_t* pool_cnt = nullptr;
+  if (a.domain != SA_DOMAIN_ROW) {
+    if (a.domain == SA_DOMAIN_GROUP && a.group < 1) return hipErrorInvalidValue;
+    const int pools = a.domain == SA_DOMAIN_GROUP ? ceil_div(a.H, a.group) : a.H;
+    const long long rows = (long long)a.H * a.Cq;
+    double* stat = s.get<double>(size_t(rows) * 3);
+    double* E = s.get<double>(size_t(a.H));
+    pool_cnt = s.get<int32_t>(size_t(rows));
+    int32_t* tie_n = s.get<int32_t>(size_t(rows));
+    unsigned long long* tie_w = s.get<unsigned long long>(size_t(rows));
+    PoolState* ps = s.get<PoolState>(size_t(pools));
+    unsigned long long* ghist = s.get<unsigned long long>(size_t(pools) * PBIN);
+    rowstat_kernel<<<unsigned((rows + 3) / 4), 256, 0, st>>>(a, L, stat);
+    head_entropy_kernel<<<a.H, 256, 0, st>>>(a, stat, E);
+    fill_i32_kernel<<<unsigned((rows + 255) / 256), 256, 0, st>>>(pool_cnt, rows, -1);
+    if (a.top_p > 0.0 && a.top_p < 1.0) {
+      // pooled Top-p (top_p >= 1 or <= 0 selects the same as every row alone)
+      const dim3 gp(ceil_div(a.Cq, 16), pool_slots(a.domain, a.group), pools);
+      fill_u64_kernel<<<unsigned((size_t(pools) * PBIN + 255) / 256), 256, 0, st>>>(ghist, size_t(pools) * PBIN);
+      pool_init_kernel<<<ceil_div(pools, 64), 64, 0, st>>>(a, E, ps, pools);
+      for (int hb = 63;;) {  // 11-bit digits from the top of the 64-bit keys
+        const int shift = hb - 10 > 0 ? hb - 10 : 0;
+        const int width = hb - shift + 1;
+        pool_hist_kernel<<<gp, 256, 0, st>>>(a, L, stat, E, ps, ghist, shift, width);
+        pool_pick_kernel<<<pools, 256, 0, st>>>(ps, ghist, shift);
+        if (shift == 0) break;
+        hb = shift - 1;
+      }
+      pool_count_kernel<<<gp, 256, 0, st>>>(a, L, stat, E, ps, pool_cnt, tie_n, tie_w);
+      pool_tie_kernel<<<pools, 64, 0, st>>>(a, L, stat, E, ps, pool_cnt, tie_n, tie_w);
+    }
+  }
   const dim3 gw(ceil_div(a.Cq, 4), a.H);
   if (a.online) {
     zero_u64<<<ceil_div(a.H, 256), 256, 0, st>>>(acc, a.H);
-    select_wave<<<gw, 256, 0, st>>>(a, L, acc, 0);
-    select_wave<<<gw, 256, 0, st>>>(a, L, acc, 1);
+    select_wave<<<gw, 256, 0, st>>>(a, L, acc, pool_cnt, 0);
+    select_wave<<<gw, 256, 0, st>>>(a, L, acc, pool_cnt, 1);
   } else {
-    select_wave<<<gw, 256, 0, st>>>(a, L, acc, 0);
+    select_wave<<<gw, 256, 0, st>>>(a, L, acc, pool_cnt, 0);
   }
   return hipGetLastError();
 }

@@ -86,6 +86,9 @@ sa_status check_select_cfg(const sa_select_cfg* c) {
   if (!c) return SA_ERR_INVALID_ARG;
   if (!isfinite(c->top_p)) return SA_ERR_INVALID_ARG;
   if (c->top_p <= 0.0 && c->topk_floor <= 0) return SA_ERR_INVALID_ARG;
+  if (c->domain != SA_DOMAIN_ROW && c->domain != SA_DOMAIN_HEAD && c->domain != SA_DOMAIN_GROUP)
+    return SA_ERR_INVALID_ARG;
+  if (c->domain == SA_DOMAIN_GROUP && (c->group < 1 || !isfinite(c->max_entropy))) return SA_ERR_INVALID_ARG;
   return SA_OK;
 }
 
@@ -159,7 +162,7 @@ struct FwdBufs {
 };
 
 FwdBufs carve_forward(const sa_problem* p, const sa_cluster_cfg* qc, const sa_cluster_cfg* kc,
-                      const sa_attn_cfg* ac, char* base, size_t* used) {
+                      const sa_select_cfg* sc, const sa_attn_cfg* ac, char* base, size_t* used) {
   const int H = p->heads, N = p->n, d = p->d;
   const int Cq = clusters_of(p, qc), Ck = clusters_of(p, kc);
   Arena a{base, 0, 0};
@@ -179,7 +182,8 @@ FwdBufs carve_forward(const sa_problem* p, const sa_cluster_cfg* qc, const sa_cl
   b.head_topk = a.get<int32_t>(size_t(H));
   const size_t fixed = a.used;
   size_t scr = cluster_qk_scratch(p, qc, kc);
-  scr = std::max(scr, select_scratch(H, Cq, Ck, kc->method == SA_SUBSPACE) + 256);
+  scr = std::max(scr, select_scratch(H, Cq, Ck, kc->method == SA_SUBSPACE, sc ? sc->domain : SA_DOMAIN_ROW,
+                                     sc ? sc->group : 1) + 256);
   scr = std::max(scr, attn_scratch(H, N, d, Cq, Ck, tile_rows(qc), ac ? ac->compensate : 0,
                                    p->dtype, max_tiles(p, qc)) + 256);
   b.scratch = base ? base + fixed : nullptr;
@@ -314,7 +318,7 @@ sa_status do_cluster_qk(const sa_problem* p, const sa_cluster_cfg* qc, const sa_
 
 sa_status do_select(const sa_problem* p, const sa_select_cfg* c, const sa_clusters* q,
                     const sa_clusters* k, uint32_t* mask, int32_t* counts, int32_t* init_counts,
-                    int32_t* head_topk, Arena& s, hipStream_t st) {
+                    int32_t* head_topk, double* head_entropy, Arena& s, hipStream_t st) {
   SelectArgs a{};
   a.H = p->heads;
   a.N = p->n;
@@ -337,6 +341,10 @@ sa_status do_select(const sa_problem* p, const sa_select_cfg* c, const sa_cluste
   a.counts = counts;
   a.init_counts = init_counts;
   a.head_topk = head_topk;
+  a.domain = c->domain;
+  a.group = c->group;
+  a.max_entropy = c->max_entropy;
+  a.head_entropy = head_entropy;
   Arena tmp = s;
   return hip_status(select_run(a, tmp, st));
 }
@@ -416,7 +424,6 @@ SA_API int32_t sa_num_clusters(const sa_problem* p, const sa_cluster_cfg* cfg) {
 SA_API sa_status sa_workspace_size(const sa_problem* p, const sa_cluster_cfg* qcfg,
                                    const sa_cluster_cfg* kcfg, const sa_select_cfg* scfg,
                                    const sa_attn_cfg* acfg, size_t* bytes) {
-  (void)scfg;
   if (!bytes) return SA_ERR_INVALID_ARG;
   sa_status st = check_problem(p);
   if (st != SA_OK) return st;
@@ -424,7 +431,7 @@ SA_API sa_status sa_workspace_size(const sa_problem* p, const sa_cluster_cfg* qc
   if (kcfg && (st = check_cluster_cfg(p, kcfg)) != SA_OK) return st;
   if (qcfg && kcfg) {
     size_t used = 0;
-    carve_forward(p, qcfg, kcfg, acfg, nullptr, &used);
+    carve_forward(p, qcfg, kcfg, scfg, acfg, nullptr, &used);
     *bytes = used + 256;
     return SA_OK;
   }
@@ -478,8 +485,8 @@ SA_API sa_status sa_permute(const sa_problem* p, const sa_clusters* c, const voi
 
 SA_API sa_status sa_select(const sa_problem* p, const sa_select_cfg* cfg, const sa_clusters* q,
                            const sa_clusters* k, uint32_t* mask, int32_t* counts,
-                           int32_t* init_counts, int32_t* head_topk, void* ws, size_t ws_bytes,
-                           void* stream) {
+                           int32_t* init_counts, int32_t* head_topk, double* head_entropy, void* ws,
+                           size_t ws_bytes, void* stream) {
   sa_status st = check_problem(p);
   if (st != SA_OK) return st;
   if ((st = check_select_cfg(cfg)) != SA_OK) return st;
@@ -490,10 +497,11 @@ SA_API sa_status sa_select(const sa_problem* p, const sa_select_cfg* cfg, const 
               k->sub_dims[0] + k->sub_dims[1] + k->sub_dims[2] != p->d))
     return SA_ERR_INVALID_ARG;
   if (!sub && k->num_clusters > SELECT_MAX) return SA_ERR_UNSUPPORTED;
-  if (ws_bytes < select_scratch(p->heads, q->num_clusters, k->num_clusters, sub) + 256)
+  if (sub && cfg->domain != SA_DOMAIN_ROW) return SA_ERR_UNSUPPORTED;
+  if (ws_bytes < select_scratch(p->heads, q->num_clusters, k->num_clusters, sub, cfg->domain, cfg->group) + 256)
     return SA_ERR_WORKSPACE;
   Arena s{(char*)ws, ws_bytes, 0};
-  return do_select(p, cfg, q, k, mask, counts, init_counts, head_topk, s, (hipStream_t)stream);
+  return do_select(p, cfg, q, k, mask, counts, init_counts, head_topk, head_entropy, s, (hipStream_t)stream);
 }
 
 SA_API sa_status sa_block_sparse_attn(const sa_problem* p, const sa_attn_cfg* cfg,
@@ -553,11 +561,12 @@ SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
   if (qcfg->method == SA_SUBSPACE) return SA_ERR_INVALID_ARG;
   if (qcfg->init != SA_INIT_FIRST || kcfg->init != SA_INIT_FIRST) return SA_ERR_INVALID_ARG;
   if (kcfg->method == SA_SUBSPACE && acfg->compensate) return SA_ERR_UNSUPPORTED;
+  if (kcfg->method == SA_SUBSPACE && scfg->domain != SA_DOMAIN_ROW) return SA_ERR_UNSUPPORTED;
   if (kcfg->method != SA_SUBSPACE && clusters_of(p, kcfg) > SELECT_MAX) return SA_ERR_UNSUPPORTED;
   size_t used = 0;
-  carve_forward(p, qcfg, kcfg, acfg, nullptr, &used);
+  carve_forward(p, qcfg, kcfg, scfg, acfg, nullptr, &used);
   if (ws_bytes < used) return SA_ERR_WORKSPACE;
-  FwdBufs b = carve_forward(p, qcfg, kcfg, acfg, (char*)ws, &used);
+  FwdBufs b = carve_forward(p, qcfg, kcfg, scfg, acfg, (char*)ws, &used);
   hipStream_t s = (hipStream_t)stream;
   Arena scr{b.scratch, b.scratch_bytes, 0};
   if ((st = do_cluster_qk(p, qcfg, kcfg, q, k, &b.q, &b.k, scr, s)) != SA_OK) return st;
@@ -565,7 +574,7 @@ SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
                                                 b.k.num_clusters, b.v_perm, b.v_means, s)
                                  : gather_rows(v, b.v_perm, b.k.perm, p->heads, p->n, p->d, p->dtype, s);
   if (e != hipSuccess) return SA_ERR_HIP;
-  if ((st = do_select(p, scfg, &b.q, &b.k, mask, b.counts, nullptr, b.head_topk, scr, s)) != SA_OK)
+  if ((st = do_select(p, scfg, &b.q, &b.k, mask, b.counts, nullptr, b.head_topk, nullptr, scr, s)) != SA_OK)
     return st;
   return do_attn(p, acfg, &b.q, &b.k, b.v_perm, b.v_means, mask, o, tile_rows(qcfg),
                  max_tiles(p, qcfg), scr, s);

@@ -146,8 +146,12 @@ struct SelectArgs {
   int32_t* counts;        // [H][Cq]
   int32_t* init_counts;   // [H][Cq] or null
   int32_t* head_topk;     // [H]
+  // competition domain (cluster mode): SA_DOMAIN_ROW / _HEAD / _GROUP
+  int domain, group;
+  double max_entropy;
+  double* head_entropy;   // [H] or null
 };
-size_t select_scratch(int H, int Cq, int Ck, int subspace);
+size_t select_scratch(int H, int Cq, int Ck, int subspace, int domain, int group);
 hipError_t select_run(const SelectArgs& a, Arena& scratch, hipStream_t st);
 
 // k_attn.hip -----------------------------------------------------------------

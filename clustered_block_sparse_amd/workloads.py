@@ -64,6 +64,9 @@ class Workload:
     compensate: bool = False
     size_weighted: bool = True
     seed: int = 0
+    domain: str = "row"          # selection competition domain: row | head | group
+    group: int = 1               # heads per group (domain "group")
+    max_entropy: float = 0.0     # heads below it are pooled (domain "group")
 
     @property
     def n(self) -> int:

@@ -91,6 +91,28 @@ typedef struct sa_cluster_cfg {
   int32_t sub_dims[3]; /* SUBSPACE column widths (t, h, w), summing to d            */
 } sa_cluster_cfg;
 
+/* Competition domains of the selection.
+ * SA_DOMAIN_ROW:   every query cluster selects among its own units (the
+ *                  hybrid Top-p rule above).
+ * SA_DOMAIN_HEAD:  VMoBA global block selection ["VMoBA: Mixture-of-Block
+ *                  Attention for Video Diffusion Models", English abstract,
+ *                  item (2)]: the (query cluster, key cluster) pairs of a
+ *                  whole head compete for one Top-p.
+ * SA_DOMAIN_GROUP: EG-Sparse ["Competition Domains Matter: Selective Head
+ *                  Globalization for Training-Free Sparse Attention in Video
+ *                  Diffusion Transformers", abstract]: heads are cut into
+ *                  groups of `group` consecutive heads; the heads of a group
+ *                  whose entropy is below `max_entropy` share one pool, the
+ *                  others select per row.
+ * A pool's pairs compete by proxy probability p_ij (descending; ties by head,
+ * row, unit), each with mass |Q_i| p_ij / n; the pool keeps the shortest
+ * prefix whose mass reaches top_p times its number of heads, which gives each
+ * query cluster its Top-p count; the floor and the online Top-k then apply
+ * per row as above.  A head's entropy is the query-size-weighted mean of its
+ * rows' proxy entropies divided by ln(number of non-empty units), in [0, 1].
+ * Key clusters only (SUBSPACE keys: SA_ERR_UNSUPPORTED). */
+enum { SA_DOMAIN_ROW = 0, SA_DOMAIN_HEAD = 1, SA_DOMAIN_GROUP = 2 };
+
 typedef struct sa_select_cfg {
   double top_p;         /* cumulative proxy mass to reach (>= 1: all non-empty);
                            double, so a configured 0.9 is compared as 0.9      */
@@ -99,6 +121,9 @@ typedef struct sa_select_cfg {
   int32_t online_topk;  /* SCOPE online per-head Top-k on/off                    */
   int32_t size_weighted;/* 1: proxy logits add ln|K_j| (softmax over per-key
                            scores); 0: plain centroid softmax                    */
+  int32_t domain;       /* SA_DOMAIN_ROW (0, default), _HEAD or _GROUP          */
+  int32_t group;        /* SA_DOMAIN_GROUP: heads per group (>= 1)              */
+  double max_entropy;   /* SA_DOMAIN_GROUP: heads below it are pooled           */
 } sa_select_cfg;
 
 typedef struct sa_attn_cfg {
@@ -186,11 +211,14 @@ SA_API sa_status sa_permute(const sa_problem* p, const sa_clusters* c, const voi
  *   counts      int32  [H, Cq]  final selected units
  *   init_counts int32  [H, Cq]  initial units n_i (may be NULL)
  *   head_topk   int32  [H]      k_h (0 when online Top-k is off)
+ *   head_entropy f64   [H]      entropy of each head's proxy attention (may be
+ *                               NULL; written only when cfg->domain is not
+ *                               SA_DOMAIN_ROW)
  * `scale` of the proxy scores is 1/sqrt(d). */
 SA_API sa_status sa_select(const sa_problem* p, const sa_select_cfg* cfg, const sa_clusters* q,
                            const sa_clusters* k, uint32_t* mask, int32_t* counts,
-                           int32_t* init_counts, int32_t* head_topk, void* ws, size_t ws_bytes,
-                           void* stream);
+                           int32_t* init_counts, int32_t* head_topk, double* head_entropy, void* ws,
+                           size_t ws_bytes, void* stream);
 
 /* Block-sparse attention [SCOPE: attention over the selected original keys
  * and values; CA: block-sparse attention over power-of-two clusters, mean

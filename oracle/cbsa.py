@@ -497,12 +497,13 @@ def head_entropy(logits, qsizes):
     [0, 1]; the head's entropy is their mean weighted by query-cluster size
     (the expected normalised entropy of a query's proxy attention)."""
     P = proxy_probs(logits)
+    units = np.isfinite(_f64(logits)).sum(axis=1)
     qsizes = np.asarray(qsizes, dtype=np.float64)
     ent = np.zeros(len(P))
     for i in range(len(P)):
         p = P[i][P[i] > 0]
-        if len(p) > 1:
-            ent[i] = -(p * np.log(p)).sum() / math.log(len(p))
+        if units[i] > 1:
+            ent[i] = -(p * np.log(p)).sum() / math.log(units[i])
     total = qsizes.sum()
     return float((qsizes * ent).sum() / total) if total > 0 else 0.0
 
