@@ -34,6 +34,7 @@ from .cbsa import (  # noqa: F401
     proxy_probs,
     select,
     select_domains,
+    stat_threshold,
     sq_dists,
     subspace_cluster,
     subspace_logits,

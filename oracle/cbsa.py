@@ -339,7 +339,18 @@ def _tie_run(sl, cut):
     return a, b
 
 
-def select(logits, units, qsizes, top_p, floor, online_topk, k_h=None, pool=None):
+def stat_threshold(p, lam):
+    """BSA's statistical dynamic threshold of one row ("Bidirectional Sparse
+    Attention for Faster Video Diffusion Training", abstract: KV blocks are
+    kept by a statistical dynamic threshold).  Reading: the mean plus `lam`
+    population standard deviations of the row's proxy probabilities over its
+    non-empty units; a unit is kept when its probability is at least that."""
+    p = _f64(p)
+    mu = p.mean()
+    return mu + lam * math.sqrt(((p - mu) ** 2).mean())
+
+
+def select(logits, units, qsizes, top_p, floor, online_topk, k_h=None, pool=None, stat_lambda=None):
     """Per-row selection over one head.
 
     logits [Cq, Ck] (-inf = empty unit), units [Ck] count of each unit
@@ -364,6 +375,10 @@ def select(logits, units, qsizes, top_p, floor, online_topk, k_h=None, pool=None
     domain take their Top-p count from the pool instead of step 3, with the
     pool's range of counts under near ties; the floor and the online Top-k
     then apply as above.
+
+    `stat_lambda` given: step 3 keeps instead the units whose probability
+    reaches the row's statistical threshold (stat_threshold), a prefix of the
+    ranking; a unit within SELECT_TIE_LOGIT_REL of the threshold flags the row.
 
     An empty query cluster (|Q_i| = 0) has no query to serve: it selects
     nothing and counts 0 (reading; it does not enter k_h either way).
@@ -413,6 +428,14 @@ def select(logits, units, qsizes, top_p, floor, online_topk, k_h=None, pool=None
                 tp_lo = tp - 1
             if abs(cm[tp - 1] - top_p) <= SELECT_TIE_MASS and tp < len(cm):
                 tp_hi = tp + 1
+        stat = stat_lambda is not None
+        if stat:
+            ps = p[o]
+            th = stat_threshold(ps, stat_lambda) if len(ps) else 0.0
+            tp = int((ps >= th).sum())
+            tol = SELECT_TIE_LOGIT_REL * max(th, 1e-300)
+            tp_lo = int((ps >= th + tol).sum())
+            tp_hi = int((ps >= th - tol).sum())
         if pool is not None and pool["count"][i] >= 0:
             tp = int(pool["count"][i])
             tp_lo, tp_hi = int(pool["lo"][i]), int(pool["hi"][i])
@@ -421,7 +444,7 @@ def select(logits, units, qsizes, top_p, floor, online_topk, k_h=None, pool=None
             t = max(tp, tf)
             lo, hi = t, t
             pooled = pool is not None and pool["count"][i] >= 0
-            if (0 < top_p < 1 or pooled) and tp >= tf:  # the mass decides the cut
+            if (0 < top_p < 1 or pooled or stat) and tp >= tf:  # the mass or threshold decides the cut
                 lo, hi = max(tp_lo, tf), max(tp_hi, tf)
             # units tied in logit with the ones at a candidate cut
             a0, _ = _tie_run(sl, lo)

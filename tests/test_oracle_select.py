@@ -218,3 +218,49 @@ def test_given_head_topk():
         assert r["k_h"] == k
         assert np.array_equal(r["n_init"], own["n_init"])
         assert np.array_equal(r["n_final"], np.maximum(own["n_init"], k))
+
+
+def test_stat_threshold_worked_example():
+    """Hand-derived: p = (1/2, 1/4, 1/8, 1/8) has mean 1/4 and population
+    variance ((1/4)^2 + 0 + 2 (1/8)^2) / 4 = 3/128, std 0.1530931...; the
+    threshold keeps p >= 1/4 + lam * 0.1530931: lam = 1 -> 0.4031 -> 1 unit,
+    lam = 0 -> 1/4 -> 2 units (1/4 itself is kept), lam = -1 -> 0.0969 ->
+    4 units; a floor of 3 raises the first to 3."""
+    p = np.array([0.5, 0.25, 0.125, 0.125])
+    lg = np.log(p)[None]
+    one = np.ones(4, np.int64)
+    assert math.isclose(oracle.stat_threshold(p, 1.0), 0.25 + math.sqrt(3 / 128), rel_tol=1e-15)
+    for lam, want in ((1.0, 1), (-1.0, 4), (2.0, 1)):
+        r = oracle.select(lg, one, [5], 0.9, 1, False, stat_lambda=lam)
+        assert r["n_init"][0] == want and not r["near_tie"][0]
+    r0 = oracle.select(lg, one, [5], 0.9, 1, False, stat_lambda=0.0)
+    # 1/4 sits exactly on the threshold: kept, and flagged as a tie at the cut
+    assert r0["n_init"][0] == 2 and r0["near_tie"][0] and (r0["cut_lo"][0], r0["cut_hi"][0]) == (1, 2)
+    assert oracle.select(lg, one, [5], 0.9, 3, False, stat_lambda=1.0)["n_init"][0] == 3
+    # a uniform row: every unit equals the mean, the std is 0 -> all kept
+    assert oracle.select(np.zeros((1, 6)), np.ones(6, np.int64), [2], 0.9, 1, False, stat_lambda=1.0)["n_init"][0] == 6
+
+
+def test_stat_threshold_keeps_an_upper_set(rng):
+    """The kept units are exactly those at or above the threshold, which is a
+    prefix of the probability ranking; the threshold ignores top_p; online
+    Top-k extends the rows below k_h as with Top-p."""
+    for trial in range(10):
+        Ck = int(rng.integers(3, 30))
+        lg = rng.normal(size=(4, Ck)) * rng.uniform(0.5, 3)
+        lg[rng.random(size=lg.shape) < 0.1] = -np.inf
+        lg[:, 0] = 0.0
+        lam = float(rng.uniform(-1, 2))
+        qs = rng.integers(1, 9, size=4)
+        r = oracle.select(lg, np.ones(Ck, np.int64), qs, float(rng.uniform(0.1, 0.9)), 1, True, stat_lambda=lam)
+        r2 = oracle.select(lg, np.ones(Ck, np.int64), qs, 0.5, 1, True, stat_lambda=lam)
+        assert np.array_equal(r["mask"], r2["mask"])
+        for i in range(4):
+            v = np.isfinite(lg[i])
+            p = np.zeros(Ck)
+            e = np.exp(lg[i][v] - lg[i][v].max())
+            p[v] = e / e.sum()
+            th = p[v].mean() + lam * p[v].std()
+            kept = max(int((p[v] >= th).sum()), 1)
+            assert r["n_init"][i] == kept
+            assert r["n_final"][i] == max(kept, min(r["k_h"], int(v.sum())))
