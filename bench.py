@@ -160,9 +160,16 @@ def stored_traffic(workload: str):
 
 def describe(name, w, natural, density):
     base = WORKLOADS[name][1]
+    rule = ""
+    if w.domain != "row":
+        rule += f", {w.domain} competition domain" + (f" (groups of {w.group}, entropy < {w.max_entropy})"
+                                                      if w.domain == "group" else "")
+    if w.rule == "stat":
+        rule += f", statistical threshold mean + {w.stat_lambda} std"
+        return f"{base}{rule}, floor {w.floor}" + (", online per-head top-k" if w.online_topk else "")
     if natural:
-        return f"{base}, top-p {w.top_p}" + (", online per-head top-k" if w.online_topk else "")
-    return f"{base}, fixed {100 * density:g}% density"
+        return f"{base}, top-p {w.top_p}" + (", online per-head top-k" if w.online_topk else "") + rule
+    return f"{base}, fixed {100 * density:g}% density" + rule
 
 
 def main():
@@ -175,6 +182,12 @@ def main():
     ap.add_argument("--cold", action="store_true", help="evict the memory-side cache before every step")
     ap.add_argument("--density", type=float, default=0.1)
     ap.add_argument("--heads", type=int, default=0, help="override the head count")
+    ap.add_argument("--domain", choices=["row", "head", "group"], default=None,
+                    help="selection competition domain (EG-Sparse groups, VMoBA head-global)")
+    ap.add_argument("--group", type=int, default=4, help="heads per group (--domain group)")
+    ap.add_argument("--max-entropy", type=float, default=1.0, help="heads below it are pooled (--domain group)")
+    ap.add_argument("--stat-lambda", type=float, default=None,
+                    help="BSA statistical threshold (mean + lambda std) in place of Top-p")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -189,6 +202,12 @@ def main():
     w = base if args.natural else base.forced_density(args.density)
     if args.heads:
         w = w.with_heads(args.heads)
+    if args.domain is not None:
+        from dataclasses import replace
+        w = replace(w, domain=args.domain, group=args.group, max_entropy=args.max_entropy)
+    if args.stat_lambda is not None:
+        from dataclasses import replace
+        w = replace(w, rule="stat", stat_lambda=args.stat_lambda, floor=max(1, w.floor))
     L.load()
     t_gen = time.perf_counter()
     q, k, v = wl.make_inputs(w, device=dev)
@@ -336,7 +355,8 @@ def main():
            "clustering": f"q {w.q.method} / k {w.k.method}",
            "query_clusters": Cq, "key_clusters": Ck,
            "top_p": w.top_p, "topk_floor": w.floor, "online_topk": w.online_topk,
-           "compensation": w.compensate, "density": density}
+           "compensation": w.compensate, "density": density,
+           "selection_domain": w.domain, "selection_rule": w.rule}
     line = {
         "metric": METRIC,
         "value": eff / (ms_step * 1e-3) / 1e12,

@@ -40,7 +40,8 @@ class ClusterCfg(ctypes.Structure):
 
 class SelectCfg(ctypes.Structure):
     _fields_ = [("top_p", ctypes.c_double), ("topk_floor", I32), ("online_topk", I32),
-                ("size_weighted", I32), ("domain", I32), ("group", I32), ("max_entropy", ctypes.c_double)]
+                ("size_weighted", I32), ("domain", I32), ("group", I32), ("max_entropy", ctypes.c_double),
+                ("rule", I32), ("stat_lambda", ctypes.c_double)]
 
 
 class AttnCfg(ctypes.Structure):
@@ -123,11 +124,16 @@ SA_DOMAIN_ROW, SA_DOMAIN_HEAD, SA_DOMAIN_GROUP = 0, 1, 2
 DOMAINS = {"row": SA_DOMAIN_ROW, "head": SA_DOMAIN_HEAD, "group": SA_DOMAIN_GROUP}
 
 
+SA_RULE_TOP_P, SA_RULE_STAT = 0, 1
+RULES = {"top_p": SA_RULE_TOP_P, "stat": SA_RULE_STAT}
+
+
 def select_cfg(top_p=0.9, topk_floor=1, online_topk=False, size_weighted=True, domain="row", group=1,
-               max_entropy=0.0) -> SelectCfg:
+               max_entropy=0.0, rule="top_p", stat_lambda=0.0) -> SelectCfg:
     d = DOMAINS[domain] if isinstance(domain, str) else int(domain)
+    r = RULES[rule] if isinstance(rule, str) else int(rule)
     return SelectCfg(float(top_p), int(topk_floor), int(bool(online_topk)), int(bool(size_weighted)), d,
-                     int(group), float(max_entropy))
+                     int(group), float(max_entropy), r, float(stat_lambda))
 
 
 def attn_cfg(compensate=False, scale=0.0, events=None) -> AttnCfg:

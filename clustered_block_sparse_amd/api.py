@@ -20,7 +20,8 @@ def cfgs(w: Workload):
                              L.SA_INIT_FIRST, spec.sub_dims)
 
     return (p, cc(w.q), cc(w.k),
-            L.select_cfg(w.top_p, w.floor, w.online_topk, w.size_weighted, w.domain, w.group, w.max_entropy),
+            L.select_cfg(w.top_p, w.floor, w.online_topk, w.size_weighted, w.domain, w.group, w.max_entropy,
+                         w.rule, w.stat_lambda),
             L.attn_cfg(w.compensate))
 
 

@@ -855,7 +855,28 @@ __global__ __launch_bounds__(256) void select_wave(SelectArgs a, const double* _
   const double P = a.top_p;
   int np;
   if (pool_cnt && pool_cnt[row] >= 0) np = pool_cnt[row];  // decided by the row's pool
-  else if (P >= 1.0) np = Vn;
+  else if (a.rule == SA_RULE_STAT) {
+    // BSA statistical threshold: mean + lambda * population std of the row's
+    // probabilities (fixed-order sums), then the units at or above it
+    double pr[SW_M], s1 = 0.0;
+#pragma unroll
+    for (int m = 0; m < SW_M; ++m) {
+      pr[m] = key[m] != NO_KEY ? exp(l[m] - mx) / z : 0.0;
+      s1 += pr[m];
+    }
+    for (int o = 32; o > 0; o >>= 1) s1 += __shfl_xor(s1, o, 64);
+    const double mu = s1 / double(Vn);
+    double s2 = 0.0;
+#pragma unroll
+    for (int m = 0; m < SW_M; ++m)
+      if (key[m] != NO_KEY) s2 += (pr[m] - mu) * (pr[m] - mu);
+    for (int o = 32; o > 0; o >>= 1) s2 += __shfl_xor(s2, o, 64);
+    const double th = mu + a.stat_lambda * sqrt(s2 / double(Vn));
+    int c = 0;
+#pragma unroll
+    for (int m = 0; m < SW_M; ++m) c += (key[m] != NO_KEY && pr[m] >= th) ? 1 : 0;
+    np = wave_sum_i32(c);
+  } else if (P >= 1.0) np = Vn;
   else if (P <= 0.0) np = 0;
   else np = count_through(wave_select(key, ms, (unsigned long long)llrint(P * MASS_ONE), hist[wv]));
   const int nf = a.floor_units > 0 ? min(a.floor_units, Vn) : 0;

@@ -85,7 +85,10 @@ sa_status check_attn_cfg(const sa_attn_cfg* c) {
 sa_status check_select_cfg(const sa_select_cfg* c) {
   if (!c) return SA_ERR_INVALID_ARG;
   if (!isfinite(c->top_p)) return SA_ERR_INVALID_ARG;
-  if (c->top_p <= 0.0 && c->topk_floor <= 0) return SA_ERR_INVALID_ARG;
+  if (c->rule != SA_RULE_TOP_P && c->rule != SA_RULE_STAT) return SA_ERR_INVALID_ARG;
+  if (c->rule == SA_RULE_TOP_P && c->top_p <= 0.0 && c->topk_floor <= 0) return SA_ERR_INVALID_ARG;
+  if (c->rule == SA_RULE_STAT && (c->topk_floor < 1 || !isfinite(c->stat_lambda))) return SA_ERR_INVALID_ARG;
+  if (c->rule == SA_RULE_STAT && c->domain != SA_DOMAIN_ROW) return SA_ERR_UNSUPPORTED;
   if (c->domain != SA_DOMAIN_ROW && c->domain != SA_DOMAIN_HEAD && c->domain != SA_DOMAIN_GROUP)
     return SA_ERR_INVALID_ARG;
   if (c->domain == SA_DOMAIN_GROUP && (c->group < 1 || !isfinite(c->max_entropy))) return SA_ERR_INVALID_ARG;
@@ -345,6 +348,8 @@ sa_status do_select(const sa_problem* p, const sa_select_cfg* c, const sa_cluste
   a.group = c->group;
   a.max_entropy = c->max_entropy;
   a.head_entropy = head_entropy;
+  a.rule = c->rule;
+  a.stat_lambda = c->stat_lambda;
   Arena tmp = s;
   return hip_status(select_run(a, tmp, st));
 }
@@ -497,7 +502,7 @@ SA_API sa_status sa_select(const sa_problem* p, const sa_select_cfg* cfg, const 
               k->sub_dims[0] + k->sub_dims[1] + k->sub_dims[2] != p->d))
     return SA_ERR_INVALID_ARG;
   if (!sub && k->num_clusters > SELECT_MAX) return SA_ERR_UNSUPPORTED;
-  if (sub && cfg->domain != SA_DOMAIN_ROW) return SA_ERR_UNSUPPORTED;
+  if (sub && (cfg->domain != SA_DOMAIN_ROW || cfg->rule != SA_RULE_TOP_P)) return SA_ERR_UNSUPPORTED;
   if (ws_bytes < select_scratch(p->heads, q->num_clusters, k->num_clusters, sub, cfg->domain, cfg->group) + 256)
     return SA_ERR_WORKSPACE;
   Arena s{(char*)ws, ws_bytes, 0};
@@ -561,7 +566,8 @@ SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
   if (qcfg->method == SA_SUBSPACE) return SA_ERR_INVALID_ARG;
   if (qcfg->init != SA_INIT_FIRST || kcfg->init != SA_INIT_FIRST) return SA_ERR_INVALID_ARG;
   if (kcfg->method == SA_SUBSPACE && acfg->compensate) return SA_ERR_UNSUPPORTED;
-  if (kcfg->method == SA_SUBSPACE && scfg->domain != SA_DOMAIN_ROW) return SA_ERR_UNSUPPORTED;
+  if (kcfg->method == SA_SUBSPACE && (scfg->domain != SA_DOMAIN_ROW || scfg->rule != SA_RULE_TOP_P))
+    return SA_ERR_UNSUPPORTED;
   if (kcfg->method != SA_SUBSPACE && clusters_of(p, kcfg) > SELECT_MAX) return SA_ERR_UNSUPPORTED;
   size_t used = 0;
   carve_forward(p, qcfg, kcfg, scfg, acfg, nullptr, &used);

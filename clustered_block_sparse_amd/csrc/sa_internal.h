@@ -150,6 +150,8 @@ struct SelectArgs {
   int domain, group;
   double max_entropy;
   double* head_entropy;   // [H] or null
+  int rule;               // SA_RULE_TOP_P / SA_RULE_STAT
+  double stat_lambda;
 };
 size_t select_scratch(int H, int Cq, int Ck, int subspace, int domain, int group);
 hipError_t select_run(const SelectArgs& a, Arena& scratch, hipStream_t st);

@@ -67,6 +67,8 @@ class Workload:
     domain: str = "row"          # selection competition domain: row | head | group
     group: int = 1               # heads per group (domain "group")
     max_entropy: float = 0.0     # heads below it are pooled (domain "group")
+    rule: str = "top_p"          # initial selection: top_p | stat (statistical threshold)
+    stat_lambda: float = 0.0     # rule "stat": standard deviations above the mean
 
     @property
     def n(self) -> int:

@@ -113,6 +113,17 @@ typedef struct sa_cluster_cfg {
  * Key clusters only (SUBSPACE keys: SA_ERR_UNSUPPORTED). */
 enum { SA_DOMAIN_ROW = 0, SA_DOMAIN_HEAD = 1, SA_DOMAIN_GROUP = 2 };
 
+/* Rule of a row's initial selection.
+ * SA_RULE_TOP_P: the shortest prefix whose proxy mass reaches top_p.
+ * SA_RULE_STAT:  BSA's statistical dynamic threshold ["Bidirectional Sparse
+ *                Attention for Faster Video Diffusion Training", abstract]:
+ *                the units whose proxy probability is at least the row's
+ *                mean plus stat_lambda population standard deviations (over
+ *                its non-empty units); top_p is ignored, the floor (>= 1) and
+ *                the online Top-k apply as with Top-p.  SA_DOMAIN_ROW and key
+ *                clusters only. */
+enum { SA_RULE_TOP_P = 0, SA_RULE_STAT = 1 };
+
 typedef struct sa_select_cfg {
   double top_p;         /* cumulative proxy mass to reach (>= 1: all non-empty);
                            double, so a configured 0.9 is compared as 0.9      */
@@ -124,6 +135,8 @@ typedef struct sa_select_cfg {
   int32_t domain;       /* SA_DOMAIN_ROW (0, default), _HEAD or _GROUP          */
   int32_t group;        /* SA_DOMAIN_GROUP: heads per group (>= 1)              */
   double max_entropy;   /* SA_DOMAIN_GROUP: heads below it are pooled           */
+  int32_t rule;         /* SA_RULE_TOP_P (0, default) or SA_RULE_STAT           */
+  double stat_lambda;   /* SA_RULE_STAT: standard deviations above the mean     */
 } sa_select_cfg;
 
 typedef struct sa_attn_cfg {

@@ -123,3 +123,26 @@ def test_permute_validation(lib):
     assert lib.sa_permute(ctypes.byref(p), ctypes.byref(cl), None, FAKE, None, None) == 1
     assert lib.sa_permute(ctypes.byref(L.problem(1, 256, 96, 4, 8, 8, "f32")), ctypes.byref(cl), FAKE, FAKE,
                           None, None) == 2
+
+
+def test_selection_rule_validation(lib):
+    """Competition domains and the statistical threshold are validated before
+    any work: unknown values, a group below one, a statistical rule without a
+    floor or combined with a pooled domain, and either on subspace keys."""
+    p = L.problem(1, 256, 64, 4, 8, 8, "f32")
+    km = L.cluster_cfg("kmeans", clusters=8)
+    a = L.attn_cfg(False)
+
+    def fwd(sc, kc=km):
+        return lib.sa_forward(ctypes.byref(p), ctypes.byref(km), ctypes.byref(kc), ctypes.byref(sc), ctypes.byref(a),
+                              FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None)
+
+    assert fwd(L.select_cfg(0.9, 1, domain=7)) == 1
+    assert fwd(L.select_cfg(0.9, 1, domain="group", group=0)) == 1
+    assert fwd(L.select_cfg(0.9, 1, rule=5)) == 1
+    assert fwd(L.select_cfg(0.0, 0, rule="stat", stat_lambda=1.0)) == 1          # no floor
+    assert fwd(L.select_cfg(0.9, 1, rule="stat", stat_lambda=float("nan"))) == 1
+    assert fwd(L.select_cfg(0.9, 1, rule="stat", domain="head")) == 5
+    sub = L.cluster_cfg("subspace", clusters=4, sub_dims=(16, 24, 24))
+    assert fwd(L.select_cfg(0.9, 1, domain="head"), sub) == 5
+    assert fwd(L.select_cfg(0.9, 1, rule="stat", stat_lambda=1.0), sub) == 5

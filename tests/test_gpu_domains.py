@@ -160,3 +160,33 @@ def test_domains_full_size_group():
     assert r["pools"] == [[1, 3]]
     del q, k, v, res
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("w", [
+    replace(WAN6, name="wan6_stat1", rule="stat", stat_lambda=1.0),
+    replace(WAN6, name="wan6_stat0_floor3", rule="stat", stat_lambda=0.0, floor=3),
+    replace(MID4, name="mid4_stat05_online", rule="stat", stat_lambda=0.5),
+    replace(wl.TABULAR, name="tab_small_stat2", heads=2, width=8292, rule="stat", stat_lambda=2.0),
+], ids=lambda w: w.name)
+def test_stat_threshold_rule(w):
+    """BSA's statistical dynamic threshold in place of Top-p: every row keeps
+    the units whose proxy probability reaches mean + lambda * std of its row."""
+    say(f"[stat rule] {w.name} H={w.heads} N={w.n} lambda={w.stat_lambda} floor={w.floor} online={w.online_topk}")
+    q, k, v = inputs(w)
+    qt, kt, mask, counts, init, ktop, ent, ws = run_select(w, q, k)
+    lg, qs = oracle_logits(w, qt, kt, list(range(w.heads)))
+    Ck = kt.num_clusters
+    units = np.ones(Ck, np.int64)
+    gm = unpack_mask(mask, Ck)
+    for h in range(w.heads):
+        def redo(kh, h=h):
+            return oracle.select(lg[h], units, qs[h], w.top_p, w.floor, w.online_topk, k_h=kh,
+                                 stat_lambda=w.stat_lambda)
+
+        s = oracle.select(lg[h], units, qs[h], w.top_p, w.floor, w.online_topk, stat_lambda=w.stat_lambda)
+        check_selection_head(gm[h], counts[h].cpu().numpy(), init[h].cpu().numpy(), ktop[h], s, redo, qs[h], w.n,
+                             w.online_topk, f"head {h}")
+        say(f"    mean clusters/row {s['n_final'].mean():.1f} of {Ck}")
+    o2, mask2 = api.forward(q, k, v, w)
+    torch.cuda.synchronize()
+    assert torch.equal(mask, mask2)
