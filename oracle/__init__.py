@@ -32,6 +32,7 @@ from .cbsa import (  # noqa: F401
     permute,
     pool_counts,
     proxy_probs,
+    raster_blocks,
     select,
     select_domains,
     stat_threshold,

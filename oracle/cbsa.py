@@ -242,6 +242,29 @@ def subspace_cluster(k, dims, Cs, iters):
 
 
 # --------------------------------------------------------------------------
+# Clustering-free raster blocks (VMoBA, English abstract, item (1): a
+# layer-wise recurrent 1D-2D-3D block partition)
+# --------------------------------------------------------------------------
+
+def raster_blocks(frames, height, width, bt, bh, bw):
+    """Block label of every token of an F x H x W grid (token n = (t*H + h)*W
+    + w) for blocks of bt x bh x bw tokens.
+
+    Reading (VMoBA gives the 1D-2D-3D scheme, not the block shapes): a block
+    partition along one axis (1D: bt consecutive frames, (bt, H, W)), two
+    (2D: spatial tiles through all frames, (F, bh, bw)) or three (3D: cubes);
+    edge blocks keep what remains; blocks are numbered in raster order of
+    their (t, h, w) block coordinates.  Returns (labels [N], C)."""
+    nt, nh, nw = -(-frames // bt), -(-height // bh), -(-width // bw)
+    labels = np.empty(frames * height * width, dtype=np.int64)
+    for t in range(frames):
+        for h in range(height):
+            for w in range(width):
+                labels[(t * height + h) * width + w] = ((t // bt) * nh + h // bh) * nw + w // bw
+    return labels, nt * nh * nw
+
+
+# --------------------------------------------------------------------------
 # Permutation into cluster order and cluster means
 # --------------------------------------------------------------------------
 
@@ -696,12 +719,13 @@ def dense_attention(q, k, v, scale):
 
 @dataclass
 class ClusterCfg:
-    method: str = "kmeans"      # "kmeans" | "bisect" | "subspace" (keys only)
+    method: str = "kmeans"      # "kmeans" | "bisect" | "subspace" (keys only) | "raster"
     clusters: int = 8           # kmeans clusters; bisect derives ceil(N/leaf)
     leaf: int = 128             # bisect leaf size
     iters: int = 5
-    sub_dims: tuple = (16, 24, 24)
+    sub_dims: tuple = (16, 24, 24)   # subspace: t/h/w column widths; raster: block extents
     sub_clusters: int = 32
+    grid: tuple = (0, 0, 0)          # raster: frames, height, width of the token grid
 
 
 @dataclass
@@ -734,6 +758,9 @@ def cluster_head(x, cfg: ClusterCfg):
     elif cfg.method == "subspace":
         r = subspace_cluster(x, cfg.sub_dims, cfg.sub_clusters, cfg.iters)
         C = cfg.sub_clusters ** 3
+    elif cfg.method == "raster":
+        labels, C = raster_blocks(*cfg.grid, *cfg.sub_dims)
+        r = dict(labels=labels)
     else:
         raise ValueError(cfg.method)
     perm, offsets = permute(r["labels"], C)
