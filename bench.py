@@ -188,6 +188,10 @@ def main():
     ap.add_argument("--max-entropy", type=float, default=1.0, help="heads below it are pooled (--domain group)")
     ap.add_argument("--stat-lambda", type=float, default=None,
                     help="BSA statistical threshold (mean + lambda std) in place of Top-p")
+    ap.add_argument("--raster", type=str, default=None,
+                    help="clustering-free raster blocks bt,bh,bw for queries and keys (VMoBA 1D/2D/3D)")
+    ap.add_argument("--quality", action="store_true",
+                    help="relative error of O against dense fp32 attention on sampled query rows")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -205,6 +209,13 @@ def main():
     if args.domain is not None:
         from dataclasses import replace
         w = replace(w, domain=args.domain, group=args.group, max_entropy=args.max_entropy)
+    if args.raster is not None:
+        from dataclasses import replace
+        ext = tuple(int(x) for x in args.raster.split(","))
+        spec = wl.ClusterSpec("raster", sub_dims=ext)
+        w = replace(w, q=spec, k=spec)
+        if not args.natural:
+            w = w.forced_density(args.density)
     if args.stat_lambda is not None:
         from dataclasses import replace
         w = replace(w, rule="stat", stat_lambda=args.stat_lambda, floor=max(1, w.floor))
@@ -322,6 +333,21 @@ def main():
     dense_list = [x for x in (dense_own, dense_sdpa) if x is not None]
     dense_best = min(dense_list) if dense_list else None
 
+    quality = None
+    if args.quality:
+        # O of sampled query rows against softmax(q k^T / sqrt(d)) v in fp32
+        gen = torch.Generator(device="cpu").manual_seed(1)
+        errs = []
+        for h in (0, w.heads - 1):
+            rows = torch.randperm(w.n, generator=gen)[:2048].to(dev)
+            qh = q[h, rows].float()
+            s_ = (qh @ k[h].float().T) / math.sqrt(w.d)
+            ref = torch.softmax(s_, dim=-1) @ v[h].float()
+            got = o[h, rows].float()
+            errs.append(float((got - ref).norm() / ref.norm()))
+            del s_, ref
+        quality = {"rel_l2_error_vs_dense": float(np.mean(errs)), "rows": 2 * 2048,
+                   "heads": [0, w.heads - 1]}
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v)
@@ -352,7 +378,7 @@ def main():
 
     cfg = {"workload": describe(args.workload, w, args.natural, args.density),
            "heads": w.heads, "n": w.n, "d": w.d, "grid": [w.frames, w.height, w.width],
-           "clustering": f"q {w.q.method} / k {w.k.method}",
+           "clustering": f"q {w.q.method} / k {w.k.method}" + (f" {tuple(w.q.sub_dims)}" if w.q.method == "raster" else ""),
            "query_clusters": Cq, "key_clusters": Ck,
            "top_p": w.top_p, "topk_floor": w.floor, "online_topk": w.online_topk,
            "compensation": w.compensate, "density": density,
@@ -397,6 +423,8 @@ def main():
     }
     if gemm is not None:
         line["gemm_probe_bf16"] = gemm
+    if quality is not None:
+        line["quality"] = quality
     print(json.dumps(line), flush=True)
 
 

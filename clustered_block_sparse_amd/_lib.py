@@ -19,11 +19,11 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsa.so")
 
 SA_F32, SA_BF16 = 0, 1
-SA_KMEANS, SA_BISECT, SA_SUBSPACE = 0, 1, 2
+SA_KMEANS, SA_BISECT, SA_SUBSPACE, SA_RASTER = 0, 1, 2, 3
 SA_INIT_FIRST, SA_INIT_GIVEN = 0, 1
 STATUS = {0: "SA_OK", 1: "SA_ERR_INVALID_ARG", 2: "SA_ERR_SHAPE", 3: "SA_ERR_DTYPE",
           4: "SA_ERR_WORKSPACE", 5: "SA_ERR_UNSUPPORTED", 6: "SA_ERR_HIP"}
-METHODS = {"kmeans": SA_KMEANS, "bisect": SA_BISECT, "subspace": SA_SUBSPACE}
+METHODS = {"kmeans": SA_KMEANS, "bisect": SA_BISECT, "subspace": SA_SUBSPACE, "raster": SA_RASTER}
 
 I32 = ctypes.c_int32
 

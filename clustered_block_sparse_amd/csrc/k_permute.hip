@@ -310,6 +310,15 @@ __global__ __launch_bounds__(256) void gather_means_kernel(const T* __restrict__
   }
 }
 
+__global__ void raster_label_kernel(int32_t* __restrict__ labels, int N, int height, int width, int bt, int bh,
+                                    int bw, int nh, int nw) {
+  const int h = blockIdx.y;
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  const int w = n % width, r = n / width, y = r % height, t = r / height;
+  labels[size_t(h) * N + n] = ((t / bt) * nh + y / bh) * nw + w / bw;
+}
+
 __global__ __launch_bounds__(256) void labels_from_off_kernel(const int32_t* __restrict__ perm,
                                                               const int32_t* __restrict__ off,
                                                               int32_t* __restrict__ labels, int N,
@@ -420,6 +429,14 @@ hipError_t gather_means(const void* x, int dtype, int d, const int32_t* perm, co
   else
     gather_means_kernel<bf16_t><<<g, 256, 0, st>>>((const bf16_t*)x, (bf16_t*)x_perm, perm, offsets, N, C, d,
                                                    means);
+  return hipGetLastError();
+}
+
+hipError_t raster_labels(int32_t* labels, int H, int frames, int height, int width, const int* ext,
+                         hipStream_t st) {
+  const int N = frames * height * width;
+  raster_label_kernel<<<dim3(ceil_div(N, 256), H), 256, 0, st>>>(labels, N, height, width, ext[0], ext[1], ext[2],
+                                                                 ceil_div(height, ext[1]), ceil_div(width, ext[2]));
   return hipGetLastError();
 }
 

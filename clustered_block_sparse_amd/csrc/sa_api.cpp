@@ -37,6 +37,11 @@ int clusters_of(const sa_problem* p, const sa_cluster_cfg* c) {
     case SA_KMEANS: return c->clusters;
     case SA_BISECT: return c->leaf >= 1 ? ceil_div(p->n, c->leaf) : -1;
     case SA_SUBSPACE: return c->clusters * c->clusters * c->clusters;
+    case SA_RASTER:
+      for (int k = 0; k < 3; ++k)
+        if (c->sub_dims[k] < 1) return -1;
+      return ceil_div(p->frames, c->sub_dims[0]) * ceil_div(p->height, c->sub_dims[1]) *
+             ceil_div(p->width, c->sub_dims[2]);
     default: return -1;
   }
 }
@@ -69,6 +74,14 @@ sa_status check_cluster_cfg(const sa_problem* p, const sa_cluster_cfg* c) {
         sum += c->sub_dims[s];
       }
       if (sum != p->d) return SA_ERR_SHAPE;
+      return SA_OK;
+    }
+    case SA_RASTER: {
+      if (c->init != SA_INIT_FIRST) return SA_ERR_INVALID_ARG;
+      const int ext[3] = {p->frames, p->height, p->width};
+      for (int k = 0; k < 3; ++k)
+        if (c->sub_dims[k] < 1 || c->sub_dims[k] > ext[k]) return SA_ERR_INVALID_ARG;
+      if (clusters_of(p, c) > 65536) return SA_ERR_SHAPE;
       return SA_OK;
     }
     default: return SA_ERR_INVALID_ARG;
@@ -115,6 +128,7 @@ size_t cluster_scratch(const sa_problem* p, const sa_cluster_cfg* c) {
       return std::max(means_scratch(H, N, c->clusters, p->d), kmeans_step_scratch(H, N, c->clusters, p->d)) +
              label_sort_scratch(H, N, c->clusters) + 512;
     case SA_BISECT: return bisect_scratch(H, N, p->d, c->leaf) + 256;
+    case SA_RASTER: return label_sort_scratch(H, N, clusters_of(p, c)) + 256;
     case SA_SUBSPACE: {
       Arena a{nullptr, 0, 0};
       a.get<int32_t>(size_t(3) * H * N);  // slice labels
@@ -255,6 +269,14 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
       if (e == hipSuccess)
         e = cluster_means(x, dt, d, 0, d, out->perm, out->offsets, H, N, C, out->centroids, d, true, msc, st);
     }
+  } else if (c->method == SA_RASTER) {
+    // block labels from the grid, then the same counting sort and one pass of
+    // row gather + member means as the bisection's outputs
+    e = raster_labels(out->labels, H, p->frames, p->height, p->width, c->sub_dims, st);
+    Arena tmp = s;
+    if (e == hipSuccess) e = label_sort(out->labels, out->perm, out->offsets, H, N, C, tmp, st);
+    if (e == hipSuccess) e = gather_means(x, dt, d, out->perm, out->offsets, H, N, C, out->x_perm, out->centroids, st);
+    return hip_status(e);
   } else if (c->method == SA_BISECT) {
     Arena tmp = s;
     e = bisect_run(x, x, H, dt, H, N, d, c->leaf, c->iters, out->perm, out->perm, out->offsets,

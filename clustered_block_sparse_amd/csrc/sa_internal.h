@@ -92,6 +92,11 @@ hipError_t cluster_means(const void* x, int dtype, int d, int col0, int dc, cons
                          const int32_t* offsets, int H, int N, int C, float* out, int out_stride,
                          bool keep_empty, float* scratch, hipStream_t st);
 
+// raster block label of every token of a frames x height x width grid for
+// blocks of ext[0] x ext[1] x ext[2] tokens (the same labels for every head)
+hipError_t raster_labels(int32_t* labels, int H, int frames, int height, int width, const int* ext,
+                         hipStream_t st);
+
 // labels[h][perm[h][p]] = cluster of position p, from offsets
 hipError_t labels_from_offsets(const int32_t* perm, const int32_t* offsets, int32_t* labels, int H,
                                int N, int C, hipStream_t st);

@@ -68,8 +68,15 @@ enum { SA_F32 = 0, SA_BF16 = 1 };
  * SA_SUBSPACE: keys only [SCOPE]: the t/h/w RoPE column slices (`sub_dims`)
  *              are k-means clustered independently with `clusters` centroids
  *              each; a key's cluster is its combo
- *              g = (a_t*clusters + a_h)*clusters + a_w, C = clusters^3. */
-enum { SA_KMEANS = 0, SA_BISECT = 1, SA_SUBSPACE = 2 };
+ *              g = (a_t*clusters + a_h)*clusters + a_w, C = clusters^3.
+ * SA_RASTER:   no clustering ["VMoBA: Mixture-of-Block Attention for Video
+ *              Diffusion Models", English abstract, item (1): a 1D-2D-3D
+ *              block partition]: the frames x height x width grid is cut
+ *              into boxes of sub_dims = (bt, bh, bw) tokens (edge boxes keep
+ *              what remains), numbered in raster order of their block
+ *              coordinates; 1D = (bt, height, width), 2D = (frames, bh, bw),
+ *              3D = cubes.  C = ceil(F/bt)*ceil(H/bh)*ceil(W/bw). */
+enum { SA_KMEANS = 0, SA_BISECT = 1, SA_SUBSPACE = 2, SA_RASTER = 3 };
 enum { SA_INIT_FIRST = 0, SA_INIT_GIVEN = 1 };
 
 typedef struct sa_problem {
@@ -88,7 +95,8 @@ typedef struct sa_cluster_cfg {
   int32_t init;        /* KMEANS / SUBSPACE: SA_INIT_FIRST, or SA_INIT_GIVEN = start
                           from the centroids already in out->centroids (SUBSPACE:
                           the expanded [3*clusters, d] layout below)               */
-  int32_t sub_dims[3]; /* SUBSPACE column widths (t, h, w), summing to d            */
+  int32_t sub_dims[3]; /* SUBSPACE column widths (t, h, w), summing to d;
+                          RASTER block extents (bt, bh, bw)                        */
 } sa_cluster_cfg;
 
 /* Competition domains of the selection.
