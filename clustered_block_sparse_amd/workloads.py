@@ -74,17 +74,21 @@ class Workload:
     def n(self) -> int:
         return self.frames * self.height * self.width
 
+    def _clusters(self, spec: ClusterSpec) -> int:
+        if spec.method == "bisect":
+            return -(-self.n // spec.leaf)
+        if spec.method == "subspace":
+            return spec.clusters ** 3
+        if spec.method == "raster":
+            bt, bh, bw = spec.sub_dims
+            return -(-self.frames // bt) * -(-self.height // bh) * -(-self.width // bw)
+        return spec.clusters
+
     def key_clusters(self) -> int:
-        if self.k.method == "bisect":
-            return -(-self.n // self.k.leaf)
-        if self.k.method == "subspace":
-            return self.k.clusters ** 3
-        return self.k.clusters
+        return self._clusters(self.k)
 
     def query_clusters(self) -> int:
-        if self.q.method == "bisect":
-            return -(-self.n // self.q.leaf)
-        return self.q.clusters
+        return self._clusters(self.q)
 
     def forced_density(self, rho: float = 0.1) -> "Workload":
         """Fixed-density variant: Top-p off, floor = round(rho * units), online
