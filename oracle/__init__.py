@@ -17,6 +17,7 @@ from .cbsa import (  # noqa: F401
     HeadResult,
     SelectCfg,
     attention,
+    attention_backward,
     bisect,
     bisect_split,
     cluster_head,

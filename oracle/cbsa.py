@@ -704,6 +704,38 @@ def attention(q, k, v, q_perm, q_off, k_perm, k_off, mask, scale,
     return O
 
 
+def attention_backward(q, k, v, q_perm, q_off, k_perm, k_off, mask, scale, dO):
+    """Gradients of the block-sparse attention without compensation (the
+    trainable use of block-sparse attention: "Bidirectional Sparse Attention
+    for Faster Video Diffusion Training", abstract; VMoBA, English abstract)
+    with respect to q, k and v, given the output gradient dO (original token
+    order).  For a query n of query cluster i over the keys of its selected
+    clusters: P_nm = softmax_m(s_nm), s_nm = <q_n, k_m> scale, and
+
+      dV_m += P_nm dO_n,   dP_nm = <dO_n, v_m>,   D_n = sum_m P_nm dP_nm,
+      dS_nm = P_nm (dP_nm - D_n),   dQ_n = scale sum_m dS_nm k_m,
+      dK_m += scale dS_nm q_n.
+
+    Returns (dq, dk, dv) in original token order."""
+    q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for i in range(len(q_off) - 1):
+        rows = q_perm[q_off[i]:q_off[i + 1]]
+        sel = np.nonzero(mask[i])[0]
+        if len(rows) == 0 or len(sel) == 0:
+            continue
+        keys = np.concatenate([k_perm[k_off[j]:k_off[j + 1]] for j in sel])
+        s = (q[rows] @ k[keys].T) * scale
+        P = np.exp(s - s.max(axis=1, keepdims=True))
+        P /= P.sum(axis=1, keepdims=True)
+        dv[keys] += P.T @ dO[rows]
+        dP = dO[rows] @ v[keys].T
+        dS = P * (dP - (P * dP).sum(axis=1, keepdims=True))
+        dq[rows] += scale * (dS @ k[keys])
+        dk[keys] += scale * (dS.T @ q[rows])
+    return dq, dk, dv
+
+
 def dense_attention(q, k, v, scale):
     """softmax(q k^T * scale) v for one head."""
     q, k, v = _f64(q), _f64(k), _f64(v)
