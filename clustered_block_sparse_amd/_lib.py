@@ -89,12 +89,16 @@ def load():
                                          vp, ctypes.c_size_t, vp]
     lib.sa_block_sparse_attn_noalloc.argtypes = [P(Problem), P(AttnCfg), P(Clusters), P(Clusters), vp, vp, vp,
                                                  vp, vp]
+    lib.sa_block_sparse_attn_bwd_workspace_size.argtypes = [P(Problem), I32, I32, P(ctypes.c_size_t)]
+    lib.sa_block_sparse_attn_bwd.argtypes = [P(Problem), P(AttnCfg), P(Clusters), P(Clusters), vp, vp, vp, vp, vp,
+                                             vp, vp, vp, ctypes.c_size_t, vp]
     lib.sa_forward.argtypes = [P(Problem), P(ClusterCfg), P(ClusterCfg), P(SelectCfg), P(AttnCfg), vp, vp,
                                vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sa_status_string.argtypes = [I32]
     lib.sa_status_string.restype = ctypes.c_char_p
     for fn in ("sa_workspace_size", "sa_cluster", "sa_cluster_qk", "sa_permute", "sa_select",
-               "sa_block_sparse_attn", "sa_block_sparse_attn_noalloc", "sa_forward"):
+               "sa_block_sparse_attn", "sa_block_sparse_attn_noalloc", "sa_forward",
+               "sa_block_sparse_attn_bwd_workspace_size", "sa_block_sparse_attn_bwd"):
         getattr(lib, fn).restype = I32
     _lib = lib
     return lib
@@ -257,6 +261,21 @@ def sa_block_sparse_attn_noalloc(p: Problem, cfg: AttnCfg, q: ClusterTensors, k:
            load().sa_block_sparse_attn_noalloc(ctypes.byref(p), ctypes.byref(cfg), ctypes.byref(q.struct()),
                                                ctypes.byref(k.struct()), _ptr(v_perm), _ptr(v_means), _ptr(mask),
                                                _ptr(o), _stream()))
+
+
+def sa_block_sparse_attn_bwd_workspace_size(p: Problem, q_clusters: int, k_clusters: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check("sa_block_sparse_attn_bwd_workspace_size",
+           load().sa_block_sparse_attn_bwd_workspace_size(ctypes.byref(p), q_clusters, k_clusters, ctypes.byref(out)))
+    return int(out.value)
+
+
+def sa_block_sparse_attn_bwd(p: Problem, cfg: AttnCfg, q: ClusterTensors, k: ClusterTensors, v_perm, mask, o, d_o,
+                             dq, dk, dv, ws):
+    _check("sa_block_sparse_attn_bwd",
+           load().sa_block_sparse_attn_bwd(ctypes.byref(p), ctypes.byref(cfg), ctypes.byref(q.struct()),
+                                           ctypes.byref(k.struct()), _ptr(v_perm), _ptr(mask), _ptr(o), _ptr(d_o),
+                                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()))
 
 
 def sa_forward(p: Problem, qcfg: ClusterCfg, kcfg: ClusterCfg, scfg: SelectCfg, acfg: AttnCfg, q, k, v, o,

@@ -22,7 +22,8 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libsa.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["sa_api.cpp", "k_permute.hip", "k_kmeans.hip", "k_bisect.hip", "k_select.hip", "k_attn.hip"]
+SOURCES = ["sa_api.cpp", "k_permute.hip", "k_kmeans.hip", "k_bisect.hip", "k_select.hip", "k_attn.hip",
+           "k_attn_bwd.hip"]
 
 CFLAGS = [
     "-x", "hip", "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

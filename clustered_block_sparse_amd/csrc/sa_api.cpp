@@ -574,6 +574,54 @@ SA_API sa_status sa_block_sparse_attn_noalloc(const sa_problem* p, const sa_attn
   return do_attn(p, cfg, q, k, v_perm, v_means, mask, o, rows, maxt, s, (hipStream_t)stream);
 }
 
+SA_API sa_status sa_block_sparse_attn_bwd_workspace_size(const sa_problem* p, int32_t q_clusters,
+                                                         int32_t k_clusters, size_t* bytes) {
+  sa_status st = check_problem(p);
+  if (st != SA_OK) return st;
+  if (!bytes || q_clusters < 1 || k_clusters < 1) return SA_ERR_INVALID_ARG;
+  *bytes = attn_bwd_scratch(p->heads, p->n, p->d, q_clusters, k_clusters) + 256;
+  return SA_OK;
+}
+
+SA_API sa_status sa_block_sparse_attn_bwd(const sa_problem* p, const sa_attn_cfg* cfg,
+                                          const sa_clusters* q, const sa_clusters* k,
+                                          const void* v_perm, const uint32_t* mask, const void* o,
+                                          const void* d_o, float* dq, float* dk, float* dv, void* ws,
+                                          size_t ws_bytes, void* stream) {
+  sa_status st = check_problem(p);
+  if (st != SA_OK) return st;
+  if (p->dtype != SA_BF16) return SA_ERR_DTYPE;
+  if (!cfg || !clusters_ok(q, true) || !clusters_ok(k, true) || !v_perm || !mask || !o || !d_o || !dq || !dk ||
+      !dv || !ws)
+    return SA_ERR_INVALID_ARG;
+  if ((st = check_attn_cfg(cfg)) != SA_OK) return st;
+  if (cfg->compensate) return SA_ERR_UNSUPPORTED;
+  if (ws_bytes < attn_bwd_scratch(p->heads, p->n, p->d, q->num_clusters, k->num_clusters) + 256)
+    return SA_ERR_WORKSPACE;
+  AttnBwdArgs a{};
+  a.H = p->heads;
+  a.N = p->n;
+  a.d = p->d;
+  a.Cq = q->num_clusters;
+  a.Ck = k->num_clusters;
+  a.scale = cfg->scale > 0.f ? cfg->scale : float(1.0 / sqrt(double(p->d)));
+  a.q_perm = q->x_perm;
+  a.q_idx = q->perm;
+  a.q_off = q->offsets;
+  a.k_perm = k->x_perm;
+  a.k_idx = k->perm;
+  a.k_off = k->offsets;
+  a.v_perm = v_perm;
+  a.mask = mask;
+  a.O = o;
+  a.dO = d_o;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  Arena s{(char*)ws, ws_bytes, 0};
+  return hip_status(attn_bwd_run(a, s, (hipStream_t)stream));
+}
+
 SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
                             const sa_cluster_cfg* kcfg, const sa_select_cfg* scfg,
                             const sa_attn_cfg* acfg, const void* q, const void* k, const void* v,

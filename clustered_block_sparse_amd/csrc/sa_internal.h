@@ -181,6 +181,27 @@ struct AttnArgs {
 };
 size_t attn_scratch(int H, int N, int d, int Cq, int Ck, int tile_rows, int compensate, int dtype,
                     int max_tiles);
+
+// k_attn_bwd.hip --------------------------------------------------------------
+struct AttnBwdArgs {
+  int H, N, d, Cq, Ck;
+  float scale;
+  const void* q_perm;     // bf16 [H][N][d] query-cluster order
+  const int32_t* q_idx;   // [H][N]
+  const int32_t* q_off;   // [H][Cq+1]
+  const void* k_perm;     // bf16 [H][N][d] key-cluster order
+  const int32_t* k_idx;   // [H][N]
+  const int32_t* k_off;   // [H][Ck+1]
+  const void* v_perm;     // bf16 [H][N][d] key-cluster order
+  const uint32_t* mask;   // [H][Cq][W]
+  const void* O;          // bf16 [H][N][d] forward output, original order
+  const void* dO;         // bf16 [H][N][d] original order
+  float* dq;              // f32 [H][N][d] original order
+  float* dk;
+  float* dv;
+};
+size_t attn_bwd_scratch(int H, int N, int d, int Cq, int Ck);
+hipError_t attn_bwd_run(const AttnBwdArgs& a, Arena& scratch, hipStream_t st);
 hipError_t attn_run(const AttnArgs& a, Arena& scratch, hipStream_t st);
 
 }  // namespace sa

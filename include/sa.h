@@ -280,6 +280,28 @@ SA_API sa_status sa_block_sparse_attn_noalloc(const sa_problem* p, const sa_attn
                                               const void* v_perm, const float* v_means,
                                               const uint32_t* mask, void* o, void* stream);
 
+/* Backward of sa_block_sparse_attn without compensation: the gradients of
+ * Q, K and V for an output gradient dO, over the same selected key clusters
+ * (the trainable use of block-sparse attention: "Bidirectional Sparse
+ * Attention for Faster Video Diffusion Training", abstract; "VMoBA:
+ * Mixture-of-Block Attention for Video Diffusion Models", English abstract).
+ * With P_nm = softmax over the selected keys m of s_nm = <q_n, k_m> scale:
+ *   dV_m = sum_n P_nm dO_n,  dS_nm = P_nm (<dO_n, v_m> - <dO_n, O_n>),
+ *   dQ_n = scale sum_m dS_nm k_m,  dK_m = scale sum_n dS_nm q_n.
+ *   q, k     clusters of sa_cluster (x_perm used), v_perm as for the forward
+ *   mask     the selection the forward used
+ *   o, d_o   bf16 [H, n, d] forward output and its gradient, original order
+ *   dq, dk, dv  f32 [H, n, d] gradients, original order (every row written)
+ * bf16 only (SA_ERR_DTYPE otherwise); compensation has no backward here.
+ * Workspace: sa_block_sparse_attn_bwd_workspace_size() bytes. */
+SA_API sa_status sa_block_sparse_attn_bwd_workspace_size(const sa_problem* p, int32_t q_clusters,
+                                                         int32_t k_clusters, size_t* bytes);
+SA_API sa_status sa_block_sparse_attn_bwd(const sa_problem* p, const sa_attn_cfg* cfg,
+                                          const sa_clusters* q, const sa_clusters* k,
+                                          const void* v_perm, const uint32_t* mask, const void* o,
+                                          const void* d_o, float* dq, float* dk, float* dv, void* ws,
+                                          size_t ws_bytes, void* stream);
+
 /* The whole path: cluster Q and K, permute V, select, attend.
  * o dtype [H, n, d] original order; mask as in sa_select. */
 SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,

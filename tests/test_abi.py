@@ -146,3 +146,24 @@ def test_selection_rule_validation(lib):
     sub = L.cluster_cfg("subspace", clusters=4, sub_dims=(16, 24, 24))
     assert fwd(L.select_cfg(0.9, 1, domain="head"), sub) == 5
     assert fwd(L.select_cfg(0.9, 1, rule="stat", stat_lambda=1.0), sub) == 5
+
+
+def test_backward_validation(lib):
+    """The backward takes bf16 only, no compensation, a workspace of the size
+    its query function reports, and non-null tensors; each is checked before
+    any work."""
+    p = L.problem(1, 256, 64, 4, 8, 8, "bf16")
+    cl = L.Clusters(FAKE, FAKE, FAKE, FAKE, FAKE, 8, 0, 0, (L.I32 * 3)(0, 0, 0))
+    need = L.sa_block_sparse_attn_bwd_workspace_size(p, 8, 8)
+    assert need > 256 * 64 * 2
+
+    def bwd(prob=p, a=L.attn_cfg(False), ws_bytes=need, d_o=FAKE):
+        return lib.sa_block_sparse_attn_bwd(ctypes.byref(prob), ctypes.byref(a), ctypes.byref(cl), ctypes.byref(cl),
+                                            FAKE, FAKE, FAKE, d_o, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+
+    assert bwd(prob=L.problem(1, 256, 64, 4, 8, 8, "f32")) == 3
+    assert bwd(a=L.attn_cfg(True)) == 5
+    assert bwd(ws_bytes=need - 1) == 4
+    assert bwd(d_o=None) == 1
+    out = ctypes.c_size_t(0)
+    assert lib.sa_block_sparse_attn_bwd_workspace_size(ctypes.byref(p), 0, 8, ctypes.byref(out)) == 1

@@ -1,0 +1,93 @@
+"""GPU parity of the block-sparse attention backward (sa_block_sparse_attn_bwd)
+against the fp64 oracle (oracle.attention_backward) given the GPU's own
+clusters, selection and forward output: bisection (a partial last leaf), k-means
+(uneven clusters) and d = 64, at fixed density and with the natural Top-p.
+
+Tolerance (bf16 inputs, fp32 gradients): the kernels round P and dS to bf16 for
+the matrix cores (2^-9 relative each) and take D_n = <dO_n, O_n> from the
+forward's bf16 output.  The rows of dS sum to zero, so dQ and dK are sums with
+cancellation: an emulation of these roundings in fp64 on the small Wan case
+gives dq errors of 0.55% of its mean magnitude (0.9% of its largest), dk 0.19%
+(0.34%), dv 0.16% (0.13%).  The bounds are about twice that: dq and dk mean-abs
+<= 1.2e-2 of the mean reference magnitude and max-abs <= 3e-2 of the largest,
+dv 4e-3 and 1.5e-2.  A dropped term (D, a selected cluster, the scale) moves
+the mean error by whole percents."""
+
+from __future__ import annotations
+
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from clustered_block_sparse_amd import _lib as L
+from clustered_block_sparse_amd import api
+
+from gpu_helpers import DEV, MID_S, TAB_S, WAN_S, inputs, say, scale_of, to_np, unpack_mask, workspace_for
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"dq": (3e-2, 1.2e-2), "dk": (3e-2, 1.2e-2), "dv": (1.5e-2, 4e-3)}  # (max, mean), relative
+
+CASES = [replace(WAN_S.forced_density(0.1), compensate=False, name="wan_small_fixed"),
+         replace(WAN_S, compensate=False, name="wan_small_p09"),
+         replace(MID_S, compensate=False, name="mid_small_kmeans"),
+         replace(TAB_S.forced_density(0.1), compensate=False, name="tab_small_d64")]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load()
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: w.name)
+def test_backward(w):
+    say(f"[backward] {w.name} H={w.heads} N={w.n} d={w.d} P={w.top_p} floor={w.floor}")
+    q, k, v = inputs(w)
+    p, qc, kc, sc, ac = api.cfgs(w)
+    ws = workspace_for(p, qc, kc, sc, ac)
+    qt = L.alloc_clusters(p, qc, DEV, q.dtype)
+    kt = L.alloc_clusters(p, kc, DEV, k.dtype)
+    L.sa_cluster_qk(p, qc, kc, q, k, qt, kt, ws)
+    Cq, Ck = qt.num_clusters, kt.num_clusters
+    v_perm = torch.empty_like(v)
+    L.sa_permute(p, kt, v, v_perm, None)
+    mask = torch.empty(w.heads, Cq, L.mask_words(Ck), dtype=torch.int32, device=DEV)
+    counts = torch.empty(w.heads, Cq, dtype=torch.int32, device=DEV)
+    ktop = torch.empty(w.heads, dtype=torch.int32, device=DEV)
+    L.sa_select(p, sc, qt, kt, mask, counts, None, ktop, ws)
+    o = torch.empty_like(q)
+    L.sa_block_sparse_attn(p, ac, qt, kt, v_perm, None, mask, o, ws)
+    g = torch.Generator(device="cpu").manual_seed(7)
+    d_o = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(DEV)
+    wsb = L.workspace(L.sa_block_sparse_attn_bwd_workspace_size(p, Cq, Ck), DEV)
+    grads = [torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV) for _ in range(3)]
+    L.sa_block_sparse_attn_bwd(p, ac, qt, kt, v_perm, mask, o, d_o, *grads, wsb)
+    again = [torch.empty_like(x) for x in grads]
+    L.sa_block_sparse_attn_bwd(p, ac, qt, kt, v_perm, mask, o, d_o, *again, wsb)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(grads, again):
+        assert torch.equal(a_, b_), "backward is not deterministic"
+    gm = unpack_mask(mask, Ck)
+    qs, ks, vs, gs = to_np(q), to_np(k), to_np(v), to_np(d_o)
+    bad = []
+    for h in range(w.heads):
+        ref = oracle.attention_backward(qs[h], ks[h], vs[h], qt.perm[h].cpu().numpy(), qt.offsets[h].cpu().numpy(),
+                                        kt.perm[h].cpu().numpy(), kt.offsets[h].cpu().numpy(), gm[h], scale_of(w),
+                                        gs[h])
+        for name, got, want in zip(("dq", "dk", "dv"), grads, ref):
+            got = got[h].double().cpu().numpy()
+            assert np.isfinite(got).all(), name
+            err = np.abs(got - want)
+            mx, mean = float(err.max()), float(err.mean())
+            rmax, rmean = float(np.abs(want).max()), float(np.abs(want).mean())
+            say(f"  head {h} {name}: max-abs {mx:.3e} ({mx / rmax:.2e} of max {rmax:.3e}), "
+                f"mean-abs {mean:.3e} ({mean / rmean:.2e} of mean {rmean:.3e})")
+            tol_max, tol_mean = TOL[name]
+            if not (mx <= tol_max * rmax and mean <= tol_mean * rmean):
+                bad.append((h, name, mx / rmax, mean / rmean))
+    assert not bad, bad
