@@ -192,6 +192,8 @@ def main():
                     help="clustering-free raster blocks bt,bh,bw for queries and keys (VMoBA 1D/2D/3D)")
     ap.add_argument("--quality", action="store_true",
                     help="relative error of O against dense fp32 attention on sampled query rows")
+    ap.add_argument("--backward", action="store_true",
+                    help="also time the block-sparse attention backward (compensation off)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-probe", action="store_true")
@@ -219,6 +221,9 @@ def main():
     if args.stat_lambda is not None:
         from dataclasses import replace
         w = replace(w, rule="stat", stat_lambda=args.stat_lambda, floor=max(1, w.floor))
+    if args.backward:
+        from dataclasses import replace
+        w = replace(w, compensate=False)
     L.load()
     t_gen = time.perf_counter()
     q, k, v = wl.make_inputs(w, device=dev)
@@ -333,6 +338,30 @@ def main():
     dense_list = [x for x in (dense_own, dense_sdpa) if x is not None]
     dense_best = min(dense_list) if dense_list else None
 
+    backward = None
+    if args.backward:
+        # gradients of the selected-block attention for a random dO, given
+        # the forward's clusters, mask and output
+        gen = torch.Generator(device="cpu").manual_seed(2)
+        d_o = torch.randn(q.shape, generator=gen).to(q.dtype).to(dev)
+        wsb = L.workspace(L.sa_block_sparse_attn_bwd_workspace_size(p, Cq, Ck), dev)
+        grads = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3)]
+        bwd = lambda: L.sa_block_sparse_attn_bwd(p, ac, qt, kt, v_perm, mask2, o2, d_o, *grads, wsb)
+        L.sa_block_sparse_attn(p, ac, qt, kt, v_perm, None, mask2, o2, ws)
+        bwd()
+        t = Timer()
+        for _ in range(reps):
+            t.start()
+            bwd()
+            t.stop()
+        bms = float(np.mean(t.ms()))
+        # 10 d flops per selected (query, key) pair: S, dP, dV, dQ, dK
+        bflops = 2.5 * eff
+        backward = {"ms": bms, "algorithmic_flops": bflops, "tflops": bflops / (bms * 1e-3) / 1e12,
+                    "flops_rule": "10 d per selected (query, key) pair (S, dP, dV, dQ, dK), LSE recomputed"}
+        print(f"# backward {bms:.3f} ms, {backward['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del wsb, grads, d_o
+
     quality = None
     if args.quality:
         # O of sampled query rows against softmax(q k^T / sqrt(d)) v in fp32
@@ -425,6 +454,8 @@ def main():
         line["gemm_probe_bf16"] = gemm
     if quality is not None:
         line["quality"] = quality
+    if backward is not None:
+        line["backward"] = backward
     print(json.dumps(line), flush=True)
 
 

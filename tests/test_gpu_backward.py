@@ -24,6 +24,7 @@ import torch
 import oracle
 from clustered_block_sparse_amd import _lib as L
 from clustered_block_sparse_amd import api
+from clustered_block_sparse_amd import workloads as wl
 
 from gpu_helpers import DEV, MID_S, TAB_S, WAN_S, inputs, say, scale_of, to_np, unpack_mask, workspace_for
 
@@ -90,4 +91,69 @@ def test_backward(w):
             tol_max, tol_mean = TOL[name]
             if not (mx <= tol_max * rmax and mean <= tol_mean * rmean):
                 bad.append((h, name, mx / rmax, mean / rmean))
+    assert not bad, bad
+
+
+def test_backward_full_size():
+    """The Wan 720p layer (natural Top-p, compensation off) at full size: the
+    oracle recomputes, for sampled key clusters of the first and last head,
+    every query cluster that selected them; dK and dV of the key cluster's
+    rows and dQ of those query clusters' rows are then complete and compared
+    element by element (the same bounds)."""
+    w = replace(wl.WAN, compensate=False)
+    say(f"[backward full size] {w.name} H={w.heads} N={w.n} d={w.d} P={w.top_p}")
+    q, k, v = wl.make_inputs(w, device=DEV)
+    p, qc, kc, sc, ac = api.cfgs(w)
+    ws = workspace_for(p, qc, kc, sc, ac)
+    qt = L.alloc_clusters(p, qc, DEV, q.dtype)
+    kt = L.alloc_clusters(p, kc, DEV, k.dtype)
+    L.sa_cluster_qk(p, qc, kc, q, k, qt, kt, ws)
+    Cq, Ck = qt.num_clusters, kt.num_clusters
+    v_perm = torch.empty_like(v)
+    L.sa_permute(p, kt, v, v_perm, None)
+    mask = torch.empty(w.heads, Cq, L.mask_words(Ck), dtype=torch.int32, device=DEV)
+    counts = torch.empty(w.heads, Cq, dtype=torch.int32, device=DEV)
+    ktop = torch.empty(w.heads, dtype=torch.int32, device=DEV)
+    L.sa_select(p, sc, qt, kt, mask, counts, None, ktop, ws)
+    o = torch.empty_like(q)
+    L.sa_block_sparse_attn(p, ac, qt, kt, v_perm, None, mask, o, ws)
+    del ws
+    g = torch.Generator(device="cpu").manual_seed(11)
+    d_o = torch.randn(q.shape, generator=g).to(torch.bfloat16).to(DEV)
+    wsb = L.workspace(L.sa_block_sparse_attn_bwd_workspace_size(p, Cq, Ck), DEV)
+    grads = [torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV) for _ in range(3)]
+    L.sa_block_sparse_attn_bwd(p, ac, qt, kt, v_perm, mask, o, d_o, *grads, wsb)
+    torch.cuda.synchronize()
+    say("  ran the forward and the backward")
+    for x in grads:
+        assert bool(torch.isfinite(x).all()), "every gradient row is written"
+    gm = unpack_mask(mask, Ck)
+    rng = np.random.default_rng(3)
+    bad = []
+    for h in (0, w.heads - 1):
+        qs, ks, vs, gs = to_np(q[h]), to_np(k[h]), to_np(v[h]), to_np(d_o[h])
+        qperm, qoff = qt.perm[h].cpu().numpy(), qt.offsets[h].cpu().numpy()
+        kperm, koff = kt.perm[h].cpu().numpy(), kt.offsets[h].cpu().numpy()
+        sel_by = gm[h].sum(0)  # query clusters selecting each key cluster
+        cand = np.nonzero(sel_by > 0)[0]
+        cand = cand[np.argsort(sel_by[cand], kind="stable")]
+        # the least selected key cluster and one from the less selected half
+        picks = np.unique([cand[0], rng.choice(cand[:max(1, len(cand) // 2)])])
+        for j in picks:
+            I = np.nonzero(gm[h][:, j])[0]
+            rows = np.concatenate([qperm[qoff[i]:qoff[i + 1]] for i in I])
+            sub_off = np.concatenate([[0], np.cumsum(qoff[I + 1] - qoff[I])])
+            ref = oracle.attention_backward(qs, ks, vs, rows, sub_off, kperm, koff, gm[h][I], scale_of(w), gs)
+            keys = kperm[koff[j]:koff[j + 1]]
+            for name, got, want, idx in zip(("dq", "dk", "dv"), grads, ref, (rows, keys, keys)):
+                got = got[h, torch.tensor(idx, device=DEV)].double().cpu().numpy()
+                want = want[idx]
+                err = np.abs(got - want)
+                mx, mean = float(err.max()), float(err.mean())
+                rmax, rmean = float(np.abs(want).max()), float(np.abs(want).mean())
+                say(f"  head {h} key cluster {j} ({len(I)} query clusters) {name}: max {mx / rmax:.2e} of max, "
+                    f"mean {mean / rmean:.2e} of mean")
+                tol_max, tol_mean = TOL[name]
+                if not (mx <= tol_max * rmax and mean <= tol_mean * rmean):
+                    bad.append((h, int(j), name, mx / rmax, mean / rmean))
     assert not bad, bad
