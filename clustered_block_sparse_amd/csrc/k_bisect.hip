@@ -1010,10 +1010,14 @@ __global__ __launch_bounds__(1024) void partition_kernel(TopBufs b, const int32_
 #pragma unroll
     for (int u = 0; u < PU; ++u) {
       const int i = base + PU * t + u;
-      if (i < sg.y) {
+      const int left = lf[u];
+      const int np = left ? sg.x + lpre : sg.x + sg.z + (i - lpre);
+      // a left token lands below sg.x + i; a right one stays inside the
+      // segment as long as at least sg.z tokens test left, which the exact
+      // rank threshold guarantees; the bound keeps a wrong threshold from
+      // writing into the next segment or past the head
+      if (i < sg.y && np < sg.x + sg.y) {
         const int p = sg.x + i;
-        const int left = lf[u];
-        const int np = left ? sg.x + lpre : sg.x + sg.z + (i - lpre);
         po[np] = pi[p];
         if constexpr (PRED) {
           const size_t hn = size_t(h) * b.N;
@@ -1455,7 +1459,8 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
           const bool left = valid && is_left(S.key[p], p, th);
           const uint64_t bal = __ballot(left);
           const int pre = __popcll(bal & lane_lt()) + run_left;
-          if (valid) S.tmp[left ? sg.x + pre : sg.x + sg.z + (i - pre)] = S.pt[p];
+          const int np = left ? sg.x + pre : sg.x + sg.z + (i - pre);
+          if (valid && np < sg.x + sg.y) S.tmp[np] = S.pt[p];  // bound as in the top phase
           run_left += __popcll(bal);
         }
       }
