@@ -203,8 +203,13 @@ __global__ __launch_bounds__(256) void assign_mfma_kernel(const bf16_t* __restri
   }
 }
 
-// One Lloyd step for bf16 rows in one pass over them: the assignment above,
-// then every workgroup's sums of its tokens' slices per cluster, as
+// One Lloyd step for bf16 rows in one pass over them: the assignment as
+// above but with the roles of registers and LDS swapped (each wave keeps the
+// three terms of one 32-cluster block in registers and reads the staged token
+// rows from LDS, so the per-step LDS traffic is the rows', not the
+// centroids' once per wave; the per-token minimum is then taken over the
+// blocks in ascending order), then every workgroup's sums of its tokens'
+// slices per cluster, as
 // onehot(labels)^T X on the same MFMA (bf16 products of x and 1 are exact,
 // sums in fp32 in a fixed order), and its per-cluster counts.  A workgroup
 // takes G groups of 128 tokens (one 32-token block per wave); each group's
@@ -235,7 +240,8 @@ constexpr int step_dcp() {
 }
 template <int DC>
 __global__ __launch_bounds__(256) void kmeans_step_kernel(const bf16_t* __restrict__ x, int d, int col0, int N,
-                                                          int C, int G, const float* __restrict__ cent,
+                                                          int C, int G, const bf16_t* __restrict__ ctab,
+                                                          const float* __restrict__ cnorm,
                                                           int32_t* __restrict__ labels, float* __restrict__ psum,
                                                           int32_t* __restrict__ pcnt) {
   constexpr int P = mfma_pitch<DC>();
@@ -245,32 +251,35 @@ __global__ __launch_bounds__(256) void kmeans_step_kernel(const bf16_t* __restri
   constexpr int NDB = DCP / 32;     // 32-column blocks of the sums
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int CP = (C + 31) & ~31;
-  bf16_t* ct = reinterpret_cast<bf16_t*>(smem);                              // [3][CP][P]
-  float* cn = reinterpret_cast<float*>(smem + size_t(3) * CP * P * 2);       // [CP]
-  bf16_t* xs = reinterpret_cast<bf16_t*>(cn + CP);                           // [128][DCP]
-  int* lab = reinterpret_cast<int*>(xs + KSTEP_TOK * DCP);                   // [128]
-  int* cnt = lab + KSTEP_TOK;                                                // [CP]
+  const int nb = CP / 32;  // 32-cluster blocks (1..4)
+  bf16_t* xs = reinterpret_cast<bf16_t*>(smem);                // [128][DCP] the group's rows
+  float* rv = reinterpret_cast<float*>(xs + KSTEP_TOK * DCP);  // [4][128] per-block minimum distance
+  int* rj = reinterpret_cast<int*>(rv + 4 * KSTEP_TOK);        // [4][128] its cluster
+  int* lab = rj + 4 * KSTEP_TOK;                               // [128]
+  int* cnt = lab + KSTEP_TOK;                                  // [CP]
   const int h = blockIdx.y, t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int col = lane & 31, hi = lane >> 5;
-  const float* ch = cent + size_t(h) * C * DC;
-  for (int e = t; e < CP * DC; e += 256) {
-    const int c = e / DC, k = e % DC;
-    const float v = c < C ? ch[size_t(c) * DC + k] : 0.f;
-    const bf16_t t0 = f2bf(v);
-    const float r1 = v - bf2f(t0);
-    const bf16_t t1 = f2bf(r1);
-    const bf16_t t2 = f2bf(r1 - bf2f(t1));
-    ct[size_t(c) * P + k] = t0;
-    ct[size_t(CP + c) * P + k] = t1;
-    ct[size_t(2 * CP + c) * P + k] = t2;
+  // this wave's cluster block, and its share of the group's four 32-token
+  // blocks (the waves of one cluster block split them)
+  const int cbw = w % nb;
+  const int gi = w / nb, gs = (4 - cbw + nb - 1) / nb;
+  // A operand of the distance: the three bf16 terms of cluster 32 cbw + col,
+  // columns 16 s + 8 hi .. + 7, in registers for the whole step; the norms of
+  // the 16 clusters whose distances the lane's D-layout elements hold
+  bf16x8_t cf[3][KS];
+  float cnv[16];
+  {
+    const bf16_t* tab = ctab + size_t(h) * 3 * CP * P;
+#pragma unroll
+    for (int term = 0; term < 3; ++term)
+#pragma unroll
+      for (int s2 = 0; s2 < KS; ++s2)
+        cf[term][s2] = __builtin_bit_cast(
+            bf16x8_t, *reinterpret_cast<const uint4*>(tab + size_t(term * CP + 32 * cbw + col) * P + 16 * s2 + 8 * hi));
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cnv[r] = cnorm[size_t(h) * CP + 32 * cbw + 8 * (r >> 2) + 4 * hi + (r & 3)];
   }
-  for (int c = t; c < CP; c += 256) {
-    float sq = 0.f;
-    if (c < C)
-      for (int k = 0; k < DC; ++k) sq = fmaf(ch[size_t(c) * DC + k], ch[size_t(c) * DC + k], sq);
-    cn[c] = sq;
-    cnt[c] = 0;
-  }
+  for (int c = t; c < CP; c += 256) cnt[c] = 0;
   // zero padding columns of the staged rows (never written afterwards)
   if constexpr (CPR > DC / 8) {
     constexpr int PADC = CPR - DC / 8;
@@ -279,7 +288,6 @@ __global__ __launch_bounds__(256) void kmeans_step_kernel(const bf16_t* __restri
       *reinterpret_cast<uint4*>(xs + r * DCP + ((c ^ xswz<CPR>(r)) << 3)) = make_uint4(0, 0, 0, 0);
     }
   }
-  __syncthreads();
   // this wave's (cluster block, column block) pairs of the sums
   const int npairs = (CP / 32) * NDB;
   floatx16 acc[4];
@@ -297,26 +305,37 @@ __global__ __launch_bounds__(256) void kmeans_step_kernel(const bf16_t* __restri
     tr_off[db] = tr_row * DCP + (((cc >> 3) ^ xswz<CPR>(tr_row)) << 3) + (cc & 7);
   }
   const int ntile = (N + KSTEP_TOK - 1) / KSTEP_TOK;
+  const int lr = 32 * w + col;  // the row this lane stages
+  // the staged row's 16-byte pieces 2 s + hi (zeros past N)
+  uint4 xf[KS];
+  auto load_rows = [&](int tile) {
+    const int tok = tile * KSTEP_TOK + lr;
+    const bool valid = tok < N;
+    const bf16_t* row = x + (size_t(h) * N + (valid ? tok : 0)) * d + col0;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      xf[s2] = *reinterpret_cast<const uint4*>(row + 16 * s2 + 8 * hi);
+      if (!valid) xf[s2] = make_uint4(0, 0, 0, 0);
+    }
+  };
+  if (int(blockIdx.x) * G < ntile) load_rows(int(blockIdx.x) * G);
 #pragma unroll 1
   for (int g = 0; g < G; ++g) {
     const int tile = blockIdx.x * G + g;
     if (tile >= ntile) break;  // uniform across the workgroup
-    // assignment of the wave's 32 tokens (as assign_mfma_kernel)
-    const int lr = 32 * w + col;  // row in the group
-    const int tok = tile * KSTEP_TOK + lr;
-    const bool valid = tok < N;
-    const bf16_t* row = x + (size_t(h) * N + (valid ? tok : 0)) * d + col0;
-    bf16x8_t xf[KS];
 #pragma unroll
-    for (int s2 = 0; s2 < KS; ++s2) {
-      uint4 u = *reinterpret_cast<const uint4*>(row + 16 * s2 + 8 * hi);
-      if (!valid) u = make_uint4(0, 0, 0, 0);
-      xf[s2] = __builtin_bit_cast(bf16x8_t, u);
-      *reinterpret_cast<uint4*>(xs + lr * DCP + (((2 * s2 + hi) ^ xswz<CPR>(lr)) << 3)) = u;
-    }
-    float best = __builtin_huge_valf();
-    int bj = 0x7fffffff;
-    for (int cb = 0; cb < CP; cb += 32) {
+    for (int s2 = 0; s2 < KS; ++s2)
+      *reinterpret_cast<uint4*>(xs + lr * DCP + (((2 * s2 + hi) ^ xswz<CPR>(lr)) << 3)) = xf[s2];
+    __syncthreads();  // the group's rows are staged
+    // the next group's rows travel while this one is computed
+    if (g + 1 < G && tile + 1 < ntile) load_rows(tile + 1);
+    // distances ||c||^2 - 2 x.c of the wave's cluster block to its token
+    // blocks (B operand: token rows from LDS), the three terms accumulated in
+    // the same order as one centroid row at a time; per token the smallest,
+    // first index on ties
+#pragma unroll 1
+    for (int tb = gi; tb < 4; tb += gs) {
+      const int xr = 32 * tb + col;
       floatx16 a2;
 #pragma unroll
       for (int r = 0; r < 16; ++r) a2[r] = 0.f;
@@ -324,30 +343,52 @@ __global__ __launch_bounds__(256) void kmeans_step_kernel(const bf16_t* __restri
       for (int term = 0; term < 3; ++term)
 #pragma unroll
         for (int s2 = 0; s2 < KS; ++s2) {
-          const uint4 u = *reinterpret_cast<const uint4*>(ct + size_t(term * CP + cb + col) * P + 16 * s2 + 8 * hi);
-          a2 = kmfma(__builtin_bit_cast(bf16x8_t, u), xf[s2], a2);
+          const uint4 u = *reinterpret_cast<const uint4*>(xs + xr * DCP + (((2 * s2 + hi) ^ xswz<CPR>(xr)) << 3));
+          a2 = kmfma(cf[term][s2], __builtin_bit_cast(bf16x8_t, u), a2);
         }
+      float best = __builtin_huge_valf();
+      int bj = 0x7fffffff;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int c = cb + 8 * (r >> 2) + 4 * hi + (r & 3);
-        const float dv = cn[c] - 2.f * a2[r];
+        const int c = 32 * cbw + 8 * (r >> 2) + 4 * hi + (r & 3);
+        const float dv = cnv[r] - 2.f * a2[r];
         if (c < C && dv < best) {
           best = dv;
           bj = c;
         }
       }
+      const float ob = __shfl_xor(best, 32, 64);
+      const int oj = __shfl_xor(bj, 32, 64);
+      if (ob < best || (ob == best && oj < bj)) {
+        best = ob;
+        bj = oj;
+      }
+      if (hi == 0) {
+        rv[cbw * KSTEP_TOK + xr] = best;
+        rj[cbw * KSTEP_TOK + xr] = bj;
+      }
     }
-    const float ob = __shfl_xor(best, 32, 64);
-    const int oj = __shfl_xor(bj, 32, 64);
-    if (ob < best || (ob == best && oj < bj)) bj = oj;
-    if (hi == 0) {
-      lab[lr] = valid ? bj : -1;
+    __syncthreads();  // every block's minimum is in LDS
+    if (t < KSTEP_TOK) {
+      // blocks in ascending order, strict: the first index among equal minima
+      float best = rv[t];
+      int bj = rj[t];
+      for (int cb = 1; cb < nb; ++cb) {
+        const float v = rv[cb * KSTEP_TOK + t];
+        if (v < best) {
+          best = v;
+          bj = rj[cb * KSTEP_TOK + t];
+        }
+      }
+      const int tok = tile * KSTEP_TOK + t;
+      const bool valid = tok < N;
+      lab[t] = valid ? bj : -1;
       if (valid) {
         labels[size_t(h) * N + tok] = bj;
         atomicAdd(&cnt[bj], 1);
       }
     }
-    __syncthreads();
+    __syncthreads();  // labels of the group are in LDS
     // sums: for every 16-token step, the one-hot B operand from the labels of
     // the lane's 8 tokens (in the order the transpose reads give them)
 #pragma unroll 1
@@ -394,21 +435,65 @@ __global__ __launch_bounds__(256) void kmeans_step_kernel(const bf16_t* __restri
   for (int c = t; c < CP; c += 256) pcnt[pb * CP + c] = cnt[c];
 }
 
-// centroid = (sum of the workgroup partials, in workgroup order) / count;
-// an empty cluster keeps its centroid
-__global__ void kmeans_combine_kernel(const float* __restrict__ psum, const int32_t* __restrict__ pcnt,
-                                      int nblk, int C, int CP, int DC, float* __restrict__ cent) {
-  const int c = blockIdx.x, h = blockIdx.y;
-  for (int dim = threadIdx.x; dim < DC; dim += blockDim.x) {
-    float s2 = 0.f;
-    long long n = 0;
-    for (int b = 0; b < nblk; ++b) {
-      const size_t pb = size_t(h) * nblk + b;
-      s2 += psum[(pb * CP + c) * DC + dim];
-      n += pcnt[pb * CP + c];
-    }
-    if (n > 0) cent[(size_t(h) * C + c) * DC + dim] = s2 / float(n);
+// The centroid terms of the matrix-core distance for one centroid row (or a
+// zero padding row when v is null): three bf16 terms hi + mid + lo of every
+// column, at [term][CP][P] of the head's table, and the fp32 norm summed over
+// the columns in ascending order.  One thread per column (DC <= 128 threads).
+template <int DC>
+__device__ __forceinline__ void write_ctab_row(const float* v, int c, int CP, bf16_t* tab, float* norm) {
+  constexpr int P = mfma_pitch<DC>();
+  const int k = threadIdx.x;
+  const float x = v ? v[k] : 0.f;
+  const bf16_t t0 = f2bf(x);
+  const float r1 = x - bf2f(t0);
+  const bf16_t t1 = f2bf(r1);
+  const bf16_t t2 = f2bf(r1 - bf2f(t1));
+  tab[size_t(c) * P + k] = t0;
+  tab[size_t(CP + c) * P + k] = t1;
+  tab[size_t(2 * CP + c) * P + k] = t2;
+  if (k == 0) {
+    float sq = 0.f;
+    if (v)
+      for (int j = 0; j < DC; ++j) sq = fmaf(v[j], v[j], sq);
+    *norm = sq;
   }
+}
+
+// the table of every centroid row (padding rows zero) from fp32 centroids:
+// before the first step of a run
+template <int DC>
+__global__ __launch_bounds__(DC) void ctab_kernel(const float* __restrict__ cent, int C, int CP,
+                                                  bf16_t* __restrict__ ctab, float* __restrict__ cnorm) {
+  __shared__ float row[DC];
+  const int c = blockIdx.x, h = blockIdx.y;
+  if (c < C) row[threadIdx.x] = cent[(size_t(h) * C + c) * DC + threadIdx.x];
+  __syncthreads();
+  write_ctab_row<DC>(c < C ? row : nullptr, c, CP, ctab + size_t(h) * 3 * CP * mfma_pitch<DC>(),
+                     cnorm + size_t(h) * CP + c);
+}
+
+// centroid = (sum of the workgroup partials, in workgroup order) / count;
+// an empty cluster keeps its centroid.  Also the next step's table row.
+template <int DC>
+__global__ __launch_bounds__(DC) void kmeans_combine_kernel(const float* __restrict__ psum,
+                                                            const int32_t* __restrict__ pcnt, int nblk, int C,
+                                                            int CP, float* __restrict__ cent,
+                                                            bf16_t* __restrict__ ctab, float* __restrict__ cnorm) {
+  __shared__ float row[DC];
+  const int c = blockIdx.x, h = blockIdx.y, dim = threadIdx.x;
+  float s2 = 0.f;
+  long long n = 0;
+  for (int b = 0; b < nblk; ++b) {
+    const size_t pb = size_t(h) * nblk + b;
+    s2 += psum[(pb * CP + c) * DC + dim];
+    n += pcnt[pb * CP + c];
+  }
+  float* dst = cent + (size_t(h) * C + c) * DC + dim;
+  const float v = n > 0 ? s2 / float(n) : *dst;
+  if (n > 0) *dst = v;
+  row[dim] = v;
+  __syncthreads();
+  write_ctab_row<DC>(row, c, CP, ctab + size_t(h) * 3 * CP * mfma_pitch<DC>(), cnorm + size_t(h) * CP + c);
 }
 
 template <typename T>
@@ -524,33 +609,93 @@ hipError_t assign_dispatch(const void* x, int d, int col0, int dc, int H, int N,
 }
 
 // Workgroups per head of the fused step: about 1024 in all, but at most one
-// per 4 CP tokens (so the partials, written and read once, move no more bytes
+// per 2 CP tokens (so the partials, written and read once, move no more bytes
 // than the rows), and whole groups of 128 tokens each.
 void step_geometry(int H, int N, int C, int& nblk, int& G) {
   const int CP = (C + 31) & ~31;
   const int ntile = (N + KSTEP_TOK - 1) / KSTEP_TOK;
   int bh = std::max(1, std::min(ntile, (1024 + H - 1) / H));
-  bh = std::max(1, std::min(bh, N / (4 * CP)));
+  bh = std::max(1, std::min(bh, N / (2 * CP)));
   G = (ntile + bh - 1) / bh;
+  nblk = (ntile + G - 1) / G;
+}
+
+// scratch of the fused step: partial sums [H][nblk][CP][DC] f32, counts
+// [H][nblk][CP], then (256-byte aligned) the centroid table [H][3][CP][P]
+// bf16 and norms [H][CP] f32
+struct StepScratch {
+  float* psum;
+  int32_t* pcnt;
+  bf16_t* ctab;
+  float* cnorm;
+  size_t bytes;
+};
+StepScratch step_scratch(int H, int N, int C, int dc, void* base) {
+  int nblk, G;
+  step_geometry(H, N, C, nblk, G);
+  const size_t CP = size_t((C + 31) & ~31);
+  const size_t P = size_t(dc) + 8;
+  StepScratch r{};
+  size_t off = 0;
+  auto take = [&](size_t b) {
+    const size_t o = off;
+    off = (off + b + 255) & ~size_t(255);
+    return static_cast<char*>(base) + o;
+  };
+  r.psum = reinterpret_cast<float*>(take(size_t(H) * nblk * CP * dc * sizeof(float)));
+  r.pcnt = reinterpret_cast<int32_t*>(take(size_t(H) * nblk * CP * sizeof(int32_t)));
+  r.ctab = reinterpret_cast<bf16_t*>(take(size_t(H) * 3 * CP * P * sizeof(bf16_t)));
+  r.cnorm = reinterpret_cast<float*>(take(size_t(H) * CP * sizeof(float)));
+  r.bytes = off;
+  return r;
+}
+
+// Groups per workgroup for the launch: at least the G of step_geometry (which
+// sizes the partials), and beyond it the G that minimises (rounds of
+// workgroups over the chip) x G, with the kernel's real occupancy; ties go to
+// the smaller G.  With one workgroup per CU, 344 workgroups of 2 groups take
+// two rounds (4 group times) where 232 of 3 take one (3).
+void launch_geometry(int H, int N, int C, int per_cu, int cus, int& nblk, int& G) {
+  step_geometry(H, N, C, nblk, G);
+  if (per_cu < 1 || cus < 1) return;
+  const int ntile = (N + KSTEP_TOK - 1) / KSTEP_TOK;
+  const long long slots = (long long)per_cu * cus;
+  long long best = -1;
+  int bestG = G;
+  for (int g = G; g <= ntile; ++g) {
+    const long long wgs = (long long)H * ((ntile + g - 1) / g);
+    const long long cost = ((wgs + slots - 1) / slots) * g;
+    if (best < 0 || cost < best) {
+      best = cost;
+      bestG = g;
+    }
+    if (wgs <= slots) break;  // one round: a larger G only adds group times
+  }
+  G = bestG;
   nblk = (ntile + G - 1) / G;
 }
 
 template <int DC>
 hipError_t kmeans_step_launch(const void* x, int d, int col0, int H, int N, int C, float* c,
-                              int32_t* labels, float* psum, hipStream_t st) {
+                              int32_t* labels, float* scratch, bool first, hipStream_t st) {
   const int CP = (C + 31) & ~31;
-  int nblk, G;
-  step_geometry(H, N, C, nblk, G);
-  int32_t* pcnt = reinterpret_cast<int32_t*>(psum + size_t(H) * nblk * CP * DC);
-  const size_t lds = size_t(3) * CP * mfma_pitch<DC>() * 2 + size_t(CP) * 4 +
-                     size_t(KSTEP_TOK) * step_dcp<DC>() * 2 + size_t(KSTEP_TOK) * 4 + size_t(CP) * 4;
+  const StepScratch sc = step_scratch(H, N, C, DC, scratch);
+  if (first) ctab_kernel<DC><<<dim3(CP, H), DC, 0, st>>>(c, C, CP, sc.ctab, sc.cnorm);
+  const size_t lds = size_t(KSTEP_TOK) * step_dcp<DC>() * 2 + size_t(9) * KSTEP_TOK * 4 + size_t(CP) * 4;
   if (lds > 64 * 1024 &&
       hipFuncSetAttribute((const void*)kmeans_step_kernel<DC>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           int(lds)) != hipSuccess)
     return hipErrorInvalidValue;
-  kmeans_step_kernel<DC><<<dim3(nblk, H), 256, lds, st>>>((const bf16_t*)x, d, col0, N, C, G, c, labels,
-                                                          psum, pcnt);
-  kmeans_combine_kernel<<<dim3(C, H), std::min(DC, 128), 0, st>>>(psum, pcnt, nblk, C, CP, DC, c);
+  int per_cu = 0, cus = 0, dev = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kmeans_step_kernel<DC>, 256, lds) != hipSuccess ||
+      hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    per_cu = cus = 0;  // the partials' geometry
+  int nblk, G;
+  launch_geometry(H, N, C, per_cu, cus, nblk, G);
+  kmeans_step_kernel<DC><<<dim3(nblk, H), 256, lds, st>>>((const bf16_t*)x, d, col0, N, C, G, sc.ctab, sc.cnorm,
+                                                          labels, sc.psum, sc.pcnt);
+  kmeans_combine_kernel<DC><<<dim3(C, H), DC, 0, st>>>(sc.psum, sc.pcnt, nblk, C, CP, c, sc.ctab, sc.cnorm);
   return hipGetLastError();
 }
 
@@ -561,20 +706,17 @@ bool kmeans_step_supported(int dtype, const void* x, int d, int col0, int dc, in
 }
 
 size_t kmeans_step_scratch(int H, int N, int C, int dc) {
-  int nblk, G;
-  step_geometry(H, N, C, nblk, G);
-  const int CP = (C + 31) & ~31;
-  return size_t(H) * nblk * CP * (size_t(dc) * sizeof(float) + sizeof(int32_t)) + 256;
+  return step_scratch(H, N, C, dc, nullptr).bytes + 256;
 }
 
 hipError_t kmeans_step(const void* x, int d, int col0, int dc, int H, int N, int C, float* c,
-                       int32_t* labels, float* scratch, hipStream_t st) {
+                       int32_t* labels, float* scratch, bool first, hipStream_t st) {
   switch (dc) {
-    case 16: return kmeans_step_launch<16>(x, d, col0, H, N, C, c, labels, scratch, st);
-    case 32: return kmeans_step_launch<32>(x, d, col0, H, N, C, c, labels, scratch, st);
-    case 48: return kmeans_step_launch<48>(x, d, col0, H, N, C, c, labels, scratch, st);
-    case 64: return kmeans_step_launch<64>(x, d, col0, H, N, C, c, labels, scratch, st);
-    case 128: return kmeans_step_launch<128>(x, d, col0, H, N, C, c, labels, scratch, st);
+    case 16: return kmeans_step_launch<16>(x, d, col0, H, N, C, c, labels, scratch, first, st);
+    case 32: return kmeans_step_launch<32>(x, d, col0, H, N, C, c, labels, scratch, first, st);
+    case 48: return kmeans_step_launch<48>(x, d, col0, H, N, C, c, labels, scratch, first, st);
+    case 64: return kmeans_step_launch<64>(x, d, col0, H, N, C, c, labels, scratch, first, st);
+    case 128: return kmeans_step_launch<128>(x, d, col0, H, N, C, c, labels, scratch, first, st);
     default: return hipErrorInvalidValue;
   }
 }

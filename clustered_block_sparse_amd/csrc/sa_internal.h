@@ -112,11 +112,14 @@ bool kmeans_width_supported(int dc);
 // One Lloyd step in one pass over bf16 rows (assignment as kmeans_assign on
 // the matrix cores, then per-workgroup cluster sums and counts, added in
 // workgroup order): labels of every token, then c[h][j] <- mean of its
-// members (unchanged when empty).  `scratch`: kmeans_step_scratch bytes.
+// members (unchanged when empty).  `scratch`: kmeans_step_scratch bytes, kept
+// between the steps of one run: it carries the centroids' matrix-core terms
+// from each step to the next; `first` builds them from c (the first step of a
+// run, or after c changed outside the steps).
 bool kmeans_step_supported(int dtype, const void* x, int d, int col0, int dc, int C);
 size_t kmeans_step_scratch(int H, int N, int C, int dc);
 hipError_t kmeans_step(const void* x, int d, int col0, int dc, int H, int N, int C, float* c,
-                       int32_t* labels, float* scratch, hipStream_t st);
+                       int32_t* labels, float* scratch, bool first, hipStream_t st);
 // labels = (a_t*Cs + a_h)*Cs + a_w
 hipError_t combo_labels(const int32_t* sub_labels, int32_t* labels, int H, int N, int Cs,
                         hipStream_t st);
