@@ -29,6 +29,11 @@
 //               first-round keys under a prediction of their first two
 //               tokens; the partition checks it, and a verified child skips
 //               its first delta pass (results identical either way)
+//    The passes that read every row (delta, the first round's sums)
+//    alternate the order in which their workgroups walk the heads and
+//    chunks, so a pass starts on the rows the previous one read last, which
+//    the memory-side cache still holds (each block writes the same outputs
+//    either way).
 //  * subtree phase: one workgroup finishes each segment of at most SUB_N
 //    tokens through all remaining levels, with positions, keys and sides in
 //    LDS and rows re-read through the caches (four rows in flight per lane).
@@ -470,6 +475,7 @@ struct TopBufs {
   uint32_t* keys_next; // [H][N] children's round-0 keys, in the children's order
   int32_t* pred_ok;    // [H][max_seg] (next level) 1: the child's round-0 keys are in place
   int max_seg, max_chunk, N, round;  // round: 0 = first round of a level
+  int rev;  // full passes over the rows: walk the blocks in reverse order
 };
 
 // A child segment starts its first round from its first two tokens, which
@@ -520,11 +526,12 @@ __global__ __launch_bounds__(256) void delta_kernel(Src2<T> x, TopBufs b, int fi
   __shared__ float wv[D], mv[D];
   __shared__ float wvc[PRED ? 2 : 1][D], mvc[PRED ? 2 : 1][D];  // children (left, right)
   __shared__ int pidx[BCH / DELTA_SPLIT];  // the part's rows (original tokens)
-  const int h = blockIdx.y, t = threadIdx.x;
+  const int bx = b.rev ? int(gridDim.x) - 1 - int(blockIdx.x) : int(blockIdx.x);
+  const int h = b.rev ? int(gridDim.y) - 1 - int(blockIdx.y) : int(blockIdx.y), t = threadIdx.x;
   // a workgroup takes one of the DELTA_SPLIT equal parts of a chunk: more,
   // shorter workgroups keep the last wave of the launch from idling the chip
-  const int4 chunk = b.chunks[blockIdx.x / DELTA_SPLIT];
-  const int r0 = (blockIdx.x % DELTA_SPLIT) * (BCH / DELTA_SPLIT);
+  const int4 chunk = b.chunks[bx / DELTA_SPLIT];
+  const int r0 = (bx % DELTA_SPLIT) * (BCH / DELTA_SPLIT);
   if (r0 >= chunk.z) return;
   const int4 ch = make_int4(chunk.x, chunk.y + r0, min(BCH / DELTA_SPLIT, chunk.z - r0), chunk.w);
   const int lane = t & 63, w = t >> 6;
@@ -818,8 +825,9 @@ __global__ __launch_bounds__(256) void sums_kernel(Src2<T> x, TopBufs b) {
   __shared__ float ws[4][2][D];
   __shared__ int list[BCH];
   __shared__ int wsum[16];
-  const int h = blockIdx.y, t = threadIdx.x;
-  const int4 ch = b.chunks[blockIdx.x];
+  const int bx = b.rev ? int(gridDim.x) - 1 - int(blockIdx.x) : int(blockIdx.x);
+  const int h = b.rev ? int(gridDim.y) - 1 - int(blockIdx.y) : int(blockIdx.y), t = threadIdx.x;
+  const int4 ch = b.chunks[bx];
   const uint2 th = b.thr[size_t(h) * b.max_seg + ch.x];
   const int32_t* ph = b.perm + size_t(h) * b.N;
   const uint32_t* kh = b.keys + size_t(h) * b.N;
@@ -941,7 +949,7 @@ __global__ __launch_bounds__(256) void sums_kernel(Src2<T> x, TopBufs b) {
     }
   }
   __syncthreads();
-  float* out = b.part + (size_t(h) * b.max_chunk + blockIdx.x) * 2 * D;
+  float* out = b.part + (size_t(h) * b.max_chunk + bx) * 2 * D;
   for (int i = t; i < 2 * D; i += 256) {
     const int sdx = i / D, c = i % D;
     out[i] = ((ws[0][sdx][c] + ws[1][sdx][c]) + ws[2][sdx][c]) + ws[3][sdx][c];
@@ -1504,6 +1512,7 @@ hipError_t run_bisect(const void* x0, const void* x1, int h0, int H, int N, int 
   int32_t* cur = pa;
   int32_t* nxt = pb;
   bool predicted = false;  // this level's first-round keys were formed by its parent
+  int dir = 0;             // direction of the next full pass over the rows
   for (int lv = 0; lv < P.t.nlev; ++lv) {
     b.segs = segs + P.t.sb[lv];
     b.chunks = chunks + P.t.cb[lv];
@@ -1514,6 +1523,8 @@ hipError_t run_bisect(const void* x0, const void* x1, int h0, int H, int N, int 
     const bool predict = iters >= 2 && lv + 1 < P.t.nlev;
     for (int it = 0; it < iters; ++it) {
       const dim3 gd(gc.x * DELTA_SPLIT, gc.y);
+      b.rev = dir;
+      dir ^= 1;
       if (predict && it + 1 == iters) {
         firsts_kernel<<<gs, 64, 0, st>>>(b);
         delta_kernel<T, D, true><<<gd, 256, 0, st>>>(x, b, 0, 0);
@@ -1527,9 +1538,13 @@ hipError_t run_bisect(const void* x0, const void* x1, int h0, int H, int N, int 
       pick_kernel<<<gs, 1024, 0, st>>>(b);
       if (it + 1 < iters) {
         if (it == 0) {
+          b.rev = dir;
+          dir ^= 1;
           sums_kernel<T, D, true><<<gc, 256, 0, st>>>(x, b);
+          b.rev = 0;
           update_kernel<D, true><<<gs, 256, 0, st>>>(b);
         } else {
+          b.rev = 0;
           sums_kernel<T, D, false><<<gc, 256, 0, st>>>(x, b);
           update_kernel<D, false><<<gs, 256, 0, st>>>(b);
         }

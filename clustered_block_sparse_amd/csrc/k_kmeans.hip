@@ -483,7 +483,24 @@ __global__ __launch_bounds__(DC) void kmeans_combine_kernel(const float* __restr
   const int c = blockIdx.x, h = blockIdx.y, dim = threadIdx.x;
   float s2 = 0.f;
   long long n = 0;
-  for (int b = 0; b < nblk; ++b) {
+  // eight partials in flight, added in workgroup order
+  int b = 0;
+  for (; b + 8 <= nblk; b += 8) {
+    float v[8];
+    int k[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const size_t pb = size_t(h) * nblk + b + u;
+      v[u] = psum[(pb * CP + c) * DC + dim];
+      k[u] = pcnt[pb * CP + c];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      s2 += v[u];
+      n += k[u];
+    }
+  }
+  for (; b < nblk; ++b) {
     const size_t pb = size_t(h) * nblk + b;
     s2 += psum[(pb * CP + c) * DC + dim];
     n += pcnt[pb * CP + c];
