@@ -135,6 +135,7 @@ def cpu_baseline(w, q, k, v, budget_s=10.0):
         heads += 1
     dt = time.perf_counter() - t0
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "host_cpus": os.cpu_count(), "cpus_in_affinity": len(os.sched_getaffinity(0)),
             "sample": f"{heads} of {w.heads} heads of the same layer and inputs (fp64 NumPy oracle: clustering, "
                       f"selection, attention{' with compensation' if w.compensate else ''}), {dt:.1f} s"}
 

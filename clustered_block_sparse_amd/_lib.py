@@ -317,8 +317,10 @@ class HipEvent:
         return float(ms.value)
 
     def __del__(self):
-        if HipEvent._hip is not None and getattr(self, "handle", None):
-            HipEvent._hip.hipEventDestroy(self.handle)
+        # type(self): the module's globals may already be gone at interpreter exit
+        hip = getattr(type(self), "_hip", None)
+        if hip is not None and getattr(self, "handle", None):
+            hip.hipEventDestroy(self.handle)
 
 
 def mask_words(num_key_clusters: int) -> int:
