@@ -492,8 +492,8 @@ struct MfmaLds {
 
 // ALIGNED: rows whose ranges are 64-aligned stream whole 64-key blocks (K and
 // V rows are plain 16-byte copies); the other instantiation gathers rows of
-// arbitrary ranges through registers.  Each workgroup runs in the
-// instantiation matching its row and exits in the other.
+// arbitrary ranges, each lane's direct load taking its listed key row.  Each
+// workgroup runs in the instantiation matching its row and exits in the other.
 template <int D, bool ALIGNED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && ALIGNED ? 3 : 2, D == 64 && ALIGNED ? 3 : 2))) void attn_mfma(AttnArgs a, Prep p, float sl2) {
   static_assert(D == 64 || D == 128, "head dim");
