@@ -26,7 +26,7 @@ from clustered_block_sparse_amd import _lib as L
 from clustered_block_sparse_amd import api
 from clustered_block_sparse_amd import workloads as wl
 
-from gpu_helpers import DEV, MID_S, TAB_S, WAN_S, inputs, say, scale_of, to_np, unpack_mask, workspace_for
+from gpu_helpers import DEV, MID_S, TAB_S, WAN_S, inputs, pack_mask, say, scale_of, to_np, unpack_mask, workspace_for
 
 pytestmark = pytest.mark.gpu
 
@@ -156,4 +156,59 @@ def test_backward_full_size():
                 tol_max, tol_mean = TOL[name]
                 if not (mx <= tol_max * rmax and mean <= tol_mean * rmean):
                     bad.append((h, int(j), name, mx / rmax, mean / rmean))
+    assert not bad, bad
+
+
+def test_backward_given_mask_edges():
+    """A hand-made mask over the GPU's clusters: rows with no selected key
+    cluster (their queries get dQ = 0 and give nothing to any key), key
+    clusters no row selects (their keys get dK = dV = 0), a row selecting
+    every cluster, and single selections; element by element against the
+    oracle, zeros exactly."""
+    w = replace(WAN_S.forced_density(0.1), compensate=False, name="wan_small_edges")
+    q, k, v = inputs(w)
+    p, qc, kc, sc, ac = api.cfgs(w)
+    ws = workspace_for(p, qc, kc, sc, ac)
+    qt = L.alloc_clusters(p, qc, DEV, q.dtype)
+    kt = L.alloc_clusters(p, kc, DEV, k.dtype)
+    L.sa_cluster_qk(p, qc, kc, q, k, qt, kt, ws)
+    Cq, Ck = qt.num_clusters, kt.num_clusters
+    v_perm = torch.empty_like(v)
+    L.sa_permute(p, kt, v, v_perm, None)
+    rng = np.random.default_rng(5)
+    gm = rng.random((w.heads, Cq, Ck)) < 0.15
+    gm[:, ::7, :] = False          # rows with no key
+    gm[:, :, ::5] = False          # key clusters nobody selects
+    gm[:, 3, :] = True             # a row with every cluster
+    gm[:, 3, ::5] = False
+    gm[:, 5, :] = False
+    gm[:, 5, 1] = True             # a single selection
+    mask = torch.tensor(pack_mask(gm), device=DEV)
+    o = torch.empty_like(q)
+    L.sa_block_sparse_attn(p, ac, qt, kt, v_perm, None, mask, o, ws)
+    d_o = torch.randn(q.shape, generator=torch.Generator(device="cpu").manual_seed(3)).to(torch.bfloat16).to(DEV)
+    wsb = L.workspace(L.sa_block_sparse_attn_bwd_workspace_size(p, Cq, Ck), DEV)
+    grads = [torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV) for _ in range(3)]
+    L.sa_block_sparse_attn_bwd(p, ac, qt, kt, v_perm, mask, o, d_o, *grads, wsb)
+    torch.cuda.synchronize()
+    qs, ks, vs, gs = to_np(q), to_np(k), to_np(v), to_np(d_o)
+    bad = []
+    for h in range(w.heads):
+        qperm, qoff = qt.perm[h].cpu().numpy(), qt.offsets[h].cpu().numpy()
+        kperm, koff = kt.perm[h].cpu().numpy(), kt.offsets[h].cpu().numpy()
+        ref = oracle.attention_backward(qs[h], ks[h], vs[h], qperm, qoff, kperm, koff, gm[h], scale_of(w), gs[h])
+        empty_rows = np.concatenate([qperm[qoff[i]:qoff[i + 1]] for i in range(Cq) if not gm[h, i].any()])
+        unused = np.concatenate([kperm[koff[j]:koff[j + 1]] for j in range(Ck) if not gm[h, :, j].any()])
+        got = [x[h].double().cpu().numpy() for x in grads]
+        assert np.all(got[0][empty_rows] == 0.0), "dQ of queries with no key"
+        assert np.all(got[1][unused] == 0.0) and np.all(got[2][unused] == 0.0), "dK, dV of unselected keys"
+        for name, g_, want in zip(("dq", "dk", "dv"), got, ref):
+            assert np.isfinite(g_).all(), name
+            err = np.abs(g_ - want)
+            mx, mean = float(err.max()), float(err.mean())
+            rmax, rmean = float(np.abs(want).max()), float(np.abs(want).mean())
+            say(f"  head {h} {name}: max {mx / rmax:.2e} of max, mean {mean / rmean:.2e} of mean")
+            tol_max, tol_mean = TOL[name]
+            if not (mx <= tol_max * rmax and mean <= tol_mean * rmean):
+                bad.append((h, name, mx / rmax, mean / rmean))
     assert not bad, bad
