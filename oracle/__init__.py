@@ -18,6 +18,7 @@ from .cbsa import (  # noqa: F401
     SelectCfg,
     attention,
     attention_backward,
+    attention_lse,
     bisect,
     bisect_split,
     cluster_head,

@@ -704,6 +704,36 @@ def attention(q, k, v, q_perm, q_off, k_perm, k_off, mask, scale,
     return O
 
 
+def attention_lse(q, k, q_perm, q_off, k_perm, k_off, mask, scale, compensate=False, kbar=None):
+    """Natural-log normaliser of the sparse attention of every query token:
+    lse_n = log( sum_{m in sel} e^{s_nm} + c sum_{j excl} |K_j| e^{<q_n,kbar_j> scale} ),
+    the log of the denominator of `attention` (same terms, same notation), so
+    its weights are e^{s_nm - lse_n}.  -inf for a query with nothing to attend
+    (no selected key and no compensated cluster).  Original token order."""
+    q, k = _f64(q), _f64(k)
+    N = q.shape[0]
+    out = np.full(N, -np.inf)
+    Ck = len(k_off) - 1
+    ksz = np.diff(np.asarray(k_off))
+    for i in range(len(q_off) - 1):
+        rows = q_perm[q_off[i]:q_off[i + 1]]
+        if len(rows) == 0:
+            continue
+        sel = np.nonzero(mask[i])[0]
+        keys = np.concatenate([k_perm[k_off[j]:k_off[j + 1]] for j in sel]) if len(sel) else np.zeros(0, np.int64)
+        s = (q[rows] @ k[keys].T) * scale
+        if compensate:
+            excl = np.array([j for j in range(Ck) if not mask[i, j] and ksz[j] > 0], dtype=np.int64)
+            if len(excl):
+                sc = (q[rows] @ _f64(kbar)[excl].T) * scale + np.log(ksz[excl].astype(np.float64))[None, :]
+                s = np.concatenate([s, sc], axis=1)
+        if s.shape[1] == 0:
+            continue
+        m = s.max(axis=1)
+        out[rows] = m + np.log(np.exp(s - m[:, None]).sum(axis=1))
+    return out
+
+
 def attention_backward(q, k, v, q_perm, q_off, k_perm, k_off, mask, scale, dO):
     """Gradients of the block-sparse attention without compensation (the
     trainable use of block-sparse attention: "Bidirectional Sparse Attention

@@ -134,3 +134,71 @@ def test_forward_subspace_all_selected_is_dense(rng):
     kc = oracle.ClusterCfg(method="subspace", iters=2, sub_dims=(2, 3, 3), sub_clusters=3)
     r = oracle.forward_head(q, k, v, qc, kc, oracle.SelectCfg(top_p=1.0, floor=0))
     np.testing.assert_allclose(r.O, oracle.dense_attention(q, k, v, 1 / math.sqrt(d)), atol=1e-12)
+
+
+def brute_lse(q, k, scale, allowed, extra=None):
+    """Scalar loops: log of the sum of exp(score) over the allowed keys of
+    each query, plus the given (log-weight) extra terms."""
+    out = []
+    for n in range(len(q)):
+        terms = [scale * sum(q[n][t] * k[m][t] for t in range(q.shape[1])) for m in allowed[n]]
+        if extra is not None:
+            terms += list(extra[n])
+        if not terms:
+            out.append(-math.inf)
+            continue
+        mx = max(terms)
+        out.append(mx + math.log(sum(math.exp(x - mx) for x in terms)))
+    return np.array(out)
+
+
+def test_lse_brute_force(rng):
+    """Without compensation: the log-sum-exp over each query's selected keys,
+    by scalar loops; a query cluster with no selection gets -inf."""
+    q, k, v, ql, kl, qp, qo, kp, ko = setup(rng)
+    mask = rng.random((4, 6)) < 0.5
+    mask[1] = False
+    allowed = [[m for m in range(len(k)) if mask[ql[n], kl[m]]] for n in range(len(q))]
+    got = oracle.attention_lse(q, k, qp, qo, kp, ko, mask, 0.7)
+    want = brute_lse(q, k, 0.7, allowed)
+    assert np.all(np.isneginf(got[ql == 1])) and np.all(np.isneginf(want[ql == 1]))
+    fin = ql != 1
+    assert np.allclose(got[fin], want[fin], rtol=0, atol=1e-12)
+
+
+def test_lse_compensated_brute_force(rng):
+    """With compensation: each excluded non-empty key cluster adds
+    log|K_j| + <q, kbar_j> scale as one term (empty clusters add nothing)."""
+    q, k, v, ql, kl, qp, qo, kp, ko = setup(rng)
+    mask = rng.random((4, 6)) < 0.4
+    mask[2] = False  # a row with every cluster excluded: compensation terms only
+    kbar = oracle.cluster_means(k, kp, ko)
+    ksz = np.diff(ko)
+    allowed = [[m for m in range(len(k)) if mask[ql[n], kl[m]]] for n in range(len(q))]
+    extra = [[math.log(ksz[j]) + 0.5 * float(np.dot(q[n], kbar[j])) for j in range(6)
+              if not mask[ql[n], j] and ksz[j] > 0] for n in range(len(q))]
+    got = oracle.attention_lse(q, k, qp, qo, kp, ko, mask, 0.5, True, kbar)
+    assert np.allclose(got, brute_lse(q, k, 0.5, allowed, extra), rtol=0, atol=1e-12)
+
+
+def test_lse_weights_reproduce_attention(rng):
+    """The weights e^{s - lse} (and |K_j| e^{<q,kbar_j> scale - lse} for the
+    compensated clusters) sum to one and give the attention output."""
+    q, k, v, ql, kl, qp, qo, kp, ko = setup(rng)
+    mask = rng.random((4, 6)) < 0.5
+    mask[:, 0] = True
+    kbar, vbar = oracle.cluster_means(k, kp, ko), oracle.cluster_means(v, kp, ko)
+    ksz = np.diff(ko)
+    for comp in (False, True):
+        lse = oracle.attention_lse(q, k, qp, qo, kp, ko, mask, 0.6, comp, kbar)
+        O = oracle.attention(q, k, v, qp, qo, kp, ko, mask, 0.6, comp, kbar, vbar)
+        for n in range(len(q)):
+            sel = [m for m in range(len(k)) if mask[ql[n], kl[m]]]
+            w = np.exp(0.6 * (k[sel] @ q[n]) - lse[n])
+            tot, acc = w.sum(), w @ v[sel]
+            if comp:
+                ex = [j for j in range(6) if not mask[ql[n], j] and ksz[j] > 0]
+                wc = ksz[ex] * np.exp(0.6 * (kbar[ex] @ q[n]) - lse[n])
+                tot, acc = tot + wc.sum(), acc + wc @ vbar[ex]
+            assert abs(tot - 1.0) <= 1e-12
+            assert np.allclose(acc, O[n], rtol=0, atol=1e-12)
