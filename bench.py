@@ -347,21 +347,29 @@ def main():
         d_o = torch.randn(q.shape, generator=gen).to(q.dtype).to(dev)
         wsb = L.workspace(L.sa_block_sparse_attn_bwd_workspace_size(p, Cq, Ck), dev)
         grads = [torch.empty(q.shape, dtype=torch.float32, device=dev) for _ in range(3)]
-        bwd = lambda: L.sa_block_sparse_attn_bwd(p, ac, qt, kt, v_perm, mask2, o2, d_o, *grads, wsb)
-        L.sa_block_sparse_attn(p, ac, qt, kt, v_perm, None, mask2, o2, ws)
-        bwd()
-        t = Timer()
-        for _ in range(reps):
-            t.start()
+        # the forward's log-sum-exp, which the backward then takes instead of
+        # recomputing it
+        lse = torch.empty(w.heads, w.n, dtype=torch.float32, device=dev)
+        L.sa_block_sparse_attn(p, L.attn_cfg(False, ac.scale, lse=lse), qt, kt, v_perm, None, mask2, o2, ws)
+        timed = {}
+        for name, given in (("lse_given", lse), ("lse_recomputed", None)):
+            bwd = lambda: L.sa_block_sparse_attn_bwd(p, ac, qt, kt, v_perm, mask2, o2, d_o, *grads, wsb, lse=given)
             bwd()
-            t.stop()
-        bms = float(np.mean(t.ms()))
+            t = Timer()
+            for _ in range(reps):
+                t.start()
+                bwd()
+                t.stop()
+            timed[name] = float(np.mean(t.ms()))
+        bms = timed["lse_given"]
         # 10 d flops per selected (query, key) pair: S, dP, dV, dQ, dK
         bflops = 2.5 * eff
         backward = {"ms": bms, "algorithmic_flops": bflops, "tflops": bflops / (bms * 1e-3) / 1e12,
-                    "flops_rule": "10 d per selected (query, key) pair (S, dP, dV, dQ, dK), LSE recomputed"}
+                    "ms_lse_recomputed": timed["lse_recomputed"],
+                    "flops_rule": "10 d per selected (query, key) pair (S, dP, dV, dQ, dK); the forward's "
+                                  "log-sum-exp given"}
         print(f"# backward {bms:.3f} ms, {backward['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
-        del wsb, grads, d_o
+        del wsb, grads, d_o, lse
 
     quality = None
     if args.quality:

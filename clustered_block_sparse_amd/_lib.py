@@ -46,7 +46,7 @@ class SelectCfg(ctypes.Structure):
 
 class AttnCfg(ctypes.Structure):
     _fields_ = [("compensate", I32), ("scale", ctypes.c_float), ("ev_start", ctypes.c_void_p),
-                ("ev_stop", ctypes.c_void_p)]
+                ("ev_stop", ctypes.c_void_p), ("lse", ctypes.c_void_p)]
 
 
 class Clusters(ctypes.Structure):
@@ -91,7 +91,7 @@ def load():
                                                  vp, vp]
     lib.sa_block_sparse_attn_bwd_workspace_size.argtypes = [P(Problem), I32, I32, P(ctypes.c_size_t)]
     lib.sa_block_sparse_attn_bwd.argtypes = [P(Problem), P(AttnCfg), P(Clusters), P(Clusters), vp, vp, vp, vp, vp,
-                                             vp, vp, vp, ctypes.c_size_t, vp]
+                                             vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sa_forward.argtypes = [P(Problem), P(ClusterCfg), P(ClusterCfg), P(SelectCfg), P(AttnCfg), vp, vp,
                                vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.sa_status_string.argtypes = [I32]
@@ -140,12 +140,13 @@ def select_cfg(top_p=0.9, topk_floor=1, online_topk=False, size_weighted=True, d
                      int(group), float(max_entropy), r, float(stat_lambda))
 
 
-def attn_cfg(compensate=False, scale=0.0, events=None) -> AttnCfg:
+def attn_cfg(compensate=False, scale=0.0, events=None, lse=None) -> AttnCfg:
     """events: optional (start, stop) HipEvent pair recorded around the
-    attention kernels of the calls made with this configuration."""
+    attention kernels of the calls made with this configuration; lse:
+    optional float32 [H, n] tensor that receives each query's log-sum-exp."""
     start, stop = events if events is not None else (None, None)
     return AttnCfg(int(bool(compensate)), float(scale), start.handle if start else None,
-                   stop.handle if stop else None)
+                   stop.handle if stop else None, None if lse is None else lse.data_ptr())
 
 
 def _ptr(t):
@@ -271,11 +272,12 @@ def sa_block_sparse_attn_bwd_workspace_size(p: Problem, q_clusters: int, k_clust
 
 
 def sa_block_sparse_attn_bwd(p: Problem, cfg: AttnCfg, q: ClusterTensors, k: ClusterTensors, v_perm, mask, o, d_o,
-                             dq, dk, dv, ws):
+                             dq, dk, dv, ws, lse=None):
     _check("sa_block_sparse_attn_bwd",
            load().sa_block_sparse_attn_bwd(ctypes.byref(p), ctypes.byref(cfg), ctypes.byref(q.struct()),
                                            ctypes.byref(k.struct()), _ptr(v_perm), _ptr(mask), _ptr(o), _ptr(d_o),
-                                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(), _stream()))
+                                           _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(ws), ws.numel(),
+                                           _stream()))
 
 
 def sa_forward(p: Problem, qcfg: ClusterCfg, kcfg: ClusterCfg, scfg: SelectCfg, acfg: AttnCfg, q, k, v, o,

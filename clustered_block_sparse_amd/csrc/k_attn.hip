@@ -423,9 +423,11 @@ __global__ __launch_bounds__(128) void attn_simple(AttnArgs a, Prep p, float sca
   }
   if (qv) {
     const float inv = l > 0.f ? 1.f / l : 0.f;
-    T* op = (T*)a.o + (size_t(h) * N + a.q_idx[size_t(h) * N + p0 + t]) * D;
+    const int32_t orig = a.q_idx[size_t(h) * N + p0 + t];
+    T* op = (T*)a.o + (size_t(h) * N + orig) * D;
 #pragma unroll
     for (int c = 0; c < D; ++c) op[c] = from_f<T>(o[c] * inv);
+    if (a.lse) a.lse[size_t(h) * N + orig] = l > 0.f ? m + logf(l) : -__builtin_huge_valf();
   }
 }
 
@@ -1031,6 +1033,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
   // ---------------- epilogue: normalise, stage, scatter to original rows ----
   const float ltot = pair_sum(lsum);
   const float inv = ltot > 0.f ? 1.f / ltot : 0.f;
+  // the normaliser: sum 2^(s sl2) = 2^m ltot, as a natural log
+  if (a.lse && qv && hi == 0)
+    a.lse[size_t(h) * N + a.q_idx[size_t(h) * N + p0 + qr]] =
+        ltot > 0.f ? (m + __log2f(ltot)) * 0.69314718055994531f : -__builtin_huge_valf();
   __syncthreads();
   // stage O in the K tiles (query rows 0..63 in K0, 64..127 in K1), then
   // scatter whole rows to their original tokens

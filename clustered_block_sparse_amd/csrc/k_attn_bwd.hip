@@ -210,6 +210,7 @@ struct BwdArgs {
   const bf16_t* v_perm;   // [H][N][D] key-cluster order
   const uint32_t* mask;   // [H][Cq][W]
   const bf16_t* dO_perm;  // [H][N][D] query-cluster order
+  const float* lse_in;    // [H][N] original order, the forward's natural-log normaliser (optional)
   const float* Dv;        // [H][N] query-cluster order
   float* lse2;            // [H][N] log2-domain log-sum-exp, query-cluster order
   const int4* qtiles;     // [H][maxTq]
@@ -289,9 +290,10 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     }
   };
 
-  // pass 1: log-sum-exp of the lane's query (log2 domain)
+  // pass 1: log-sum-exp of the lane's query (log2 domain), unless the
+  // forward's is given
   float m = -__builtin_huge_valf(), l = 0.f;
-  walk(false, [&](int nv) {
+  if (!a.lse_in) walk(false, [&](int nv) {
     floatx16 s;
     scores(s, nv);
     float mx = -__builtin_huge_valf();
@@ -305,7 +307,11 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     l = l * __builtin_amdgcn_exp2f(m - mn) + pair_sum(acc);
     m = mn;
   });
-  const float lse = l > 0.f ? m + __log2f(l) : __builtin_huge_valf();  // no key: P = 0
+  float lse = l > 0.f ? m + __log2f(l) : __builtin_huge_valf();  // no key: P = 0
+  if (a.lse_in) {
+    const float ln = qv ? a.lse_in[size_t(h) * N + a.q_idx[qpos]] : 0.f;
+    lse = ln == -__builtin_huge_valf() ? __builtin_huge_valf() : ln * LOG2E;
+  }
   const float dn = qv ? a.Dv[qpos] : 0.f;
   if (qv && hi == 0) a.lse2[qpos] = lse;
 
@@ -502,6 +508,7 @@ hipError_t attn_bwd_run(const AttnBwdArgs& g, Arena& s, hipStream_t st) {
   a.v_perm = (const bf16_t*)g.v_perm;
   a.mask = g.mask;
   a.dO_perm = b.dO_perm;
+  a.lse_in = g.lse;
   a.Dv = b.Dv;
   a.lse2 = b.lse2;
   a.qtiles = b.qtiles;

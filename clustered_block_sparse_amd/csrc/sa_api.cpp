@@ -402,6 +402,7 @@ sa_status do_attn(const sa_problem* p, const sa_attn_cfg* c, const sa_clusters* 
   a.o = o;
   a.ev_start = static_cast<hipEvent_t>(c->ev_start);
   a.ev_stop = static_cast<hipEvent_t>(c->ev_stop);
+  a.lse = static_cast<float*>(c->lse);
   Arena tmp = s;
   return hip_status(attn_run(a, tmp, st));
 }
@@ -586,8 +587,8 @@ SA_API sa_status sa_block_sparse_attn_bwd_workspace_size(const sa_problem* p, in
 SA_API sa_status sa_block_sparse_attn_bwd(const sa_problem* p, const sa_attn_cfg* cfg,
                                           const sa_clusters* q, const sa_clusters* k,
                                           const void* v_perm, const uint32_t* mask, const void* o,
-                                          const void* d_o, float* dq, float* dk, float* dv, void* ws,
-                                          size_t ws_bytes, void* stream) {
+                                          const void* d_o, const float* lse, float* dq, float* dk,
+                                          float* dv, void* ws, size_t ws_bytes, void* stream) {
   sa_status st = check_problem(p);
   if (st != SA_OK) return st;
   if (p->dtype != SA_BF16) return SA_ERR_DTYPE;
@@ -615,6 +616,7 @@ SA_API sa_status sa_block_sparse_attn_bwd(const sa_problem* p, const sa_attn_cfg
   a.mask = mask;
   a.O = o;
   a.dO = d_o;
+  a.lse = lse;
   a.dq = dq;
   a.dk = dk;
   a.dv = dv;

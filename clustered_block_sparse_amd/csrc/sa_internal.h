@@ -181,6 +181,7 @@ struct AttnArgs {
   void* o;                // [H][N][d] original order
   hipEvent_t ev_start;    // recorded right before / after the attention
   hipEvent_t ev_stop;     // kernels when not null (caller's timing events)
+  float* lse;             // [H][N] original order, natural-log normaliser (optional)
 };
 size_t attn_scratch(int H, int N, int d, int Cq, int Ck, int tile_rows, int compensate, int dtype,
                     int max_tiles);
@@ -199,6 +200,7 @@ struct AttnBwdArgs {
   const uint32_t* mask;   // [H][Cq][W]
   const void* O;          // bf16 [H][N][d] forward output, original order
   const void* dO;         // bf16 [H][N][d] original order
+  const float* lse;       // f32 [H][N] original order, the forward's normaliser (optional)
   float* dq;              // f32 [H][N][d] original order
   float* dk;
   float* dv;

@@ -159,6 +159,15 @@ typedef struct sa_attn_cfg {
    * NULL with one non-NULL is SA_ERR_INVALID_ARG. */
   void* ev_start;
   void* ev_stop;
+  /* Optional output, or NULL: float [H, n] in the original token order, the
+   * natural-log normaliser of each query's attention (the log of the
+   * softmax denominator over its selected keys' scaled scores, plus the
+   * compensation terms log|K_j| + <q, kbar_j> scale when compensate is on;
+   * -inf for a query with nothing to attend).  Written by
+   * sa_block_sparse_attn, its allocation-free form and sa_forward; the
+   * backward takes it (from a forward without compensation) instead of
+   * recomputing it. */
+  void* lse;
 } sa_attn_cfg;
 
 /* Clustering of one tensor (Q or K).  Every pointer is caller-owned device
@@ -291,6 +300,8 @@ SA_API sa_status sa_block_sparse_attn_noalloc(const sa_problem* p, const sa_attn
  *   q, k     clusters of sa_cluster (x_perm used), v_perm as for the forward
  *   mask     the selection the forward used
  *   o, d_o   bf16 [H, n, d] forward output and its gradient, original order
+ *   lse      optional f32 [H, n]: the forward's normaliser (sa_attn_cfg.lse of
+ *            the same forward, without compensation); NULL recomputes it
  *   dq, dk, dv  f32 [H, n, d] gradients, original order (every row written)
  * bf16 only (SA_ERR_DTYPE otherwise); compensation has no backward here.
  * Workspace: sa_block_sparse_attn_bwd_workspace_size() bytes. */
@@ -299,8 +310,8 @@ SA_API sa_status sa_block_sparse_attn_bwd_workspace_size(const sa_problem* p, in
 SA_API sa_status sa_block_sparse_attn_bwd(const sa_problem* p, const sa_attn_cfg* cfg,
                                           const sa_clusters* q, const sa_clusters* k,
                                           const void* v_perm, const uint32_t* mask, const void* o,
-                                          const void* d_o, float* dq, float* dk, float* dv, void* ws,
-                                          size_t ws_bytes, void* stream);
+                                          const void* d_o, const float* lse, float* dq, float* dk,
+                                          float* dv, void* ws, size_t ws_bytes, void* stream);
 
 /* The whole path: cluster Q and K, permute V, select, attend.
  * o dtype [H, n, d] original order; mask as in sa_select. */

@@ -159,7 +159,7 @@ def test_backward_validation(lib):
 
     def bwd(prob=p, a=L.attn_cfg(False), ws_bytes=need, d_o=FAKE):
         return lib.sa_block_sparse_attn_bwd(ctypes.byref(prob), ctypes.byref(a), ctypes.byref(cl), ctypes.byref(cl),
-                                            FAKE, FAKE, FAKE, d_o, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
+                                            FAKE, FAKE, FAKE, d_o, None, FAKE, FAKE, FAKE, FAKE, ws_bytes, None)
 
     assert bwd(prob=L.problem(1, 256, 64, 4, 8, 8, "f32")) == 3
     assert bwd(a=L.attn_cfg(True)) == 5

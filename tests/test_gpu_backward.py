@@ -212,3 +212,87 @@ def test_backward_given_mask_edges():
             if not (mx <= tol_max * rmax and mean <= tol_mean * rmean):
                 bad.append((h, name, mx / rmax, mean / rmean))
     assert not bad, bad
+
+
+LSE_CASES = [replace(wl.TINY, name="tiny_f32"),
+             replace(wl.TINY, compensate=True, name="tiny_f32_comp"),
+             replace(WAN_S.forced_density(0.1), compensate=False, name="wan_small_fixed"),
+             replace(WAN_S.forced_density(0.1), name="wan_small_fixed_comp"),
+             replace(TAB_S.forced_density(0.1), name="tab_small_d64_comp"),
+             replace(WAN_S, compensate=False, name="wan_small_p09")]
+
+
+@pytest.mark.parametrize("w", LSE_CASES, ids=lambda w: w.name)
+def test_forward_lse_and_backward_given_lse(w):
+    """The forward's log-sum-exp output against oracle.attention_lse given the
+    GPU's clusters, mask and means (absolute, in the log domain: the kernel's
+    denominator adds bf16-rounded probabilities, up to 2^-9 relative each, so
+    at most 2^-8 ~ 4e-3 on any query, and 2^-10 ~ 1e-3 on average, the mean
+    rounding error when one key dominates the sum); then, without compensation,
+    the backward taking it in place of its own pass: the oracle bounds of the
+    other cases, and the recomputing backward within the same bounds.  The
+    fp32 path (no rounded probabilities) to 1e-5."""
+    say(f"[lse] {w.name} H={w.heads} N={w.n} d={w.d} comp={w.compensate}")
+    q, k, v = inputs(w)
+    p, qc, kc, sc, ac = api.cfgs(w)
+    ws = workspace_for(p, qc, kc, sc, ac)
+    qt = L.alloc_clusters(p, qc, DEV, q.dtype)
+    kt = L.alloc_clusters(p, kc, DEV, k.dtype)
+    L.sa_cluster_qk(p, qc, kc, q, k, qt, kt, ws)
+    Cq, Ck = qt.num_clusters, kt.num_clusters
+    v_perm = torch.empty_like(v)
+    vbar = torch.empty(w.heads, Ck, w.d, dtype=torch.float32, device=DEV) if w.compensate else None
+    L.sa_permute(p, kt, v, v_perm, vbar)
+    mask = torch.empty(w.heads, Cq, L.mask_words(Ck), dtype=torch.int32, device=DEV)
+    counts = torch.empty(w.heads, Cq, dtype=torch.int32, device=DEV)
+    ktop = torch.empty(w.heads, dtype=torch.int32, device=DEV)
+    L.sa_select(p, sc, qt, kt, mask, counts, None, ktop, ws)
+    o = torch.empty_like(q)
+    lse = torch.full((w.heads, w.n), float("nan"), dtype=torch.float32, device=DEV)
+    L.sa_block_sparse_attn(p, L.attn_cfg(w.compensate, 0.0, lse=lse), qt, kt, v_perm, vbar, mask, o, ws)
+    o_plain = torch.empty_like(q)
+    L.sa_block_sparse_attn(p, ac, qt, kt, v_perm, vbar, mask, o_plain, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_plain), "the log-sum-exp output changes nothing else"
+    gm = unpack_mask(mask, Ck)
+    qs, ks = to_np(q), to_np(k)
+    for h in range(w.heads):
+        kb = kt.centroids[h].double().cpu().numpy() if w.compensate else None
+        ref = oracle.attention_lse(qs[h], ks[h], qt.perm[h].cpu().numpy(), qt.offsets[h].cpu().numpy(),
+                                   kt.perm[h].cpu().numpy(), kt.offsets[h].cpu().numpy(), gm[h], scale_of(w),
+                                   w.compensate, kb)
+        got = lse[h].double().cpu().numpy()
+        err = np.abs(got - ref)
+        say(f"  head {h}: lse max-abs {err.max():.2e} mean-abs {err.mean():.2e} (range {ref.min():.2f}..{ref.max():.2f})")
+        if w.dtype == "f32":  # fp32 path: no rounding of the probabilities
+            assert np.isfinite(got).all() and err.max() <= 1e-5
+        else:
+            assert np.isfinite(got).all() and err.max() <= 4e-3 and err.mean() <= 1e-3
+    if w.compensate or w.dtype != "bf16":  # the backward is bf16 without compensation
+        return
+    d_o = torch.randn(q.shape, generator=torch.Generator(device="cpu").manual_seed(9)).to(torch.bfloat16).to(DEV)
+    wsb = L.workspace(L.sa_block_sparse_attn_bwd_workspace_size(p, Cq, Ck), DEV)
+    given = [torch.full(q.shape, float("nan"), dtype=torch.float32, device=DEV) for _ in range(3)]
+    L.sa_block_sparse_attn_bwd(p, ac, qt, kt, v_perm, mask, o, d_o, *given, wsb, lse=lse)
+    recomp = [torch.empty_like(x) for x in given]
+    L.sa_block_sparse_attn_bwd(p, ac, qt, kt, v_perm, mask, o, d_o, *recomp, wsb)
+    torch.cuda.synchronize()
+    vs, gs = to_np(v), to_np(d_o)
+    bad = []
+    for h in range(w.heads):
+        ref = oracle.attention_backward(qs[h], ks[h], vs[h], qt.perm[h].cpu().numpy(), qt.offsets[h].cpu().numpy(),
+                                        kt.perm[h].cpu().numpy(), kt.offsets[h].cpu().numpy(), gm[h], scale_of(w),
+                                        gs[h])
+        for name, g_, r_, want in zip(("dq", "dk", "dv"), given, recomp, ref):
+            g_ = g_[h].double().cpu().numpy()
+            r_ = r_[h].double().cpu().numpy()
+            assert np.isfinite(g_).all(), name
+            rmax, rmean = float(np.abs(want).max()), float(np.abs(want).mean())
+            tol_max, tol_mean = TOL[name]
+            for label, x in (("oracle", want), ("recomputing backward", r_)):
+                err = np.abs(g_ - x)
+                mx, mean = float(err.max()), float(err.mean())
+                say(f"  head {h} {name} vs {label}: max {mx / rmax:.2e} of max, mean {mean / rmean:.2e} of mean")
+                if not (mx <= tol_max * rmax and mean <= tol_mean * rmean):
+                    bad.append((h, name, label, mx / rmax, mean / rmean))
+    assert not bad, bad
