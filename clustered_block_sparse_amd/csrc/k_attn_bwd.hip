@@ -227,8 +227,10 @@ struct BwdArgs {
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   constexpr int DS = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Kt[TB * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[TB * D];
+  // a step covers up to SBK 32-key blocks behind one load and barrier
+  constexpr int SBK = 2;
+  __shared__ __attribute__((aligned(16))) bf16_t Kt[SBK * TB * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Vt[SBK * TB * D];
   const int h = blockIdx.y, tix = blockIdx.x;
   if (tix >= a.nqt[h]) return;
   const int4 td = a.qtiles[size_t(h) * a.maxTq + tix];
@@ -257,17 +259,17 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   const int W = ceil_div(a.Ck, 32);
 
   // S^T of one 32-key step (keys of this step past `nv` -> -inf)
-  auto scores = [&](floatx16& s, int nv) {
+  auto scores = [&](floatx16& s, const bf16_t* Kb, int nv) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
 #pragma unroll
-    for (int st = 0; st < DS; ++st) s = mfma32(frag_rows<D>(Kt, st), qf[st], s);
+    for (int st = 0; st < DS; ++st) s = mfma32(frag_rows<D>(Kb, st), qf[st], s);
 #pragma unroll
     for (int r = 0; r < 16; ++r)
       if (drow(r, hi) >= nv) s[r] = -__builtin_huge_valf();
   };
-  // every selected key cluster in 32-key steps; body(nv) after the step's
-  // tiles are in LDS
+  // every selected key cluster in steps of up to SBK 32-key blocks;
+  // body(K block, V block, nv) for each block after the step's tiles are in LDS
   auto walk = [&](bool with_v, auto&& body) {
     for (int wd = 0; wd < W; ++wd) {
       uint32_t bits = mr[wd];
@@ -277,14 +279,17 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
         const int j = 32 * wd + __ffs(bits) - 1;
         bits &= bits - 1;
         const int k0 = ko[j], k1 = ko[j + 1];
-        for (int p = k0; p < k1; p += TB) {
-          const int nv = min(TB, k1 - p);
+        for (int p = k0; p < k1; p += SBK * TB) {
+          const int nv = min(SBK * TB, k1 - p);
+          const int nb = ceil_div(nv, TB);  // blocks in this step (uniform)
           __syncthreads();  // the previous step is done with the tiles
-          load_tile<D>(kh, kbytes, Kt, p, nv);
-          if (with_v) load_tile<D>(vh, kbytes, Vt, p, nv);
+          for (int b = 0; b < nb; ++b) {
+            load_tile<D>(kh, kbytes, Kt + b * TB * D, p + b * TB, min(TB, nv - b * TB));
+            if (with_v) load_tile<D>(vh, kbytes, Vt + b * TB * D, p + b * TB, min(TB, nv - b * TB));
+          }
           __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
           __syncthreads();
-          body(nv);
+          for (int b = 0; b < nb; ++b) body(Kt + b * TB * D, Vt + b * TB * D, min(TB, nv - b * TB));
         }
       }
     }
@@ -293,9 +298,9 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   // pass 1: log-sum-exp of the lane's query (log2 domain), unless the
   // forward's is given
   float m = -__builtin_huge_valf(), l = 0.f;
-  if (!a.lse_in) walk(false, [&](int nv) {
+  if (!a.lse_in) walk(false, [&](const bf16_t* Kb, const bf16_t*, int nv) {
     floatx16 s;
-    scores(s, nv);
+    scores(s, Kb, nv);
     float mx = -__builtin_huge_valf();
 #pragma unroll
     for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
@@ -321,13 +326,13 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
-  walk(true, [&](int nv) {
+  walk(true, [&](const bf16_t* Kb, const bf16_t* Vb, int nv) {
     floatx16 s, dp;
-    scores(s, nv);
+    scores(s, Kb, nv);
 #pragma unroll
     for (int r = 0; r < 16; ++r) dp[r] = 0.f;
 #pragma unroll
-    for (int st = 0; st < DS; ++st) dp = mfma32(frag_rows<D>(Vt, st), gf[st], dp);  // dP^T = V dO^T
+    for (int st = 0; st < DS; ++st) dp = mfma32(frag_rows<D>(Vb, st), gf[st], dp);  // dP^T = V dO^T
     uint32_t pk[8];
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
@@ -339,7 +344,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     for (int ks = 0; ks < 2; ++ks) {
       const bf16x8_t bf = as_bf8(make_uint4(pk[4 * ks], pk[4 * ks + 1], pk[4 * ks + 2], pk[4 * ks + 3]));
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(frag_tr<D>(Kt, dt, ks), bf, acc[dt]);
+      for (int dt = 0; dt < DT; ++dt) acc[dt] = mfma32(frag_tr<D>(Kb, dt, ks), bf, acc[dt]);
     }
   });
   // lane (col, hi) holds dQ^T[32 dt + drow(r)][query col]
@@ -358,9 +363,12 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
 template <int D>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   constexpr int DS = D / 16, DT = D / 32;
-  __shared__ __attribute__((aligned(16))) bf16_t Qt[TB * D];
-  __shared__ __attribute__((aligned(16))) bf16_t Gt[TB * D];
-  __shared__ float lse_s[TB], d_s[TB];
+  // a step covers up to SB 32-row blocks of query rows behind one load and
+  // barrier (the kernel runs one workgroup per CU: registers, not LDS, bound it)
+  constexpr int SB = 4;
+  __shared__ __attribute__((aligned(16))) bf16_t Qt[SB * TB * D];
+  __shared__ __attribute__((aligned(16))) bf16_t Gt[SB * TB * D];
+  __shared__ float lse_s[SB * TB], d_s[SB * TB];
   const int h = blockIdx.y, tix = blockIdx.x;
   if (tix >= a.nkt[h]) return;
   const int4 td = a.ktiles[size_t(h) * a.maxTk + tix];
@@ -393,50 +401,57 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) dka[dt][r] = dva[dt][r] = 0.f;
+  // one 32-row block of the step: S = Q K^T (rows queries, lane column =
+  // key), dP = dO V^T, then dV^T += dO^T P and dK^T += Q^T dS
+  auto block = [&](const bf16_t* Qb, const bf16_t* Gb, const float* lse_b, const float* d_b) {
+    floatx16 s, dp;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+#pragma unroll
+    for (int st = 0; st < DS; ++st) {
+      s = mfma32(frag_rows<D>(Qb, st), kf[st], s);
+      dp = mfma32(frag_rows<D>(Gb, st), vf[st], dp);
+    }
+    uint32_t pp[8], ds[8];
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const int r0 = drow(r, hi), r1 = drow(r + 1, hi);
+      // query rows past nv carry lse = +inf: P = 0
+      const float e0 = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse_b[r0]));
+      const float e1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], sl2, -lse_b[r1]));
+      pp[r >> 1] = pack2(e0, e1);
+      ds[r >> 1] = pack2(e0 * (dp[r] - d_b[r0]), e1 * (dp[r + 1] - d_b[r1]));
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const bf16x8_t pb = as_bf8(make_uint4(pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]));
+      const bf16x8_t db = as_bf8(make_uint4(ds[4 * ks], ds[4 * ks + 1], ds[4 * ks + 2], ds[4 * ks + 3]));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        dva[dt] = mfma32(frag_tr<D>(Gb, dt, ks), pb, dva[dt]);  // dV^T += dO^T P
+        dka[dt] = mfma32(frag_tr<D>(Qb, dt, ks), db, dka[dt]);  // dK^T += Q^T dS
+      }
+    }
+  };
   for (int u = 0; u < nsel; ++u) {
     const int i = lst[u];
     const int q0 = qo[i], q1 = qo[i + 1];
-    for (int p = q0; p < q1; p += TB) {
-      const int nv = min(TB, q1 - p);
+    for (int p = q0; p < q1; p += SB * TB) {
+      const int nv = min(SB * TB, q1 - p);
+      const int nb = ceil_div(nv, TB);  // blocks in this step (uniform)
       __syncthreads();  // the previous step is done with the tiles
-      load_tile<D>(qh, qbytes, Qt, p, nv);
-      load_tile<D>(gh, qbytes, Gt, p, nv);
-      if (t < TB) {
+      for (int b = 0; b < nb; ++b) {
+        load_tile<D>(qh, qbytes, Qt + b * TB * D, p + b * TB, min(TB, nv - b * TB));
+        load_tile<D>(gh, qbytes, Gt + b * TB * D, p + b * TB, min(TB, nv - b * TB));
+      }
+      if (t < SB * TB) {
         const bool ok = t < nv;
         lse_s[t] = ok ? a.lse2[size_t(h) * N + p + t] : __builtin_huge_valf();
         d_s[t] = ok ? a.Dv[size_t(h) * N + p + t] : 0.f;
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
       __syncthreads();
-      // S = Q K^T (rows queries, lane column = key), dP = dO V^T
-      floatx16 s, dp;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
-#pragma unroll
-      for (int st = 0; st < DS; ++st) {
-        s = mfma32(frag_rows<D>(Qt, st), kf[st], s);
-        dp = mfma32(frag_rows<D>(Gt, st), vf[st], dp);
-      }
-      uint32_t pp[8], ds[8];
-#pragma unroll
-      for (int r = 0; r < 16; r += 2) {
-        const int r0 = drow(r, hi), r1 = drow(r + 1, hi);
-        // query rows past nv carry lse = +inf: P = 0
-        const float e0 = __builtin_amdgcn_exp2f(fmaf(s[r], sl2, -lse_s[r0]));
-        const float e1 = __builtin_amdgcn_exp2f(fmaf(s[r + 1], sl2, -lse_s[r1]));
-        pp[r >> 1] = pack2(e0, e1);
-        ds[r >> 1] = pack2(e0 * (dp[r] - d_s[r0]), e1 * (dp[r + 1] - d_s[r1]));
-      }
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8_t pb = as_bf8(make_uint4(pp[4 * ks], pp[4 * ks + 1], pp[4 * ks + 2], pp[4 * ks + 3]));
-        const bf16x8_t db = as_bf8(make_uint4(ds[4 * ks], ds[4 * ks + 1], ds[4 * ks + 2], ds[4 * ks + 3]));
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          dva[dt] = mfma32(frag_tr<D>(Gt, dt, ks), pb, dva[dt]);  // dV^T += dO^T P
-          dka[dt] = mfma32(frag_tr<D>(Qt, dt, ks), db, dka[dt]);  // dK^T += Q^T dS
-        }
-      }
+      for (int b = 0; b < nb; ++b) block(Qt + b * TB * D, Gt + b * TB * D, lse_s + b * TB, d_s + b * TB);
     }
   }
   if (kv) {
