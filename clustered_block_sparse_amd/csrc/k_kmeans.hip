@@ -243,7 +243,7 @@ __global__ __launch_bounds__(256) void kmeans_step_kernel(const bf16_t* __restri
                                                           int C, int G, const bf16_t* __restrict__ ctab,
                                                           const float* __restrict__ cnorm,
                                                           int32_t* __restrict__ labels, float* __restrict__ psum,
-                                                          int32_t* __restrict__ pcnt) {
+                                                          int32_t* __restrict__ pcnt, int32_t* __restrict__ rank) {
   constexpr int P = mfma_pitch<DC>();
   constexpr int KS = DC / 16;
   constexpr int DCP = step_dcp<DC>();
@@ -385,10 +385,24 @@ __global__ __launch_bounds__(256) void kmeans_step_kernel(const bf16_t* __restri
       lab[t] = valid ? bj : -1;
       if (valid) {
         labels[size_t(h) * N + tok] = bj;
-        atomicAdd(&cnt[bj], 1);
+        if (!rank) atomicAdd(&cnt[bj], 1);
       }
     }
     __syncthreads();  // labels of the group are in LDS
+    if (rank) {
+      // each token's rank among the workgroup's tokens of its cluster, in
+      // token order: the count before this group plus the group's earlier
+      // tokens with the same label (a stable counting sort's position inside
+      // the workgroup's share of the cluster)
+      const int bj = t < KSTEP_TOK ? lab[t] : -1;
+      if (bj >= 0) {
+        int r = 0;
+        for (int u = 0; u < t; ++u) r += lab[u] == bj ? 1 : 0;
+        rank[size_t(h) * N + tile * KSTEP_TOK + t] = cnt[bj] + r;
+      }
+      __syncthreads();  // every count read before this group's are added
+      if (bj >= 0) atomicAdd(&cnt[bj], 1);
+    }
     // sums: for every 16-token step, the one-hot B operand from the labels of
     // the lane's 8 tokens (in the order the transpose reads give them)
 #pragma unroll 1
@@ -625,6 +639,70 @@ hipError_t assign_dispatch(const void* x, int d, int col0, int dc, int H, int N,
   }
 }
 
+// After the last fused step: the stable counting sort of the labels and the
+// rows in cluster order, in one pass.  Workgroup (b, h) takes the tokens the
+// step's workgroup b covered (whole groups of 128, in token order); a token
+// of cluster c lands at offset[c] + (tokens of c in earlier workgroups) +
+// its rank inside its workgroup, i.e. in (label, index) order.  Offsets come
+// from the step's per-workgroup counts.  Cluster counts up to 128.
+__global__ __launch_bounds__(256) void kmeans_scatter_kernel(const bf16_t* __restrict__ x, int d, int N, int C,
+                                                             int CP, int nblk, int G,
+                                                             const int32_t* __restrict__ pcnt,
+                                                             const int32_t* __restrict__ labels,
+                                                             const int32_t* __restrict__ rank,
+                                                             int32_t* __restrict__ perm, int32_t* __restrict__ offsets,
+                                                             bf16_t* __restrict__ x_perm) {
+  __shared__ int base[128], tot[128], off[129];
+  const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  if (t < CP) {
+    int tb = 0, tt = 0;
+    const int32_t* pc = pcnt + size_t(h) * nblk * CP + t;
+    int bb = 0;
+    for (; bb + 8 <= nblk; bb += 8) {  // eight counts in flight
+      int v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = pc[size_t(bb + u) * CP];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        if (bb + u < b) tb += v[u];
+        tt += v[u];
+      }
+    }
+    for (; bb < nblk; ++bb) {
+      const int v = pc[size_t(bb) * CP];
+      if (bb < b) tb += v;
+      tt += v;
+    }
+    base[t] = tb;
+    tot[t] = tt;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int run = 0;
+    for (int c = 0; c < CP; ++c) {
+      off[c] = run;
+      run += tot[c];
+    }
+    off[CP] = run;
+  }
+  __syncthreads();
+  if (b == 0)
+    for (int c = t; c <= C; c += 256) offsets[size_t(h) * (C + 1) + c] = off[c];
+  const int t0 = b * G * KSTEP_TOK, t1 = min(N, t0 + G * KSTEP_TOK);
+  const size_t hn = size_t(h) * N;
+  auto pos_of = [&](int tok) {
+    const int c = labels[hn + tok];
+    return off[c] + base[c] + rank[hn + tok];
+  };
+  for (int tok = t0 + t; tok < t1; tok += 256) perm[hn + pos_of(tok)] = tok;
+  const int cpr = d / 8;  // 16-byte chunks of a row
+  for (int v = t; v < (t1 - t0) * cpr; v += 256) {
+    const int tok = t0 + v / cpr, ch = v % cpr;
+    *reinterpret_cast<uint4*>(x_perm + (hn + pos_of(tok)) * d + ch * 8) =
+        *reinterpret_cast<const uint4*>(x + (hn + tok) * d + ch * 8);
+  }
+}
+
 // Workgroups per head of the fused step: about 1024 in all, but at most one
 // per 2 CP tokens (so the partials, written and read once, move no more bytes
 // than the rows), and whole groups of 128 tokens each.
@@ -645,6 +723,7 @@ struct StepScratch {
   int32_t* pcnt;
   bf16_t* ctab;
   float* cnorm;
+  int32_t* rank;
   size_t bytes;
 };
 StepScratch step_scratch(int H, int N, int C, int dc, void* base) {
@@ -663,6 +742,7 @@ StepScratch step_scratch(int H, int N, int C, int dc, void* base) {
   r.pcnt = reinterpret_cast<int32_t*>(take(size_t(H) * nblk * CP * sizeof(int32_t)));
   r.ctab = reinterpret_cast<bf16_t*>(take(size_t(H) * 3 * CP * P * sizeof(bf16_t)));
   r.cnorm = reinterpret_cast<float*>(take(size_t(H) * CP * sizeof(float)));
+  r.rank = reinterpret_cast<int32_t*>(take(size_t(H) * N * sizeof(int32_t)));
   r.bytes = off;
   return r;
 }
@@ -694,7 +774,7 @@ void launch_geometry(int H, int N, int C, int per_cu, int cus, int& nblk, int& G
 
 template <int DC>
 hipError_t kmeans_step_launch(const void* x, int d, int col0, int H, int N, int C, float* c,
-                              int32_t* labels, float* scratch, bool first, hipStream_t st) {
+                              int32_t* labels, float* scratch, bool first, const StepSort* sort, hipStream_t st) {
   const int CP = (C + 31) & ~31;
   const StepScratch sc = step_scratch(H, N, C, DC, scratch);
   if (first) ctab_kernel<DC><<<dim3(CP, H), DC, 0, st>>>(c, C, CP, sc.ctab, sc.cnorm);
@@ -711,8 +791,11 @@ hipError_t kmeans_step_launch(const void* x, int d, int col0, int H, int N, int 
   int nblk, G;
   launch_geometry(H, N, C, per_cu, cus, nblk, G);
   kmeans_step_kernel<DC><<<dim3(nblk, H), 256, lds, st>>>((const bf16_t*)x, d, col0, N, C, G, sc.ctab, sc.cnorm,
-                                                          labels, sc.psum, sc.pcnt);
+                                                          labels, sc.psum, sc.pcnt, sort ? sc.rank : nullptr);
   kmeans_combine_kernel<DC><<<dim3(C, H), DC, 0, st>>>(sc.psum, sc.pcnt, nblk, C, CP, c, sc.ctab, sc.cnorm);
+  if (sort)
+    kmeans_scatter_kernel<<<dim3(nblk, H), 256, 0, st>>>((const bf16_t*)x, d, N, C, CP, nblk, G, sc.pcnt, labels,
+                                                        sc.rank, sort->perm, sort->offsets, (bf16_t*)sort->x_perm);
   return hipGetLastError();
 }
 
@@ -727,13 +810,15 @@ size_t kmeans_step_scratch(int H, int N, int C, int dc) {
 }
 
 hipError_t kmeans_step(const void* x, int d, int col0, int dc, int H, int N, int C, float* c,
-                       int32_t* labels, float* scratch, bool first, hipStream_t st) {
+                       int32_t* labels, float* scratch, bool first, const StepSort* sort, hipStream_t st) {
+  // the fused sort covers whole rows only
+  if (sort && (col0 != 0 || dc != d)) return hipErrorInvalidValue;
   switch (dc) {
-    case 16: return kmeans_step_launch<16>(x, d, col0, H, N, C, c, labels, scratch, first, st);
-    case 32: return kmeans_step_launch<32>(x, d, col0, H, N, C, c, labels, scratch, first, st);
-    case 48: return kmeans_step_launch<48>(x, d, col0, H, N, C, c, labels, scratch, first, st);
-    case 64: return kmeans_step_launch<64>(x, d, col0, H, N, C, c, labels, scratch, first, st);
-    case 128: return kmeans_step_launch<128>(x, d, col0, H, N, C, c, labels, scratch, first, st);
+    case 16: return kmeans_step_launch<16>(x, d, col0, H, N, C, c, labels, scratch, first, sort, st);
+    case 32: return kmeans_step_launch<32>(x, d, col0, H, N, C, c, labels, scratch, first, sort, st);
+    case 48: return kmeans_step_launch<48>(x, d, col0, H, N, C, c, labels, scratch, first, sort, st);
+    case 64: return kmeans_step_launch<64>(x, d, col0, H, N, C, c, labels, scratch, first, sort, st);
+    case 128: return kmeans_step_launch<128>(x, d, col0, H, N, C, c, labels, scratch, first, sort, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -257,10 +257,12 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
     for (int it = 0; it < c->iters && e == hipSuccess; ++it) {
       Arena tmp = s;
       if (fused) {
+        // the last step also sorts the labels and permutes the rows
         float* ksc = (float*)tmp.take(kmeans_step_scratch(H, N, C, d));
-        e = kmeans_step(x, d, 0, d, H, N, C, out->centroids, out->labels, ksc, it == 0, st);
-        if (e == hipSuccess && it + 1 == c->iters)
-          e = label_sort(out->labels, out->perm, out->offsets, H, N, C, tmp, st);
+        const StepSort so{out->perm, out->offsets, out->x_perm};
+        e = kmeans_step(x, d, 0, d, H, N, C, out->centroids, out->labels, ksc, it == 0,
+                        it + 1 == c->iters ? &so : nullptr, st);
+        if (e == hipSuccess && it + 1 == c->iters) return hip_status(e);
         continue;
       }
       float* msc = (float*)tmp.take(means_scratch(H, N, C, d));
@@ -310,7 +312,7 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
       for (int it = 0; it < c->iters && e == hipSuccess; ++it) {
         Arena t2 = tmp;
         if (fused) {
-          e = kmeans_step(x, d, col0, ds, H, N, Cs, cs, lab, msc, it == 0, st);
+          e = kmeans_step(x, d, col0, ds, H, N, Cs, cs, lab, msc, it == 0, nullptr, st);
           continue;
         }
         e = kmeans_assign(x, dt, d, col0, ds, H, N, Cs, cs, lab, st);

@@ -116,10 +116,18 @@ bool kmeans_width_supported(int dc);
 // between the steps of one run: it carries the centroids' matrix-core terms
 // from each step to the next; `first` builds them from c (the first step of a
 // run, or after c changed outside the steps).
+// With `sort` (whole rows only: col0 = 0, dc = d), the step also writes the
+// stable counting sort of its labels (perm, offsets) and x in that order
+// (x_perm), as label_sort and gather_rows would, in one extra pass.
+struct StepSort {
+  int32_t* perm;
+  int32_t* offsets;
+  void* x_perm;
+};
 bool kmeans_step_supported(int dtype, const void* x, int d, int col0, int dc, int C);
 size_t kmeans_step_scratch(int H, int N, int C, int dc);
 hipError_t kmeans_step(const void* x, int d, int col0, int dc, int H, int N, int C, float* c,
-                       int32_t* labels, float* scratch, bool first, hipStream_t st);
+                       int32_t* labels, float* scratch, bool first, const StepSort* sort, hipStream_t st);
 // labels = (a_t*Cs + a_h)*Cs + a_w
 hipError_t combo_labels(const int32_t* sub_labels, int32_t* labels, int H, int N, int Cs,
                         hipStream_t st);
