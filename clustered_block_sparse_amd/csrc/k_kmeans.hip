@@ -474,13 +474,21 @@ __device__ __forceinline__ void write_ctab_row(const float* v, int c, int CP, bf
 }
 
 // the table of every centroid row (padding rows zero) from fp32 centroids:
-// before the first step of a run
+// before the first step of a run.  With sx (first-k seeding), the centroids
+// are first set to the slice's first C rows of x, as seed_kernel would.
 template <int DC>
-__global__ __launch_bounds__(DC) void ctab_kernel(const float* __restrict__ cent, int C, int CP,
-                                                  bf16_t* __restrict__ ctab, float* __restrict__ cnorm) {
+__global__ __launch_bounds__(DC) void ctab_kernel(float* __restrict__ cent, int C, int CP,
+                                                  bf16_t* __restrict__ ctab, float* __restrict__ cnorm,
+                                                  const bf16_t* __restrict__ sx, int d, int col0, int N) {
   __shared__ float row[DC];
   const int c = blockIdx.x, h = blockIdx.y;
-  if (c < C) row[threadIdx.x] = cent[(size_t(h) * C + c) * DC + threadIdx.x];
+  if (c < C && sx) {
+    const float v = bf2f(sx[(size_t(h) * N + c) * d + col0 + threadIdx.x]);
+    cent[(size_t(h) * C + c) * DC + threadIdx.x] = v;
+    row[threadIdx.x] = v;
+  } else if (c < C) {
+    row[threadIdx.x] = cent[(size_t(h) * C + c) * DC + threadIdx.x];
+  }
   __syncthreads();
   write_ctab_row<DC>(c < C ? row : nullptr, c, CP, ctab + size_t(h) * 3 * CP * mfma_pitch<DC>(),
                      cnorm + size_t(h) * CP + c);
@@ -774,10 +782,13 @@ void launch_geometry(int H, int N, int C, int per_cu, int cus, int& nblk, int& G
 
 template <int DC>
 hipError_t kmeans_step_launch(const void* x, int d, int col0, int H, int N, int C, float* c,
-                              int32_t* labels, float* scratch, bool first, const StepSort* sort, hipStream_t st) {
+                              int32_t* labels, float* scratch, bool first, bool seed, const StepSort* sort,
+                              hipStream_t st) {
   const int CP = (C + 31) & ~31;
   const StepScratch sc = step_scratch(H, N, C, DC, scratch);
-  if (first) ctab_kernel<DC><<<dim3(CP, H), DC, 0, st>>>(c, C, CP, sc.ctab, sc.cnorm);
+  if (first)
+    ctab_kernel<DC><<<dim3(CP, H), DC, 0, st>>>(c, C, CP, sc.ctab, sc.cnorm, seed ? (const bf16_t*)x : nullptr, d,
+                                                col0, N);
   const size_t lds = size_t(KSTEP_TOK) * step_dcp<DC>() * 2 + size_t(9) * KSTEP_TOK * 4 + size_t(CP) * 4;
   if (lds > 64 * 1024 &&
       hipFuncSetAttribute((const void*)kmeans_step_kernel<DC>, hipFuncAttributeMaxDynamicSharedMemorySize,
@@ -810,15 +821,16 @@ size_t kmeans_step_scratch(int H, int N, int C, int dc) {
 }
 
 hipError_t kmeans_step(const void* x, int d, int col0, int dc, int H, int N, int C, float* c,
-                       int32_t* labels, float* scratch, bool first, const StepSort* sort, hipStream_t st) {
-  // the fused sort covers whole rows only
-  if (sort && (col0 != 0 || dc != d)) return hipErrorInvalidValue;
+                       int32_t* labels, float* scratch, bool first, bool seed, const StepSort* sort,
+                       hipStream_t st) {
+  // the fused sort covers whole rows only; seeding goes with the first step
+  if ((sort && (col0 != 0 || dc != d)) || (seed && !first)) return hipErrorInvalidValue;
   switch (dc) {
-    case 16: return kmeans_step_launch<16>(x, d, col0, H, N, C, c, labels, scratch, first, sort, st);
-    case 32: return kmeans_step_launch<32>(x, d, col0, H, N, C, c, labels, scratch, first, sort, st);
-    case 48: return kmeans_step_launch<48>(x, d, col0, H, N, C, c, labels, scratch, first, sort, st);
-    case 64: return kmeans_step_launch<64>(x, d, col0, H, N, C, c, labels, scratch, first, sort, st);
-    case 128: return kmeans_step_launch<128>(x, d, col0, H, N, C, c, labels, scratch, first, sort, st);
+    case 16: return kmeans_step_launch<16>(x, d, col0, H, N, C, c, labels, scratch, first, seed, sort, st);
+    case 32: return kmeans_step_launch<32>(x, d, col0, H, N, C, c, labels, scratch, first, seed, sort, st);
+    case 48: return kmeans_step_launch<48>(x, d, col0, H, N, C, c, labels, scratch, first, seed, sort, st);
+    case 64: return kmeans_step_launch<64>(x, d, col0, H, N, C, c, labels, scratch, first, seed, sort, st);
+    case 128: return kmeans_step_launch<128>(x, d, col0, H, N, C, c, labels, scratch, first, seed, sort, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -252,15 +252,17 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
   out->sub_clusters = c->method == SA_SUBSPACE ? c->clusters : 0;
   for (int k = 0; k < 3; ++k) out->sub_dims[k] = c->method == SA_SUBSPACE ? c->sub_dims[k] : 0;
   if (c->method == SA_KMEANS) {
-    if (c->init == SA_INIT_FIRST) e = kmeans_seed(x, dt, d, 0, d, H, N, C, out->centroids, st);
     const bool fused = kmeans_step_supported(dt, x, d, 0, d, C);
+    // the fused step seeds inside its first set-up
+    const bool seed = c->init == SA_INIT_FIRST;
+    if (seed && !fused) e = kmeans_seed(x, dt, d, 0, d, H, N, C, out->centroids, st);
     for (int it = 0; it < c->iters && e == hipSuccess; ++it) {
       Arena tmp = s;
       if (fused) {
         // the last step also sorts the labels and permutes the rows
         float* ksc = (float*)tmp.take(kmeans_step_scratch(H, N, C, d));
         const StepSort so{out->perm, out->offsets, out->x_perm};
-        e = kmeans_step(x, d, 0, d, H, N, C, out->centroids, out->labels, ksc, it == 0,
+        e = kmeans_step(x, d, 0, d, H, N, C, out->centroids, out->labels, ksc, it == 0, it == 0 && seed,
                         it + 1 == c->iters ? &so : nullptr, st);
         if (e == hipSuccess && it + 1 == c->iters) return hip_status(e);
         continue;
@@ -307,12 +309,13 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
       const int ds = c->sub_dims[k];
       float* cs = sub_c + coff;
       int32_t* lab = sub_labels + size_t(k) * H * N;
-      if (c->init == SA_INIT_FIRST) e = kmeans_seed(x, dt, d, col0, ds, H, N, Cs, cs, st);
       const bool fused = kmeans_step_supported(dt, x, d, col0, ds, Cs);
+      const bool seed = c->init == SA_INIT_FIRST;
+      if (seed && !fused) e = kmeans_seed(x, dt, d, col0, ds, H, N, Cs, cs, st);
       for (int it = 0; it < c->iters && e == hipSuccess; ++it) {
         Arena t2 = tmp;
         if (fused) {
-          e = kmeans_step(x, d, col0, ds, H, N, Cs, cs, lab, msc, it == 0, nullptr, st);
+          e = kmeans_step(x, d, col0, ds, H, N, Cs, cs, lab, msc, it == 0, it == 0 && seed, nullptr, st);
           continue;
         }
         e = kmeans_assign(x, dt, d, col0, ds, H, N, Cs, cs, lab, st);

@@ -126,8 +126,10 @@ struct StepSort {
 };
 bool kmeans_step_supported(int dtype, const void* x, int d, int col0, int dc, int C);
 size_t kmeans_step_scratch(int H, int N, int C, int dc);
+// `seed` (with `first`): first-k seeding of c from x inside the step's set-up.
 hipError_t kmeans_step(const void* x, int d, int col0, int dc, int H, int N, int C, float* c,
-                       int32_t* labels, float* scratch, bool first, const StepSort* sort, hipStream_t st);
+                       int32_t* labels, float* scratch, bool first, bool seed, const StepSort* sort,
+                       hipStream_t st);
 // labels = (a_t*Cs + a_h)*Cs + a_w
 hipError_t combo_labels(const int32_t* sub_labels, int32_t* labels, int H, int N, int Cs,
                         hipStream_t st);
