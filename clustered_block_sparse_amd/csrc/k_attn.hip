@@ -28,8 +28,9 @@
 // every lane owns one query column and keeps the online-softmax state in
 // registers; P stays in registers and feeds O^T = V^T P^T directly, whose V^T
 // operand comes from row-major V tiles by the LDS transpose read.  Rescaling
-// is lazy (only when the running max grows by more than 2^8).  kbar enters the compensation logits as a bf16
-// hi + lo pair so those logits are fp32-accurate.
+// is lazy (only when the running max grows by more than 2^8).  The cluster
+// means enter the compensation as bf16 rows, 64 clusters to a tile, through
+// the same pipeline.
 // fp32 path: one thread per query row, fp32 FMA (parity-grade, small inputs).
 
 #include <math.h>
@@ -61,8 +62,7 @@ struct Prep {
   int2* ranges;       // [H][Cq][Rmax] {start, end}
   int32_t* rcount;    // [H][Cq]
   int32_t* raligned;  // [H][Cq] 1 if every range starts at a multiple of 64 and ends at one or at N
-  bf16_t* kbh;        // [H][Ckp][D]  kbar, bf16 high part
-  bf16_t* kbl;        // [H][Ckp][D]  kbar - high, bf16
+  bf16_t* kbh;        // [H][Ckp][D]  kbar, bf16
   bf16_t* vbr;        // [H][Ckp][D]  vbar, bf16
   float* logsz;       // [H][Ckp]  ln|K_j| or -inf for empty
   float* kbf;         // fp32 path: [H][Ckp][D]
@@ -197,7 +197,7 @@ __device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* p) {
 __global__ __launch_bounds__(128) void comp_prep_kernel(const float* __restrict__ kbar,
                                                         const float* __restrict__ vbar,
                                                         const int32_t* __restrict__ k_off, int Ck,
-                                                        int Ckp, int D, bf16_t* kbh, bf16_t* kbl,
+                                                        int Ckp, int D, bf16_t* kbh,
                                                         bf16_t* vbr, float* kbf, float* vbf,
                                                         float* logsz) {
   const int j = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
@@ -209,9 +209,7 @@ __global__ __launch_bounds__(128) void comp_prep_kernel(const float* __restrict_
     const float kv = (in && sz > 0) ? kbar[(size_t(h) * Ck + j) * D + c] : 0.f;
     const float vv = (in && sz > 0) ? vbar[(size_t(h) * Ck + j) * D + c] : 0.f;
     if (kbh) {
-      const bf16_t hi = f2bf(kv);
-      kbh[o + c] = hi;
-      kbl[o + c] = f2bf(kv - bf2f(hi));
+      kbh[o + c] = f2bf(kv);
       vbr[o + c] = f2bf(vv);
     }
     if (kbf) {
@@ -489,7 +487,7 @@ struct MfmaLds {
   int wsum[16];
   int fsh[2];
   int rowidx[3][KT];  // general path: key row of each position of tile t in [t % 3]
-  float cbias[3][HK];  // compensation: log2-domain bias of the pseudo keys of half j in [j % 3]
+  float cbias[3][KT];  // compensation: score bias of the n-th live tile of cluster means in [n % 3]
 };
 
 // ALIGNED: rows whose ranges are 64-aligned stream whole 64-key blocks (K and
@@ -966,67 +964,145 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     }
   }
 
-  // ---------------- compensation pseudo keys ----------------
+  // ---------------- compensation: tiles of cluster means ----------------
+  // Each 64 consecutive key clusters form one tile of pseudo keys (their
+  // means kbar, vbar as bf16 rows), run through the same pipeline as the
+  // selected tiles.  Pseudo key j carries the score bias ln|K_j| / scale, so
+  // that the log2-domain logit is <q, kbar_j> scale log2(e) + ln|K_j| log2(e);
+  // the bias is -inf where the row selected cluster j or the cluster is
+  // empty.  Tiles without a live pseudo key are skipped: the barrier before
+  // each tile's loads also reports whether any of its 64 biases is finite.
   if (a.compensate) {
     const uint32_t* mr = a.mask + (size_t(h) * a.Cq + i) * p.W;
     const bf16_t* kbh = p.kbh + size_t(h) * p.Ckp * D;
-    const bf16_t* kbl = p.kbl + size_t(h) * p.Ckp * D;
     const bf16_t* vbr = p.vbr + size_t(h) * p.Ckp * D;
-    // Pseudo keys in 32-key halves, pipelined: half j + 1 arrives by direct
-    // loads while half j is computed.  Stage j & 1 holds K̄ hi in rows 0..31
-    // and K̄ lo in rows 32..63 of its K buffer, and V̄ in its lower V half.
-    // The biases of half j (-inf where selected or empty) sit in slot j % 3:
-    // written before the barrier that precedes the half's loads, read after
-    // the next one.  A half with no live pseudo key is neither loaded nor
-    // computed.
     const int cbytes = p.Ckp * D * 2;
-    const int nh = p.Ckp / HK;
-    auto comp_bias = [&](int j) -> int {
+    const int nct = p.Ckp / KT;
+    const float isc = LOG2E / sl2;  // 1 / scale
+    // a query with no finite score so far: a finite running maximum far
+    // below any logit keeps a dead half from forming inf - inf (the first
+    // live half rescales the empty sums by 0)
+    if (m == -__builtin_huge_valf()) m = -1e30f;
+    uint32_t ckoff[CK], cvoff[CH];
+#pragma unroll
+    for (int q = 0; q < CK; ++q) {
+      const int sl = (4 * q + w) * 64 + lane;
+      const int r = sl / DG, kc = (sl % DG) ^ swz<DG>(r);
+      ckoff[q] = uint32_t(r * D + kc * 8) * 2;
+    }
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const int sl = (4 * q + w) * 64 + lane;
+      const int r = sl / DG, c = (sl % DG) ^ vswz<DG>(r);
+      cvoff[q] = uint32_t(r * D + c * 8) * 2;
+    }
+    auto issue_ck = [&](bf16_t* Kd, int t) {
+      const uint32_t b = uint32_t(t * KT) * (D * 2);
+#pragma unroll
+      for (int q = 0; q < CK; ++q) buf_load_lds16(kbh, cbytes, Kd + (4 * q + w) * 512, b + ckoff[q]);
+    };
+    auto issue_cv = [&](bf16_t* Vd, int t, int kt) {
+      const uint32_t b = uint32_t(t * KT + HK * kt) * (D * 2);
+#pragma unroll
+      for (int q = 0; q < CH; ++q) buf_load_lds16(vbr, cbytes, Vd + (4 * q + w) * 512, b + cvoff[q]);
+    };
+    // the biases of tile t into slot sl; 1 if one of them is finite
+    auto comp_bias = [&](int t, int sl) -> int {
       int fin = 0;
-      if (tid < HK) {
-        const int jj = j * HK + tid;
+      if (tid < KT) {
+        const int jj = t * KT + tid;
         float b = -__builtin_huge_valf();
         if (jj < a.Ck && !((mr[jj >> 5] >> (jj & 31)) & 1u)) b = p.logsz[size_t(h) * p.Ckp + jj];
-        S.cbias[j % 3][tid] = b * LOG2E;
         fin = b != -__builtin_huge_valf();
+        S.cbias[sl][tid] = b * isc;
       }
       return fin;
     };
-    auto issue_comp = [&](int j) {
-      bf16_t* Kd = (j & 1) ? K1 : K0;
-      bf16_t* Vd = (j & 1) ? VL1 : VL0;
-      const uint32_t rb = uint32_t(j * HK) * (D * 2);
+    // Waits for this wave's loads, then takes the barrier that precedes the
+    // next loads; it also finds the first live tile from t on (nct if none),
+    // whose biases are then in slot sl.  A slot is written before that
+    // barrier and read after the next one, so three slots rotate.
+    auto next_live = [&](int t, int sl) -> int {
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+      while (!__syncthreads_or(t < nct ? comp_bias(t, sl) : 1)) ++t;
+      return t;
+    };
+    // the scores of a half start from its biases: the MFMAs accumulate onto them
+    auto bias16 = [&](floatx16& sc, const float* cb) {
 #pragma unroll
-      for (int q = 0; q < CH; ++q) {
-        const int sl = (4 * q + w) * 64 + lane;
-        const int r = sl / DG, c = sl % DG;
-        buf_load_lds16(kbh, cbytes, Kd + (4 * q + w) * 512, rb + uint32_t(r * D + ((c ^ swz<DG>(r)) << 3)) * 2);
-        buf_load_lds16(kbl, cbytes, Kd + HK * D + (4 * q + w) * 512,
-                       rb + uint32_t(r * D + ((c ^ swz<DG>(HK + r)) << 3)) * 2);
-        buf_load_lds16(vbr, cbytes, Vd + (4 * q + w) * 512, rb + uint32_t(r * D + ((c ^ vswz<DG>(r)) << 3)) * 2);
+      for (int g = 0; g < 4; ++g) {
+        const float4 bv = *reinterpret_cast<const float4*>(cb + 8 * g + 4 * hi);
+        sc[4 * g] = bv.x;
+        sc[4 * g + 1] = bv.y;
+        sc[4 * g + 2] = bv.z;
+        sc[4 * g + 3] = bv.w;
       }
     };
-    int live = __syncthreads_or(comp_bias(0));  // also: every buffer is free
-    if (live) issue_comp(0);
-    for (int j = 0; j < nh; ++j) {
-      const int fin = j + 1 < nh ? comp_bias(j + 1) : 0;
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of half j
-      const int live_next = __syncthreads_or(fin);
-      if (live_next) issue_comp(j + 1);
-      if (live) {
-        const bf16_t* Kc = (j & 1) ? K1 : K0;
-        floatx16 sc;
-        zero16(sc);
-        qk_half(sc, Kc, 0);  // q . kbar hi
-        qk_half(sc, Kc, 1);  // + q . kbar lo
-        const float* cb = S.cbias[j % 3];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[r] = sc[r] * sl2 + cb[8 * (r >> 2) + 4 * hi + (r & 3)];
-        rescale_to(max_half(sc, 1.f));
-        exp_half(sc, 1.f, pk);
-        pv_half(pk, (j & 1) ? VL1 : VL0);
+    // the selected pipeline's tile step, scores starting from the biases
+    auto ctile = [&](const bf16_t* Kc, const bf16_t* VLc, const bf16_t* VHp, const float* cb) {
+      bias16(s0, cb);
+      qk_half(s0, Kc, 0);
+      exp_half(s1, sl2, pk);
+      pv_half(pk, VHp);
+      rescale_to(max_half(s0, sl2));
+      bias16(s1, cb + HK);
+      qk_half(s1, Kc, 1);
+      exp_half(s0, sl2, pk);
+      pv_half(pk, VLc);
+      rescale_to(max_half(s1, sl2));
+    };
+    auto cfirst = [&](const bf16_t* Kc, const bf16_t* VLc, const float* cb) {
+      bias16(s0, cb);
+      qk_half(s0, Kc, 0);
+      rescale_to(max_half(s0, sl2));
+      bias16(s1, cb + HK);
+      qk_half(s1, Kc, 1);
+      exp_half(s0, sl2, pk);
+      pv_half(pk, VLc);
+      rescale_to(max_half(s1, sl2));
+    };
+    // the first barrier also ends every wave's reads of the selected tiles
+    int tc = next_live(0, 0);
+    if (tc < nct) {
+      issue_ck(K0, tc);
+      issue_cv(VL0, tc, 0);
+      int tn = next_live(tc + 1, 1);
+      if (tn < nct) {
+        issue_ck(K1, tn);
+        issue_cv(VL1, tn, 0);
       }
-      live = live_next;
+      issue_cv(VH0, tc, 1);
+      cfirst(K0, VL0, S.cbias[0]);
+      int o = 1;              // live ordinal of tile tn
+      bool last_odd = false;  // parity of the last tile
+      while (tn < nct) {
+        tc = tn;
+        tn = next_live(tc + 1, (o + 1) % 3);
+        if (tn < nct) {
+          issue_ck(K0, tn);
+          issue_cv(VL0, tn, 0);
+        }
+        issue_cv(VH1, tc, 1);
+        ctile(K1, VL1, VH0, S.cbias[o % 3]);
+        ++o;
+        if (tn >= nct) {
+          last_odd = true;
+          break;
+        }
+        tc = tn;
+        tn = next_live(tc + 1, (o + 1) % 3);
+        if (tn < nct) {
+          issue_ck(K1, tn);
+          issue_cv(VL1, tn, 0);
+        }
+        issue_cv(VH0, tc, 1);
+        ctile(K0, VL0, VH1, S.cbias[o % 3]);
+        ++o;
+      }
+      // drain: P V of the last tile's upper half
+      sync_loads();
+      exp_half(s1, sl2, pk);
+      pv_half(pk, last_odd ? VH1 : VH0);
     }
   }
 
@@ -1078,7 +1154,6 @@ Prep carve(const AttnArgs& a, Arena& s) {
     p.logsz = s.get<float>(size_t(a.H) * p.Ckp);
     if (a.dtype == SA_BF16) {
       p.kbh = s.get<bf16_t>(size_t(a.H) * p.Ckp * a.d);
-      p.kbl = s.get<bf16_t>(size_t(a.H) * p.Ckp * a.d);
       p.vbr = s.get<bf16_t>(size_t(a.H) * p.Ckp * a.d);
     } else {
       p.kbf = s.get<float>(size_t(a.H) * p.Ckp * a.d);
@@ -1117,7 +1192,7 @@ hipError_t attn_run(const AttnArgs& a, Arena& s, hipStream_t st) {
   tiles_kernel<<<a.H, 1024, 0, st>>>(a.q_off, a.Cq, a.tile_rows, p.maxT, p.tiles, p.ntiles);
   if (a.compensate)
     comp_prep_kernel<<<dim3(p.Ckp, a.H), 128, 0, st>>>(a.kbar, a.vbar, a.k_off, a.Ck, p.Ckp, a.d,
-                                                       p.kbh, p.kbl, p.vbr, p.kbf, p.vbf, p.logsz);
+                                                       p.kbh, p.vbr, p.kbf, p.vbf, p.logsz);
   const int grid = 8 * a.H * ceil_div(p.maxT, 8);
   const float sl2 = a.scale * LOG2E;
   // the caller's timing events bracket the attention kernels only (prep excluded)

@@ -95,12 +95,13 @@ def test_backward(w):
 
 
 def test_backward_full_size():
-    """The Wan 720p layer (natural Top-p, compensation off) at full size: the
-    oracle recomputes, for sampled key clusters of the first and last head,
-    every query cluster that selected them; dK and dV of the key cluster's
-    rows and dQ of those query clusters' rows are then complete and compared
-    element by element (the same bounds)."""
-    w = replace(wl.WAN, compensate=False)
+    """The Wan 720p layer at full size in the configuration the backward bench
+    times (fixed 10% density, compensation off; natural Top-p is covered by
+    the smaller cases): the oracle recomputes, for sampled key clusters of the
+    first and last head, every query cluster that selected them; dK and dV of
+    the key cluster's rows and dQ of those query clusters' rows are then
+    complete and compared element by element (the same bounds)."""
+    w = replace(wl.WAN.forced_density(0.1), compensate=False)
     say(f"[backward full size] {w.name} H={w.heads} N={w.n} d={w.d} P={w.top_p}")
     q, k, v = wl.make_inputs(w, device=DEV)
     p, qc, kc, sc, ac = api.cfgs(w)
