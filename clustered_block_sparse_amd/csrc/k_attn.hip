@@ -62,6 +62,8 @@ struct Prep {
   int2* ranges;       // [H][Cq][Rmax] {start, end}
   int32_t* rcount;    // [H][Cq]
   int32_t* raligned;  // [H][Cq] 1 if every range starts at a multiple of 64 and ends at one or at N
+  int32_t* korder;    // [H][Ck] key clusters by how many query clusters selected them (most first)
+  int2* krange;       // [H][Ck] key positions {start, end} of those clusters, in the same order
   bf16_t* kbh;        // [H][Ckp][D]  kbar, bf16
   bf16_t* vbr;        // [H][Ckp][D]  vbar, bf16
   float* logsz;       // [H][Ckp]  ln|K_j| or -inf for empty
@@ -73,9 +75,57 @@ struct Prep {
 // --------------------------------------------------------------------------
 // preparation
 // --------------------------------------------------------------------------
+// Walk order of a head's key clusters: by the number of query clusters that
+// selected each (most first, ties by index).  Tiles that run side by side on
+// one XCD then reach their shared key blocks at about the same step, while the
+// XCD's L2 still holds them (in ascending order the positions of a shared
+// cluster drift apart by the clusters only one of the rows selected).  One
+// workgroup per head: selection counts in LDS, each cluster's rank by
+// counting the clusters ahead of it.
+constexpr int RANK_THREADS = 1024;
+__global__ __launch_bounds__(RANK_THREADS) void key_rank_kernel(const uint32_t* __restrict__ mask,
+                                                                const int32_t* __restrict__ k_off, int Cq, int Ck,
+                                                                int W, int32_t* __restrict__ korder,
+                                                                int2* __restrict__ krange) {
+  __shared__ int pop[ALIGNED_MAX_CK];
+  const int h = blockIdx.x, t = threadIdx.x;
+  const uint32_t* mh = mask + size_t(h) * Cq * W;
+  for (int j = t; j < Ck; j += RANK_THREADS) pop[j] = 0;
+  __syncthreads();
+  // coalesced mask words; each set bit adds one to its cluster (integer LDS
+  // atomics: the counts do not depend on their order)
+  for (int e = t; e < Cq * W; e += RANK_THREADS) {
+    const int wc = e % W;
+    uint32_t m = mh[e];
+    if (wc == W - 1 && (Ck & 31)) m &= (1u << (Ck & 31)) - 1u;
+    while (m) {
+      atomicAdd(&pop[wc * 32 + __ffs(m) - 1], 1);
+      m &= m - 1u;
+    }
+  }
+  __syncthreads();
+  for (int j = t; j < Ck; j += RANK_THREADS) {
+    const int pj = pop[j];
+    int r = 0;
+    for (int i = 0; i < Ck; ++i) {
+      const int pi = pop[i];
+      r += (pi > pj || (pi == pj && i < j)) ? 1 : 0;
+    }
+    korder[size_t(h) * Ck + r] = j;
+    krange[size_t(h) * Ck + r] = make_int2(k_off[size_t(h) * (Ck + 1) + j], k_off[size_t(h) * (Ck + 1) + j + 1]);
+  }
+}
+
+// Row i's selected key clusters as ranges of key positions, in the head's
+// walk order (one range per non-empty cluster) when the row selects at most
+// Rmax clusters; otherwise in ascending order with adjacent clusters merged
+// (at most Ck/2 + 1 ranges).  Either way a range ending at N (the only one
+// whose last tile can be partial) comes last.
 __global__ __launch_bounds__(64) void ranges_kernel(const uint32_t* __restrict__ mask,
                                                     const int32_t* __restrict__ k_off, int Cq,
                                                     int Ck, int W, int Rmax, int N,
+                                                    const int32_t* __restrict__ korder,
+                                                    const int2* __restrict__ krange,
                                                     int2* __restrict__ ranges,
                                                     int32_t* __restrict__ rcount,
                                                     int32_t* __restrict__ raligned) {
@@ -83,28 +133,73 @@ __global__ __launch_bounds__(64) void ranges_kernel(const uint32_t* __restrict__
   const uint32_t* mr = mask + (size_t(h) * Cq + i) * W;
   const int32_t* ko = k_off + size_t(h) * (Ck + 1);
   int2* out = ranges + (size_t(h) * Cq + i) * Rmax;
-  int ns = 0, ne = 0;
   bool misaligned = false;
   const uint64_t lt = (uint64_t(1) << lane) - 1;
-  for (int j0 = 0; j0 < Ck; j0 += 64) {
-    const int j = j0 + lane;
-    const bool in = j < Ck;
-    const bool sel = in && ((mr[j >> 5] >> (j & 31)) & 1u);
-    const bool selp = in && j > 0 && ((mr[(j - 1) >> 5] >> ((j - 1) & 31)) & 1u);
-    const bool seln = in && (j + 1 < Ck) && ((mr[(j + 1) >> 5] >> ((j + 1) & 31)) & 1u);
-    const bool st = sel && !selp;
-    const bool en = sel && !seln;
-    const uint64_t bs = __ballot(st), be = __ballot(en);
-    if (st) {
-      out[ns + __popcll(bs & lt)].x = ko[j];
-      misaligned |= (ko[j] & (KT - 1)) != 0;
+  // the row's mask words in registers (word w in lane w % 64 of register
+  // w / 64; Ck <= 4096, so at most two)
+  uint32_t mw0 = 0, mw1 = 0;
+  if (lane < W) mw0 = mr[lane];
+  if (lane + 64 < W) mw1 = mr[lane + 64];
+  const uint32_t tail = (Ck & 31) ? (1u << (Ck & 31)) - 1u : ~0u;
+  if (lane == W - 1) mw0 &= tail;
+  if (lane + 64 == W - 1) mw1 &= tail;
+  int nsel = __popc(mw0) + __popc(mw1);
+  for (int o = 32; o > 0; o >>= 1) nsel += __shfl_xor(nsel, o);
+  int ns = 0;
+  if (nsel <= Rmax && Ck <= 4096) {
+    const int32_t* ord = korder + size_t(h) * Ck;
+    const int2* kr = krange + size_t(h) * Ck;
+    int last_a = -1;  // start of the selected cluster ending at N
+    for (int r0 = 0; r0 < Ck; r0 += 64) {
+      const int r = r0 + lane;
+      int j = 0;
+      int2 ab = make_int2(0, 0);
+      if (r < Ck) {
+        j = ord[r];
+        ab = kr[r];
+      }
+      const int wd = j >> 5;
+      const uint32_t w0 = __shfl(mw0, wd & 63), w1 = __shfl(mw1, wd & 63);  // every lane takes part
+      const uint32_t word = wd < 64 ? w0 : w1;
+      const int a = ab.x, b = ab.y;
+      const bool sel = r < Ck && ((word >> (j & 31)) & 1u);
+      const bool at_end = sel && b > a && b == N;
+      const bool take = sel && b > a && !at_end;
+      const uint64_t bt = __ballot(take), bl = __ballot(at_end);
+      if (take) {
+        out[ns + __popcll(bt & lt)] = make_int2(a, b);
+        misaligned |= (a & (KT - 1)) != 0 || (b & (KT - 1)) != 0;
+      }
+      ns += __popcll(bt);
+      if (bl) last_a = __shfl(a, __ffsll((unsigned long long)bl) - 1);
     }
-    if (en) {
-      out[ne + __popcll(be & lt)].y = ko[j + 1];
-      misaligned |= (ko[j + 1] & (KT - 1)) != 0 && ko[j + 1] != N;
+    if (last_a >= 0) {
+      if (lane == 0) out[ns] = make_int2(last_a, N);
+      misaligned |= lane == 0 && (last_a & (KT - 1)) != 0;
+      ++ns;
     }
-    ns += __popcll(bs);
-    ne += __popcll(be);
+  } else {
+    int ne = 0;
+    for (int j0 = 0; j0 < Ck; j0 += 64) {
+      const int j = j0 + lane;
+      const bool in = j < Ck;
+      const bool sel = in && ((mr[j >> 5] >> (j & 31)) & 1u);
+      const bool selp = in && j > 0 && ((mr[(j - 1) >> 5] >> ((j - 1) & 31)) & 1u);
+      const bool seln = in && (j + 1 < Ck) && ((mr[(j + 1) >> 5] >> ((j + 1) & 31)) & 1u);
+      const bool st = sel && !selp;
+      const bool en = sel && !seln;
+      const uint64_t bs = __ballot(st), be = __ballot(en);
+      if (st) {
+        out[ns + __popcll(bs & lt)].x = ko[j];
+        misaligned |= (ko[j] & (KT - 1)) != 0;
+      }
+      if (en) {
+        out[ne + __popcll(be & lt)].y = ko[j + 1];
+        misaligned |= (ko[j + 1] & (KT - 1)) != 0 && ko[j + 1] != N;
+      }
+      ns += __popcll(bs);
+      ne += __popcll(be);
+    }
   }
   const bool any_mis = __ballot(misaligned) != 0;
   if (lane == 0) {
@@ -704,6 +799,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     // tile base is added per load.
     const bf16_t* vrh = (const bf16_t*)a.v_perm + size_t(h) * N * D;
     int ri = 0, pos = R > 0 ? rg[0].x : 0, rend = R > 0 ? rg[0].y : 0;
+    // the range after the current one, loaded one range ahead
+    int2 rnext = R > 1 ? const_load_int2(rg, 1) : make_int2(0, 0);
     const int kbytes = N * D * 2, vbytes = N * D * 2;
     uint32_t koff[CK], voff[CH];
 #pragma unroll
@@ -753,9 +850,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
       pos += KT;
       if (pos >= rend) {
         if (++ri >= R) return false;
-        const int2 r2 = const_load_int2(rg, ri);
-        pos = r2.x;
-        rend = r2.y;
+        pos = rnext.x;
+        rend = rnext.y;
+        if (ri + 1 < R) rnext = const_load_int2(rg, ri + 1);
       }
       if (rend - pos < KT) {
         have_tail = true;
@@ -1150,6 +1247,8 @@ Prep carve(const AttnArgs& a, Arena& s) {
   p.ranges = p.Rmax ? s.get<int2>(size_t(a.H) * a.Cq * p.Rmax) : nullptr;
   p.rcount = s.get<int32_t>(size_t(a.H) * a.Cq);
   p.raligned = s.get<int32_t>(size_t(a.H) * a.Cq);
+  p.korder = p.Rmax ? s.get<int32_t>(size_t(a.H) * a.Ck) : nullptr;
+  p.krange = p.Rmax ? s.get<int2>(size_t(a.H) * a.Ck) : nullptr;
   if (a.compensate) {
     p.logsz = s.get<float>(size_t(a.H) * p.Ckp);
     if (a.dtype == SA_BF16) {
@@ -1184,9 +1283,11 @@ size_t attn_scratch(int H, int N, int d, int Cq, int Ck, int tile_rows, int comp
 
 hipError_t attn_run(const AttnArgs& a, Arena& s, hipStream_t st) {
   const Prep p = carve(a, s);
-  if (p.Rmax)
-    ranges_kernel<<<dim3(a.Cq, a.H), 64, 0, st>>>(a.mask, a.k_off, a.Cq, a.Ck, p.W, p.Rmax, a.N,
-                                                  p.ranges, p.rcount, p.raligned);
+  if (p.Rmax) {
+    key_rank_kernel<<<a.H, RANK_THREADS, 0, st>>>(a.mask, a.k_off, a.Cq, a.Ck, p.W, p.korder, p.krange);
+    ranges_kernel<<<dim3(a.Cq, a.H), 64, 0, st>>>(a.mask, a.k_off, a.Cq, a.Ck, p.W, p.Rmax, a.N, p.korder,
+                                                  p.krange, p.ranges, p.rcount, p.raligned);
+  }
   else
     fill_zero_kernel<<<ceil_div(a.H * a.Cq, 256), 256, 0, st>>>(p.raligned, a.H * a.Cq);
   tiles_kernel<<<a.H, 1024, 0, st>>>(a.q_off, a.Cq, a.tile_rows, p.maxT, p.tiles, p.ntiles);
