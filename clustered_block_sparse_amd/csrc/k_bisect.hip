@@ -445,6 +445,17 @@ struct Src2 {
   }
 };
 
+// Optional outputs of the subtree phase: every head's rows in cluster order
+// and its leaf (cluster) means, split between two tensors like Src2.
+template <typename T>
+struct LeafOut {
+  T* xp0;
+  T* xp1;
+  float* c0;
+  float* c1;
+  int C;  // leaves per head
+};
+
 // ---------------------------------------------------------------------------
 // top phase kernels (grid.y = heads)
 // ---------------------------------------------------------------------------
@@ -1182,11 +1193,65 @@ __device__ void subtree_select(SubShared<D>& S, int A, int n0) {
   __syncthreads();
 }
 
+// The rows of a root (positions start .. start + n0 - 1, in final order:
+// token tok(r) at position start + r) in cluster order, and its leaves'
+// means, while the rows are still in the caches.  Roots are whole leaves of
+// L positions (the head's last one may be shorter).  Wave w takes leaves w,
+// w + NW, ...; lane (row group rsub, slice sub) sums rows rsub, rsub + RPW,
+// ... of the leaf, then the row groups are added by a fixed butterfly.
+template <typename T, int D, typename Tok>
+__device__ void emit_leaves(const T* __restrict__ xh, Tok tok, const LeafOut<T>& lo, int h0, int h, int N,
+                            int start, int n0, int L) {
+  using G = RowGeo<T, D>;
+  constexpr int NW = SUB_THREADS / 64;
+  constexpr int U = 4;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int sub = lane % G::LPR, rsub = lane / G::LPR;
+  T* xo = (h < h0 ? lo.xp0 + size_t(h) * N * D : lo.xp1 + size_t(h - h0) * N * D) + size_t(start) * D;
+  float* co = (h < h0 ? lo.c0 + size_t(h) * lo.C * D : lo.c1 + size_t(h - h0) * lo.C * D) +
+              size_t(start / L) * D;
+  const int nleaf = ceil_div(n0, L);
+  for (int f = w; f < nleaf; f += NW) {
+    const int r0 = f * L, r1 = min(r0 + L, n0);
+    float acc[G::EPV];
+#pragma unroll
+    for (int e = 0; e < G::EPV; ++e) acc[e] = 0.f;
+    for (int rb = r0 + rsub; rb < r1; rb += U * G::RPW) {
+      uint4 raw[U];
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int r = rb + q * G::RPW;
+        raw[q] = r < r1 ? ld16(xh + size_t(tok(r)) * D + sub * G::EPV) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < U; ++q) {
+        const int r = rb + q * G::RPW;
+        if (r < r1) {
+          *reinterpret_cast<uint4*>(xo + size_t(r) * D + sub * G::EPV) = raw[q];
+          float v[G::EPV];
+          unpack_vec<T, G::EPV>(raw[q], v);
+#pragma unroll
+          for (int e = 0; e < G::EPV; ++e) acc[e] += v[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int o = G::LPR; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < G::EPV; ++e) acc[e] += __shfl_xor(acc[e], o);
+    if (rsub == 0) {
+      const float inv = 1.f / float(r1 - r0);
+#pragma unroll
+      for (int e = 0; e < G::EPV; ++e) co[size_t(f) * D + sub * G::EPV + e] = acc[e] * inv;
+    }
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 4))) void subtree_kernel(Src2<T> x, const int32_t* __restrict__ perm,
                                                               int32_t* out0, int32_t* out1,
                                                               const int4* __restrict__ roots, int N,
-                                                              int L, int iters) {
+                                                              int L, int iters, LeafOut<T> lo) {
   using G = RowGeo<T, D>;
   constexpr int NW = SUB_THREADS / 64;
   constexpr int U = 4;
@@ -1197,11 +1262,13 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
   const int start = root.x, n0 = root.y;
   const int32_t* ph = perm + size_t(h) * N + start;
   int32_t* po = (h < x.h0 ? out0 + size_t(h) * N : out1 + size_t(h - x.h0) * N) + start;
-  if (ceil_div(n0, L) < 2) {  // a leaf already: its order is final
+  const T* __restrict__ xh = x.head(h, N, D);
+  // a leaf already (possibly longer than SUB_N): its order is final
+  if (ceil_div(n0, L) < 2) {
     for (int i = t; i < n0; i += SUB_THREADS) po[i] = ph[i];
+    if (lo.xp0) emit_leaves<T, D>(xh, [&](int r) { return ph[r]; }, lo, x.h0, h, N, start, n0, L);
     return;
   }
-  const T* __restrict__ xh = x.head(h, N, D);
   for (int i = t; i < n0; i += SUB_THREADS) S.pt[i] = ph[i];
   if (t == 0) {
     S.list[0][0] = make_int2(0, n0);
@@ -1490,6 +1557,7 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
   }
   __syncthreads();
   for (int i = t; i < n0; i += SUB_THREADS) po[i] = S.pt[i];
+  if (lo.xp0) emit_leaves<T, D>(xh, [&](int r) { return S.pt[r]; }, lo, x.h0, h, N, start, n0, L);
 }
 
 __global__ void leaf_offsets_kernel(int32_t* off0, int32_t* off1, int h0, int C, int N, int L) {
@@ -1503,8 +1571,10 @@ template <typename T, int D>
 hipError_t run_bisect(const void* x0, const void* x1, int h0, int H, int N, int L, int iters,
                       const TreePlan& P, int4* segs, int4* chunks, const int32_t* kids, int32_t* pa,
                       int32_t* pb,
-                      int32_t* out0, int32_t* out1, TopBufs b, hipStream_t st) {
+                      int32_t* out0, int32_t* out1, void* xp0, void* xp1, float* c0, float* c1, TopBufs b,
+                      hipStream_t st) {
   const Src2<T> x{(const T*)x0, (const T*)x1, h0};
+  const LeafOut<T> lo{(T*)xp0, (T*)xp1, c0, c1, ceil_div(N, L)};
   const size_t sub_lds = sizeof(SubShared<D>);
   if (hipFuncSetAttribute((const void*)subtree_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
                           int(sub_lds)) != hipSuccess)
@@ -1565,7 +1635,7 @@ hipError_t run_bisect(const void* x0, const void* x1, int h0, int H, int N, int 
   }
   const int nroots = P.t.nseg[P.t.nlev];
   subtree_kernel<T, D><<<dim3(nroots, H), SUB_THREADS, sub_lds, st>>>(x, cur, out0, out1,
-                                                                     segs + P.t.sb[P.t.nlev], N, L, iters);
+                                                                     segs + P.t.sb[P.t.nlev], N, L, iters, lo);
   return hipGetLastError();
 }
 
@@ -1599,8 +1669,8 @@ size_t bisect_scratch(int H, int N, int d, int leaf) {
 }
 
 hipError_t bisect_run(const void* x0, const void* x1, int h0, int dtype, int H, int N, int d, int leaf,
-                      int iters, int32_t* perm0, int32_t* perm1, int32_t* off0, int32_t* off1, Arena& s,
-                      hipStream_t st) {
+                      int iters, int32_t* perm0, int32_t* perm1, int32_t* off0, int32_t* off1, void* xp0,
+                      void* xp1, float* cen0, float* cen1, Arena& s, hipStream_t st) {
   const TreePlan P = plan_tree(N, leaf, SUB_N);
   int4* segs = s.get<int4>(size_t(P.total_seg));
   int4* chunks = s.get<int4>(size_t(P.total_chunk + 1));
@@ -1637,13 +1707,17 @@ hipError_t bisect_run(const void* x0, const void* x1, int h0, int dtype, int H, 
   build_tree_kernel<<<1, 1024, 0, st>>>(P.t, N, segs, chunks, kids);
   hipError_t e;
   if (dtype == SA_F32 && d == 64)
-    e = run_bisect<float, 64>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, kids, pa, pb, perm0, perm1, b, st);
+    e = run_bisect<float, 64>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, kids, pa, pb, perm0, perm1, xp0, xp1,
+                                   cen0, cen1, b, st);
   else if (dtype == SA_F32 && d == 128)
-    e = run_bisect<float, 128>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, kids, pa, pb, perm0, perm1, b, st);
+    e = run_bisect<float, 128>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, kids, pa, pb, perm0, perm1, xp0, xp1,
+                                   cen0, cen1, b, st);
   else if (dtype == SA_BF16 && d == 64)
-    e = run_bisect<bf16_t, 64>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, kids, pa, pb, perm0, perm1, b, st);
+    e = run_bisect<bf16_t, 64>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, kids, pa, pb, perm0, perm1, xp0, xp1,
+                                   cen0, cen1, b, st);
   else
-    e = run_bisect<bf16_t, 128>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, kids, pa, pb, perm0, perm1, b, st);
+    e = run_bisect<bf16_t, 128>(x0, x1, h0, H, N, leaf, iters, P, segs, chunks, kids, pa, pb, perm0, perm1, xp0, xp1,
+                                   cen0, cen1, b, st);
   if (e != hipSuccess) return e;
   const int C = ceil_div(N, leaf);
   leaf_offsets_kernel<<<dim3(ceil_div(C + 1, 256), H), 256, 0, st>>>(off0, off1, h0, C, N, leaf);

@@ -214,19 +214,16 @@ sa_status hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP
 // ---------------------------------------------------------------------------
 // component implementations (arguments already validated)
 // ---------------------------------------------------------------------------
-// after the bisection proper: labels, member means and the rows in cluster
-// order (shared by the one- and two-tensor paths)
-sa_status bisect_tail(const sa_problem* p, const sa_cluster_cfg* c, const void* x, sa_clusters* out,
-                      hipStream_t st) {
-  const int H = p->heads, N = p->n, d = p->d, dt = p->dtype;
+// after the bisection proper: labels (the subtree phase has already written
+// the member means and the rows in cluster order)
+sa_status bisect_tail(const sa_problem* p, const sa_cluster_cfg* c, sa_clusters* out, hipStream_t st) {
+  const int H = p->heads, N = p->n;
   const int C = clusters_of(p, c);
   out->num_clusters = C;
   out->method = c->method;
   out->sub_clusters = 0;
   for (int k = 0; k < 3; ++k) out->sub_dims[k] = 0;
-  hipError_t e = labels_from_offsets(out->perm, out->offsets, out->labels, H, N, C, st);
-  if (e == hipSuccess) e = gather_means(x, dt, d, out->perm, out->offsets, H, N, C, out->x_perm, out->centroids, st);
-  return hip_status(e);
+  return hip_status(labels_from_offsets(out->perm, out->offsets, out->labels, H, N, C, st));
 }
 
 sa_status do_cluster_pair(const sa_problem* p, const sa_cluster_cfg* qc, const sa_cluster_cfg* kc,
@@ -235,10 +232,11 @@ sa_status do_cluster_pair(const sa_problem* p, const sa_cluster_cfg* qc, const s
   const int H = p->heads;
   Arena tmp = s;
   const hipError_t e = bisect_run(q, k, H, p->dtype, 2 * H, p->n, p->d, qc->leaf, qc->iters, qo->perm,
-                                  ko->perm, qo->offsets, ko->offsets, tmp, st);
+                                  ko->perm, qo->offsets, ko->offsets, qo->x_perm, ko->x_perm, qo->centroids,
+                                  ko->centroids, tmp, st);
   if (e != hipSuccess) return SA_ERR_HIP;
-  sa_status r = bisect_tail(p, qc, q, qo, st);
-  if (r == SA_OK) r = bisect_tail(p, kc, k, ko, st);
+  sa_status r = bisect_tail(p, qc, qo, st);
+  if (r == SA_OK) r = bisect_tail(p, kc, ko, st);
   return r;
 }
 
@@ -284,8 +282,8 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
   } else if (c->method == SA_BISECT) {
     Arena tmp = s;
     e = bisect_run(x, x, H, dt, H, N, d, c->leaf, c->iters, out->perm, out->perm, out->offsets,
-                   out->offsets, tmp, st);
-    if (e == hipSuccess) return bisect_tail(p, c, x, out, st);
+                   out->offsets, out->x_perm, out->x_perm, out->centroids, out->centroids, tmp, st);
+    if (e == hipSuccess) return bisect_tail(p, c, out, st);
   } else {
     const int Cs = c->clusters;
     Arena tmp = s;

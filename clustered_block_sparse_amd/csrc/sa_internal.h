@@ -144,9 +144,11 @@ hipError_t compact_sub_centroids(const float* expanded, int H, int Cs, int d, co
 size_t bisect_scratch(int H, int N, int d, int leaf);
 // Heads below h0 are rows of x0 (order and leaf offsets to perm0 / off0), the
 // others of x1 (perm1 / off1); H counts both.  One tensor: x1 = x0, h0 = H.
+// With xp0 non-null, the rows in cluster order go to xp0 / xp1 and the leaf
+// means (fp32 [heads][C][d]) to cen0 / cen1 as well.
 hipError_t bisect_run(const void* x0, const void* x1, int h0, int dtype, int H, int N, int d, int leaf,
-                      int iters, int32_t* perm0, int32_t* perm1, int32_t* off0, int32_t* off1, Arena& s,
-                      hipStream_t st);
+                      int iters, int32_t* perm0, int32_t* perm1, int32_t* off0, int32_t* off1, void* xp0,
+                      void* xp1, float* cen0, float* cen1, Arena& s, hipStream_t st);
 
 // k_select.hip ---------------------------------------------------------------
 struct SelectArgs {
