@@ -641,33 +641,47 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const int
 // --------------------------------------------------------------------------
 // key clusters
 // --------------------------------------------------------------------------
-// Logits of a head: 32 x 32 output tiles; each output sums over d in order.
-constexpr int LT = 32;
+// Logits of a head: 64 x 64 output tiles, 4 x 4 outputs per thread (rows
+// ti + 16 r, columns tj + 16 c), so each pair of LDS reads feeds two FMAs;
+// each output sums over d in order, one fp64 FMA per column.
+constexpr int LT = 64;   // output tile edge
+constexpr int LC = 32;   // columns of d staged at a time
 __global__ __launch_bounds__(256) void logits_kernel(SelectArgs a, double* __restrict__ L) {
-  __shared__ double qs[LT][LT + 1], ks[LT][LT + 1];
+  __shared__ double qs[LT][LC + 1], ks[LT][LC + 1];
   const int h = blockIdx.z, i0 = blockIdx.y * LT, j0 = blockIdx.x * LT, t = threadIdx.x;
-  const int ti = t >> 4, tj = t & 15;  // outputs (i0 + ti + 16 r, j0 + tj + 16 c), r, c < 2
-  double acc[2][2] = {{0.0, 0.0}, {0.0, 0.0}};
-  for (int c0 = 0; c0 < a.d; c0 += LT) {
-    for (int e = t; e < LT * LT; e += 256) {
-      const int r = e / LT, c = e % LT;
+  const int ti = t >> 4, tj = t & 15;
+  double acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
+  for (int c0 = 0; c0 < a.d; c0 += LC) {
+    for (int e = t; e < LT * LC; e += 256) {
+      const int r = e / LC, c = e % LC;
       const int qi = i0 + r, kj = j0 + r;
       qs[r][c] = qi < a.Cq ? double(a.qbar[(size_t(h) * a.Cq + qi) * a.d + c0 + c]) : 0.0;
       ks[r][c] = kj < a.Ck ? double(a.kbar[(size_t(h) * a.Ck + kj) * a.d + c0 + c]) : 0.0;
     }
     __syncthreads();
-    for (int c = 0; c < LT; ++c)
+#pragma unroll 4
+    for (int c = 0; c < LC; ++c) {
+      double qv[4], kv[4];
 #pragma unroll
-      for (int r = 0; r < 2; ++r)
+      for (int r = 0; r < 4; ++r) qv[r] = qs[ti + 16 * r][c];
 #pragma unroll
-        for (int cc = 0; cc < 2; ++cc) acc[r][cc] = fma(qs[ti + 16 * r][c], ks[tj + 16 * cc][c], acc[r][cc]);
+      for (int cc = 0; cc < 4; ++cc) kv[cc] = ks[tj + 16 * cc][c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) acc[r][cc] = fma(qv[r], kv[cc], acc[r][cc]);
+    }
     __syncthreads();
   }
   const int32_t* ko = a.k_off + size_t(h) * (a.Ck + 1);
 #pragma unroll
-  for (int r = 0; r < 2; ++r)
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
-    for (int cc = 0; cc < 2; ++cc) {
+    for (int cc = 0; cc < 4; ++cc) {
       const int i = i0 + ti + 16 * r, j = j0 + tj + 16 * cc;
       if (i >= a.Cq || j >= a.Ck) continue;
       const int sz = ko[j + 1] - ko[j];
@@ -1251,7 +1265,7 @@ hipError_t select_run(const SelectArgs& a, Arena& s, hipStream_t st) {
     }
     return hipGetLastError();
   }
-  if (a.Ck > SEL_MAX || a.d % LT) return hipErrorInvalidValue;
+  if (a.Ck > SEL_MAX || a.d % LC) return hipErrorInvalidValue;
   double* L = s.get<double>(size_t(a.H) * a.Cq * a.Ck);
   logits_kernel<<<dim3(ceil_div(a.Ck, LT), ceil_div(a.Cq, LT), a.H), 256, 0, st>>>(a, L);
   int32_t* pool_cnt = nullptr;
