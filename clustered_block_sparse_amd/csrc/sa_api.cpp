@@ -162,9 +162,10 @@ bool paired_bisect(const sa_cluster_cfg* qc, const sa_cluster_cfg* kc) {
 
 // scratch the two-tensor clustering needs (the paired bisection's, or the
 // larger of the two separate ones)
+// Q and K clustered separately run side by side, each in its own part
 size_t cluster_qk_scratch(const sa_problem* p, const sa_cluster_cfg* qc, const sa_cluster_cfg* kc) {
   return paired_bisect(qc, kc) ? bisect_scratch(2 * p->heads, p->n, p->d, qc->leaf) + 256
-                               : std::max(cluster_scratch(p, qc), cluster_scratch(p, kc));
+                               : cluster_scratch(p, qc) + 256 + cluster_scratch(p, kc);
 }
 
 // carve the persistent buffers of sa_forward; null base = size only
@@ -335,12 +336,47 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
   return hip_status(e);
 }
 
+// Q and K clustered separately (different methods or settings) are two chains
+// of mostly short launches: K's runs on a second stream of the device (default
+// priority, created on first use), forked from the caller's stream and joined
+// back to it with events, so the two chains overlap.  The record/wait pairs
+// of one call are made under a lock, so calls on distinct workspaces stay
+// independent.
+constexpr int MAX_DEVICES = 64;
+struct ForkJoin {
+  hipStream_t s2;
+  hipEvent_t fork, join;
+};
+std::mutex g_fork_mu;
+ForkJoin g_fork[MAX_DEVICES];
+
 sa_status do_cluster_qk(const sa_problem* p, const sa_cluster_cfg* qc, const sa_cluster_cfg* kc,
                         const void* q, const void* k, sa_clusters* qo, sa_clusters* ko, Arena& s,
                         hipStream_t st) {
   if (paired_bisect(qc, kc)) return do_cluster_pair(p, qc, kc, q, k, qo, ko, s, st);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return SA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_fork_mu);
+  ForkJoin& f = g_fork[dev];
+  if (!f.s2) {
+    ForkJoin n{};
+    if (hipStreamCreateWithFlags(&n.s2, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess)
+      return SA_ERR_HIP;
+    f = n;
+  }
+  Arena sk = s;  // K's scratch follows Q's
+  sk.take(cluster_scratch(p, qc));
+  if (hipEventRecord(f.fork, st) != hipSuccess || hipStreamWaitEvent(f.s2, f.fork, 0) != hipSuccess)
+    return SA_ERR_HIP;
   sa_status r = do_cluster(p, qc, q, qo, s, st);
-  if (r == SA_OK) r = do_cluster(p, kc, k, ko, s, st);
+  const sa_status rk = do_cluster(p, kc, k, ko, sk, f.s2);
+  // joined whatever happened, so that later work on the caller's stream
+  // follows everything enqueued on the second one
+  const bool joined = hipEventRecord(f.join, f.s2) == hipSuccess && hipStreamWaitEvent(st, f.join, 0) == hipSuccess;
+  if (r == SA_OK) r = rk;
+  if (r == SA_OK && !joined) r = SA_ERR_HIP;
   return r;
 }
 
@@ -420,7 +456,6 @@ sa_status do_attn(const sa_problem* p, const sa_attn_cfg* c, const sa_clusters* 
 constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(SA_NOALLOC_ATTN_SCRATCH_BYTES);
 __device__ __align__(256) char scratch[NOALLOC_SCRATCH_BYTES];
 
-constexpr int MAX_DEVICES = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[MAX_DEVICES];
 

@@ -23,7 +23,14 @@
  *    sa_workspace_size() bytes (256-byte aligned).
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
  *    enqueues kernels on it: no device->host copy, no synchronisation.
- *    Calls on distinct workspaces are reentrant.
+ *    Calls on distinct workspaces are reentrant.  One exception to "only on
+ *    `stream`": when Q and K are clustered with different settings,
+ *    sa_cluster_qk and sa_forward enqueue K's clustering on a second stream
+ *    of the current device (default priority; created with two events by the
+ *    first such call on that device, kept until the process ends), ordered
+ *    after the work already on `stream` and joined back to it by events, so
+ *    everything enqueued on `stream` afterwards follows it.  A graph capture
+ *    of `stream` captures both; make the first such call outside a capture.
  *  - Arguments are validated before anything is enqueued: a call that
  *    returns an error has done no work.  SA_ERR_HIP reports a launch failure
  *    (hipGetLastError after a launch).  No C++ exception crosses the ABI.
@@ -216,7 +223,9 @@ SA_API sa_status sa_cluster(const sa_problem* p, const sa_cluster_cfg* cfg, cons
 /* Cluster Q with qcfg and K with kcfg, exactly as two sa_cluster calls would
  * (bit-identical results), as sa_forward does.  When both use BISECT with
  * the same leaf and iters, the two tensors are bisected together as one
- * problem of 2H heads, so every kernel launch covers both.  Workspace: as
+ * problem of 2H heads, so every kernel launch covers both; otherwise K's
+ * clustering runs beside Q's on the device's second stream (see the stream
+ * convention above), each in its own part of the workspace.  Workspace: as
  * returned by sa_workspace_size with both configurations. */
 SA_API sa_status sa_cluster_qk(const sa_problem* p, const sa_cluster_cfg* qcfg,
                                const sa_cluster_cfg* kcfg, const void* q, const void* k,
