@@ -350,10 +350,10 @@ struct ForkJoin {
 std::mutex g_fork_mu;
 ForkJoin g_fork[MAX_DEVICES];
 
-sa_status do_cluster_qk(const sa_problem* p, const sa_cluster_cfg* qc, const sa_cluster_cfg* kc,
-                        const void* q, const void* k, sa_clusters* qo, sa_clusters* ko, Arena& s,
-                        hipStream_t st) {
-  if (paired_bisect(qc, kc)) return do_cluster_pair(p, qc, kc, q, k, qo, ko, s, st);
+// enqueue a(st) and b(s2) side by side: s2 starts after the work already on
+// st, and st continues after both
+template <typename A, typename B>
+sa_status side_by_side(hipStream_t st, A&& a, B&& b) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return SA_ERR_HIP;
   std::lock_guard<std::mutex> lock(g_fork_mu);
@@ -366,18 +366,27 @@ sa_status do_cluster_qk(const sa_problem* p, const sa_cluster_cfg* qc, const sa_
       return SA_ERR_HIP;
     f = n;
   }
-  Arena sk = s;  // K's scratch follows Q's
-  sk.take(cluster_scratch(p, qc));
   if (hipEventRecord(f.fork, st) != hipSuccess || hipStreamWaitEvent(f.s2, f.fork, 0) != hipSuccess)
     return SA_ERR_HIP;
-  sa_status r = do_cluster(p, qc, q, qo, s, st);
-  const sa_status rk = do_cluster(p, kc, k, ko, sk, f.s2);
+  sa_status r = a(st);
+  const sa_status rb = b(f.s2);
   // joined whatever happened, so that later work on the caller's stream
   // follows everything enqueued on the second one
   const bool joined = hipEventRecord(f.join, f.s2) == hipSuccess && hipStreamWaitEvent(st, f.join, 0) == hipSuccess;
-  if (r == SA_OK) r = rk;
+  if (r == SA_OK) r = rb;
   if (r == SA_OK && !joined) r = SA_ERR_HIP;
   return r;
+}
+
+sa_status do_cluster_qk(const sa_problem* p, const sa_cluster_cfg* qc, const sa_cluster_cfg* kc,
+                        const void* q, const void* k, sa_clusters* qo, sa_clusters* ko, Arena& s,
+                        hipStream_t st) {
+  if (paired_bisect(qc, kc)) return do_cluster_pair(p, qc, kc, q, k, qo, ko, s, st);
+  Arena sk = s;  // K's scratch follows Q's
+  sk.take(cluster_scratch(p, qc));
+  return side_by_side(
+      st, [&](hipStream_t x) { return do_cluster(p, qc, q, qo, s, x); },
+      [&](hipStream_t x) { return do_cluster(p, kc, k, ko, sk, x); });
 }
 
 sa_status do_select(const sa_problem* p, const sa_select_cfg* c, const sa_clusters* q,
