@@ -485,6 +485,12 @@ struct TopBufs {
   uint32_t* keyR;      // [H][N] ... for the predicted right child
   uint32_t* keys_next; // [H][N] children's round-0 keys, in the children's order
   int32_t* pred_ok;    // [H][max_seg] (next level) 1: the child's round-0 keys are in place
+  // A child's total is its side's sum in the parent's final split, so its
+  // first round sums only its right side (never the larger one) and takes
+  // the left as total - right.
+  float* ctot;         // [H][max_seg][D] total of each segment of the level (from its parent)
+  int tot_out;         // the partition writes the children's totals
+  int d;
   int max_seg, max_chunk, N, round;  // round: 0 = first round of a level
   int rev;  // full passes over the rows: walk the blocks in reverse order
 };
@@ -828,7 +834,7 @@ __global__ __launch_bounds__(1024) void pick_kernel(TopBufs b) {
 // scratch.  Otherwise: the tokens whose side changed since the previous round,
 // found with vectorised key/side reads and compacted in position order, give
 // the change of the left sum; only their rows are read.  Sides are updated.
-template <typename T, int D, bool FULL>
+template <typename T, int D, bool FULL, bool RIGHT = false>
 __global__ __launch_bounds__(256) void sums_kernel(Src2<T> x, TopBufs b) {
   using G = RowGeo<T, D>;
   constexpr int U = FULL ? 8 : 4;
@@ -894,7 +900,7 @@ __global__ __launch_bounds__(256) void sums_kernel(Src2<T> x, TopBufs b) {
     cnt = tot;
     __syncthreads();
   }
-  if constexpr (FULL) {
+  if constexpr (FULL && !RIGHT) {
     // the chunk's rows and sides, staged (sides are written here)
     for (int i = t; i < ch.z; i += 256) {
       const int p = ch.y + i;
@@ -902,6 +908,33 @@ __global__ __launch_bounds__(256) void sums_kernel(Src2<T> x, TopBufs b) {
       list[i] = left ? ph[p] : ~ph[p];
       sd[p] = left ? 1 : 0;
     }
+    __syncthreads();
+  }
+  if constexpr (FULL && RIGHT) {
+    // sides written for every row; only the right side's rows are listed
+    // (in position order), the left side's sum follows from the total
+    const int i0 = 4 * t;
+    int nr = 0, tok[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      tok[q] = -1;
+      const int i = i0 + q;
+      if (i < ch.z) {
+        const int p = ch.y + i;
+        const bool left = is_left(kh[p], p, th);
+        sd[p] = left ? 1 : 0;
+        if (!left) {
+          tok[q] = ph[p];
+          ++nr;
+        }
+      }
+    }
+    int tot;
+    int pre = block_excl_scan<int>(nr, wsum, tot);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (tok[q] >= 0) list[pre++] = ~tok[q];
+    cnt = tot;
     __syncthreads();
   }
   float s0[G::EPV], s1[G::EPV];  // FULL: left, right.  Otherwise: change of left
@@ -968,13 +1001,27 @@ __global__ __launch_bounds__(256) void sums_kernel(Src2<T> x, TopBufs b) {
 }
 
 // Per segment: partials in chunk order -> sums and means of the two sides.
-template <int D, bool FULL>
+template <int D, bool FULL, bool RIGHT = false>
 __global__ __launch_bounds__(256) void update_kernel(TopBufs b) {
   const int h = blockIdx.y, t = threadIdx.x;
   const int4 sg = b.segs[blockIdx.x];
   if (sg.z == 0) return;
   const int nch = ceil_div(sg.y, BCH);
   const size_t so = (size_t(h) * b.max_seg + blockIdx.x) * 2 * D;
+  if constexpr (RIGHT) {
+    // right side from the partials in chunk order, left = total - right
+    const float* tt = b.ctot + (size_t(h) * b.max_seg + blockIdx.x) * D;
+    for (int c = t; c < D; c += 256) {
+      float r = 0.f;
+      for (int q = 0; q < nch; ++q) r += b.part[(size_t(h) * b.max_chunk + sg.w + q) * 2 * D + D + c];
+      const float l = tt[c] - r;
+      b.ssum[so + c] = l;
+      b.ssum[so + D + c] = r;
+      b.cen[so + c] = l / float(sg.z);
+      b.cen[so + D + c] = r / float(sg.y - sg.z);
+    }
+    return;
+  }
   for (int i = t; i < 2 * D; i += 256) {
     const int sdx = i / D, c = i % D;
     const int src = FULL ? i : c;
@@ -1078,6 +1125,13 @@ __global__ __launch_bounds__(1024) void partition_kernel(TopBufs b, const int32_
       if (okl) b.segmm[ko] = make_uint2(cmm[0][0], cmm[0][1]);
       if (okr) b.segmm[ko + 1] = make_uint2(cmm[1][0], cmm[1][1]);
     }
+  }
+  if (b.tot_out) {
+    // the final split's side sums are the children's totals (children kid and
+    // kid + 1 are adjacent, as the two sides are in ssum)
+    const float* ss = b.ssum + si * 2 * b.d;
+    float* ct = b.ctot + (size_t(h) * b.max_seg + b.kids[blockIdx.x]) * b.d;
+    for (int i = t; i < 2 * b.d; i += 1024) ct[i] = ss[i];
   }
 }
 
@@ -1582,6 +1636,9 @@ hipError_t run_bisect(const void* x0, const void* x1, int h0, int H, int N, int 
   int32_t* cur = pa;
   int32_t* nxt = pb;
   bool predicted = false;  // this level's first-round keys were formed by its parent
+  // children start from their parent's final side sums (needs a previous
+  // round to find the last round's switchers)
+  const bool totals = iters >= 2;
   int dir = 0;             // direction of the next full pass over the rows
   for (int lv = 0; lv < P.t.nlev; ++lv) {
     b.segs = segs + P.t.sb[lv];
@@ -1610,16 +1667,29 @@ hipError_t run_bisect(const void* x0, const void* x1, int h0, int H, int N, int 
         if (it == 0) {
           b.rev = dir;
           dir ^= 1;
-          sums_kernel<T, D, true><<<gc, 256, 0, st>>>(x, b);
-          b.rev = 0;
-          update_kernel<D, true><<<gs, 256, 0, st>>>(b);
+          if (lv > 0 && totals) {
+            sums_kernel<T, D, true, true><<<gc, 256, 0, st>>>(x, b);
+            b.rev = 0;
+            update_kernel<D, true, true><<<gs, 256, 0, st>>>(b);
+          } else {
+            sums_kernel<T, D, true><<<gc, 256, 0, st>>>(x, b);
+            b.rev = 0;
+            update_kernel<D, true><<<gs, 256, 0, st>>>(b);
+          }
         } else {
           b.rev = 0;
           sums_kernel<T, D, false><<<gc, 256, 0, st>>>(x, b);
           update_kernel<D, false><<<gs, 256, 0, st>>>(b);
         }
+      } else if (totals && lv + 1 < P.t.nlev) {
+        // the final split's side sums (the tokens that switched in the last
+        // round), which the partition hands to the children as their totals
+        b.rev = 0;
+        sums_kernel<T, D, false><<<gc, 256, 0, st>>>(x, b);
+        update_kernel<D, false><<<gs, 256, 0, st>>>(b);
       }
     }
+    b.tot_out = totals && lv + 1 < P.t.nlev;
     if (predict) {
       partition_kernel<true><<<gs, 1024, 0, st>>>(b, cur, nxt);
       uint32_t* k = b.keys;  // the children's keys become the next level's
@@ -1665,6 +1735,7 @@ size_t bisect_scratch(int H, int N, int d, int leaf) {
   a.get<uint32_t>(size_t(H) * N);       // keyR
   a.get<uint32_t>(size_t(H) * N);       // keys_next
   a.get<int32_t>(size_t(H) * P.max_seg);  // pred_ok
+  a.get<float>(size_t(H) * P.max_seg * d);  // ctot
   return a.used;
 }
 
@@ -1694,6 +1765,8 @@ hipError_t bisect_run(const void* x0, const void* x1, int h0, int dtype, int H, 
   b.keyR = s.get<uint32_t>(size_t(H) * N);
   b.keys_next = s.get<uint32_t>(size_t(H) * N);
   b.pred_ok = s.get<int32_t>(size_t(H) * P.max_seg);
+  b.ctot = s.get<float>(size_t(H) * P.max_seg * d);
+  b.d = d;
   b.max_seg = P.max_seg;
   b.max_chunk = P.max_chunk;
   b.N = N;
