@@ -539,7 +539,7 @@ __global__ __launch_bounds__(64) void firsts_kernel(TopBufs b) {
 template <typename T, int D, bool PRED>
 __global__ __launch_bounds__(256) void delta_kernel(Src2<T> x, TopBufs b, int first, int use_ok) {
   using G = RowGeo<T, D>;
-  constexpr int U = PRED ? 16 : 8;  // wave steps in flight
+  constexpr int U = PRED ? 4 : 8;  // wave steps in flight (three dot products per row in PRED)
   __shared__ float wv[D], mv[D];
   __shared__ float wvc[PRED ? 2 : 1][D], mvc[PRED ? 2 : 1][D];  // children (left, right)
   __shared__ int pidx[BCH / DELTA_SPLIT];  // the part's rows (original tokens)
