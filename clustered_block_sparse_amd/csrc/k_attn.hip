@@ -427,7 +427,8 @@ __global__ __launch_bounds__(128) void attn_simple(AttnArgs a, Prep p, float sca
   const int t = threadIdx.x;
   const int N = a.N;
   const bool qv = t < nr;
-  const T* qp = (const T*)a.q_perm + (size_t(h) * N + p0 + (qv ? t : 0)) * D;
+  const T* qp = a.q_src ? (const T*)a.q_src + (size_t(h) * N + a.q_idx[size_t(h) * N + p0 + (qv ? t : 0)]) * D
+                        : (const T*)a.q_perm + (size_t(h) * N + p0 + (qv ? t : 0)) * D;
   float q[D], o[D];
 #pragma unroll
   for (int c = 0; c < D; ++c) {
@@ -618,7 +619,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
   // Q fragments (B operand of S^T = K Q^T): query 32w+col, d = 16s + 8hi + e
   const int qr = 32 * w + col;
   const bool qv = qr < nr;
-  const bf16_t* qrow = (const bf16_t*)a.q_perm + (size_t(h) * N + p0 + (qv ? qr : 0)) * D;
+  // query rows from the cluster-order copy, or from the original order
+  // through the cluster permutation
+  const bf16_t* qrow =
+      a.q_src ? (const bf16_t*)a.q_src + (size_t(h) * N + a.q_idx[size_t(h) * N + p0 + (qv ? qr : 0)]) * D
+              : (const bf16_t*)a.q_perm + (size_t(h) * N + p0 + (qv ? qr : 0)) * D;
   bf16x8_t qf[DS];
 #pragma unroll
   for (int s = 0; s < DS; ++s) {

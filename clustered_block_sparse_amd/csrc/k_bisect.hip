@@ -1261,7 +1261,8 @@ __device__ void emit_leaves(const T* __restrict__ xh, Tok tok, const LeafOut<T>&
   constexpr int U = 4;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const int sub = lane % G::LPR, rsub = lane / G::LPR;
-  T* xo = (h < h0 ? lo.xp0 + size_t(h) * N * D : lo.xp1 + size_t(h - h0) * N * D) + size_t(start) * D;
+  T* xb = h < h0 ? lo.xp0 : lo.xp1;  // null: this tensor's rows are not wanted, only its means
+  T* xo = xb ? xb + (size_t(h < h0 ? h : h - h0) * N + start) * D : nullptr;
   float* co = (h < h0 ? lo.c0 + size_t(h) * lo.C * D : lo.c1 + size_t(h - h0) * lo.C * D) +
               size_t(start / L) * D;
   const int nleaf = ceil_div(n0, L);
@@ -1281,7 +1282,7 @@ __device__ void emit_leaves(const T* __restrict__ xh, Tok tok, const LeafOut<T>&
       for (int q = 0; q < U; ++q) {
         const int r = rb + q * G::RPW;
         if (r < r1) {
-          *reinterpret_cast<uint4*>(xo + size_t(r) * D + sub * G::EPV) = raw[q];
+          if (xo) *reinterpret_cast<uint4*>(xo + size_t(r) * D + sub * G::EPV) = raw[q];
           float v[G::EPV];
           unpack_vec<T, G::EPV>(raw[q], v);
 #pragma unroll
@@ -1320,7 +1321,7 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
   // a leaf already (possibly longer than SUB_N): its order is final
   if (ceil_div(n0, L) < 2) {
     for (int i = t; i < n0; i += SUB_THREADS) po[i] = ph[i];
-    if (lo.xp0) emit_leaves<T, D>(xh, [&](int r) { return ph[r]; }, lo, x.h0, h, N, start, n0, L);
+    if (lo.c0) emit_leaves<T, D>(xh, [&](int r) { return ph[r]; }, lo, x.h0, h, N, start, n0, L);
     return;
   }
   for (int i = t; i < n0; i += SUB_THREADS) S.pt[i] = ph[i];
@@ -1611,7 +1612,7 @@ __global__ __launch_bounds__(SUB_THREADS) __attribute__((amdgpu_waves_per_eu(4, 
   }
   __syncthreads();
   for (int i = t; i < n0; i += SUB_THREADS) po[i] = S.pt[i];
-  if (lo.xp0) emit_leaves<T, D>(xh, [&](int r) { return S.pt[r]; }, lo, x.h0, h, N, start, n0, L);
+  if (lo.c0) emit_leaves<T, D>(xh, [&](int r) { return S.pt[r]; }, lo, x.h0, h, N, start, n0, L);
 }
 
 __global__ void leaf_offsets_kernel(int32_t* off0, int32_t* off1, int h0, int C, int N, int L) {

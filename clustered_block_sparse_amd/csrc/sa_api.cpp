@@ -227,22 +227,25 @@ sa_status bisect_tail(const sa_problem* p, const sa_cluster_cfg* c, sa_clusters*
   return hip_status(labels_from_offsets(out->perm, out->offsets, out->labels, H, N, C, st));
 }
 
+// q_rows false: Q's rows in cluster order are not written (sa_forward's
+// attention reads Q through the permutation); its means are.
 sa_status do_cluster_pair(const sa_problem* p, const sa_cluster_cfg* qc, const sa_cluster_cfg* kc,
                           const void* q, const void* k, sa_clusters* qo, sa_clusters* ko, Arena& s,
-                          hipStream_t st) {
+                          hipStream_t st, bool q_rows = true) {
   const int H = p->heads;
   Arena tmp = s;
   const hipError_t e = bisect_run(q, k, H, p->dtype, 2 * H, p->n, p->d, qc->leaf, qc->iters, qo->perm,
-                                  ko->perm, qo->offsets, ko->offsets, qo->x_perm, ko->x_perm, qo->centroids,
-                                  ko->centroids, tmp, st);
+                                  ko->perm, qo->offsets, ko->offsets, q_rows ? qo->x_perm : nullptr, ko->x_perm,
+                                  qo->centroids, ko->centroids, tmp, st);
   if (e != hipSuccess) return SA_ERR_HIP;
   sa_status r = bisect_tail(p, qc, qo, st);
   if (r == SA_OK) r = bisect_tail(p, kc, ko, st);
   return r;
 }
 
+// rows false: a bisection writes the means but not the rows in cluster order
 sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x, sa_clusters* out,
-                     Arena& s, hipStream_t st) {
+                     Arena& s, hipStream_t st, bool rows = true) {
   const int H = p->heads, N = p->n, d = p->d, dt = p->dtype;
   const int C = clusters_of(p, c);
   hipError_t e = hipSuccess;
@@ -282,8 +285,9 @@ sa_status do_cluster(const sa_problem* p, const sa_cluster_cfg* c, const void* x
     return hip_status(e);
   } else if (c->method == SA_BISECT) {
     Arena tmp = s;
+    void* xp = rows ? out->x_perm : nullptr;
     e = bisect_run(x, x, H, dt, H, N, d, c->leaf, c->iters, out->perm, out->perm, out->offsets,
-                   out->offsets, out->x_perm, out->x_perm, out->centroids, out->centroids, tmp, st);
+                   out->offsets, xp, xp, out->centroids, out->centroids, tmp, st);
     if (e == hipSuccess) return bisect_tail(p, c, out, st);
   } else {
     const int Cs = c->clusters;
@@ -380,12 +384,12 @@ sa_status side_by_side(hipStream_t st, A&& a, B&& b) {
 
 sa_status do_cluster_qk(const sa_problem* p, const sa_cluster_cfg* qc, const sa_cluster_cfg* kc,
                         const void* q, const void* k, sa_clusters* qo, sa_clusters* ko, Arena& s,
-                        hipStream_t st) {
-  if (paired_bisect(qc, kc)) return do_cluster_pair(p, qc, kc, q, k, qo, ko, s, st);
+                        hipStream_t st, bool q_rows = true) {
+  if (paired_bisect(qc, kc)) return do_cluster_pair(p, qc, kc, q, k, qo, ko, s, st, q_rows);
   Arena sk = s;  // K's scratch follows Q's
   sk.take(cluster_scratch(p, qc));
   return side_by_side(
-      st, [&](hipStream_t x) { return do_cluster(p, qc, q, qo, s, x); },
+      st, [&](hipStream_t x) { return do_cluster(p, qc, q, qo, s, x, q_rows); },
       [&](hipStream_t x) { return do_cluster(p, kc, k, ko, sk, x); });
 }
 
@@ -426,7 +430,8 @@ sa_status do_select(const sa_problem* p, const sa_select_cfg* c, const sa_cluste
 
 sa_status do_attn(const sa_problem* p, const sa_attn_cfg* c, const sa_clusters* q,
                   const sa_clusters* k, const void* v_perm, const float* v_means,
-                  const uint32_t* mask, void* o, int rows, int maxt, Arena& s, hipStream_t st) {
+                  const uint32_t* mask, void* o, int rows, int maxt, Arena& s, hipStream_t st,
+                  const void* q_src = nullptr) {
   AttnArgs a{};
   a.H = p->heads;
   a.N = p->n;
@@ -439,6 +444,7 @@ sa_status do_attn(const sa_problem* p, const sa_attn_cfg* c, const sa_clusters* 
   a.compensate = c->compensate != 0;
   a.scale = c->scale > 0.f ? c->scale : float(1.0 / sqrt(double(p->d)));
   a.q_perm = q->x_perm;
+  a.q_src = q_src;  // set: query rows from the original order through q_idx
   a.q_idx = q->perm;
   a.q_off = q->offsets;
   a.k_perm = k->x_perm;
@@ -694,7 +700,9 @@ SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
   FwdBufs b = carve_forward(p, qcfg, kcfg, scfg, acfg, (char*)ws, &used);
   hipStream_t s = (hipStream_t)stream;
   Arena scr{b.scratch, b.scratch_bytes, 0};
-  if ((st = do_cluster_qk(p, qcfg, kcfg, q, k, &b.q, &b.k, scr, s)) != SA_OK) return st;
+  // the attention reads Q through the query-cluster permutation, so no
+  // cluster-order copy of Q is written (a bisection skips it)
+  if ((st = do_cluster_qk(p, qcfg, kcfg, q, k, &b.q, &b.k, scr, s, false)) != SA_OK) return st;
   const hipError_t e = b.v_means ? gather_means(v, p->dtype, p->d, b.k.perm, b.k.offsets, p->heads, p->n,
                                                 b.k.num_clusters, b.v_perm, b.v_means, s)
                                  : gather_rows(v, b.v_perm, b.k.perm, p->heads, p->n, p->d, p->dtype, s);
@@ -702,7 +710,7 @@ SA_API sa_status sa_forward(const sa_problem* p, const sa_cluster_cfg* qcfg,
   if ((st = do_select(p, scfg, &b.q, &b.k, mask, b.counts, nullptr, b.head_topk, nullptr, scr, s)) != SA_OK)
     return st;
   return do_attn(p, acfg, &b.q, &b.k, b.v_perm, b.v_means, mask, o, tile_rows(qcfg),
-                 max_tiles(p, qcfg), scr, s);
+                 max_tiles(p, qcfg), scr, s, q);
 }
 
 SA_API const char* sa_status_string(sa_status s) {

@@ -144,8 +144,8 @@ hipError_t compact_sub_centroids(const float* expanded, int H, int Cs, int d, co
 size_t bisect_scratch(int H, int N, int d, int leaf);
 // Heads below h0 are rows of x0 (order and leaf offsets to perm0 / off0), the
 // others of x1 (perm1 / off1); H counts both.  One tensor: x1 = x0, h0 = H.
-// With xp0 non-null, the rows in cluster order go to xp0 / xp1 and the leaf
-// means (fp32 [heads][C][d]) to cen0 / cen1 as well.
+// With cen0 non-null, the leaf means (fp32 [heads][C][d]) go to cen0 / cen1
+// and the rows in cluster order to xp0 / xp1 where those are non-null.
 hipError_t bisect_run(const void* x0, const void* x1, int h0, int dtype, int H, int N, int d, int leaf,
                       int iters, int32_t* perm0, int32_t* perm1, int32_t* off0, int32_t* off1, void* xp0,
                       void* xp1, float* cen0, float* cen1, Arena& s, hipStream_t st);
@@ -182,6 +182,7 @@ struct AttnArgs {
   int max_tiles;          // upper bound on query tiles per head (0 = derive)
   float scale;
   const void* q_perm;     // [H][N][d] queries in query-cluster order
+  const void* q_src;      // if set: [H][N][d] queries in original order, read through q_idx instead
   const int32_t* q_idx;   // [H][N] original index of query position
   const int32_t* q_off;   // [H][Cq+1]
   const void* k_perm;     // [H][N][d]
