@@ -844,18 +844,28 @@ __global__ __launch_bounds__(256) void select_wave(SelectArgs a, const double* _
     mx = fmax(mx, l[m]);
   }
   for (int o = 32; o > 0; o >>= 1) mx = fmax(mx, __shfl_xor(mx, o, 64));
+  const double P = a.top_p;
+  const bool pooled = pool_cnt && pool_cnt[row] >= 0;
+  // probabilities only where the rule reads them: a mass target strictly
+  // between 0 and 1, or the statistical threshold (a fixed floor needs the
+  // ranking alone)
+  const bool need_mass = !pooled && a.rule != SA_RULE_STAT && P > 0.0 && P < 1.0;
+  const bool need_z = !pooled && (need_mass || a.rule == SA_RULE_STAT);
   double z = 0.0;
+  if (need_z) {
 #pragma unroll
-  for (int m = 0; m < SW_M; ++m)
-    if (l[m] != -__builtin_huge_val()) z += exp(l[m] - mx);
-  for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
+    for (int m = 0; m < SW_M; ++m)
+      if (l[m] != -__builtin_huge_val()) z += exp(l[m] - mx);
+    for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, 64);
+  }
   unsigned long long key[SW_M], ms[SW_M], one[SW_M];
   int nv = 0;
 #pragma unroll
   for (int m = 0; m < SW_M; ++m) {
     const bool v = l[m] != -__builtin_huge_val();
     key[m] = v ? order_key(l[m]) : NO_KEY;
-    ms[m] = v ? (unsigned long long)llrint(exp(l[m] - mx) / z * MASS_ONE) : 0ull;
+    ms[m] = 0ull;
+    if (need_mass && v) ms[m] = (unsigned long long)llrint(exp(l[m] - mx) / z * MASS_ONE);
     one[m] = v ? 1ull : 0ull;
     nv += v ? 1 : 0;
   }
@@ -866,9 +876,8 @@ __global__ __launch_bounds__(256) void select_wave(SelectArgs a, const double* _
     for (int m = 0; m < SW_M; ++m) c += through(key[m], lane + 64 * m, b) ? 1 : 0;
     return wave_sum_i32(c);
   };
-  const double P = a.top_p;
   int np;
-  if (pool_cnt && pool_cnt[row] >= 0) np = pool_cnt[row];  // decided by the row's pool
+  if (pooled) np = pool_cnt[row];  // decided by the row's pool
   else if (a.rule == SA_RULE_STAT) {
     // BSA statistical threshold: mean + lambda * population std of the row's
     // probabilities (fixed-order sums), then the units at or above it
