@@ -641,20 +641,23 @@ __global__ __launch_bounds__(SUB_T) void select_subspace(SelectArgs a, const int
 // --------------------------------------------------------------------------
 // key clusters
 // --------------------------------------------------------------------------
-// Logits of a head: 64 x 64 output tiles, 4 x 4 outputs per thread (rows
-// ti + 16 r, columns tj + 16 c), so each pair of LDS reads feeds two FMAs;
-// each output sums over d in order, one fp64 FMA per column.
-constexpr int LT = 64;   // output tile edge
+// Logits of a head: LT x LT output tiles, (LT/16) x (LT/16) outputs per
+// thread (rows ti + 16 r, columns tj + 16 c), so each LDS read feeds LT/16
+// FMAs; each output sums over d in order, one fp64 FMA per column.  64-wide
+// tiles halve the LDS reads per FMA; 32-wide ones keep small problems spread
+// over more workgroups.
 constexpr int LC = 32;   // columns of d staged at a time
+template <int LT>
 __global__ __launch_bounds__(256) void logits_kernel(SelectArgs a, double* __restrict__ L) {
+  constexpr int RB = LT / 16;  // outputs per thread along each axis
   __shared__ double qs[LT][LC + 1], ks[LT][LC + 1];
   const int h = blockIdx.z, i0 = blockIdx.y * LT, j0 = blockIdx.x * LT, t = threadIdx.x;
   const int ti = t >> 4, tj = t & 15;
-  double acc[4][4];
+  double acc[RB][RB];
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < RB; ++r)
 #pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = 0.0;
+    for (int c = 0; c < RB; ++c) acc[r][c] = 0.0;
   for (int c0 = 0; c0 < a.d; c0 += LC) {
     for (int e = t; e < LT * LC; e += 256) {
       const int r = e / LC, c = e % LC;
@@ -665,23 +668,23 @@ __global__ __launch_bounds__(256) void logits_kernel(SelectArgs a, double* __res
     __syncthreads();
 #pragma unroll 4
     for (int c = 0; c < LC; ++c) {
-      double qv[4], kv[4];
+      double qv[RB], kv[RB];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) qv[r] = qs[ti + 16 * r][c];
+      for (int r = 0; r < RB; ++r) qv[r] = qs[ti + 16 * r][c];
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) kv[cc] = ks[tj + 16 * cc][c];
+      for (int cc = 0; cc < RB; ++cc) kv[cc] = ks[tj + 16 * cc][c];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int r = 0; r < RB; ++r)
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) acc[r][cc] = fma(qv[r], kv[cc], acc[r][cc]);
+        for (int cc = 0; cc < RB; ++cc) acc[r][cc] = fma(qv[r], kv[cc], acc[r][cc]);
     }
     __syncthreads();
   }
   const int32_t* ko = a.k_off + size_t(h) * (a.Ck + 1);
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < RB; ++r)
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) {
+    for (int cc = 0; cc < RB; ++cc) {
       const int i = i0 + ti + 16 * r, j = j0 + tj + 16 * cc;
       if (i >= a.Cq || j >= a.Ck) continue;
       const int sz = ko[j + 1] - ko[j];
@@ -1276,7 +1279,11 @@ hipError_t select_run(const SelectArgs& a, Arena& s, hipStream_t st) {
   }
   if (a.Ck > SEL_MAX || a.d % LC) return hipErrorInvalidValue;
   double* L = s.get<double>(size_t(a.H) * a.Cq * a.Ck);
-  logits_kernel<<<dim3(ceil_div(a.Ck, LT), ceil_div(a.Cq, LT), a.H), 256, 0, st>>>(a, L);
+  // 64-wide tiles when they still give about a thousand workgroups
+  if (size_t(ceil_div(a.Ck, 64)) * ceil_div(a.Cq, 64) * a.H >= 1024)
+    logits_kernel<64><<<dim3(ceil_div(a.Ck, 64), ceil_div(a.Cq, 64), a.H), 256, 0, st>>>(a, L);
+  else
+    logits_kernel<32><<<dim3(ceil_div(a.Ck, 32), ceil_div(a.Cq, 32), a.H), 256, 0, st>>>(a, L);
   int32_t* pool_cnt = nullptr;
   if (a.domain != SA_DOMAIN_ROW) {
     if (a.domain == SA_DOMAIN_GROUP && a.group < 1) return hipErrorInvalidValue;
