@@ -537,7 +537,9 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8_t a, bf16x8_t b, floatx16 c) {
 __device__ __forceinline__ bf16x8_t as_bf8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
 
 // 16 bytes per lane from a raw buffer over [base, base + nbytes) into LDS
-// (lane l of the wave lands at lds + 16 l); `off` is the lane's byte offset
+// (lane l of the wave lands at lds + 16 l); `off` is the lane's byte offset.
+// The record count is unsigned 32-bit: nbytes carries sizes up to 2^32 - 1
+// (callers form it in uint32_t arithmetic; a head's rows stay below 4 GiB).
 __device__ __forceinline__ void buf_load_lds16(const void* base, int nbytes, bf16_t* lds, uint32_t off) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, BUF_DWORD3);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, off, 0, 0, 0);
@@ -806,7 +808,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
     int ri = 0, pos = R > 0 ? rg[0].x : 0, rend = R > 0 ? rg[0].y : 0;
     // the range after the current one, loaded one range ahead
     int2 rnext = R > 1 ? const_load_int2(rg, 1) : make_int2(0, 0);
-    const int kbytes = N * D * 2, vbytes = N * D * 2;
+    const int kbytes = int(uint32_t(N) * (D * 2)), vbytes = kbytes;
     uint32_t koff[CK], voff[CH];
 #pragma unroll
     for (int q = 0; q < CK; ++q) {
@@ -926,7 +928,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 && 
   } else {
     // ---------------- selected keys, general ranges: row gather --------------
     const bf16_t* vh = (const bf16_t*)a.v_perm + size_t(h) * N * D;
-    const int hbytes = N * D * 2;
+    const int hbytes = int(uint32_t(N) * (D * 2));
     const uint32_t* mrow = a.mask + (size_t(h) * a.Cq + i) * p.W;
     const int32_t* kof = a.k_off + size_t(h) * (a.Ck + 1);
     int scan_word = 0;

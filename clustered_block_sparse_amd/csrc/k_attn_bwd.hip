@@ -56,7 +56,8 @@ __device__ __forceinline__ uint2 lds_read_tr16(const bf16_t* p) {
   return __builtin_bit_cast(uint2, r);
 }
 // 16 bytes per lane from a raw buffer over [base, base + nbytes) into LDS
-// (lane l lands at lds + 16 l; offsets past the end read zeros)
+// (lane l lands at lds + 16 l; offsets past the end read zeros).  nbytes is
+// the unsigned 32-bit record count carried in an int (up to 2^32 - 1).
 __device__ __forceinline__ void buf_load_lds16(const void* base, int nbytes, bf16_t* lds, uint32_t off) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, nbytes, BUF_DWORD3);
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds, 16, off, 0, 0, 0);
@@ -251,7 +252,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs a) {
     gf[s] = as_bf8(g);
   }
   const float sl2 = a.scale * LOG2E;
-  const int kbytes = N * D * 2;
+  const int kbytes = int(uint32_t(N) * (D * 2));
   const bf16_t* kh = a.k_perm + size_t(h) * N * D;
   const bf16_t* vh = a.v_perm + size_t(h) * N * D;
   const int32_t* ko = a.k_off + size_t(h) * (a.Ck + 1);
@@ -389,7 +390,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     vf[s] = as_bf8(v);
   }
   const float sl2 = a.scale * LOG2E;
-  const int qbytes = N * D * 2;
+  const int qbytes = int(uint32_t(N) * (D * 2));
   const bf16_t* qh = a.q_perm + size_t(h) * N * D;
   const bf16_t* gh = a.dO_perm + size_t(h) * N * D;
   const int32_t* qo = a.q_off + size_t(h) * (a.Cq + 1);

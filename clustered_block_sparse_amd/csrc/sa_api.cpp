@@ -29,6 +29,8 @@ sa_status check_problem(const sa_problem* p) {
   if (int64_t(p->frames) * p->height * p->width != p->n) return SA_ERR_SHAPE;
   if (p->d != 64 && p->d != 128) return SA_ERR_SHAPE;
   if (p->n > (1 << 24) || int64_t(p->heads) * p->n > (int64_t(1) << 31)) return SA_ERR_SHAPE;
+  // the kernels address one head's rows of a tensor with 32-bit byte offsets
+  if (int64_t(p->n) * p->d * esize(p->dtype) >= (int64_t(1) << 32)) return SA_ERR_SHAPE;
   return SA_OK;
 }
 

@@ -86,6 +86,9 @@ enum { SA_F32 = 0, SA_BF16 = 1 };
 enum { SA_KMEANS = 0, SA_BISECT = 1, SA_SUBSPACE = 2, SA_RASTER = 3 };
 enum { SA_INIT_FIRST = 0, SA_INIT_GIVEN = 1 };
 
+/* Size limits (SA_ERR_SHAPE otherwise): n <= 2^24, heads*n <= 2^31, and one
+ * head's rows of a tensor, n*d*(2 for bf16, 4 for f32) bytes, below 4 GiB
+ * (kernels address them with 32-bit byte offsets; bf16 at d = 128: n < 2^24). */
 typedef struct sa_problem {
   int32_t heads, n, d;            /* d in {64, 128}                                 */
   int32_t frames, height, width;  /* n == frames*height*width; (1,1,n) unstructured */
@@ -93,7 +96,7 @@ typedef struct sa_problem {
 } sa_problem;
 
 typedef struct sa_cluster_cfg {
-  int32_t method;      /* SA_KMEANS | SA_BISECT | SA_SUBSPACE                       */
+  int32_t method;      /* SA_KMEANS | SA_BISECT | SA_SUBSPACE | SA_RASTER           */
   int32_t clusters;    /* KMEANS: C (1..1024, <= n); SUBSPACE: per-slice C (<= 32)  */
   int32_t leaf;        /* BISECT leaf size (>= 4)                                   */
   int32_t tile_cap;    /* upper bound on query rows per attention tile (tiling

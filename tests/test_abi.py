@@ -82,6 +82,21 @@ def test_validation_before_work(lib):
     assert lib.sa_cluster(ctypes.byref(ok), ctypes.byref(km), None, None, FAKE, 1 << 30, None) == 1
 
 
+def test_size_limits(lib):
+    """n <= 2^24, heads*n <= 2^31, and one head's rows of a tensor below 4 GiB
+    (32-bit byte offsets inside a head)."""
+    km = L.cluster_cfg("kmeans", clusters=8)
+    assert call_cluster(lib, L.problem(1, (1 << 24) + 64, 64, 1, 1, (1 << 24) + 64, "bf16"), km) == 2
+    assert call_cluster(lib, L.problem(129, 1 << 24, 64, 1, 1, 1 << 24, "bf16"), km) == 2  # heads*n
+    # bf16 d=128: 2^24 rows are exactly 4 GiB per head; one row fewer fits
+    assert call_cluster(lib, L.problem(1, 1 << 24, 128, 1, 1, 1 << 24, "bf16"), km) == 2
+    assert call_cluster(lib, L.problem(1, (1 << 24) - 1, 128, 1, 1, (1 << 24) - 1, "bf16"), km, 16) == 4
+    # f32 d=128: the bound is 2^23 rows
+    assert call_cluster(lib, L.problem(1, 1 << 23, 128, 1, 1, 1 << 23, "f32"), km) == 2
+    assert call_cluster(lib, L.problem(1, (1 << 23) - 1, 128, 1, 1, (1 << 23) - 1, "f32"), km, 16) == 4
+    assert call_cluster(lib, L.problem(1, 1 << 24, 64, 1, 1, 1 << 24, "bf16"), km, 16) == 4
+
+
 def test_select_and_forward_validation(lib):
     p = L.problem(1, 256, 64, 4, 8, 8, "f32")
     km = L.cluster_cfg("kmeans", clusters=8)
