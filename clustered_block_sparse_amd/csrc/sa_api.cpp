@@ -368,8 +368,13 @@ sa_status side_by_side(hipStream_t st, A&& a, B&& b) {
     ForkJoin n{};
     if (hipStreamCreateWithFlags(&n.s2, hipStreamNonBlocking) != hipSuccess ||
         hipEventCreateWithFlags(&n.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess)
+        hipEventCreateWithFlags(&n.join, hipEventDisableTiming) != hipSuccess) {
+      // release what was made, so that a later call starts over
+      if (n.join) (void)hipEventDestroy(n.join);
+      if (n.fork) (void)hipEventDestroy(n.fork);
+      if (n.s2) (void)hipStreamDestroy(n.s2);
       return SA_ERR_HIP;
+    }
     f = n;
   }
   if (hipEventRecord(f.fork, st) != hipSuccess || hipStreamWaitEvent(f.s2, f.fork, 0) != hipSuccess)
