@@ -127,9 +127,13 @@ def test_stage_E_select(w):
 MID_ODD = replace(MID_S, name="mid_small_odd_c", q=replace(MID_S.q, clusters=50), k=replace(MID_S.k, clusters=77))
 TAB_KM = replace(TAB_S, name="tab_small_kmeans", q=wl.ClusterSpec("kmeans", 40, iters=5),
                  k=wl.ClusterSpec("kmeans", 100, iters=5))
+# more than 128 clusters: the assignment on the vector ALUs and the separate
+# member-mean pass, up to the largest supported count (1024)
+MID_BIG_C = replace(MID_S, name="mid_small_c300_c1024", q=replace(MID_S.q, clusters=300),
+                    k=replace(MID_S.k, clusters=1024))
 
 
-@pytest.mark.parametrize("w", [TINY, MID_S, MID_ODD, TAB_KM], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [TINY, MID_S, MID_ODD, TAB_KM, MID_BIG_C], ids=lambda w: w.name)
 def test_stage_AB_kmeans_step(w):
     """One assignment + update from given centroids."""
     say(f"[stage A/B] {w.name}")
