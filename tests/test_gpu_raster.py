@@ -18,7 +18,7 @@ from clustered_block_sparse_amd import _lib as L
 from clustered_block_sparse_amd import api
 from clustered_block_sparse_amd import workloads as wl
 
-from gpu_helpers import (DEV, WAN_S, assert_attn_close, check_selection_head, inputs, say, scale_of, to_np,
+from gpu_helpers import (DEV, TAB_S, WAN_S, assert_attn_close, check_selection_head, inputs, say, scale_of, to_np,
                          unpack_mask, workspace_for)
 
 pytestmark = pytest.mark.gpu
@@ -35,6 +35,8 @@ CASES = [
     raster(WAN_S, (1, 24, 40), "wan_small_raster1d", top_p=0.7, floor=2),  # one frame per block
     raster(WAN_S, (2, 7, 9), "wan_small_raster3d_head_global", domain="head", top_p=0.85),
     raster(WAN_S, (1, 8, 16), "wan_small_raster3d_fixed", top_p=0.0, floor=5, compensate=True),
+    # d = 64 on an unstructured 1 x 1 x N grid: runs of 128 consecutive tokens (65 blocks, the last of 100)
+    raster(TAB_S, (1, 1, 128), "tab_small_raster_runs", top_p=0.9, floor=2, compensate=True),
 ]
 
 
