@@ -73,7 +73,7 @@ def trace_table(stats_csv: str, title: str, cmd: str) -> str:
         a[0] += c
         a[1] += t
     total = sum(t for _, t in agg.values()) or 1.0
-    out = [f"# {title}", "", "Command (from the repo root on the GPU box):", "", "```", cmd, "```", "",
+    out = [f"# {title}", "", "Command (from the repo root, on the MI355X):", "", "```", cmd, "```", "",
            "| kernel | calls | total ms | avg us | % |", "|---|---|---|---|---|"]
     for s, (c, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
         out.append(f"| {s} | {c} | {t / 1e6:.2f} | {t / c / 1e3:.1f} | {100 * t / total:.1f} |")
@@ -90,7 +90,7 @@ def bench_table(paths: list[str], title: str, cmd: str) -> str:
                     rows.append(json.loads(line))
                 except ValueError:
                     pass
-    out = [f"# {title}", "", "Commands (from the repo root on the GPU box):", "", "```", cmd, "```", "",
+    out = [f"# {title}", "", "Commands (from the repo root, on the MI355X):", "", "```", cmd, "```", "",
            "| workload | H x N x d | density | cache | ms/layer | step median / min (ms) | cluster | permute V | "
            "select | attention call | attention kernels (ms) | TFLOP/s (frac) | dense own / SDPA (ms) | "
            "speedup | value TFLOP/s |",
@@ -122,7 +122,7 @@ def counters_table(counter_csv: str, title: str, cmd: str) -> str:
     for (kn, _), d in acc.items():
         per[kn].append(d)
     cols = sorted(names)
-    out = [f"# {title}", "", "Command (from the repo root on the GPU box):", "", "```", cmd, "```", "",
+    out = [f"# {title}", "", "Command (from the repo root, on the MI355X):", "", "```", cmd, "```", "",
            "Per-dispatch means.", "", "| kernel | dispatches | " + " | ".join(cols) + " |",
            "|---|---|" + "---|" * len(cols)]
     for kn, ds in sorted(per.items()):
@@ -189,7 +189,7 @@ def kernel_traffic_table(fetch_csv: str, write_csv: str, stats_csv: str, copy_by
         us = dur[k][1] / dur[k][0] / 1e3
         rows.append((dur[k][1], f"| {k} | {len(f[k])} | {rd / 1e6:.1f} | {wr / 1e6:.1f} | {us:.1f} | "
                                 f"{(rd + wr) / (us * 1e-6) / 1e12:.2f} |"))
-    out = [f"# {title}", "", "Commands (from the repo root on the GPU box):", "", "```", cmd, "```", "",
+    out = [f"# {title}", "", "Commands (from the repo root, on the MI355X):", "", "```", cmd, "```", "",
            f"Counters scaled by the readings of 1 GiB device copies: FETCH_SIZE x {fs:.3f}, WRITE_SIZE x {wsc:.3f}.",
            "Rows by total time in the trace.", "",
            "| kernel | dispatches | read MB / dispatch | written MB / dispatch | avg us (trace) | TB/s |",
