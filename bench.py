@@ -32,7 +32,7 @@ step (warm-up and timed), which evicts the 256 MB memory-side cache, so each
 step starts from HBM; the fills sit between the events, and in that mode
 `ms_per_step` and `value` come from the events' mean.  `--gemm-probe` adds the
 rate of torch's bf16 GEMM (hipBLASLt) on 16384^3, a practical ceiling for MFMA
-work on the same box.
+work on the same GPU.
 """
 
 from __future__ import annotations
