@@ -51,8 +51,11 @@ def oracle_select(w, rq, rk, qbar=None, kbar=None):
     return out
 
 
+# fp32 inputs (the one-thread-per-row path) at d = 128 and 64, several tiles,
+# compensation on
+F32_CASES = [replace(WAN_S, dtype="f32", name="wan_small_f32"), replace(TAB_S, dtype="f32", name="tab_small_f32")]
 ATTN_CASES = [TINY, MID_S, WAN_S, TAB_S, WAN_S.forced_density(0.1), TAB_S.forced_density(0.1),
-              replace(WAN_S, compensate=False, name="wan_small_nocomp")]
+              replace(WAN_S, compensate=False, name="wan_small_nocomp")] + F32_CASES
 
 
 @pytest.mark.parametrize("w", ATTN_CASES, ids=lambda w: f"{w.name}-P{w.top_p}-k{w.floor}")
@@ -263,7 +266,9 @@ WAN_M = replace(wl.WAN, name="wan_mid", heads=2, frames=10, height=30, width=40)
 TAB_M = replace(wl.TABULAR, name="tab_mid", heads=2, width=20000 + 77)             # N = 20077, d = 64
 
 
-@pytest.mark.parametrize("w", [WAN_S, replace(WAN_S, d=64, name="wan_small_d64"), WAN_M, TAB_M],
+@pytest.mark.parametrize("w", [WAN_S, replace(WAN_S, d=64, name="wan_small_d64"), WAN_M, TAB_M,
+                               replace(WAN_M, dtype="f32", name="wan_mid_f32"),
+                               replace(TAB_S, dtype="f32", name="tab_small_f32")],
                          ids=lambda w: w.name)
 def test_stage_C_bisect_smooth(w):
     """Smooth fields have near-tie medians.  Walking the oracle's tree from
@@ -312,7 +317,7 @@ def test_stage_C_bisect_smooth(w):
             assert np.array_equal(perm, r["perm"])
 
 
-FWD_CASES = [TINY, MID_S, WAN_S, TAB_S, WAN_S.forced_density(0.1)]
+FWD_CASES = [TINY, MID_S, WAN_S, TAB_S, WAN_S.forced_density(0.1)] + F32_CASES
 
 
 @pytest.mark.parametrize("w", FWD_CASES, ids=lambda w: f"{w.name}-P{w.top_p}")
