@@ -22,6 +22,9 @@ pytestmark = pytest.mark.gpu
 HY_S = replace(wl.HUNYUAN, name="hy_small", heads=2, frames=5, height=16, width=24)   # N = 1920, 32^3 combos
 HY_S8 = replace(HY_S, name="hy_small_cs8", k=replace(wl.HUNYUAN.k, clusters=8))
 HY_CASES = [HY_S, HY_S8, HY_S.forced_density(0.1), replace(HY_S8, online_topk=False, top_p=0.7, floor=40)]
+# fp32 inputs: each slice's k-means on the vector ALUs, the attention one
+# thread per query row
+HY_F32 = replace(HY_S, name="hy_small_f32", dtype="f32")
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -67,7 +70,7 @@ def subspace_step(p, w, x, start, ws):
     return out
 
 
-@pytest.mark.parametrize("w", [HY_S, HY_S8], ids=lambda w: w.name)
+@pytest.mark.parametrize("w", [HY_S, HY_S8, HY_F32], ids=lambda w: w.name)
 def test_subspace_stage_A_slices(w):
     """One step of each slice's k-means from given centroids (the 32- and
     48-column slices at d = 128): slice labels bit-exact except oracle near
@@ -232,7 +235,7 @@ def test_subspace_attention(w):
     assert_attn_close(o, ref, q.dtype, w.name)
 
 
-@pytest.mark.parametrize("w", [HY_S, HY_S8.forced_density(0.1)], ids=lambda w: f"{w.name}-P{w.top_p}")
+@pytest.mark.parametrize("w", [HY_S, HY_S8.forced_density(0.1), HY_F32], ids=lambda w: f"{w.name}-P{w.top_p}")
 def test_subspace_forward(w):
     say(f"[subspace forward] {w.name}")
     q, k, v = inputs(w)
